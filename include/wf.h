@@ -1,0 +1,225 @@
+/*
+ * wf.h — C ABI of the block-verification engine for Whisper-shaped decoders
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The calls follow the problem as the pages state it:
+ *
+ *  - wf_encode_kv: the cross-attention keys and values of every decoder
+ *    layer are computed from the audio memory once per request and are only
+ *    read afterwards (SGLang-Omni "Whisper ASR" cookbook, section "Breakable
+ *    Prefill CUDA Graph").
+ *  - wf_verify_block: one causal target pass over the anchor plus K
+ *    candidates yields the target's prediction at every position
+ *    ("Whisper-Flash: Acoustically Conditioned Parallel Drafting for Faster
+ *    Whisper Decoding", section 3.1, eq. 1). A prefill is the same call with
+ *    the prompt as the block.
+ *  - wf_accept: keep candidates while they agree and emit the target's own
+ *    token at the first disagreement, or a bonus after a full block (section
+ *    3.1); at temperature T > 0 accept with probability min(1, p/q) and
+ *    resample from (p - q)+ (section 3.1, appendix A.4).
+ *  - wf_rollback: keep L + 1 + a cache positions, the old anchor plus the
+ *    accepted candidates (appendix A.1).
+ *
+ * Conventions
+ *  - Every pointer named d_* is device memory (HIP); h_* is host memory.
+ *  - The caller owns all memory: weights, KV pools, page table, workspace and
+ *    per-call inputs/outputs. The engine stores raw pointers and never
+ *    allocates or frees device memory; keep the buffers alive until
+ *    wf_destroy.
+ *  - All calls except wf_create, wf_destroy and wf_device_state are
+ *    asynchronous on the given stream (a hipStream_t passed as void*; NULL is
+ *    the null stream) and make no host<->device copies, so a sequence of
+ *    them can be captured in a HIP graph.
+ *  - Host-checkable errors (null pointers, shapes, capacities) return a
+ *    negative wf_status before anything is launched; wf_last_error() then
+ *    returns a thread-local message. Data-dependent errors are set in a
+ *    per-slot device error word (WF_DERR_* bits) and that request's work is
+ *    skipped; wf_device_state copies the words to the host.
+ *  - One engine is used from one host thread at a time. Nothing throws
+ *    across the ABI.
+ *
+ * Numerics
+ *  - Weights are bf16. GEMMs run on bf16 MFMA with fp32 accumulation; the
+ *    activation operand is carried as an unevaluated pair of bf16 values
+ *    (hi + lo), so its rounding error is about 2^-16 relative.
+ *  - The residual stream, layer-norm statistics, softmax and GELU are fp32.
+ *  - Self-attention K/V pages and cross-attention K/V are stored in fp16;
+ *    attention products run on fp16 MFMA with fp32 accumulation.
+ *  - Every reduction has a fixed order that does not depend on the number
+ *    of rows in the block or on the block length: a row's logits are the
+ *    same bits whether it is verified alone or inside a block. No float
+ *    atomics are used; repeated calls give identical bits.
+ */
+#ifndef WF_H
+#define WF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct wf_engine wf_engine;
+
+typedef enum {
+    WF_OK = 0,
+    WF_EINVAL = -1,     /* null pointer or bad scalar argument */
+    WF_ESHAPE = -2,     /* unsupported model shape */
+    WF_ECAPACITY = -3,  /* a buffer is too small or a count exceeds a maximum */
+    WF_EHIP = -4,       /* a HIP runtime call failed */
+    WF_EDEVICE = -5,    /* no usable gfx950 device */
+    WF_ESTATE = -6      /* call out of order */
+} wf_status;
+
+/* Bits of the per-slot device error word. A slot with a nonzero word is
+ * skipped by every later call until wf_reset clears it. */
+#define WF_DERR_CONTEXT 1   /* L + n_tok > n_ctx */
+#define WF_DERR_TOKEN   2   /* token id outside [0, vocab) or n_tok > T */
+#define WF_DERR_STATE   4   /* verify on a slot whose last verify was not rolled back */
+#define WF_DERR_ACCEPT  8   /* rollback with a > n_tok - 1, or k > budget - 1 */
+#define WF_DERR_NAN     16  /* a NaN logit */
+#define WF_DERR_PAGE    32  /* page-table entry outside [0, n_pages) */
+#define WF_DERR_SAMPLE  64  /* sampling inputs missing or q(y) = 0 for a draft */
+
+/* Model and capacity description. The supported shapes have head_dim 16 or
+ * 64, d_model = n_heads * head_dim with d_model a multiple of 64, d_ffn a
+ * multiple of 64, n_ctx a multiple of 32 and page_size 16. */
+typedef struct {
+    int32_t n_layers;     /* decoder layers (32 for large-v3, 4 for turbo) */
+    int32_t d_model;      /* width (1280) */
+    int32_t n_heads;      /* attention heads (20) */
+    int32_t head_dim;     /* 64 (16 for the tiny test model) */
+    int32_t d_ffn;        /* MLP width (5120) */
+    int32_t vocab;        /* vocabulary (51866); the LM head is tied to tok_emb */
+    int32_t n_frames;     /* audio frames per request (1500 for a 30 s window) */
+    int32_t n_ctx;        /* decoder context (448) */
+    int32_t max_batch;    /* number of request slots; slot ids are [0, max_batch) */
+    int32_t max_rows;     /* largest n * T of one wf_verify_block call */
+    int32_t page_size;    /* tokens per KV page; must be 16 */
+    int32_t n_pages;      /* physical pages in the KV pool */
+    int32_t eos_id;       /* end-of-transcript token id */
+    float ln_eps;         /* layer-norm epsilon (1e-5) */
+} wf_config;
+
+/* Per-layer weights: bf16, PyTorch Linear convention (weight [out, in],
+ * row-major). Layer-norm gains/biases and all biases are bf16 vectors.
+ * Self-attention has no key bias, cross-attention no key bias. */
+typedef struct {
+    const void *ln1_g, *ln1_b;                   /* [d] */
+    const void *wq, *bq, *wk, *wv, *bv, *wo, *bo; /* [d,d] / [d] */
+    const void *ln2_g, *ln2_b;
+    const void *wqc, *bqc, *wkc, *wvc, *bvc, *woc, *boc;
+    const void *ln3_g, *ln3_b;
+    const void *w1, *b1;                          /* [d_ffn, d], [d_ffn] */
+    const void *w2, *b2;                          /* [d, d_ffn], [d] */
+} wf_layer_weights;
+
+typedef struct {
+    const void *tok_emb;   /* [vocab, d]; also the LM head */
+    const void *pos_emb;   /* [n_ctx, d] learned positions */
+    const void *lnf_g, *lnf_b;
+    const wf_layer_weights *layers; /* host array of n_layers entries (copied) */
+} wf_weights;
+
+/* Sizes of the caller-allocated device buffers for a configuration.
+ * kv_pool:  fp16 [n_layers][n_pages][2][n_heads][page_size][head_dim]
+ *           (the V half of a page is stored transposed, [head_dim][page_size]).
+ * xkv_pool: fp16 per slot, per layer: K [n_heads][F_pad][head_dim] then
+ *           V [n_heads][head_dim][F_pad], F_pad = n_frames rounded up to 32.
+ *           Must be zero-filled before the first wf_encode_kv.
+ * workspace: engine-private scratch and slot state.
+ * Return 0 for an invalid configuration. */
+size_t wf_kv_pool_bytes(const wf_config *cfg);
+size_t wf_xkv_pool_bytes(const wf_config *cfg);
+size_t wf_workspace_bytes(const wf_config *cfg);
+
+/* Create an engine on the current HIP device. d_page_table is int32
+ * [max_batch][n_ctx / page_size]: slot s's logical page j lives in physical
+ * page d_page_table[s][j] of kv_pool (the caller may shuffle them). The
+ * workspace is zeroed here (synchronously). Fails with WF_EDEVICE when the
+ * current device is not gfx950. */
+wf_status wf_create(const wf_config *cfg, const wf_weights *w,
+                    void *kv_pool, size_t kv_bytes,
+                    void *xkv_pool, size_t xkv_bytes,
+                    const int32_t *d_page_table,
+                    void *workspace, size_t ws_bytes,
+                    wf_engine **out);
+void wf_destroy(wf_engine *e);
+const char *wf_last_error(void);
+
+/* Set cache length 0, clear the pending-verify flag and the error word of
+ * n slots. */
+wf_status wf_reset(wf_engine *e, int32_t n, const int32_t *d_slots, void *stream);
+
+/* Write-once cross K/V for n slots from the audio memory d_enc, bf16
+ * [n][n_frames][d_model]:  K_c = enc Wkc^T,  V_c = enc Wvc^T + bvc,  for every
+ * layer. */
+wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots,
+                       const void *d_enc, void *stream);
+
+/* One causal pass over a block of T rows per request.
+ * d_tokens int32 [n][T]: row 0 is the anchor, rows 1..n_tok-1 the
+ *   candidates (for a prefill: the prompt). Rows at or beyond n_tok[b] are
+ *   padding: computed but never written to the cache.
+ * d_n_tok int32 [n], 0 <= n_tok <= T; 0 marks an inactive request (skipped).
+ * Row i of request b sits at position L_b + i, L_b = the slot's cache length,
+ *   attends to cache positions 0..L_b-1 and block rows 0..i, and its K/V are
+ *   written at L_b + i when i < n_tok[b]. The slot is then pending until
+ *   wf_rollback.
+ * d_argmax int32 [n][T]: the target's choice for the position after each
+ *   row (largest logit, lowest id on ties); -1 for skipped rows.
+ * d_logits: NULL, or fp32 [n][T][vocab] logits.
+ * Requires n <= max_batch, n*T <= max_rows, 1 <= T <= n_ctx. */
+wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
+                          const int32_t *d_tokens, int32_t T,
+                          const int32_t *d_n_tok, int32_t *d_argmax,
+                          float *d_logits, void *stream);
+
+/* Acceptance for one round, per request b with k = n_tok[b] - 1 candidates
+ * and R = d_budget[b] output tokens left (k <= R - 1 is required).
+ * temperature == 0: greedy — a = the longest prefix with
+ *   tokens[b][i] == argmax[b][i-1] for i = 1..a; an accepted EOS stops there
+ *   with no bonus; otherwise c = argmax[b][a] is emitted and is the next
+ *   anchor.
+ * temperature > 0: rejection sampling on fp32 softmax(logits / T) with the
+ *   optional suppression mask d_suppress (uint8 [vocab], nonzero = id never
+ *   emitted), draft probabilities d_q fp32 [n][T-1][vocab] (row i-1 is q_i,
+ *   the distribution candidate i was drawn from) and Philox4x64-10 uniforms
+ *   keyed by (seed, d_request_id[b], d_step[b], position, stream).
+ * Outputs (int32 [n]): d_n_acc = a; d_next_token = c or -1 when an accepted
+ *   EOS ended the request; d_n_emit = tokens emitted this round;
+ *   d_done = 1 when the request ended (EOS emitted or budget used up).
+ * Emitted tokens are tokens[b][1..a] followed by next_token (if >= 0). */
+wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
+                    const int32_t *d_n_tok, const int32_t *d_budget,
+                    const int32_t *d_argmax, const float *d_logits,
+                    const float *d_q, const uint8_t *d_suppress,
+                    float temperature, uint64_t seed,
+                    const int32_t *d_request_id, const int32_t *d_step,
+                    int32_t *d_n_acc, int32_t *d_next_token,
+                    int32_t *d_n_emit, int32_t *d_done, void *stream);
+
+/* Keep L + 1 + a positions of each pending slot (d_n_acc int32 [n]); entries
+ * beyond stay allocated and are masked by the length. A slot with no pending
+ * verify is left unchanged. a > n_tok - 1 sets WF_DERR_ACCEPT. */
+wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots,
+                      const int32_t *d_n_acc, void *stream);
+
+/* Synchronise the stream and copy max_batch error words and cache lengths
+ * to the host (either pointer may be NULL). */
+wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *stream);
+
+/* Measurement. While timing is enabled every launch is bracketed with HIP
+ * events on its stream (so calls are no longer graph-capturable).
+ * wf_get_timing synchronises and returns the summed duration and the number
+ * of launches of one kind since timing was last enabled:
+ * 0 = decoder projection GEMMs, 1 = LM head, 2 = self-attention,
+ * 3 = cross-attention, 4 = everything else. */
+wf_status wf_set_timing(wf_engine *e, int32_t enable);
+wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* WF_H */

@@ -1,0 +1,238 @@
+"""ctypes binding of libwf.so — argument marshalling only.
+
+Every compute step runs in the library's HIP kernels; this module turns
+torch tensors into pointers, picks the current stream and raises on a
+negative status. ``Engine`` additionally owns the device buffers the C ABI
+expects the caller to provide (weights, KV pools, page table, workspace),
+allocated with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libwf.so")
+HEADER = os.path.join(HERE, "..", "include", "wf.h")
+
+_lib = None
+
+
+class WFError(RuntimeError):
+    pass
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "d_model", "n_heads", "head_dim", "d_ffn", "vocab", "n_frames", "n_ctx",
+        "max_batch", "max_rows", "page_size", "n_pages", "eos_id")] + [("ln_eps", ctypes.c_float)]
+
+
+LAYER_FIELDS = ["ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
+                "ln2_g", "ln2_b", "wqc", "bqc", "wkc", "wvc", "bvc", "woc", "boc",
+                "ln3_g", "ln3_b", "w1", "b1", "w2", "b2"]
+
+
+class LayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [("tok_emb", ctypes.c_void_p), ("pos_emb", ctypes.c_void_p),
+                ("lnf_g", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LayerWeights))]
+
+
+def header_functions() -> list:
+    """Names of the functions include/wf.h declares."""
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wf_[a-z_]+)\s*\(", txt)))
+
+
+def load():
+    """Load libwf.so; fails loudly when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m speculative_decoding_encoder_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, SZ, VP = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p
+    cfgp = ctypes.POINTER(Config)
+    sig = {
+        "wf_kv_pool_bytes": (SZ, [cfgp]),
+        "wf_xkv_pool_bytes": (SZ, [cfgp]),
+        "wf_workspace_bytes": (SZ, [cfgp]),
+        "wf_create": (I32, [cfgp, ctypes.POINTER(Weights), P, SZ, P, SZ, P, P, SZ,
+                            ctypes.POINTER(VP)]),
+        "wf_destroy": (None, [P]),
+        "wf_last_error": (ctypes.c_char_p, []),
+        "wf_reset": (I32, [P, I32, P, P]),
+        "wf_encode_kv": (I32, [P, I32, P, P, P]),
+        "wf_verify_block": (I32, [P, I32, P, P, I32, P, P, P, P]),
+        "wf_accept": (I32, [P, I32, P, I32, P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64,
+                            P, P, P, P, P, P, P]),
+        "wf_rollback": (I32, [P, I32, P, P, P]),
+        "wf_device_state": (I32, [P, P, P, P]),
+        "wf_set_timing": (I32, [P, I32]),
+        "wf_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
+                                ctypes.POINTER(ctypes.c_int32)]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().wf_last_error().decode(errors="replace")
+        raise WFError(f"{what} failed with status {status}: {msg}")
+
+
+def _p(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def make_config(shape, max_batch: int, max_rows: int, n_pages: Optional[int] = None) -> Config:
+    pps = shape.n_ctx // 16
+    return Config(n_layers=shape.n_layers, d_model=shape.d_model, n_heads=shape.n_heads,
+                  head_dim=shape.head_dim, d_ffn=shape.d_ffn, vocab=shape.vocab,
+                  n_frames=shape.n_frames, n_ctx=shape.n_ctx, max_batch=max_batch,
+                  max_rows=max_rows, page_size=16,
+                  n_pages=n_pages if n_pages is not None else max_batch * pps,
+                  eos_id=shape.eos_id, ln_eps=shape.ln_eps)
+
+
+def workspace_bytes(cfg: Config) -> int:
+    return int(load().wf_workspace_bytes(ctypes.byref(cfg)))
+
+
+class Engine:
+    """One engine on the current CUDA (HIP) device with its buffers.
+
+    ``weights_bits``: name -> bf16 bit patterns (uint16 numpy arrays), the
+    naming of ``synthetic.make_weights``. ``page_table``: optional int32
+    numpy array [max_batch, n_ctx/16] of physical page ids.
+    """
+
+    def __init__(self, shape, weights_bits: Dict[str, np.ndarray], max_batch: int,
+                 max_rows: int, page_table: Optional[np.ndarray] = None,
+                 n_pages: Optional[int] = None):
+        import torch
+        self.torch = torch
+        self.lib = load()
+        self.shape = shape
+        self.dev = torch.device("cuda", torch.cuda.current_device())
+        self.cfg = make_config(shape, max_batch, max_rows, n_pages)
+        pps = shape.n_ctx // 16
+        self.w = {}
+        for k, v in weights_bits.items():
+            t = torch.from_numpy(np.ascontiguousarray(v).view(np.int16))
+            self.w[k] = t.to(self.dev).view(torch.bfloat16)
+        lw = (LayerWeights * shape.n_layers)()
+        for l in range(shape.n_layers):
+            for f in LAYER_FIELDS:
+                setattr(lw[l], f, self.w[f"L{l}.{f}"].data_ptr())
+        self._lw = lw
+        self._weights = Weights(self.w["tok_emb"].data_ptr(), self.w["pos_emb"].data_ptr(),
+                                self.w["lnf_g"].data_ptr(), self.w["lnf_b"].data_ptr(), lw)
+        cfgp = ctypes.byref(self.cfg)
+        kvb = int(self.lib.wf_kv_pool_bytes(cfgp))
+        xkvb = int(self.lib.wf_xkv_pool_bytes(cfgp))
+        wsb = int(self.lib.wf_workspace_bytes(cfgp))
+        if kvb == 0 or xkvb == 0 or wsb == 0:
+            raise WFError("invalid configuration for libwf")
+        self.kv = torch.zeros(kvb, dtype=torch.uint8, device=self.dev)
+        self.xkv = torch.zeros(xkvb, dtype=torch.uint8, device=self.dev)
+        self.ws = torch.zeros(wsb, dtype=torch.uint8, device=self.dev)
+        if page_table is None:
+            page_table = np.arange(max_batch * pps, dtype=np.int32).reshape(max_batch, pps)
+        self.page_table = torch.from_numpy(np.ascontiguousarray(page_table, dtype=np.int32)).to(self.dev)
+        h = ctypes.c_void_p()
+        torch.cuda.synchronize()
+        _check(self.lib.wf_create(cfgp, ctypes.byref(self._weights), self.kv.data_ptr(), kvb,
+                                  self.xkv.data_ptr(), xkvb, self.page_table.data_ptr(),
+                                  self.ws.data_ptr(), wsb, ctypes.byref(h)), "wf_create")
+        self.h = h
+
+    def close(self):
+        if getattr(self, "h", None):
+            self.lib.wf_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -- thin wrappers with the C names ----------------------------------
+    def wf_reset(self, slots, stream=None):
+        _check(self.lib.wf_reset(self.h, slots.numel(), _p(slots), _stream(stream)), "wf_reset")
+
+    def wf_encode_kv(self, slots, enc, stream=None):
+        _check(self.lib.wf_encode_kv(self.h, slots.numel(), _p(slots), _p(enc), _stream(stream)),
+               "wf_encode_kv")
+
+    def wf_verify_block(self, slots, tokens, n_tok, argmax, logits=None, stream=None):
+        n, T = tokens.shape
+        _check(self.lib.wf_verify_block(self.h, n, _p(slots), _p(tokens), T, _p(n_tok),
+                                        _p(argmax), _p(logits), _stream(stream)),
+               "wf_verify_block")
+
+    def wf_accept(self, tokens, n_tok, budget, argmax, n_acc, next_token, n_emit, done,
+                  logits=None, q=None, suppress=None, temperature=0.0, seed=0,
+                  request_id=None, step=None, stream=None):
+        n, T = tokens.shape
+        _check(self.lib.wf_accept(self.h, n, _p(tokens), T, _p(n_tok), _p(budget), _p(argmax),
+                                  _p(logits), _p(q), _p(suppress), float(temperature), int(seed),
+                                  _p(request_id), _p(step), _p(n_acc), _p(next_token),
+                                  _p(n_emit), _p(done), _stream(stream)), "wf_accept")
+
+    def wf_rollback(self, slots, n_acc, stream=None):
+        _check(self.lib.wf_rollback(self.h, slots.numel(), _p(slots), _p(n_acc),
+                                    _stream(stream)), "wf_rollback")
+
+    def wf_device_state(self, stream=None):
+        mb = self.cfg.max_batch
+        err = (ctypes.c_int32 * mb)()
+        ln = (ctypes.c_int32 * mb)()
+        _check(self.lib.wf_device_state(self.h, err, ln, _stream(stream)), "wf_device_state")
+        return np.array(err[:], np.int32), np.array(ln[:], np.int32)
+
+    def wf_set_timing(self, enable: bool):
+        _check(self.lib.wf_set_timing(self.h, 1 if enable else 0), "wf_set_timing")
+
+    def wf_get_timing(self, kind: int):
+        ms = ctypes.c_double()
+        cnt = ctypes.c_int32()
+        _check(self.lib.wf_get_timing(self.h, kind, ctypes.byref(ms), ctypes.byref(cnt)),
+               "wf_get_timing")
+        return ms.value, cnt.value
+
+    # -- helpers ---------------------------------------------------------
+    def i32(self, a: Sequence[int]):
+        return self.torch.as_tensor(np.asarray(a, dtype=np.int32), device=self.dev)
+
+    def bf16(self, bits: np.ndarray):
+        t = self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+        return t.to(self.dev).view(self.torch.bfloat16)
+
+
+TIMING_GEMM, TIMING_LMHEAD, TIMING_SELF, TIMING_CROSS, TIMING_OTHER = range(5)

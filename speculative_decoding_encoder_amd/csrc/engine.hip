@@ -1,0 +1,589 @@
+// Host side of libwf.so: argument checks, workspace layout, and the launch
+// plan of one verify pass (embed, then per layer LN1 -> QKV + KV append ->
+// self-attention -> O + residual -> LN2 -> cross Q -> cross-attention ->
+// O_c + residual -> LN3 -> fc1 + GELU -> fc2 + residual, then the final LN,
+// the tied LM head with its argmax, and the per-row argmax merge).
+#include "../../include/wf.h"
+#include "wf_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+using namespace wf;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+wf_status fail(wf_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+struct LayerW {
+    const uint16_t *ln1_g, *ln1_b, *wq, *bq, *wk, *wv, *bv, *wo, *bo;
+    const uint16_t *ln2_g, *ln2_b, *wqc, *bqc, *wkc, *wvc, *bvc, *woc, *boc;
+    const uint16_t *ln3_g, *ln3_b, *w1, *b1, *w2, *b2;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// K chunking of the GEMMs: a function of K only (see k_gemm.hip).
+void gemm_chunks(int K, int &ck, int &S) {
+    const int ks = K / 32;
+    ck = (ks % 8 == 0 && ks >= 80) ? 8 : (ks % 4 == 0 ? 4 : 2);
+    S = ks / ck;
+}
+
+// Frames per cross-attention chunk: enough waves to cover the GPU when the
+// batch is small, one chunk per (request, head) when it is large. Depends on
+// the number of requests only, never on the block length.
+void cross_chunks(int n, int H, int F, int &cf, int &nch) {
+    const int steps = cdiv(F, 32);
+    int want = cdiv(1024, n * H);
+    want = want < 1 ? 1 : (want > 16 ? 16 : want);
+    const int per = cdiv(steps, want);
+    cf = per * 32;
+    nch = cdiv(F, cf);
+}
+
+struct Layout {
+    size_t x, xs, hs, q, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
+    size_t total;
+    size_t part_bytes, xapart_bytes;
+    int n_vtiles;
+};
+
+bool config_ok(const wf_config *c, std::string *why) {
+    auto bad = [&](const char *m) { if (why) *why = m; return false; };
+    if (!c) return bad("null config");
+    if (c->n_layers < 1) return bad("n_layers < 1");
+    if (c->head_dim != 16 && c->head_dim != 64) return bad("head_dim must be 16 or 64");
+    if (c->n_heads < 1 || c->d_model != c->n_heads * c->head_dim) return bad("d_model != n_heads*head_dim");
+    if (c->d_model % 64) return bad("d_model must be a multiple of 64");
+    if (c->d_ffn < 64 || c->d_ffn % 64) return bad("d_ffn must be a positive multiple of 64");
+    if (c->vocab < 2) return bad("vocab < 2");
+    if (c->n_frames < 1) return bad("n_frames < 1");
+    if (c->n_ctx < 32 || c->n_ctx % 32) return bad("n_ctx must be a positive multiple of 32");
+    if (c->page_size != 16) return bad("page_size must be 16");
+    if (c->max_batch < 1 || c->max_rows < 1) return bad("max_batch and max_rows must be >= 1");
+    if (c->n_pages < 1) return bad("n_pages < 1");
+    if (c->eos_id < 0 || c->eos_id >= c->vocab) return bad("eos_id outside the vocabulary");
+    if (!(c->ln_eps > 0.f)) return bad("ln_eps must be > 0");
+    return true;
+}
+
+Layout layout_of(const wf_config *c) {
+    Layout L{};
+    const size_t M = (size_t)c->max_rows, d = c->d_model, f = c->d_ffn;
+    const int H = c->n_heads, hd = c->head_dim;
+    L.n_vtiles = cdiv(c->vocab, 64);
+    // split-K partials: only for M <= 64
+    size_t part = 0;
+    const int KN[4][2] = {{(int)d, 3 * (int)d}, {(int)d, (int)d}, {(int)d, (int)f}, {(int)f, (int)d}};
+    for (auto &kn : KN) {
+        int ck, S;
+        gemm_chunks(kn[0], ck, S);
+        part = std::max(part, (size_t)S * 64 * kn[1] * 4);
+    }
+    L.part_bytes = part;
+    size_t xap = 0;
+    for (int n = 1; n <= c->max_batch; ++n) {
+        int cf, nch;
+        cross_chunks(n, H, c->n_frames, cf, nch);
+        if (nch > 1) xap = std::max(xap, (size_t)n * H * nch * 16 * (hd + 2) * 4);
+    }
+    xap = std::max(xap, (size_t)8 << 20);
+    L.xapart_bytes = xap;
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
+    L.x = take(M * d * 4);
+    L.xs = take(M * 2 * d * 2);
+    L.hs = take(M * 2 * f * 2);
+    L.q = take(M * d * 2);
+    L.part = take(part);
+    L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 64) * 4 + 64);
+    L.xapart = take(xap);
+    L.xacnt = take((size_t)c->max_batch * H * (c->n_ctx / 16 + 1) * 4);
+    L.lmmax = take((size_t)L.n_vtiles * M * 4);
+    L.lmidx = take((size_t)L.n_vtiles * M * 4);
+    L.reqL = take((size_t)c->max_batch * 4);
+    L.reqN = take((size_t)c->max_batch * 4);
+    L.len = take((size_t)c->max_batch * 4);
+    L.pend = take((size_t)c->max_batch * 4);
+    L.err = take((size_t)c->max_batch * 4);
+    L.total = o;
+    return L;
+}
+
+int f_pad_of(const wf_config *c) { return cdiv(c->n_frames, 32) * 32; }
+
+enum TimingKind { TK_GEMM = 0, TK_LMHEAD = 1, TK_SELF = 2, TK_CROSS = 3, TK_OTHER = 4, TK_N = 5 };
+
+}  // namespace
+
+struct wf_engine {
+    wf_config c;
+    Layout lay;
+    int F_pad, pt_stride, page_elems;
+    const uint16_t *tok_emb, *pos_emb, *lnf_g, *lnf_b;
+    std::vector<LayerW> layers;
+    uint16_t *kv, *xkv;
+    size_t kv_layer_elems, xkv_slot_elems, xkv_layer_elems;
+    const int32_t *pt;
+    char *ws;
+    float *x;
+    uint16_t *xs, *hs, *q;
+    float *part;
+    int32_t *gcnt;
+    float *xapart;
+    int32_t *xacnt;
+    float *lmmax;
+    int32_t *lmidx;
+    int32_t *reqL, *reqN, *len, *pend, *err;
+    // optional per-kernel timing with HIP events
+    bool timing = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> spans[TK_N];
+};
+
+namespace {
+
+hipEvent_t next_event(wf_engine *e) {
+    if (e->ev_used == e->ev_pool.size()) {
+        hipEvent_t ev;
+        if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+        e->ev_pool.push_back(ev);
+    }
+    return e->ev_pool[e->ev_used++];
+}
+
+// Launch wrapper that optionally brackets the launch with events.
+template <typename F>
+wf_status timed(wf_engine *e, int kind, hipStream_t st, F &&launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (e->timing) {
+        a = next_event(e);
+        b = next_event(e);
+        if (a) (void)hipEventRecord(a, st);
+    }
+    hipError_t err = launch();
+    if (err != hipSuccess) return fail(WF_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    if (e->timing && a && b) {
+        (void)hipEventRecord(b, st);
+        e->spans[kind].push_back({a, b});
+    }
+    return WF_OK;
+}
+
+wf_status run_gemm(wf_engine *e, int epi, const uint16_t *X, bool xsplit, int M, int K,
+                   const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n, int N,
+                   const EpiArgs &ea, hipStream_t st) {
+    GemmArgs a{};
+    a.X = X;
+    a.W0 = W0;
+    a.W1 = W1 ? W1 : W0;
+    a.W2 = W2 ? W2 : W0;
+    a.M = M;
+    a.K = K;
+    a.N = N;
+    a.seg_n = seg_n;
+    int ck, S;
+    gemm_chunks(K, ck, S);
+    a.S = S;
+    a.n_tiles = cdiv(N, 64);
+    a.split = (epi != EPI_ARGMAX && epi != EPI_XKV && M <= 64 && S > 1) ? 1 : 0;
+    if (a.split) {
+        a.m_blocks = 1;
+        a.n_groups = S;
+        if ((size_t)S * M * N * 4 > e->lay.part_bytes)
+            return fail(WF_ECAPACITY, "split-K scratch too small");
+    } else {
+        a.m_blocks = cdiv(M, 64);
+        a.n_groups = 1;
+    }
+    a.n_wg = a.n_tiles * a.m_blocks * a.n_groups;
+    a.part = e->part;
+    a.cnt = e->gcnt;
+    a.e = ea;
+    const int kind = epi == EPI_ARGMAX ? TK_LMHEAD : TK_GEMM;
+    return timed(e, kind, st, [&] { return launch_gemm(epi, a, ck, xsplit, st); });
+}
+
+wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
+    LnArgs a{e->x, M, e->c.d_model, g, b, e->c.ln_eps, e->xs};
+    return timed(e, TK_OTHER, st, [&] { return launch_layernorm(a, st); });
+}
+
+#define WF_TRY(expr)                      \
+    do {                                  \
+        wf_status _s = (expr);            \
+        if (_s != WF_OK) return _s;       \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t wf_kv_pool_bytes(const wf_config *c) {
+    if (!config_ok(c, nullptr)) return 0;
+    return (size_t)c->n_layers * c->n_pages * 2 * c->n_heads * c->page_size * c->head_dim * 2;
+}
+
+size_t wf_xkv_pool_bytes(const wf_config *c) {
+    if (!config_ok(c, nullptr)) return 0;
+    return (size_t)c->max_batch * c->n_layers * 2 * c->n_heads * f_pad_of(c) * c->head_dim * 2;
+}
+
+size_t wf_workspace_bytes(const wf_config *c) {
+    if (!config_ok(c, nullptr)) return 0;
+    return layout_of(c).total;
+}
+
+const char *wf_last_error(void) { return g_err; }
+
+wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, size_t kv_bytes,
+                    void *xkv_pool, size_t xkv_bytes, const int32_t *d_page_table,
+                    void *workspace, size_t ws_bytes, wf_engine **out) {
+    if (!out) return fail(WF_EINVAL, "out is null");
+    *out = nullptr;
+    std::string why;
+    if (!config_ok(cfg, &why)) return fail(WF_ESHAPE, "bad config: %s", why.c_str());
+    if (!w || !w->tok_emb || !w->pos_emb || !w->lnf_g || !w->lnf_b || !w->layers)
+        return fail(WF_EINVAL, "null weight pointer");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const wf_layer_weights &L = w->layers[l];
+        const void *ps[] = {L.ln1_g, L.ln1_b, L.wq, L.bq, L.wk, L.wv, L.bv, L.wo, L.bo,
+                            L.ln2_g, L.ln2_b, L.wqc, L.bqc, L.wkc, L.wvc, L.bvc, L.woc, L.boc,
+                            L.ln3_g, L.ln3_b, L.w1, L.b1, L.w2, L.b2};
+        for (const void *p : ps)
+            if (!p) return fail(WF_EINVAL, "null weight pointer in layer %d", l);
+    }
+    if (!kv_pool || !xkv_pool || !d_page_table || !workspace)
+        return fail(WF_EINVAL, "null pool, page table or workspace");
+    if (kv_bytes < wf_kv_pool_bytes(cfg)) return fail(WF_ECAPACITY, "kv_pool too small");
+    if (xkv_bytes < wf_xkv_pool_bytes(cfg)) return fail(WF_ECAPACITY, "xkv_pool too small");
+    if (ws_bytes < wf_workspace_bytes(cfg)) return fail(WF_ECAPACITY, "workspace too small");
+
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return fail(WF_EDEVICE, "no HIP device");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return fail(WF_EDEVICE, "device is %s, not gfx950", prop.gcnArchName);
+
+    wf_engine *e = new wf_engine();
+    e->c = *cfg;
+    e->lay = layout_of(cfg);
+    e->F_pad = f_pad_of(cfg);
+    e->pt_stride = cfg->n_ctx / cfg->page_size;
+    e->page_elems = 2 * cfg->n_heads * cfg->page_size * cfg->head_dim;
+    e->tok_emb = (const uint16_t *)w->tok_emb;
+    e->pos_emb = (const uint16_t *)w->pos_emb;
+    e->lnf_g = (const uint16_t *)w->lnf_g;
+    e->lnf_b = (const uint16_t *)w->lnf_b;
+    e->layers.resize(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const wf_layer_weights &s = w->layers[l];
+        LayerW &t = e->layers[l];
+        t = LayerW{(const uint16_t *)s.ln1_g, (const uint16_t *)s.ln1_b, (const uint16_t *)s.wq,
+                   (const uint16_t *)s.bq,    (const uint16_t *)s.wk,    (const uint16_t *)s.wv,
+                   (const uint16_t *)s.bv,    (const uint16_t *)s.wo,    (const uint16_t *)s.bo,
+                   (const uint16_t *)s.ln2_g, (const uint16_t *)s.ln2_b, (const uint16_t *)s.wqc,
+                   (const uint16_t *)s.bqc,   (const uint16_t *)s.wkc,   (const uint16_t *)s.wvc,
+                   (const uint16_t *)s.bvc,   (const uint16_t *)s.woc,   (const uint16_t *)s.boc,
+                   (const uint16_t *)s.ln3_g, (const uint16_t *)s.ln3_b, (const uint16_t *)s.w1,
+                   (const uint16_t *)s.b1,    (const uint16_t *)s.w2,    (const uint16_t *)s.b2};
+    }
+    e->kv = (uint16_t *)kv_pool;
+    e->xkv = (uint16_t *)xkv_pool;
+    e->kv_layer_elems = (size_t)cfg->n_pages * e->page_elems;
+    e->xkv_layer_elems = (size_t)2 * cfg->n_heads * e->F_pad * cfg->head_dim;
+    e->xkv_slot_elems = (size_t)cfg->n_layers * e->xkv_layer_elems;
+    e->pt = d_page_table;
+    char *ws = (char *)workspace;
+    const Layout &L = e->lay;
+    e->ws = ws;
+    e->x = (float *)(ws + L.x);
+    e->xs = (uint16_t *)(ws + L.xs);
+    e->hs = (uint16_t *)(ws + L.hs);
+    e->q = (uint16_t *)(ws + L.q);
+    e->part = (float *)(ws + L.part);
+    e->gcnt = (int32_t *)(ws + L.gcnt);
+    e->xapart = (float *)(ws + L.xapart);
+    e->xacnt = (int32_t *)(ws + L.xacnt);
+    e->lmmax = (float *)(ws + L.lmmax);
+    e->lmidx = (int32_t *)(ws + L.lmidx);
+    e->reqL = (int32_t *)(ws + L.reqL);
+    e->reqN = (int32_t *)(ws + L.reqN);
+    e->len = (int32_t *)(ws + L.len);
+    e->pend = (int32_t *)(ws + L.pend);
+    e->err = (int32_t *)(ws + L.err);
+    if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
+        delete e;
+        return fail(WF_EHIP, "clearing the workspace failed");
+    }
+    *out = e;
+    return WF_OK;
+}
+
+void wf_destroy(wf_engine *e) {
+    if (!e) return;
+    for (hipEvent_t ev : e->ev_pool) hipEventDestroy(ev);
+    delete e;
+}
+
+wf_status wf_reset(wf_engine *e, int32_t n, const int32_t *d_slots, void *stream) {
+    if (!e || !d_slots) return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st,
+                 [&] {
+                     return launch_reset(n, e->c.max_batch, d_slots, e->len, e->pend, e->err, st);
+                 });
+}
+
+wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const void *d_enc,
+                       void *stream) {
+    if (!e || !d_slots || !d_enc) return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    const wf_config &c = e->c;
+    const long long M = (long long)n * c.n_frames;
+    if (M > 0x7fffffffLL / 2) return fail(WF_ECAPACITY, "too many frames");
+    hipStream_t st = (hipStream_t)stream;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const LayerW &w = e->layers[l];
+        EpiArgs ea{};
+        ea.b0 = nullptr;
+        ea.b1 = w.bvc;
+        ea.xkv = e->xkv;
+        ea.xkv_slot_stride = (int64_t)e->xkv_slot_elems;
+        ea.xkv_layer_off = (int64_t)l * e->xkv_layer_elems;
+        ea.F = c.n_frames;
+        ea.F_pad = e->F_pad;
+        ea.slots = d_slots;
+        ea.H = c.n_heads;
+        ea.hd = c.head_dim;
+        ea.max_batch = c.max_batch;
+        WF_TRY(run_gemm(e, EPI_XKV, (const uint16_t *)d_enc, false, (int)M, c.d_model, w.wkc,
+                        w.wvc, nullptr, c.d_model, 2 * c.d_model, ea, st));
+    }
+    return WF_OK;
+}
+
+wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
+                          const int32_t *d_tokens, int32_t T, const int32_t *d_n_tok,
+                          int32_t *d_argmax, float *d_logits, void *stream) {
+    if (!e || !d_slots || !d_tokens || !d_n_tok || !d_argmax)
+        return fail(WF_EINVAL, "null argument");
+    const wf_config &c = e->c;
+    if (n < 1 || n > c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    if (T < 1 || T > c.n_ctx) return fail(WF_EINVAL, "T outside [1, n_ctx]");
+    if ((long long)n * T > c.max_rows) return fail(WF_ECAPACITY, "n*T exceeds max_rows");
+    hipStream_t st = (hipStream_t)stream;
+    const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
+    const int mt = cdiv(T, 16);
+
+    PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
+                   d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
+    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_prepare(pa, st); }));
+    EmbedArgs ema{M, T, d, c.vocab, c.n_ctx, d_tokens, e->reqL, e->tok_emb, e->pos_emb, e->x};
+    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_embed(ema, st); }));
+
+    int cf, nch;
+    cross_chunks(n, H, c.n_frames, cf, nch);
+    const size_t rowbytes = (size_t)16 * (hd + 2) * 4;
+    if (nch > 1 && (size_t)n * H * mt * nch * rowbytes > e->lay.xapart_bytes) {
+        // long prefill blocks: fewer, longer chunks so the partials fit
+        const size_t fit = e->lay.xapart_bytes / ((size_t)n * H * mt * rowbytes);
+        const int steps = cdiv(c.n_frames, 32);
+        const int want = fit < 1 ? 1 : (int)fit;
+        cf = cdiv(steps, want) * 32;
+        nch = cdiv(c.n_frames, cf);
+    }
+
+    for (int l = 0; l < c.n_layers; ++l) {
+        const LayerW &w = e->layers[l];
+        uint16_t *kvl = e->kv + (size_t)l * e->kv_layer_elems;
+        // self-attention sublayer
+        WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
+        EpiArgs qa{};
+        qa.b0 = w.bq;
+        qa.b2 = w.bv;
+        qa.out = e->q;
+        qa.kv_layer = kvl;
+        qa.page_table = e->pt;
+        qa.pt_stride = e->pt_stride;
+        qa.slots = d_slots;
+        qa.req_L = e->reqL;
+        qa.req_ntok = e->reqN;
+        qa.T = T;
+        qa.H = H;
+        qa.hd = hd;
+        qa.page_elems = e->page_elems;
+        WF_TRY(run_gemm(e, EPI_QKV, e->xs, true, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
+        SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
+                        e->page_elems, n, T, H, d, 1.0f / std::sqrt((float)hd), e->xs};
+        WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, mt, st); }));
+        EpiArgs ra{};
+        ra.b0 = w.bo;
+        ra.x = e->x;
+        WF_TRY(run_gemm(e, EPI_RESID, e->xs, true, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
+        // cross-attention sublayer
+        WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
+        EpiArgs fa{};
+        fa.b0 = w.bqc;
+        fa.out = e->q;
+        WF_TRY(run_gemm(e, EPI_F16, e->xs, true, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
+        CrossAttnArgs ca{};
+        ca.q = e->q;
+        ca.xkv = e->xkv;
+        ca.slot_stride = (int64_t)e->xkv_slot_elems;
+        ca.layer_off = (int64_t)l * e->xkv_layer_elems;
+        ca.slots = d_slots;
+        ca.req_ntok = e->reqN;
+        ca.n = n;
+        ca.T = T;
+        ca.H = H;
+        ca.d = d;
+        ca.F = c.n_frames;
+        ca.F_pad = e->F_pad;
+        ca.mt = mt;
+        ca.nch = nch;
+        ca.cf = cf;
+        ca.n_items = n * H * mt * nch;
+        ca.scale = 1.0f / std::sqrt((float)hd);
+        ca.part = e->xapart;
+        ca.cnt = e->xacnt;
+        ca.out = e->xs;
+        WF_TRY(timed(e, TK_CROSS, st, [&] { return launch_cross_attn(ca, hd, st); }));
+        EpiArgs oa{};
+        oa.b0 = w.boc;
+        oa.x = e->x;
+        WF_TRY(run_gemm(e, EPI_RESID, e->xs, true, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
+        // MLP sublayer
+        WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
+        EpiArgs ga{};
+        ga.b0 = w.b1;
+        ga.out = e->hs;
+        WF_TRY(run_gemm(e, EPI_GELU, e->xs, true, M, d, w.w1, nullptr, nullptr, c.d_ffn,
+                        c.d_ffn, ga, st));
+        EpiArgs f2{};
+        f2.b0 = w.b2;
+        f2.x = e->x;
+        WF_TRY(run_gemm(e, EPI_RESID, e->hs, true, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
+                        st));
+    }
+    WF_TRY(run_ln(e, M, e->lnf_g, e->lnf_b, st));
+    EpiArgs la{};
+    la.logits = d_logits;
+    la.tile_max = e->lmmax;
+    la.tile_idx = e->lmidx;
+    la.ld = c.max_rows;
+    WF_TRY(run_gemm(e, EPI_ARGMAX, e->xs, true, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
+                    c.vocab, la, st));
+    LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, M, T, d_slots, e->reqN,
+                    e->err, d_argmax};
+    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_lm_reduce(lr, st); }));
+    return WF_OK;
+}
+
+wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
+                    const int32_t *d_n_tok, const int32_t *d_budget, const int32_t *d_argmax,
+                    const float *d_logits, const float *d_q, const uint8_t *d_suppress,
+                    float temperature, uint64_t seed, const int32_t *d_request_id,
+                    const int32_t *d_step, int32_t *d_n_acc, int32_t *d_next_token,
+                    int32_t *d_n_emit, int32_t *d_done, void *stream) {
+    if (!e || !d_tokens || !d_n_tok || !d_budget || !d_n_acc || !d_next_token || !d_n_emit ||
+        !d_done)
+        return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    if (T < 1 || T > e->c.n_ctx) return fail(WF_EINVAL, "T outside [1, n_ctx]");
+    if (!(temperature >= 0.f) || std::isinf(temperature))
+        return fail(WF_EINVAL, "temperature must be finite and >= 0");
+    if (temperature == 0.f && !d_argmax) return fail(WF_EINVAL, "greedy accept needs d_argmax");
+    if (temperature > 0.f) {
+        if (!d_logits || !d_q || !d_request_id || !d_step)
+            return fail(WF_EINVAL, "sampling needs logits, q, request ids and steps");
+        return fail(WF_EINVAL, "temperature sampling is not built in this library");
+    }
+    AcceptArgs a{};
+    a.n = n;
+    a.T = T;
+    a.V = e->c.vocab;
+    a.eos = e->c.eos_id;
+    a.tokens = d_tokens;
+    a.n_tok = d_n_tok;
+    a.budget = d_budget;
+    a.argmax = d_argmax;
+    a.n_acc = d_n_acc;
+    a.next_token = d_next_token;
+    a.n_emit = d_n_emit;
+    a.done = d_done;
+    a.logits = d_logits;
+    a.q = d_q;
+    a.suppress = d_suppress;
+    a.temperature = temperature;
+    a.seed = seed;
+    a.request_id = d_request_id;
+    a.step = d_step;
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_accept(a, st); });
+}
+
+wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_n_acc,
+                      void *stream) {
+    if (!e || !d_slots || !d_n_acc) return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    RollbackArgs a{n, e->c.max_batch, d_slots, d_n_acc, e->len, e->pend, e->err};
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_rollback(a, st); });
+}
+
+wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *stream) {
+    if (!e) return fail(WF_EINVAL, "null engine");
+    hipStream_t st = (hipStream_t)stream;
+    if (hipStreamSynchronize(st) != hipSuccess) return fail(WF_EHIP, "stream synchronize failed");
+    const size_t bytes = (size_t)e->c.max_batch * 4;
+    if (h_err && hipMemcpy(h_err, e->err, bytes, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(WF_EHIP, "copy of error words failed");
+    if (h_len && hipMemcpy(h_len, e->len, bytes, hipMemcpyDeviceToHost) != hipSuccess)
+        return fail(WF_EHIP, "copy of lengths failed");
+    return WF_OK;
+}
+
+wf_status wf_set_timing(wf_engine *e, int32_t enable) {
+    if (!e) return fail(WF_EINVAL, "null engine");
+    e->timing = enable != 0;
+    for (auto &v : e->spans) v.clear();
+    e->ev_used = 0;
+    return WF_OK;
+}
+
+wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count) {
+    if (!e || !total_ms || !count) return fail(WF_EINVAL, "null argument");
+    if (kind < 0 || kind >= TK_N) return fail(WF_EINVAL, "unknown timing kind");
+    double tot = 0;
+    for (auto &p : e->spans[kind]) {
+        if (hipEventSynchronize(p.second) != hipSuccess)
+            return fail(WF_EHIP, "event synchronize failed");
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess)
+            return fail(WF_EHIP, "elapsed time failed");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *count = (int32_t)e->spans[kind].size();
+    return WF_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,98 @@
+// Device helpers for the gfx950 kernels: vector types, MFMA wrappers,
+// bf16/fp16 conversions and wavefront reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define WF_WAVE 64
+
+// 16 bytes from global memory as one vector load.
+__device__ __forceinline__ u32x4 ld16(const void *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+__device__ __forceinline__ u32x2 ld8(const void *p) {
+    return *reinterpret_cast<const u32x2 *>(p);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16_k16(u32x2 a, u32x2 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, a),
+                                                  __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
+}
+
+// bf16 <-> fp32. Rounding to bf16 is to nearest, ties to even.
+__device__ __forceinline__ float bf2f(uint16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ uint16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;  // NaN stays NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+// Split x into hi + lo, both bf16: hi = bf16(x), lo = bf16(x - hi).
+__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
+    hi = f2bf(x);
+    lo = f2bf(x - bf2f(hi));
+}
+__device__ __forceinline__ uint16_t f2h_bits(float f) {
+    _Float16 h = (_Float16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float h2f_bits(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Reductions within groups of 16 lanes (lanes 16g .. 16g+15), fixed tree.
+__device__ __forceinline__ float max16(float v) {
+    v = fmaxf(v, __shfl_xor(v, 1));
+    v = fmaxf(v, __shfl_xor(v, 2));
+    v = fmaxf(v, __shfl_xor(v, 4));
+    v = fmaxf(v, __shfl_xor(v, 8));
+    return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+    v += __shfl_xor(v, 1);
+    v += __shfl_xor(v, 2);
+    v += __shfl_xor(v, 4);
+    v += __shfl_xor(v, 8);
+    return v;
+}
+// Whole-wave reductions, fixed tree.
+__device__ __forceinline__ float wave_sum(float v) {
+    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+// (value, index) argmax: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ void argmax_merge(float &v, int &i, float v2, int i2) {
+    if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
+}
+__device__ __forceinline__ void wave_argmax(float &v, int &i) {
+    for (int o = 1; o < 64; o <<= 1) {
+        float v2 = __shfl_xor(v, o);
+        int i2 = __shfl_xor(i, o);
+        argmax_merge(v, i, v2, i2);
+    }
+}
+
+// Agent-scope fences around the last-arriver handoff between workgroups.
+__device__ __forceinline__ void fence_release() { __threadfence(); }
+__device__ __forceinline__ void fence_acquire() { __threadfence(); }

@@ -1,0 +1,140 @@
+// Kernel argument blocks and launch functions shared by the kernel files and
+// the engine. Everything here is internal to libwf.so.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace wf {
+
+// GEMM epilogues: what happens to C[m][n] = sum_k X[m][k] W[n][k].
+enum Epi : int {
+    EPI_QKV = 0,    // q -> fp16 buffer; k, v -> the slot's KV pages (valid rows)
+    EPI_RESID = 1,  // x[m][n] += C + b[n]            (fp32 residual stream)
+    EPI_F16 = 2,    // out[m][n] = fp16(C + b[n])      (cross-attention query)
+    EPI_GELU = 3,   // out = split-bf16(GELU(C + b))   (MLP hidden)
+    EPI_ARGMAX = 4, // tied LM head: per 64-column tile (max, lowest argmax), logits
+    EPI_XKV = 5,    // cross K/V of one layer into the write-once pool
+};
+
+struct EpiArgs {
+    const uint16_t *b0, *b1, *b2;  // bias per weight segment (bf16), may be null
+    float *x;                      // EPI_RESID
+    uint16_t *out;                 // EPI_F16 / EPI_QKV (q) fp16 [M][N or d]; EPI_GELU split
+    // EPI_QKV: KV append
+    uint16_t *kv_layer;            // this layer's first page
+    const int32_t *page_table;
+    int32_t pt_stride;
+    const int32_t *slots, *req_L, *req_ntok;
+    int32_t T, H, hd, page_elems;
+    // EPI_XKV
+    uint16_t *xkv;
+    int64_t xkv_slot_stride, xkv_layer_off;
+    int32_t F, F_pad;
+    int32_t max_batch;             // slot ids outside [0, max_batch) are skipped
+    // EPI_ARGMAX
+    float *logits;                 // null or [M][V]
+    float *tile_max;               // [n_tiles][ld]
+    int32_t *tile_idx;
+    int32_t ld;
+};
+
+struct GemmArgs {
+    const uint16_t *X;             // split-bf16 [M][K/8][hi 8 | lo 8], or plain bf16 [M][K]
+    const uint16_t *W0, *W1, *W2;  // weight segments, each [seg_n][K] bf16
+    int32_t M, K, N, seg_n;
+    int32_t S;                     // number of K chunks (fixed per K)
+    int32_t split;                 // 1: one chunk per workgroup, last arriver reduces
+    int32_t n_tiles, m_blocks, n_groups;  // logical grid; n_groups = chunks (split) or 1
+    int32_t n_wg;                  // logical workgroups (grid is padded to 8k)
+    float *part;                   // split partials [S][M][N]
+    int32_t *cnt;                  // split arrival counters [n_tiles]
+    EpiArgs e;
+};
+
+struct PrepareArgs {
+    int32_t n, T, V, n_ctx, n_pages, pt_stride, page_size, max_batch;
+    const int32_t *slots, *tokens, *n_tok, *page_table;
+    int32_t *slot_len, *slot_pending, *slot_err;
+    int32_t *req_L, *req_ntok;
+};
+
+struct EmbedArgs {
+    int32_t M, T, d, V, n_ctx;
+    const int32_t *tokens, *req_L;
+    const uint16_t *tok_emb, *pos_emb;
+    float *x;
+};
+
+struct LnArgs {
+    const float *x;
+    int32_t M, d;
+    const uint16_t *g, *b;
+    float eps;
+    uint16_t *out;                 // split-bf16 [M][d/8][16]
+};
+
+struct SelfAttnArgs {
+    const uint16_t *q;             // fp16 [M][d]
+    const uint16_t *kv_layer;      // this layer's page base
+    const int32_t *page_table, *slots, *req_L, *req_ntok;
+    int32_t pt_stride, page_elems;
+    int32_t n, T, H, d;
+    float scale;
+    uint16_t *out;                 // split-bf16 [M][d]
+};
+
+struct CrossAttnArgs {
+    const uint16_t *q;             // fp16 [M][d]
+    const uint16_t *xkv;           // pool base
+    int64_t slot_stride, layer_off;
+    const int32_t *slots, *req_ntok;
+    int32_t n, T, H, d, F, F_pad;
+    int32_t mt, nch, cf;           // m-tiles per request, chunks, frames per chunk
+    int32_t n_items;
+    float scale;
+    float *part;                   // [item][16][hd+2]
+    int32_t *cnt;                  // [n*H*mt]
+    uint16_t *out;                 // split-bf16 [M][d]
+};
+
+struct LmReduceArgs {
+    const float *tile_max;
+    const int32_t *tile_idx;
+    int32_t n_tiles, ld, M, T;
+    const int32_t *slots, *req_ntok;
+    int32_t *slot_err;
+    int32_t *argmax;
+};
+
+struct AcceptArgs {
+    int32_t n, T, V, eos;
+    const int32_t *tokens, *n_tok, *budget, *argmax;
+    int32_t *n_acc, *next_token, *n_emit, *done;
+    // sampling (temperature > 0)
+    const float *logits, *q;
+    const uint8_t *suppress;
+    float temperature;
+    uint64_t seed;
+    const int32_t *request_id, *step;
+};
+
+struct RollbackArgs {
+    int32_t n, max_batch;
+    const int32_t *slots, *n_acc;
+    int32_t *slot_len, *slot_pending, *slot_err;
+};
+
+hipError_t launch_gemm(int epi, const GemmArgs &a, int ck, bool xsplit, hipStream_t st);
+hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
+hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
+hipError_t launch_layernorm(const LnArgs &a, hipStream_t st);
+hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t st);
+hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st);
+hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st);
+hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
+hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st);
+hipError_t launch_reset(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,
+                        int32_t *pending, int32_t *err, hipStream_t st);
+
+}  // namespace wf

@@ -1,0 +1,346 @@
+"""GPU parity of the verify path through the C ABI against the CPU oracle.
+
+Covers: the tiny 2-layer model (several tiles, ragged tails, head_dim 16),
+the full 32-layer large-v3 shape at batch 1 with a 64-token prefix and a
+block of K+1 = 9, the 4-layer turbo shape at batch 32 with ragged prefixes
+and a shuffled page table, row invariance (a row gives the same bits alone
+or inside a block; speculative = greedy on the GPU), and the device error
+words.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import (assert_argmax_where_clear, assert_logits_close, log,
+                        oracle_accept_pinned)
+from oracle import decode as od
+from oracle import model as om
+from synthetic import (LARGE_V3, TINY, TURBO, WORKLOADS, make_draft_table, make_encoder_out,
+                       make_prefixes, make_weights)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _engine(shape, wbits, max_batch, max_rows, page_table=None):
+    from speculative_decoding_encoder_amd.binding import Engine
+    return Engine(shape, wbits, max_batch=max_batch, max_rows=max_rows, page_table=page_table)
+
+
+def _verify(eng, slots, tokens, n_tok, logits=True):
+    torch = eng.torch
+    tokens = np.asarray(tokens, np.int32)
+    n, T = tokens.shape
+    am = torch.empty((n, T), dtype=torch.int32, device=eng.dev)
+    lg = torch.empty((n, T, eng.shape.vocab), dtype=torch.float32, device=eng.dev) if logits else None
+    eng.wf_verify_block(eng.i32(slots), eng.i32(tokens), eng.i32(n_tok), am, lg)
+    torch.cuda.synchronize()
+    return am.cpu().numpy(), (lg.cpu().numpy() if logits else None)
+
+
+# --------------------------------------------------------------------------
+# tiny model
+@pytest.fixture(scope="module", params=["ln_identity", "ln_random"])
+def tiny(request, torch_cuda):
+    wl = WORKLOADS[0]
+    wbits = make_weights(TINY, wl.cfg_id, ln_random=request.param == "ln_random")
+    enc = make_encoder_out(TINY, wl.cfg_id, 0)
+    prefix = make_prefixes(wl)[0]
+    m = om.Model(TINY, wbits)
+    greedy = od.greedy_decode(m, enc, prefix, wl.n_max, TINY.eos_id)
+    eng = _engine(TINY, wbits, max_batch=4, max_rows=512)
+    eng.wf_encode_kv(eng.i32([0]), eng.bf16(enc[None]))
+    return dict(wl=wl, wbits=wbits, enc=enc, prefix=prefix, model=m, greedy=greedy, eng=eng)
+
+
+def test_tiny_teacher_forced_sequence(tiny):
+    """Prefix + the oracle's 32 greedy tokens as one block of 36 rows."""
+    eng, m = tiny["eng"], tiny["model"]
+    seq = np.concatenate([tiny["prefix"], tiny["greedy"]]).astype(np.int32)
+    eng.wf_reset(eng.i32([0]))
+    am, lg = _verify(eng, [0], seq[None], [len(seq)])
+    ref = m.rows(m.new_request(tiny["enc"]), seq, 0)
+    err = assert_logits_close(lg[0], ref, what="tiny teacher-forced")
+    clear, tot = assert_argmax_where_clear(am[0], ref, what="tiny teacher-forced")
+    log(f"tiny teacher-forced: max err {err:.2e}, argmax pinned at {clear}/{tot} rows")
+    eng.wf_rollback(eng.i32([0]), eng.i32([len(seq) - 1]))
+    err_w, ln = eng.wf_device_state()
+    assert err_w[0] == 0 and ln[0] == len(seq)
+
+
+def test_tiny_block_after_prefill(tiny):
+    eng, m, wl = tiny["eng"], tiny["model"], tiny["wl"]
+    prefix, greedy = tiny["prefix"], tiny["greedy"]
+    P = len(prefix)
+    eng.wf_reset(eng.i32([0]))
+    am, lg = _verify(eng, [0], prefix[None], [P])
+    req = m.new_request(tiny["enc"])
+    ref = m.rows(req, prefix, 0)
+    assert_logits_close(lg[0], ref, what="tiny prefill")
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    keep, repl = make_draft_table(wl, 0)
+    drafts = od.table_drafts(greedy, P, keep, repl)(P, greedy[0], 4)
+    block = np.array([greedy[0]] + drafts, np.int32)
+    am, lg = _verify(eng, [0], block[None], [5])
+    refb = m.rows(req, block, P)
+    assert_logits_close(lg[0], refb, what="tiny block")
+    assert_argmax_where_clear(am[0], refb, what="tiny block")
+
+
+def test_tiny_block_rows_equal_single_rows_bitwise(tiny):
+    """Row invariance: a block of 5 at L equals 5 one-row passes at L..L+4."""
+    eng = tiny["eng"]
+    prefix, greedy = tiny["prefix"], tiny["greedy"]
+    P = len(prefix)
+    block = np.array(greedy[:5], np.int32)
+    eng.wf_reset(eng.i32([0]))
+    _verify(eng, [0], prefix[None], [P], logits=False)
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    _, lg_block = _verify(eng, [0], block[None], [5])
+    eng.wf_reset(eng.i32([0]))
+    _verify(eng, [0], prefix[None], [P], logits=False)
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    rows = []
+    for i in range(5):
+        _, lg = _verify(eng, [0], block[i:i + 1][None], [1])
+        eng.wf_rollback(eng.i32([0]), eng.i32([0]))
+        rows.append(lg[0, 0])
+    assert np.array_equal(np.stack(rows).view(np.uint32), lg_block[0].view(np.uint32))
+
+
+def test_tiny_speculative_equals_greedy_on_gpu(tiny):
+    from speculative_decoding_encoder_amd.harness import run_loop, table_drafter
+    eng, wl = tiny["eng"], tiny["wl"]
+    prefix = tiny["prefix"]
+    eng.wf_reset(eng.i32([0]))
+    g = run_loop(eng, [0], [prefix], wl.n_max, 0, None, TINY.eos_id)
+    gpu_greedy = g.tokens[0]
+    assert len(gpu_greedy) == wl.n_max
+    for p_keep in (0.7, 1.0, 0.0):
+        eng.wf_reset(eng.i32([0]))
+        fn = table_drafter([gpu_greedy], [len(prefix)], [make_draft_table(wl, 0, p_keep)])
+        s = run_loop(eng, [0], [prefix], wl.n_max, wl.k_draft, fn, TINY.eos_id)
+        assert s.tokens[0] == gpu_greedy, p_keep
+        if p_keep == 1.0:
+            assert s.rounds < len(gpu_greedy) // 2
+    log(f"tiny: GPU speculative == GPU greedy over {len(gpu_greedy)} tokens")
+
+
+def test_tiny_oracle_steered_loop(tiny):
+    """Each round: the GPU's accepted length and next token must equal the
+    oracle's wherever the margins pin them; then both continue from the
+    oracle's outcome."""
+    from speculative_decoding_encoder_amd.harness import run_loop, table_drafter
+    eng, m, wl = tiny["eng"], tiny["model"], tiny["wl"]
+    prefix, greedy = tiny["prefix"], tiny["greedy"]
+    P = len(prefix)
+    req = m.new_request(tiny["enc"])
+    m.rows(req, prefix, 0)
+    fn = table_drafter([greedy], [P], [make_draft_table(wl, 0)])
+    stats = {"pinned": 0, "rounds": 0}
+
+    def steer(b, L, toks, k, am, a, c):
+        ref = m.rows(req, toks[:k + 1], L)
+        a_ref, c_ref, pinned = oracle_accept_pinned(list(toks[1:k + 1]), ref, k)
+        stats["rounds"] += 1
+        if pinned:
+            stats["pinned"] += 1
+            assert (a, c) == (a_ref, c_ref), (L, a, c, a_ref, c_ref)
+        return a_ref, c_ref
+
+    eng.wf_reset(eng.i32([0]))
+    res = run_loop(eng, [0], [prefix], wl.n_max, wl.k_draft, fn, TINY.eos_id, steer=steer)
+    assert res.tokens[0] == greedy
+    log(f"tiny steered: {stats['pinned']}/{stats['rounds']} rounds pinned by margin")
+
+
+def test_device_error_words(tiny):
+    from speculative_decoding_encoder_amd.binding import WFError
+    eng = tiny["eng"]
+    torch = eng.torch
+    V = TINY.vocab
+    eng.wf_reset(eng.i32([0, 1]))
+    # token out of range on slot 1 only; slot 0 proceeds
+    toks = np.array([[1, 2, 3], [4, V, 5]], np.int32)
+    _verify(eng, [0, 1], toks, [3, 3], logits=False)
+    err, ln = eng.wf_device_state()
+    assert err[0] == 0 and err[1] & 2
+    eng.wf_rollback(eng.i32([0, 1]), eng.i32([2, 0]))
+    err, ln = eng.wf_device_state()
+    assert ln[0] == 3 and ln[1] == 0
+    # verify twice without rollback
+    _verify(eng, [0], np.array([[1]], np.int32), [1], logits=False)
+    _verify(eng, [0], np.array([[1]], np.int32), [1], logits=False)
+    err, _ = eng.wf_device_state()
+    assert err[0] & 4
+    # rollback beyond the block
+    eng.wf_reset(eng.i32([0]))
+    _verify(eng, [0], np.array([[1, 2]], np.int32), [2], logits=False)
+    eng.wf_rollback(eng.i32([0]), eng.i32([2]))
+    err, _ = eng.wf_device_state()
+    assert err[0] & 8
+    # context overflow
+    eng.wf_reset(eng.i32([0]))
+    long = np.ones((1, TINY.n_ctx), np.int32)
+    _verify(eng, [0], long, [TINY.n_ctx], logits=False)
+    eng.wf_rollback(eng.i32([0]), eng.i32([TINY.n_ctx - 1]))
+    _verify(eng, [0], np.array([[1]], np.int32), [1], logits=False)
+    err, ln = eng.wf_device_state()
+    assert err[0] & 1 and ln[0] == TINY.n_ctx
+    # host-side checks
+    with pytest.raises(WFError):
+        eng.wf_verify_block(eng.i32([0]), eng.i32(np.zeros((1, TINY.n_ctx + 1))), eng.i32([1]),
+                            torch.empty((1, TINY.n_ctx + 1), dtype=torch.int32, device=eng.dev))
+    eng.wf_reset(eng.i32([0, 1]))
+    err, ln = eng.wf_device_state()
+    assert err[0] == 0 and err[1] == 0 and ln[0] == 0
+
+
+# --------------------------------------------------------------------------
+# full 32-layer shape, batch 1, prefix 64, one block of 9
+def test_large_v3_b1_prefix64_block9(torch_cuda):
+    wl = WORKLOADS[1]
+    log("large-v3 b1: generating weights")
+    wbits = make_weights(LARGE_V3, wl.cfg_id)
+    enc = make_encoder_out(LARGE_V3, wl.cfg_id, 0)
+    prefix = make_prefixes(wl)[0]
+    P = len(prefix)
+    log("large-v3 b1: oracle prefill + greedy continuation")
+    m = om.Model(LARGE_V3, wbits)
+    req = m.new_request(enc)
+    ref_pre = m.rows(req, prefix, 0)
+    y = od.argmax_lowest(ref_pre[-1])
+    greedy = [y]
+    L = P
+    for _ in range(8):
+        lg = m.rows(req, [greedy[-1]], L)
+        L += 1
+        greedy.append(od.argmax_lowest(lg[0]))
+    keep, repl = make_draft_table(wl, 0)
+    drafts = od.table_drafts(greedy, P, keep, repl)(P, greedy[0], 8)
+    block = np.array([greedy[0]] + drafts, np.int32)
+    req2 = m.new_request(enc)
+    m.rows(req2, prefix, 0)
+    ref_blk = m.rows(req2, block, P)
+    del m
+    log("large-v3 b1: GPU")
+    eng = _engine(LARGE_V3, wbits, max_batch=2, max_rows=128)
+    eng.wf_encode_kv(eng.i32([0]), eng.bf16(enc[None]))
+    am, lg_pre = _verify(eng, [0], prefix[None], [P])
+    e1 = assert_logits_close(lg_pre[0], ref_pre, what="large prefill")
+    assert_argmax_where_clear(am[0], ref_pre, what="large prefill")
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    am, lg_blk = _verify(eng, [0], block[None], [9])
+    e2 = assert_logits_close(lg_blk[0], ref_blk, what="large block")
+    assert_argmax_where_clear(am[0], ref_blk, what="large block")
+    a_ref, c_ref, pinned = oracle_accept_pinned(drafts, ref_blk, 8)
+    torch = eng.torch
+    outs = [torch.empty(1, dtype=torch.int32, device=eng.dev) for _ in range(4)]
+    eng.wf_accept(eng.i32(block[None]), eng.i32([9]), eng.i32([wl.n_max - 1]),
+                  eng.i32(am), *outs)
+    a_gpu, c_gpu = int(outs[0].item()), int(outs[1].item())
+    if pinned:
+        assert (a_gpu, c_gpu) == (a_ref, c_ref)
+    log(f"large-v3 b1: prefill err {e1:.2e}, block err {e2:.2e}, a={a_gpu} (oracle {a_ref}, pinned={pinned})")
+    # row invariance at full shape: prefix+block as one block of 73 rows
+    # (full-mode GEMMs) equals prefill 64 + block 9 (split-mode GEMMs)
+    eng.wf_rollback(eng.i32([0]), eng.i32([0]))
+    eng.wf_reset(eng.i32([0]))
+    seq = np.concatenate([prefix, block]).astype(np.int32)
+    _, lg_all = _verify(eng, [0], seq[None], [len(seq)])
+    assert np.array_equal(lg_all[0, :P].view(np.uint32), lg_pre[0].view(np.uint32))
+    assert np.array_equal(lg_all[0, P:].view(np.uint32), lg_blk[0].view(np.uint32))
+    eng.close()
+
+
+# --------------------------------------------------------------------------
+# turbo shape, batch 32, ragged prefixes, shuffled pages
+def test_turbo_b32_ragged_shuffled_pages(torch_cuda):
+    wl = WORKLOADS[2]
+    shape = TURBO
+    B = wl.batch
+    wbits = make_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    prefixes = make_prefixes(wl)
+    pps = shape.n_ctx // 16
+    perm = np.random.default_rng(5).permutation(B * pps).astype(np.int32)
+    eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224, page_table=perm.reshape(B, pps))
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    T = max(len(p) for p in prefixes)
+    toks = np.zeros((B, T), np.int32)
+    for b, p in enumerate(prefixes):
+        toks[b, :len(p)] = p
+    lens = np.array([len(p) for p in prefixes], np.int32)
+    am, lg = _verify(eng, slots, toks, lens)
+    eng.wf_rollback(eng.i32(slots), eng.i32(lens - 1))
+    m = om.Model(shape, wbits)
+    sample = [0, 7, int(np.argmax(lens))]
+    anchors = {}
+    for b in sample:
+        req = m.new_request(encs[b])
+        ref = m.rows(req, prefixes[b], 0)
+        P = lens[b]
+        assert_logits_close(lg[b, :P], ref, what=f"turbo prefill req {b}")
+        assert_argmax_where_clear(am[b, :P], ref, what=f"turbo prefill req {b}")
+        anchors[b] = (req, int(am[b, P - 1]))
+    # one block of 9 per request; sampled requests use drafts from their
+    # oracle greedy continuation, the rest random ids
+    blocks = np.random.default_rng(6).integers(0, shape.vocab, (B, 9)).astype(np.int32)
+    blocks[:, 0] = [am[b, lens[b] - 1] for b in range(B)]
+    refs = {}
+    for b in sample:
+        req, y = anchors[b]
+        L = lens[b]
+        gl = [y]
+        tmp = om.Request(m._shape_nl(), req.xkv, m.dtype)
+        for l in range(m.n_layers):
+            tmp.K[l][:] = req.K[l]
+            tmp.V[l][:] = req.V[l]
+        for i in range(8):
+            gl.append(od.argmax_lowest(m.rows(tmp, [gl[-1]], L + i)[0]))
+        keep, repl = make_draft_table(wl, b)
+        blocks[b, 1:] = od.table_drafts(gl, L, keep, repl)(L, y, 8)
+        refs[b] = m.rows(req, blocks[b], L)
+    am2, lg2 = _verify(eng, slots, blocks, [9] * B)
+    for b in sample:
+        assert_logits_close(lg2[b], refs[b], what=f"turbo block req {b}")
+        assert_argmax_where_clear(am2[b], refs[b], what=f"turbo block req {b}")
+    err, ln = eng.wf_device_state()
+    assert (err == 0).all()
+    log("turbo b32: parity on sampled requests ok")
+    eng.close()
+
+
+def test_turbo_b32_speculative_equals_greedy_on_gpu(torch_cuda):
+    from speculative_decoding_encoder_amd.harness import run_loop, table_drafter
+    wl = WORKLOADS[2]
+    shape = TURBO
+    B = wl.batch
+    wbits = make_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    prefixes = make_prefixes(wl)
+    pps = shape.n_ctx // 16
+    perm = np.random.default_rng(7).permutation(B * pps).astype(np.int32)
+    eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224, page_table=perm.reshape(B, pps))
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    n_max = 40
+    eng.wf_reset(eng.i32(slots))
+    g = run_loop(eng, slots, prefixes, n_max, 0, None, shape.eos_id)
+    fn = table_drafter(g.tokens, [len(p) for p in prefixes],
+                       [make_draft_table(wl, b) for b in range(B)])
+    eng.wf_reset(eng.i32(slots))
+    s = run_loop(eng, slots, prefixes, n_max, wl.k_draft, fn, shape.eos_id)
+    for b in range(B):
+        assert s.tokens[b] == g.tokens[b], b
+    acc = [a for b in range(B) for a in s.accepted[b]]
+    log(f"turbo b32: speculative == greedy for all {B} requests, {s.rounds} rounds vs "
+        f"{g.rounds}, mean accepted {np.mean(acc):.2f}")
+    eng.close()
