@@ -1,0 +1,301 @@
+"""Benchmark of the block-verification hot path on one MI355X.
+
+A step is one full round of the path over one batch: wf_verify_block on the
+anchor plus K = 8 candidates per request (every decoder layer, the tied LM
+head and the per-row argmax), wf_accept and wf_rollback, followed by
+wf_truncate back to the prefix length so that every step verifies the same
+block from the same state. Inputs are seeded and synthetic (no datasets, no
+trained weights); weights, audio memory, prompts and KV caches are resident
+in HBM before the timed region starts.
+
+Workloads (``--config``):
+  1  32-layer large-v3 shape, batch 1, 64-token prefix, one block of 9,
+     drafts = the greedy token with probability 0.7, else a uniform id (default)
+  2  4-layer turbo shape, batch 32, prefixes uniform in [4, 200], p = 0.75
+  4  32-layer large-v3 shape, batch 32, prefixes uniform in [4, 200], p = 0.7
+     (the batch-32 verify pass; greedy acceptance)
+The greedy continuation that drafts copy is the engine's own, computed before
+timing. Tokens per second count the tokens a round emits, sum over requests
+of (accepted + 1); audio seconds per second divide that by 3.5 tokens per
+audio second (the tokens-to-audio ratio of Whisper-Flash Table 1).
+
+The timed loop replays one HIP graph per step. Kernel durations for the
+roofline come from HIP events around every launch over a second pass of the
+same steps; the dominant kernel is the one with the largest total time.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+TOKENS_PER_AUDIO_S = 3.5
+METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
+KIND_NAMES = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
+              "cross_attn", "other", "encode_kv"]
+# kernel symbol (rocprofv3 name prefix) of each timing kind
+KIND_SYMBOL = {
+    "qkv": "gemm_kernel<0, 4, true>", "oproj": "gemm_kernel<1, 4, true>",
+    "cross_q": "gemm_kernel<2, 4, true>", "fc1": "gemm_kernel<3, 4, true>",
+    "fc2": "gemm_kernel<1, 8, true>", "lm_head": "gemm_kernel<4, 4, true>",
+    "self_attn": "self_attn_kernel<64>", "cross_attn": "cross_attn_kernel<64>",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Workload:
+    def __init__(self, cfg_id: int):
+        from synthetic import (WORKLOADS, make_draft_table, make_encoder_out, make_prefixes,
+                               make_weights)
+        from speculative_decoding_encoder_amd.binding import Engine
+        from speculative_decoding_encoder_amd.harness import prefill, run_loop
+        import torch
+        self.torch = torch
+        self.wl = wl = WORKLOADS[cfg_id]
+        self.shape = s = wl.shape
+        self.B = B = wl.batch
+        self.K = wl.k_draft
+        self.name = wl.name if cfg_id != 4 else "large-v3-verify-b32-greedy"
+        t0 = time.time()
+        self.wbits = make_weights(s, wl.cfg_id)
+        self.encs = np.stack([make_encoder_out(s, wl.cfg_id, r) for r in range(B)])
+        self.prefixes = make_prefixes(wl)
+        self.P = np.array([len(p) for p in self.prefixes], np.int32)
+        log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
+        max_rows = max(B * (self.K + 1), B * int(self.P.max()))
+        self.eng = eng = Engine(s, self.wbits, max_batch=B, max_rows=max_rows)
+        self.slots = list(range(B))
+        self.d_slots = eng.i32(self.slots)
+        d_enc = eng.bf16(self.encs)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eng.wf_encode_kv(self.d_slots, d_enc)
+        torch.cuda.synchronize()
+        self.encode_kv_s = time.perf_counter() - t0
+        del d_enc
+        # the engine's own greedy continuation (untimed) for the drafts
+        eng.wf_reset(self.d_slots)
+        g = run_loop(eng, self.slots, self.prefixes, self.K + 1, 0, None, s.eos_id)
+        self.greedy = g.tokens
+        eng.wf_reset(self.d_slots)
+        anchors = prefill(eng, self.slots, self.prefixes)
+        blocks = np.zeros((B, self.K + 1), np.int32)
+        for b in range(B):
+            keep, repl = make_draft_table(wl, b)
+            L = int(self.P[b])
+            blocks[b, 0] = anchors[b]
+            for i in range(1, self.K + 1):
+                j = i  # greedy[b][i] sits at position L + i
+                gt = self.greedy[b][j] if j < len(self.greedy[b]) else int(repl[L + i])
+                blocks[b, i] = gt if keep[L + i] else repl[L + i]
+        self.blocks = blocks
+        T = self.K + 1
+        self.d_tok = eng.i32(blocks)
+        self.d_ntok = eng.i32(np.full(B, T, np.int32))
+        self.d_budget = eng.i32(np.full(B, wl.n_max - 1, np.int32))
+        self.d_am = torch.empty((B, T), dtype=torch.int32, device=eng.dev)
+        self.outs = [torch.empty(B, dtype=torch.int32, device=eng.dev) for _ in range(4)]
+        self.d_P = eng.i32(self.P)
+
+    def step(self):
+        e = self.eng
+        e.wf_verify_block(self.d_slots, self.d_tok, self.d_ntok, self.d_am)
+        e.wf_accept(self.d_tok, self.d_ntok, self.d_budget, self.d_am, *self.outs)
+        e.wf_rollback(self.d_slots, self.outs[0])
+        e.wf_truncate(self.d_slots, self.d_P)
+
+    # algorithmic HBM bytes per launch of each kernel kind (weights and KV
+    # caches; activations stay in L2 / the Infinity Cache)
+    def kind_bytes(self):
+        s = self.shape
+        d, F, V = s.d_model, s.d_ffn, s.vocab
+        T = self.K + 1
+        kv_pos = 4 * d                              # fp16 K and V of one position, one layer
+        self_bytes = kv_pos * float(np.sum(self.P + T))
+        cross_bytes = self.B * s.n_frames * 4.0 * d
+        return {
+            "qkv": 3.0 * d * d * 2 + kv_pos * self.B * T,   # weights + K/V appended
+            "oproj": d * d * 2.0, "cross_q": d * d * 2.0, "fc1": d * F * 2.0,
+            "fc2": F * d * 2.0, "lm_head": V * d * 2.0, "self_attn": self_bytes,
+            "cross_attn": cross_bytes,
+        }
+
+    def pass_bytes(self):
+        """bytes_pass = N_L (45.875 MB + sum_b [7.68 MB + 5120 (L_b + n_tok_b)])
+        + 132.78 MB at the large-v3 width (weights + caches)."""
+        kb = self.kind_bytes()
+        nl = self.shape.n_layers
+        per_layer = kb["qkv"] + 2 * kb["oproj"] + kb["cross_q"] + kb["fc1"] + kb["fc2"] \
+            + kb["self_attn"] + kb["cross_attn"]
+        return nl * per_layer + kb["lm_head"]
+
+
+def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
+    """The oracle, as it stands (fp64 numpy), on a bounded sample of the same
+    workload: the verify pass (K+1 rows through every layer and the LM head)
+    of the first requests, each repeated up to 3 times, until about
+    ``timed_s`` seconds of timed CPU work (building each request's cross K/V
+    and prefix cache is not timed)."""
+    from oracle import decode as od
+    from oracle import model as om
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    m = om.Model(w.shape, w.wbits)
+    toks = 0
+    t_total = 0.0
+    passes = 0
+    reqs = 0
+    t_start = time.time()
+    for b in range(w.B):
+        req = m.new_request(w.encs[b])
+        m.rows(req, w.prefixes[b], 0)
+        reqs += 1
+        for _ in range(3):
+            t0 = time.perf_counter()
+            lg = m.rows(req, w.blocks[b], int(w.P[b]))
+            t_total += time.perf_counter() - t0
+            g = [od.argmax_lowest(r) for r in lg]
+            d = list(w.blocks[b, 1:])
+            a = 0
+            while a < len(d) and d[a] == g[a]:
+                a += 1
+            toks += a + 1
+            passes += 1
+            if t_total >= timed_s:
+                break
+        if t_total >= timed_s or time.time() - t_start > wall_s:
+            break
+    return {"value": round(toks / t_total, 3), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{passes} verify passes (K+1 = {w.K + 1} rows, all layers, LM head) over "
+                      f"{reqs} of {w.B} requests, fp64 numpy, {t_total:.2f} s timed; cross K/V "
+                      f"and prefix caches built untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
+              "single MI355X (requests shard by data parallelism with no exchange; see "
+              "DESIGN.md). --gpus N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    w = Workload(args.config)
+    eng = w.eng
+    K, W = args.steps, args.warmup
+
+    # warm-up, then one step to read the round's outcome
+    for _ in range(max(W, 1)):
+        w.step()
+    torch.cuda.synchronize()
+    n_acc = w.outs[0].cpu().numpy()
+    err, lens = eng.wf_device_state()
+    assert (err == 0).all() and (n_acc >= 0).all(), "engine reported an error"
+    tokens_per_step = int(np.sum(n_acc + 1))
+
+    stream = torch.cuda.Stream()
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            w.step()
+        torch.cuda.synchronize()
+        for _ in range(W):
+            graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        if graph is not None:
+            graph.replay()
+        else:
+            w.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    n_acc2 = w.outs[0].cpu().numpy()
+    assert np.array_equal(n_acc, n_acc2), "graph replay changed the round's outcome"
+
+    # per-kernel durations from HIP events (eager launches of the same steps)
+    eng.wf_set_timing(True)
+    for _ in range(K):
+        w.step()
+    torch.cuda.synchronize()
+    kinds = {}
+    for i, name in enumerate(KIND_NAMES):
+        ms, cnt = eng.wf_get_timing(i)
+        if cnt:
+            kinds[name] = {"total_ms_per_step": ms / K, "launches_per_step": cnt // K,
+                           "avg_us": ms * 1e3 / cnt}
+    eng.wf_set_timing(False)
+    kb = w.kind_bytes()
+    dom = max((k for k in kinds if k in kb), key=lambda k: kinds[k]["total_ms_per_step"])
+    avg_s = kinds[dom]["avg_us"] * 1e-6
+    achieved = kb[dom] / avg_s / 1e9
+    for k in kinds:
+        if k in kb:
+            kinds[k]["gbs"] = kb[k] / (kinds[k]["avg_us"] * 1e-6) / 1e9
+    bytes_pass = w.pass_bytes()
+
+    value = tokens_per_step / (ms_step * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded weights N(0,0.02) in bf16, audio memory N(0,1), "
+                "Bernoulli-copy drafts)",
+        "config": {"workload": w.name, "layers": w.shape.n_layers,
+                   "d_model": w.shape.d_model, "batch": w.B, "K": w.K,
+                   "prefix": w.wl.prefix, "p_keep": w.wl.p_keep,
+                   "graph": graph is not None},
+        "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
+        "tokens_per_step": tokens_per_step,
+        "accepted": [int(a) for a in n_acc[:8]],
+        "pass": {"bytes": bytes_pass, "roofline_frac_of_step": round(
+            bytes_pass / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)},
+        "roofline": {"bound": "hbm", "kernel": dom, "symbol": KIND_SYMBOL.get(dom, dom),
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": kb[dom], "avg_us": round(kinds[dom]["avg_us"], 3)},
+        "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kinds.items()},
+        "encode_kv_s": round(w.encode_kv_s, 4),
+    }
+    if not args.no_cpu:
+        t0 = time.time()
+        out["cpu_baseline"] = cpu_baseline(w)
+        log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

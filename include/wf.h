@@ -206,6 +206,12 @@ wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
 wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots,
                       const int32_t *d_n_acc, void *stream);
 
+/* Shorten the cache of n slots to d_len[b] positions (0 <= d_len[b] <= the
+ * current length; the slot must not be pending), e.g. to verify the same
+ * block again from the same state. A bad length sets WF_DERR_STATE. */
+wf_status wf_truncate(wf_engine *e, int32_t n, const int32_t *d_slots,
+                      const int32_t *d_len, void *stream);
+
 /* Synchronise the stream and copy max_batch error words and cache lengths
  * to the host (either pointer may be NULL). */
 wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *stream);
@@ -213,9 +219,12 @@ wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *st
 /* Measurement. While timing is enabled every launch is bracketed with HIP
  * events on its stream (so calls are no longer graph-capturable).
  * wf_get_timing synchronises and returns the summed duration and the number
- * of launches of one kind since timing was last enabled:
- * 0 = decoder projection GEMMs, 1 = LM head, 2 = self-attention,
- * 3 = cross-attention, 4 = everything else. */
+ * of launches of one kind since timing was last enabled. Kinds (each is one
+ * kernel instantiation): 0 QKV projection + KV append, 1 self/cross output
+ * projections + residual, 2 cross-attention query, 3 fc1 + GELU,
+ * 4 fc2 + residual, 5 tied LM head + argmax, 6 self-attention,
+ * 7 cross-attention, 8 everything else (embed, layer norms, argmax merge,
+ * accept, rollback), 9 write-once cross K/V. */
 wf_status wf_set_timing(wf_engine *e, int32_t enable);
 wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count);
 

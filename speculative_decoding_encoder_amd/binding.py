@@ -79,6 +79,7 @@ def load():
         "wf_accept": (I32, [P, I32, P, I32, P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64,
                             P, P, P, P, P, P, P]),
         "wf_rollback": (I32, [P, I32, P, P, P]),
+        "wf_truncate": (I32, [P, I32, P, P, P]),
         "wf_device_state": (I32, [P, P, P, P]),
         "wf_set_timing": (I32, [P, I32]),
         "wf_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
@@ -209,6 +210,10 @@ class Engine:
         _check(self.lib.wf_rollback(self.h, slots.numel(), _p(slots), _p(n_acc),
                                     _stream(stream)), "wf_rollback")
 
+    def wf_truncate(self, slots, lens, stream=None):
+        _check(self.lib.wf_truncate(self.h, slots.numel(), _p(slots), _p(lens),
+                                    _stream(stream)), "wf_truncate")
+
     def wf_device_state(self, stream=None):
         mb = self.cfg.max_batch
         err = (ctypes.c_int32 * mb)()
@@ -235,4 +240,5 @@ class Engine:
         return t.to(self.dev).view(self.torch.bfloat16)
 
 
-TIMING_GEMM, TIMING_LMHEAD, TIMING_SELF, TIMING_CROSS, TIMING_OTHER = range(5)
+TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn", "cross_attn",
+                "other", "encode_kv"]

@@ -39,9 +39,10 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 // K chunking of the GEMMs: a function of K only (see k_gemm.hip).
 void gemm_chunks(int K, int &ck, int &S) {
     const int ks = K / 32;
-    ck = (ks % 8 == 0 && ks >= 80) ? 8 : (ks % 4 == 0 ? 4 : 2);
-    S = ks / ck;
+    S = (ks % 8 == 0) ? 8 : 2;
+    ck = ks / S;
 }
+constexpr int kSplitRowsCap = 128;   // GEMM K-split scratch sized for this many rows x 8
 
 // Frames per cross-attention chunk: enough waves to cover the GPU when the
 // batch is small, one chunk per (request, head) when it is large. Depends on
@@ -86,14 +87,8 @@ Layout layout_of(const wf_config *c) {
     const size_t M = (size_t)c->max_rows, d = c->d_model, f = c->d_ffn;
     const int H = c->n_heads, hd = c->head_dim;
     L.n_vtiles = cdiv(c->vocab, 64);
-    // split-K partials: only for M <= 64
-    size_t part = 0;
-    const int KN[4][2] = {{(int)d, 3 * (int)d}, {(int)d, (int)d}, {(int)d, (int)f}, {(int)f, (int)d}};
-    for (auto &kn : KN) {
-        int ck, S;
-        gemm_chunks(kn[0], ck, S);
-        part = std::max(part, (size_t)S * 64 * kn[1] * 4);
-    }
+    // K-split subtree sums: up to 8 groups of kSplitRowsCap rows of the widest projection
+    size_t part = (size_t)8 * kSplitRowsCap * std::max(3 * d, f) * 4;
     L.part_bytes = part;
     size_t xap = 0;
     for (int n = 1; n <= c->max_batch; ++n) {
@@ -110,7 +105,7 @@ Layout layout_of(const wf_config *c) {
     L.hs = take(M * 2 * f * 2);
     L.q = take(M * d * 2);
     L.part = take(part);
-    L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 64) * 4 + 64);
+    L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 64) * (cdiv((int)M, 16) + 1) * 4);
     L.xapart = take(xap);
     L.xacnt = take((size_t)c->max_batch * H * (c->n_ctx / 16 + 1) * 4);
     L.lmmax = take((size_t)L.n_vtiles * M * 4);
@@ -126,7 +121,10 @@ Layout layout_of(const wf_config *c) {
 
 int f_pad_of(const wf_config *c) { return cdiv(c->n_frames, 32) * 32; }
 
-enum TimingKind { TK_GEMM = 0, TK_LMHEAD = 1, TK_SELF = 2, TK_CROSS = 3, TK_OTHER = 4, TK_N = 5 };
+enum TimingKind {
+    TK_QKV = 0, TK_OPROJ = 1, TK_QC = 2, TK_FC1 = 3, TK_FC2 = 4, TK_LMHEAD = 5,
+    TK_SELF = 6, TK_CROSS = 7, TK_OTHER = 8, TK_XKV = 9, TK_N = 10
+};
 
 }  // namespace
 
@@ -185,9 +183,9 @@ wf_status timed(wf_engine *e, int kind, hipStream_t st, F &&launch) {
     return WF_OK;
 }
 
-wf_status run_gemm(wf_engine *e, int epi, const uint16_t *X, bool xsplit, int M, int K,
-                   const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n, int N,
-                   const EpiArgs &ea, hipStream_t st) {
+wf_status run_gemm(wf_engine *e, int kind, int epi, const uint16_t *X, bool xsplit, int M,
+                   int K, const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n,
+                   int N, const EpiArgs &ea, hipStream_t st) {
     GemmArgs a{};
     a.X = X;
     a.W0 = W0;
@@ -200,23 +198,29 @@ wf_status run_gemm(wf_engine *e, int epi, const uint16_t *X, bool xsplit, int M,
     int ck, S;
     gemm_chunks(K, ck, S);
     a.S = S;
+    a.ck = ck;
     a.n_tiles = cdiv(N, 64);
-    a.split = (epi != EPI_ARGMAX && epi != EPI_XKV && M <= 64 && S > 1) ? 1 : 0;
-    if (a.split) {
-        a.m_blocks = 1;
-        a.n_groups = S;
-        if ((size_t)S * M * N * 4 > e->lay.part_bytes)
-            return fail(WF_ECAPACITY, "split-K scratch too small");
-    } else {
-        a.m_blocks = cdiv(M, 64);
-        a.n_groups = 1;
+    // Row blocks: the tallest block (up to 32 rows) that still gives about
+    // 256 workgroups; the row blocks of one weight tile share it through L2.
+    int mb = 2;
+    while (mb > 1 && a.n_tiles * cdiv(M, 16 * mb) < 256) mb >>= 1;
+    const int mt_need = cdiv(M, 16);
+    while (mb > 1 && (mb >> 1) >= mt_need) mb >>= 1;
+    a.m_blocks = cdiv(M, 16 * mb);
+    // Physical K split only for short blocks (<= 32 rows), where the
+    // subtree sums that cross workgroups are small.
+    int P = 1;
+    if (epi != EPI_ARGMAX && epi != EPI_XKV && M <= 32) {
+        while (P < S && a.n_tiles * a.m_blocks * P < 512 &&
+               (size_t)(2 * P) * M * N * 4 <= e->lay.part_bytes)
+            P *= 2;
     }
+    a.n_groups = P;
     a.n_wg = a.n_tiles * a.m_blocks * a.n_groups;
     a.part = e->part;
     a.cnt = e->gcnt;
     a.e = ea;
-    const int kind = epi == EPI_ARGMAX ? TK_LMHEAD : TK_GEMM;
-    return timed(e, kind, st, [&] { return launch_gemm(epi, a, ck, xsplit, st); });
+    return timed(e, kind, st, [&] { return launch_gemm(epi, a, mb, xsplit, st); });
 }
 
 wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
@@ -374,7 +378,7 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
         ea.H = c.n_heads;
         ea.hd = c.head_dim;
         ea.max_batch = c.max_batch;
-        WF_TRY(run_gemm(e, EPI_XKV, (const uint16_t *)d_enc, false, (int)M, c.d_model, w.wkc,
+        WF_TRY(run_gemm(e, TK_XKV, EPI_XKV, (const uint16_t *)d_enc, false, (int)M, c.d_model, w.wkc,
                         w.wvc, nullptr, c.d_model, 2 * c.d_model, ea, st));
     }
     return WF_OK;
@@ -406,7 +410,7 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         // long prefill blocks: fewer, longer chunks so the partials fit
         const size_t fit = e->lay.xapart_bytes / ((size_t)n * H * mt * rowbytes);
         const int steps = cdiv(c.n_frames, 32);
-        const int want = fit < 1 ? 1 : (int)fit;
+        const int want = fit < 1 ? 1 : (fit > 16 ? 16 : (int)fit);
         cf = cdiv(steps, want) * 32;
         nch = cdiv(c.n_frames, cf);
     }
@@ -430,20 +434,20 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         qa.H = H;
         qa.hd = hd;
         qa.page_elems = e->page_elems;
-        WF_TRY(run_gemm(e, EPI_QKV, e->xs, true, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
+        WF_TRY(run_gemm(e, TK_QKV, EPI_QKV, e->xs, true, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
                         e->page_elems, n, T, H, d, 1.0f / std::sqrt((float)hd), e->xs};
         WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, mt, st); }));
         EpiArgs ra{};
         ra.b0 = w.bo;
         ra.x = e->x;
-        WF_TRY(run_gemm(e, EPI_RESID, e->xs, true, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
+        WF_TRY(run_gemm(e, TK_OPROJ, EPI_RESID, e->xs, true, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
         // cross-attention sublayer
         WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
         EpiArgs fa{};
         fa.b0 = w.bqc;
         fa.out = e->q;
-        WF_TRY(run_gemm(e, EPI_F16, e->xs, true, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
+        WF_TRY(run_gemm(e, TK_QC, EPI_F16, e->xs, true, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
         CrossAttnArgs ca{};
         ca.q = e->q;
         ca.xkv = e->xkv;
@@ -469,18 +473,18 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         EpiArgs oa{};
         oa.b0 = w.boc;
         oa.x = e->x;
-        WF_TRY(run_gemm(e, EPI_RESID, e->xs, true, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
+        WF_TRY(run_gemm(e, TK_OPROJ, EPI_RESID, e->xs, true, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
         // MLP sublayer
         WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
         EpiArgs ga{};
         ga.b0 = w.b1;
         ga.out = e->hs;
-        WF_TRY(run_gemm(e, EPI_GELU, e->xs, true, M, d, w.w1, nullptr, nullptr, c.d_ffn,
+        WF_TRY(run_gemm(e, TK_FC1, EPI_GELU, e->xs, true, M, d, w.w1, nullptr, nullptr, c.d_ffn,
                         c.d_ffn, ga, st));
         EpiArgs f2{};
         f2.b0 = w.b2;
         f2.x = e->x;
-        WF_TRY(run_gemm(e, EPI_RESID, e->hs, true, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
+        WF_TRY(run_gemm(e, TK_FC2, EPI_RESID, e->hs, true, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
                         st));
     }
     WF_TRY(run_ln(e, M, e->lnf_g, e->lnf_b, st));
@@ -489,7 +493,7 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     la.tile_max = e->lmmax;
     la.tile_idx = e->lmidx;
     la.ld = c.max_rows;
-    WF_TRY(run_gemm(e, EPI_ARGMAX, e->xs, true, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
+    WF_TRY(run_gemm(e, TK_LMHEAD, EPI_ARGMAX, e->xs, true, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
                     c.vocab, la, st));
     LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, M, T, d_slots, e->reqN,
                     e->err, d_argmax};
@@ -547,6 +551,15 @@ wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots, const int
     RollbackArgs a{n, e->c.max_batch, d_slots, d_n_acc, e->len, e->pend, e->err};
     hipStream_t st = (hipStream_t)stream;
     return timed(e, TK_OTHER, st, [&] { return launch_rollback(a, st); });
+}
+
+wf_status wf_truncate(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_len,
+                      void *stream) {
+    if (!e || !d_slots || !d_len) return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    RollbackArgs a{n, e->c.max_batch, d_slots, d_len, e->len, e->pend, e->err};
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_truncate(a, st); });
 }
 
 wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *stream) {

@@ -223,12 +223,42 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
 
     const int f0 = ch * a.cf;
     const int f1 = min(f0 + a.cf, a.F);
-    for (int fb = f0; fb < f1; fb += 32) {
-        f32x4 s[2];
+    // K/V fragments of one 32-frame step; the next step is loaded while the
+    // current one is computed
+    struct KV {
+        u32x4 k[2][2];     // [16-frame tile][dim half] (HD = 64)
+        u32x2 k16[2];      // HD = 16
+        u32x4 v[NDT];
+    };
+    auto load_kv = [&](int fb, KV &f) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *krow = kh + (size_t)(fb + 16 * t + r16) * HD;
-            s[t] = qk_tile<HD>(q, krow, g);
+            if constexpr (HD == 64) {
+                f.k[t][0] = ld16(krow + 8 * g);
+                f.k[t][1] = ld16(krow + 32 + 8 * g);
+            } else {
+                f.k16[t] = ld8(krow + 4 * g);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            f.v[dt] = ld16(vh + (size_t)(dt * 16 + r16) * a.F_pad + fb + 8 * g);
+    };
+    KV cur, nxt;
+    load_kv(f0, cur);
+    for (int fb = f0; fb < f1; fb += 32) {
+        if (fb + 32 < f1) load_kv(fb + 32, nxt);
+        f32x4 s[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (HD == 64) {
+                s[t] = mfma_f16_k32(q.a[0], cur.k[t][0], s[t]);
+                s[t] = mfma_f16_k32(q.a[1], cur.k[t][1], s[t]);
+            } else {
+                s[t] = mfma_f16_k16(q.h, cur.k16[t], s[t]);
+            }
             const bool ok = fb + 16 * t + r16 < f1;
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[t][r] = ok ? s[t][r] * a.scale : -INFINITY;
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
         const bool tail = vf + 8 > f1;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt) {
-            u32x4 vb = ld16(vh + (size_t)(dt * 16 + r16) * a.F_pad + vf);
+            u32x4 vb = cur.v[dt];
             if (tail) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -254,6 +284,7 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
             o[dt] = mfma_f16_k32(pa, vb, o[dt]);
         }
         __syncthreads();
+        cur = nxt;
     }
 
     if (a.nch == 1) {
@@ -274,35 +305,44 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
     for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;
         if (r16 == 0) {
-            pp[row * PW + 0] = mrun[r];
-            pp[row * PW + 1] = lrun[r];
+            store_coherent(pp + row * PW + 0, mrun[r]);
+            store_coherent(pp + row * PW + 1, lrun[r]);
         }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) pp[row * PW + 2 + dt * 16 + r16] = o[dt][r];
+        for (int dt = 0; dt < NDT; ++dt) store_coherent(pp + row * PW + 2 + dt * 16 + r16, o[dt][r]);
     }
-    fence_release();
+    wait_vmem();
     int prev = 0;
-    if (lane == 0) prev = atomicAdd(&a.cnt[bhm], 1);
+    if (lane == 0) prev = arrive(&a.cnt[bhm]);
     prev = __shfl(prev, 0);
     if (prev != a.nch - 1) return;
-    fence_acquire();
-    if (lane == 0) a.cnt[bhm] = 0;
-    // merge chunks in order: each lane owns (row, dim) pairs
+    if (lane == 0) rearm(&a.cnt[bhm]);
+    // merge chunks in order. Per row r: M = max_c m_c, w_c = exp(m_c - M),
+    // L = sum_c l_c w_c; then o = sum_c o_c w_c / L.
+    __shared__ float wts[16][17];
     const float *pb = a.part + (size_t)(item - ch) * 16 * PW;
+    if (lane < 16) {
+        const int rr = lane;
+        float mx = -INFINITY;
+        for (int c = 0; c < a.nch; ++c) mx = fmaxf(mx, load_coherent(pb + (size_t)c * 16 * PW + rr * PW));
+        float l = 0.f;
+        for (int c = 0; c < a.nch; ++c) {
+            const float *pc = pb + (size_t)c * 16 * PW + rr * PW;
+            const float w = __expf(load_coherent(pc) - mx);
+            l += load_coherent(pc + 1) * w;
+            wts[rr][c] = w;
+        }
+        wts[rr][16] = l;
+    }
+    __syncthreads();
     for (int idx = lane; idx < 16 * HD; idx += 64) {
         const int rr = idx / HD, dim = idx - rr * HD;
         const int row = row0 + rr;
         if (row >= a.T) continue;
-        float mx = -INFINITY;
-        for (int c = 0; c < a.nch; ++c) mx = fmaxf(mx, pb[(size_t)c * 16 * PW + rr * PW]);
-        float l = 0.f, acc = 0.f;
-        for (int c = 0; c < a.nch; ++c) {
-            const float *pc = pb + (size_t)c * 16 * PW + rr * PW;
-            const float w = __expf(pc[0] - mx);
-            l += pc[1] * w;
-            acc += pc[2 + dim] * w;
-        }
-        store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dim, acc / l);
+        float acc = 0.f;
+        for (int c = 0; c < a.nch; ++c)
+            acc += load_coherent(pb + (size_t)c * 16 * PW + rr * PW + 2 + dim) * wts[rr][c];
+        store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dim, acc / wts[rr][16]);
     }
 }
 

@@ -1,30 +1,34 @@
 // Skinny bf16 GEMM for the decoder projections, the tied LM head and the
 // write-once cross K/V:  C[m][n] = sum_k X[m][k] * W[n][k].
 //
-// Design for gfx950 (wave64, 16x16x32 bf16 MFMA):
-//  * A workgroup is 4 waves; each wave owns 16 weight rows (output columns)
-//    and a block of up to 4 16-row M tiles. A lane loads its 16-byte weight
-//    fragments straight from HBM into registers (one pass over the weights
-//    per M block) and its activation fragments from L1/L2.
-//  * The activation operand is split-bf16: X = hi + lo, two MFMAs per k-step
+// Design for gfx950 (wave64, 16x16x32 bf16 MFMA, fp32 accumulate):
+//  * A workgroup is 4 waves and owns 64 output columns (16 per wave) of a
+//    block of BM = 16 * MB rows. Each wave streams its 16 weight rows from
+//    HBM straight into registers through a 3-deep prefetch ring (one pass
+//    over the weights per row block); the activation slice of each 32-deep
+//    k-step is staged once per workgroup in LDS (double-buffered) and read
+//    by all four waves.
+//  * The activation operand is split-bf16, X = hi + lo: two MFMAs per k-step
 //    with the same weight fragment, so activations carry ~16 mantissa bits
-//    while weights stay bf16.
-//  * K is cut into S chunks of CK k-steps that depend only on K. A chunk's
-//    partial sum always starts from zero and the partials are added in chunk
-//    order. A workgroup either owns one chunk (split mode: partials go to
-//    scratch and the last workgroup to arrive adds them up and runs the
-//    epilogue) or all chunks (full mode). Both give the same bits, and no
-//    result depends on M: a row's output is identical whether it is verified
-//    alone or inside a block.
+//    while the weights stay bf16.
+//  * K is cut into S = 8 chunks (2 when K = 64). A chunk's partial sum
+//    starts from zero, and the partials are combined by a fixed pairwise tree
+//    ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)). A workgroup owns S/P consecutive
+//    chunks (P = 1, 2, 4 or S) and reduces them with the same tree; when
+//    P > 1 the subtree sums go to scratch and the last workgroup of the tile
+//    to arrive combines them and runs the epilogue. Every P gives the same
+//    bits, and nothing depends on M: a row's output is identical whether it
+//    is verified alone or inside a block.
+//  * Split partials cross workgroups (and XCDs) with device-coherent stores
+//    and loads (agent-scope relaxed atomics), completed with a vector-memory
+//    wait before the arrival counter is bumped, instead of a full L2
+//    write-back fence.
 //  * Logical workgroups are remapped so that those sharing a weight tile (the
-//    M blocks or K chunks of one N tile) are consecutive on one XCD and hit
-//    the same L2.
+//    row blocks and K groups of one N tile) are consecutive on one XCD.
 #include "wf_device.h"
 #include "wf_internal.h"
 
 namespace wf {
-
-static constexpr int MB = 4;  // 16-row M tiles per workgroup
 
 __device__ __forceinline__ float gelu_erf(float t) {
     return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
@@ -91,8 +95,65 @@ __device__ __forceinline__ void epi_elem(const GemmArgs &a, int m, int n, float 
     }
 }
 
-template <int EPI, int CK, bool XS>
+template <int MB>
+__device__ __forceinline__ void acc_zero(f32x4 (&c)[MB]) {
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) c[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+template <int MB>
+__device__ __forceinline__ void acc_add(f32x4 (&dst)[MB], const f32x4 (&src)[MB]) {
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) dst[mt] = dst[mt] + src[mt];
+}
+
+// Pairwise-tree accumulation of consecutive chunk partials. After chunk j
+// (0-based within the group) the partial p is merged with the stack as a
+// binary counter: ((p0+p1)+(p2+p3))+... with the left operand always the
+// older sum.
+template <int MB>
+struct Tree {
+    f32x4 l0[MB], l1[MB], l2[MB];
+    __device__ __forceinline__ void push(int j, f32x4 (&p)[MB]) {
+        if ((j & 1) == 0) {
+            if (j == 0) { for (int mt = 0; mt < MB; ++mt) l0[mt] = p[mt]; }
+            else if (j == 2 || j == 6) { for (int mt = 0; mt < MB; ++mt) l1[mt] = p[mt]; }
+            else { for (int mt = 0; mt < MB; ++mt) l2[mt] = p[mt]; }   // j == 4
+            return;
+        }
+        // odd j: combine with the pending left sibling(s)
+        if (j == 1) { for (int mt = 0; mt < MB; ++mt) l0[mt] = l0[mt] + p[mt]; }
+        else if (j == 3) {
+            for (int mt = 0; mt < MB; ++mt) l1[mt] = l1[mt] + p[mt];
+            for (int mt = 0; mt < MB; ++mt) l0[mt] = l0[mt] + l1[mt];
+        } else if (j == 5) { for (int mt = 0; mt < MB; ++mt) l2[mt] = l2[mt] + p[mt]; }
+        else {   // j == 7
+            for (int mt = 0; mt < MB; ++mt) l1[mt] = l1[mt] + p[mt];
+            for (int mt = 0; mt < MB; ++mt) l2[mt] = l2[mt] + l1[mt];
+            for (int mt = 0; mt < MB; ++mt) l0[mt] = l0[mt] + l2[mt];
+        }
+    }
+};
+
+// Combine P subtree sums with the pairwise tree (P in {2, 4, 8}).
+__device__ __forceinline__ float tree_combine(const float *part, size_t stride, int P) {
+    float v[8];
+    for (int s = 0; s < P; ++s) v[s] = load_coherent(part + (size_t)s * stride);
+    if (P == 2) return v[0] + v[1];
+    if (P == 4) return (v[0] + v[1]) + (v[2] + v[3]);
+    return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+template <int EPI, int MB, int KS, bool XS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    constexpr int BM = MB * 16;
+    constexpr int XROW = XS ? 72 : 40;            // uint16 per row per k-step (padded: no
+                                                  // bank conflicts across 16 rows)
+    constexpr int XPARTS = XS ? 8 : 4;            // 16-byte parts per row per k-step
+    constexpr int NPARTS = BM * KS * XPARTS;      // 16-byte parts per stage
+    constexpr int XV = (NPARTS + 255) / 256;      // parts per thread
+    // stage layout in LDS: [k-step][row][XROW]
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][KS * BM * XROW];
+
     // XCD-aware remap: hardware workgroup w runs on XCD w % 8; logical ids
     // that are consecutive within one XCD share an N tile.
     const int per = gridDim.x >> 3;
@@ -105,6 +166,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
+    const int m_base = mblock * BM;
+    const int rows = min(BM, a.M - m_base);
 
     const int n_lane = ntile * 64 + wave * 16 + r16;  // weight row this lane streams
     const bool wok = n_lane < a.N;
@@ -112,64 +175,111 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     if (wok) {
         const int seg = n_lane / a.seg_n;
         const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
-        wrow = wb + (size_t)(n_lane - seg * a.seg_n) * a.K;
+        wrow = wb + (size_t)(n_lane - seg * a.seg_n) * a.K + 8 * g;
     }
-    const int s_lo = a.split ? grp : 0;
-    const int s_hi = a.split ? grp + 1 : a.S;
-    const int m_base = mblock * MB * 16;
+    const int cpg = a.S / a.n_groups;               // chunks per group
+    const int ck = a.ck;                            // k-steps per chunk (multiple of KS)
+    const int t0 = grp * cpg * ck;                  // first k-step of this group
+    const int nstages = cpg * ck / KS;
+    const int spc = ck / KS;                        // stages per chunk
 
-    f32x4 total[MB];
+    // activation stage (KS k-steps of this block's rows): global -> registers
+    // one stage ahead -> LDS
+    u32x4 xr[XV];
+    auto load_x = [&](int st) {
+        const int tb = t0 + st * KS;
 #pragma unroll
-    for (int mt = 0; mt < MB; ++mt) total[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    for (int s = s_lo; s < s_hi; ++s) {
-        const int k0 = s * CK * 32;
-        u32x4 wf[CK];
-#pragma unroll
-        for (int kk = 0; kk < CK; ++kk)
-            wf[kk] = wok ? ld16(wrow + k0 + kk * 32 + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int mt = 0; mt < MB; ++mt) {
-            f32x4 c = {0.f, 0.f, 0.f, 0.f};
-            const int mrow0 = m_base + mt * 16;
-            if (mrow0 < a.M) {
-                const int m = mrow0 + r16;
-                const bool mok = m < a.M;
-                if constexpr (XS) {
-                    const uint16_t *xr = a.X + (size_t)m * (2 * a.K);
-                    u32x4 xh[CK], xl[CK];
-#pragma unroll
-                    for (int kk = 0; kk < CK; ++kk) {
-                        const uint16_t *p = xr + (size_t)(((k0 + kk * 32) >> 3) + g) * 16;
-                        xh[kk] = mok ? ld16(p) : u32x4{0u, 0u, 0u, 0u};
-                        xl[kk] = mok ? ld16(p + 8) : u32x4{0u, 0u, 0u, 0u};
-                    }
-#pragma unroll
-                    for (int kk = 0; kk < CK; ++kk) {
-                        c = mfma_bf16_k32(xh[kk], wf[kk], c);
-                        c = mfma_bf16_k32(xl[kk], wf[kk], c);
-                    }
-                } else {
-                    const uint16_t *xr = a.X + (size_t)m * a.K;
-                    u32x4 xh[CK];
-#pragma unroll
-                    for (int kk = 0; kk < CK; ++kk)
-                        xh[kk] = mok ? ld16(xr + k0 + kk * 32 + 8 * g) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-                    for (int kk = 0; kk < CK; ++kk) c = mfma_bf16_k32(xh[kk], wf[kk], c);
+        for (int v = 0; v < XV; ++v) {
+            const int idx = tid + v * 256;
+            xr[v] = u32x4{0u, 0u, 0u, 0u};
+            if (idx < NPARTS) {
+                const int kk = idx / (BM * XPARTS);
+                const int r2 = idx - kk * (BM * XPARTS);
+                const int rr = r2 / XPARTS, part = r2 - (r2 / XPARTS) * XPARTS;
+                const int k0 = (tb + kk) * 32;
+                if (rr < rows) {
+                    if constexpr (XS)
+                        xr[v] = ld16(a.X + (size_t)(m_base + rr) * (2 * a.K) +
+                                     (size_t)(k0 >> 3) * 16 + part * 8);
+                    else
+                        xr[v] = ld16(a.X + (size_t)(m_base + rr) * a.K + k0 + part * 8);
                 }
             }
-            if (s == s_lo) total[mt] = c;
-            else total[mt] += c;
         }
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int v = 0; v < XV; ++v) {
+            const int idx = tid + v * 256;
+            if (idx < NPARTS) {
+                const int kr = idx / XPARTS, part = idx - (idx / XPARTS) * XPARTS;
+                *reinterpret_cast<u32x4 *>(&xs[buf][kr * XROW + part * 8]) = xr[v];
+            }
+        }
+    };
+    // weight fragments of one stage
+    struct WS { u32x4 f[KS]; };
+    auto load_w = [&](int st, WS &w) {
+        const int tb = t0 + st * KS;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+            w.f[kk] = wok ? ld16(wrow + (tb + kk) * 32) : u32x4{0u, 0u, 0u, 0u};
+    };
+
+    Tree<MB> tree;
+    f32x4 c[MB];
+    acc_zero(c);
+    WS wa, wb, wc;                        // stages s, s+1, s+2
+    load_w(0, wa);
+    if (nstages > 1) load_w(1, wb);
+    load_x(0);
+    store_x(0);
+    if (nstages > 1) load_x(1);
+    __syncthreads();
+    const int mt_live = (rows + 15) >> 4;
+    for (int s = 0; s < nstages; ++s) {
+        const int buf = s & 1;
+        if (s + 1 < nstages) store_x(buf ^ 1);     // stage s+1 into the other buffer
+        if (s + 2 < nstages) {
+            load_x(s + 2);
+            load_w(s + 2, wc);
+        }
+        const uint16_t *xb = xs[buf];
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const u32x4 wcur = wa.f[kk];
+#pragma unroll
+            for (int mt = 0; mt < MB; ++mt) {
+                if (mt < mt_live) {
+                    const uint16_t *xrow = xb + (kk * BM + mt * 16 + r16) * XROW;
+                    if constexpr (XS) {
+                        const u32x4 xh = *reinterpret_cast<const u32x4 *>(xrow + g * 16);
+                        const u32x4 xl = *reinterpret_cast<const u32x4 *>(xrow + g * 16 + 8);
+                        c[mt] = mfma_bf16_k32(xh, wcur, c[mt]);
+                        c[mt] = mfma_bf16_k32(xl, wcur, c[mt]);
+                    } else {
+                        const u32x4 xh = *reinterpret_cast<const u32x4 *>(xrow + g * 8);
+                        c[mt] = mfma_bf16_k32(xh, wcur, c[mt]);
+                    }
+                }
+            }
+        }
+        if ((s + 1) % spc == 0) {          // end of a chunk
+            tree.push(s / spc, c);
+            acc_zero(c);
+        }
+        wa = wb;
+        wb = wc;
+        __syncthreads();
     }
+    f32x4 (&total)[MB] = tree.l0;
 
     const int n_out = ntile * 64 + wave * 16 + r16;   // C column held by this lane
 
     if constexpr (EPI == EPI_ARGMAX) {
-        __shared__ float smax[4][MB * 16];
-        __shared__ int sidx[4][MB * 16];
-        __shared__ int snan[4][MB * 16];
+        __shared__ float smax[4][BM];
+        __shared__ int sidx[4][BM];
+        __shared__ int snan[4][BM];
         const EpiArgs &e = a.e;
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt) {
@@ -199,7 +309,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
             }
         }
         __syncthreads();
-        if (tid < MB * 16) {
+        if (tid < BM) {
             const int m = m_base + tid;
             if (m < a.M) {
                 float bv = smax[0][tid];
@@ -215,7 +325,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         }
         return;
     } else {
-        if (!a.split) {
+        if (a.n_groups == 1) {
 #pragma unroll
             for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
@@ -225,66 +335,65 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 }
             return;
         }
-        // split mode: publish this chunk's partial, the last arriver reduces.
+        // publish this group's subtree sum; the last arriver combines
+        const size_t stride = (size_t)a.M * a.N;
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int m = m_base + mt * 16 + 4 * g + r;
                 if (m < a.M && n_out < a.N)
-                    a.part[((size_t)s_lo * a.M + m) * a.N + n_out] = total[mt][r];
+                    store_coherent(a.part + (size_t)grp * stride + (size_t)m * a.N + n_out,
+                                   total[mt][r]);
             }
+        wait_vmem();
         __shared__ int last;
-        fence_release();
         __syncthreads();
-        if (tid == 0) {
-            const int prev = atomicAdd(&a.cnt[ntile], 1);
-            last = (prev == a.S - 1);
-        }
+        const int cidx = ntile * a.m_blocks + mblock;
+        if (tid == 0) last = (arrive(&a.cnt[cidx]) == a.n_groups - 1);
         __syncthreads();
         if (!last) return;
-        fence_acquire();
-        if (tid == 0) a.cnt[ntile] = 0;   // ready for the next launch
-        const int rows = min(MB * 16, a.M - m_base);
+        if (tid == 0) rearm(&a.cnt[cidx]);
         for (int idx = tid; idx < rows * 64; idx += 256) {
             const int rr = idx >> 6, cc = idx & 63;
             const int m = m_base + rr, n = ntile * 64 + cc;
             if (n >= a.N) continue;
-            float v = a.part[(size_t)m * a.N + n];
-            for (int s = 1; s < a.S; ++s) v += a.part[((size_t)s * a.M + m) * a.N + n];
-            epi_elem<EPI>(a, m, n, v);
+            epi_elem<EPI>(a, m, n, tree_combine(a.part + (size_t)m * a.N + n, stride,
+                                                a.n_groups));
         }
     }
 }
 
-template <int EPI, int CK, bool XS>
+template <int EPI, int MB, int KS, bool XS>
 static hipError_t launch_one(const GemmArgs &a, hipStream_t st) {
     const int grid = ((a.n_wg + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_kernel<EPI, CK, XS>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<EPI, MB, KS, XS>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
+// stage depth: 5 k-steps when the chunk allows it, else 1
 template <int EPI, bool XS>
-static hipError_t launch_ck(const GemmArgs &a, int ck, hipStream_t st) {
-    switch (ck) {
-        case 2: return launch_one<EPI, 2, XS>(a, st);
-        case 4: return launch_one<EPI, 4, XS>(a, st);
-        case 8: return launch_one<EPI, 8, XS>(a, st);
+static hipError_t launch_mb(const GemmArgs &a, int mb, hipStream_t st) {
+    const bool k5 = a.ck % 5 == 0;
+    switch (mb) {
+        case 1: return k5 ? launch_one<EPI, 1, 5, XS>(a, st) : launch_one<EPI, 1, 1, XS>(a, st);
+        case 2: return k5 ? launch_one<EPI, 2, 5, XS>(a, st) : launch_one<EPI, 2, 1, XS>(a, st);
+        case 4: return k5 ? launch_one<EPI, 4, 5, XS>(a, st) : launch_one<EPI, 4, 1, XS>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int epi, const GemmArgs &a, int ck, bool xsplit, hipStream_t st) {
+hipError_t launch_gemm(int epi, const GemmArgs &a, int mb, bool xsplit, hipStream_t st) {
     if (!xsplit) {
         if (epi != EPI_XKV) return hipErrorInvalidValue;
-        return launch_ck<EPI_XKV, false>(a, ck, st);
+        return launch_mb<EPI_XKV, false>(a, mb, st);
     }
     switch (epi) {
-        case EPI_QKV: return launch_ck<EPI_QKV, true>(a, ck, st);
-        case EPI_RESID: return launch_ck<EPI_RESID, true>(a, ck, st);
-        case EPI_F16: return launch_ck<EPI_F16, true>(a, ck, st);
-        case EPI_GELU: return launch_ck<EPI_GELU, true>(a, ck, st);
-        case EPI_ARGMAX: return launch_ck<EPI_ARGMAX, true>(a, ck, st);
+        case EPI_QKV: return launch_mb<EPI_QKV, true>(a, mb, st);
+        case EPI_RESID: return launch_mb<EPI_RESID, true>(a, mb, st);
+        case EPI_F16: return launch_mb<EPI_F16, true>(a, mb, st);
+        case EPI_GELU: return launch_mb<EPI_GELU, true>(a, mb, st);
+        case EPI_ARGMAX: return launch_mb<EPI_ARGMAX, true>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

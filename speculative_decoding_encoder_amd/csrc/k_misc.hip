@@ -192,6 +192,20 @@ __global__ void rollback_kernel(RollbackArgs a) {
     a.slot_pending[slot] = 0;
 }
 
+// Shorten a slot's cache to a given length (never lengthen it).
+__global__ void truncate_kernel(RollbackArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.n) return;
+    const int slot = a.slots[b];
+    if (slot < 0 || slot >= a.max_batch) return;
+    const int nl = a.n_acc[b];
+    if (a.slot_pending[slot] != 0 || nl < 0 || nl > a.slot_len[slot]) {
+        atomicOr(&a.slot_err[slot], WF_DERR_STATE);
+        return;
+    }
+    a.slot_len[slot] = nl;
+}
+
 __global__ void reset_kernel(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,
                              int32_t *pending, int32_t *err) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
@@ -226,6 +240,10 @@ hipError_t launch_accept(const AcceptArgs &a, hipStream_t st) {
 }
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(rollback_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(truncate_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_reset(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,

@@ -93,6 +93,24 @@ __device__ __forceinline__ void wave_argmax(float &v, int &i) {
     }
 }
 
-// Agent-scope fences around the last-arriver handoff between workgroups.
-__device__ __forceinline__ void fence_release() { __threadfence(); }
-__device__ __forceinline__ void fence_acquire() { __threadfence(); }
+// Handoff of partial results between workgroups (possibly on different
+// XCDs): the producer writes with device-coherent stores (agent-scope relaxed
+// atomics, which write through to the device coherence point), waits until
+// all its vector memory operations have completed, then bumps an arrival
+// counter; the last arriver reads the partials with device-coherent loads.
+// This avoids a full L2 write-back per producer.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): every vector memory operation of this wave (stores
+// included) has completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ int arrive(int *cnt) {
+    return __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void rearm(int *cnt) {
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}

@@ -43,12 +43,11 @@ struct GemmArgs {
     const uint16_t *X;             // split-bf16 [M][K/8][hi 8 | lo 8], or plain bf16 [M][K]
     const uint16_t *W0, *W1, *W2;  // weight segments, each [seg_n][K] bf16
     int32_t M, K, N, seg_n;
-    int32_t S;                     // number of K chunks (fixed per K)
-    int32_t split;                 // 1: one chunk per workgroup, last arriver reduces
-    int32_t n_tiles, m_blocks, n_groups;  // logical grid; n_groups = chunks (split) or 1
+    int32_t S, ck;                 // K chunks (fixed per K) and k-steps per chunk
+    int32_t n_tiles, m_blocks, n_groups;  // logical grid; n_groups = physical K split P
     int32_t n_wg;                  // logical workgroups (grid is padded to 8k)
-    float *part;                   // split partials [S][M][N]
-    int32_t *cnt;                  // split arrival counters [n_tiles]
+    float *part;                   // subtree sums [P][M][N] when P > 1
+    int32_t *cnt;                  // arrival counters [n_tiles * m_blocks]
     EpiArgs e;
 };
 
@@ -125,7 +124,7 @@ struct RollbackArgs {
     int32_t *slot_len, *slot_pending, *slot_err;
 };
 
-hipError_t launch_gemm(int epi, const GemmArgs &a, int ck, bool xsplit, hipStream_t st);
+hipError_t launch_gemm(int epi, const GemmArgs &a, int mb, bool xsplit, hipStream_t st);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
 hipError_t launch_layernorm(const LnArgs &a, hipStream_t st);
@@ -134,6 +133,7 @@ hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st);
 hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st);
+hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st);  // n_acc = new lengths
 hipError_t launch_reset(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,
                         int32_t *pending, int32_t *err, hipStream_t st);
 
