@@ -42,12 +42,12 @@ TOKENS_PER_AUDIO_S = 3.5
 METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
 KIND_NAMES = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
               "cross_attn", "other", "encode_kv"]
-# kernel symbol (rocprofv3 name prefix) of each timing kind
+# kernel symbol (rocprofv3 name prefix) of each timing kind; the GEMM's first
+# template argument is its role
 KIND_SYMBOL = {
-    "qkv": "gemm_kernel<0, 4, true>", "oproj": "gemm_kernel<1, 4, true>",
-    "cross_q": "gemm_kernel<2, 4, true>", "fc1": "gemm_kernel<3, 4, true>",
-    "fc2": "gemm_kernel<1, 8, true>", "lm_head": "gemm_kernel<4, 4, true>",
-    "self_attn": "self_attn_kernel<64>", "cross_attn": "cross_attn_kernel<64>",
+    "qkv": "wf::gemm_kernel<0,", "oproj": "wf::gemm_kernel<1,", "cross_q": "wf::gemm_kernel<2,",
+    "fc1": "wf::gemm_kernel<3,", "fc2": "wf::gemm_kernel<4,", "lm_head": "wf::gemm_kernel<5,",
+    "self_attn": "wf::self_attn_kernel<64>", "cross_attn": "wf::cross_attn_kernel<64>",
 }
 
 
@@ -195,6 +195,9 @@ def main():
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run device-to-device copies of this size (calibrates "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
@@ -290,6 +293,14 @@ def main():
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kinds.items()},
         "encode_kv_s": round(w.encode_kv_s, 4),
     }
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=eng.dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["calib_copy_bytes"] = n
     if not args.no_cpu:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(w)

@@ -183,9 +183,10 @@ wf_status timed(wf_engine *e, int kind, hipStream_t st, F &&launch) {
     return WF_OK;
 }
 
-wf_status run_gemm(wf_engine *e, int kind, int epi, const uint16_t *X, bool xsplit, int M,
+wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                    int K, const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n,
                    int N, const EpiArgs &ea, hipStream_t st) {
+    const bool split_k_ok = role != ROLE_LM_HEAD && role != ROLE_XKV;
     GemmArgs a{};
     a.X = X;
     a.W0 = W0;
@@ -210,7 +211,7 @@ wf_status run_gemm(wf_engine *e, int kind, int epi, const uint16_t *X, bool xspl
     // Physical K split only for short blocks (<= 32 rows), where the
     // subtree sums that cross workgroups are small.
     int P = 1;
-    if (epi != EPI_ARGMAX && epi != EPI_XKV && M <= 32) {
+    if (split_k_ok && M <= 32) {
         while (P < S && a.n_tiles * a.m_blocks * P < 512 &&
                (size_t)(2 * P) * M * N * 4 <= e->lay.part_bytes)
             P *= 2;
@@ -220,7 +221,7 @@ wf_status run_gemm(wf_engine *e, int kind, int epi, const uint16_t *X, bool xspl
     a.part = e->part;
     a.cnt = e->gcnt;
     a.e = ea;
-    return timed(e, kind, st, [&] { return launch_gemm(epi, a, mb, xsplit, st); });
+    return timed(e, kind, st, [&] { return launch_gemm(role, a, mb, st); });
 }
 
 wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
@@ -378,7 +379,7 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
         ea.H = c.n_heads;
         ea.hd = c.head_dim;
         ea.max_batch = c.max_batch;
-        WF_TRY(run_gemm(e, TK_XKV, EPI_XKV, (const uint16_t *)d_enc, false, (int)M, c.d_model, w.wkc,
+        WF_TRY(run_gemm(e, TK_XKV, ROLE_XKV, (const uint16_t *)d_enc, (int)M, c.d_model, w.wkc,
                         w.wvc, nullptr, c.d_model, 2 * c.d_model, ea, st));
     }
     return WF_OK;
@@ -434,20 +435,20 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         qa.H = H;
         qa.hd = hd;
         qa.page_elems = e->page_elems;
-        WF_TRY(run_gemm(e, TK_QKV, EPI_QKV, e->xs, true, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
+        WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
                         e->page_elems, n, T, H, d, 1.0f / std::sqrt((float)hd), e->xs};
         WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, mt, st); }));
         EpiArgs ra{};
         ra.b0 = w.bo;
         ra.x = e->x;
-        WF_TRY(run_gemm(e, TK_OPROJ, EPI_RESID, e->xs, true, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
+        WF_TRY(run_gemm(e, TK_OPROJ, ROLE_OPROJ, e->xs, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
         // cross-attention sublayer
         WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
         EpiArgs fa{};
         fa.b0 = w.bqc;
         fa.out = e->q;
-        WF_TRY(run_gemm(e, TK_QC, EPI_F16, e->xs, true, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
+        WF_TRY(run_gemm(e, TK_QC, ROLE_CROSS_Q, e->xs, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
         CrossAttnArgs ca{};
         ca.q = e->q;
         ca.xkv = e->xkv;
@@ -473,18 +474,18 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         EpiArgs oa{};
         oa.b0 = w.boc;
         oa.x = e->x;
-        WF_TRY(run_gemm(e, TK_OPROJ, EPI_RESID, e->xs, true, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
+        WF_TRY(run_gemm(e, TK_OPROJ, ROLE_OPROJ, e->xs, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
         // MLP sublayer
         WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
         EpiArgs ga{};
         ga.b0 = w.b1;
         ga.out = e->hs;
-        WF_TRY(run_gemm(e, TK_FC1, EPI_GELU, e->xs, true, M, d, w.w1, nullptr, nullptr, c.d_ffn,
+        WF_TRY(run_gemm(e, TK_FC1, ROLE_FC1, e->xs, M, d, w.w1, nullptr, nullptr, c.d_ffn,
                         c.d_ffn, ga, st));
         EpiArgs f2{};
         f2.b0 = w.b2;
         f2.x = e->x;
-        WF_TRY(run_gemm(e, TK_FC2, EPI_RESID, e->hs, true, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
+        WF_TRY(run_gemm(e, TK_FC2, ROLE_FC2, e->hs, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
                         st));
     }
     WF_TRY(run_ln(e, M, e->lnf_g, e->lnf_b, st));
@@ -493,7 +494,7 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     la.tile_max = e->lmmax;
     la.tile_idx = e->lmidx;
     la.ld = c.max_rows;
-    WF_TRY(run_gemm(e, TK_LMHEAD, EPI_ARGMAX, e->xs, true, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
+    WF_TRY(run_gemm(e, TK_LMHEAD, ROLE_LM_HEAD, e->xs, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
                     c.vocab, la, st));
     LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, M, T, d_slots, e->reqN,
                     e->err, d_argmax};

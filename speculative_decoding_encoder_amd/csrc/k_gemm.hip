@@ -143,8 +143,18 @@ __device__ __forceinline__ float tree_combine(const float *part, size_t stride, 
     return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
 }
 
-template <int EPI, int MB, int KS, bool XS>
+__host__ __device__ constexpr int epi_of(int role) {
+    return role == ROLE_QKV ? EPI_QKV
+         : role == ROLE_CROSS_Q ? EPI_F16
+         : role == ROLE_FC1 ? EPI_GELU
+         : role == ROLE_LM_HEAD ? EPI_ARGMAX
+         : role == ROLE_XKV ? EPI_XKV : EPI_RESID;
+}
+
+template <int ROLE, int MB, int KS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
+    constexpr int EPI = epi_of(ROLE);
+    constexpr bool XS = ROLE != ROLE_XKV;   // split-bf16 activations (the audio memory is bf16)
     constexpr int BM = MB * 16;
     constexpr int XROW = XS ? 72 : 40;            // uint16 per row per k-step (padded: no
                                                   // bank conflicts across 16 rows)
@@ -364,36 +374,34 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     }
 }
 
-template <int EPI, int MB, int KS, bool XS>
+template <int ROLE, int MB, int KS>
 static hipError_t launch_one(const GemmArgs &a, hipStream_t st) {
     const int grid = ((a.n_wg + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_kernel<EPI, MB, KS, XS>), dim3(grid), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((gemm_kernel<ROLE, MB, KS>), dim3(grid), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 
 // stage depth: 5 k-steps when the chunk allows it, else 1
-template <int EPI, bool XS>
+template <int ROLE>
 static hipError_t launch_mb(const GemmArgs &a, int mb, hipStream_t st) {
     const bool k5 = a.ck % 5 == 0;
     switch (mb) {
-        case 1: return k5 ? launch_one<EPI, 1, 5, XS>(a, st) : launch_one<EPI, 1, 1, XS>(a, st);
-        case 2: return k5 ? launch_one<EPI, 2, 5, XS>(a, st) : launch_one<EPI, 2, 1, XS>(a, st);
-        case 4: return k5 ? launch_one<EPI, 4, 5, XS>(a, st) : launch_one<EPI, 4, 1, XS>(a, st);
+        case 1: return k5 ? launch_one<ROLE, 1, 5>(a, st) : launch_one<ROLE, 1, 1>(a, st);
+        case 2: return k5 ? launch_one<ROLE, 2, 5>(a, st) : launch_one<ROLE, 2, 1>(a, st);
+        case 4: return k5 ? launch_one<ROLE, 4, 5>(a, st) : launch_one<ROLE, 4, 1>(a, st);
     }
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm(int epi, const GemmArgs &a, int mb, bool xsplit, hipStream_t st) {
-    if (!xsplit) {
-        if (epi != EPI_XKV) return hipErrorInvalidValue;
-        return launch_mb<EPI_XKV, false>(a, mb, st);
-    }
-    switch (epi) {
-        case EPI_QKV: return launch_mb<EPI_QKV, true>(a, mb, st);
-        case EPI_RESID: return launch_mb<EPI_RESID, true>(a, mb, st);
-        case EPI_F16: return launch_mb<EPI_F16, true>(a, mb, st);
-        case EPI_GELU: return launch_mb<EPI_GELU, true>(a, mb, st);
-        case EPI_ARGMAX: return launch_mb<EPI_ARGMAX, true>(a, mb, st);
+hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st) {
+    switch (role) {
+        case ROLE_QKV: return launch_mb<ROLE_QKV>(a, mb, st);
+        case ROLE_OPROJ: return launch_mb<ROLE_OPROJ>(a, mb, st);
+        case ROLE_CROSS_Q: return launch_mb<ROLE_CROSS_Q>(a, mb, st);
+        case ROLE_FC1: return launch_mb<ROLE_FC1>(a, mb, st);
+        case ROLE_FC2: return launch_mb<ROLE_FC2>(a, mb, st);
+        case ROLE_LM_HEAD: return launch_mb<ROLE_LM_HEAD>(a, mb, st);
+        case ROLE_XKV: return launch_mb<ROLE_XKV>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

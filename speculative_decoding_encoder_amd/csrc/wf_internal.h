@@ -124,7 +124,12 @@ struct RollbackArgs {
     int32_t *slot_len, *slot_pending, *slot_err;
 };
 
-hipError_t launch_gemm(int epi, const GemmArgs &a, int mb, bool xsplit, hipStream_t st);
+// GEMM roles: each is its own kernel instantiation (and profiler symbol).
+enum Role : int {
+    ROLE_QKV = 0, ROLE_OPROJ = 1, ROLE_CROSS_Q = 2, ROLE_FC1 = 3, ROLE_FC2 = 4,
+    ROLE_LM_HEAD = 5, ROLE_XKV = 6,
+};
+hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
 hipError_t launch_layernorm(const LnArgs &a, hipStream_t st);
