@@ -12,8 +12,12 @@ Workloads (``--config``):
   1  32-layer large-v3 shape, batch 1, 64-token prefix, one block of 9,
      drafts = the greedy token with probability 0.7, else a uniform id (default)
   2  4-layer turbo shape, batch 32, prefixes uniform in [4, 200], p = 0.75
-  4  32-layer large-v3 shape, batch 32, prefixes uniform in [4, 200], p = 0.7
-     (the batch-32 verify pass; greedy acceptance)
+  4  32-layer large-v3 shape, batch 32, prefixes uniform in [4, 200], temperature
+     0.7 rejection sampling; draft distributions q_i = 0.7 p~_i + 0.3 softmax(z_i),
+     z_i ~ N(0, 1) seeded, where p~_i is the target's T = 0.7 distribution along
+     its own greedy continuation; candidates are drawn from q_i. With --greedy:
+     the same batch-32 pass with Bernoulli-copy drafts (p = 0.7) and greedy
+     acceptance.
 The greedy continuation that drafts copy is the engine's own, computed before
 timing. Tokens per second count the tokens a round emits, sum over requests
 of (accepted + 1); audio seconds per second divide that by 3.5 tokens per
@@ -56,7 +60,7 @@ def log(*a):
 
 
 class Workload:
-    def __init__(self, cfg_id: int):
+    def __init__(self, cfg_id: int, greedy: bool = False):
         from synthetic import (WORKLOADS, make_draft_table, make_encoder_out, make_prefixes,
                                make_weights)
         from speculative_decoding_encoder_amd.binding import Engine
@@ -67,7 +71,9 @@ class Workload:
         self.shape = s = wl.shape
         self.B = B = wl.batch
         self.K = wl.k_draft
-        self.name = wl.name if cfg_id != 4 else "large-v3-verify-b32-greedy"
+        self.sampling = cfg_id == 4 and not greedy
+        self.temperature = wl.temperature if self.sampling else 0.0
+        self.name = wl.name if (cfg_id != 4 or self.sampling) else "large-v3-verify-b32-greedy"
         t0 = time.time()
         self.wbits = make_weights(s, wl.cfg_id)
         self.encs = np.stack([make_encoder_out(s, wl.cfg_id, r) for r in range(B)])
@@ -100,8 +106,15 @@ class Workload:
                 j = i  # greedy[b][i] sits at position L + i
                 gt = self.greedy[b][j] if j < len(self.greedy[b]) else int(repl[L + i])
                 blocks[b, i] = gt if keep[L + i] else repl[L + i]
-        self.blocks = blocks
         T = self.K + 1
+        self.d_q = None
+        self.d_logits = None
+        if self.sampling:
+            blocks = self._sampling_blocks(anchors, T)
+            self.d_logits = torch.empty((B, T, s.vocab), dtype=torch.float32, device=eng.dev)
+            self.d_req = eng.i32(np.arange(B, dtype=np.int32))
+            self.d_step = eng.i32(np.zeros(B, np.int32))
+        self.blocks = blocks
         self.d_tok = eng.i32(blocks)
         self.d_ntok = eng.i32(np.full(B, T, np.int32))
         self.d_budget = eng.i32(np.full(B, wl.n_max - 1, np.int32))
@@ -109,10 +122,49 @@ class Workload:
         self.outs = [torch.empty(B, dtype=torch.int32, device=eng.dev) for _ in range(4)]
         self.d_P = eng.i32(self.P)
 
+    def _sampling_blocks(self, anchors, T):
+        """Candidates drawn from q_i = 0.7 p~_i + 0.3 softmax(z_i) (untimed)."""
+        from synthetic import rng
+        torch, eng, s, B, K = self.torch, self.eng, self.shape, self.B, self.K
+        greedy_blk = np.zeros((B, T), np.int32)
+        for b in range(B):
+            greedy_blk[b, 0] = anchors[b]
+            greedy_blk[b, 1:] = self.greedy[b][1:T]
+        lg = torch.empty((B, T, s.vocab), dtype=torch.float32, device=eng.dev)
+        am = torch.empty((B, T), dtype=torch.int32, device=eng.dev)
+        eng.wf_verify_block(self.d_slots, eng.i32(greedy_blk), eng.i32(np.full(B, T, np.int32)),
+                            am, lg)
+        eng.wf_rollback(self.d_slots, eng.i32(np.zeros(B, np.int32)))
+        eng.wf_truncate(self.d_slots, eng.i32(self.P))
+        z = lg.cpu().numpy()[:, :K, :] / np.float32(self.temperature)
+        z -= z.max(-1, keepdims=True)
+        pt = np.exp(z)
+        pt /= pt.sum(-1, keepdims=True)
+        q = np.empty((B, K, s.vocab), np.float32)
+        blocks = np.zeros((B, T), np.int32)
+        blocks[:, 0] = anchors
+        for b in range(B):
+            g = rng(self.wl.cfg_id, 4000 + b)
+            for i in range(K):
+                zz = g.standard_normal(s.vocab)
+                sm = np.exp(zz - zz.max())
+                qi = 0.7 * pt[b, i].astype(np.float64) + 0.3 * sm / sm.sum()
+                q[b, i] = qi.astype(np.float32)
+                blocks[b, i + 1] = g.choice(s.vocab, p=qi / qi.sum())
+        self.q_host = q
+        self.d_q = torch.from_numpy(q).to(eng.dev)
+        del lg
+        return blocks
+
     def step(self):
         e = self.eng
-        e.wf_verify_block(self.d_slots, self.d_tok, self.d_ntok, self.d_am)
-        e.wf_accept(self.d_tok, self.d_ntok, self.d_budget, self.d_am, *self.outs)
+        e.wf_verify_block(self.d_slots, self.d_tok, self.d_ntok, self.d_am, self.d_logits)
+        if self.sampling:
+            e.wf_accept(self.d_tok, self.d_ntok, self.d_budget, self.d_am, *self.outs,
+                        logits=self.d_logits, q=self.d_q, temperature=self.temperature,
+                        seed=0, request_id=self.d_req, step=self.d_step)
+        else:
+            e.wf_accept(self.d_tok, self.d_ntok, self.d_budget, self.d_am, *self.outs)
         e.wf_rollback(self.d_slots, self.outs[0])
         e.wf_truncate(self.d_slots, self.d_P)
 
@@ -139,7 +191,11 @@ class Workload:
         nl = self.shape.n_layers
         per_layer = kb["qkv"] + 2 * kb["oproj"] + kb["cross_q"] + kb["fc1"] + kb["fc2"] \
             + kb["self_attn"] + kb["cross_attn"]
-        return nl * per_layer + kb["lm_head"]
+        extra = 0.0
+        if self.sampling:   # logits written and read back, q read
+            extra = self.B * (self.K + 1) * self.shape.vocab * 4.0 * 2 \
+                + self.B * self.K * self.shape.vocab * 4.0
+        return nl * per_layer + kb["lm_head"] + extra
 
 
 def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
@@ -150,6 +206,7 @@ def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
     and prefix cache is not timed)."""
     from oracle import decode as od
     from oracle import model as om
+    from oracle import sampling as osmp
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -168,12 +225,16 @@ def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
         for _ in range(3):
             t0 = time.perf_counter()
             lg = m.rows(req, w.blocks[b], int(w.P[b]))
+            d = [int(t) for t in w.blocks[b, 1:]]
+            if w.sampling:
+                a, *_ = osmp.sample_round(lg.astype(np.float32), w.q_host[b], d, w.temperature,
+                                          0, b, 0, w.shape.eos_id, w.wl.n_max - 1)
+            else:
+                g = [od.argmax_lowest(r) for r in lg]
+                a = 0
+                while a < len(d) and d[a] == g[a]:
+                    a += 1
             t_total += time.perf_counter() - t0
-            g = [od.argmax_lowest(r) for r in lg]
-            d = list(w.blocks[b, 1:])
-            a = 0
-            while a < len(d) and d[a] == g[a]:
-                a += 1
             toks += a + 1
             passes += 1
             if t_total >= timed_s:
@@ -182,7 +243,8 @@ def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
             break
     return {"value": round(toks / t_total, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{passes} verify passes (K+1 = {w.K + 1} rows, all layers, LM head) over "
+            "sample": f"{passes} verify passes (K+1 = {w.K + 1} rows, all layers, LM head"
+                      f"{', rejection sampling' if w.sampling else ''}) over "
                       f"{reqs} of {w.B} requests, fp64 numpy, {t_total:.2f} s timed; cross K/V "
                       f"and prefix caches built untimed"}
 
@@ -194,6 +256,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--greedy", action="store_true",
+                    help="config 4 with greedy acceptance instead of T = 0.7 sampling")
     ap.add_argument("--no-graph", action="store_true", help="time eager launches")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run device-to-device copies of this size (calibrates "
@@ -206,7 +270,7 @@ def main():
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)
-    w = Workload(args.config)
+    w = Workload(args.config, greedy=args.greedy)
     eng = w.eng
     K, W = args.steps, args.warmup
 
@@ -279,8 +343,8 @@ def main():
                 "Bernoulli-copy drafts)",
         "config": {"workload": w.name, "layers": w.shape.n_layers,
                    "d_model": w.shape.d_model, "batch": w.B, "K": w.K,
-                   "prefix": w.wl.prefix, "p_keep": w.wl.p_keep,
-                   "graph": graph is not None},
+                   "prefix": w.wl.prefix, "p_keep": w.wl.p_keep if not w.sampling else None,
+                   "temperature": w.temperature, "graph": graph is not None},
         "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
         "tokens_per_step": tokens_per_step,
         "accepted": [int(a) for a in n_acc[:8]],

@@ -516,11 +516,8 @@ wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
     if (!(temperature >= 0.f) || std::isinf(temperature))
         return fail(WF_EINVAL, "temperature must be finite and >= 0");
     if (temperature == 0.f && !d_argmax) return fail(WF_EINVAL, "greedy accept needs d_argmax");
-    if (temperature > 0.f) {
-        if (!d_logits || !d_q || !d_request_id || !d_step)
-            return fail(WF_EINVAL, "sampling needs logits, q, request ids and steps");
-        return fail(WF_EINVAL, "temperature sampling is not built in this library");
-    }
+    if (temperature > 0.f && (!d_logits || (T > 1 && !d_q) || !d_request_id || !d_step))
+        return fail(WF_EINVAL, "sampling needs logits, q (when T > 1), request ids and steps");
     AcceptArgs a{};
     a.n = n;
     a.T = T;

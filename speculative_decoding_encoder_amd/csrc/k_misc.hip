@@ -234,7 +234,7 @@ hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st) {
-    if (a.temperature > 0.f) return hipErrorNotSupported;
+    if (a.temperature > 0.f) return launch_accept_sample(a, st);
     hipLaunchKernelGGL(accept_greedy_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
     return hipGetLastError();
 }

@@ -1,0 +1,260 @@
+// Temperature rejection sampling for one verification round
+// (Whisper-Flash section 3.1 and appendix A.4).
+//
+// Candidate i (drawn by the drafter from q_i) is accepted when
+// u * q_i(y) < p_i(y), u uniform on [0, 1) — the same as accepting with
+// probability min(1, p_i(y) / q_i(y)). p_i = softmax(z_i / T) in fp32 with
+// suppressed ids at probability 0. At the first rejection the next token is
+// drawn from the normalised residual (p_i - q_i)+, and after a fully accepted
+// block a bonus token is drawn from the next row's p. Draws use the inverse
+// CDF in ascending id order. An accepted EOS ends the request with no bonus;
+// the output budget works as in greedy decoding.
+//
+// Uniforms come from Philox4x64-10 (Salmon et al., SC'11) with key
+// (seed, 0) and counter (request, step, position, stream): the top 24 bits
+// of the first output word times 2^-24, exact in fp32.
+//
+// One 1024-thread workgroup per request walks the candidate rows in order;
+// row statistics (max, sum of exp) and the residual's segment sums are block
+// reductions in a fixed order.
+#include "wf_device.h"
+#include "wf_internal.h"
+#include "../../include/wf.h"
+
+namespace wf {
+
+namespace {
+
+constexpr int NT = 1024;
+constexpr uint64_t PM0 = 0xD2E7470EE14C6C93ull;
+constexpr uint64_t PM1 = 0xCA5A826395121157ull;
+constexpr uint64_t PW0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t PW1 = 0xBB67AE8584CAA73Bull;
+constexpr int STREAM_ACCEPT = 0;
+constexpr int STREAM_RESAMPLE = 1;
+
+__device__ uint64_t philox_word0(uint64_t c0, uint64_t c1, uint64_t c2, uint64_t c3,
+                                 uint64_t k0, uint64_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += PW0;
+            k1 += PW1;
+        }
+        const uint64_t hi0 = __umul64hi(PM0, c0), lo0 = PM0 * c0;
+        const uint64_t hi1 = __umul64hi(PM1, c2), lo1 = PM1 * c2;
+        const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+    }
+    return c0;
+}
+
+__device__ float uniform24(uint64_t seed, int req, int step, int pos, int stream) {
+    const uint64_t w = philox_word0((uint64_t)(uint32_t)req, (uint64_t)(uint32_t)step,
+                                    (uint64_t)(uint32_t)pos, (uint64_t)stream, seed, 0);
+    return (float)(w >> 40) * 5.9604644775390625e-08f;   // 2^-24
+}
+
+// Block reductions over NT threads (fixed order: waves, then wave 0 over
+// the per-wave results).
+__device__ float block_max(float v, float *sh) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float x = threadIdx.x < NT / 64 ? sh[threadIdx.x] : -INFINITY;
+        x = wave_max(x);
+        if (threadIdx.x == 0) sh[NT / 64] = x;
+    }
+    __syncthreads();
+    const float r = sh[NT / 64];
+    __syncthreads();
+    return r;
+}
+__device__ float block_sum(float v, float *sh) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float x = threadIdx.x < NT / 64 ? sh[threadIdx.x] : 0.f;
+        x = wave_sum(x);
+        if (threadIdx.x == 0) sh[NT / 64] = x;
+    }
+    __syncthreads();
+    const float r = sh[NT / 64];
+    __syncthreads();
+    return r;
+}
+
+struct RowStats {
+    float m, s;   // max of z over unsuppressed ids, sum of exp(z - m)
+};
+
+__device__ __forceinline__ float zval(const float *row, int v, float T, const uint8_t *sup) {
+    if (sup && sup[v]) return -INFINITY;
+    return row[v] / T;
+}
+
+__device__ RowStats row_stats(const float *row, int V, float T, const uint8_t *sup, float *sh) {
+    float m = -INFINITY;
+    for (int v = threadIdx.x; v < V; v += NT) m = fmaxf(m, zval(row, v, T, sup));
+    m = block_max(m, sh);
+    float s = 0.f;
+    for (int v = threadIdx.x; v < V; v += NT) {
+        const float z = zval(row, v, T, sup);
+        s += (z == -INFINITY) ? 0.f : expf(z - m);
+    }
+    s = block_sum(s, sh);
+    return RowStats{m, s};
+}
+
+__device__ __forceinline__ float prob(const float *row, int v, float T, const uint8_t *sup,
+                                      const RowStats &st) {
+    const float z = zval(row, v, T, sup);
+    return (z == -INFINITY) ? 0.f : expf(z - st.m) / st.s;
+}
+
+// Inverse CDF in ascending id order over weights w_v (p_v, or (p_v - q_v)+):
+// the smallest v with cumsum_v > u * total. Each thread owns a contiguous
+// segment; segment sums are scanned in order through LDS.
+template <bool RESID>
+__device__ int icdf(const float *row, const float *qrow, int V, float T, const uint8_t *sup,
+                    const RowStats &st, float u, float *sh, float *seg, int *found) {
+    const int seglen = (V + NT - 1) / NT;
+    const int v0 = threadIdx.x * seglen;
+    const int v1 = min(v0 + seglen, V);
+    auto weight = [&](int v) -> float {
+        const float p = prob(row, v, T, sup, st);
+        if constexpr (RESID) return fmaxf(p - qrow[v], 0.f);
+        return p;
+    };
+    float local = 0.f;
+    for (int v = v0; v < v1; ++v) local += weight(v);
+    seg[threadIdx.x] = local;
+    if (threadIdx.x == 0) *found = 0x7fffffff;
+    __syncthreads();
+    if (threadIdx.x == 0) {               // exclusive prefix over segments, in order
+        float acc = 0.f;
+        for (int t = 0; t < NT; ++t) {
+            const float x = seg[t];
+            seg[t] = acc;
+            acc += x;
+        }
+        sh[NT / 64 + 1] = acc;
+    }
+    __syncthreads();
+    const float total = sh[NT / 64 + 1];
+    const float thr = u * total;
+    float c = seg[threadIdx.x];
+    if (c <= thr && v0 < v1) {
+        for (int v = v0; v < v1; ++v) {
+            c += weight(v);
+            if (c > thr) {
+                atomicMin(found, v);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    int r = *found;
+    __syncthreads();
+    if (r == 0x7fffffff) {                // rounding put thr at or past the end
+        int last = -1;
+        for (int v = threadIdx.x; v < V; v += NT)
+            if (weight(v) > 0.f) last = max(last, v);
+        if (threadIdx.x == 0) *found = -1;
+        __syncthreads();
+        atomicMax(found, last);
+        __syncthreads();
+        r = *found;
+        __syncthreads();
+    }
+    return r;
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
+    __shared__ float sh[NT / 64 + 2];
+    __shared__ float seg[NT];
+    __shared__ int found;
+    const int b = blockIdx.x;
+    const int nt = a.n_tok[b];
+    int n_acc = 0, next = -1, n_emit = 0, done = 0;
+    if (nt > 0) {
+        const int k = nt - 1;
+        const int R = a.budget[b];
+        const int32_t *tok = a.tokens + (size_t)b * a.T;
+        bool ok = !(R < 1 || k > R - 1 || nt > a.T);
+        for (int i = 1; ok && i <= k; ++i)
+            if (tok[i] < 0 || tok[i] >= a.V) ok = false;
+        if (!ok) {
+            n_acc = -1;
+            done = 1;
+        } else {
+            const int req = a.request_id[b], step = a.step[b];
+            const float T = a.temperature;
+            int acc = 0;
+            bool stopped = false;
+            for (int i = 0; i < k && !stopped; ++i) {
+                const float *row = a.logits + ((size_t)b * a.T + i) * a.V;
+                const float *qrow = a.q + ((size_t)b * (a.T - 1) + i) * a.V;
+                const RowStats st = row_stats(row, a.V, T, a.suppress, sh);
+                const int y = tok[i + 1];
+                const float py = prob(row, y, T, a.suppress, st);
+                const float qy = qrow[y];
+                const float u = uniform24(a.seed, req, step, i, STREAM_ACCEPT);
+                if (u * qy < py) {
+                    acc = i + 1;
+                    if (y == a.eos) {          // accepted EOS: finished, no bonus
+                        n_emit = acc;
+                        done = 1;
+                        stopped = true;
+                    }
+                    continue;
+                }
+                // first rejection: draw from (p - q)+, or p when that is all zero
+                const float ur = uniform24(a.seed, req, step, i, STREAM_RESAMPLE);
+                float rs = 0.f;
+                for (int v = threadIdx.x; v < a.V; v += NT)
+                    rs += fmaxf(prob(row, v, T, a.suppress, st) - qrow[v], 0.f);
+                rs = block_sum(rs, sh);
+                const int c = rs > 0.f
+                    ? icdf<true>(row, qrow, a.V, T, a.suppress, st, ur, sh, seg, &found)
+                    : icdf<false>(row, qrow, a.V, T, a.suppress, st, ur, sh, seg, &found);
+                next = c;
+                n_emit = acc + 1;
+                done = (c == a.eos) || (acc + 1 >= R) || c < 0;
+                stopped = true;
+            }
+            if (!stopped) {                    // every candidate accepted: bonus from row k
+                const float *row = a.logits + ((size_t)b * a.T + k) * a.V;
+                const RowStats st = row_stats(row, a.V, T, a.suppress, sh);
+                const float ub = uniform24(a.seed, req, step, k, STREAM_RESAMPLE);
+                const int c = icdf<false>(row, nullptr, a.V, T, a.suppress, st, ub, sh, seg, &found);
+                next = c;
+                n_emit = acc + 1;
+                done = (c == a.eos) || (acc + 1 >= R) || c < 0;
+            }
+            n_acc = acc;
+        }
+    }
+    if (threadIdx.x == 0) {
+        a.n_acc[b] = n_acc;
+        a.next_token[b] = next;
+        a.n_emit[b] = n_emit;
+        a.done[b] = done;
+    }
+}
+
+hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(accept_sample_kernel, dim3(a.n), dim3(NT), 0, st, a);
+    return hipGetLastError();
+}
+
+}  // namespace wf

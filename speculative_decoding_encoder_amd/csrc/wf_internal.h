@@ -137,6 +137,7 @@ hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t s
 hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st);
 hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
+hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st);
 hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st);  // n_acc = new lengths
 hipError_t launch_reset(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,
