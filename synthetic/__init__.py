@@ -34,8 +34,13 @@ __all__ = [
     "ModelShape", "Workload", "WORKLOADS", "TINY", "LARGE_V3", "TURBO",
     "rng", "f32_to_bf16_bits", "bf16_bits_to_f32", "make_weights",
     "make_encoder_out", "make_prefixes", "make_draft_table", "LAYER_TENSORS",
-    "GLOBAL_TENSORS", "layer_tensor_shapes", "global_tensor_shapes",
+    "GLOBAL_TENSORS", "layer_tensor_shapes", "global_tensor_shapes", "make_drafter_weights",
+    "DRAFTER_TAPS",
 ]
+
+# residual streams of these target blocks (zero-based) feed the drafter's
+# history (Whisper-Flash App. A.2)
+DRAFTER_TAPS = (1, 8, 15, 22, 29)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -221,3 +226,23 @@ def make_draft_table(wl: Workload, request: int, p_keep: Optional[float] = None)
     keep = g.random(n) < p
     repl = g.integers(0, wl.shape.vocab, size=n).astype(np.int32)
     return keep, repl
+
+
+def make_drafter_weights(shape: ModelShape, cfg_id: int, n_layers: int = 2, n_taps: int = 5,
+                         ln_random: bool = False) -> Dict[str, np.ndarray]:
+    """Random-init parallel drafter (bf16 bits): ``"D<l>.<name>"`` layers with
+    the target block's tensors (including its own cross K/V projections),
+    ``w_hist`` [d, n_taps*d] (history projection, no bias), ``mask`` [d]
+    (the learned mask vector) and its final norm ``lnd_g`` / ``lnd_b``."""
+    out: Dict[str, np.ndarray] = {}
+    ls = layer_tensor_shapes(shape)
+    for l in range(n_layers):
+        for name in LAYER_TENSORS:
+            out[f"D{l}.{name}"] = _ln_or_weight(cfg_id, 200 + l, name, ls[name], ln_random)
+    d = shape.d_model
+    out["w_hist"] = _draw(cfg_id, 30001, (d, n_taps * d), 0.02)
+    out["mask"] = _draw(cfg_id, 30002, (d,), 0.02)
+    out["lnd_g"] = _ln_or_weight(cfg_id, None, "lnf_g", (d,), ln_random) if not ln_random \
+        else _draw(cfg_id, 30003, (d,), 0.1, 1.0)
+    out["lnd_b"] = np.zeros((d,), np.uint16) if not ln_random else _draw(cfg_id, 30004, (d,), 0.1)
+    return out
