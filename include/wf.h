@@ -100,6 +100,12 @@ typedef struct {
     int32_t n_pages;      /* physical pages in the KV pool */
     int32_t eos_id;       /* end-of-transcript token id */
     float ln_eps;         /* layer-norm epsilon (1e-5) */
+    /* Parallel drafter (Whisper-Flash section 3.2, appendix A.2); 0 layers
+     * disables it. History features are the residual streams after target
+     * blocks tap_layers[0..n_taps) (zero-based, before the final LN). */
+    int32_t drafter_layers;   /* 0 or the number of drafter blocks (2) */
+    int32_t n_taps;           /* 5 */
+    int32_t tap_layers[8];    /* 1, 8, 15, 22, 29 for large-v3 */
 } wf_config;
 
 /* Per-layer weights: bf16, PyTorch Linear convention (weight [out, in],
@@ -115,18 +121,30 @@ typedef struct {
     const void *w2, *b2;                          /* [d, d_ffn], [d] */
 } wf_layer_weights;
 
+/* Drafter weights (bf16). Each drafter block has the target block's
+ * tensors, including its own cross-attention K/V projections. */
+typedef struct {
+    const wf_layer_weights *layers; /* host array of drafter_layers entries (copied) */
+    const void *w_hist;             /* [d, n_taps * d], history projection, no bias */
+    const void *mask_emb;           /* [d], the learned mask vector */
+    const void *lnd_g, *lnd_b;      /* the drafter's final layer norm */
+} wf_drafter_weights;
+
 typedef struct {
     const void *tok_emb;   /* [vocab, d]; also the LM head */
     const void *pos_emb;   /* [n_ctx, d] learned positions */
     const void *lnf_g, *lnf_b;
     const wf_layer_weights *layers; /* host array of n_layers entries (copied) */
+    const wf_drafter_weights *drafter; /* NULL unless drafter_layers > 0 */
 } wf_weights;
 
 /* Sizes of the caller-allocated device buffers for a configuration.
- * kv_pool:  fp16 [n_layers][n_pages][2][n_heads][page_size][head_dim]
- *           (the V half of a page is stored transposed, [head_dim][page_size]).
- * xkv_pool: fp16 per slot, per layer: K [n_heads][F_pad][head_dim] then
- *           V [n_heads][head_dim][F_pad], F_pad = n_frames rounded up to 32.
+ * kv_pool:  fp16 [n_layers + drafter_layers][n_pages][2][n_heads][page_size][head_dim]
+ *           (the V half of a page is stored transposed, [head_dim][page_size]);
+ *           the drafter's layers hold its history keys (rotated) and values.
+ * xkv_pool: fp16 per slot, per layer (target layers, then drafter layers):
+ *           K [n_heads][F_pad][head_dim] then V [n_heads][head_dim][F_pad],
+ *           F_pad = n_frames rounded up to 32.
  *           Must be zero-filled before the first wf_encode_kv.
  * workspace: engine-private scratch and slot state.
  * Return 0 for an invalid configuration. */
@@ -154,7 +172,7 @@ wf_status wf_reset(wf_engine *e, int32_t n, const int32_t *d_slots, void *stream
 
 /* Write-once cross K/V for n slots from the audio memory d_enc, bf16
  * [n][n_frames][d_model]:  K_c = enc Wkc^T,  V_c = enc Wvc^T + bvc,  for every
- * layer. */
+ * target layer and every drafter layer. */
 wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots,
                        const void *d_enc, void *stream);
 
@@ -170,11 +188,30 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots,
  * d_argmax int32 [n][T]: the target's choice for the position after each
  *   row (largest logit, lowest id on ties); -1 for skipped rows.
  * d_logits: NULL, or fp32 [n][T][vocab] logits.
+ * With a drafter, the pass also projects the tapped residual streams of the
+ * rows it writes into the cache and appends them to the drafter history at
+ * the same positions (so the history always covers the cache length).
  * Requires n <= max_batch, n*T <= max_rows, 1 <= T <= n_ctx. */
 wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
                           const int32_t *d_tokens, int32_t T,
                           const int32_t *d_n_tok, int32_t *d_argmax,
                           float *d_logits, void *stream);
+
+/* Parallel drafter pass (Whisper-Flash section 3.2, eq. 2; appendix A.2):
+ * for each request the block [Emb(anchor), m, ..., m] (K mask copies) at
+ * text positions L..L+K, L = the slot's cache length, goes through the
+ * drafter blocks: one softmax over the history (positions < L) and the
+ * block (bidirectional), RoPE (base 10000, fp32 phases) on queries and keys,
+ * cross-attention to the drafter's own audio K/V, the MLP; then the
+ * drafter's final LN and the shared head. Mask row i proposes the token at
+ * position L+i (argmax, lowest id on ties).
+ * d_anchor int32 [n]; d_block int32 [n][K+1] receives the anchor followed
+ * by the K drafts, ready for wf_verify_block; d_logits: NULL or fp32
+ * [n][K+1][vocab] drafter logits (row 0 is the anchor row). The slot must not be pending;
+ * its length is unchanged. Requires drafter_layers > 0, 1 <= K,
+ * n*(K+1) <= max_rows. */
+wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_anchor,
+                   int32_t K, int32_t *d_block, float *d_logits, void *stream);
 
 /* Acceptance for one round, per request b with k = n_tok[b] - 1 candidates
  * and R = d_budget[b] output tokens left (k <= R - 1 is required).
@@ -224,7 +261,8 @@ wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *st
  * projections + residual, 2 cross-attention query, 3 fc1 + GELU,
  * 4 fc2 + residual, 5 tied LM head + argmax, 6 self-attention,
  * 7 cross-attention, 8 everything else (embed, layer norms, argmax merge,
- * accept, rollback), 9 write-once cross K/V. */
+ * accept, rollback), 9 write-once cross K/V, 10 drafter pass, 11 drafter
+ * history append inside the verify pass. */
 wf_status wf_set_timing(wf_engine *e, int32_t enable);
 wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count);
 

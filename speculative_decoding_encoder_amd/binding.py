@@ -29,7 +29,9 @@ class WFError(RuntimeError):
 class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_heads", "head_dim", "d_ffn", "vocab", "n_frames", "n_ctx",
-        "max_batch", "max_rows", "page_size", "n_pages", "eos_id")] + [("ln_eps", ctypes.c_float)]
+        "max_batch", "max_rows", "page_size", "n_pages", "eos_id")] + [
+        ("ln_eps", ctypes.c_float), ("drafter_layers", ctypes.c_int32),
+        ("n_taps", ctypes.c_int32), ("tap_layers", ctypes.c_int32 * 8)]
 
 
 LAYER_FIELDS = ["ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
@@ -41,10 +43,17 @@ class LayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in LAYER_FIELDS]
 
 
+class DrafterWeights(ctypes.Structure):
+    _fields_ = [("layers", ctypes.POINTER(LayerWeights)), ("w_hist", ctypes.c_void_p),
+                ("mask_emb", ctypes.c_void_p), ("lnd_g", ctypes.c_void_p),
+                ("lnd_b", ctypes.c_void_p)]
+
+
 class Weights(ctypes.Structure):
     _fields_ = [("tok_emb", ctypes.c_void_p), ("pos_emb", ctypes.c_void_p),
                 ("lnf_g", ctypes.c_void_p), ("lnf_b", ctypes.c_void_p),
-                ("layers", ctypes.POINTER(LayerWeights))]
+                ("layers", ctypes.POINTER(LayerWeights)),
+                ("drafter", ctypes.POINTER(DrafterWeights))]
 
 
 def header_functions() -> list:
@@ -79,6 +88,7 @@ def load():
         "wf_accept": (I32, [P, I32, P, I32, P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64,
                             P, P, P, P, P, P, P]),
         "wf_rollback": (I32, [P, I32, P, P, P]),
+        "wf_draft": (I32, [P, I32, P, P, I32, P, P, P]),
         "wf_truncate": (I32, [P, I32, P, P, P]),
         "wf_device_state": (I32, [P, P, P, P]),
         "wf_set_timing": (I32, [P, I32]),
@@ -110,14 +120,17 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def make_config(shape, max_batch: int, max_rows: int, n_pages: Optional[int] = None) -> Config:
+def make_config(shape, max_batch: int, max_rows: int, n_pages: Optional[int] = None,
+                drafter_layers: int = 0, taps: Sequence[int] = ()) -> Config:
     pps = shape.n_ctx // 16
+    tl = (ctypes.c_int32 * 8)(*list(taps)[:8])
     return Config(n_layers=shape.n_layers, d_model=shape.d_model, n_heads=shape.n_heads,
                   head_dim=shape.head_dim, d_ffn=shape.d_ffn, vocab=shape.vocab,
                   n_frames=shape.n_frames, n_ctx=shape.n_ctx, max_batch=max_batch,
                   max_rows=max_rows, page_size=16,
                   n_pages=n_pages if n_pages is not None else max_batch * pps,
-                  eos_id=shape.eos_id, ln_eps=shape.ln_eps)
+                  eos_id=shape.eos_id, ln_eps=shape.ln_eps, drafter_layers=drafter_layers,
+                  n_taps=len(taps), tap_layers=tl)
 
 
 def workspace_bytes(cfg: Config) -> int:
@@ -134,16 +147,21 @@ class Engine:
 
     def __init__(self, shape, weights_bits: Dict[str, np.ndarray], max_batch: int,
                  max_rows: int, page_table: Optional[np.ndarray] = None,
-                 n_pages: Optional[int] = None):
+                 n_pages: Optional[int] = None,
+                 drafter_bits: Optional[Dict[str, np.ndarray]] = None,
+                 taps: Sequence[int] = ()):
         import torch
         self.torch = torch
         self.lib = load()
         self.shape = shape
         self.dev = torch.device("cuda", torch.cuda.current_device())
-        self.cfg = make_config(shape, max_batch, max_rows, n_pages)
+        n_dl = 0
+        if drafter_bits is not None:
+            n_dl = len({k.split(".")[0] for k in drafter_bits if k.startswith("D")})
+        self.cfg = make_config(shape, max_batch, max_rows, n_pages, n_dl, taps)
         pps = shape.n_ctx // 16
         self.w = {}
-        for k, v in weights_bits.items():
+        for k, v in list(weights_bits.items()) + list((drafter_bits or {}).items()):
             t = torch.from_numpy(np.ascontiguousarray(v).view(np.int16))
             self.w[k] = t.to(self.dev).view(torch.bfloat16)
         lw = (LayerWeights * shape.n_layers)()
@@ -151,8 +169,19 @@ class Engine:
             for f in LAYER_FIELDS:
                 setattr(lw[l], f, self.w[f"L{l}.{f}"].data_ptr())
         self._lw = lw
+        dptr = None
+        if n_dl:
+            dlw = (LayerWeights * n_dl)()
+            for l in range(n_dl):
+                for f in LAYER_FIELDS:
+                    setattr(dlw[l], f, self.w[f"D{l}.{f}"].data_ptr())
+            self._dlw = dlw
+            self._dw = DrafterWeights(dlw, self.w["w_hist"].data_ptr(),
+                                      self.w["mask"].data_ptr(), self.w["lnd_g"].data_ptr(),
+                                      self.w["lnd_b"].data_ptr())
+            dptr = ctypes.pointer(self._dw)
         self._weights = Weights(self.w["tok_emb"].data_ptr(), self.w["pos_emb"].data_ptr(),
-                                self.w["lnf_g"].data_ptr(), self.w["lnf_b"].data_ptr(), lw)
+                                self.w["lnf_g"].data_ptr(), self.w["lnf_b"].data_ptr(), lw, dptr)
         cfgp = ctypes.byref(self.cfg)
         kvb = int(self.lib.wf_kv_pool_bytes(cfgp))
         xkvb = int(self.lib.wf_xkv_pool_bytes(cfgp))
@@ -210,6 +239,10 @@ class Engine:
         _check(self.lib.wf_rollback(self.h, slots.numel(), _p(slots), _p(n_acc),
                                     _stream(stream)), "wf_rollback")
 
+    def wf_draft(self, slots, anchor, K, block, logits=None, stream=None):
+        _check(self.lib.wf_draft(self.h, slots.numel(), _p(slots), _p(anchor), int(K), _p(block),
+                                 _p(logits), _stream(stream)), "wf_draft")
+
     def wf_truncate(self, slots, lens, stream=None):
         _check(self.lib.wf_truncate(self.h, slots.numel(), _p(slots), _p(lens),
                                     _stream(stream)), "wf_truncate")
@@ -241,4 +274,4 @@ class Engine:
 
 
 TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn", "cross_attn",
-                "other", "encode_kv"]
+                "other", "encode_kv", "draft", "history"]

@@ -56,8 +56,11 @@ void cross_chunks(int n, int H, int F, int &cf, int &nch) {
     nch = cdiv(F, cf);
 }
 
+int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
+
 struct Layout {
     size_t x, xs, hs, q, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
+    size_t taps, dam;
     size_t total;
     size_t part_bytes, xapart_bytes;
     int n_vtiles;
@@ -79,6 +82,13 @@ bool config_ok(const wf_config *c, std::string *why) {
     if (c->n_pages < 1) return bad("n_pages < 1");
     if (c->eos_id < 0 || c->eos_id >= c->vocab) return bad("eos_id outside the vocabulary");
     if (!(c->ln_eps > 0.f)) return bad("ln_eps must be > 0");
+    if (c->drafter_layers < 0 || c->drafter_layers > 8) return bad("drafter_layers outside [0, 8]");
+    if (c->drafter_layers > 0) {
+        if (c->n_taps < 1 || c->n_taps > 8) return bad("n_taps outside [1, 8]");
+        for (int j = 0; j < c->n_taps; ++j)
+            if (c->tap_layers[j] < 0 || c->tap_layers[j] >= c->n_layers)
+                return bad("tap layer outside the decoder");
+    }
     return true;
 }
 
@@ -115,6 +125,8 @@ Layout layout_of(const wf_config *c) {
     L.len = take((size_t)c->max_batch * 4);
     L.pend = take((size_t)c->max_batch * 4);
     L.err = take((size_t)c->max_batch * 4);
+    L.taps = take(c->drafter_layers > 0 ? M * (size_t)c->n_taps * d * 4 : 0);
+    L.dam = take(M * 4);
     L.total = o;
     return L;
 }
@@ -123,7 +135,7 @@ int f_pad_of(const wf_config *c) { return cdiv(c->n_frames, 32) * 32; }
 
 enum TimingKind {
     TK_QKV = 0, TK_OPROJ = 1, TK_QC = 2, TK_FC1 = 3, TK_FC2 = 4, TK_LMHEAD = 5,
-    TK_SELF = 6, TK_CROSS = 7, TK_OTHER = 8, TK_XKV = 9, TK_N = 10
+    TK_SELF = 6, TK_CROSS = 7, TK_OTHER = 8, TK_XKV = 9, TK_DRAFT = 10, TK_HIST = 11, TK_N = 12
 };
 
 }  // namespace
@@ -134,6 +146,10 @@ struct wf_engine {
     int F_pad, pt_stride, page_elems;
     const uint16_t *tok_emb, *pos_emb, *lnf_g, *lnf_b;
     std::vector<LayerW> layers;
+    std::vector<LayerW> dlayers;            // drafter blocks
+    const uint16_t *w_hist, *mask_emb, *lnd_g, *lnd_b;
+    uint16_t *taps;                         // split-bf16 [max_rows][n_taps*d]
+    int32_t *dam;                           // drafter argmax [max_rows]
     uint16_t *kv, *xkv;
     size_t kv_layer_elems, xkv_slot_elems, xkv_layer_elems;
     const int32_t *pt;
@@ -241,12 +257,12 @@ extern "C" {
 
 size_t wf_kv_pool_bytes(const wf_config *c) {
     if (!config_ok(c, nullptr)) return 0;
-    return (size_t)c->n_layers * c->n_pages * 2 * c->n_heads * c->page_size * c->head_dim * 2;
+    return (size_t)all_layers(c) * c->n_pages * 2 * c->n_heads * c->page_size * c->head_dim * 2;
 }
 
 size_t wf_xkv_pool_bytes(const wf_config *c) {
     if (!config_ok(c, nullptr)) return 0;
-    return (size_t)c->max_batch * c->n_layers * 2 * c->n_heads * f_pad_of(c) * c->head_dim * 2;
+    return (size_t)c->max_batch * all_layers(c) * 2 * c->n_heads * f_pad_of(c) * c->head_dim * 2;
 }
 
 size_t wf_workspace_bytes(const wf_config *c) {
@@ -273,6 +289,19 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
         for (const void *p : ps)
             if (!p) return fail(WF_EINVAL, "null weight pointer in layer %d", l);
     }
+    if (cfg->drafter_layers > 0) {
+        const wf_drafter_weights *dw = w->drafter;
+        if (!dw || !dw->layers || !dw->w_hist || !dw->mask_emb || !dw->lnd_g || !dw->lnd_b)
+            return fail(WF_EINVAL, "null drafter weight pointer");
+        for (int l = 0; l < cfg->drafter_layers; ++l) {
+            const wf_layer_weights &L = dw->layers[l];
+            const void *ps[] = {L.ln1_g, L.ln1_b, L.wq, L.bq, L.wk, L.wv, L.bv, L.wo, L.bo,
+                                L.ln2_g, L.ln2_b, L.wqc, L.bqc, L.wkc, L.wvc, L.bvc, L.woc, L.boc,
+                                L.ln3_g, L.ln3_b, L.w1, L.b1, L.w2, L.b2};
+            for (const void *p : ps)
+                if (!p) return fail(WF_EINVAL, "null weight pointer in drafter layer %d", l);
+        }
+    }
     if (!kv_pool || !xkv_pool || !d_page_table || !workspace)
         return fail(WF_EINVAL, "null pool, page table or workspace");
     if (kv_bytes < wf_kv_pool_bytes(cfg)) return fail(WF_ECAPACITY, "kv_pool too small");
@@ -296,11 +325,8 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->pos_emb = (const uint16_t *)w->pos_emb;
     e->lnf_g = (const uint16_t *)w->lnf_g;
     e->lnf_b = (const uint16_t *)w->lnf_b;
-    e->layers.resize(cfg->n_layers);
-    for (int l = 0; l < cfg->n_layers; ++l) {
-        const wf_layer_weights &s = w->layers[l];
-        LayerW &t = e->layers[l];
-        t = LayerW{(const uint16_t *)s.ln1_g, (const uint16_t *)s.ln1_b, (const uint16_t *)s.wq,
+    auto conv = [](const wf_layer_weights &s) {
+        return LayerW{(const uint16_t *)s.ln1_g, (const uint16_t *)s.ln1_b, (const uint16_t *)s.wq,
                    (const uint16_t *)s.bq,    (const uint16_t *)s.wk,    (const uint16_t *)s.wv,
                    (const uint16_t *)s.bv,    (const uint16_t *)s.wo,    (const uint16_t *)s.bo,
                    (const uint16_t *)s.ln2_g, (const uint16_t *)s.ln2_b, (const uint16_t *)s.wqc,
@@ -308,12 +334,24 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
                    (const uint16_t *)s.bvc,   (const uint16_t *)s.woc,   (const uint16_t *)s.boc,
                    (const uint16_t *)s.ln3_g, (const uint16_t *)s.ln3_b, (const uint16_t *)s.w1,
                    (const uint16_t *)s.b1,    (const uint16_t *)s.w2,    (const uint16_t *)s.b2};
+    };
+    e->layers.resize(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers; ++l) e->layers[l] = conv(w->layers[l]);
+    e->w_hist = e->mask_emb = e->lnd_g = e->lnd_b = nullptr;
+    if (cfg->drafter_layers > 0) {
+        const wf_drafter_weights *dw = w->drafter;
+        e->dlayers.resize(cfg->drafter_layers);
+        for (int l = 0; l < cfg->drafter_layers; ++l) e->dlayers[l] = conv(dw->layers[l]);
+        e->w_hist = (const uint16_t *)dw->w_hist;
+        e->mask_emb = (const uint16_t *)dw->mask_emb;
+        e->lnd_g = (const uint16_t *)dw->lnd_g;
+        e->lnd_b = (const uint16_t *)dw->lnd_b;
     }
     e->kv = (uint16_t *)kv_pool;
     e->xkv = (uint16_t *)xkv_pool;
     e->kv_layer_elems = (size_t)cfg->n_pages * e->page_elems;
     e->xkv_layer_elems = (size_t)2 * cfg->n_heads * e->F_pad * cfg->head_dim;
-    e->xkv_slot_elems = (size_t)cfg->n_layers * e->xkv_layer_elems;
+    e->xkv_slot_elems = (size_t)all_layers(cfg) * e->xkv_layer_elems;
     e->pt = d_page_table;
     char *ws = (char *)workspace;
     const Layout &L = e->lay;
@@ -333,6 +371,8 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->len = (int32_t *)(ws + L.len);
     e->pend = (int32_t *)(ws + L.pend);
     e->err = (int32_t *)(ws + L.err);
+    e->taps = (uint16_t *)(ws + L.taps);
+    e->dam = (int32_t *)(ws + L.dam);
     if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         delete e;
         return fail(WF_EHIP, "clearing the workspace failed");
@@ -365,8 +405,8 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
     const long long M = (long long)n * c.n_frames;
     if (M > 0x7fffffffLL / 2) return fail(WF_ECAPACITY, "too many frames");
     hipStream_t st = (hipStream_t)stream;
-    for (int l = 0; l < c.n_layers; ++l) {
-        const LayerW &w = e->layers[l];
+    for (int l = 0; l < all_layers(&c); ++l) {
+        const LayerW &w = l < c.n_layers ? e->layers[l] : e->dlayers[l - c.n_layers];
         EpiArgs ea{};
         ea.b0 = nullptr;
         ea.b1 = w.bvc;
@@ -385,6 +425,137 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
     return WF_OK;
 }
 
+namespace {
+
+// Frame chunking of the cross-attention for n requests and mt row tiles.
+void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &nch) {
+    const wf_config &c = e->c;
+    const int H = c.n_heads, hd = c.head_dim;
+    cross_chunks(n, H, c.n_frames, cf, nch);
+    const size_t rowbytes = (size_t)16 * (hd + 2) * 4;
+    if (nch > 1 && (size_t)n * H * mt * nch * rowbytes > e->lay.xapart_bytes) {
+        // long prefill blocks: fewer, longer chunks so the partials fit
+        const size_t fit = e->lay.xapart_bytes / ((size_t)n * H * mt * rowbytes);
+        const int steps = cdiv(c.n_frames, 32);
+        const int want = fit < 1 ? 1 : (fit > 16 ? 16 : (int)fit);
+        cf = cdiv(steps, want) * 32;
+        nch = cdiv(c.n_frames, cf);
+    }
+}
+
+struct Pass {
+    int n, T, M, mt, cf, nch;
+    const int32_t *slots;
+    int kind;   // -1: per-kernel kinds; else every launch is timed under this kind
+};
+
+int K_(const Pass &p, int k) { return p.kind < 0 ? k : p.kind; }
+
+// Self-attention output projection, cross-attention sublayer and MLP sublayer
+// of one block (target layer or drafter layer); xkv_layer indexes the
+// write-once pool.
+wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const Pass &p,
+                            hipStream_t st) {
+    const wf_config &c = e->c;
+    const int M = p.M, d = c.d_model, H = c.n_heads, hd = c.head_dim;
+    EpiArgs ra{};
+    ra.b0 = w.bo;
+    ra.x = e->x;
+    WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.wo, nullptr, nullptr, d, d, ra,
+                    st));
+    WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
+    EpiArgs fa{};
+    fa.b0 = w.bqc;
+    fa.out = e->q;
+    WF_TRY(run_gemm(e, K_(p, TK_QC), ROLE_CROSS_Q, e->xs, M, d, w.wqc, nullptr, nullptr, d, d, fa,
+                    st));
+    CrossAttnArgs ca{};
+    ca.q = e->q;
+    ca.xkv = e->xkv;
+    ca.slot_stride = (int64_t)e->xkv_slot_elems;
+    ca.layer_off = (int64_t)xkv_layer * e->xkv_layer_elems;
+    ca.slots = p.slots;
+    ca.req_ntok = e->reqN;
+    ca.n = p.n;
+    ca.T = p.T;
+    ca.H = H;
+    ca.d = d;
+    ca.F = c.n_frames;
+    ca.F_pad = e->F_pad;
+    ca.mt = p.mt;
+    ca.nch = p.nch;
+    ca.cf = p.cf;
+    ca.n_items = p.n * H * p.mt * p.nch;
+    ca.scale = 1.0f / std::sqrt((float)hd);
+    ca.part = e->xapart;
+    ca.cnt = e->xacnt;
+    ca.out = e->xs;
+    WF_TRY(timed(e, K_(p, TK_CROSS), st, [&] { return launch_cross_attn(ca, hd, st); }));
+    EpiArgs oa{};
+    oa.b0 = w.boc;
+    oa.x = e->x;
+    WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.woc, nullptr, nullptr, d, d, oa,
+                    st));
+    WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
+    EpiArgs ga{};
+    ga.b0 = w.b1;
+    ga.out = e->hs;
+    WF_TRY(run_gemm(e, K_(p, TK_FC1), ROLE_FC1, e->xs, M, d, w.w1, nullptr, nullptr, c.d_ffn,
+                    c.d_ffn, ga, st));
+    EpiArgs f2{};
+    f2.b0 = w.b2;
+    f2.x = e->x;
+    WF_TRY(run_gemm(e, K_(p, TK_FC2), ROLE_FC2, e->hs, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
+                    st));
+    return WF_OK;
+}
+
+// Final layer norm, tied LM head with its argmax epilogue, per-row merge.
+wf_status run_head(wf_engine *e, const uint16_t *g, const uint16_t *b, const Pass &p,
+                   float *d_logits, int32_t *d_argmax, hipStream_t st) {
+    const wf_config &c = e->c;
+    WF_TRY(run_ln(e, p.M, g, b, st));
+    EpiArgs la{};
+    la.logits = d_logits;
+    la.tile_max = e->lmmax;
+    la.tile_idx = e->lmidx;
+    la.ld = c.max_rows;
+    WF_TRY(run_gemm(e, K_(p, TK_LMHEAD), ROLE_LM_HEAD, e->xs, p.M, c.d_model, e->tok_emb, nullptr,
+                    nullptr, c.vocab, c.vocab, la, st));
+    LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, p.M, p.T, p.slots, e->reqN,
+                    e->err, d_argmax};
+    return timed(e, K_(p, TK_OTHER), st, [&] { return launch_lm_reduce(lr, st); });
+}
+
+// RoPE of the drafter's projections in the fp32 temporary and append of
+// keys/values at positions L+i (rows i < req_ntok) of drafter layer dl.
+wf_status run_rope_append(wf_engine *e, int dl, const Pass &p, int ncols, int q_off, int k_off,
+                          int v_off, int kind, hipStream_t st) {
+    const wf_config &c = e->c;
+    RopeArgs ra{};
+    ra.tmp = reinterpret_cast<const float *>(e->hs);
+    ra.ncols = ncols;
+    ra.q_off = q_off;
+    ra.k_off = k_off;
+    ra.v_off = v_off;
+    ra.M = p.M;
+    ra.T = p.T;
+    ra.H = c.n_heads;
+    ra.hd = c.head_dim;
+    ra.d = c.d_model;
+    ra.slots = p.slots;
+    ra.req_L = e->reqL;
+    ra.req_ntok = e->reqN;
+    ra.page_table = e->pt;
+    ra.pt_stride = e->pt_stride;
+    ra.page_elems = e->page_elems;
+    ra.kv_layer = e->kv + (size_t)(c.n_layers + dl) * e->kv_layer_elems;
+    ra.q_out = e->q;
+    return timed(e, kind, st, [&] { return launch_rope_append(ra, st); });
+}
+
+}  // namespace
+
 wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
                           const int32_t *d_tokens, int32_t T, const int32_t *d_n_tok,
                           int32_t *d_argmax, float *d_logits, void *stream) {
@@ -396,7 +567,8 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     if ((long long)n * T > c.max_rows) return fail(WF_ECAPACITY, "n*T exceeds max_rows");
     hipStream_t st = (hipStream_t)stream;
     const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
-    const int mt = cdiv(T, 16);
+    Pass p{n, T, M, cdiv(T, 16), 0, 0, d_slots, -1};
+    cross_plan(e, n, p.mt, p.cf, p.nch);
 
     PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
                    d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
@@ -404,22 +576,10 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     EmbedArgs ema{M, T, d, c.vocab, c.n_ctx, d_tokens, e->reqL, e->tok_emb, e->pos_emb, e->x};
     WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_embed(ema, st); }));
 
-    int cf, nch;
-    cross_chunks(n, H, c.n_frames, cf, nch);
-    const size_t rowbytes = (size_t)16 * (hd + 2) * 4;
-    if (nch > 1 && (size_t)n * H * mt * nch * rowbytes > e->lay.xapart_bytes) {
-        // long prefill blocks: fewer, longer chunks so the partials fit
-        const size_t fit = e->lay.xapart_bytes / ((size_t)n * H * mt * rowbytes);
-        const int steps = cdiv(c.n_frames, 32);
-        const int want = fit < 1 ? 1 : (fit > 16 ? 16 : (int)fit);
-        cf = cdiv(steps, want) * 32;
-        nch = cdiv(c.n_frames, cf);
-    }
-
     for (int l = 0; l < c.n_layers; ++l) {
         const LayerW &w = e->layers[l];
         uint16_t *kvl = e->kv + (size_t)l * e->kv_layer_elems;
-        // self-attention sublayer
+        // self-attention sublayer: QKV with the K/V append, causal attention
         WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
         EpiArgs qa{};
         qa.b0 = w.bq;
@@ -437,69 +597,79 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         qa.page_elems = e->page_elems;
         WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
-                        e->page_elems, n, T, H, d, 1.0f / std::sqrt((float)hd), e->xs};
-        WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, mt, st); }));
-        EpiArgs ra{};
-        ra.b0 = w.bo;
-        ra.x = e->x;
-        WF_TRY(run_gemm(e, TK_OPROJ, ROLE_OPROJ, e->xs, M, d, w.wo, nullptr, nullptr, d, d, ra, st));
-        // cross-attention sublayer
-        WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
-        EpiArgs fa{};
-        fa.b0 = w.bqc;
-        fa.out = e->q;
-        WF_TRY(run_gemm(e, TK_QC, ROLE_CROSS_Q, e->xs, M, d, w.wqc, nullptr, nullptr, d, d, fa, st));
-        CrossAttnArgs ca{};
-        ca.q = e->q;
-        ca.xkv = e->xkv;
-        ca.slot_stride = (int64_t)e->xkv_slot_elems;
-        ca.layer_off = (int64_t)l * e->xkv_layer_elems;
-        ca.slots = d_slots;
-        ca.req_ntok = e->reqN;
-        ca.n = n;
-        ca.T = T;
-        ca.H = H;
-        ca.d = d;
-        ca.F = c.n_frames;
-        ca.F_pad = e->F_pad;
-        ca.mt = mt;
-        ca.nch = nch;
-        ca.cf = cf;
-        ca.n_items = n * H * mt * nch;
-        ca.scale = 1.0f / std::sqrt((float)hd);
-        ca.part = e->xapart;
-        ca.cnt = e->xacnt;
-        ca.out = e->xs;
-        WF_TRY(timed(e, TK_CROSS, st, [&] { return launch_cross_attn(ca, hd, st); }));
-        EpiArgs oa{};
-        oa.b0 = w.boc;
-        oa.x = e->x;
-        WF_TRY(run_gemm(e, TK_OPROJ, ROLE_OPROJ, e->xs, M, d, w.woc, nullptr, nullptr, d, d, oa, st));
-        // MLP sublayer
-        WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
-        EpiArgs ga{};
-        ga.b0 = w.b1;
-        ga.out = e->hs;
-        WF_TRY(run_gemm(e, TK_FC1, ROLE_FC1, e->xs, M, d, w.w1, nullptr, nullptr, c.d_ffn,
-                        c.d_ffn, ga, st));
-        EpiArgs f2{};
-        f2.b0 = w.b2;
-        f2.x = e->x;
-        WF_TRY(run_gemm(e, TK_FC2, ROLE_FC2, e->hs, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
-                        st));
+                        e->page_elems, n, T, H, d, 1, 1.0f / std::sqrt((float)hd), e->xs};
+        WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, p.mt, st); }));
+        WF_TRY(run_out_cross_mlp(e, w, l, p, st));
+        // history taps for the drafter (residual stream after this block)
+        for (int j = 0; j < (c.drafter_layers > 0 ? c.n_taps : 0); ++j) {
+            if (c.tap_layers[j] != l) continue;
+            TapArgs ta{e->x, M, d, j, c.n_taps, e->taps};
+            WF_TRY(timed(e, TK_HIST, st, [&] { return launch_tap(ta, st); }));
+        }
     }
-    WF_TRY(run_ln(e, M, e->lnf_g, e->lnf_b, st));
-    EpiArgs la{};
-    la.logits = d_logits;
-    la.tile_max = e->lmmax;
-    la.tile_idx = e->lmidx;
-    la.ld = c.max_rows;
-    WF_TRY(run_gemm(e, TK_LMHEAD, ROLE_LM_HEAD, e->xs, M, d, e->tok_emb, nullptr, nullptr, c.vocab,
-                    c.vocab, la, st));
-    LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, M, T, d_slots, e->reqN,
-                    e->err, d_argmax};
-    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_lm_reduce(lr, st); }));
+    WF_TRY(run_head(e, e->lnf_g, e->lnf_b, p, d_logits, d_argmax, st));
+
+    if (c.drafter_layers > 0) {
+        // drafter history of the rows just written to the cache: h = W_h taps
+        // (into the residual buffer, free after the head), then per drafter
+        // layer k = RoPE(W_k LN1(h)), v = W_v LN1(h) + b_v into its pages
+        EpiArgs ha{};
+        ha.out32 = e->x;
+        WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST, e->taps, M, c.n_taps * d, e->w_hist, nullptr,
+                        nullptr, d, d, ha, st));
+        for (int dl = 0; dl < c.drafter_layers; ++dl) {
+            const LayerW &w = e->dlayers[dl];
+            WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
+            EpiArgs ka{};
+            ka.b1 = w.bv;
+            ka.out32 = reinterpret_cast<float *>(e->hs);
+            WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST_KV, e->xs, M, d, w.wk, w.wv, nullptr, d, 2 * d, ka,
+                            st));
+            WF_TRY(run_rope_append(e, dl, p, 2 * d, -1, 0, d, TK_HIST, st));
+        }
+    }
     return WF_OK;
+}
+
+wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_anchor,
+                   int32_t K, int32_t *d_block, float *d_logits, void *stream) {
+    if (!e || !d_slots || !d_anchor || !d_block) return fail(WF_EINVAL, "null argument");
+    const wf_config &c = e->c;
+    if (c.drafter_layers < 1) return fail(WF_ESTATE, "the engine has no drafter");
+    if (n < 1 || n > c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    if (K < 1 || K + 1 > c.n_ctx) return fail(WF_EINVAL, "K outside [1, n_ctx - 1]");
+    const int T = K + 1;
+    if ((long long)n * T > c.max_rows) return fail(WF_ECAPACITY, "n*(K+1) exceeds max_rows");
+    hipStream_t st = (hipStream_t)stream;
+    const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
+    Pass p{n, T, M, cdiv(T, 16), 0, 0, d_slots, TK_DRAFT};
+    cross_plan(e, n, p.mt, p.cf, p.nch);
+
+    PrepareDraftArgs pa{n, K, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.max_batch, d_slots,
+                        d_anchor, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
+    WF_TRY(timed(e, TK_DRAFT, st, [&] { return launch_prepare_draft(pa, st); }));
+    EmbedDraftArgs ea{M, T, d, c.vocab, d_anchor, e->tok_emb, e->mask_emb, e->x};
+    WF_TRY(timed(e, TK_DRAFT, st, [&] { return launch_embed_draft(ea, st); }));
+    for (int dl = 0; dl < c.drafter_layers; ++dl) {
+        const LayerW &w = e->dlayers[dl];
+        WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
+        EpiArgs qa{};
+        qa.b0 = w.bq;
+        qa.b2 = w.bv;
+        qa.out32 = reinterpret_cast<float *>(e->hs);
+        WF_TRY(run_gemm(e, TK_DRAFT, ROLE_DRAFT_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa,
+                        st));
+        WF_TRY(run_rope_append(e, dl, p, 3 * d, 0, d, 2 * d, TK_DRAFT, st));
+        uint16_t *kvl = e->kv + (size_t)(c.n_layers + dl) * e->kv_layer_elems;
+        SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
+                        e->page_elems, n, T, H, d, 0, 1.0f / std::sqrt((float)hd), e->xs};
+        WF_TRY(timed(e, TK_DRAFT, st, [&] { return launch_self_attn(sa, hd, p.mt, st); }));
+        WF_TRY(run_out_cross_mlp(e, w, c.n_layers + dl, p, st));
+    }
+    WF_TRY(run_head(e, e->lnd_g, e->lnd_b, p, d_logits, e->dam, st));
+    return timed(e, TK_DRAFT, st, [&] {
+        return launch_draft_out(d_anchor, e->dam, e->reqN, n, K, d_block, st);
+    });
 }
 
 wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,

@@ -116,10 +116,11 @@ __global__ __launch_bounds__(64) void self_attn_kernel(SelfAttnArgs a) {
     const int qrow = row0 + r16;
     const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
 
+    // last key any row of this tile may see (the whole block when not causal)
+    const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
     int lim[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) lim[r] = L + min(row0 + 4 * g + r, ntok - 1);
-    const int kmax = L + min(row0 + 15, ntok - 1);
+    for (int r = 0; r < 4; ++r) lim[r] = a.causal ? L + min(row0 + 4 * g + r, ntok - 1) : kmax;
 
     float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float lrun[4] = {0.f, 0.f, 0.f, 0.f};

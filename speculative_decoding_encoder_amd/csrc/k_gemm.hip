@@ -76,6 +76,10 @@ __device__ __forceinline__ void epi_elem(const GemmArgs &a, int m, int n, float 
             pg[(size_t)e.H * 16 * e.hd + ((size_t)h * e.hd + dim) * 16 + off] =
                 f2h_bits(v + bias_at(e.b2, c));
         }
+    } else if constexpr (EPI == EPI_STORE32) {
+        const int seg = n / a.seg_n;
+        const uint16_t *bb = seg == 0 ? e.b0 : (seg == 1 ? e.b1 : e.b2);
+        e.out32[(size_t)m * a.N + n] = v + bias_at(bb, n - seg * a.seg_n);
     } else if constexpr (EPI == EPI_XKV) {
         const int d = a.seg_n;
         const int seg = n / d;
@@ -148,7 +152,9 @@ __host__ __device__ constexpr int epi_of(int role) {
          : role == ROLE_CROSS_Q ? EPI_F16
          : role == ROLE_FC1 ? EPI_GELU
          : role == ROLE_LM_HEAD ? EPI_ARGMAX
-         : role == ROLE_XKV ? EPI_XKV : EPI_RESID;
+         : role == ROLE_XKV ? EPI_XKV
+         : (role == ROLE_DRAFT_QKV || role == ROLE_HIST || role == ROLE_HIST_KV) ? EPI_STORE32
+         : EPI_RESID;
 }
 
 template <int ROLE, int MB, int KS>
@@ -402,6 +408,9 @@ hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st) {
         case ROLE_FC2: return launch_mb<ROLE_FC2>(a, mb, st);
         case ROLE_LM_HEAD: return launch_mb<ROLE_LM_HEAD>(a, mb, st);
         case ROLE_XKV: return launch_mb<ROLE_XKV>(a, mb, st);
+        case ROLE_DRAFT_QKV: return launch_mb<ROLE_DRAFT_QKV>(a, mb, st);
+        case ROLE_HIST: return launch_mb<ROLE_HIST>(a, mb, st);
+        case ROLE_HIST_KV: return launch_mb<ROLE_HIST_KV>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

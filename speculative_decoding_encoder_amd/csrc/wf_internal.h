@@ -15,11 +15,13 @@ enum Epi : int {
     EPI_GELU = 3,   // out = split-bf16(GELU(C + b))   (MLP hidden)
     EPI_ARGMAX = 4, // tied LM head: per 64-column tile (max, lowest argmax), logits
     EPI_XKV = 5,    // cross K/V of one layer into the write-once pool
+    EPI_STORE32 = 6,// out32[m][n] = C + b_seg[n]      (drafter temporaries, history)
 };
 
 struct EpiArgs {
     const uint16_t *b0, *b1, *b2;  // bias per weight segment (bf16), may be null
     float *x;                      // EPI_RESID
+    float *out32;                  // EPI_STORE32 [M][N]
     uint16_t *out;                 // EPI_F16 / EPI_QKV (q) fp16 [M][N or d]; EPI_GELU split
     // EPI_QKV: KV append
     uint16_t *kv_layer;            // this layer's first page
@@ -79,6 +81,7 @@ struct SelfAttnArgs {
     const int32_t *page_table, *slots, *req_L, *req_ntok;
     int32_t pt_stride, page_elems;
     int32_t n, T, H, d;
+    int32_t causal;                // 1: row i sees keys <= L+i; 0: the whole block
     float scale;
     uint16_t *out;                 // split-bf16 [M][d]
 };
@@ -128,7 +131,47 @@ struct RollbackArgs {
 enum Role : int {
     ROLE_QKV = 0, ROLE_OPROJ = 1, ROLE_CROSS_Q = 2, ROLE_FC1 = 3, ROLE_FC2 = 4,
     ROLE_LM_HEAD = 5, ROLE_XKV = 6,
+    ROLE_DRAFT_QKV = 7,   // drafter q, k, v (fp32 temporaries before RoPE)
+    ROLE_HIST = 8,        // history projection of the tapped streams
+    ROLE_HIST_KV = 9,     // drafter k, v of history rows
 };
+
+struct TapArgs {
+    const float *x;
+    int32_t M, d, j, n_taps;
+    uint16_t *out;                 // split-bf16 [M][n_taps*d]
+};
+
+struct RopeArgs {
+    const float *tmp;              // [M][ncols] fp32 projections
+    int32_t ncols, q_off, k_off, v_off;   // column offsets; q_off < 0: no query
+    int32_t M, T, H, hd, d;
+    const int32_t *slots, *req_L, *req_ntok, *page_table;
+    int32_t pt_stride, page_elems;
+    uint16_t *kv_layer;            // drafter layer's first page
+    uint16_t *q_out;               // fp16 [M][d] rotated queries
+};
+
+struct PrepareDraftArgs {
+    int32_t n, K, V, n_ctx, n_pages, pt_stride, max_batch;
+    const int32_t *slots, *anchor, *page_table;
+    int32_t *slot_len, *slot_pending, *slot_err;
+    int32_t *req_L, *req_ntok;
+};
+
+struct EmbedDraftArgs {
+    int32_t M, T, d, V;
+    const int32_t *anchor;
+    const uint16_t *tok_emb, *mask;
+    float *x;
+};
+
+hipError_t launch_tap(const TapArgs &a, hipStream_t st);
+hipError_t launch_rope_append(const RopeArgs &a, hipStream_t st);
+hipError_t launch_prepare_draft(const PrepareDraftArgs &a, hipStream_t st);
+hipError_t launch_embed_draft(const EmbedDraftArgs &a, hipStream_t st);
+hipError_t launch_draft_out(const int32_t *anchor, const int32_t *argmax, const int32_t *req_ntok,
+                            int n, int K, int32_t *block, hipStream_t st);
 hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);

@@ -139,3 +139,56 @@ def run_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], n_max: i
             y[b] = int(nxt[b])
             done[b] = bool(dn[b])
     return res
+
+
+def run_drafter_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], n_max: int,
+                     K: int, eos: int) -> LoopResult:
+    """Speculative decoding with the engine's own parallel drafter: every
+    round is wf_draft (anchor + K drafts on the device) -> wf_verify_block
+    with k = min(K, R-1) candidates -> wf_accept -> wf_rollback."""
+    torch = eng.torch
+    n = len(slots)
+    res = LoopResult(n)
+    anchors = prefill(eng, slots, prefixes)
+    y = [int(a) for a in anchors]
+    for b in range(n):
+        res.tokens[b].append(y[b])
+    done = [y[b] == eos or n_max <= 1 for b in range(n)]
+    T = K + 1
+    d_slots = eng.i32(slots)
+    d_block = torch.empty((n, T), dtype=torch.int32, device=eng.dev)
+    d_am = torch.empty((n, T), dtype=torch.int32, device=eng.dev)
+    outs = [torch.empty(n, dtype=torch.int32, device=eng.dev) for _ in range(4)]
+    while not all(done):
+        ntok = np.zeros(n, np.int32)
+        budget = np.ones(n, np.int32)
+        for b in range(n):
+            if done[b]:
+                continue
+            R = n_max - len(res.tokens[b])
+            ntok[b] = 1 + min(K, R - 1)
+            budget[b] = R
+        anchor = np.array([max(v, 0) for v in y], np.int32)
+        eng.wf_draft(d_slots, eng.i32(anchor), K, d_block)
+        d_ntok = eng.i32(ntok)
+        eng.wf_verify_block(d_slots, d_block, d_ntok, d_am)
+        eng.wf_accept(d_block, d_ntok, eng.i32(budget), d_am, *outs)
+        eng.wf_rollback(d_slots, outs[0])
+        blk = d_block.cpu().numpy()
+        n_acc, nxt, n_emit, dn = (o.cpu().numpy() for o in outs)
+        res.rounds += 1
+        for b in range(n):
+            if ntok[b] == 0:
+                continue
+            a = int(n_acc[b])
+            if a < 0:
+                raise RuntimeError(f"request {b}: accept failed")
+            emitted = [int(t) for t in blk[b, 1:1 + a]]
+            if nxt[b] >= 0:
+                emitted.append(int(nxt[b]))
+            res.tokens[b].extend(emitted)
+            res.accepted[b].append(a)
+            res.proposed[b].append(int(ntok[b] - 1))
+            y[b] = int(nxt[b])
+            done[b] = bool(dn[b])
+    return res

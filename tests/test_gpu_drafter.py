@@ -1,0 +1,142 @@
+"""GPU parallel drafter (wf_draft, and the history the verify pass appends)
+against the oracle drafter.
+
+* tiny model: drafter logits after a prefill, and again after a verify
+  round whose accepted rows extended the history, within 2e-2 of the
+  oracle (parity beyond the oracle's self-consistency pins is unpinned: the
+  pages print no drafter values);
+* speculative decoding with the engine's own drafter equals GPU greedy
+  decoding (the lossless property holds for any drafts);
+* the full large-v3 shape with taps after blocks 1, 8, 15, 22 and 29.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import assert_argmax_where_clear, assert_logits_close, log
+from oracle import decode as od
+from oracle import drafter as odr
+from oracle import model as om
+from synthetic import (DRAFTER_TAPS, LARGE_V3, TINY, WORKLOADS, make_drafter_weights,
+                       make_encoder_out, make_prefixes, make_weights)
+
+pytestmark = pytest.mark.gpu
+TINY_TAPS = (1, 0, 1, 1, 0)
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _engine(shape, tw, dw, taps, max_batch, max_rows):
+    from speculative_decoding_encoder_amd.binding import Engine
+    return Engine(shape, tw, max_batch=max_batch, max_rows=max_rows, drafter_bits=dw, taps=taps)
+
+
+def _draft(eng, slots, anchors, K):
+    torch = eng.torch
+    n = len(slots)
+    blk = torch.empty((n, K + 1), dtype=torch.int32, device=eng.dev)
+    lg = torch.empty((n, K + 1, eng.shape.vocab), dtype=torch.float32, device=eng.dev)
+    eng.wf_draft(eng.i32(slots), eng.i32(anchors), K, blk, lg)
+    torch.cuda.synchronize()
+    return blk.cpu().numpy(), lg.cpu().numpy()
+
+
+@pytest.mark.parametrize("ln_random", [False, True])
+def test_tiny_drafter_logits_before_and_after_a_round(torch_cuda, ln_random):
+    torch = torch_cuda
+    wl = WORKLOADS[0]
+    tw = make_weights(TINY, wl.cfg_id, ln_random=ln_random)
+    dw = make_drafter_weights(TINY, wl.cfg_id, ln_random=ln_random)
+    enc = make_encoder_out(TINY, wl.cfg_id, 0)
+    prefix = make_prefixes(wl)[0]
+    P = len(prefix)
+    m = om.Model(TINY, tw)
+    dr = odr.Drafter(TINY, tw, dw, taps=TINY_TAPS)
+    req, dreq = m.new_request(enc), dr.new_request(enc)
+    lg, taps = m.rows(req, prefix, 0, taps=set(TINY_TAPS))
+    dr.append_history(dreq, taps, 0)
+    anchor = od.argmax_lowest(lg[-1])
+    K = 4
+    ref = dr.block(dreq, anchor, P, K)
+
+    eng = _engine(TINY, tw, dw, TINY_TAPS, 2, 64)
+    eng.wf_encode_kv(eng.i32([0]), eng.bf16(enc[None]))
+    am = torch.empty((1, P), dtype=torch.int32, device=eng.dev)
+    eng.wf_verify_block(eng.i32([0]), eng.i32(prefix[None]), eng.i32([P]), am)
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    blk, glg = _draft(eng, [0], [anchor], K)
+    e1 = assert_logits_close(glg[0], ref, what="tiny drafter after prefill")
+    assert blk[0, 0] == anchor
+    assert_argmax_where_clear(blk[0, 1:], ref[1:], what="tiny drafts")
+    # a verify round with the oracle's drafts, 2 accepted, then draft again
+    drafts = odr.draft_tokens(ref, K)
+    block = np.array([anchor] + drafts, np.int32)
+    lgv, taps = m.rows(req, block, P, taps=set(TINY_TAPS))
+    a = 2
+    dr.append_history(dreq, {t: v[:a + 1] for t, v in taps.items()}, P)
+    L2 = P + 1 + a
+    anchor2 = int(block[a + 1])
+    ref2 = dr.block(dreq, anchor2, L2, K)
+    amb = torch.empty((1, K + 1), dtype=torch.int32, device=eng.dev)
+    eng.wf_verify_block(eng.i32([0]), eng.i32(block[None]), eng.i32([K + 1]), amb)
+    eng.wf_rollback(eng.i32([0]), eng.i32([a]))
+    blk2, glg2 = _draft(eng, [0], [anchor2], K)
+    e2 = assert_logits_close(glg2[0], ref2, what="tiny drafter after a round")
+    err, ln = eng.wf_device_state()
+    assert err[0] == 0 and ln[0] == L2
+    log(f"tiny drafter (ln_random={ln_random}): max err {e1:.2e} / {e2:.2e}")
+    eng.close()
+
+
+def test_tiny_drafter_loop_equals_greedy(torch_cuda):
+    from speculative_decoding_encoder_amd.harness import run_drafter_loop, run_loop
+    wl = WORKLOADS[0]
+    tw = make_weights(TINY, wl.cfg_id)
+    dw = make_drafter_weights(TINY, wl.cfg_id)
+    encs = np.stack([make_encoder_out(TINY, wl.cfg_id, r) for r in range(3)])
+    prefixes = [make_prefixes(wl)[0], np.array([5, 6, 7, 8, 9, 10, 11], np.int32),
+                np.array([300], np.int32)]
+    eng = _engine(TINY, tw, dw, TINY_TAPS, 3, 64)
+    eng.wf_encode_kv(eng.i32([0, 1, 2]), eng.bf16(encs))
+    g = run_loop(eng, [0, 1, 2], prefixes, 40, 0, None, TINY.eos_id)
+    eng.wf_reset(eng.i32([0, 1, 2]))
+    s = run_drafter_loop(eng, [0, 1, 2], prefixes, 40, 8, TINY.eos_id)
+    for b in range(3):
+        assert s.tokens[b] == g.tokens[b], b
+    log(f"tiny drafter loop == greedy; rounds {s.rounds} vs {g.rounds}")
+    eng.close()
+
+
+def test_large_v3_drafter_logits(torch_cuda):
+    torch = torch_cuda
+    wl = WORKLOADS[3]
+    tw = make_weights(LARGE_V3, wl.cfg_id)
+    dw = make_drafter_weights(LARGE_V3, wl.cfg_id)
+    enc = make_encoder_out(LARGE_V3, wl.cfg_id, 0)
+    prefix = make_prefixes(wl)[0]
+    P = len(prefix)
+    log(f"large-v3 drafter: oracle (prefix {P})")
+    m = om.Model(LARGE_V3, tw)
+    dr = odr.Drafter(LARGE_V3, tw, dw, taps=DRAFTER_TAPS)
+    req, dreq = m.new_request(enc), dr.new_request(enc)
+    lg, taps = m.rows(req, prefix, 0, taps=set(DRAFTER_TAPS))
+    dr.append_history(dreq, taps, 0)
+    anchor = od.argmax_lowest(lg[-1])
+    ref = dr.block(dreq, anchor, P, 8)
+    del m
+    log("large-v3 drafter: GPU")
+    eng = _engine(LARGE_V3, tw, dw, DRAFTER_TAPS, 2, 256)
+    eng.wf_encode_kv(eng.i32([0]), eng.bf16(enc[None]))
+    am = torch.empty((1, P), dtype=torch.int32, device=eng.dev)
+    eng.wf_verify_block(eng.i32([0]), eng.i32(prefix[None]), eng.i32([P]), am)
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    blk, glg = _draft(eng, [0], [anchor], 8)
+    err = assert_logits_close(glg[0], ref, what="large-v3 drafter")
+    assert_argmax_where_clear(blk[0, 1:], ref[1:], what="large-v3 drafts")
+    log(f"large-v3 drafter: max err {err:.2e}")
+    eng.close()
