@@ -12,6 +12,9 @@ Workloads (``--config``):
   1  32-layer large-v3 shape, batch 1, 64-token prefix, one block of 9,
      drafts = the greedy token with probability 0.7, else a uniform id (default)
   2  4-layer turbo shape, batch 32, prefixes uniform in [4, 200], p = 0.75
+  3  32-layer large-v3 shape, batch 96, prefixes Poisson(80) clipped to
+     [4, 224], shuffled 16-token pages; K = 8 drafts come from the 2-layer
+     random-init parallel drafter (wf_draft), timed together with the verify
   4  32-layer large-v3 shape, batch 32, prefixes uniform in [4, 200], temperature
      0.7 rejection sampling; draft distributions q_i = 0.7 p~_i + 0.3 softmax(z_i),
      z_i ~ N(0, 1) seeded, where p~_i is the target's T = 0.7 distribution along
@@ -45,7 +48,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TOKENS_PER_AUDIO_S = 3.5
 METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
 KIND_NAMES = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
-              "cross_attn", "other", "encode_kv"]
+              "cross_attn", "other", "encode_kv", "draft", "history"]
 # kernel symbol (rocprofv3 name prefix) of each timing kind; the GEMM's first
 # template argument is its role
 KIND_SYMBOL = {
@@ -61,8 +64,8 @@ def log(*a):
 
 class Workload:
     def __init__(self, cfg_id: int, greedy: bool = False):
-        from synthetic import (WORKLOADS, make_draft_table, make_encoder_out, make_prefixes,
-                               make_weights)
+        from synthetic import (DRAFTER_TAPS, WORKLOADS, make_draft_table, make_drafter_weights,
+                               make_encoder_out, make_prefixes, make_weights, rng)
         from speculative_decoding_encoder_amd.binding import Engine
         from speculative_decoding_encoder_amd.harness import prefill, run_loop
         import torch
@@ -76,12 +79,20 @@ class Workload:
         self.name = wl.name if (cfg_id != 4 or self.sampling) else "large-v3-verify-b32-greedy"
         t0 = time.time()
         self.wbits = make_weights(s, wl.cfg_id)
+        self.drafter = wl.drafter_layers > 0
+        self.dbits = make_drafter_weights(s, wl.cfg_id, wl.drafter_layers) if self.drafter else None
         self.encs = np.stack([make_encoder_out(s, wl.cfg_id, r) for r in range(B)])
         self.prefixes = make_prefixes(wl)
         self.P = np.array([len(p) for p in self.prefixes], np.int32)
         log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
         max_rows = max(B * (self.K + 1), B * int(self.P.max()))
-        self.eng = eng = Engine(s, self.wbits, max_batch=B, max_rows=max_rows)
+        pps = s.n_ctx // 16
+        page_table = None
+        if wl.paged_shuffle:
+            page_table = rng(wl.cfg_id, 5000).permutation(B * pps).astype(np.int32).reshape(B, pps)
+        self.eng = eng = Engine(s, self.wbits, max_batch=B, max_rows=max_rows,
+                                page_table=page_table, drafter_bits=self.dbits,
+                                taps=DRAFTER_TAPS if self.drafter else ())
         self.slots = list(range(B))
         self.d_slots = eng.i32(self.slots)
         d_enc = eng.bf16(self.encs)
@@ -93,12 +104,14 @@ class Workload:
         del d_enc
         # the engine's own greedy continuation (untimed) for the drafts
         eng.wf_reset(self.d_slots)
-        g = run_loop(eng, self.slots, self.prefixes, self.K + 1, 0, None, s.eos_id)
-        self.greedy = g.tokens
-        eng.wf_reset(self.d_slots)
+        if not self.drafter:
+            g = run_loop(eng, self.slots, self.prefixes, self.K + 1, 0, None, s.eos_id)
+            self.greedy = g.tokens
+            eng.wf_reset(self.d_slots)
         anchors = prefill(eng, self.slots, self.prefixes)
+        self.anchors = anchors
         blocks = np.zeros((B, self.K + 1), np.int32)
-        for b in range(B):
+        for b in range(B if not self.drafter else 0):
             keep, repl = make_draft_table(wl, b)
             L = int(self.P[b])
             blocks[b, 0] = anchors[b]
@@ -114,8 +127,14 @@ class Workload:
             self.d_logits = torch.empty((B, T, s.vocab), dtype=torch.float32, device=eng.dev)
             self.d_req = eng.i32(np.arange(B, dtype=np.int32))
             self.d_step = eng.i32(np.zeros(B, np.int32))
+        if self.drafter:
+            self.d_anchor = eng.i32(anchors)
+            self.d_tok = torch.empty((B, T), dtype=torch.int32, device=eng.dev)
+            eng.wf_draft(self.d_slots, self.d_anchor, self.K, self.d_tok)
+            blocks = self.d_tok.cpu().numpy()
+        else:
+            self.d_tok = eng.i32(blocks)
         self.blocks = blocks
-        self.d_tok = eng.i32(blocks)
         self.d_ntok = eng.i32(np.full(B, T, np.int32))
         self.d_budget = eng.i32(np.full(B, wl.n_max - 1, np.int32))
         self.d_am = torch.empty((B, T), dtype=torch.int32, device=eng.dev)
@@ -158,6 +177,8 @@ class Workload:
 
     def step(self):
         e = self.eng
+        if self.drafter:
+            e.wf_draft(self.d_slots, self.d_anchor, self.K, self.d_tok)
         e.wf_verify_block(self.d_slots, self.d_tok, self.d_ntok, self.d_am, self.d_logits)
         if self.sampling:
             e.wf_accept(self.d_tok, self.d_ntok, self.d_budget, self.d_am, *self.outs,
@@ -192,48 +213,96 @@ class Workload:
         per_layer = kb["qkv"] + 2 * kb["oproj"] + kb["cross_q"] + kb["fc1"] + kb["fc2"] \
             + kb["self_attn"] + kb["cross_attn"]
         extra = 0.0
+        if self.drafter:
+            # drafter pass: its layers' weights, its cross K/V and history per
+            # request, the LM head; history append in the verify: W_h and
+            # each drafter layer's W_k, W_v
+            s = self.shape
+            d = s.d_model
+            nd = self.wl.drafter_layers
+            kb_ = self.kind_bytes()
+            layer_w = kb_["qkv"] - 4 * d * self.B * (self.K + 1) + 2 * kb_["oproj"] \
+                + kb_["cross_q"] + kb_["fc1"] + kb_["fc2"]
+            hist = 4.0 * d * float(np.sum(self.P + self.K + 1))
+            extra += nd * (layer_w + kb_["cross_attn"] + hist) + kb_["lm_head"]
+            extra += 5 * d * d * 2.0 + nd * 2 * d * d * 2.0
         if self.sampling:   # logits written and read back, q read
             extra = self.B * (self.K + 1) * self.shape.vocab * 4.0 * 2 \
                 + self.B * self.K * self.shape.vocab * 4.0
         return nl * per_layer + kb["lm_head"] + extra
 
 
-def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
+def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 90.0):
     """The oracle, as it stands (fp64 numpy), on a bounded sample of the same
-    workload: the verify pass (K+1 rows through every layer and the LM head)
-    of the first requests, each repeated up to 3 times, until about
-    ``timed_s`` seconds of timed CPU work (building each request's cross K/V
-    and prefix cache is not timed)."""
+    workload. For each of the first requests it builds, untimed, the request's
+    cross K/V and prefix cache and its own block by the workload's recipe (its
+    own greedy continuation for Bernoulli-copy drafts, its own probe logits
+    for the sampling q, its own drafter history); it then times the round's
+    work — the drafter pass (config 3), the verify pass (K+1 rows through
+    every layer and the LM head) and the acceptance — up to 3 times per
+    request (as often as needed with one request), until about ``timed_s``
+    seconds of timed CPU work."""
     from oracle import decode as od
+    from oracle import drafter as odr
     from oracle import model as om
     from oracle import sampling as osmp
+    from synthetic import DRAFTER_TAPS, make_draft_table, rng
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
-    m = om.Model(w.shape, w.wbits)
+    s = w.shape
+    K = w.K
+    m = om.Model(s, w.wbits)
+    dr = odr.Drafter(s, w.wbits, w.dbits, taps=DRAFTER_TAPS) if w.drafter else None
     toks = 0
     t_total = 0.0
     passes = 0
     reqs = 0
     t_start = time.time()
     for b in range(w.B):
+        P = int(w.P[b])
         req = m.new_request(w.encs[b])
-        m.rows(req, w.prefixes[b], 0)
-        reqs += 1
-        for _ in range(3):
-            t0 = time.perf_counter()
-            lg = m.rows(req, w.blocks[b], int(w.P[b]))
-            d = [int(t) for t in w.blocks[b, 1:]]
+        if dr is not None:
+            dreq = dr.new_request(w.encs[b])
+            lg, taps = m.rows(req, w.prefixes[b], 0, taps=set(DRAFTER_TAPS))
+            dr.append_history(dreq, taps, 0)
+        else:
+            lg = m.rows(req, w.prefixes[b], 0)
+        anchor = od.argmax_lowest(lg[-1])
+        q = None
+        if dr is None:
+            greedy = [anchor]
+            for i in range(K):
+                greedy.append(od.argmax_lowest(m.rows(req, [greedy[-1]], P + i)[0]))
             if w.sampling:
-                a, *_ = osmp.sample_round(lg.astype(np.float32), w.q_host[b], d, w.temperature,
-                                          0, b, 0, w.shape.eos_id, w.wl.n_max - 1)
+                plg = m.rows(req, greedy, P)
+                g = rng(w.wl.cfg_id, 4000 + b)
+                q = np.empty((K, s.vocab), np.float32)
+                drafts = []
+                for i in range(K):
+                    pt = osmp.probs(plg[i], w.temperature).astype(np.float64)
+                    zz = g.standard_normal(s.vocab)
+                    sm = np.exp(zz - zz.max())
+                    qi = 0.7 * pt + 0.3 * sm / sm.sum()
+                    q[i] = qi.astype(np.float32)
+                    drafts.append(int(g.choice(s.vocab, p=qi / qi.sum())))
             else:
-                g = [od.argmax_lowest(r) for r in lg]
-                a = 0
-                while a < len(d) and d[a] == g[a]:
-                    a += 1
+                keep, repl = make_draft_table(w.wl, b)
+                drafts = [greedy[i] if keep[P + i] else int(repl[P + i]) for i in range(1, K + 1)]
+        reqs += 1
+        for _ in range(3 if w.B > 1 else 200):
+            t0 = time.perf_counter()
+            if dr is not None:
+                drafts = odr.draft_tokens(dr.block(dreq, anchor, P, K), K)
+            lg = m.rows(req, [anchor] + drafts, P)
+            if w.sampling:
+                a, *_ = osmp.sample_round(lg.astype(np.float32), q, drafts, w.temperature, 0, b,
+                                          0, s.eos_id, w.wl.n_max - 1)
+            else:
+                a, *_ = od.greedy_accept(drafts, [od.argmax_lowest(r) for r in lg], s.eos_id,
+                                         w.wl.n_max - 1)
             t_total += time.perf_counter() - t0
             toks += a + 1
             passes += 1
@@ -241,12 +310,13 @@ def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 60.0):
                 break
         if t_total >= timed_s or time.time() - t_start > wall_s:
             break
+    what = "drafter pass + verify pass" if dr is not None else "verify pass"
     return {"value": round(toks / t_total, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{passes} verify passes (K+1 = {w.K + 1} rows, all layers, LM head"
-                      f"{', rejection sampling' if w.sampling else ''}) over "
-                      f"{reqs} of {w.B} requests, fp64 numpy, {t_total:.2f} s timed; cross K/V "
-                      f"and prefix caches built untimed"}
+            "sample": f"{passes} rounds ({what}, K+1 = {K + 1} rows, all layers, LM head, "
+                      f"{'rejection sampling' if w.sampling else 'greedy acceptance'}) over "
+                      f"{reqs} of {w.B} requests, fp64 numpy, {t_total:.2f} s timed; cross K/V, "
+                      f"prefix caches and blocks built untimed by the oracle itself"}
 
 
 def main():
@@ -254,7 +324,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 4])
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--greedy", action="store_true",
                     help="config 4 with greedy acceptance instead of T = 0.7 sampling")
@@ -343,7 +413,9 @@ def main():
                 "Bernoulli-copy drafts)",
         "config": {"workload": w.name, "layers": w.shape.n_layers,
                    "d_model": w.shape.d_model, "batch": w.B, "K": w.K,
-                   "prefix": w.wl.prefix, "p_keep": w.wl.p_keep if not w.sampling else None,
+                   "prefix": w.wl.prefix,
+                   "p_keep": w.wl.p_keep if not (w.sampling or w.drafter) else None,
+                   "drafter_layers": w.wl.drafter_layers,
                    "temperature": w.temperature, "graph": graph is not None},
         "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
         "tokens_per_step": tokens_per_step,
