@@ -84,7 +84,7 @@ typedef enum {
 
 /* Model and capacity description. The supported shapes have head_dim 16 or
  * 64, d_model = n_heads * head_dim with d_model a multiple of 64, d_ffn a
- * multiple of 64, n_ctx a multiple of 32 and page_size 16. */
+ * multiple of 64, n_ctx a multiple of 32 no larger than 1024 and page_size 16. */
 typedef struct {
     int32_t n_layers;     /* decoder layers (32 for large-v3, 4 for turbo) */
     int32_t d_model;      /* width (1280) */

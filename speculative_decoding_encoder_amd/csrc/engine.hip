@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <string>
 #include <vector>
@@ -44,16 +45,18 @@ void gemm_chunks(int K, int &ck, int &S) {
 }
 constexpr int kSplitRowsCap = 128;   // GEMM K-split scratch sized for this many rows x 8
 
-// Frames per cross-attention chunk: enough waves to cover the GPU when the
-// batch is small, one chunk per (request, head) when it is large. Depends on
-// the number of requests only, never on the block length.
-void cross_chunks(int n, int H, int F, int &cf, int &nch) {
+// Cross-attention chunking: 4, 8 or 16 chunks per (request, head) -- enough
+// waves to cover the GPU when the batch is small -- of spw 32-frame steps
+// each (a multiple of 3). Depends on the number of requests only, never on
+// the block length, so a row's bits do not depend on its block.
+void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
     const int steps = cdiv(F, 32);
-    int want = cdiv(1024, n * H);
-    want = want < 1 ? 1 : (want > 16 ? 16 : want);
-    const int per = cdiv(steps, want);
-    cf = per * 32;
-    nch = cdiv(F, cf);
+    const int want = cdiv(2048, n * H);
+    int C = want >= 16 ? 16 : (want >= 8 ? 8 : 4);
+    while (C > 4 && C > steps) C >>= 1;
+    spw = cdiv(cdiv(steps, C), 3) * 3;
+    cf = spw * 32;
+    G = C / 4;
 }
 
 int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
@@ -76,7 +79,8 @@ bool config_ok(const wf_config *c, std::string *why) {
     if (c->d_ffn < 64 || c->d_ffn % 64) return bad("d_ffn must be a positive multiple of 64");
     if (c->vocab < 2) return bad("vocab < 2");
     if (c->n_frames < 1) return bad("n_frames < 1");
-    if (c->n_ctx < 32 || c->n_ctx % 32) return bad("n_ctx must be a positive multiple of 32");
+    if (c->n_ctx < 32 || c->n_ctx % 32 || c->n_ctx > 1024)
+        return bad("n_ctx must be a multiple of 32 in [32, 1024]");
     if (c->page_size != 16) return bad("page_size must be 16");
     if (c->max_batch < 1 || c->max_rows < 1) return bad("max_batch and max_rows must be >= 1");
     if (c->n_pages < 1) return bad("n_pages < 1");
@@ -102,9 +106,9 @@ Layout layout_of(const wf_config *c) {
     L.part_bytes = part;
     size_t xap = 0;
     for (int n = 1; n <= c->max_batch; ++n) {
-        int cf, nch;
-        cross_chunks(n, H, c->n_frames, cf, nch);
-        if (nch > 1) xap = std::max(xap, (size_t)n * H * nch * 16 * (hd + 2) * 4);
+        int cf, G, spw;
+        cross_chunks(n, H, c->n_frames, cf, G, spw);
+        if (G > 1) xap = std::max(xap, (size_t)n * H * G * 16 * (hd + 2) * 4);
     }
     xap = std::max(xap, (size_t)8 << 20);
     L.xapart_bytes = xap;
@@ -115,7 +119,7 @@ Layout layout_of(const wf_config *c) {
     L.hs = take(M * 2 * f * 2);
     L.q = take(M * d * 2);
     L.part = take(part);
-    L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 64) * (cdiv((int)M, 16) + 1) * 4);
+    L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 16) * (cdiv((int)M, 16) + 1) * 4);
     L.xapart = take(xap);
     L.xacnt = take((size_t)c->max_batch * H * (c->n_ctx / 16 + 1) * 4);
     L.lmmax = take((size_t)L.n_vtiles * M * 4);
@@ -163,6 +167,7 @@ struct wf_engine {
     float *lmmax;
     int32_t *lmidx;
     int32_t *reqL, *reqN, *len, *pend, *err;
+    int tiles_ovr[16][3] = {};               // WF_GEMM_TILES: per role (mb, nb, P)
     // optional per-kernel timing with HIP events
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -199,10 +204,12 @@ wf_status timed(wf_engine *e, int kind, hipStream_t st, F &&launch) {
     return WF_OK;
 }
 
+// Rows up to which the verify-pass GEMMs use the register-tiled kernel.
+constexpr int kRegTiledMaxRows = 1024;
+
 wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                    int K, const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n,
                    int N, const EpiArgs &ea, hipStream_t st) {
-    const bool split_k_ok = role != ROLE_LM_HEAD && role != ROLE_XKV;
     GemmArgs a{};
     a.X = X;
     a.W0 = W0;
@@ -216,28 +223,83 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     gemm_chunks(K, ck, S);
     a.S = S;
     a.ck = ck;
-    a.n_tiles = cdiv(N, 64);
-    // Row blocks: the tallest block (up to 32 rows) that still gives about
-    // 256 workgroups; the row blocks of one weight tile share it through L2.
-    int mb = 2;
-    while (mb > 1 && a.n_tiles * cdiv(M, 16 * mb) < 256) mb >>= 1;
-    const int mt_need = cdiv(M, 16);
-    while (mb > 1 && (mb >> 1) >= mt_need) mb >>= 1;
-    a.m_blocks = cdiv(M, 16 * mb);
-    // Physical K split only for short blocks (<= 32 rows), where the
-    // subtree sums that cross workgroups are small.
-    int P = 1;
-    if (split_k_ok && M <= 32) {
-        while (P < S && a.n_tiles * a.m_blocks * P < 512 &&
-               (size_t)(2 * P) * M * N * 4 <= e->lay.part_bytes)
-            P *= 2;
-    }
-    a.n_groups = P;
-    a.n_wg = a.n_tiles * a.m_blocks * a.n_groups;
     a.part = e->part;
     a.cnt = e->gcnt;
     a.e = ea;
+    const bool split_k_ok = role != ROLE_LM_HEAD && role != ROLE_XKV;
+    const int mt_need = cdiv(M, 16);
+    if (M <= kRegTiledMaxRows && gemm_rk_built(role, ck)) {
+        // Register-tiled kernel (tiles from a sweep on MI355X). One row tile:
+        // 16 columns per workgroup and a 2-way K split (a weight-streaming
+        // GEMV, latency-bound); the LM head 64 columns. Taller blocks: 32 x 64
+        // tiles (the LM head 64 x 64: it reads the activations once per
+        // column tile), and a K split only while the grid is small.
+        int mb, nb, P = 1;
+        if (mt_need <= 1) {
+            mb = 1;
+            nb = role == ROLE_LM_HEAD ? 4 : 1;
+            if (split_k_ok && S >= 2 && (size_t)2 * M * N * 4 <= e->lay.part_bytes) P = 2;
+        } else {
+            mb = role == ROLE_LM_HEAD && mt_need > 2 ? 4 : 2;
+            nb = 4;
+            if (split_k_ok) {
+                while (P < S && cdiv(N, 16 * nb) * cdiv(M, 16 * mb) * P < 128 &&
+                       (size_t)(2 * P) * M * N * 4 <= e->lay.part_bytes)
+                    P *= 2;
+            }
+        }
+        const int *o = e->tiles_ovr[role];
+        if (o[0] > 0) {
+            mb = o[0];
+            nb = o[1];
+            if (role == ROLE_LM_HEAD) nb = 4;
+            P = split_k_ok ? o[2] : 1;
+            if (P < 1 || P > S || (size_t)P * M * N * 4 > e->lay.part_bytes) P = 1;
+        }
+        a.n_tiles = cdiv(N, 16 * nb);
+        a.m_blocks = cdiv(M, 16 * mb);
+        a.n_groups = P;
+        a.n_wg = a.n_tiles * a.m_blocks * a.n_groups;
+        return timed(e, kind, st, [&] { return launch_gemm_rk(role, a, mb, nb, st); });
+    }
+    a.n_tiles = cdiv(N, 64);
+    // LDS-staged kernel for tall blocks (prefill, the cross K/V): row blocks
+    // of up to 32 rows, the tallest that still gives about 256 workgroups; the
+    // row blocks of one weight tile share it through L2.
+    int mb = 2;
+    while (mb > 1 && a.n_tiles * cdiv(M, 16 * mb) < 256) mb >>= 1;
+    while (mb > 1 && (mb >> 1) >= mt_need) mb >>= 1;
+    a.m_blocks = cdiv(M, 16 * mb);
+    a.n_groups = 1;
+    a.n_wg = a.n_tiles * a.m_blocks;
     return timed(e, kind, st, [&] { return launch_gemm(role, a, mb, st); });
+}
+
+// WF_GEMM_TILES="role:mb:nb:P;..." (role an integer or '*') fixes the tiles
+// of the register-tiled GEMM per role; a tuning aid, read at wf_create.
+void read_tile_override(wf_engine *e) {
+    const char *env = std::getenv("WF_GEMM_TILES");
+    if (!env) return;
+    std::string s(env);
+    size_t pos = 0;
+    while (pos < s.size()) {
+        size_t end = s.find(';', pos);
+        if (end == std::string::npos) end = s.size();
+        const std::string item = s.substr(pos, end - pos);
+        pos = end + 1;
+        char r[8] = {0};
+        int mb = 0, nb = 0, P = 0;
+        if (std::sscanf(item.c_str(), "%7[^:]:%d:%d:%d", r, &mb, &nb, &P) != 4) continue;
+        const bool ok_t = (mb == 1 || mb == 2 || mb == 4) && (nb == 1 || nb == 2 || nb == 4) &&
+                          !(mb > 1 && nb == 1) && (P == 1 || P == 2 || P == 4 || P == 8);
+        if (!ok_t) continue;
+        for (int role = 0; role < 16; ++role) {
+            if (r[0] != '*' && std::atoi(r) != role) continue;
+            e->tiles_ovr[role][0] = mb;
+            e->tiles_ovr[role][1] = nb;
+            e->tiles_ovr[role][2] = P;
+        }
+    }
 }
 
 wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
@@ -318,6 +380,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     wf_engine *e = new wf_engine();
     e->c = *cfg;
     e->lay = layout_of(cfg);
+    read_tile_override(e);
     e->F_pad = f_pad_of(cfg);
     e->pt_stride = cfg->n_ctx / cfg->page_size;
     e->page_elems = 2 * cfg->n_heads * cfg->page_size * cfg->head_dim;
@@ -428,23 +491,21 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
 namespace {
 
 // Frame chunking of the cross-attention for n requests and mt row tiles.
-void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &nch) {
+void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &G, int &spw) {
     const wf_config &c = e->c;
     const int H = c.n_heads, hd = c.head_dim;
-    cross_chunks(n, H, c.n_frames, cf, nch);
+    cross_chunks(n, H, c.n_frames, cf, G, spw);
     const size_t rowbytes = (size_t)16 * (hd + 2) * 4;
-    if (nch > 1 && (size_t)n * H * mt * nch * rowbytes > e->lay.xapart_bytes) {
-        // long prefill blocks: fewer, longer chunks so the partials fit
-        const size_t fit = e->lay.xapart_bytes / ((size_t)n * H * mt * rowbytes);
-        const int steps = cdiv(c.n_frames, 32);
-        const int want = fit < 1 ? 1 : (fit > 16 ? 16 : (int)fit);
-        cf = cdiv(steps, want) * 32;
-        nch = cdiv(c.n_frames, cf);
+    while (G > 1 && (size_t)n * H * mt * G * rowbytes > e->lay.xapart_bytes) {
+        // long prefill blocks: fewer, longer chunks so the group partials fit
+        G >>= 1;
+        spw = cdiv(cdiv(cdiv(c.n_frames, 32), 4 * G), 3) * 3;
+        cf = spw * 32;
     }
 }
 
 struct Pass {
-    int n, T, M, mt, cf, nch;
+    int n, T, M, mt, cf, G, spw;
     const int32_t *slots;
     int kind;   // -1: per-kernel kinds; else every launch is timed under this kind
 };
@@ -483,9 +544,10 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     ca.F = c.n_frames;
     ca.F_pad = e->F_pad;
     ca.mt = p.mt;
-    ca.nch = p.nch;
+    ca.G = p.G;
     ca.cf = p.cf;
-    ca.n_items = p.n * H * p.mt * p.nch;
+    ca.spw = p.spw;
+    ca.n_items = p.n * H * p.mt * p.G;
     ca.scale = 1.0f / std::sqrt((float)hd);
     ca.part = e->xapart;
     ca.cnt = e->xacnt;
@@ -567,8 +629,8 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     if ((long long)n * T > c.max_rows) return fail(WF_ECAPACITY, "n*T exceeds max_rows");
     hipStream_t st = (hipStream_t)stream;
     const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
-    Pass p{n, T, M, cdiv(T, 16), 0, 0, d_slots, -1};
-    cross_plan(e, n, p.mt, p.cf, p.nch);
+    Pass p{n, T, M, cdiv(T, 16), 0, 0, 0, d_slots, -1};
+    cross_plan(e, n, p.mt, p.cf, p.G, p.spw);
 
     PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
                    d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
@@ -642,8 +704,8 @@ wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_
     if ((long long)n * T > c.max_rows) return fail(WF_ECAPACITY, "n*(K+1) exceeds max_rows");
     hipStream_t st = (hipStream_t)stream;
     const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
-    Pass p{n, T, M, cdiv(T, 16), 0, 0, d_slots, TK_DRAFT};
-    cross_plan(e, n, p.mt, p.cf, p.nch);
+    Pass p{n, T, M, cdiv(T, 16), 0, 0, 0, d_slots, TK_DRAFT};
+    cross_plan(e, n, p.mt, p.cf, p.G, p.spw);
 
     PrepareDraftArgs pa{n, K, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.max_batch, d_slots,
                         d_anchor, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};

@@ -1,0 +1,269 @@
+// Register-tiled GEMM for short row blocks (the verify pass, M = B(K+1)):
+// C[m][n] = sum_k X[m][k] W[n][k], bf16 MFMA 16x16x32, fp32 accumulate.
+//
+//  * A workgroup owns a BM x BN output tile (BM = 16 MB, BN = 16 NB) and the
+//    S/P consecutive K chunks of its K group; it has one wave per chunk.
+//  * A wave keeps all MB x NB MFMA tiles of its chunk in registers, so one
+//    activation fragment feeds NB MFMAs and one weight fragment feeds MB (2 MB
+//    with split-bf16 activations). Both operands go from global memory
+//    straight into a D-deep register ring; the chunk's CK k-steps are fully
+//    unrolled, so every ring slot is a fixed register set. Each weight
+//    fragment is loaded by exactly one wave per row block.
+//  * The chunk's k-steps run in order, hi before lo per step, from zero; the
+//    waves' chunk sums meet in LDS in the pairwise tree
+//    ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)), and K groups (P > 1) in the same
+//    tree through scratch. That is also the order of the LDS-staged kernel,
+//    so a row gets the same bits from either kernel whatever M, the tile
+//    shape or P.
+#pragma once
+#include "gemm_common.h"
+
+namespace wf {
+
+template <int ROLE, int MB, int NB, int CK>
+__global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
+    constexpr int EPI = epi_of(ROLE);
+    constexpr bool XS = ROLE != ROLE_XKV;          // split-bf16 activations
+    constexpr int NT = MB * NB;
+    constexpr int NX = XS ? 2 * MB : MB;           // activation fragments per k-step
+    // ring of ~144 VGPRs (~96 for the largest tile over long chunks: no spills)
+    constexpr int D0 = (NT >= 16 && CK > 5 ? 24 : 36) / (NX + NB);
+    constexpr int D1 = D0 < 1 ? 1 : D0;
+    constexpr int D = D1 > CK ? CK : D1;
+    constexpr int XSTEP = XS ? 64 : 32;            // uint16 per k-step along an X row
+    constexpr int BM = 16 * MB, BN = 16 * NB;
+    __shared__ f32x4 red[2][NT][64];
+
+    const int per = gridDim.x >> 3;
+    const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (lid >= a.n_wg) return;
+    const int ntile = lid / (a.m_blocks * a.n_groups);
+    const int rem = lid - ntile * (a.m_blocks * a.n_groups);
+    const int mblock = rem / a.n_groups;
+    const int grp = rem - mblock * a.n_groups;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int W = a.S / a.n_groups;                // waves = chunks of this K group
+    const int m_base = mblock * BM, n_base = ntile * BN;
+    const int ts = (grp * W + wave) * CK;          // first k-step of this wave's chunk
+
+    // Rows past M and columns past N load a clamped (valid) row instead:
+    // their results are never stored, and unconditional loads keep the
+    // compiler's wait counts exact, so the ring really overlaps.
+    const uint16_t *xp[MB];
+#pragma unroll
+    for (int mt = 0; mt < MB; ++mt) {
+        const int m = min(m_base + mt * 16 + r16, a.M - 1);
+        const size_t off = XS ? (size_t)m * 2 * a.K + g * 16 : (size_t)m * a.K + g * 8;
+        xp[mt] = a.X + off + (size_t)ts * XSTEP;
+    }
+    const uint16_t *wp[NB];
+#pragma unroll
+    for (int nt = 0; nt < NB; ++nt) {
+        const int n = min(n_base + nt * 16 + r16, a.N - 1);
+        const int seg = n / a.seg_n;
+        const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
+        wp[nt] = wb + (size_t)(n - seg * a.seg_n) * a.K + g * 8 + (size_t)ts * 32;
+    }
+    struct Fr { u32x4 x[NX]; u32x4 w[NB]; };
+    auto load = [&](Fr &fr, int s) {
+#pragma unroll
+        for (int mt = 0; mt < MB; ++mt) {
+            fr.x[mt] = ld16(xp[mt] + s * XSTEP);
+            if constexpr (XS) fr.x[MB + mt] = ld16(xp[mt] + s * XSTEP + 8);
+        }
+#pragma unroll
+        for (int nt = 0; nt < NB; ++nt) fr.w[nt] = ld16(wp[nt] + s * 32);
+    };
+
+    // sched_barrier(0) pins the issue order (the scheduler would otherwise
+    // sink the ring's loads next to their MFMAs to save registers)
+    Fr f[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) load(f[i], i);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 c[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < CK; ++s) {
+        Fr &cur = f[s % D];
+#pragma unroll
+        for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NB; ++nt)
+                c[mt * NB + nt] = mfma_bf16_k32(cur.x[mt], cur.w[nt], c[mt * NB + nt]);
+        if constexpr (XS) {
+#pragma unroll
+            for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NB; ++nt)
+                    c[mt * NB + nt] = mfma_bf16_k32(cur.x[MB + mt], cur.w[nt], c[mt * NB + nt]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + D < CK) load(cur, s + D);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Pairwise tree over the waves: at stride st, wave r (a multiple of 2st)
+    // adds wave r+st; pairs go through LDS two at a time.
+    for (int st = 1; st < W; st <<= 1) {
+        const int pairs = W / (2 * st);
+        for (int p0 = 0; p0 < pairs; p0 += 2) {
+            const int p = wave / (2 * st);              // this wave's pair
+            const bool in_batch = p >= p0 && p < p0 + 2;
+            const int pos = wave - p * 2 * st;          // 0: receiver, st: sender
+            if (in_batch && pos == st) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) red[p - p0][j][lane] = c[j];
+            }
+            __syncthreads();
+            if (in_batch && pos == 0) {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) c[j] = c[j] + red[p - p0][j][lane];
+            }
+            __syncthreads();
+        }
+    }
+    // wave 0 holds the workgroup's sum; share it
+    if (wave == 0) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) red[0][j][lane] = c[j];
+    }
+    __syncthreads();
+
+    if constexpr (EPI == EPI_ARGMAX) {
+        // per row: (max, lowest index) over this workgroup's BN columns
+        const EpiArgs &e = a.e;
+        for (int mt = wave; mt < MB; mt += W) {
+            f32x4 v[NB];
+#pragma unroll
+            for (int nt = 0; nt < NB; ++nt) v[nt] = red[0][mt * NB + nt][lane];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m_base + mt * 16 + 4 * g + r;
+                float bv = -INFINITY;
+                int bi = 0x7fffffff, nn = 0;
+#pragma unroll
+                for (int nt = 0; nt < NB; ++nt) {
+                    const int n = n_base + nt * 16 + r16;
+                    if (n >= a.N) continue;
+                    const float x = v[nt][r];
+                    if (e.logits && m < a.M) e.logits[(size_t)m * a.N + n] = x;
+                    if (x != x) nn = 1;
+                    else argmax_merge(bv, bi, x, n);
+                }
+#pragma unroll
+                for (int o = 1; o < 16; o <<= 1) {
+                    const float v2 = __shfl_xor(bv, o);
+                    const int i2 = __shfl_xor(bi, o);
+                    argmax_merge(bv, bi, v2, i2);
+                    nn |= __shfl_xor(nn, o);
+                }
+                if (r16 == 0 && m < a.M) {
+                    e.tile_max[(size_t)ntile * e.ld + m] = bv;
+                    e.tile_idx[(size_t)ntile * e.ld + m] = nn ? -1 : bi;
+                }
+            }
+        }
+        return;
+    } else {
+        if (a.n_groups == 1) {
+            for (int j = wave; j < NT; j += W) {
+                const int mt = j / NB, nt = j - (j / NB) * NB;
+                const f32x4 v = red[0][j][lane];
+                const int n = n_base + nt * 16 + r16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int m = m_base + mt * 16 + 4 * g + r;
+                    if (m < a.M && n < a.N) epi_elem<EPI>(a, m, n, v[r]);
+                }
+            }
+            return;
+        }
+        // publish this K group's sum; the last group to arrive combines
+        const size_t stride = (size_t)a.M * a.N;
+        for (int j = wave; j < NT; j += W) {
+            const int mt = j / NB, nt = j - (j / NB) * NB;
+            const f32x4 v = red[0][j][lane];
+            const int n = n_base + nt * 16 + r16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m_base + mt * 16 + 4 * g + r;
+                if (m < a.M && n < a.N)
+                    store_coherent(a.part + (size_t)grp * stride + (size_t)m * a.N + n, v[r]);
+            }
+        }
+        wait_vmem();
+        __shared__ int last;
+        __syncthreads();
+        const int cidx = ntile * a.m_blocks + mblock;
+        if (tid == 0) last = (arrive(&a.cnt[cidx]) == a.n_groups - 1);
+        __syncthreads();
+        if (!last) return;
+        if (tid == 0) rearm(&a.cnt[cidx]);
+        const int rows = min(BM, a.M - m_base);
+        for (int idx = tid; idx < rows * BN; idx += 64 * W) {
+            const int rr = idx / BN, cc = idx - (idx / BN) * BN;
+            const int m = m_base + rr, n = n_base + cc;
+            if (n >= a.N) continue;
+            epi_elem<EPI>(a, m, n, tree_combine(a.part + (size_t)m * a.N + n, stride,
+                                                a.n_groups));
+        }
+    }
+}
+
+template <int ROLE, int MB, int NB, int CK>
+hipError_t launch_rk(const GemmArgs &a, hipStream_t st) {
+    const int grid = ((a.n_wg + 7) / 8) * 8;
+    const int waves = a.S / a.n_groups;
+    hipLaunchKernelGGL((gemm_rk_kernel<ROLE, MB, NB, CK>), dim3(grid), dim3(64 * waves), 0, st, a);
+    return hipGetLastError();
+}
+
+// chunk lengths (k-steps) each role is built for: K = d_model gives 1 (width
+// 64) or 5 (width 1280); fc2 (K = d_ffn) 1 or 20; the history projection
+// (K = 5 d_model) 5 or 25
+template <int ROLE>
+constexpr bool rk_ck_built(int ck) {
+    return ROLE == ROLE_FC2 ? (ck == 1 || ck == 20)
+         : ROLE == ROLE_HIST ? (ck == 5 || ck == 25)
+         : (ck == 1 || ck == 5);
+}
+
+template <int ROLE, int MB, int NB>
+hipError_t launch_rk_ck(const GemmArgs &a, hipStream_t st) {
+    switch (a.ck) {
+        case 1: if constexpr (rk_ck_built<ROLE>(1)) return launch_rk<ROLE, MB, NB, 1>(a, st); break;
+        case 5: if constexpr (rk_ck_built<ROLE>(5)) return launch_rk<ROLE, MB, NB, 5>(a, st); break;
+        case 20: if constexpr (rk_ck_built<ROLE>(20)) return launch_rk<ROLE, MB, NB, 20>(a, st); break;
+        case 25: if constexpr (rk_ck_built<ROLE>(25)) return launch_rk<ROLE, MB, NB, 25>(a, st); break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <int ROLE>
+hipError_t launch_rk_role(const GemmArgs &a, int mb, int nb, hipStream_t st) {
+    if constexpr (ROLE == ROLE_LM_HEAD) {
+        switch (mb) {
+            case 1: return launch_rk_ck<ROLE, 1, 4>(a, st);
+            case 2: return launch_rk_ck<ROLE, 2, 4>(a, st);
+            case 4: return launch_rk_ck<ROLE, 4, 4>(a, st);
+        }
+        return hipErrorInvalidValue;
+    } else {
+        switch (mb * 8 + nb) {
+            case 1 * 8 + 1: return launch_rk_ck<ROLE, 1, 1>(a, st);
+            case 1 * 8 + 2: return launch_rk_ck<ROLE, 1, 2>(a, st);
+            case 1 * 8 + 4: return launch_rk_ck<ROLE, 1, 4>(a, st);
+            case 2 * 8 + 2: return launch_rk_ck<ROLE, 2, 2>(a, st);
+            case 2 * 8 + 4: return launch_rk_ck<ROLE, 2, 4>(a, st);
+            case 4 * 8 + 2: return launch_rk_ck<ROLE, 4, 2>(a, st);
+            case 4 * 8 + 4: return launch_rk_ck<ROLE, 4, 4>(a, st);
+        }
+        return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace wf

@@ -17,9 +17,16 @@
 // candidates", Whisper-Flash section 3.1).
 //
 // Cross-attention reads the write-once pool (K [head][F_pad][hd], V^T
-// [head][hd][F_pad]); the frames are split into chunks handled by separate
-// waves, whose (m, l, o) partials are merged in chunk order by the last wave
-// to finish.
+// [head][hd][F_pad]).
+//
+// A workgroup is four waves. In self-attention they split the 32-key steps
+// of one (request, head, 16-row tile) by absolute step index (wave w takes
+// steps w, w+4, ...); in cross-attention each wave takes one chunk of frames
+// and a workgroup four consecutive chunks. The waves' (m, l, o) partials
+// meet in LDS as ((w0+w1)+(w2+w3)); cross-attention workgroups of one tile
+// meet the same way through device-coherent scratch (the last to arrive
+// merges). A partial that saw only masked keys has m = -inf and weight 0, so
+// steps or chunks a row cannot see leave its bits unchanged.
 #include "wf_device.h"
 #include "wf_internal.h"
 
@@ -89,14 +96,136 @@ __device__ __forceinline__ void store_split(uint16_t *out, size_t row_off, int c
     out[base + 8] = lo;
 }
 
-// ---------------------------------------------------------------------------
-// Self-attention over the paged KV cache, causal inside the block.
-// grid = (n * H, ceil(T / 16)), block = one wave.
+// Intra-wave ordering of LDS traffic (the P tile is private to a wave).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Running softmax state of the 4 rows (4g+r) a lane holds.
+template <int NDT>
+struct SmState {
+    float m[4], l[4];
+    f32x4 o[NDT];
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+// Partial (m, l, o) of 16 rows in LDS: row-major [16][HD + 2].
+template <int HD, int NDT>
+__device__ __forceinline__ void put_partial(float *buf, const SmState<NDT> &s, int g, int r16) {
+    constexpr int PW = HD + 2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        if (r16 == 0) {
+            buf[row * PW] = s.m[r];
+            buf[row * PW + 1] = s.l[r];
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) buf[row * PW + 2 + dt * 16 + r16] = s.o[dt][r];
+    }
+}
+
+// s = s (+) partial in buf: rescale both to the larger running max.
+template <int HD, int NDT>
+__device__ __forceinline__ void merge_partial(SmState<NDT> &s, const float *buf, int g, int r16) {
+    constexpr int PW = HD + 2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;
+        const float mb = buf[row * PW], lb = buf[row * PW + 1];
+        const float M = fmaxf(s.m[r], mb);
+        const float wa = (s.m[r] == -INFINITY) ? 0.f : __expf(s.m[r] - M);
+        const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - M);
+        s.l[r] = s.l[r] * wa + lb * wb;
+        s.m[r] = M;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            s.o[dt][r] = s.o[dt][r] * wa + buf[row * PW + 2 + dt * 16 + r16] * wb;
+    }
+}
+
+// ((w0+w1)+(w2+w3)) over the four waves; the result lands in wave 0.
+template <int HD, int NDT>
+__device__ __forceinline__ void merge_waves(SmState<NDT> &s, float (*mbuf)[16 * (HD + 2)],
+                                            int wave, int g, int r16) {
+    if (wave & 1) put_partial<HD>(mbuf[wave >> 1], s, g, r16);
+    __syncthreads();
+    if (!(wave & 1)) merge_partial<HD>(s, mbuf[wave >> 1], g, r16);
+    __syncthreads();
+    if (wave == 2) put_partial<HD>(mbuf[0], s, g, r16);
+    __syncthreads();
+    if (wave == 0) merge_partial<HD>(s, mbuf[0], g, r16);
+}
+
+// K and V^T fragments of one 32-key step.
 template <int HD>
-__global__ __launch_bounds__(64) void self_attn_kernel(SelfAttnArgs a) {
+struct KVStep {
+    u32x4 k[2][2];     // HD = 64: [16-key tile][dim half]
+    u32x2 k16[2];      // HD = 16
+    u32x4 v[HD / 16];  // V^T: 16 dims x 8 keys per lane
+};
+
+// One 32-key step of the online softmax: scores of the two 16-key tiles
+// (key index key0 + 16t + r16 is live for row 4g+r iff live(r, key)), then
+// P V with the probabilities staged through this wave's LDS tile.
+template <int HD, typename Live>
+__device__ __forceinline__ void attend_step(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
+                                            int vlive_to, float scale, SmState<HD / 16> &st,
+                                            uint16_t *P, int g, int r16, Live live) {
     constexpr int NDT = HD / 16;
-    __shared__ __attribute__((aligned(16))) uint16_t P[16 * 32];
-    const int lane = threadIdx.x, r16 = lane & 15, g = lane >> 4;
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (HD == 64) {
+            s[t] = mfma_f16_k32(q.a[0], f.k[t][0], s[t]);
+            s[t] = mfma_f16_k32(q.a[1], f.k[t][1], s[t]);
+        } else {
+            s[t] = mfma_f16_k16(q.h, f.k16[t], s[t]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            s[t][r] = live(r, key0 + 16 * t + r16) ? s[t][r] * scale : -INFINITY;
+    }
+    softmax_step<NDT>(s[0], s[1], st.m, st.l, st.o, P, g, r16);
+    wave_lds_sync();
+    const u32x4 pa = *reinterpret_cast<const u32x4 *>(&P[r16 * 32 + 8 * g]);
+    const int vk = key0 + 8 * g;                  // this lane's 8 keys
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        u32x4 vb = f.v[dt];
+        if (vk + 8 > vlive_to) {                  // keys at or past vlive_to: zero operand
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint32_t w = vb[j];
+                if (vk + 2 * j >= vlive_to) w &= 0xffff0000u;
+                if (vk + 2 * j + 1 >= vlive_to) w &= 0x0000ffffu;
+                vb[j] = w;
+            }
+        }
+        st.o[dt] = mfma_f16_k32(pa, vb, st.o[dt]);
+    }
+    wave_lds_sync();
+}
+
+// ---------------------------------------------------------------------------
+// Self-attention over the paged KV cache, causal inside the block (or over
+// the whole block, causal = 0). grid = (n * H, ceil(T / 16)), 256 threads.
+template <int HD>
+__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
+    constexpr int NDT = HD / 16;
+    constexpr int PW = HD + 2;
+    __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
+    __shared__ float mbuf[2][16 * PW];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
     const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
     const int row0 = blockIdx.y * 16;
     const int ntok = a.req_ntok[b];
@@ -104,7 +233,7 @@ __global__ __launch_bounds__(64) void self_attn_kernel(SelfAttnArgs a) {
 
     if (ntok == 0 || row0 >= ntok) {
         // skipped request or a tile of padding rows: zeros
-        for (int idx = lane; idx < 16 * HD; idx += 64) {
+        for (int idx = tid; idx < 16 * HD; idx += 256) {
             const int rr = idx / HD, c = idx - rr * HD;
             const int row = row0 + rr;
             if (row < a.T) store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + c, 0.f);
@@ -112,126 +241,101 @@ __global__ __launch_bounds__(64) void self_attn_kernel(SelfAttnArgs a) {
         return;
     }
     const int L = a.req_L[b];
-    const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
-    const int qrow = row0 + r16;
-    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
-
     // last key any row of this tile may see (the whole block when not causal)
     const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
     int lim[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) lim[r] = a.causal ? L + min(row0 + 4 * g + r, ntok - 1) : kmax;
-
-    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float lrun[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 o[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int last_page = kmax >> 4;   // pages past this one were never validated
+    // the request's page ids, one per lane (at most 64 pages)
+    const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
+    const int ptl = lane <= last_page ? pt[lane] : 0;
+    const int qrow = row0 + r16;
+    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
 
     const uint16_t *kvl = a.kv_layer;
     const size_t vt_off = (size_t)a.H * 16 * HD;
-    const int last_page = kmax >> 4;   // pages past this one were never validated
-
-    for (int kb = 0; kb <= kmax; kb += 32) {
-        f32x4 s[2];
+    auto load = [&](int j, KVStep<HD> &f) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const int lp = (kb >> 4) + t;
-            if (lp <= last_page) {
-                const int page = pt[lp];
-                const uint16_t *krow =
-                    kvl + (size_t)page * a.page_elems + ((size_t)h * 16 + r16) * HD;
-                s[t] = qk_tile<HD>(q, krow, g);
+            const int page = __shfl(ptl, min(2 * j + t, last_page));
+            const uint16_t *krow = kvl + (size_t)page * a.page_elems + ((size_t)h * 16 + r16) * HD;
+            if constexpr (HD == 64) {
+                f.k[t][0] = ld16(krow + 8 * g);
+                f.k[t][1] = ld16(krow + 32 + 8 * g);
             } else {
-                s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+                f.k16[t] = ld8(krow + 4 * g);
             }
+        }
+        const int vkey = 32 * j + 8 * g;
+        const int vpage = __shfl(ptl, min(vkey >> 4, last_page));
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+            f.v[dt] = ld16(kvl + (size_t)vpage * a.page_elems + vt_off +
+                           ((size_t)h * HD + dt * 16 + r16) * 16 + (vkey & 15));
+    };
+    auto live = [&](int r, int key) { return key <= lim[r]; };
+
+    SmState<NDT> st;
+    st.init();
+    const int nsteps = (kmax >> 5) + 1;             // absolute 32-key steps
+    KVStep<HD> cur, nxt;
+    if (wave < nsteps) load(wave, cur);
+    for (int j = wave; j < nsteps; j += 4) {
+        if (j + 4 < nsteps) load(j + 4, nxt);
+        attend_step<HD>(q, cur, 32 * j, kmax + 1, a.scale, st, Pt[wave], g, r16, live);
+        cur = nxt;
+    }
+    merge_waves<HD>(st, mbuf, wave, g, r16);
+    if (wave == 0) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int key = kb + 16 * t + r16;
-                s[t][r] = (key <= lim[r]) ? s[t][r] * a.scale : -INFINITY;
+                const int row = row0 + 4 * g + r;
+                if (row < a.T)
+                    store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dt * 16 + r16,
+                                st.o[dt][r] / st.l[r]);
             }
-        }
-        softmax_step<NDT>(s[0], s[1], mrun, lrun, o, P, g, r16);
-        __syncthreads();
-        const u32x4 pa = *reinterpret_cast<const u32x4 *>(&P[r16 * 32 + 8 * g]);
-        const int vkey = kb + 8 * g;                 // this lane's 8 keys
-        const bool vlive = (vkey >> 4) <= last_page;
-        const int vpage = vlive ? pt[vkey >> 4] : 0;
-        const bool tail = (vkey + 8 > kmax + 1);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            const uint16_t *vp = kvl + (size_t)vpage * a.page_elems + vt_off +
-                                 ((size_t)h * HD + dt * 16 + r16) * 16 + (vkey & 15);
-            u32x4 vb = vlive ? ld16(vp) : u32x4{0u, 0u, 0u, 0u};
-            if (tail) {   // keys past the last live one: zero the operand
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int k0 = vkey + 2 * j;
-                    uint32_t w = vb[j];
-                    if (k0 > kmax) w &= 0xffff0000u;
-                    if (k0 + 1 > kmax) w &= 0x0000ffffu;
-                    vb[j] = w;
-                }
-            }
-            o[dt] = mfma_f16_k32(pa, vb, o[dt]);
-        }
-        __syncthreads();
     }
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = row0 + 4 * g + r;
-            if (row < a.T)
-                store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dt * 16 + r16,
-                            o[dt][r] / lrun[r]);
-        }
 }
 
 // ---------------------------------------------------------------------------
-// Cross-attention over the write-once audio K/V. One wave (one workgroup)
-// per item (request, head, m-tile, frame chunk).
+// Cross-attention over the write-once pool. Workgroup = (request, head,
+// 16-row tile, chunk group); wave w takes chunk 4 * group + w of cf frames
+// (spw 32-frame steps, a multiple of 3: a 3-deep load ring).
 template <int HD>
-__global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
+__global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
     constexpr int NDT = HD / 16;
-    constexpr int PW = HD + 2;   // partial row: m, l, o[HD]
-    __shared__ __attribute__((aligned(16))) uint16_t P[16 * 32];
-    const int lane = threadIdx.x;
+    constexpr int PW = HD + 2;
+    __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
+    __shared__ float mbuf[2][16 * PW];
+    __shared__ float wts[16][5];
+    __shared__ int last;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
     const int item = blockIdx.x;
-    const int ch = item % a.nch;
-    const int bhm = item / a.nch;            // (b * H + h) * mt + mtile
+    const int grp = item % a.G;
+    const int bhm = item / a.G;               // (b * H + h) * mt + mtile
     const int mtile = bhm % a.mt;
     const int bh = bhm / a.mt;
     const int b = bh / a.H, h = bh - (bh / a.H) * a.H;
     const int ntok = a.req_ntok[b];
-    if (ntok == 0) return;                   // every chunk of this request skips
+    if (ntok == 0) return;                    // every group of this request skips
     const int row0 = mtile * 16;
     const size_t ld_out = (size_t)2 * a.d;
 
     const uint16_t *base = a.xkv + (size_t)a.slots[b] * a.slot_stride + a.layer_off;
     const uint16_t *kh = base + (size_t)h * a.F_pad * HD;
     const uint16_t *vh = base + (size_t)a.H * a.F_pad * HD + (size_t)h * HD * a.F_pad;
-
     const int qrow = row0 + r16;
     const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
 
-    float mrun[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    float lrun[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 o[NDT];
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int f0 = ch * a.cf;
-    const int f1 = min(f0 + a.cf, a.F);
-    // K/V fragments of one 32-frame step; the next step is loaded while the
-    // current one is computed
-    struct KV {
-        u32x4 k[2][2];     // [16-frame tile][dim half] (HD = 64)
-        u32x2 k16[2];      // HD = 16
-        u32x4 v[NDT];
-    };
-    auto load_kv = [&](int fb, KV &f) {
+    const int c0 = (grp * 4 + wave) * a.cf;        // first frame of this wave's chunk
+    const int c1 = min(c0 + a.cf, a.F);            // end of its live frames
+    const int last_fb = a.F_pad - 32;              // loads stay inside this head's frames
+    auto load = [&](int s, KVStep<HD> &f) {
+        const int fb = min(c0 + 32 * s, last_fb);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             const uint16_t *krow = kh + (size_t)(fb + 16 * t + r16) * HD;
@@ -246,119 +350,102 @@ __global__ __launch_bounds__(64) void cross_attn_kernel(CrossAttnArgs a) {
         for (int dt = 0; dt < NDT; ++dt)
             f.v[dt] = ld16(vh + (size_t)(dt * 16 + r16) * a.F_pad + fb + 8 * g);
     };
-    KV cur, nxt;
-    load_kv(f0, cur);
-    for (int fb = f0; fb < f1; fb += 32) {
-        if (fb + 32 < f1) load_kv(fb + 32, nxt);
-        f32x4 s[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (HD == 64) {
-                s[t] = mfma_f16_k32(q.a[0], cur.k[t][0], s[t]);
-                s[t] = mfma_f16_k32(q.a[1], cur.k[t][1], s[t]);
-            } else {
-                s[t] = mfma_f16_k16(q.h, cur.k16[t], s[t]);
-            }
-            const bool ok = fb + 16 * t + r16 < f1;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) s[t][r] = ok ? s[t][r] * a.scale : -INFINITY;
-        }
-        softmax_step<NDT>(s[0], s[1], mrun, lrun, o, P, g, r16);
-        __syncthreads();
-        const u32x4 pa = *reinterpret_cast<const u32x4 *>(&P[r16 * 32 + 8 * g]);
-        const int vf = fb + 8 * g;
-        const bool tail = vf + 8 > f1;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-            u32x4 vb = cur.v[dt];
-            if (tail) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int k0 = vf + 2 * j;
-                    uint32_t w = vb[j];
-                    if (k0 >= f1) w &= 0xffff0000u;
-                    if (k0 + 1 >= f1) w &= 0x0000ffffu;
-                    vb[j] = w;
-                }
-            }
-            o[dt] = mfma_f16_k32(pa, vb, o[dt]);
-        }
-        __syncthreads();
-        cur = nxt;
-    }
+    auto live = [&](int, int frame) { return frame < c1; };
 
-    if (a.nch == 1) {
+    SmState<NDT> st;
+    st.init();
+    KVStep<HD> f[3];
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
+    for (int i = 0; i < 3; ++i) load(i, f[i]);
+    for (int s0 = 0; s0 < a.spw; s0 += 3) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 4 * g + r;
-                if (row < a.T)
-                    store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dt * 16 + r16,
-                                o[dt][r] / lrun[r]);
-            }
+        for (int i = 0; i < 3; ++i) {
+            attend_step<HD>(q, f[i], c0 + 32 * (s0 + i), c1, a.scale, st, Pt[wave], g, r16, live);
+            if (s0 + 3 < a.spw) load(s0 + i + 3, f[i]);
+        }
+    }
+    merge_waves<HD>(st, mbuf, wave, g, r16);
+
+    if (a.G == 1) {
+        if (wave == 0) {
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + 4 * g + r;
+                    if (row < a.T)
+                        store_split(a.out, (size_t)(b * a.T + row) * ld_out,
+                                    h * HD + dt * 16 + r16, st.o[dt][r] / st.l[r]);
+                }
+        }
         return;
     }
-    // publish (m, l, o) for this chunk
-    float *pp = a.part + (size_t)item * 16 * PW;
+    // publish this group's (m, l, o); the last group to arrive merges
+    if (wave == 0) {
+        float *pp = a.part + (size_t)item * 16 * PW;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        if (r16 == 0) {
-            store_coherent(pp + row * PW + 0, mrun[r]);
-            store_coherent(pp + row * PW + 1, lrun[r]);
-        }
+        for (int r = 0; r < 4; ++r) {
+            const int row = 4 * g + r;
+            if (r16 == 0) {
+                store_coherent(pp + row * PW + 0, st.m[r]);
+                store_coherent(pp + row * PW + 1, st.l[r]);
+            }
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) store_coherent(pp + row * PW + 2 + dt * 16 + r16, o[dt][r]);
-    }
-    wait_vmem();
-    int prev = 0;
-    if (lane == 0) prev = arrive(&a.cnt[bhm]);
-    prev = __shfl(prev, 0);
-    if (prev != a.nch - 1) return;
-    if (lane == 0) rearm(&a.cnt[bhm]);
-    // merge chunks in order. Per row r: M = max_c m_c, w_c = exp(m_c - M),
-    // L = sum_c l_c w_c; then o = sum_c o_c w_c / L.
-    __shared__ float wts[16][17];
-    const float *pb = a.part + (size_t)(item - ch) * 16 * PW;
-    if (lane < 16) {
-        const int rr = lane;
-        float mx = -INFINITY;
-        for (int c = 0; c < a.nch; ++c) mx = fmaxf(mx, load_coherent(pb + (size_t)c * 16 * PW + rr * PW));
-        float l = 0.f;
-        for (int c = 0; c < a.nch; ++c) {
-            const float *pc = pb + (size_t)c * 16 * PW + rr * PW;
-            const float w = __expf(load_coherent(pc) - mx);
-            l += load_coherent(pc + 1) * w;
-            wts[rr][c] = w;
+            for (int dt = 0; dt < NDT; ++dt)
+                store_coherent(pp + row * PW + 2 + dt * 16 + r16, st.o[dt][r]);
         }
-        wts[rr][16] = l;
+        wait_vmem();
+        int prev = 0;
+        if (lane == 0) prev = arrive(&a.cnt[bhm]);
+        prev = __shfl(prev, 0);
+        if (lane == 0) last = (prev == a.G - 1);
     }
     __syncthreads();
-    for (int idx = lane; idx < 16 * HD; idx += 64) {
+    if (!last) return;
+    if (tid == 0) rearm(&a.cnt[bhm]);
+    // per row: M = max_g m_g, w_g = exp(m_g - M), L = sum_g l_g w_g (pairwise)
+    const float *pb = a.part + (size_t)(item - grp) * 16 * PW;
+    if (tid < 16) {
+        float mg[4], lg[4];
+        float M = -INFINITY;
+        for (int q2 = 0; q2 < a.G; ++q2) {
+            mg[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + tid * PW);
+            lg[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + tid * PW + 1);
+            M = fmaxf(M, mg[q2]);
+        }
+        float w[4];
+        for (int q2 = 0; q2 < a.G; ++q2) {
+            w[q2] = (mg[q2] == -INFINITY) ? 0.f : __expf(mg[q2] - M);
+            wts[tid][q2] = w[q2];
+        }
+        wts[tid][4] = (a.G == 2) ? lg[0] * w[0] + lg[1] * w[1]
+                                 : (lg[0] * w[0] + lg[1] * w[1]) + (lg[2] * w[2] + lg[3] * w[3]);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 16 * HD; idx += 256) {
         const int rr = idx / HD, dim = idx - rr * HD;
         const int row = row0 + rr;
         if (row >= a.T) continue;
-        float acc = 0.f;
-        for (int c = 0; c < a.nch; ++c)
-            acc += load_coherent(pb + (size_t)c * 16 * PW + rr * PW + 2 + dim) * wts[rr][c];
-        store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dim, acc / wts[rr][16]);
+        float v[4];
+        for (int q2 = 0; q2 < a.G; ++q2)
+            v[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + rr * PW + 2 + dim) * wts[rr][q2];
+        const float acc = (a.G == 2) ? v[0] + v[1] : (v[0] + v[1]) + (v[2] + v[3]);
+        store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dim, acc / wts[rr][4]);
     }
 }
 
 hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t st) {
     dim3 grid(a.n * a.H, mt);
-    if (hd == 64) hipLaunchKernelGGL(self_attn_kernel<64>, grid, dim3(64), 0, st, a);
-    else if (hd == 16) hipLaunchKernelGGL(self_attn_kernel<16>, grid, dim3(64), 0, st, a);
+    if (hd == 64) hipLaunchKernelGGL(self_attn_kernel<64>, grid, dim3(256), 0, st, a);
+    else if (hd == 16) hipLaunchKernelGGL(self_attn_kernel<16>, grid, dim3(256), 0, st, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st) {
     dim3 grid(a.n_items);
-    if (hd == 64) hipLaunchKernelGGL(cross_attn_kernel<64>, grid, dim3(64), 0, st, a);
-    else if (hd == 16) hipLaunchKernelGGL(cross_attn_kernel<16>, grid, dim3(64), 0, st, a);
+    if (hd == 64) hipLaunchKernelGGL(cross_attn_kernel<64>, grid, dim3(256), 0, st, a);
+    else if (hd == 16) hipLaunchKernelGGL(cross_attn_kernel<16>, grid, dim3(256), 0, st, a);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -92,10 +92,11 @@ struct CrossAttnArgs {
     int64_t slot_stride, layer_off;
     const int32_t *slots, *req_ntok;
     int32_t n, T, H, d, F, F_pad;
-    int32_t mt, nch, cf;           // m-tiles per request, chunks, frames per chunk
-    int32_t n_items;
+    int32_t mt, G, cf, spw;        // m-tiles per request, chunk groups (of 4 chunks),
+                                   // frames per chunk, 32-frame steps per chunk (3k)
+    int32_t n_items;               // n * H * mt * G workgroups
     float scale;
-    float *part;                   // [item][16][hd+2]
+    float *part;                   // [item][16][hd+2] when G > 1
     int32_t *cnt;                  // [n*H*mt]
     uint16_t *out;                 // split-bf16 [M][d]
 };
@@ -173,6 +174,11 @@ hipError_t launch_embed_draft(const EmbedDraftArgs &a, hipStream_t st);
 hipError_t launch_draft_out(const int32_t *anchor, const int32_t *argmax, const int32_t *req_ntok,
                             int n, int K, int32_t *block, hipStream_t st);
 hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
+// register-tiled variant for short blocks: (mb, nb) in {1x1, 1x2, 1x4, 2x2,
+// 2x4, 4x2, 4x4} (the LM head: nb = 4); built for the chunk lengths
+// gemm_rk_built accepts, one wave per chunk of the workgroup's K group
+hipError_t launch_gemm_rk(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
+bool gemm_rk_built(int role, int ck);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
 hipError_t launch_layernorm(const LnArgs &a, hipStream_t st);
