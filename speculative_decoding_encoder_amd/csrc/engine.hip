@@ -115,8 +115,9 @@ Layout layout_of(const wf_config *c) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     L.x = take(M * d * 4);
-    L.xs = take(M * 2 * d * 2);
-    L.hs = take(M * 2 * f * 2);
+    const size_t Mp = (M + 15) / 16 * 16;   // split-bf16 buffers hold whole 16-row tiles
+    L.xs = take(Mp * 2 * d * 2);
+    L.hs = take(Mp * 2 * f * 2);
     L.q = take(M * d * 2);
     L.part = take(part);
     L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 16) * (cdiv((int)M, 16) + 1) * 4);
@@ -129,7 +130,7 @@ Layout layout_of(const wf_config *c) {
     L.len = take((size_t)c->max_batch * 4);
     L.pend = take((size_t)c->max_batch * 4);
     L.err = take((size_t)c->max_batch * 4);
-    L.taps = take(c->drafter_layers > 0 ? M * (size_t)c->n_taps * d * 4 : 0);
+    L.taps = take(c->drafter_layers > 0 ? Mp * (size_t)c->n_taps * d * 4 : 0);
     L.dam = take(M * 4);
     L.total = o;
     return L;
@@ -168,6 +169,7 @@ struct wf_engine {
     int32_t *lmidx;
     int32_t *reqL, *reqN, *len, *pend, *err;
     int tiles_ovr[16][3] = {};               // WF_GEMM_TILES: per role (mb, nb, P)
+    bool ln_fusion = true;                   // WF_LN_FUSION=0 turns the LN prologue off
     // optional per-kernel timing with HIP events
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -204,12 +206,27 @@ wf_status timed(wf_engine *e, int kind, hipStream_t st, F &&launch) {
     return WF_OK;
 }
 
+wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
+    LnArgs a{e->x, M, e->c.d_model, g, b, e->c.ln_eps, e->xs};
+    return timed(e, TK_OTHER, st, [&] { return launch_layernorm(a, st); });
+}
+
+#define WF_TRY_(expr)                     \
+    do {                                  \
+        wf_status _s = (expr);            \
+        if (_s != WF_OK) return _s;       \
+    } while (0)
+
 // Rows up to which the verify-pass GEMMs use the register-tiled kernel.
 constexpr int kRegTiledMaxRows = 1024;
 
+// X W^T with role's epilogue. With lng/lnb the input is LN(x) of the
+// residual stream: fused into the GEMM's prologue for one row tile, else the
+// layer-norm kernel writes X (= xs) first.
 wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                    int K, const uint16_t *W0, const uint16_t *W1, const uint16_t *W2, int seg_n,
-                   int N, const EpiArgs &ea, hipStream_t st) {
+                   int N, const EpiArgs &ea, hipStream_t st, const uint16_t *lng = nullptr,
+                   const uint16_t *lnb = nullptr) {
     GemmArgs a{};
     a.X = X;
     a.W0 = W0;
@@ -228,7 +245,19 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     a.e = ea;
     const bool split_k_ok = role != ROLE_LM_HEAD && role != ROLE_XKV;
     const int mt_need = cdiv(M, 16);
-    if (M <= kRegTiledMaxRows && gemm_rk_built(role, ck)) {
+    const bool rk = M <= kRegTiledMaxRows && gemm_rk_built(role, ck);
+    // the prologue holds a row in registers: K <= 16 * 8 * LN_GPL. Not for
+    // the LM head: its 811 column tiles would each recompute the statistics.
+    const bool fuse_ln = lng && rk && mt_need <= 1 && e->ln_fusion && K <= 1280 &&
+                         role != ROLE_LM_HEAD;
+    if (lng && !fuse_ln) WF_TRY_(run_ln(e, M, lng, lnb, st));
+    if (fuse_ln) {
+        a.lnx = e->x;
+        a.lng = lng;
+        a.lnb = lnb;
+        a.ln_eps = e->c.ln_eps;
+    }
+    if (rk) {
         // Register-tiled kernel (tiles from a sweep on MI355X). One row tile:
         // 16 columns per workgroup and a 2-way K split (a weight-streaming
         // GEMV, latency-bound); the LM head 64 columns. Taller blocks: 32 x 64
@@ -236,9 +265,13 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
         // column tile), and a K split only while the grid is small.
         int mb, nb, P = 1;
         if (mt_need <= 1) {
+            // with the layer-norm prologue every workgroup recomputes the row
+            // statistics: wide projections take 64-column tiles
             mb = 1;
-            nb = role == ROLE_LM_HEAD ? 4 : 1;
-            if (split_k_ok && S >= 2 && (size_t)2 * M * N * 4 <= e->lay.part_bytes) P = 2;
+            nb = (role == ROLE_LM_HEAD || (fuse_ln && N >= 4096)) ? 4 : 1;
+            if (split_k_ok && S >= 2 && cdiv(N, 16 * nb) < 128 &&
+                (size_t)2 * M * N * 4 <= e->lay.part_bytes)
+                P = 2;
         } else {
             mb = role == ROLE_LM_HEAD && mt_need > 2 ? 4 : 2;
             nb = 4;
@@ -249,7 +282,7 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
             }
         }
         const int *o = e->tiles_ovr[role];
-        if (o[0] > 0) {
+        if (o[0] > 0 && (!fuse_ln || (o[0] == 1 && (o[1] == 1 || o[1] == 4)))) {
             mb = o[0];
             nb = o[1];
             if (role == ROLE_LM_HEAD) nb = 4;
@@ -300,11 +333,6 @@ void read_tile_override(wf_engine *e) {
             e->tiles_ovr[role][2] = P;
         }
     }
-}
-
-wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipStream_t st) {
-    LnArgs a{e->x, M, e->c.d_model, g, b, e->c.ln_eps, e->xs};
-    return timed(e, TK_OTHER, st, [&] { return launch_layernorm(a, st); });
 }
 
 #define WF_TRY(expr)                      \
@@ -381,6 +409,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->c = *cfg;
     e->lay = layout_of(cfg);
     read_tile_override(e);
+    if (const char *f = std::getenv("WF_LN_FUSION")) e->ln_fusion = std::strcmp(f, "0") != 0;
     e->F_pad = f_pad_of(cfg);
     e->pt_stride = cfg->n_ctx / cfg->page_size;
     e->page_elems = 2 * cfg->n_heads * cfg->page_size * cfg->head_dim;
@@ -524,12 +553,11 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     ra.x = e->x;
     WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.wo, nullptr, nullptr, d, d, ra,
                     st));
-    WF_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, st));
     EpiArgs fa{};
     fa.b0 = w.bqc;
     fa.out = e->q;
     WF_TRY(run_gemm(e, K_(p, TK_QC), ROLE_CROSS_Q, e->xs, M, d, w.wqc, nullptr, nullptr, d, d, fa,
-                    st));
+                    st, w.ln2_g, w.ln2_b));
     CrossAttnArgs ca{};
     ca.q = e->q;
     ca.xkv = e->xkv;
@@ -558,12 +586,11 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     oa.x = e->x;
     WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.woc, nullptr, nullptr, d, d, oa,
                     st));
-    WF_TRY(run_ln(e, M, w.ln3_g, w.ln3_b, st));
     EpiArgs ga{};
     ga.b0 = w.b1;
     ga.out = e->hs;
     WF_TRY(run_gemm(e, K_(p, TK_FC1), ROLE_FC1, e->xs, M, d, w.w1, nullptr, nullptr, c.d_ffn,
-                    c.d_ffn, ga, st));
+                    c.d_ffn, ga, st, w.ln3_g, w.ln3_b));
     EpiArgs f2{};
     f2.b0 = w.b2;
     f2.x = e->x;
@@ -576,15 +603,14 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
 wf_status run_head(wf_engine *e, const uint16_t *g, const uint16_t *b, const Pass &p,
                    float *d_logits, int32_t *d_argmax, hipStream_t st) {
     const wf_config &c = e->c;
-    WF_TRY(run_ln(e, p.M, g, b, st));
     EpiArgs la{};
     la.logits = d_logits;
     la.tile_max = e->lmmax;
     la.tile_idx = e->lmidx;
-    la.ld = c.max_rows;
+    la.ld = e->lay.n_vtiles;
     WF_TRY(run_gemm(e, K_(p, TK_LMHEAD), ROLE_LM_HEAD, e->xs, p.M, c.d_model, e->tok_emb, nullptr,
-                    nullptr, c.vocab, c.vocab, la, st));
-    LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, c.max_rows, p.M, p.T, p.slots, e->reqN,
+                    nullptr, c.vocab, c.vocab, la, st, g, b));
+    LmReduceArgs lr{e->lmmax, e->lmidx, e->lay.n_vtiles, e->lay.n_vtiles, p.M, p.T, p.slots, e->reqN,
                     e->err, d_argmax};
     return timed(e, K_(p, TK_OTHER), st, [&] { return launch_lm_reduce(lr, st); });
 }
@@ -642,7 +668,6 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         const LayerW &w = e->layers[l];
         uint16_t *kvl = e->kv + (size_t)l * e->kv_layer_elems;
         // self-attention sublayer: QKV with the K/V append, causal attention
-        WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
         EpiArgs qa{};
         qa.b0 = w.bq;
         qa.b2 = w.bv;
@@ -657,7 +682,8 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         qa.H = H;
         qa.hd = hd;
         qa.page_elems = e->page_elems;
-        WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st));
+        WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st,
+                        w.ln1_g, w.ln1_b));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
                         e->page_elems, n, T, H, d, 1, 1.0f / std::sqrt((float)hd), e->xs};
         WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, p.mt, st); }));
@@ -681,12 +707,11 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
                         nullptr, d, d, ha, st));
         for (int dl = 0; dl < c.drafter_layers; ++dl) {
             const LayerW &w = e->dlayers[dl];
-            WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
             EpiArgs ka{};
             ka.b1 = w.bv;
             ka.out32 = reinterpret_cast<float *>(e->hs);
             WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST_KV, e->xs, M, d, w.wk, w.wv, nullptr, d, 2 * d, ka,
-                            st));
+                            st, w.ln1_g, w.ln1_b));
             WF_TRY(run_rope_append(e, dl, p, 2 * d, -1, 0, d, TK_HIST, st));
         }
     }
@@ -714,13 +739,12 @@ wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_
     WF_TRY(timed(e, TK_DRAFT, st, [&] { return launch_embed_draft(ea, st); }));
     for (int dl = 0; dl < c.drafter_layers; ++dl) {
         const LayerW &w = e->dlayers[dl];
-        WF_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, st));
         EpiArgs qa{};
         qa.b0 = w.bq;
         qa.b2 = w.bv;
         qa.out32 = reinterpret_cast<float *>(e->hs);
         WF_TRY(run_gemm(e, TK_DRAFT, ROLE_DRAFT_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa,
-                        st));
+                        st, w.ln1_g, w.ln1_b));
         WF_TRY(run_rope_append(e, dl, p, 3 * d, 0, d, 2 * d, TK_DRAFT, st));
         uint16_t *kvl = e->kv + (size_t)(c.n_layers + dl) * e->kv_layer_elems;
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,

@@ -28,9 +28,9 @@ __device__ __forceinline__ void epi_elem(const GemmArgs &a, int m, int n, float 
         float t = gelu_erf(v + bias_at(e.b0, n));
         uint16_t hi, lo;
         split_bf16(t, hi, lo);
-        size_t base = (size_t)m * (2 * a.N) + (size_t)(n >> 3) * 16 + (n & 7);
+        const size_t base = xt_index(m, n, a.N);
         e.out[base] = hi;
-        e.out[base + 8] = lo;
+        e.out[base + XT_LO] = lo;
     } else if constexpr (EPI == EPI_QKV) {
         const int d = a.seg_n;
         const int seg = n / d;

@@ -15,13 +15,18 @@
 //    tree through scratch. That is also the order of the LDS-staged kernel,
 //    so a row gets the same bits from either kernel whatever M, the tile
 //    shape or P.
+//  * LNX (one row tile): the activations are LN(x) of the fp32 residual
+//    stream, normalised while the fragments are loaded; the row statistics
+//    come from the same code as the standalone layer-norm kernel, so the
+//    fragments carry the bits it would have written.
 #pragma once
 #include "gemm_common.h"
 
 namespace wf {
 
-template <int ROLE, int MB, int NB, int CK>
+template <int ROLE, int MB, int NB, int CK, bool LNX>
 __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
+    static_assert(!LNX || MB == 1, "the layer-norm prologue covers one row tile");
     constexpr int EPI = epi_of(ROLE);
     constexpr bool XS = ROLE != ROLE_XKV;          // split-bf16 activations
     constexpr int NT = MB * NB;
@@ -29,8 +34,10 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     // ring of ~144 VGPRs (~96 for the largest tile over long chunks: no spills)
     constexpr int D0 = (NT >= 16 && CK > 5 ? 24 : 36) / (NX + NB);
     constexpr int D1 = D0 < 1 ? 1 : D0;
-    constexpr int D = D1 > CK ? CK : D1;
-    constexpr int XSTEP = XS ? 64 : 32;            // uint16 per k-step along an X row
+    constexpr int D2 = D1 > CK ? CK : D1;
+    constexpr int D = LNX && D2 > 3 ? 3 : D2;       // LNX also holds a row of x
+    constexpr int XSTEP = XS ? 1024 : 32;          // uint16 per k-step (fragment-tiled X: one
+                                                   // hi + lo block pair per 16-row tile)
     constexpr int BM = 16 * MB, BN = 16 * NB;
     __shared__ f32x4 red[2][NT][64];
 
@@ -52,11 +59,22 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     // their results are never stored, and unconditional loads keep the
     // compiler's wait counts exact, so the ring really overlaps.
     const uint16_t *xp[MB];
+    const float *lxp = nullptr;
+    if constexpr (LNX) {
+        const int m = min(m_base + r16, a.M - 1);
+        lxp = a.lnx + (size_t)m * a.K + (size_t)ts * 32 + g * 8;
+    } else {
 #pragma unroll
-    for (int mt = 0; mt < MB; ++mt) {
-        const int m = min(m_base + mt * 16 + r16, a.M - 1);
-        const size_t off = XS ? (size_t)m * 2 * a.K + g * 16 : (size_t)m * a.K + g * 8;
-        xp[mt] = a.X + off + (size_t)ts * XSTEP;
+        for (int mt = 0; mt < MB; ++mt) {
+            if constexpr (XS) {
+                // whole 16-row tiles are allocated: rows past M are read, never stored
+                const int tile = (m_base >> 4) + mt;
+                xp[mt] = a.X + ((size_t)tile * (a.K >> 5) + ts) * 1024 + (g * 16 + r16) * 8;
+            } else {
+                const int m = min(m_base + mt * 16 + r16, a.M - 1);
+                xp[mt] = a.X + (size_t)m * a.K + g * 8 + (size_t)ts * 32;
+            }
+        }
     }
     const uint16_t *wp[NB];
 #pragma unroll
@@ -66,29 +84,71 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
         const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
         wp[nt] = wb + (size_t)(n - seg * a.seg_n) * a.K + g * 8 + (size_t)ts * 32;
     }
-    struct Fr { u32x4 x[NX]; u32x4 w[NB]; };
+    struct Fr {
+        u32x4 x[NX];
+        float4 lx0, lx1;     // LNX: raw x of the fragment's 8 columns
+        u32x4 lg, lb;        // LNX: their gains and biases
+        u32x4 w[NB];
+    };
     auto load = [&](Fr &fr, int s) {
+        if constexpr (LNX) {
+            fr.lx0 = *reinterpret_cast<const float4 *>(lxp + s * 32);
+            fr.lx1 = *reinterpret_cast<const float4 *>(lxp + s * 32 + 4);
+            const int k0 = (ts + s) * 32 + g * 8;
+            fr.lg = ld16(a.lng + k0);
+            fr.lb = ld16(a.lnb + k0);
+        } else {
 #pragma unroll
-        for (int mt = 0; mt < MB; ++mt) {
-            fr.x[mt] = ld16(xp[mt] + s * XSTEP);
-            if constexpr (XS) fr.x[MB + mt] = ld16(xp[mt] + s * XSTEP + 8);
+            for (int mt = 0; mt < MB; ++mt) {
+                fr.x[mt] = ld16(xp[mt] + s * XSTEP);
+                if constexpr (XS) fr.x[MB + mt] = ld16(xp[mt] + s * XSTEP + XT_LO);
+            }
         }
 #pragma unroll
         for (int nt = 0; nt < NB; ++nt) fr.w[nt] = ld16(wp[nt] + s * 32);
     };
 
+    // LNX: row 4w+g of x goes out first (16 lanes per row), then the ring;
+    // its statistics are reduced from registers while the ring is in
+    // flight. With fewer than four waves, later rows (4w+g + 4W i) follow.
+    LnRow lrow;
+    const int ln_rows = min(16, a.M - m_base);
+    if constexpr (LNX) {
+        if (4 * wave < ln_rows)
+            ln_load16(a.lnx + (size_t)(m_base + min(4 * wave + g, ln_rows - 1)) * a.K, a.K, r16,
+                      lrow);
+    }
     // sched_barrier(0) pins the issue order (the scheduler would otherwise
     // sink the ring's loads next to their MFMAs to save registers)
     Fr f[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) load(f[i], i);
     __builtin_amdgcn_sched_barrier(0);
+    float ln_mean = 0.f, ln_rstd = 0.f;
+    if constexpr (LNX) {
+        __shared__ float lnst[16][2];
+        for (int r = 4 * wave + g; r < ln_rows; r += 4 * W) {
+            if (r >= 4 * W) ln_load16(a.lnx + (size_t)(m_base + r) * a.K, a.K, r16, lrow);
+            float mean, rstd;
+            ln_reduce16(lrow, a.K, r16, a.ln_eps, mean, rstd);
+            if (r16 == 0) {
+                lnst[r][0] = mean;
+                lnst[r][1] = rstd;
+            }
+        }
+        __syncthreads();
+        const int rr = min(r16, ln_rows - 1);
+        ln_mean = lnst[rr][0];
+        ln_rstd = lnst[rr][1];
+    }
     f32x4 c[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < CK; ++s) {
         Fr &cur = f[s % D];
+        if constexpr (LNX) ln_split8(cur.lx0, cur.lx1, cur.lg, cur.lb, ln_mean, ln_rstd, cur.x[0],
+                                     cur.x[1]);
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
@@ -162,8 +222,8 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
                     nn |= __shfl_xor(nn, o);
                 }
                 if (r16 == 0 && m < a.M) {
-                    e.tile_max[(size_t)ntile * e.ld + m] = bv;
-                    e.tile_idx[(size_t)ntile * e.ld + m] = nn ? -1 : bi;
+                    e.tile_max[(size_t)m * e.ld + ntile] = bv;
+                    e.tile_idx[(size_t)m * e.ld + ntile] = nn ? -1 : bi;
                 }
             }
         }
@@ -214,11 +274,12 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     }
 }
 
-template <int ROLE, int MB, int NB, int CK>
+template <int ROLE, int MB, int NB, int CK, bool LNX>
 hipError_t launch_rk(const GemmArgs &a, hipStream_t st) {
     const int grid = ((a.n_wg + 7) / 8) * 8;
     const int waves = a.S / a.n_groups;
-    hipLaunchKernelGGL((gemm_rk_kernel<ROLE, MB, NB, CK>), dim3(grid), dim3(64 * waves), 0, st, a);
+    hipLaunchKernelGGL((gemm_rk_kernel<ROLE, MB, NB, CK, LNX>), dim3(grid), dim3(64 * waves), 0, st,
+                       a);
     return hipGetLastError();
 }
 
@@ -231,36 +292,51 @@ constexpr bool rk_ck_built(int ck) {
          : ROLE == ROLE_HIST ? (ck == 5 || ck == 25)
          : (ck == 1 || ck == 5);
 }
+// roles whose input is a layer norm of the residual stream
+template <int ROLE>
+constexpr bool rk_has_ln() {
+    return ROLE == ROLE_QKV || ROLE == ROLE_CROSS_Q || ROLE == ROLE_FC1 || ROLE == ROLE_LM_HEAD ||
+           ROLE == ROLE_DRAFT_QKV || ROLE == ROLE_HIST_KV;
+}
 
-template <int ROLE, int MB, int NB>
+template <int ROLE, int MB, int NB, bool LNX>
 hipError_t launch_rk_ck(const GemmArgs &a, hipStream_t st) {
     switch (a.ck) {
-        case 1: if constexpr (rk_ck_built<ROLE>(1)) return launch_rk<ROLE, MB, NB, 1>(a, st); break;
-        case 5: if constexpr (rk_ck_built<ROLE>(5)) return launch_rk<ROLE, MB, NB, 5>(a, st); break;
-        case 20: if constexpr (rk_ck_built<ROLE>(20)) return launch_rk<ROLE, MB, NB, 20>(a, st); break;
-        case 25: if constexpr (rk_ck_built<ROLE>(25)) return launch_rk<ROLE, MB, NB, 25>(a, st); break;
+        case 1: if constexpr (rk_ck_built<ROLE>(1)) return launch_rk<ROLE, MB, NB, 1, LNX>(a, st); break;
+        case 5: if constexpr (rk_ck_built<ROLE>(5)) return launch_rk<ROLE, MB, NB, 5, LNX>(a, st); break;
+        case 20: if constexpr (rk_ck_built<ROLE>(20)) return launch_rk<ROLE, MB, NB, 20, LNX>(a, st); break;
+        case 25: if constexpr (rk_ck_built<ROLE>(25)) return launch_rk<ROLE, MB, NB, 25, LNX>(a, st); break;
     }
     return hipErrorInvalidValue;
 }
 
 template <int ROLE>
 hipError_t launch_rk_role(const GemmArgs &a, int mb, int nb, hipStream_t st) {
+    if (a.lnx) {
+        // layer-norm prologue: one row tile, 16 or 64 columns (the LM head 64)
+        if constexpr (rk_has_ln<ROLE>()) {
+            if (mb == 1 && nb == 4) return launch_rk_ck<ROLE, 1, 4, true>(a, st);
+            if constexpr (ROLE != ROLE_LM_HEAD)
+                if (mb == 1 && nb == 1) return launch_rk_ck<ROLE, 1, 1, true>(a, st);
+        }
+        return hipErrorInvalidValue;
+    }
     if constexpr (ROLE == ROLE_LM_HEAD) {
         switch (mb) {
-            case 1: return launch_rk_ck<ROLE, 1, 4>(a, st);
-            case 2: return launch_rk_ck<ROLE, 2, 4>(a, st);
-            case 4: return launch_rk_ck<ROLE, 4, 4>(a, st);
+            case 1: return launch_rk_ck<ROLE, 1, 4, false>(a, st);
+            case 2: return launch_rk_ck<ROLE, 2, 4, false>(a, st);
+            case 4: return launch_rk_ck<ROLE, 4, 4, false>(a, st);
         }
         return hipErrorInvalidValue;
     } else {
         switch (mb * 8 + nb) {
-            case 1 * 8 + 1: return launch_rk_ck<ROLE, 1, 1>(a, st);
-            case 1 * 8 + 2: return launch_rk_ck<ROLE, 1, 2>(a, st);
-            case 1 * 8 + 4: return launch_rk_ck<ROLE, 1, 4>(a, st);
-            case 2 * 8 + 2: return launch_rk_ck<ROLE, 2, 2>(a, st);
-            case 2 * 8 + 4: return launch_rk_ck<ROLE, 2, 4>(a, st);
-            case 4 * 8 + 2: return launch_rk_ck<ROLE, 4, 2>(a, st);
-            case 4 * 8 + 4: return launch_rk_ck<ROLE, 4, 4>(a, st);
+            case 1 * 8 + 1: return launch_rk_ck<ROLE, 1, 1, false>(a, st);
+            case 1 * 8 + 2: return launch_rk_ck<ROLE, 1, 2, false>(a, st);
+            case 1 * 8 + 4: return launch_rk_ck<ROLE, 1, 4, false>(a, st);
+            case 2 * 8 + 2: return launch_rk_ck<ROLE, 2, 2, false>(a, st);
+            case 2 * 8 + 4: return launch_rk_ck<ROLE, 2, 4, false>(a, st);
+            case 4 * 8 + 2: return launch_rk_ck<ROLE, 4, 2, false>(a, st);
+            case 4 * 8 + 4: return launch_rk_ck<ROLE, 4, 4, false>(a, st);
         }
         return hipErrorInvalidValue;
     }

@@ -88,12 +88,13 @@ __device__ __forceinline__ void softmax_step(f32x4 &s0, f32x4 &s1, float (&mrun)
     }
 }
 
-__device__ __forceinline__ void store_split(uint16_t *out, size_t row_off, int c, float v) {
+// element (row, c) of a fragment-tiled split-bf16 buffer of width K
+__device__ __forceinline__ void store_split(uint16_t *out, int row, int c, int K, float v) {
     uint16_t hi, lo;
     split_bf16(v, hi, lo);
-    const size_t base = row_off + (size_t)(c >> 3) * 16 + (c & 7);
+    const size_t base = xt_index(row, c, K);
     out[base] = hi;
-    out[base + 8] = lo;
+    out[base + XT_LO] = lo;
 }
 
 // Intra-wave ordering of LDS traffic (the P tile is private to a wave).
@@ -229,14 +230,13 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
     const int row0 = blockIdx.y * 16;
     const int ntok = a.req_ntok[b];
-    const size_t ld_out = (size_t)2 * a.d;
 
     if (ntok == 0 || row0 >= ntok) {
         // skipped request or a tile of padding rows: zeros
         for (int idx = tid; idx < 16 * HD; idx += 256) {
             const int rr = idx / HD, c = idx - rr * HD;
             const int row = row0 + rr;
-            if (row < a.T) store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + c, 0.f);
+            if (row < a.T) store_split(a.out, b * a.T + row, h * HD + c, a.d, 0.f);
         }
         return;
     }
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * g + r;
                 if (row < a.T)
-                    store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dt * 16 + r16,
+                    store_split(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
                                 st.o[dt][r] / st.l[r]);
             }
     }
@@ -323,7 +323,6 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
     const int ntok = a.req_ntok[b];
     if (ntok == 0) return;                    // every group of this request skips
     const int row0 = mtile * 16;
-    const size_t ld_out = (size_t)2 * a.d;
 
     const uint16_t *base = a.xkv + (size_t)a.slots[b] * a.slot_stride + a.layer_off;
     const uint16_t *kh = base + (size_t)h * a.F_pad * HD;
@@ -374,8 +373,8 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int row = row0 + 4 * g + r;
                     if (row < a.T)
-                        store_split(a.out, (size_t)(b * a.T + row) * ld_out,
-                                    h * HD + dt * 16 + r16, st.o[dt][r] / st.l[r]);
+                        store_split(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
+                                    st.o[dt][r] / st.l[r]);
                 }
         }
         return;
@@ -430,7 +429,7 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
         for (int q2 = 0; q2 < a.G; ++q2)
             v[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + rr * PW + 2 + dim) * wts[rr][q2];
         const float acc = (a.G == 2) ? v[0] + v[1] : (v[0] + v[1]) + (v[2] + v[3]);
-        store_split(a.out, (size_t)(b * a.T + row) * ld_out, h * HD + dim, acc / wts[rr][4]);
+        store_split(a.out, b * a.T + row, h * HD + dim, a.d, acc / wts[rr][4]);
     }
 }
 

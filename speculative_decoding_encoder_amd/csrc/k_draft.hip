@@ -20,7 +20,6 @@ __global__ __launch_bounds__(256) void tap_kernel(TapArgs a) {
     if (m >= a.M) return;
     const float *x = a.x + (size_t)m * a.d;
     const size_t width = (size_t)a.n_taps * a.d;
-    uint16_t *out = a.out + (size_t)m * 2 * width + (size_t)(a.j * a.d / 8) * 16;
     for (int kg = lane; kg < a.d / 8; kg += 64) {
         u32x4 vh, vl;
         for (int j = 0; j < 4; ++j) {
@@ -30,8 +29,9 @@ __global__ __launch_bounds__(256) void tap_kernel(TapArgs a) {
             vh[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
             vl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
-        *reinterpret_cast<u32x4 *>(out + kg * 16) = vh;
-        *reinterpret_cast<u32x4 *>(out + kg * 16 + 8) = vl;
+        uint16_t *o = a.out + xt_index(m, a.j * a.d + kg * 8, (int)width);
+        *reinterpret_cast<u32x4 *>(o) = vh;
+        *reinterpret_cast<u32x4 *>(o + XT_LO) = vl;
     }
 }
 

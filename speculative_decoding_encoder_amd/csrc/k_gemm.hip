@@ -125,9 +125,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 const int rr = r2 / XPARTS, part = r2 - (r2 / XPARTS) * XPARTS;
                 const int k0 = (tb + kk) * 32;
                 if (rr < rows) {
-                    if constexpr (XS)
-                        xr[v] = ld16(a.X + (size_t)(m_base + rr) * (2 * a.K) +
-                                     (size_t)(k0 >> 3) * 16 + part * 8);
+                    if constexpr (XS)   // part = 2 g + (0: hi, 1: lo), fragment-tiled X
+                        xr[v] = ld16(a.X + xt_index(m_base + rr, k0 + 8 * (part >> 1), a.K) +
+                                     (part & 1) * XT_LO);
                     else
                         xr[v] = ld16(a.X + (size_t)(m_base + rr) * a.K + k0 + part * 8);
                 }
@@ -246,8 +246,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                     argmax_merge(bv, bi, smax[w][tid], sidx[w][tid]);
                     nn |= snan[w][tid];
                 }
-                e.tile_max[(size_t)ntile * e.ld + m] = bv;
-                e.tile_idx[(size_t)ntile * e.ld + m] = nn ? -1 : bi;
+                e.tile_max[(size_t)m * e.ld + ntile] = bv;
+                e.tile_idx[(size_t)m * e.ld + ntile] = nn ? -1 : bi;
             }
         }
         return;

@@ -44,84 +44,91 @@ __global__ void prepare_kernel(PrepareArgs a) {
     a.req_ntok[b] = code == 0 ? nt : 0;
 }
 
-// x[m] = tok_emb[token] + pos_emb[L + i]  (fp32). One wave per row; tokens
-// and positions are clamped so that padding rows stay in bounds.
+// x[m] = tok_emb[token] + pos_emb[L + i]  (fp32). One thread per 8 columns
+// of a row; tokens and positions are clamped so that padding rows stay in
+// bounds.
 __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (m >= a.M) return;
+    const int ng = a.d >> 3;
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (long)a.M * ng) return;
+    const int m = (int)(idx / ng), kg = (int)(idx - (long)m * ng);
     const int b = m / a.T, i = m - (m / a.T) * a.T;
     int tok = a.tokens[m];
     tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
     int pos = a.req_L[b] + i;
     pos = pos >= a.n_ctx ? a.n_ctx - 1 : pos;
-    const uint16_t *e = a.tok_emb + (size_t)tok * a.d;
-    const uint16_t *p = a.pos_emb + (size_t)pos * a.d;
-    float *x = a.x + (size_t)m * a.d;
-    for (int c = lane; c < a.d; c += 64) x[c] = bf2f(e[c]) + bf2f(p[c]);
+    const u32x4 e = ld16(a.tok_emb + (size_t)tok * a.d + kg * 8);
+    const u32x4 p = ld16(a.pos_emb + (size_t)pos * a.d + kg * 8);
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        v[2 * j] = bf2f((uint16_t)(e[j] & 0xffffu)) + bf2f((uint16_t)(p[j] & 0xffffu));
+        v[2 * j + 1] = bf2f((uint16_t)(e[j] >> 16)) + bf2f((uint16_t)(p[j] >> 16));
+    }
+    float *x = a.x + (size_t)m * a.d + kg * 8;
+    *reinterpret_cast<float4 *>(x) = make_float4(v[0], v[1], v[2], v[3]);
+    *reinterpret_cast<float4 *>(x + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Layer norm of fp32 rows into the split-bf16 operand layout
-// [M][d/8][hi 8 | lo 8]. Mean and variance in fp32, two passes, fixed
-// reduction order. One wave per row; a lane owns groups of 8 columns.
-__global__ __launch_bounds__(256) void layernorm_kernel(LnArgs a) {
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+// Layer norm of the fp32 residual stream into fragment-tiled split-bf16
+// activations (ln_load16 / ln_reduce16 / ln_apply): 16 lanes per row, 4 rows
+// per workgroup.
+__global__ __launch_bounds__(64) void layernorm_kernel(LnArgs a) {
+    const int m = blockIdx.x * 4 + (threadIdx.x >> 4);
+    const int r16 = threadIdx.x & 15;
     if (m >= a.M) return;
     const float *x = a.x + (size_t)m * a.d;
-    const int ng = a.d >> 3;
-    float s = 0.f;
-    for (int kg = lane; kg < ng; kg += 64) {
-        const float4 v0 = *reinterpret_cast<const float4 *>(x + kg * 8);
-        const float4 v1 = *reinterpret_cast<const float4 *>(x + kg * 8 + 4);
-        s += ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
-    }
-    const float mean = wave_sum(s) / (float)a.d;
-    float q = 0.f;
-    for (int kg = lane; kg < ng; kg += 64) {
-        for (int j = 0; j < 8; ++j) {
-            const float t = x[kg * 8 + j] - mean;
-            q += t * t;
-        }
-    }
-    const float var = wave_sum(q) / (float)a.d;
-    const float rstd = 1.0f / sqrtf(var + a.eps);
-    uint16_t *out = a.out + (size_t)m * 2 * a.d;
-    for (int kg = lane; kg < ng; kg += 64) {
-        uint16_t hi[8], lo[8];
-        for (int j = 0; j < 8; ++j) {
-            const int c = kg * 8 + j;
-            const float y = (x[c] - mean) * rstd * bf2f(a.g[c]) + bf2f(a.b[c]);
-            split_bf16(y, hi[j], lo[j]);
-        }
+    LnRow row;
+    ln_load16(x, a.d, r16, row);
+    float mean, rstd;
+    ln_reduce16(row, a.d, r16, a.eps, mean, rstd);
+#pragma unroll
+    for (int i = 0; i < LN_GPL; ++i) {
+        const int kg = r16 + 16 * i;
+        if (kg >= (a.d >> 3)) break;
+        const int c = kg * 8;
         u32x4 vh, vl;
-        for (int j = 0; j < 4; ++j) {
-            vh[j] = (uint32_t)hi[2 * j] | ((uint32_t)hi[2 * j + 1] << 16);
-            vl[j] = (uint32_t)lo[2 * j] | ((uint32_t)lo[2 * j + 1] << 16);
-        }
-        *reinterpret_cast<u32x4 *>(out + kg * 16) = vh;
-        *reinterpret_cast<u32x4 *>(out + kg * 16 + 8) = vl;
+        ln_split8(row.v[2 * i], row.v[2 * i + 1], ld16(a.g + c), ld16(a.b + c), mean, rstd, vh, vl);
+        uint16_t *o = a.out + xt_index(m, c, a.d);
+        *reinterpret_cast<u32x4 *>(o) = vh;
+        *reinterpret_cast<u32x4 *>(o + XT_LO) = vl;
     }
 }
 
 // Per row: merge the LM head's per-tile (max, lowest argmax) in a fixed
 // order. -1 for rows of skipped requests and for padding rows; a NaN logit
 // flags the slot.
+// One workgroup per row; the row's tiles are contiguous ([M][ld]).
 __global__ __launch_bounds__(256) void lm_reduce_kernel(LmReduceArgs a) {
-    const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    if (m >= a.M) return;
+    __shared__ float sv[4];
+    __shared__ int si[4], sn[4];
+    const int m = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     float v = -INFINITY;
     int idx = 0x7fffffff;
     int nan = 0;
-    for (int t = lane; t < a.n_tiles; t += 64) {
-        const int ti = a.tile_idx[(size_t)t * a.ld + m];
-        if (ti < 0) { nan = 1; continue; }
-        argmax_merge(v, idx, a.tile_max[(size_t)t * a.ld + m], ti);
+    const float *tm = a.tile_max + (size_t)m * a.ld;
+    const int32_t *tx = a.tile_idx + (size_t)m * a.ld;
+#pragma unroll 4
+    for (int t = tid; t < a.n_tiles; t += 256) {
+        const int ti = tx[t];
+        const float tv = tm[t];
+        if (ti < 0) nan = 1;
+        else argmax_merge(v, idx, tv, ti);
     }
     wave_argmax(v, idx);
     for (int o = 1; o < 64; o <<= 1) nan |= __shfl_xor(nan, o);
     if (lane == 0) {
+        sv[wave] = v;
+        si[wave] = idx;
+        sn[wave] = nan;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w = 1; w < 4; ++w) {
+            argmax_merge(v, idx, sv[w], si[w]);
+            nan |= sn[w];
+        }
         const int b = m / a.T, i = m - (m / a.T) * a.T;
         int out = idx;
         if (i >= a.req_ntok[b]) out = -1;
@@ -222,15 +229,16 @@ hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(embed_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(embed_kernel, dim3((unsigned)(((long)a.M * (a.d >> 3) + 255) / 256)),
+                       dim3(256), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_layernorm(const LnArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(layernorm_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(layernorm_kernel, dim3((a.M + 3) / 4), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st) {
-    hipLaunchKernelGGL(lm_reduce_kernel, dim3((a.M + 3) / 4), dim3(256), 0, st, a);
+    hipLaunchKernelGGL(lm_reduce_kernel, dim3(a.M), dim3(256), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st) {

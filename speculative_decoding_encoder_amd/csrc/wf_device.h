@@ -34,6 +34,18 @@ __device__ __forceinline__ f32x4 mfma_f16_k16(u32x2 a, u32x2 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
+// Split-bf16 activations (x = hi + lo, both bf16) are stored fragment-tiled:
+// for each 16-row tile and 32-column step, a 1 KB hi block then a 1 KB lo
+// block, each in the lane order of the MFMA A operand (lane g*16 + r holds
+// row r, columns 8g..8g+7). A fragment load is one contiguous 1 KB read.
+// Buffers hold whole 16-row tiles. xt_index gives the hi element of (m, k);
+// its lo element is XT_LO further.
+#define XT_LO 512
+__host__ __device__ __forceinline__ size_t xt_index(int m, int k, int K) {
+    return (((size_t)(m >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 128 +
+            (size_t)(((k >> 3) & 3) * 16 + (m & 15))) * 8 + (size_t)(k & 7);
+}
+
 // bf16 <-> fp32. Rounding to bf16 is to nearest, ties to even.
 __device__ __forceinline__ float bf2f(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
@@ -113,4 +125,74 @@ __device__ __forceinline__ int arrive(int *cnt) {
 }
 __device__ __forceinline__ void rearm(int *cnt) {
     __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Layer norm of one row by the 16 lanes of a lane group (lanes 16q..16q+15):
+// lane r16 owns the 8-column groups r16, r16+16, ... (rows up to
+// 16 * 8 * LN_GPL columns), holds them in registers, and the mean and
+// variance come from two passes over those registers in a fixed order with
+// the sum16 butterfly. The normalised value is fma((x - mean) * rstd, gain,
+// bias). The standalone kernel and the GEMM prologue both use exactly this,
+// so a row normalises to the same bits either way.
+#define LN_GPL 10
+struct LnRow {
+    float4 v[2 * LN_GPL];
+};
+// Loads only (clamped to the row: unconditional, so they can be in flight
+// together with other loads issued after them).
+__device__ __forceinline__ void ln_load16(const float *xrow, int d, int r16, LnRow &row) {
+    const int last = (d >> 3) - 1;
+#pragma unroll
+    for (int i = 0; i < LN_GPL; ++i) {
+        const int kg = min(r16 + 16 * i, last);
+        row.v[2 * i] = *reinterpret_cast<const float4 *>(xrow + kg * 8);
+        row.v[2 * i + 1] = *reinterpret_cast<const float4 *>(xrow + kg * 8 + 4);
+    }
+}
+__device__ __forceinline__ void ln_reduce16(const LnRow &row, int d, int r16, float eps,
+                                            float &mean, float &rstd) {
+    const int ng = d >> 3;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_GPL; ++i) {
+        if (r16 + 16 * i < ng) {
+            const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
+            s += ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
+        }
+    }
+    mean = sum16(s) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < LN_GPL; ++i) {
+        if (r16 + 16 * i < ng) {
+            const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
+            const float t[8] = {v0.x - mean, v0.y - mean, v0.z - mean, v0.w - mean,
+                                v1.x - mean, v1.y - mean, v1.z - mean, v1.w - mean};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q = __fmaf_rn(t[j], t[j], q);
+        }
+    }
+    const float var = sum16(q) / (float)d;
+    rstd = 1.0f / sqrtf(var + eps);
+}
+__device__ __forceinline__ float ln_apply(float x, float mean, float rstd, float g, float b) {
+    return __fmaf_rn((x - mean) * rstd, g, b);
+}
+// Eight consecutive columns (x at c..c+7, gains and biases as bf16x8) to one
+// split-bf16 fragment pair.
+__device__ __forceinline__ void ln_split8(float4 x0, float4 x1, u32x4 gg, u32x4 bb, float mean,
+                                          float rstd, u32x4 &vh, u32x4 &vl) {
+    const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        uint16_t h0, l0, h1, l1;
+        const float y0 = ln_apply(xv[2 * j], mean, rstd, bf2f((uint16_t)(gg[j] & 0xffffu)),
+                                  bf2f((uint16_t)(bb[j] & 0xffffu)));
+        const float y1 = ln_apply(xv[2 * j + 1], mean, rstd, bf2f((uint16_t)(gg[j] >> 16)),
+                                  bf2f((uint16_t)(bb[j] >> 16)));
+        split_bf16(y0, h0, l0);
+        split_bf16(y1, h1, l1);
+        vh[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        vl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+    }
 }

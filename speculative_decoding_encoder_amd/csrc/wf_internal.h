@@ -36,13 +36,13 @@ struct EpiArgs {
     int32_t max_batch;             // slot ids outside [0, max_batch) are skipped
     // EPI_ARGMAX
     float *logits;                 // null or [M][V]
-    float *tile_max;               // [n_tiles][ld]
+    float *tile_max;               // [M][ld]: per row, its 64-column tiles
     int32_t *tile_idx;
     int32_t ld;
 };
 
 struct GemmArgs {
-    const uint16_t *X;             // split-bf16 [M][K/8][hi 8 | lo 8], or plain bf16 [M][K]
+    const uint16_t *X;             // split-bf16, fragment-tiled (xt_index), or plain bf16 [M][K]
     const uint16_t *W0, *W1, *W2;  // weight segments, each [seg_n][K] bf16
     int32_t M, K, N, seg_n;
     int32_t S, ck;                 // K chunks (fixed per K) and k-steps per chunk
@@ -50,6 +50,11 @@ struct GemmArgs {
     int32_t n_wg;                  // logical workgroups (grid is padded to 8k)
     float *part;                   // subtree sums [P][M][N] when P > 1
     int32_t *cnt;                  // arrival counters [n_tiles * m_blocks]
+    // layer norm in the prologue (register-tiled kernel, one row tile): X is
+    // LN(lnx) computed on the fly; lnx is the fp32 residual stream [M][K]
+    const float *lnx;
+    const uint16_t *lng, *lnb;
+    float ln_eps;
     EpiArgs e;
 };
 
@@ -72,7 +77,7 @@ struct LnArgs {
     int32_t M, d;
     const uint16_t *g, *b;
     float eps;
-    uint16_t *out;                 // split-bf16 [M][d/8][16]
+    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
 };
 
 struct SelfAttnArgs {
@@ -83,7 +88,7 @@ struct SelfAttnArgs {
     int32_t n, T, H, d;
     int32_t causal;                // 1: row i sees keys <= L+i; 0: the whole block
     float scale;
-    uint16_t *out;                 // split-bf16 [M][d]
+    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
 };
 
 struct CrossAttnArgs {
@@ -98,13 +103,13 @@ struct CrossAttnArgs {
     float scale;
     float *part;                   // [item][16][hd+2] when G > 1
     int32_t *cnt;                  // [n*H*mt]
-    uint16_t *out;                 // split-bf16 [M][d]
+    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
 };
 
 struct LmReduceArgs {
     const float *tile_max;
     const int32_t *tile_idx;
-    int32_t n_tiles, ld, M, T;
+    int32_t n_tiles, ld, M, T;     // tiles [M][ld]
     const int32_t *slots, *req_ntok;
     int32_t *slot_err;
     int32_t *argmax;
@@ -140,7 +145,7 @@ enum Role : int {
 struct TapArgs {
     const float *x;
     int32_t M, d, j, n_taps;
-    uint16_t *out;                 // split-bf16 [M][n_taps*d]
+    uint16_t *out;                 // split-bf16 [M][n_taps*d], fragment-tiled
 };
 
 struct RopeArgs {

@@ -114,6 +114,40 @@ def test_tiny_block_rows_equal_single_rows_bitwise(tiny):
     assert np.array_equal(np.stack(rows).view(np.uint32), lg_block[0].view(np.uint32))
 
 
+def test_tiny_fused_layer_norm_bitwise(tiny):
+    """Blocks of at most 16 rows normalise inside the GEMM prologue, taller
+    blocks run the layer-norm kernel first: a row's logits must not depend
+    on which (same block through an engine with the prologue turned off,
+    and the block of one request beside three others: 20 rows)."""
+    import os
+    eng, wbits = tiny["eng"], tiny["wbits"]
+    prefix, greedy = tiny["prefix"], tiny["greedy"]
+    P = len(prefix)
+    block = np.array(greedy[:5], np.int32)
+    enc = tiny["enc"]
+
+    def run(e, n):
+        slots = list(range(n))
+        e.wf_reset(e.i32(slots))
+        e.wf_encode_kv(e.i32(slots), e.bf16(np.stack([enc] * n)))
+        _verify(e, slots, np.stack([prefix] * n), [P] * n, logits=False)
+        e.wf_rollback(e.i32(slots), e.i32([P - 1] * n))
+        return _verify(e, slots, np.stack([block] * n), [5] * n)[1]
+
+    fused = run(eng, 1)[0]
+    os.environ["WF_LN_FUSION"] = "0"
+    try:
+        plain_eng = _engine(TINY, wbits, max_batch=4, max_rows=512)
+    finally:
+        del os.environ["WF_LN_FUSION"]
+    plain = run(plain_eng, 1)[0]
+    assert np.array_equal(fused.view(np.uint32), plain.view(np.uint32))
+    four = run(eng, 4)
+    for r in range(4):
+        assert np.array_equal(four[r].view(np.uint32), fused.view(np.uint32)), r
+    plain_eng.close()
+
+
 def test_tiny_speculative_equals_greedy_on_gpu(tiny):
     from speculative_decoding_encoder_amd.harness import run_loop, table_drafter
     eng, wl = tiny["eng"], tiny["wl"]
