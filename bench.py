@@ -49,11 +49,13 @@ TOKENS_PER_AUDIO_S = 3.5
 METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
 KIND_NAMES = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
               "cross_attn", "other", "encode_kv", "draft", "history"]
-# kernel symbol (rocprofv3 name prefix) of each timing kind; the GEMM's first
-# template argument is its role
+# kernel symbols (rocprofv3 name prefixes) of each timing kind: a GEMM role
+# runs the register-tiled, the tall-block or the LDS-staged kernel by block
+# height; the first template argument is the role
 KIND_SYMBOL = {
-    "qkv": "wf::gemm_kernel<0,", "oproj": "wf::gemm_kernel<1,", "cross_q": "wf::gemm_kernel<2,",
-    "fc1": "wf::gemm_kernel<3,", "fc2": "wf::gemm_kernel<4,", "lm_head": "wf::gemm_kernel<5,",
+    **{k: "|".join(f"wf::{kern}<{r}," for kern in ("gemm_rk_kernel", "gemm_tl_kernel",
+                                                    "gemm_kernel"))
+       for r, k in enumerate(["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head"])},
     "self_attn": "wf::self_attn_kernel<64>", "cross_attn": "wf::cross_attn_kernel<64>",
 }
 

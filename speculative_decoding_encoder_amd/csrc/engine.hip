@@ -170,6 +170,7 @@ struct wf_engine {
     int32_t *reqL, *reqN, *len, *pend, *err;
     int tiles_ovr[16][3] = {};               // WF_GEMM_TILES: per role (mb, nb, P)
     bool ln_fusion = true;                   // WF_LN_FUSION=0 turns the LN prologue off
+    bool tall_gemm = true;                   // WF_TALL_GEMM=0 turns the tall-block kernel off
     // optional per-kernel timing with HIP events
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -219,6 +220,9 @@ wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipS
 
 // Rows up to which the verify-pass GEMMs use the register-tiled kernel.
 constexpr int kRegTiledMaxRows = 1024;
+// Row range in which QKV and fc1 use the tall-block kernel (on MI355X at 288
+// rows: QKV 34 us against 40, fc1 28 against 38; on par at 864 rows).
+constexpr int kTallMinRows = 97, kTallMaxRows = 576;
 
 // X W^T with role's epilogue. With lng/lnb the input is LN(x) of the
 // residual stream: fused into the GEMM's prologue for one row tile, else the
@@ -256,6 +260,15 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
         a.lng = lng;
         a.lnb = lnb;
         a.ln_eps = e->c.ln_eps;
+    }
+    if (e->tall_gemm && M >= kTallMinRows && M <= kTallMaxRows && gemm_tl_built(role, S, ck) &&
+        !fuse_ln) {
+        // tall blocks (tens of requests): 96 x 64 tiles over the whole of K
+        a.n_tiles = cdiv(N, 64);
+        a.m_blocks = cdiv(M, 96);
+        a.n_groups = 1;
+        a.n_wg = a.n_tiles * a.m_blocks;
+        return timed(e, kind, st, [&] { return launch_gemm_tl(role, a, st); });
     }
     if (rk) {
         // Register-tiled kernel (tiles from a sweep on MI355X). One row tile:
@@ -410,6 +423,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->lay = layout_of(cfg);
     read_tile_override(e);
     if (const char *f = std::getenv("WF_LN_FUSION")) e->ln_fusion = std::strcmp(f, "0") != 0;
+    if (const char *f = std::getenv("WF_TALL_GEMM")) e->tall_gemm = std::strcmp(f, "0") != 0;
     e->F_pad = f_pad_of(cfg);
     e->pt_stride = cfg->n_ctx / cfg->page_size;
     e->page_elems = 2 * cfg->n_heads * cfg->page_size * cfg->head_dim;

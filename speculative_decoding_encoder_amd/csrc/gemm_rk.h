@@ -67,8 +67,9 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt) {
             if constexpr (XS) {
-                // whole 16-row tiles are allocated: rows past M are read, never stored
-                const int tile = (m_base >> 4) + mt;
+                // rows of the last tile past M are read, never stored; tiles
+                // past the last one repeat it
+                const int tile = min((m_base >> 4) + mt, (a.M - 1) >> 4);
                 xp[mt] = a.X + ((size_t)tile * (a.K >> 5) + ts) * 1024 + (g * 16 + r16) * 8;
             } else {
                 const int m = min(m_base + mt * 16 + r16, a.M - 1);

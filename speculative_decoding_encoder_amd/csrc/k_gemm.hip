@@ -314,6 +314,21 @@ hipError_t launch_gemm_rk_a(int role, const GemmArgs &a, int mb, int nb, hipStre
 hipError_t launch_gemm_rk_b(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 hipError_t launch_gemm_rk_c(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 
+hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, hipStream_t st);
+
+hipError_t launch_gemm_tl(int role, const GemmArgs &a, hipStream_t st) {
+    switch (role) {
+        case ROLE_QKV: return launch_gemm_tl_a(role, a, st);
+        case ROLE_FC1: return launch_gemm_tl_b(role, a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool gemm_tl_built(int role, int S, int ck) {
+    return (role == ROLE_QKV || role == ROLE_FC1) && S == 8 && ck == 5;
+}
+
 hipError_t launch_gemm_rk(int role, const GemmArgs &a, int mb, int nb, hipStream_t st) {
     switch (role) {
         case ROLE_QKV: case ROLE_OPROJ: case ROLE_CROSS_Q:

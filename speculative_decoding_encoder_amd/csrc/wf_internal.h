@@ -184,6 +184,11 @@ hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
 // gemm_rk_built accepts, one wave per chunk of the workgroup's K group
 hipError_t launch_gemm_rk(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 bool gemm_rk_built(int role, int ck);
+// tall-block kernel for verify passes of many requests: 96 x 64 tiles, four
+// waves sharing the activations through LDS, the whole of K per workgroup
+// (QKV and fc1; K = 1280)
+hipError_t launch_gemm_tl(int role, const GemmArgs &a, hipStream_t st);
+bool gemm_tl_built(int role, int S, int ck);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
 hipError_t launch_layernorm(const LnArgs &a, hipStream_t st);

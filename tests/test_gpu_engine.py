@@ -352,6 +352,42 @@ def test_turbo_b32_ragged_shuffled_pages(torch_cuda):
     eng.close()
 
 
+def test_tall_gemm_matches_register_tiled_bitwise(torch_cuda):
+    """A verify block of 32 requests x 9 rows (288 rows: QKV, fc1 and the LM
+    head take the tall-block kernel) gives every logit the same bits as with
+    that kernel switched off (the register-tiled kernel); both reduce K in
+    the same chunk order."""
+    import os
+    wl = WORKLOADS[2]
+    shape = TURBO
+    B = wl.batch
+    wbits = make_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    prefixes = make_prefixes(wl)
+    blocks = np.random.default_rng(11).integers(0, shape.vocab, (B, 9)).astype(np.int32)
+    out = []
+    for tall in ("1", "0"):
+        os.environ["WF_TALL_GEMM"] = tall
+        try:
+            eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224)
+        finally:
+            del os.environ["WF_TALL_GEMM"]
+        slots = list(range(B))
+        eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+        T = max(len(p) for p in prefixes)
+        toks = np.zeros((B, T), np.int32)
+        for b, p in enumerate(prefixes):
+            toks[b, :len(p)] = p
+        lens = np.array([len(p) for p in prefixes], np.int32)
+        _verify(eng, slots, toks, lens, logits=False)
+        eng.wf_rollback(eng.i32(slots), eng.i32(lens - 1))
+        am, lg = _verify(eng, slots, blocks, [9] * B)
+        out.append((am, lg))
+        eng.close()
+    assert np.array_equal(out[0][0], out[1][0])
+    assert np.array_equal(out[0][1].view(np.uint32), out[1][1].view(np.uint32))
+
+
 def test_turbo_b32_speculative_equals_greedy_on_gpu(torch_cuda):
     from speculative_decoding_encoder_amd.harness import run_loop, table_drafter
     wl = WORKLOADS[2]
