@@ -143,7 +143,8 @@ typedef struct {
  *           (the V half of a page is stored transposed, [head_dim][page_size]);
  *           the drafter's layers hold its history keys (rotated) and values.
  * xkv_pool: fp16 per slot, per layer (target layers, then drafter layers):
- *           K [n_heads][F_pad][head_dim] then V [n_heads][head_dim][F_pad],
+ *           K [n_heads][F_pad][head_dim] then V [n_heads][F_pad/32][head_dim][32]
+ *           (each 32-frame step of V transposed and contiguous),
  *           F_pad = n_frames rounded up to 32.
  *           Must be zero-filled before the first wf_encode_kv.
  * workspace: engine-private scratch and slot state.

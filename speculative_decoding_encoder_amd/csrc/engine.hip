@@ -47,14 +47,20 @@ constexpr int kSplitRowsCap = 128;   // GEMM K-split scratch sized for this many
 
 // Cross-attention chunking: 4, 8 or 16 chunks per (request, head) -- enough
 // waves to cover the GPU when the batch is small -- of spw 32-frame steps
-// each (a multiple of 3). Depends on the number of requests only, never on
+// each (a multiple of the load ring depth). Depends on the number of requests only, never on
 // the block length, so a row's bits do not depend on its block.
+// WF_XA_CHUNKS (4, 8 or 16) fixes the chunk count: a tuning aid. The merge
+// scratch is sized for 16 chunks (4 groups) at every batch size.
 void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
     const int steps = cdiv(F, 32);
     const int want = cdiv(2048, n * H);
     int C = want >= 16 ? 16 : (want >= 8 ? 8 : 4);
+    if (const char *ov = std::getenv("WF_XA_CHUNKS")) {
+        const int o = std::atoi(ov);
+        if (o == 4 || o == 8 || o == 16) C = o;
+    }
     while (C > 4 && C > steps) C >>= 1;
-    spw = cdiv(cdiv(steps, C), 3) * 3;
+    spw = cdiv(cdiv(steps, C), kXaRing) * kXaRing;
     cf = spw * 32;
     G = C / 4;
 }
@@ -104,13 +110,10 @@ Layout layout_of(const wf_config *c) {
     // K-split subtree sums: up to 8 groups of kSplitRowsCap rows of the widest projection
     size_t part = (size_t)8 * kSplitRowsCap * std::max(3 * d, f) * 4;
     L.part_bytes = part;
-    size_t xap = 0;
-    for (int n = 1; n <= c->max_batch; ++n) {
-        int cf, G, spw;
-        cross_chunks(n, H, c->n_frames, cf, G, spw);
-        if (G > 1) xap = std::max(xap, (size_t)n * H * G * 16 * (hd + 2) * 4);
-    }
-    xap = std::max(xap, (size_t)8 << 20);
+    // cross-attention merge partials: 4 chunk groups (the most any chunk
+    // count gives) per (request, head) for verify blocks of one row tile;
+    // taller blocks take fewer groups when they would not fit
+    const size_t xap = std::max((size_t)c->max_batch * H * 4 * 16 * (hd + 2) * 4, (size_t)8 << 20);
     L.xapart_bytes = xap;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
@@ -542,7 +545,7 @@ void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &G, int &spw) {
     while (G > 1 && (size_t)n * H * mt * G * rowbytes > e->lay.xapart_bytes) {
         // long prefill blocks: fewer, longer chunks so the group partials fit
         G >>= 1;
-        spw = cdiv(cdiv(cdiv(c.n_frames, 32), 4 * G), 3) * 3;
+        spw = cdiv(cdiv(cdiv(c.n_frames, 32), 4 * G), kXaRing) * kXaRing;
         cf = spw * 32;
     }
 }

@@ -70,8 +70,10 @@ __device__ __forceinline__ void epi_elem(const GemmArgs &a, int m, int n, float 
         if (seg == 0) {
             base[((size_t)h * e.F_pad + f) * e.hd + dim] = f2h_bits(v);
         } else {
-            base[(size_t)e.H * e.F_pad * e.hd + ((size_t)h * e.hd + dim) * e.F_pad + f] =
-                f2h_bits(v + bias_at(e.b1, c));
+            // V: per head, 32-frame steps of [hd][32 frames] (one contiguous
+            // block per step, in the order the attention kernel reads it)
+            base[(size_t)e.H * e.F_pad * e.hd + (size_t)h * e.F_pad * e.hd +
+                 ((size_t)(f >> 5) * e.hd + dim) * 32 + (f & 31)] = f2h_bits(v + bias_at(e.b1, c));
         }
     }
 }

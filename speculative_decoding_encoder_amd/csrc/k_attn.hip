@@ -16,8 +16,10 @@
 // L+i) sees keys 0..L+i ("one causal target pass over the anchor and the
 // candidates", Whisper-Flash section 3.1).
 //
-// Cross-attention reads the write-once pool (K [head][F_pad][hd], V^T
-// [head][hd][F_pad]).
+// Cross-attention reads the write-once pool: K [head][F_pad][hd] and V
+// [head][F_pad / 32][hd][32], the transposed V of each 32-frame step one
+// contiguous block, so that both operands of a step stream from
+// consecutive addresses.
 //
 // A workgroup is four waves. In self-attention they split the 32-key steps
 // of one (request, head, 16-row tile) by absolute step index (wave w takes
@@ -303,9 +305,11 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
 // ---------------------------------------------------------------------------
 // Cross-attention over the write-once pool. Workgroup = (request, head,
 // 16-row tile, chunk group); wave w takes chunk 4 * group + w of cf frames
-// (spw 32-frame steps, a multiple of 3: a 3-deep load ring).
+// (spw 32-frame steps, a multiple of the load ring depth kXaRing). Three
+// workgroups fit a CU, so a batch of 32 requests (640 workgroups) runs in one
+// round.
 template <int HD>
-__global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
+__global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     constexpr int NDT = HD / 16;
     constexpr int PW = HD + 2;
     __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
@@ -326,7 +330,7 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
 
     const uint16_t *base = a.xkv + (size_t)a.slots[b] * a.slot_stride + a.layer_off;
     const uint16_t *kh = base + (size_t)h * a.F_pad * HD;
-    const uint16_t *vh = base + (size_t)a.H * a.F_pad * HD + (size_t)h * HD * a.F_pad;
+    const uint16_t *vh = base + (size_t)a.H * a.F_pad * HD + (size_t)h * a.F_pad * HD;
     const int qrow = row0 + r16;
     const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
 
@@ -347,20 +351,20 @@ __global__ __launch_bounds__(256) void cross_attn_kernel(CrossAttnArgs a) {
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            f.v[dt] = ld16(vh + (size_t)(dt * 16 + r16) * a.F_pad + fb + 8 * g);
+            f.v[dt] = ld16(vh + ((size_t)(fb >> 5) * HD + dt * 16 + r16) * 32 + 8 * g);
     };
     auto live = [&](int, int frame) { return frame < c1; };
 
     SmState<NDT> st;
     st.init();
-    KVStep<HD> f[3];
+    KVStep<HD> f[kXaRing];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) load(i, f[i]);
-    for (int s0 = 0; s0 < a.spw; s0 += 3) {
+    for (int i = 0; i < kXaRing; ++i) load(i, f[i]);
+    for (int s0 = 0; s0 < a.spw; s0 += kXaRing) {
 #pragma unroll
-        for (int i = 0; i < 3; ++i) {
+        for (int i = 0; i < kXaRing; ++i) {
             attend_step<HD>(q, f[i], c0 + 32 * (s0 + i), c1, a.scale, st, Pt[wave], g, r16, live);
-            if (s0 + 3 < a.spw) load(s0 + i + 3, f[i]);
+            if (s0 + kXaRing < a.spw) load(s0 + i + kXaRing, f[i]);
         }
     }
     merge_waves<HD>(st, mbuf, wave, g, r16);

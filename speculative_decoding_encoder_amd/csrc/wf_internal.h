@@ -91,6 +91,10 @@ struct SelfAttnArgs {
     uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
 };
 
+// Cross-attention load ring depth (32-frame steps in flight per wave); a
+// chunk's step count is a multiple of it.
+constexpr int kXaRing = 2;
+
 struct CrossAttnArgs {
     const uint16_t *q;             // fp16 [M][d]
     const uint16_t *xkv;           // pool base
@@ -98,7 +102,8 @@ struct CrossAttnArgs {
     const int32_t *slots, *req_ntok;
     int32_t n, T, H, d, F, F_pad;
     int32_t mt, G, cf, spw;        // m-tiles per request, chunk groups (of 4 chunks),
-                                   // frames per chunk, 32-frame steps per chunk (3k)
+                                   // frames per chunk, 32-frame steps per chunk
+                                   // (a multiple of kXaRing)
     int32_t n_items;               // n * H * mt * G workgroups
     float scale;
     float *part;                   // [item][16][hd+2] when G > 1
