@@ -118,9 +118,10 @@ Layout layout_of(const wf_config *c) {
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
     L.x = take(M * d * 4);
-    const size_t Mp = (M + 15) / 16 * 16;   // split-bf16 buffers hold whole 16-row tiles
-    L.xs = take(Mp * 2 * d * 2);
-    L.hs = take(Mp * 2 * f * 2);
+    const size_t Mp = (M + 15) / 16 * 16;   // fp16 activation buffers hold whole 16-row tiles
+    L.xs = take(Mp * d * 2);
+    // the MLP hidden layer (fp16), or the drafter's fp32 projections [M][3d]
+    L.hs = take(Mp * std::max(f * 2, 3 * d * 4));
     L.q = take(M * d * 2);
     L.part = take(part);
     L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 16) * (cdiv((int)M, 16) + 1) * 4);
@@ -133,7 +134,7 @@ Layout layout_of(const wf_config *c) {
     L.len = take((size_t)c->max_batch * 4);
     L.pend = take((size_t)c->max_batch * 4);
     L.err = take((size_t)c->max_batch * 4);
-    L.taps = take(c->drafter_layers > 0 ? Mp * (size_t)c->n_taps * d * 4 : 0);
+    L.taps = take(c->drafter_layers > 0 ? Mp * (size_t)c->n_taps * d * 2 : 0);
     L.dam = take(M * 4);
     L.total = o;
     return L;
@@ -156,7 +157,7 @@ struct wf_engine {
     std::vector<LayerW> layers;
     std::vector<LayerW> dlayers;            // drafter blocks
     const uint16_t *w_hist, *mask_emb, *lnd_g, *lnd_b;
-    uint16_t *taps;                         // split-bf16 [max_rows][n_taps*d]
+    uint16_t *taps;                         // fp16 [max_rows][n_taps*d], fragment-tiled
     int32_t *dam;                           // drafter argmax [max_rows]
     uint16_t *kv, *xkv;
     size_t kv_layer_elems, xkv_slot_elems, xkv_layer_elems;
@@ -223,9 +224,9 @@ wf_status run_ln(wf_engine *e, int M, const uint16_t *g, const uint16_t *b, hipS
 
 // Rows up to which the verify-pass GEMMs use the register-tiled kernel.
 constexpr int kRegTiledMaxRows = 1024;
-// Row range in which QKV and fc1 use the tall-block kernel (on MI355X at 288
-// rows: QKV 34 us against 40, fc1 28 against 38; on par at 864 rows).
-constexpr int kTallMinRows = 97, kTallMaxRows = 576;
+// Row range in which QKV and fc1 use the tall-block kernel (on MI355X, QKV
+// at 288 rows: 31 us against 40; at 864 rows 49 against 54 in isolation).
+constexpr int kTallMinRows = 97, kTallMaxRows = 1024;
 
 // X W^T with role's epilogue. With lng/lnb the input is LN(x) of the
 // residual stream: fused into the GEMM's prologue for one row tile, else the
@@ -266,12 +267,14 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     }
     if (e->tall_gemm && M >= kTallMinRows && M <= kTallMaxRows && gemm_tl_built(role, S, ck) &&
         !fuse_ln) {
-        // tall blocks (tens of requests): 96 x 64 tiles over the whole of K
+        // tall blocks (tens of requests): 96- or 128-row x 64-column tiles
+        // over the whole of K
+        const int mbt = M <= 576 ? 6 : 8;
         a.n_tiles = cdiv(N, 64);
-        a.m_blocks = cdiv(M, 96);
+        a.m_blocks = cdiv(M, 16 * mbt);
         a.n_groups = 1;
         a.n_wg = a.n_tiles * a.m_blocks;
-        return timed(e, kind, st, [&] { return launch_gemm_tl(role, a, st); });
+        return timed(e, kind, st, [&] { return launch_gemm_tl(role, a, mbt, st); });
     }
     if (rk) {
         // Register-tiled kernel (tiles from a sweep on MI355X). One row tile:
@@ -289,7 +292,9 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                 (size_t)2 * M * N * 4 <= e->lay.part_bytes)
                 P = 2;
         } else {
-            mb = role == ROLE_LM_HEAD && mt_need > 2 ? 4 : 2;
+            // the LM head reads the activations once per 64-column tile:
+            // 96-row blocks from 6 row tiles on (1.2x faster at 288 rows)
+            mb = role != ROLE_LM_HEAD || mt_need <= 2 ? 2 : (mt_need >= 6 ? 6 : 4);
             nb = 4;
             if (split_k_ok) {
                 while (P < S && cdiv(N, 16 * nb) * cdiv(M, 16 * mb) * P < 128 &&

@@ -25,12 +25,7 @@ __device__ __forceinline__ void epi_elem(const GemmArgs &a, int m, int n, float 
     } else if constexpr (EPI == EPI_F16) {
         e.out[(size_t)m * a.N + n] = f2h_bits(v + bias_at(e.b0, n));
     } else if constexpr (EPI == EPI_GELU) {
-        float t = gelu_erf(v + bias_at(e.b0, n));
-        uint16_t hi, lo;
-        split_bf16(t, hi, lo);
-        const size_t base = xt_index(m, n, a.N);
-        e.out[base] = hi;
-        e.out[base + XT_LO] = lo;
+        e.out[xh_index(m, n, a.N)] = f2h_bits(gelu_erf(v + bias_at(e.b0, n)));
     } else if constexpr (EPI == EPI_QKV) {
         const int d = a.seg_n;
         const int seg = n / d;

@@ -1,15 +1,17 @@
 // Register-tiled GEMM for short row blocks (the verify pass, M = B(K+1)):
-// C[m][n] = sum_k X[m][k] W[n][k], bf16 MFMA 16x16x32, fp32 accumulate.
+// C[m][n] = sum_k X[m][k] W[n][k]; fp16 activations against the bf16 weights
+// converted to fp16 in registers (fp16 MFMA 16x16x32), fp32 accumulate. The
+// cross K/V projection takes the bf16 audio memory as is (bf16 MFMA).
 //
 //  * A workgroup owns a BM x BN output tile (BM = 16 MB, BN = 16 NB) and the
 //    S/P consecutive K chunks of its K group; it has one wave per chunk.
 //  * A wave keeps all MB x NB MFMA tiles of its chunk in registers, so one
-//    activation fragment feeds NB MFMAs and one weight fragment feeds MB (2 MB
-//    with split-bf16 activations). Both operands go from global memory
+//    activation fragment feeds NB MFMAs and one weight fragment (converted
+//    once) feeds MB. Both operands go from global memory
 //    straight into a D-deep register ring; the chunk's CK k-steps are fully
 //    unrolled, so every ring slot is a fixed register set. Each weight
 //    fragment is loaded by exactly one wave per row block.
-//  * The chunk's k-steps run in order, hi before lo per step, from zero; the
+//  * The chunk's k-steps run in order from zero; the
 //    waves' chunk sums meet in LDS in the pairwise tree
 //    ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)), and K groups (P > 1) in the same
 //    tree through scratch. That is also the order of the LDS-staged kernel,
@@ -28,16 +30,16 @@ template <int ROLE, int MB, int NB, int CK, bool LNX>
 __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     static_assert(!LNX || MB == 1, "the layer-norm prologue covers one row tile");
     constexpr int EPI = epi_of(ROLE);
-    constexpr bool XS = ROLE != ROLE_XKV;          // split-bf16 activations
+    constexpr bool XH = ROLE != ROLE_XKV;          // fp16 fragment-tiled activations
     constexpr int NT = MB * NB;
-    constexpr int NX = XS ? 2 * MB : MB;           // activation fragments per k-step
+    constexpr int NX = MB;                         // activation fragments per k-step
     // ring of ~144 VGPRs (~96 for the largest tile over long chunks: no spills)
     constexpr int D0 = (NT >= 16 && CK > 5 ? 24 : 36) / (NX + NB);
     constexpr int D1 = D0 < 1 ? 1 : D0;
     constexpr int D2 = D1 > CK ? CK : D1;
     constexpr int D = LNX && D2 > 3 ? 3 : D2;       // LNX also holds a row of x
-    constexpr int XSTEP = XS ? 1024 : 32;          // uint16 per k-step (fragment-tiled X: one
-                                                   // hi + lo block pair per 16-row tile)
+    constexpr int XSTEP = XH ? 512 : 32;           // uint16 per k-step (fragment-tiled X: one
+                                                   // 1 KB block per 16-row tile)
     constexpr int BM = 16 * MB, BN = 16 * NB;
     __shared__ f32x4 red[2][NT][64];
 
@@ -66,11 +68,11 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     } else {
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt) {
-            if constexpr (XS) {
+            if constexpr (XH) {
                 // rows of the last tile past M are read, never stored; tiles
                 // past the last one repeat it
                 const int tile = min((m_base >> 4) + mt, (a.M - 1) >> 4);
-                xp[mt] = a.X + ((size_t)tile * (a.K >> 5) + ts) * 1024 + (g * 16 + r16) * 8;
+                xp[mt] = a.X + ((size_t)tile * (a.K >> 5) + ts) * 512 + (g * 16 + r16) * 8;
             } else {
                 const int m = min(m_base + mt * 16 + r16, a.M - 1);
                 xp[mt] = a.X + (size_t)m * a.K + g * 8 + (size_t)ts * 32;
@@ -100,10 +102,7 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
             fr.lb = ld16(a.lnb + k0);
         } else {
 #pragma unroll
-            for (int mt = 0; mt < MB; ++mt) {
-                fr.x[mt] = ld16(xp[mt] + s * XSTEP);
-                if constexpr (XS) fr.x[MB + mt] = ld16(xp[mt] + s * XSTEP + XT_LO);
-            }
+            for (int mt = 0; mt < MB; ++mt) fr.x[mt] = ld16(xp[mt] + s * XSTEP);
         }
 #pragma unroll
         for (int nt = 0; nt < NB; ++nt) fr.w[nt] = ld16(wp[nt] + s * 32);
@@ -148,19 +147,22 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
 #pragma unroll
     for (int s = 0; s < CK; ++s) {
         Fr &cur = f[s % D];
-        if constexpr (LNX) ln_split8(cur.lx0, cur.lx1, cur.lg, cur.lb, ln_mean, ln_rstd, cur.x[0],
-                                     cur.x[1]);
+        if constexpr (LNX) cur.x[0] = ln_h8(cur.lx0, cur.lx1, cur.lg, cur.lb, ln_mean, ln_rstd);
+        if constexpr (XH) {
+            u32x4 wh[NB];
 #pragma unroll
-        for (int mt = 0; mt < MB; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < NB; ++nt)
-                c[mt * NB + nt] = mfma_bf16_k32(cur.x[mt], cur.w[nt], c[mt * NB + nt]);
-        if constexpr (XS) {
+            for (int nt = 0; nt < NB; ++nt) wh[nt] = bf16x8_to_f16x8(cur.w[nt]);
 #pragma unroll
             for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
                 for (int nt = 0; nt < NB; ++nt)
-                    c[mt * NB + nt] = mfma_bf16_k32(cur.x[MB + mt], cur.w[nt], c[mt * NB + nt]);
+                    c[mt * NB + nt] = mfma_f16_k32(cur.x[mt], wh[nt], c[mt * NB + nt]);
+        } else {
+#pragma unroll
+            for (int mt = 0; mt < MB; ++mt)
+#pragma unroll
+                for (int nt = 0; nt < NB; ++nt)
+                    c[mt * NB + nt] = mfma_bf16_k32(cur.x[mt], cur.w[nt], c[mt * NB + nt]);
         }
         __builtin_amdgcn_sched_barrier(0);
         if (s + D < CK) load(cur, s + D);
@@ -327,6 +329,7 @@ hipError_t launch_rk_role(const GemmArgs &a, int mb, int nb, hipStream_t st) {
             case 1: return launch_rk_ck<ROLE, 1, 4, false>(a, st);
             case 2: return launch_rk_ck<ROLE, 2, 4, false>(a, st);
             case 4: return launch_rk_ck<ROLE, 4, 4, false>(a, st);
+            case 6: return launch_rk_ck<ROLE, 6, 4, false>(a, st);
         }
         return hipErrorInvalidValue;
     } else {

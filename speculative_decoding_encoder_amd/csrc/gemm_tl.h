@@ -1,12 +1,12 @@
 // Tall-block GEMM for verify passes of many requests (M = B(K+1) in the
-// hundreds): C[m][n] = sum_k X[m][k] W[n][k], split-bf16 X (fragment-tiled),
-// bf16 W, MFMA 16x16x32, fp32 accumulate.
+// hundreds): C[m][n] = sum_k X[m][k] W[n][k], fp16 X (fragment-tiled), bf16 W
+// converted to fp16 in registers, fp16 MFMA 16x16x32, fp32 accumulate.
 //
 //  * A workgroup is four waves, one per SIMD, and owns a BM x BN tile
 //    (BM = 16 MB rows, BN = 64 NW columns). Every wave covers all BM rows
 //    and its own 16 NW columns, so a wave keeps MB x NW accumulator tiles and
-//    one weight fragment feeds 2 MB MFMAs, one activation fragment NW.
-//  * The activations of a k-step (2 MB fragments of 1 KB, already in MFMA
+//    one weight fragment feeds MB MFMAs, one activation fragment NW.
+//  * The activations of a k-step (MB fragments of 1 KB, already in MFMA
 //    lane order) are fetched once per workgroup into a register ring D
 //    k-steps ahead and copied to a triple-buffered LDS stage two k-steps
 //    ahead; all four waves read them from there, the next k-step's
@@ -15,8 +15,8 @@
 //    same ring; each weight element is loaded by exactly one wave per row
 //    block.
 //  * The workgroup walks the CPG consecutive K chunks of its K group in
-//    order. Per accumulator the k-steps run in order, hi before lo, from
-//    zero per chunk; chunk sums meet in the pairwise tree
+//    order. Per accumulator the k-steps run in order from zero per chunk;
+//    chunk sums meet in the pairwise tree
 //    ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)), K groups (P = S / CPG > 1) in the
 //    same tree through scratch. That is the order of the register-tiled and
 //    LDS-staged kernels, so a row's bits do not depend on the kernel, the
@@ -69,15 +69,14 @@ struct ChunkStack {
 
 template <int ROLE, int MB, int NW, int CPG, int CK, int D = 5>
 __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
-    static_assert(MB % 2 == 0, "the activation stage is whole 16-byte rounds of 256 threads");
     constexpr int EPI = epi_of(ROLE);
     constexpr int NT = MB * NW;                    // accumulator tiles per wave
     // D: ring depth (k-steps ahead); the k-step loop is unrolled by L, a
     // multiple of D and of 2 (the fragment double buffer)
     constexpr int L = D % 2 == 0 ? D : 2 * D;
     static_assert((CPG * CK) % L == 0, "the K group is a whole number of unrolled turns");
-    constexpr int XF = 2 * MB;                     // activation fragments per k-step
-    constexpr int XL = XF * 64 / 256;              // 16-byte activation loads per thread
+    constexpr int XF = MB;                         // activation fragments per k-step
+    constexpr int XL = (XF * 64 + 255) / 256;      // 16-byte activation loads per thread
     constexpr int BM = 16 * MB, BN = 64 * NW;
     constexpr int P = 8 / CPG;                     // K groups (the K chunks are 8)
     __shared__ __attribute__((aligned(16))) uint16_t xs[3][XF * 512];
@@ -98,16 +97,17 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     constexpr int NSTEPS = CPG * CK;
     const int KS = a.K >> 5;
 
-    // activation piece q of a stage: fragment f = q / 64 (row tile f / 2,
-    // hi/lo f % 2), 16 bytes of lane q % 64; k-step t of it sits at
-    // ((tile * KS + t) * 2 + hl) * 512. Tiles past the last repeat it.
+    // activation piece q of a stage: fragment (row tile) f = q / 64, 16 bytes
+    // of lane q % 64; k-step t of it sits at (tile * KS + t) * 512. Tiles
+    // past the last repeat it; pieces past the stage (q >= XF * 64) load a
+    // valid address and are not staged.
     const uint16_t *xsrc[XL];
 #pragma unroll
     for (int v = 0; v < XL; ++v) {
         const int q = tid + v * 256;
-        const int f = q >> 6;
-        const int tile = min((m_base >> 4) + (f >> 1), (a.M - 1) >> 4);
-        xsrc[v] = a.X + ((size_t)tile * KS * 2 + (f & 1)) * 512 + (size_t)ts * 1024 + (q & 63) * 8;
+        const int f = min(q >> 6, XF - 1);
+        const int tile = min((m_base >> 4) + f, (a.M - 1) >> 4);
+        xsrc[v] = a.X + ((size_t)tile * KS + ts) * 512 + (q & 63) * 8;
     }
     const uint16_t *wp[NW];
 #pragma unroll
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     auto load_x = [&](Slot &r, int s) {                 // s: k-step within the group
         const int t = min(s, NSTEPS - 1);               // past the end: a valid repeat
 #pragma unroll
-        for (int v = 0; v < XL; ++v) r.x[v] = ld16(xsrc[v] + (size_t)t * 1024);
+        for (int v = 0; v < XL; ++v) r.x[v] = ld16(xsrc[v] + (size_t)t * 512);
     };
     auto load_w = [&](Slot &r, int s) {
         const int t = min(s, NSTEPS - 1);
@@ -131,7 +131,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     auto stage = [&](const Slot &r, int buf) {
 #pragma unroll
         for (int v = 0; v < XL; ++v)
-            *reinterpret_cast<u32x4 *>(&xs[buf][(tid + v * 256) * 8]) = r.x[v];
+            if (XL * 256 == XF * 64 || tid + v * 256 < XF * 64)
+                *reinterpret_cast<u32x4 *>(&xs[buf][(tid + v * 256) * 8]) = r.x[v];
     };
     auto read_frags = [&](u32x4 (&xf)[XF], int buf) {
 #pragma unroll
@@ -173,13 +174,14 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         read_frags(xn, (s + 1) % 3);
         __builtin_amdgcn_sched_barrier(0);
+        u32x4 wh[NW];
+#pragma unroll
+        for (int nt = 0; nt < NW; ++nt) wh[nt] = bf16x8_to_f16x8(cur.w[nt]);
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt)
 #pragma unroll
-            for (int nt = 0; nt < NW; ++nt) {
-                c[mt * NW + nt] = mfma_bf16_k32(xc[2 * mt], cur.w[nt], c[mt * NW + nt]);
-                c[mt * NW + nt] = mfma_bf16_k32(xc[2 * mt + 1], cur.w[nt], c[mt * NW + nt]);
-            }
+            for (int nt = 0; nt < NW; ++nt)
+                c[mt * NW + nt] = mfma_f16_k32(xc[mt], wh[nt], c[mt * NW + nt]);
         __builtin_amdgcn_sched_barrier(0);
         load_w(cur, s + D);
         if ((s + 1) % CK == 0) tree.push(s / CK, c);
@@ -298,13 +300,18 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     }
 }
 
-// The verify-pass instance: 96 x 64 tiles, the whole of K per workgroup
-// (no scratch), 5 k-steps per chunk (K = 1280).
+// The verify-pass instances: 96 x 64 tiles up to 576 rows, 128 x 64 above;
+// the whole of K per workgroup (no scratch), 5 k-steps per chunk (K = 1280).
 template <int ROLE>
-hipError_t launch_tl(const GemmArgs &a, hipStream_t st) {
+hipError_t launch_tl(const GemmArgs &a, int mb, hipStream_t st) {
     if (a.S != 8 || a.ck != 5 || a.n_groups != 1) return hipErrorInvalidValue;
     const int grid = ((a.n_wg + 7) / 8) * 8;
-    hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
+    if (mb == 6)
+        hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
+    else if (mb == 8)
+        hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 8, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -90,13 +90,9 @@ __device__ __forceinline__ void softmax_step(f32x4 &s0, f32x4 &s1, float (&mrun)
     }
 }
 
-// element (row, c) of a fragment-tiled split-bf16 buffer of width K
-__device__ __forceinline__ void store_split(uint16_t *out, int row, int c, int K, float v) {
-    uint16_t hi, lo;
-    split_bf16(v, hi, lo);
-    const size_t base = xt_index(row, c, K);
-    out[base] = hi;
-    out[base + XT_LO] = lo;
+// element (row, c) of a fragment-tiled fp16 activation buffer of width K
+__device__ __forceinline__ void store_act(uint16_t *out, int row, int c, int K, float v) {
+    out[xh_index(row, c, K)] = f2h_bits(v);
 }
 
 // Intra-wave ordering of LDS traffic (the P tile is private to a wave).
@@ -238,7 +234,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
         for (int idx = tid; idx < 16 * HD; idx += 256) {
             const int rr = idx / HD, c = idx - rr * HD;
             const int row = row0 + rr;
-            if (row < a.T) store_split(a.out, b * a.T + row, h * HD + c, a.d, 0.f);
+            if (row < a.T) store_act(a.out, b * a.T + row, h * HD + c, a.d, 0.f);
         }
         return;
     }
@@ -296,7 +292,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
             for (int r = 0; r < 4; ++r) {
                 const int row = row0 + 4 * g + r;
                 if (row < a.T)
-                    store_split(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
+                    store_act(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
                                 st.o[dt][r] / st.l[r]);
             }
     }
@@ -377,7 +373,7 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int row = row0 + 4 * g + r;
                     if (row < a.T)
-                        store_split(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
+                        store_act(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
                                     st.o[dt][r] / st.l[r]);
                 }
         }
@@ -433,7 +429,7 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
         for (int q2 = 0; q2 < a.G; ++q2)
             v[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + rr * PW + 2 + dim) * wts[rr][q2];
         const float acc = (a.G == 2) ? v[0] + v[1] : (v[0] + v[1]) + (v[2] + v[3]);
-        store_split(a.out, b * a.T + row, h * HD + dim, a.d, acc / wts[rr][4]);
+        store_act(a.out, b * a.T + row, h * HD + dim, a.d, acc / wts[rr][4]);
     }
 }
 

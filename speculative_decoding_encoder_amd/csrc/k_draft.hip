@@ -1,7 +1,7 @@
 // Kernels of the parallel drafter (Whisper-Flash section 3.2, eq. 2, and
 // appendix A.2) around the shared GEMM / attention kernels:
 //  * tap_kernel: the target's residual stream after a tapped block, written
-//    as one column block of the split-bf16 history operand [M][n_taps*d];
+//    as one column block of the fp16 history operand [M][n_taps*d];
 //  * rope_append_kernel: rotary embedding (base 10000, fp32 phases, explicit
 //    text positions; dimension i pairs with i + hd/2) of queries and keys,
 //    and the append of keys and values into the drafter's KV pages;
@@ -21,17 +21,9 @@ __global__ __launch_bounds__(256) void tap_kernel(TapArgs a) {
     const float *x = a.x + (size_t)m * a.d;
     const size_t width = (size_t)a.n_taps * a.d;
     for (int kg = lane; kg < a.d / 8; kg += 64) {
-        u32x4 vh, vl;
-        for (int j = 0; j < 4; ++j) {
-            uint16_t h0, l0, h1, l1;
-            split_bf16(x[kg * 8 + 2 * j], h0, l0);
-            split_bf16(x[kg * 8 + 2 * j + 1], h1, l1);
-            vh[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            vl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
-        }
-        uint16_t *o = a.out + xt_index(m, a.j * a.d + kg * 8, (int)width);
-        *reinterpret_cast<u32x4 *>(o) = vh;
-        *reinterpret_cast<u32x4 *>(o + XT_LO) = vl;
+        u32x4 v;
+        for (int j = 0; j < 4; ++j) v[j] = pack_h2(x[kg * 8 + 2 * j], x[kg * 8 + 2 * j + 1]);
+        *reinterpret_cast<u32x4 *>(a.out + xh_index(m, a.j * a.d + kg * 8, (int)width)) = v;
     }
 }
 

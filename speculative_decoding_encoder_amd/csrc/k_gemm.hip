@@ -1,5 +1,5 @@
-// Skinny bf16 GEMM for the decoder projections, the tied LM head and the
-// write-once cross K/V:  C[m][n] = sum_k X[m][k] * W[n][k].
+// LDS-staged GEMM for tall blocks (long prefill blocks) and the write-once
+// cross K/V: C[m][n] = sum_k X[m][k] * W[n][k].
 //
 // Design for gfx950 (wave64, 16x16x32 bf16 MFMA, fp32 accumulate):
 //  * A workgroup is 4 waves and owns 64 output columns (16 per wave) of a
@@ -8,9 +8,10 @@
 //    over the weights per row block); the activation slice of each 32-deep
 //    k-step is staged once per workgroup in LDS (double-buffered) and read
 //    by all four waves.
-//  * The activation operand is split-bf16, X = hi + lo: two MFMAs per k-step
-//    with the same weight fragment, so activations carry ~16 mantissa bits
-//    while the weights stay bf16.
+//  * The activation operand is fp16 (fragment-tiled); the bf16 weights are
+//    converted to fp16 in registers for the fp16 MFMA. The cross K/V
+//    projection multiplies the bf16 audio memory with the bf16 weights as
+//    they are (bf16 MFMA).
 //  * K is cut into S = 8 chunks (2 when K = 64). A chunk's partial sum
 //    starts from zero, and the partials are combined by a fixed pairwise tree
 //    ((c0+c1)+(c2+c3))+((c4+c5)+(c6+c7)). A workgroup owns S/P consecutive
@@ -71,11 +72,11 @@ struct Tree {
 template <int ROLE, int MB, int KS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
     constexpr int EPI = epi_of(ROLE);
-    constexpr bool XS = ROLE != ROLE_XKV;   // split-bf16 activations (the audio memory is bf16)
+    constexpr bool XH = ROLE != ROLE_XKV;   // fp16 activations (the audio memory is bf16)
     constexpr int BM = MB * 16;
-    constexpr int XROW = XS ? 72 : 40;            // uint16 per row per k-step (padded: no
+    constexpr int XROW = 40;                      // uint16 per row per k-step (padded: no
                                                   // bank conflicts across 16 rows)
-    constexpr int XPARTS = XS ? 8 : 4;            // 16-byte parts per row per k-step
+    constexpr int XPARTS = 4;                     // 16-byte parts per row per k-step
     constexpr int NPARTS = BM * KS * XPARTS;      // 16-byte parts per stage
     constexpr int XV = (NPARTS + 255) / 256;      // parts per thread
     // stage layout in LDS: [k-step][row][XROW]
@@ -125,9 +126,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 const int rr = r2 / XPARTS, part = r2 - (r2 / XPARTS) * XPARTS;
                 const int k0 = (tb + kk) * 32;
                 if (rr < rows) {
-                    if constexpr (XS)   // part = 2 g + (0: hi, 1: lo), fragment-tiled X
-                        xr[v] = ld16(a.X + xt_index(m_base + rr, k0 + 8 * (part >> 1), a.K) +
-                                     (part & 1) * XT_LO);
+                    if constexpr (XH)   // fragment-tiled X
+                        xr[v] = ld16(a.X + xh_index(m_base + rr, k0 + 8 * part, a.K));
                     else
                         xr[v] = ld16(a.X + (size_t)(m_base + rr) * a.K + k0 + part * 8);
                 }
@@ -174,20 +174,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         const uint16_t *xb = xs[buf];
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            const u32x4 wcur = wa.f[kk];
+            const u32x4 wcur = XH ? bf16x8_to_f16x8(wa.f[kk]) : wa.f[kk];
 #pragma unroll
             for (int mt = 0; mt < MB; ++mt) {
                 if (mt < mt_live) {
                     const uint16_t *xrow = xb + (kk * BM + mt * 16 + r16) * XROW;
-                    if constexpr (XS) {
-                        const u32x4 xh = *reinterpret_cast<const u32x4 *>(xrow + g * 16);
-                        const u32x4 xl = *reinterpret_cast<const u32x4 *>(xrow + g * 16 + 8);
-                        c[mt] = mfma_bf16_k32(xh, wcur, c[mt]);
-                        c[mt] = mfma_bf16_k32(xl, wcur, c[mt]);
-                    } else {
-                        const u32x4 xh = *reinterpret_cast<const u32x4 *>(xrow + g * 8);
-                        c[mt] = mfma_bf16_k32(xh, wcur, c[mt]);
-                    }
+                    const u32x4 xf = *reinterpret_cast<const u32x4 *>(xrow + g * 8);
+                    if constexpr (XH) c[mt] = mfma_f16_k32(xf, wcur, c[mt]);
+                    else c[mt] = mfma_bf16_k32(xf, wcur, c[mt]);
                 }
             }
         }
@@ -314,13 +308,13 @@ hipError_t launch_gemm_rk_a(int role, const GemmArgs &a, int mb, int nb, hipStre
 hipError_t launch_gemm_rk_b(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 hipError_t launch_gemm_rk_c(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 
-hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, hipStream_t st);
-hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, hipStream_t st);
+hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, int mb, hipStream_t st);
+hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, int mb, hipStream_t st);
 
-hipError_t launch_gemm_tl(int role, const GemmArgs &a, hipStream_t st) {
+hipError_t launch_gemm_tl(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
-        case ROLE_QKV: return launch_gemm_tl_a(role, a, st);
-        case ROLE_FC1: return launch_gemm_tl_b(role, a, st);
+        case ROLE_QKV: return launch_gemm_tl_a(role, a, mb, st);
+        case ROLE_FC1: return launch_gemm_tl_b(role, a, mb, st);
     }
     return hipErrorInvalidValue;
 }

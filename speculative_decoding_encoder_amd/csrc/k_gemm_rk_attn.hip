@@ -13,9 +13,9 @@ hipError_t launch_gemm_rk_a(int role, const GemmArgs &a, int mb, int nb, hipStre
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, hipStream_t st) {
+hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
-        case ROLE_QKV: return launch_tl<ROLE_QKV>(a, st);
+        case ROLE_QKV: return launch_tl<ROLE_QKV>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

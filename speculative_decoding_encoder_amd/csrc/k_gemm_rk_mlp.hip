@@ -12,9 +12,9 @@ hipError_t launch_gemm_rk_b(int role, const GemmArgs &a, int mb, int nb, hipStre
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, hipStream_t st) {
+hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
-        case ROLE_FC1: return launch_tl<ROLE_FC1>(a, st);
+        case ROLE_FC1: return launch_tl<ROLE_FC1>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

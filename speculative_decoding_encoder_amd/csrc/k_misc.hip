@@ -1,5 +1,5 @@
 // Small kernels around the verify pass: per-request validation and slot
-// state, token + position embedding, layer norm into split-bf16, the final
+// state, token + position embedding, layer norm into fp16 activations, the final
 // argmax reduction of the tied LM head, greedy acceptance and rollback.
 #include "wf_device.h"
 #include "wf_internal.h"
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     *reinterpret_cast<float4 *>(x + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-// Layer norm of the fp32 residual stream into fragment-tiled split-bf16
+// Layer norm of the fp32 residual stream into fragment-tiled fp16
 // activations (ln_load16 / ln_reduce16 / ln_apply): 16 lanes per row, 4 rows
 // per workgroup.
 __global__ __launch_bounds__(64) void layernorm_kernel(LnArgs a) {
@@ -87,11 +87,8 @@ __global__ __launch_bounds__(64) void layernorm_kernel(LnArgs a) {
         const int kg = r16 + 16 * i;
         if (kg >= (a.d >> 3)) break;
         const int c = kg * 8;
-        u32x4 vh, vl;
-        ln_split8(row.v[2 * i], row.v[2 * i + 1], ld16(a.g + c), ld16(a.b + c), mean, rstd, vh, vl);
-        uint16_t *o = a.out + xt_index(m, c, a.d);
-        *reinterpret_cast<u32x4 *>(o) = vh;
-        *reinterpret_cast<u32x4 *>(o + XT_LO) = vl;
+        *reinterpret_cast<u32x4 *>(a.out + xh_index(m, c, a.d)) =
+            ln_h8(row.v[2 * i], row.v[2 * i + 1], ld16(a.g + c), ld16(a.b + c), mean, rstd);
     }
 }
 

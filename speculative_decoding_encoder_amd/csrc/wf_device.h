@@ -34,15 +34,14 @@ __device__ __forceinline__ f32x4 mfma_f16_k16(u32x2 a, u32x2 b, f32x4 c) {
                                                   __builtin_bit_cast(f16x4, b), c, 0, 0, 0);
 }
 
-// Split-bf16 activations (x = hi + lo, both bf16) are stored fragment-tiled:
-// for each 16-row tile and 32-column step, a 1 KB hi block then a 1 KB lo
-// block, each in the lane order of the MFMA A operand (lane g*16 + r holds
-// row r, columns 8g..8g+7). A fragment load is one contiguous 1 KB read.
-// Buffers hold whole 16-row tiles. xt_index gives the hi element of (m, k);
-// its lo element is XT_LO further.
-#define XT_LO 512
-__host__ __device__ __forceinline__ size_t xt_index(int m, int k, int K) {
-    return (((size_t)(m >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 128 +
+// GEMM activations (the A operand: layer-norm outputs, attention outputs,
+// the MLP hidden layer, the drafter's history taps) are fp16, stored
+// fragment-tiled: for each 16-row tile and 32-column step one 1 KB block in
+// the lane order of the MFMA A operand (lane g*16 + r holds row r, columns
+// 8g..8g+7). A fragment load is one contiguous 1 KB read. Buffers hold whole
+// 16-row tiles. xh_index gives the element (m, k).
+__host__ __device__ __forceinline__ size_t xh_index(int m, int k, int K) {
+    return (((size_t)(m >> 4) * (size_t)(K >> 5) + (size_t)(k >> 5)) * 64 +
             (size_t)(((k >> 3) & 3) * 16 + (m & 15))) * 8 + (size_t)(k & 7);
 }
 
@@ -56,17 +55,28 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
     u += 0x7fffu + ((u >> 16) & 1u);
     return (uint16_t)(u >> 16);
 }
-// Split x into hi + lo, both bf16: hi = bf16(x), lo = bf16(x - hi).
-__device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) {
-    hi = f2bf(x);
-    lo = f2bf(x - bf2f(hi));
-}
 __device__ __forceinline__ uint16_t f2h_bits(float f) {
     _Float16 h = (_Float16)f;
     return __builtin_bit_cast(uint16_t, h);
 }
 __device__ __forceinline__ float h2f_bits(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
+}
+// Two floats to packed fp16 (round to nearest even).
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+    return (uint32_t)f2h_bits(lo) | ((uint32_t)f2h_bits(hi) << 16);
+}
+// Eight bf16 weights to fp16 for the fp16 MFMA. Exact for |w| >= 2^-14 (every
+// bf16 value there has an fp16 twin); below, fp16 subnormals keep |w| to
+// 2^-24 (the packed conversion rounds toward zero).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float lo = __uint_as_float(w[j] << 16), hi = __uint_as_float(w[j] & 0xffff0000u);
+        r[j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    }
+    return r;
 }
 
 // Reductions within groups of 16 lanes (lanes 16g .. 16g+15), fixed tree.
@@ -179,20 +189,18 @@ __device__ __forceinline__ float ln_apply(float x, float mean, float rstd, float
     return __fmaf_rn((x - mean) * rstd, g, b);
 }
 // Eight consecutive columns (x at c..c+7, gains and biases as bf16x8) to one
-// split-bf16 fragment pair.
-__device__ __forceinline__ void ln_split8(float4 x0, float4 x1, u32x4 gg, u32x4 bb, float mean,
-                                          float rstd, u32x4 &vh, u32x4 &vl) {
+// fp16 activation fragment.
+__device__ __forceinline__ u32x4 ln_h8(float4 x0, float4 x1, u32x4 gg, u32x4 bb, float mean,
+                                       float rstd) {
     const float xv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    u32x4 v;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-        uint16_t h0, l0, h1, l1;
         const float y0 = ln_apply(xv[2 * j], mean, rstd, bf2f((uint16_t)(gg[j] & 0xffffu)),
                                   bf2f((uint16_t)(bb[j] & 0xffffu)));
         const float y1 = ln_apply(xv[2 * j + 1], mean, rstd, bf2f((uint16_t)(gg[j] >> 16)),
                                   bf2f((uint16_t)(bb[j] >> 16)));
-        split_bf16(y0, h0, l0);
-        split_bf16(y1, h1, l1);
-        vh[j] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        vl[j] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        v[j] = pack_h2(y0, y1);
     }
+    return v;
 }

@@ -12,7 +12,7 @@ enum Epi : int {
     EPI_QKV = 0,    // q -> fp16 buffer; k, v -> the slot's KV pages (valid rows)
     EPI_RESID = 1,  // x[m][n] += C + b[n]            (fp32 residual stream)
     EPI_F16 = 2,    // out[m][n] = fp16(C + b[n])      (cross-attention query)
-    EPI_GELU = 3,   // out = split-bf16(GELU(C + b))   (MLP hidden)
+    EPI_GELU = 3,   // out = fp16(GELU(C + b)), fragment-tiled (MLP hidden)
     EPI_ARGMAX = 4, // tied LM head: per 64-column tile (max, lowest argmax), logits
     EPI_XKV = 5,    // cross K/V of one layer into the write-once pool
     EPI_STORE32 = 6,// out32[m][n] = C + b_seg[n]      (drafter temporaries, history)
@@ -22,7 +22,7 @@ struct EpiArgs {
     const uint16_t *b0, *b1, *b2;  // bias per weight segment (bf16), may be null
     float *x;                      // EPI_RESID
     float *out32;                  // EPI_STORE32 [M][N]
-    uint16_t *out;                 // EPI_F16 / EPI_QKV (q) fp16 [M][N or d]; EPI_GELU split
+    uint16_t *out;                 // EPI_F16 / EPI_QKV (q) fp16 [M][N or d]; EPI_GELU fp16 tiled
     // EPI_QKV: KV append
     uint16_t *kv_layer;            // this layer's first page
     const int32_t *page_table;
@@ -42,7 +42,7 @@ struct EpiArgs {
 };
 
 struct GemmArgs {
-    const uint16_t *X;             // split-bf16, fragment-tiled (xt_index), or plain bf16 [M][K]
+    const uint16_t *X;             // fp16, fragment-tiled (xh_index), or plain bf16 [M][K]
     const uint16_t *W0, *W1, *W2;  // weight segments, each [seg_n][K] bf16
     int32_t M, K, N, seg_n;
     int32_t S, ck;                 // K chunks (fixed per K) and k-steps per chunk
@@ -77,7 +77,7 @@ struct LnArgs {
     int32_t M, d;
     const uint16_t *g, *b;
     float eps;
-    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
+    uint16_t *out;                 // fp16 [M][d], fragment-tiled
 };
 
 struct SelfAttnArgs {
@@ -88,7 +88,7 @@ struct SelfAttnArgs {
     int32_t n, T, H, d;
     int32_t causal;                // 1: row i sees keys <= L+i; 0: the whole block
     float scale;
-    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
+    uint16_t *out;                 // fp16 [M][d], fragment-tiled
 };
 
 // Cross-attention load ring depth (32-frame steps in flight per wave); a
@@ -108,7 +108,7 @@ struct CrossAttnArgs {
     float scale;
     float *part;                   // [item][16][hd+2] when G > 1
     int32_t *cnt;                  // [n*H*mt]
-    uint16_t *out;                 // split-bf16 [M][d], fragment-tiled
+    uint16_t *out;                 // fp16 [M][d], fragment-tiled
 };
 
 struct LmReduceArgs {
@@ -150,7 +150,7 @@ enum Role : int {
 struct TapArgs {
     const float *x;
     int32_t M, d, j, n_taps;
-    uint16_t *out;                 // split-bf16 [M][n_taps*d], fragment-tiled
+    uint16_t *out;                 // fp16 [M][n_taps*d], fragment-tiled
 };
 
 struct RopeArgs {
@@ -185,14 +185,14 @@ hipError_t launch_draft_out(const int32_t *anchor, const int32_t *argmax, const 
                             int n, int K, int32_t *block, hipStream_t st);
 hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
 // register-tiled variant for short blocks: (mb, nb) in {1x1, 1x2, 1x4, 2x2,
-// 2x4, 4x2, 4x4} (the LM head: nb = 4); built for the chunk lengths
+// 2x4, 4x2, 4x4} (the LM head: nb = 4, mb up to 6); built for the chunk lengths
 // gemm_rk_built accepts, one wave per chunk of the workgroup's K group
 hipError_t launch_gemm_rk(int role, const GemmArgs &a, int mb, int nb, hipStream_t st);
 bool gemm_rk_built(int role, int ck);
-// tall-block kernel for verify passes of many requests: 96 x 64 tiles, four
-// waves sharing the activations through LDS, the whole of K per workgroup
-// (QKV and fc1; K = 1280)
-hipError_t launch_gemm_tl(int role, const GemmArgs &a, hipStream_t st);
+// tall-block kernel for verify passes of many requests: 16 mb x 64 tiles
+// (mb 6 or 8), four waves sharing the activations through LDS, the whole of
+// K per workgroup (QKV and fc1; K = 1280)
+hipError_t launch_gemm_tl(int role, const GemmArgs &a, int mb, hipStream_t st);
 bool gemm_tl_built(int role, int S, int ck);
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs &a, hipStream_t st);
