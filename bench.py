@@ -321,32 +321,11 @@ def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 90.0):
                       f"prefix caches and blocks built untimed by the oracle itself"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
-    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--greedy", action="store_true",
-                    help="config 4 with greedy acceptance instead of T = 0.7 sampling")
-    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
-    ap.add_argument("--calib-copy-mib", type=int, default=0,
-                    help="also run device-to-device copies of this size (calibrates "
-                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
-              "single MI355X (requests shard by data parallelism with no exchange; see "
-              "DESIGN.md). --gpus N > 1 is not supported.", file=sys.stderr)
-        sys.exit(2)
+def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
+    """Warm up, time K graph-replayed steps, then a second pass of K steps
+    with HIP events around every launch for the per-kernel durations."""
     import torch
-    torch.cuda.set_device(0)
-    w = Workload(args.config, greedy=args.greedy)
     eng = w.eng
-    K, W = args.steps, args.warmup
-
-    # warm-up, then one step to read the round's outcome
     for _ in range(max(W, 1)):
         w.step()
     torch.cuda.synchronize()
@@ -354,10 +333,11 @@ def main():
     err, lens = eng.wf_device_state()
     assert (err == 0).all() and (n_acc >= 0).all(), "engine reported an error"
     tokens_per_step = int(np.sum(n_acc + 1))
+    log(f"[bench] {w.name}: warm-up done")
 
     stream = torch.cuda.Stream()
     graph = None
-    if not args.no_graph:
+    if use_graph:
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=stream):
             w.step()
@@ -376,8 +356,12 @@ def main():
     ms_step = (t1 - t0) * 1e3 / K
     n_acc2 = w.outs[0].cpu().numpy()
     assert np.array_equal(n_acc, n_acc2), "graph replay changed the round's outcome"
+    used_graph = graph is not None
+    del graph
+    log(f"[bench] {w.name}: timed {K} steps, {ms_step:.3f} ms/step")
 
-    # per-kernel durations from HIP events (eager launches of the same steps)
+    # per-kernel durations from HIP events on the engine's stream (eager
+    # launches of the same steps)
     eng.wf_set_timing(True)
     for _ in range(K):
         w.step()
@@ -391,14 +375,99 @@ def main():
     eng.wf_set_timing(False)
     kb = w.kind_bytes()
     dom = max((k for k in kinds if k in kb), key=lambda k: kinds[k]["total_ms_per_step"])
-    avg_s = kinds[dom]["avg_us"] * 1e-6
-    achieved = kb[dom] / avg_s / 1e9
+    achieved = kb[dom] / (kinds[dom]["avg_us"] * 1e-6) / 1e9
     for k in kinds:
         if k in kb:
             kinds[k]["gbs"] = kb[k] / (kinds[k]["avg_us"] * 1e-6) / 1e9
     bytes_pass = w.pass_bytes()
-
     value = tokens_per_step / (ms_step * 1e-3)
+    return {
+        "value": value, "ms_step": ms_step, "tokens_per_step": tokens_per_step,
+        "accepted": [int(a) for a in n_acc[:8]], "bytes_pass": bytes_pass,
+        "pass_frac": bytes_pass / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "dom": dom, "achieved": achieved, "dom_bytes": kb[dom],
+        "dom_avg_us": kinds[dom]["avg_us"], "kinds": kinds, "graph": used_graph,
+    }
+
+
+def traffic_of(workload: str, symbol_kind: str):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 counter
+    summary (profiles/hbm_traffic.json: FETCH_SIZE and WRITE_SIZE per
+    dispatch, each scaled by the factor a copy of known size gives), or
+    None when there is none for this workload and kernel, or the kernel
+    sources have changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            entries = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = kernel_source_hash()
+    for ent in entries:
+        if ent.get("workload") == workload and ent.get("kind") == symbol_kind \
+                and ent.get("source_hash") == h:
+            return float(ent["hbm_bytes_per_launch"])
+    return None
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources (csrc/*.hip, csrc/*.h), in name order."""
+    import hashlib
+    csrc = os.path.join(ROOT, "speculative_decoding_encoder_amd", "csrc")
+    hsh = hashlib.sha256()
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                hsh.update(name.encode() + b"\0" + f.read())
+    return hsh.hexdigest()[:16]
+
+
+def summary(w: "Workload", r: dict) -> dict:
+    return {
+        "workload": w.name, "batch": w.B, "layers": w.shape.n_layers,
+        "tokens_per_s": round(r["value"], 2),
+        "audio_s_per_s": round(r["value"] / TOKENS_PER_AUDIO_S, 2),
+        "ms_per_step": round(r["ms_step"], 4), "tokens_per_step": r["tokens_per_step"],
+        "pass_bytes": r["bytes_pass"], "pass_roofline_frac": round(r["pass_frac"], 4),
+        "dominant_kernel": r["dom"], "dominant_gbs": round(r["achieved"], 1),
+        "dominant_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+    }
+
+
+EXTRA = {"32": (4, True), "96": (3, False)}   # batch -> (config, greedy)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=[1, 2, 3, 4])
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--greedy", action="store_true",
+                    help="config 4 with greedy acceptance instead of T = 0.7 sampling")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches")
+    ap.add_argument("--batches", default="32,96",
+                    help="also measure these batch sizes (32: large-v3 greedy verify, 96: "
+                         "large-v3 with the parallel drafter); empty for none")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run device-to-device copies of this size (calibrates "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
+              "single MI355X (requests shard by data parallelism with no exchange; see "
+              "DESIGN.md). --gpus N > 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+    K, W = args.steps, args.warmup
+    w = Workload(args.config, greedy=args.greedy)
+    r = measure(w, K, W, use_graph=not args.no_graph)
+    kinds, dom = r["kinds"], r["dom"]
+    value = r["value"]
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -406,11 +475,14 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(r["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "fp16",
+        "precision": "fp16 activations and attention operands, bf16 weights (converted to "
+                     "fp16 in registers), fp32 accumulate, fp32 residual stream, softmax and "
+                     "layer-norm statistics",
         "data": "synthetic (seeded weights N(0,0.02) in bf16, audio memory N(0,1), "
                 "Bernoulli-copy drafts)",
         "config": {"workload": w.name, "layers": w.shape.n_layers,
@@ -418,31 +490,47 @@ def main():
                    "prefix": w.wl.prefix,
                    "p_keep": w.wl.p_keep if not (w.sampling or w.drafter) else None,
                    "drafter_layers": w.wl.drafter_layers,
-                   "temperature": w.temperature, "graph": graph is not None},
+                   "temperature": w.temperature, "graph": r["graph"]},
         "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
-        "tokens_per_step": tokens_per_step,
-        "accepted": [int(a) for a in n_acc[:8]],
-        "pass": {"bytes": bytes_pass, "roofline_frac_of_step": round(
-            bytes_pass / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 4)},
+        "tokens_per_step": r["tokens_per_step"],
+        "accepted": r["accepted"],
+        "pass": {"bytes": r["bytes_pass"], "roofline_frac_of_step": round(r["pass_frac"], 4)},
         "roofline": {"bound": "hbm", "kernel": dom, "symbol": KIND_SYMBOL.get(dom, dom),
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": kb[dom], "avg_us": round(kinds[dom]["avg_us"], 3)},
+                     "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_of(w.name, dom),
+                     "bytes_per_launch": r["dom_bytes"], "avg_us": round(r["dom_avg_us"], 3)},
         "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kinds.items()},
         "encode_kv_s": round(w.encode_kv_s, 4),
+        "batches": {str(w.B): summary(w, r)},
     }
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=eng.dev)
+        src = torch.ones(n, dtype=torch.uint8, device=w.eng.dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
         out["calib_copy_bytes"] = n
+        del src, dst
     if not args.no_cpu:
         t0 = time.time()
         out["cpu_baseline"] = cpu_baseline(w)
         log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
+    # the other batch sizes of the metric, each its own engine
+    for bkey in [b for b in args.batches.split(",") if b.strip()]:
+        if bkey not in EXTRA or bkey == str(w.B):
+            continue
+        w.eng.close()
+        del w
+        torch.cuda.empty_cache()
+        cfg, greedy = EXTRA[bkey]
+        w = Workload(cfg, greedy=greedy)
+        r2 = measure(w, max(5, K // 2), max(2, W // 2), use_graph=not args.no_graph)
+        out["batches"][bkey] = summary(w, r2)
+        out["batches"][bkey]["kernels_avg_us"] = {k: round(v["avg_us"], 2)
+                                                  for k, v in r2["kinds"].items()}
+        log(f"[bench] batch {bkey}: {r2['ms_step']:.3f} ms/step")
     print(json.dumps(out), flush=True)
 
 

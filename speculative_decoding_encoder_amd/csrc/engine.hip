@@ -186,8 +186,10 @@ namespace {
 
 hipEvent_t next_event(wf_engine *e) {
     if (e->ev_used == e->ev_pool.size()) {
+        // no system-scope fence at the timestamps: the events only bracket
+        // kernels on this stream, and the fence would add to every interval
         hipEvent_t ev;
-        if (hipEventCreate(&ev) != hipSuccess) return nullptr;
+        if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return nullptr;
         e->ev_pool.push_back(ev);
     }
     return e->ev_pool[e->ev_used++];
