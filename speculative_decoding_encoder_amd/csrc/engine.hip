@@ -69,7 +69,7 @@ int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
 
 struct Layout {
     size_t x, xs, hs, q, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
-    size_t taps, dam;
+    size_t taps, dam, rowkv;
     size_t total;
     size_t part_bytes, xapart_bytes;
     int n_vtiles;
@@ -136,6 +136,7 @@ Layout layout_of(const wf_config *c) {
     L.err = take((size_t)c->max_batch * 4);
     L.taps = take(c->drafter_layers > 0 ? Mp * (size_t)c->n_taps * d * 2 : 0);
     L.dam = take(M * 4);
+    L.rowkv = take(M * 4);
     L.total = o;
     return L;
 }
@@ -172,6 +173,7 @@ struct wf_engine {
     float *lmmax;
     int32_t *lmidx;
     int32_t *reqL, *reqN, *len, *pend, *err;
+    int32_t *rowkv;                          // per verify row: KV page * 16 + offset, or -1
     int tiles_ovr[16][3] = {};               // WF_GEMM_TILES: per role (mb, nb, P)
     bool ln_fusion = true;                   // WF_LN_FUSION=0 turns the LN prologue off
     bool tall_gemm = true;                   // WF_TALL_GEMM=0 turns the tall-block kernel off
@@ -493,6 +495,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->len = (int32_t *)(ws + L.len);
     e->pend = (int32_t *)(ws + L.pend);
     e->err = (int32_t *)(ws + L.err);
+    e->rowkv = (int32_t *)(ws + L.rowkv);
     e->taps = (uint16_t *)(ws + L.taps);
     e->dam = (int32_t *)(ws + L.dam);
     if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
@@ -691,7 +694,8 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
                    d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
     WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_prepare(pa, st); }));
-    EmbedArgs ema{M, T, d, c.vocab, c.n_ctx, d_tokens, e->reqL, e->tok_emb, e->pos_emb, e->x};
+    EmbedArgs ema{M,      T,      d,        c.vocab,         c.n_ctx, d_tokens, e->reqL,
+                  e->tok_emb, e->pos_emb, e->x, e->reqN, d_slots, e->pt, e->pt_stride, e->rowkv};
     WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_embed(ema, st); }));
 
     for (int l = 0; l < c.n_layers; ++l) {
@@ -712,6 +716,7 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         qa.H = H;
         qa.hd = hd;
         qa.page_elems = e->page_elems;
+        qa.row_kv = e->rowkv;
         WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st,
                         w.ln1_g, w.ln1_b));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,

@@ -235,13 +235,9 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
         if (a.n_groups == 1) {
             for (int j = wave; j < NT; j += W) {
                 const int mt = j / NB, nt = j - (j / NB) * NB;
-                const f32x4 v = red[0][j][lane];
-                const int n = n_base + nt * 16 + r16;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m_base + mt * 16 + 4 * g + r;
-                    if (m < a.M && n < a.N) epi_elem<EPI>(a, m, n, v[r]);
-                }
+                const f32x4 v[1] = {red[0][j][lane]};
+                const int m0[1] = {m_base + mt * 16 + 4 * g};
+                epi_column<EPI, 1>(a, m0, n_base + nt * 16 + r16, v);
             }
             return;
         }

@@ -286,17 +286,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
             e.tile_idx[(size_t)m * e.ld + t64] = nn ? -1 : bi;
         }
     } else {
+        int m0[MB];
 #pragma unroll
-        for (int mt = 0; mt < MB; ++mt)
+        for (int mt = 0; mt < MB; ++mt) m0[mt] = m_base + mt * 16 + 4 * g;
 #pragma unroll
-            for (int nt = 0; nt < NW; ++nt) {
-                const int n = n_wave + nt * 16 + r16;
+        for (int nt = 0; nt < NW; ++nt) {
+            f32x4 v[MB];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m_base + mt * 16 + 4 * g + r;
-                    if (m < a.M && n < a.N) epi_elem<EPI>(a, m, n, total[mt * NW + nt][r]);
-                }
-            }
+            for (int mt = 0; mt < MB; ++mt) v[mt] = total[mt * NW + nt];
+            epi_column<EPI, MB>(a, m0, n_wave + nt * 16 + r16, v);
+        }
     }
 }
 

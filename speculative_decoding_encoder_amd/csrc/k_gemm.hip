@@ -247,13 +247,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
         return;
     } else {
         if (a.n_groups == 1) {
+            int m0[MB];
 #pragma unroll
-            for (int mt = 0; mt < MB; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int m = m_base + mt * 16 + 4 * g + r;
-                    if (m < a.M && n_out < a.N) epi_elem<EPI>(a, m, n_out, total[mt][r]);
-                }
+            for (int mt = 0; mt < MB; ++mt) m0[mt] = m_base + mt * 16 + 4 * g;
+            epi_column<EPI, MB>(a, m0, n_out, total);
             return;
         }
         // publish this group's subtree sum; the last arriver combines

@@ -68,6 +68,16 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     float *x = a.x + (size_t)m * a.d + kg * 8;
     *reinterpret_cast<float4 *>(x) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(x + 4) = make_float4(v[4], v[5], v[6], v[7]);
+    if (kg == 0) {
+        // position L + i of a row that is appended (i < n_tok; the prepare
+        // step has checked its page), else -1
+        int rk = -1;
+        if (i < a.req_ntok[b]) {
+            const int p = a.req_L[b] + i;
+            rk = a.page_table[(size_t)a.slots[b] * a.pt_stride + (p >> 4)] * 16 + (p & 15);
+        }
+        a.row_kv[m] = rk;
+    }
 }
 
 // Layer norm of the fp32 residual stream into fragment-tiled fp16
@@ -80,15 +90,24 @@ __global__ __launch_bounds__(64) void layernorm_kernel(LnArgs a) {
     const float *x = a.x + (size_t)m * a.d;
     LnRow row;
     ln_load16(x, a.d, r16, row);
+    // gains and biases go out with the row (clamped, unconditional), so the
+    // kernel waits for memory once
+    const int last = (a.d >> 3) - 1;
+    u32x4 gg[LN_GPL], bb[LN_GPL];
+#pragma unroll
+    for (int i = 0; i < LN_GPL; ++i) {
+        const int kg = min(r16 + 16 * i, last);
+        gg[i] = ld16(a.g + kg * 8);
+        bb[i] = ld16(a.b + kg * 8);
+    }
     float mean, rstd;
     ln_reduce16(row, a.d, r16, a.eps, mean, rstd);
 #pragma unroll
     for (int i = 0; i < LN_GPL; ++i) {
         const int kg = r16 + 16 * i;
-        if (kg >= (a.d >> 3)) break;
-        const int c = kg * 8;
-        *reinterpret_cast<u32x4 *>(a.out + xh_index(m, c, a.d)) =
-            ln_h8(row.v[2 * i], row.v[2 * i + 1], ld16(a.g + c), ld16(a.b + c), mean, rstd);
+        if (kg > last) break;
+        *reinterpret_cast<u32x4 *>(a.out + xh_index(m, kg * 8, a.d)) =
+            ln_h8(row.v[2 * i], row.v[2 * i + 1], gg[i], bb[i], mean, rstd);
     }
 }
 

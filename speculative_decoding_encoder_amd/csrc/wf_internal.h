@@ -29,6 +29,7 @@ struct EpiArgs {
     int32_t pt_stride;
     const int32_t *slots, *req_L, *req_ntok;
     int32_t T, H, hd, page_elems;
+    const int32_t *row_kv;         // per row: page * 16 + offset of its position, -1: no append
     // EPI_XKV
     uint16_t *xkv;
     int64_t xkv_slot_stride, xkv_layer_off;
@@ -70,6 +71,10 @@ struct EmbedArgs {
     const int32_t *tokens, *req_L;
     const uint16_t *tok_emb, *pos_emb;
     float *x;
+    // the KV destination of every row, shared by all layers of the pass
+    const int32_t *req_ntok, *slots, *page_table;
+    int32_t pt_stride;
+    int32_t *row_kv;               // [M]: page * 16 + offset, or -1 (padding / skipped)
 };
 
 struct LnArgs {
