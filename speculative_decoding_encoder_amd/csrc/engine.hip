@@ -287,14 +287,17 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
         // tiles (the LM head 64 x 64: it reads the activations once per
         // column tile), and a K split only while the grid is small.
         int mb, nb, P = 1;
+        // K-group sums go to scratch in the MFMA lane layout: whole tiles
+        auto fits = [&](int P_) {
+            return (size_t)P_ * cdiv(N, 16 * nb) * cdiv(M, 16 * mb) * (16 * mb) * (16 * nb) * 4 <=
+                   e->lay.part_bytes;
+        };
         if (mt_need <= 1) {
             // with the layer-norm prologue every workgroup recomputes the row
             // statistics: wide projections take 64-column tiles
             mb = 1;
             nb = (role == ROLE_LM_HEAD || (fuse_ln && N >= 4096)) ? 4 : 1;
-            if (split_k_ok && S >= 2 && cdiv(N, 16 * nb) < 128 &&
-                (size_t)2 * M * N * 4 <= e->lay.part_bytes)
-                P = 2;
+            if (split_k_ok && S >= 2 && cdiv(N, 16 * nb) < 128 && fits(2)) P = 2;
         } else {
             // the LM head reads the activations once per 64-column tile:
             // 96-row blocks from 6 row tiles on (1.2x faster at 288 rows);
@@ -307,8 +310,7 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                 nb = 2;
             }
             if (split_k_ok) {
-                while (P < S && cdiv(N, 16 * nb) * cdiv(M, 16 * mb) * P < 128 &&
-                       (size_t)(2 * P) * M * N * 4 <= e->lay.part_bytes)
+                while (P < S && cdiv(N, 16 * nb) * cdiv(M, 16 * mb) * P < 128 && fits(2 * P))
                     P *= 2;
             }
         }
@@ -318,7 +320,7 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
             nb = o[1];
             if (role == ROLE_LM_HEAD) nb = 4;
             P = split_k_ok ? o[2] : 1;
-            if (P < 1 || P > S || (size_t)P * M * N * 4 > e->lay.part_bytes) P = 1;
+            if ((P != 1 && P != 2 && P != 4 && P != 8) || P > S || S % P || !fits(P)) P = 1;
         }
         a.n_tiles = cdiv(N, 16 * nb);
         a.m_blocks = cdiv(M, 16 * mb);

@@ -241,34 +241,36 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
             }
             return;
         }
-        // publish this K group's sum; the last group to arrive combines
-        const size_t stride = (size_t)a.M * a.N;
-        for (int j = wave; j < NT; j += W) {
-            const int mt = j / NB, nt = j - (j / NB) * NB;
-            const f32x4 v = red[0][j][lane];
-            const int n = n_base + nt * 16 + r16;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int m = m_base + mt * 16 + 4 * g + r;
-                if (m < a.M && n < a.N)
-                    store_coherent(a.part + (size_t)grp * stride + (size_t)m * a.N + n, v[r]);
-            }
-        }
+        // K groups: each publishes its sum in the MFMA lane layout (16 bytes
+        // per lane and tile, device-coherent); the last group to arrive loads
+        // them all and combines each tile in the pairwise tree.
+        const int P = a.n_groups;
+        const int cidx = ntile * a.m_blocks + mblock;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            a.part + (size_t)cidx * P * NT * 256, 0, 0x7fffffff, 0x00020000);
+        for (int j = wave; j < NT; j += W)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, red[0][j][lane]), rs,
+                                                   (grp * NT + j) * 1024 + lane * 16, 0, CPOL_SC1);
         wait_vmem();
         __shared__ int last;
         __syncthreads();
-        const int cidx = ntile * a.m_blocks + mblock;
-        if (tid == 0) last = (arrive(&a.cnt[cidx]) == a.n_groups - 1);
+        if (tid == 0) last = (arrive(&a.cnt[cidx]) == P - 1);
         __syncthreads();
         if (!last) return;
         if (tid == 0) rearm(&a.cnt[cidx]);
-        const int rows = min(BM, a.M - m_base);
-        for (int idx = tid; idx < rows * BN; idx += 64 * W) {
-            const int rr = idx / BN, cc = idx - (idx / BN) * BN;
-            const int m = m_base + rr, n = n_base + cc;
-            if (n >= a.N) continue;
-            epi_elem<EPI>(a, m, n, tree_combine(a.part + (size_t)m * a.N + n, stride,
-                                                a.n_groups));
+        for (int j = wave; j < NT; j += W) {
+            f32x4 v[8];
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                if (s < P)
+                    v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                               rs, (s * NT + j) * 1024 + lane * 16, 0, CPOL_SC1));
+            f32x4 t[1];
+            if (P == 2) t[0] = v[0] + v[1];
+            else if (P == 4) t[0] = (v[0] + v[1]) + (v[2] + v[3]);
+            else t[0] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+            const int m0[1] = {m_base + (j / NB) * 16 + 4 * g};
+            epi_column<EPI, 1>(a, m0, n_base + (j % NB) * 16 + r16, t);
         }
     }
 }

@@ -26,10 +26,6 @@
 
 namespace wf {
 
-// cache policy of device-coherent buffer accesses (write through to, and
-// read from, the device coherence point)
-#define CPOL_SC1 16
-
 // Pairwise-tree accumulation of consecutive chunk sums: after chunk j the
 // partial p merges with the pending left siblings like a binary counter,
 // ((p0+p1)+(p2+p3))+..., the older sum always on the left. l0 ends as the

@@ -127,6 +127,10 @@ __device__ __forceinline__ void store_coherent(float *p, float v) {
 __device__ __forceinline__ float load_coherent(const float *p) {
     return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// cache policy of device-coherent buffer accesses (write through to, and
+// read from, the device coherence point)
+#define CPOL_SC1 16
+
 // s_waitcnt vmcnt(0): every vector memory operation of this wave (stores
 // included) has completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
