@@ -45,22 +45,23 @@ void gemm_chunks(int K, int &ck, int &S) {
 }
 constexpr int kSplitRowsCap = 128;   // GEMM K-split scratch sized for this many rows x 8
 
-// Cross-attention chunking: 4, 8 or 16 chunks per (request, head) -- enough
+// Cross-attention chunking: up to 32 chunks per (request, head) -- enough
 // waves to cover the GPU when the batch is small -- of spw 32-frame steps
-// each (a multiple of the load ring depth). Depends on the number of requests only, never on
-// the block length, so a row's bits do not depend on its block.
-// WF_XA_CHUNKS (4, 8 or 16) fixes the chunk count: a tuning aid. The merge
-// scratch is sized for 16 chunks (4 groups) at every batch size.
+// each (a multiple of the load ring depth), then the fewest chunks (a
+// multiple of 4, one per wave of a group) that still cover the frames at that
+// length. Depends on the number of requests only, never on the block length,
+// so a row's bits do not depend on its block. WF_XA_CHUNKS (4, 8, 16 or 32)
+// fixes the first choice: a tuning aid.
 void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
     const int steps = cdiv(F, 32);
     const int want = cdiv(2048, n * H);
-    int C = want >= 16 ? 16 : (want >= 8 ? 8 : 4);
+    int C = want >= 32 ? 32 : (want >= 16 ? 16 : (want >= 8 ? 8 : 4));
     if (const char *ov = std::getenv("WF_XA_CHUNKS")) {
         const int o = std::atoi(ov);
-        if (o == 4 || o == 8 || o == 16) C = o;
+        if (o == 4 || o == 8 || o == 16 || o == 32) C = o;
     }
-    while (C > 4 && C > steps) C >>= 1;
     spw = cdiv(cdiv(steps, C), kXaRing) * kXaRing;
+    C = cdiv(cdiv(steps, spw), 4) * 4;
     cf = spw * 32;
     G = C / 4;
 }
@@ -110,10 +111,11 @@ Layout layout_of(const wf_config *c) {
     // K-split subtree sums: up to 8 groups of kSplitRowsCap rows of the widest projection
     size_t part = (size_t)8 * kSplitRowsCap * std::max(3 * d, f) * 4;
     L.part_bytes = part;
-    // cross-attention merge partials: 4 chunk groups (the most any chunk
-    // count gives) per (request, head) for verify blocks of one row tile;
-    // taller blocks take fewer groups when they would not fit
-    const size_t xap = std::max((size_t)c->max_batch * H * 4 * 16 * (hd + 2) * 4, (size_t)8 << 20);
+    // cross-attention merge partials: 4 chunk groups per (request, head) at
+    // the largest batch for verify blocks of one row tile (small batches take
+    // up to 8 groups in the same bytes); blocks that would not fit take fewer
+    // groups
+    const size_t xap = std::max((size_t)c->max_batch * H * 4 * 16 * (hd + 4) * 4, (size_t)8 << 20);
     L.xapart_bytes = xap;
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t at = o; o += align256(bytes); return at; };
@@ -559,7 +561,7 @@ void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &G, int &spw) {
     const wf_config &c = e->c;
     const int H = c.n_heads, hd = c.head_dim;
     cross_chunks(n, H, c.n_frames, cf, G, spw);
-    const size_t rowbytes = (size_t)16 * (hd + 2) * 4;
+    const size_t rowbytes = (size_t)16 * (hd + 4) * 4;
     while (G > 1 && (size_t)n * H * mt * G * rowbytes > e->lay.xapart_bytes) {
         // long prefill blocks: fewer, longer chunks so the group partials fit
         G >>= 1;

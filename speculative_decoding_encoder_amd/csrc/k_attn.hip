@@ -310,7 +310,6 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     constexpr int PW = HD + 2;
     __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
     __shared__ float mbuf[2][16 * PW];
-    __shared__ float wts[16][5];
     __shared__ int last;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
@@ -379,19 +378,24 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
         }
         return;
     }
-    // publish this group's (m, l, o); the last group to arrive merges
+    // publish this group's (o, m, l) rows; the last group to arrive merges
+    constexpr int GPW = HD + 4;                   // o[HD], m, l, 2 spare: 16-byte rows
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        a.part + (size_t)(item - grp) * 16 * GPW, 0, 0x7fffffff, 0x00020000);
     if (wave == 0) {
-        float *pp = a.part + (size_t)item * 16 * PW;
+        const int gb = grp * 16 * GPW * 4;        // this group's bytes
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * g + r;
-            if (r16 == 0) {
-                store_coherent(pp + row * PW + 0, st.m[r]);
-                store_coherent(pp + row * PW + 1, st.l[r]);
-            }
+            if (r16 == 0)
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{__float_as_uint(st.m[r]), __float_as_uint(st.l[r])}, rs,
+                    gb + (row * GPW + HD) * 4, 0, CPOL_SC1);
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
-                store_coherent(pp + row * PW + 2 + dt * 16 + r16, st.o[dt][r]);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.o[dt][r]), rs,
+                                                      gb + (row * GPW + dt * 16 + r16) * 4, 0,
+                                                      CPOL_SC1);
         }
         wait_vmem();
         int prev = 0;
@@ -402,34 +406,59 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     __syncthreads();
     if (!last) return;
     if (tid == 0) rearm(&a.cnt[bhm]);
-    // per row: M = max_g m_g, w_g = exp(m_g - M), L = sum_g l_g w_g (pairwise)
-    const float *pb = a.part + (size_t)(item - grp) * 16 * PW;
-    if (tid < 16) {
-        float mg[4], lg[4];
-        float M = -INFINITY;
-        for (int q2 = 0; q2 < a.G; ++q2) {
-            mg[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + tid * PW);
-            lg[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + tid * PW + 1);
-            M = fmaxf(M, mg[q2]);
+    // thread: row rr, HD/16 consecutive dims; every group's (m, l) and o
+    // values load at once. Per row: M = max_g m_g, w_g = exp(m_g - M), and
+    // L = sum_g l_g w_g, o = sum_g o_g w_g in the pairwise tree over 8
+    // groups (missing groups add zero).
+    constexpr int DPT = HD / 16;
+    const int rr = tid >> 4, d0 = (tid & 15) * DPT;
+    u32x2 ml[8];
+    float ov[8][DPT];
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+        if (q2 < a.G) {
+            const int gb = (q2 * 16 * GPW + rr * GPW) * 4;
+            ml[q2] = __builtin_amdgcn_raw_buffer_load_b64(rs, gb + HD * 4, 0, CPOL_SC1);
+            if constexpr (DPT == 4) {
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rs, gb + d0 * 4, 0, CPOL_SC1);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) ov[q2][k] = __uint_as_float(v[k]);
+            } else {
+#pragma unroll
+                for (int k = 0; k < DPT; ++k)
+                    ov[q2][k] = __uint_as_float(
+                        __builtin_amdgcn_raw_buffer_load_b32(rs, gb + (d0 + k) * 4, 0, CPOL_SC1));
+            }
         }
-        float w[4];
-        for (int q2 = 0; q2 < a.G; ++q2) {
-            w[q2] = (mg[q2] == -INFINITY) ? 0.f : __expf(mg[q2] - M);
-            wts[tid][q2] = w[q2];
-        }
-        wts[tid][4] = (a.G == 2) ? lg[0] * w[0] + lg[1] * w[1]
-                                 : (lg[0] * w[0] + lg[1] * w[1]) + (lg[2] * w[2] + lg[3] * w[3]);
     }
-    __syncthreads();
-    for (int idx = tid; idx < 16 * HD; idx += 256) {
-        const int rr = idx / HD, dim = idx - rr * HD;
-        const int row = row0 + rr;
-        if (row >= a.T) continue;
-        float v[4];
-        for (int q2 = 0; q2 < a.G; ++q2)
-            v[q2] = load_coherent(pb + (size_t)q2 * 16 * PW + rr * PW + 2 + dim) * wts[rr][q2];
-        const float acc = (a.G == 2) ? v[0] + v[1] : (v[0] + v[1]) + (v[2] + v[3]);
-        store_act(a.out, b * a.T + row, h * HD + dim, a.d, acc / wts[rr][4]);
+    float M = -INFINITY;
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2)
+        if (q2 < a.G) M = fmaxf(M, __uint_as_float(ml[q2][0]));
+    float lw[8], ow[8][DPT];
+#pragma unroll
+    for (int q2 = 0; q2 < 8; ++q2) {
+        float w = 0.f;
+        if (q2 < a.G) {
+            const float mg = __uint_as_float(ml[q2][0]);
+            w = (mg == -INFINITY) ? 0.f : __expf(mg - M);
+        }
+        lw[q2] = q2 < a.G ? __uint_as_float(ml[q2][1]) * w : 0.f;
+#pragma unroll
+        for (int k = 0; k < DPT; ++k) ow[q2][k] = q2 < a.G ? ov[q2][k] * w : 0.f;
+    }
+    auto tree8 = [](const float (&v)[8]) {
+        return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    };
+    const float L = tree8(lw);
+    const int row = row0 + rr;
+    if (row < a.T) {
+#pragma unroll
+        for (int k = 0; k < DPT; ++k) {
+            const float t[8] = {ow[0][k], ow[1][k], ow[2][k], ow[3][k],
+                                ow[4][k], ow[5][k], ow[6][k], ow[7][k]};
+            store_act(a.out, b * a.T + row, h * HD + d0 + k, a.d, tree8(t) / L);
+        }
     }
 }
 
@@ -442,6 +471,7 @@ hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t s
 }
 
 hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st) {
+    if (a.G < 1 || a.G > 8) return hipErrorInvalidValue;   // the merge holds 8 groups
     dim3 grid(a.n_items);
     if (hd == 64) hipLaunchKernelGGL(cross_attn_kernel<64>, grid, dim3(256), 0, st, a);
     else if (hd == 16) hipLaunchKernelGGL(cross_attn_kernel<16>, grid, dim3(256), 0, st, a);

@@ -111,7 +111,7 @@ struct CrossAttnArgs {
                                    // (a multiple of kXaRing)
     int32_t n_items;               // n * H * mt * G workgroups
     float scale;
-    float *part;                   // [item][16][hd+2] when G > 1
+    float *part;                   // [item][16][hd+4] (o, m, l, spare) when G > 1
     int32_t *cnt;                  // [n*H*mt]
     uint16_t *out;                 // fp16 [M][d], fragment-tiled
 };

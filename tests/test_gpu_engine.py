@@ -352,6 +352,47 @@ def test_turbo_b32_ragged_shuffled_pages(torch_cuda):
     eng.close()
 
 
+def test_turbo_small_batches_cross_attention_groups(torch_cuda):
+    """Small batches split each (request, head)'s 1500 frames over more
+    waves: 6 requests take 3 chunk groups merged through scratch, 3 requests
+    6 groups. Prefill logits (6 requests) and block logits (two calls of 3)
+    against the oracle."""
+    wl = WORKLOADS[2]
+    shape = TURBO
+    B = 6
+    wbits = make_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    prefixes = [p[:40] for p in make_prefixes(wl)[:B]]
+    eng = _engine(shape, wbits, max_batch=B, max_rows=B * 64)
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    T = max(len(p) for p in prefixes)
+    toks = np.zeros((B, T), np.int32)
+    for b, p in enumerate(prefixes):
+        toks[b, :len(p)] = p
+    lens = np.array([len(p) for p in prefixes], np.int32)
+    am, lg = _verify(eng, slots, toks, lens)
+    eng.wf_rollback(eng.i32(slots), eng.i32(lens - 1))   # keep the whole prefix
+    m = om.Model(shape, wbits)
+    reqs = {}
+    for b in (0, 4):
+        req = m.new_request(encs[b])
+        ref = m.rows(req, prefixes[b], 0)
+        assert_logits_close(lg[b, :lens[b]], ref, what=f"6-request prefill req {b}")
+        reqs[b] = req
+    blocks = np.random.default_rng(12).integers(0, shape.vocab, (B, 9)).astype(np.int32)
+    for half in (slice(0, 3), slice(3, 6)):
+        sl = slots[half]
+        _, lg2 = _verify(eng, sl, blocks[half], [9] * 3)
+        for i, b in enumerate(sl):
+            if b in reqs:
+                ref = m.rows(reqs[b], blocks[b], int(lens[b]))
+                assert_logits_close(lg2[i], ref, what=f"3-request block req {b}")
+    err, _ = eng.wf_device_state()
+    assert (err == 0).all()
+    eng.close()
+
+
 def test_tall_gemm_matches_register_tiled_bitwise(torch_cuda):
     """A verify block of 32 requests x 9 rows (288 rows: QKV, fc1 and the LM
     head take the tall-block kernel) gives every logit the same bits as with
