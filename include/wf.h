@@ -143,8 +143,15 @@ typedef struct {
  *           (the V half of a page is stored transposed, [head_dim][page_size]);
  *           the drafter's layers hold its history keys (rotated) and values.
  * xkv_pool: fp16 per slot, per layer (target layers, then drafter layers):
- *           K [n_heads][F_pad][head_dim] then V [n_heads][F_pad/32][head_dim][32]
- *           (each 32-frame step of V transposed and contiguous),
+ *           K [n_heads][F_pad/32][32 * head_dim] then
+ *           V [n_heads][F_pad/32][head_dim][32]. Each 32-frame step of K is
+ *           one block in MFMA operand order: for 16-frame tile t (0, 1),
+ *           dim block k (32 dims for head_dim 64, 16 for head_dim 16) and
+ *           lane L = 16g + r (g = 0..3, r = 0..15), the values of frame
+ *           16t + r, dims 8g..8g+7 (head_dim 16: 4g..4g+3) of block k, lanes
+ *           in order. Each 32-frame step of V is transposed and contiguous;
+ *           within a step, position 8g+i holds frame 4g+i for i < 4 and
+ *           frame 16+4g+i-4 for i >= 4.
  *           F_pad = n_frames rounded up to 32.
  *           Must be zero-filled before the first wf_encode_kv.
  * workspace: engine-private scratch and slot state.

@@ -100,12 +100,12 @@ __device__ __forceinline__ void epi_store(const GemmArgs &a, const EpiCol &k, in
         if (slot < 0 || slot >= e.max_batch) return;
         uint16_t *base = e.xkv + (size_t)slot * e.xkv_slot_stride + e.xkv_layer_off;
         if (k.seg == 0) {
-            base[((size_t)k.h * e.F_pad + f) * e.hd + k.dim] = f2h_bits(v);
+            base[(size_t)k.h * e.F_pad * e.hd + xk_index(f, k.dim, e.hd)] = f2h_bits(v);
         } else {
-            // V: per head, 32-frame steps of [hd][32 frames] (one contiguous
-            // block per step, in the order the attention kernel reads it)
+            // V: per head, 32-frame steps of [hd][32 positions] (one
+            // contiguous block per step, frame j of a step at xv_pos(j))
             base[(size_t)e.H * e.F_pad * e.hd + (size_t)k.h * e.F_pad * e.hd +
-                 ((size_t)(f >> 5) * e.hd + k.dim) * 32 + (f & 31)] = f2h_bits(v + k.bias);
+                 ((size_t)(f >> 5) * e.hd + k.dim) * 32 + xv_pos(f & 31)] = f2h_bits(v + k.bias);
         }
     }
 }

@@ -19,7 +19,18 @@
 // Cross-attention reads the write-once pool: K [head][F_pad][hd] and V
 // [head][F_pad / 32][hd][32], the transposed V of each 32-frame step one
 // contiguous block, so that both operands of a step stream from
-// consecutive addresses.
+// consecutive addresses. It computes the transposed products, so that a lane
+// owns one query row and the probabilities never leave its registers:
+//  S^T = K Q^T : A = 16 keys x 32 dims, B = Q^T; lane (g, r16) gets row r16's
+//                scores for keys 4g..4g+3 of each 16-key tile.
+//  O^T += V^T P^T : A = V^T (16 dims x 32 keys), B = P^T, which is those 8
+//                probabilities packed as they are: the 32 frames of a step sit
+//                in the V block in that order (block position 8g + j holds
+//                frame 4g + j for j < 4, frame 16 + 4g + j - 4 otherwise).
+//                Lane (g, r16) accumulates row r16, dims 4g..4g+3 of each
+//                16-dim tile.
+// Row max and sum then take a local pass over 8 values and two lane
+// exchanges, instead of a 16-lane reduction per row.
 //
 // A workgroup is four waves. In self-attention they split the 32-key steps
 // of one (request, head, 16-row tile) by absolute step index (wave w takes
@@ -299,6 +310,120 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Transposed online softmax (cross-attention): the running state of query row
+// r16, its output for dims dt * 16 + 4g + r.
+template <int NDT>
+struct SmRow {
+    float m, l;
+    f32x4 o[NDT];
+    __device__ __forceinline__ void init() {
+        m = -INFINITY;
+        l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+};
+
+// One 32-frame step (frames key0 .. key0 + 31; frames >= live_to are masked).
+template <int HD>
+__device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
+                                              int live_to, float scale, SmRow<HD / 16> &st,
+                                              int g) {
+    constexpr int NDT = HD / 16;
+    f32x4 s[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (HD == 64) {
+            s[t] = mfma_f16_k32(f.k[t][0], q.a[0], s[t]);
+            s[t] = mfma_f16_k32(f.k[t][1], q.a[1], s[t]);
+        } else {
+            s[t] = mfma_f16_k16(f.k16[t], q.h, s[t]);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            s[t][r] = key0 + 16 * t + 4 * g + r < live_to ? s[t][r] * scale : -INFINITY;
+    }
+    float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                     fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    tm = fmaxf(tm, __shfl_xor(tm, 16));
+    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    const float mnew = fmaxf(st.m, tm);
+    const float alpha = (mnew == -INFINITY) ? 0.f : __expf(st.m - mnew);
+    float p[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            p[t][r] = (s[t][r] == -INFINITY) ? 0.f : __expf(s[t][r] - mnew);
+    float ls = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+    ls += __shfl_xor(ls, 16);                 // a + b = b + a: the four lanes agree
+    ls += __shfl_xor(ls, 32);
+    st.l = alpha * st.l + ls;
+    st.m = mnew;
+    const u32x4 pb = {pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]),
+                      pack_h2(p[1][0], p[1][1]), pack_h2(p[1][2], p[1][3])};
+    const bool tail = key0 + 32 > live_to;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+        st.o[dt] *= alpha;
+        u32x4 vb = f.v[dt];
+        if (tail) {                               // dead frames: zero operand
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                // block positions 8g + 2w, 8g + 2w + 1
+                const int fr = key0 + (w < 2 ? 4 * g + 2 * w : 16 + 4 * g + 2 * (w - 2));
+                uint32_t x = vb[w];
+                if (fr >= live_to) x &= 0xffff0000u;
+                if (fr + 1 >= live_to) x &= 0x0000ffffu;
+                vb[w] = x;
+            }
+        }
+        st.o[dt] = mfma_f16_k32(vb, pb, st.o[dt]);
+    }
+}
+
+// Partial (o, m, l) of 16 rows in LDS, rows of HD + 4 floats.
+template <int HD, int NDT>
+__device__ __forceinline__ void put_row(float *buf, const SmRow<NDT> &s, int g, int r16) {
+    constexpr int PW = HD + 4;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        *reinterpret_cast<f32x4 *>(&buf[r16 * PW + dt * 16 + 4 * g]) = s.o[dt];
+    if (g == 0) {
+        buf[r16 * PW + HD] = s.m;
+        buf[r16 * PW + HD + 1] = s.l;
+    }
+}
+// s = s (+) partial in buf: rescale both to the larger running max.
+template <int HD, int NDT>
+__device__ __forceinline__ void merge_row(SmRow<NDT> &s, const float *buf, int g, int r16) {
+    constexpr int PW = HD + 4;
+    const float mb = buf[r16 * PW + HD], lb = buf[r16 * PW + HD + 1];
+    const float M = fmaxf(s.m, mb);
+    const float wa = (s.m == -INFINITY) ? 0.f : __expf(s.m - M);
+    const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - M);
+    s.l = s.l * wa + lb * wb;
+    s.m = M;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+        s.o[dt] = s.o[dt] * wa + *reinterpret_cast<const f32x4 *>(&buf[r16 * PW + dt * 16 + 4 * g]) * wb;
+}
+// ((w0+w1)+(w2+w3)) over the four waves; the result lands in wave 0.
+template <int HD, int NDT>
+__device__ __forceinline__ void merge_waves_t(SmRow<NDT> &s, float (*mbuf)[16 * (HD + 4)],
+                                              int wave, int g, int r16) {
+    if (wave & 1) put_row<HD>(mbuf[wave >> 1], s, g, r16);
+    __syncthreads();
+    if (!(wave & 1)) merge_row<HD>(s, mbuf[wave >> 1], g, r16);
+    __syncthreads();
+    if (wave == 2) put_row<HD>(mbuf[0], s, g, r16);
+    __syncthreads();
+    if (wave == 0) merge_row<HD>(s, mbuf[0], g, r16);
+}
+
+// ---------------------------------------------------------------------------
 // Cross-attention over the write-once pool. Workgroup = (request, head,
 // 16-row tile, chunk group); wave w takes chunk 4 * group + w of cf frames
 // (spw 32-frame steps, a multiple of the load ring depth kXaRing). Three
@@ -307,9 +432,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
 template <int HD>
 __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     constexpr int NDT = HD / 16;
-    constexpr int PW = HD + 2;
-    __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
-    __shared__ float mbuf[2][16 * PW];
+    __shared__ __attribute__((aligned(16))) float mbuf[2][16 * (HD + 4)];
     __shared__ int last;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
@@ -334,23 +457,21 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     const int last_fb = a.F_pad - 32;              // loads stay inside this head's frames
     auto load = [&](int s, KVStep<HD> &f) {
         const int fb = min(c0 + 32 * s, last_fb);
+        const uint16_t *kstep = kh + (size_t)(fb >> 5) * 32 * HD;   // fragment-order K block
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-            const uint16_t *krow = kh + (size_t)(fb + 16 * t + r16) * HD;
             if constexpr (HD == 64) {
-                f.k[t][0] = ld16(krow + 8 * g);
-                f.k[t][1] = ld16(krow + 32 + 8 * g);
+                f.k[t][0] = ld16(kstep + (t * 2 + 0) * 512 + lane * 8);
+                f.k[t][1] = ld16(kstep + (t * 2 + 1) * 512 + lane * 8);
             } else {
-                f.k16[t] = ld8(krow + 4 * g);
+                f.k16[t] = ld8(kstep + t * 256 + lane * 4);
             }
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
             f.v[dt] = ld16(vh + ((size_t)(fb >> 5) * HD + dt * 16 + r16) * 32 + 8 * g);
     };
-    auto live = [&](int, int frame) { return frame < c1; };
-
-    SmState<NDT> st;
+    SmRow<NDT> st;
     st.init();
     KVStep<HD> f[kXaRing];
 #pragma unroll
@@ -358,23 +479,20 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     for (int s0 = 0; s0 < a.spw; s0 += kXaRing) {
 #pragma unroll
         for (int i = 0; i < kXaRing; ++i) {
-            attend_step<HD>(q, f[i], c0 + 32 * (s0 + i), c1, a.scale, st, Pt[wave], g, r16, live);
+            attend_step_t<HD>(q, f[i], c0 + 32 * (s0 + i), c1, a.scale, st, g);
             if (s0 + kXaRing < a.spw) load(s0 + i + kXaRing, f[i]);
         }
     }
-    merge_waves<HD>(st, mbuf, wave, g, r16);
+    merge_waves_t<HD>(st, mbuf, wave, g, r16);
 
     if (a.G == 1) {
-        if (wave == 0) {
+        if (wave == 0 && qrow < a.T) {
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int row = row0 + 4 * g + r;
-                    if (row < a.T)
-                        store_act(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
-                                    st.o[dt][r] / st.l[r]);
-                }
+                for (int r = 0; r < 4; ++r)
+                    store_act(a.out, b * a.T + qrow, h * HD + dt * 16 + 4 * g + r, a.d,
+                              st.o[dt][r] / st.l);
         }
         return;
     }
@@ -384,19 +502,14 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
         a.part + (size_t)(item - grp) * 16 * GPW, 0, 0x7fffffff, 0x00020000);
     if (wave == 0) {
         const int gb = grp * 16 * GPW * 4;        // this group's bytes
+        if (g == 0)
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(st.m), __float_as_uint(st.l)},
+                                                  rs, gb + (r16 * GPW + HD) * 4, 0, CPOL_SC1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * g + r;
-            if (r16 == 0)
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{__float_as_uint(st.m[r]), __float_as_uint(st.l[r])}, rs,
-                    gb + (row * GPW + HD) * 4, 0, CPOL_SC1);
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(st.o[dt][r]), rs,
-                                                      gb + (row * GPW + dt * 16 + r16) * 4, 0,
-                                                      CPOL_SC1);
-        }
+        for (int dt = 0; dt < NDT; ++dt)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.o[dt]), rs,
+                                                   gb + (r16 * GPW + dt * 16 + 4 * g) * 4, 0,
+                                                   CPOL_SC1);
         wait_vmem();
         int prev = 0;
         if (lane == 0) prev = arrive(&a.cnt[bhm]);

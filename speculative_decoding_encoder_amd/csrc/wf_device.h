@@ -45,6 +45,27 @@ __host__ __device__ __forceinline__ size_t xh_index(int m, int k, int K) {
             (size_t)(((k >> 3) & 3) * 16 + (m & 15))) * 8 + (size_t)(k & 7);
 }
 
+// Cross-attention V blocks (one per 32-frame step, [hd][32]): the position of
+// frame j (0..31 within its step). Position 8g + i holds frame 4g + i for
+// i < 4 and frame 16 + 4g + i - 4 otherwise, the order in which the
+// transposed score tiles leave the probabilities in a lane's registers.
+__host__ __device__ __forceinline__ int xv_pos(int j) {
+    return j < 16 ? 8 * (j >> 2) + (j & 3) : 8 * ((j - 16) >> 2) + 4 + (j & 3);
+}
+
+// Cross-attention K (per head, F_pad frames x hd): each 32-frame step is one
+// block in the lane order of the MFMA A operand of S^T = K Q^T, a 1 KB (hd
+// 64) or 512 B (hd 16) piece per 16-frame tile and operand load, so every
+// load of a step reads consecutive addresses. Element offset of (frame f,
+// dim c) within the head.
+__host__ __device__ __forceinline__ size_t xk_index(int f, int c, int hd) {
+    const size_t step = (size_t)(f >> 5) * 32 * hd;
+    const int t = (f >> 4) & 1, r = f & 15;
+    if (hd == 16) return step + t * 256 + ((c >> 2) * 16 + r) * 4 + (c & 3);
+    return step + ((size_t)(t * (hd >> 5) + (c >> 5)) * 64 + ((c >> 3) & 3) * 16 + r) * 8 +
+           (c & 7);
+}
+
 // bf16 <-> fp32. Rounding to bf16 is to nearest, ties to even.
 __device__ __forceinline__ float bf2f(uint16_t h) {
     return __uint_as_float(((uint32_t)h) << 16);
