@@ -291,7 +291,7 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     KVStep<HD> cur, nxt;
     if (wave < nsteps) load(wave, cur);
     for (int j = wave; j < nsteps; j += 4) {
-        if (j + 4 < nsteps) load(j + 4, nxt);
+        load(min(j + 4, nsteps - 1), nxt);        // unconditional: exact wait counts
         attend_step<HD>(q, cur, 32 * j, kmax + 1, a.scale, st, Pt[wave], g, r16, live);
         cur = nxt;
     }
@@ -324,10 +324,14 @@ struct SmRow {
     }
 };
 
-// One 32-frame step (frames key0 .. key0 + 31; frames >= live_to are masked).
-template <int HD>
+// One 32-frame step (frames key0 .. key0 + 31). Scores stay unscaled: the
+// running max m is in raw score units and every weight is
+// 2^((s - m) * sl2e), sl2e = scale * log2(e). MASK (the chunk's tail step):
+// frames >= live_to get weight 0 and a zero V operand; other steps skip the
+// masking and the -inf guards (their scores are finite).
+template <int HD, bool MASK>
 __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
-                                              int live_to, float scale, SmRow<HD / 16> &st,
+                                              int live_to, float sl2e, SmRow<HD / 16> &st,
                                               int g) {
     constexpr int NDT = HD / 16;
     f32x4 s[2];
@@ -340,22 +344,28 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
         } else {
             s[t] = mfma_f16_k16(f.k16[t], q.h, s[t]);
         }
+        if constexpr (MASK) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            s[t][r] = key0 + 16 * t + 4 * g + r < live_to ? s[t][r] * scale : -INFINITY;
+            for (int r = 0; r < 4; ++r)
+                if (key0 + 16 * t + 4 * g + r >= live_to) s[t][r] = -INFINITY;
+        }
     }
     float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
     tm = fmaxf(tm, __shfl_xor(tm, 16));
     tm = fmaxf(tm, __shfl_xor(tm, 32));
     const float mnew = fmaxf(st.m, tm);
-    const float alpha = (mnew == -INFINITY) ? 0.f : __expf(st.m - mnew);
+    const float ms = mnew * sl2e;
+    // unmasked steps: mnew is finite, and st.m = -inf (first step) gives 0
+    const float alpha = (MASK && mnew == -INFINITY) ? 0.f
+                                                    : __builtin_amdgcn_exp2f(__fmaf_rn(st.m, sl2e, -ms));
     float p[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-            p[t][r] = (s[t][r] == -INFINITY) ? 0.f : __expf(s[t][r] - mnew);
+            p[t][r] = (MASK && s[t][r] == -INFINITY) ? 0.f
+                                                      : __builtin_amdgcn_exp2f(__fmaf_rn(s[t][r], sl2e, -ms));
     float ls = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
                ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
     ls += __shfl_xor(ls, 16);                 // a + b = b + a: the four lanes agree
@@ -364,23 +374,19 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
     st.m = mnew;
     const u32x4 pb = {pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]),
                       pack_h2(p[1][0], p[1][1]), pack_h2(p[1][2], p[1][3])};
-    const bool tail = key0 + 32 > live_to;
+    u32x4 vm = {~0u, ~0u, ~0u, ~0u};
+    if constexpr (MASK) {
+        // block positions 8g + 2w, 8g + 2w + 1 of dead frames: zero operand
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int fr = key0 + (w < 2 ? 4 * g + 2 * w : 16 + 4 * g + 2 * (w - 2));
+            vm[w] = (fr < live_to ? 0x0000ffffu : 0u) | (fr + 1 < live_to ? 0xffff0000u : 0u);
+        }
+    }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
         st.o[dt] *= alpha;
-        u32x4 vb = f.v[dt];
-        if (tail) {                               // dead frames: zero operand
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                // block positions 8g + 2w, 8g + 2w + 1
-                const int fr = key0 + (w < 2 ? 4 * g + 2 * w : 16 + 4 * g + 2 * (w - 2));
-                uint32_t x = vb[w];
-                if (fr >= live_to) x &= 0xffff0000u;
-                if (fr + 1 >= live_to) x &= 0x0000ffffu;
-                vb[w] = x;
-            }
-        }
-        st.o[dt] = mfma_f16_k32(vb, pb, st.o[dt]);
+        st.o[dt] = mfma_f16_k32(MASK ? (f.v[dt] & vm) : f.v[dt], pb, st.o[dt]);
     }
 }
 
@@ -398,12 +404,13 @@ __device__ __forceinline__ void put_row(float *buf, const SmRow<NDT> &s, int g, 
 }
 // s = s (+) partial in buf: rescale both to the larger running max.
 template <int HD, int NDT>
-__device__ __forceinline__ void merge_row(SmRow<NDT> &s, const float *buf, int g, int r16) {
+__device__ __forceinline__ void merge_row(SmRow<NDT> &s, const float *buf, float sl2e, int g,
+                                          int r16) {
     constexpr int PW = HD + 4;
     const float mb = buf[r16 * PW + HD], lb = buf[r16 * PW + HD + 1];
     const float M = fmaxf(s.m, mb);
-    const float wa = (s.m == -INFINITY) ? 0.f : __expf(s.m - M);
-    const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - M);
+    const float wa = (s.m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((s.m - M) * sl2e);
+    const float wb = (mb == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mb - M) * sl2e);
     s.l = s.l * wa + lb * wb;
     s.m = M;
 #pragma unroll
@@ -413,14 +420,14 @@ __device__ __forceinline__ void merge_row(SmRow<NDT> &s, const float *buf, int g
 // ((w0+w1)+(w2+w3)) over the four waves; the result lands in wave 0.
 template <int HD, int NDT>
 __device__ __forceinline__ void merge_waves_t(SmRow<NDT> &s, float (*mbuf)[16 * (HD + 4)],
-                                              int wave, int g, int r16) {
+                                              float sl2e, int wave, int g, int r16) {
     if (wave & 1) put_row<HD>(mbuf[wave >> 1], s, g, r16);
     __syncthreads();
-    if (!(wave & 1)) merge_row<HD>(s, mbuf[wave >> 1], g, r16);
+    if (!(wave & 1)) merge_row<HD>(s, mbuf[wave >> 1], sl2e, g, r16);
     __syncthreads();
     if (wave == 2) put_row<HD>(mbuf[0], s, g, r16);
     __syncthreads();
-    if (wave == 0) merge_row<HD>(s, mbuf[0], g, r16);
+    if (wave == 0) merge_row<HD>(s, mbuf[0], sl2e, g, r16);
 }
 
 // ---------------------------------------------------------------------------
@@ -429,7 +436,10 @@ __device__ __forceinline__ void merge_waves_t(SmRow<NDT> &s, float (*mbuf)[16 * 
 // (spw 32-frame steps, a multiple of the load ring depth kXaRing). Three
 // workgroups fit a CU, so a batch of 32 requests (640 workgroups) runs in one
 // round.
-template <int HD>
+// SPW > 0: the chunk length is a compile-time a.spw and the step loop is
+// straight-line code (the compiler's wait counts then keep kXaRing - 1
+// steps in flight; across a loop back-edge it waits for the whole ring).
+template <int HD, int SPW>
 __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     constexpr int NDT = HD / 16;
     __shared__ __attribute__((aligned(16))) float mbuf[2][16 * (HD + 4)];
@@ -476,14 +486,27 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
     KVStep<HD> f[kXaRing];
 #pragma unroll
     for (int i = 0; i < kXaRing; ++i) load(i, f[i]);
-    for (int s0 = 0; s0 < a.spw; s0 += kXaRing) {
+    // the refill is unconditional (past the chunk: its last step again, an
+    // L2 hit) and pinned after the step
+    const float sl2e = a.scale * 1.4426950408889634f;
+    auto two = [&](int s0) {
 #pragma unroll
         for (int i = 0; i < kXaRing; ++i) {
-            attend_step_t<HD>(q, f[i], c0 + 32 * (s0 + i), c1, a.scale, st, g);
-            if (s0 + kXaRing < a.spw) load(s0 + i + kXaRing, f[i]);
+            const int key0 = c0 + 32 * (s0 + i);
+            if (key0 + 32 > c1) attend_step_t<HD, true>(q, f[i], key0, c1, sl2e, st, g);
+            else attend_step_t<HD, false>(q, f[i], key0, c1, sl2e, st, g);
+            __builtin_amdgcn_sched_barrier(0);
+            load(min(s0 + i + kXaRing, a.spw - 1), f[i]);
+            __builtin_amdgcn_sched_barrier(0);
         }
+    };
+    if constexpr (SPW > 0) {
+#pragma unroll
+        for (int s0 = 0; s0 < SPW; s0 += kXaRing) two(s0);
+    } else {
+        for (int s0 = 0; s0 < a.spw; s0 += kXaRing) two(s0);
     }
-    merge_waves_t<HD>(st, mbuf, wave, g, r16);
+    merge_waves_t<HD>(st, mbuf, sl2e, wave, g, r16);
 
     if (a.G == 1) {
         if (wave == 0 && qrow < a.T) {
@@ -554,7 +577,7 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
         float w = 0.f;
         if (q2 < a.G) {
             const float mg = __uint_as_float(ml[q2][0]);
-            w = (mg == -INFINITY) ? 0.f : __expf(mg - M);
+            w = (mg == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((mg - M) * sl2e);
         }
         lw[q2] = q2 < a.G ? __uint_as_float(ml[q2][1]) * w : 0.f;
 #pragma unroll
@@ -586,8 +609,17 @@ hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t s
 hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st) {
     if (a.G < 1 || a.G > 8) return hipErrorInvalidValue;   // the merge holds 8 groups
     dim3 grid(a.n_items);
-    if (hd == 64) hipLaunchKernelGGL(cross_attn_kernel<64>, grid, dim3(256), 0, st, a);
-    else if (hd == 16) hipLaunchKernelGGL(cross_attn_kernel<16>, grid, dim3(256), 0, st, a);
+    if (hd == 64) {
+        // the chunk lengths of 1500 frames: batches of 32 and more (12
+        // steps), small batches (2), a few in between (4, 6)
+        if (a.spw == 12) hipLaunchKernelGGL((cross_attn_kernel<64, 12>), grid, dim3(256), 0, st, a);
+        else if (a.spw == 6) hipLaunchKernelGGL((cross_attn_kernel<64, 6>), grid, dim3(256), 0, st, a);
+        else if (a.spw == 4) hipLaunchKernelGGL((cross_attn_kernel<64, 4>), grid, dim3(256), 0, st, a);
+        else if (a.spw == 2) hipLaunchKernelGGL((cross_attn_kernel<64, 2>), grid, dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((cross_attn_kernel<64, 0>), grid, dim3(256), 0, st, a);
+    } else if (hd == 16) {
+        hipLaunchKernelGGL((cross_attn_kernel<16, 0>), grid, dim3(256), 0, st, a);
+    }
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
