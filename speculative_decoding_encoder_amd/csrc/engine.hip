@@ -273,14 +273,24 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     }
     if (e->tall_gemm && M >= kTallMinRows && M <= kTallMaxRows && gemm_tl_built(role, S, ck) &&
         !fuse_ln) {
-        // tall blocks (tens of requests): 96- or 128-row x 64-column tiles
-        // over the whole of K
-        const int mbt = M <= 576 ? 6 : 8;
+        // tall blocks (tens of requests), 64-column tiles (from a sweep on
+        // MI355X): the wide projections (QKV, fc1) 96 rows (128 above 576)
+        // over the whole of K; the d-wide ones (O, O_c, cross Q) 96 rows
+        // from 576 rows on (below, the register-tiled kernel's 64 x 32 tiles
+        // win); fc2 (K = 5120) 96 rows in 4 K groups
+        int mbt = 6, P = 1;
+        bool take = true;
+        if (role == ROLE_QKV || role == ROLE_FC1) mbt = M <= 576 ? 6 : 8;
+        else if (role == ROLE_OPROJ || role == ROLE_CROSS_Q) take = M >= 576;
+        else P = 4;
         a.n_tiles = cdiv(N, 64);
         a.m_blocks = cdiv(M, 16 * mbt);
-        a.n_groups = 1;
-        a.n_wg = a.n_tiles * a.m_blocks;
-        return timed(e, kind, st, [&] { return launch_gemm_tl(role, a, mbt, st); });
+        a.n_groups = P;
+        a.n_wg = a.n_tiles * a.m_blocks * P;
+        // K-group sums: per (tile, K group) 4 waves x mb tiles of 1 KB
+        if (P > 1 && (size_t)a.n_tiles * a.m_blocks * P * 4 * mbt * 1024 > e->lay.part_bytes)
+            take = false;
+        if (take) return timed(e, kind, st, [&] { return launch_gemm_tl(role, a, mbt, st); });
     }
     if (rk) {
         // Register-tiled kernel (tiles from a sweep on MI355X). One row tile:

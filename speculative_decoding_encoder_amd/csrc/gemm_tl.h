@@ -295,16 +295,19 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     }
 }
 
-// The verify-pass instances: 96 x 64 tiles up to 576 rows, 128 x 64 above;
-// the whole of K per workgroup (no scratch), 5 k-steps per chunk (K = 1280).
+// The verify-pass instances. K = 1280 (5 k-steps per chunk): 96 x 64 tiles
+// (mb 6) or 128 x 64 (mb 8) over the whole of K. K = 5120 (fc2, 20 k-steps
+// per chunk): 96 x 64 tiles in 4 K groups of 2 chunks.
 template <int ROLE>
 hipError_t launch_tl(const GemmArgs &a, int mb, hipStream_t st) {
-    if (a.S != 8 || a.ck != 5 || a.n_groups != 1) return hipErrorInvalidValue;
+    if (a.S != 8) return hipErrorInvalidValue;
     const int grid = ((a.n_wg + 7) / 8) * 8;
-    if (mb == 6)
+    if (a.ck == 5 && a.n_groups == 1 && mb == 6)
         hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
-    else if (mb == 8)
+    else if (a.ck == 5 && a.n_groups == 1 && mb == 8)
         hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 8, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
+    else if (a.ck == 20 && a.n_groups == 4 && mb == 6)
+        hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 2, 20, 4>), dim3(grid), dim3(256), 0, st, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();

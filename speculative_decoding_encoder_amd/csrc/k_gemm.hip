@@ -310,14 +310,17 @@ hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, int mb, hipStream_t st)
 
 hipError_t launch_gemm_tl(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
-        case ROLE_QKV: return launch_gemm_tl_a(role, a, mb, st);
-        case ROLE_FC1: return launch_gemm_tl_b(role, a, mb, st);
+        case ROLE_QKV: case ROLE_OPROJ: case ROLE_CROSS_Q: return launch_gemm_tl_a(role, a, mb, st);
+        case ROLE_FC1: case ROLE_FC2: return launch_gemm_tl_b(role, a, mb, st);
     }
     return hipErrorInvalidValue;
 }
 
 bool gemm_tl_built(int role, int S, int ck) {
-    return (role == ROLE_QKV || role == ROLE_FC1) && S == 8 && ck == 5;
+    if (S != 8) return false;
+    if (role == ROLE_QKV || role == ROLE_FC1 || role == ROLE_OPROJ || role == ROLE_CROSS_Q)
+        return ck == 5;
+    return role == ROLE_FC2 && ck == 20;
 }
 
 hipError_t launch_gemm_rk(int role, const GemmArgs &a, int mb, int nb, hipStream_t st) {

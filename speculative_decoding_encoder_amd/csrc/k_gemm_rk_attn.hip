@@ -16,6 +16,8 @@ hipError_t launch_gemm_rk_a(int role, const GemmArgs &a, int mb, int nb, hipStre
 hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
         case ROLE_QKV: return launch_tl<ROLE_QKV>(a, mb, st);
+        case ROLE_OPROJ: return launch_tl<ROLE_OPROJ>(a, mb, st);
+        case ROLE_CROSS_Q: return launch_tl<ROLE_CROSS_Q>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }

@@ -15,6 +15,7 @@ hipError_t launch_gemm_rk_b(int role, const GemmArgs &a, int mb, int nb, hipStre
 hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
         case ROLE_FC1: return launch_tl<ROLE_FC1>(a, mb, st);
+        case ROLE_FC2: return launch_tl<ROLE_FC2>(a, mb, st);
     }
     return hipErrorInvalidValue;
 }
