@@ -471,15 +471,15 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             if constexpr (HD == 64) {
-                f.k[t][0] = ld16(kstep + (t * 2 + 0) * 512 + lane * 8);
-                f.k[t][1] = ld16(kstep + (t * 2 + 1) * 512 + lane * 8);
+                f.k[t][0] = ld16_nt(kstep + (t * 2 + 0) * 512 + lane * 8);
+                f.k[t][1] = ld16_nt(kstep + (t * 2 + 1) * 512 + lane * 8);
             } else {
-                f.k16[t] = ld8(kstep + t * 256 + lane * 4);
+                f.k16[t] = ld8_nt(kstep + t * 256 + lane * 4);
             }
         }
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
-            f.v[dt] = ld16(vh + ((size_t)(fb >> 5) * HD + dt * 16 + r16) * 32 + 8 * g);
+            f.v[dt] = ld16_nt(vh + ((size_t)(fb >> 5) * HD + dt * 16 + r16) * 32 + 8 * g);
     };
     SmRow<NDT> st;
     st.init();

@@ -20,6 +20,14 @@ __device__ __forceinline__ u32x4 ld16(const void *p) {
 __device__ __forceinline__ u32x2 ld8(const void *p) {
     return *reinterpret_cast<const u32x2 *>(p);
 }
+// Streaming loads (data read once): non-temporal, so they do not compete
+// with reused lines in the caches.
+__device__ __forceinline__ u32x4 ld16_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x2 ld8_nt(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(p));
+}
 
 __device__ __forceinline__ f32x4 mfma_bf16_k32(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
