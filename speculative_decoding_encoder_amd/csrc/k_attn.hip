@@ -6,31 +6,27 @@
 // indices, so a row's result does not depend on how many other rows share
 // its tile: a block of K+1 rows and K+1 single-row passes give the same bits.
 //
-//  S = Q K^T : A = Q rows (16 x 32 dims per MFMA), B = 16 keys.
-//  O += P V  : A = P (16 rows x 32 keys, fp16, staged through LDS to change
-//              from the C layout to the A layout), B = V^T (16 dims x 32 keys).
-//
-// Self-attention reads the paged cache: a page holds 16 positions; K is
-// [head][16][hd] and V is stored transposed, [head][hd][16], so that both
-// MFMA B operands are contiguous 16-byte loads. Row i of the block (position
-// L+i) sees keys 0..L+i ("one causal target pass over the anchor and the
-// candidates", Whisper-Flash section 3.1).
-//
-// Cross-attention reads the write-once pool: K [head][F_pad][hd] and V
-// [head][F_pad / 32][hd][32], the transposed V of each 32-frame step one
-// contiguous block, so that both operands of a step stream from
-// consecutive addresses. It computes the transposed products, so that a lane
-// owns one query row and the probabilities never leave its registers:
+// Both compute the transposed products, so that a lane owns one query row and
+// the probabilities never leave its registers:
 //  S^T = K Q^T : A = 16 keys x 32 dims, B = Q^T; lane (g, r16) gets row r16's
 //                scores for keys 4g..4g+3 of each 16-key tile.
 //  O^T += V^T P^T : A = V^T (16 dims x 32 keys), B = P^T, which is those 8
-//                probabilities packed as they are: the 32 frames of a step sit
-//                in the V block in that order (block position 8g + j holds
-//                frame 4g + j for j < 4, frame 16 + 4g + j - 4 otherwise).
-//                Lane (g, r16) accumulates row r16, dims 4g..4g+3 of each
-//                16-dim tile.
-// Row max and sum then take a local pass over 8 values and two lane
-// exchanges, instead of a 16-lane reduction per row.
+//                probabilities packed as they are (keys 4g..4g+3 of each
+//                tile). Lane (g, r16) accumulates row r16, dims 4g..4g+3 of
+//                each 16-dim tile.
+// Row max and sum take a local pass over 8 values and two lane exchanges.
+//
+// Self-attention reads the paged cache: a page holds 16 positions; K is
+// [head][16][hd] and V is stored transposed, [head][hd][16], so that a V^T
+// operand is two 8-byte loads (positions 4g..4g+3 of the step's two pages).
+// Row i of the block (position L+i) sees keys 0..L+i ("one causal target pass
+// over the anchor and the candidates", Whisper-Flash section 3.1).
+//
+// Cross-attention reads the write-once pool: K steps in MFMA operand order
+// and V [head][F_pad / 32][hd][32], the transposed V of each 32-frame step one
+// contiguous block with its frames in the order of the score tiles (block
+// position 8g + j holds frame 4g + j for j < 4, frame 16 + 4g + j - 4
+// otherwise), so that every operand load reads consecutive addresses.
 //
 // A workgroup is four waves. In self-attention they split the 32-key steps
 // of one (request, head, 16-row tile) by absolute step index (wave w takes
@@ -63,115 +59,9 @@ __device__ __forceinline__ QFrag<HD> load_q(const uint16_t *qrow, bool ok, int g
     return f;
 }
 
-// 16x16 score tile: rows of Q against the 16 keys whose rows start at krow
-// (this lane's key row; lane r16 loads key r16).
-template <int HD>
-__device__ __forceinline__ f32x4 qk_tile(const QFrag<HD> &q, const uint16_t *krow, int g) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (HD == 64) {
-        s = mfma_f16_k32(q.a[0], ld16(krow + 8 * g), s);
-        s = mfma_f16_k32(q.a[1], ld16(krow + 32 + 8 * g), s);
-    } else {
-        s = mfma_f16_k16(q.h, ld8(krow + 4 * g), s);
-    }
-    return s;
-}
-
-// Online-softmax update for the 4 rows a lane holds (C layout rows 4g+r)
-// given two 16-key score tiles already scaled and masked (-inf = masked).
-// Writes the fp16 probabilities into this wave's LDS tile P[16][32].
-template <int NDT>
-__device__ __forceinline__ void softmax_step(f32x4 &s0, f32x4 &s1, float (&mrun)[4],
-                                             float (&lrun)[4], f32x4 (&o)[NDT],
-                                             uint16_t *P, int g, int r16) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const float tm = max16(fmaxf(s0[r], s1[r]));
-        const float mnew = fmaxf(mrun[r], tm);
-        const float alpha = (mnew == -INFINITY) ? 0.f : __expf(mrun[r] - mnew);
-        const float p0 = (s0[r] == -INFINITY) ? 0.f : __expf(s0[r] - mnew);
-        const float p1 = (s1[r] == -INFINITY) ? 0.f : __expf(s1[r] - mnew);
-        lrun[r] = alpha * lrun[r] + sum16(p0 + p1);
-        mrun[r] = mnew;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt][r] *= alpha;
-        const int row = 4 * g + r;
-        P[row * 32 + r16] = f2h_bits(p0);
-        P[row * 32 + 16 + r16] = f2h_bits(p1);
-    }
-}
-
 // element (row, c) of a fragment-tiled fp16 activation buffer of width K
 __device__ __forceinline__ void store_act(uint16_t *out, int row, int c, int K, float v) {
     out[xh_index(row, c, K)] = f2h_bits(v);
-}
-
-// Intra-wave ordering of LDS traffic (the P tile is private to a wave).
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-// Running softmax state of the 4 rows (4g+r) a lane holds.
-template <int NDT>
-struct SmState {
-    float m[4], l[4];
-    f32x4 o[NDT];
-    __device__ __forceinline__ void init() {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-};
-
-// Partial (m, l, o) of 16 rows in LDS: row-major [16][HD + 2].
-template <int HD, int NDT>
-__device__ __forceinline__ void put_partial(float *buf, const SmState<NDT> &s, int g, int r16) {
-    constexpr int PW = HD + 2;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        if (r16 == 0) {
-            buf[row * PW] = s.m[r];
-            buf[row * PW + 1] = s.l[r];
-        }
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) buf[row * PW + 2 + dt * 16 + r16] = s.o[dt][r];
-    }
-}
-
-// s = s (+) partial in buf: rescale both to the larger running max.
-template <int HD, int NDT>
-__device__ __forceinline__ void merge_partial(SmState<NDT> &s, const float *buf, int g, int r16) {
-    constexpr int PW = HD + 2;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        const float mb = buf[row * PW], lb = buf[row * PW + 1];
-        const float M = fmaxf(s.m[r], mb);
-        const float wa = (s.m[r] == -INFINITY) ? 0.f : __expf(s.m[r] - M);
-        const float wb = (mb == -INFINITY) ? 0.f : __expf(mb - M);
-        s.l[r] = s.l[r] * wa + lb * wb;
-        s.m[r] = M;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            s.o[dt][r] = s.o[dt][r] * wa + buf[row * PW + 2 + dt * 16 + r16] * wb;
-    }
-}
-
-// ((w0+w1)+(w2+w3)) over the four waves; the result lands in wave 0.
-template <int HD, int NDT>
-__device__ __forceinline__ void merge_waves(SmState<NDT> &s, float (*mbuf)[16 * (HD + 2)],
-                                            int wave, int g, int r16) {
-    if (wave & 1) put_partial<HD>(mbuf[wave >> 1], s, g, r16);
-    __syncthreads();
-    if (!(wave & 1)) merge_partial<HD>(s, mbuf[wave >> 1], g, r16);
-    __syncthreads();
-    if (wave == 2) put_partial<HD>(mbuf[0], s, g, r16);
-    __syncthreads();
-    if (wave == 0) merge_partial<HD>(s, mbuf[0], g, r16);
 }
 
 // K and V^T fragments of one 32-key step.
@@ -181,133 +71,6 @@ struct KVStep {
     u32x2 k16[2];      // HD = 16
     u32x4 v[HD / 16];  // V^T: 16 dims x 8 keys per lane
 };
-
-// One 32-key step of the online softmax: scores of the two 16-key tiles
-// (key index key0 + 16t + r16 is live for row 4g+r iff live(r, key)), then
-// P V with the probabilities staged through this wave's LDS tile.
-template <int HD, typename Live>
-__device__ __forceinline__ void attend_step(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
-                                            int vlive_to, float scale, SmState<HD / 16> &st,
-                                            uint16_t *P, int g, int r16, Live live) {
-    constexpr int NDT = HD / 16;
-    f32x4 s[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (HD == 64) {
-            s[t] = mfma_f16_k32(q.a[0], f.k[t][0], s[t]);
-            s[t] = mfma_f16_k32(q.a[1], f.k[t][1], s[t]);
-        } else {
-            s[t] = mfma_f16_k16(q.h, f.k16[t], s[t]);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            s[t][r] = live(r, key0 + 16 * t + r16) ? s[t][r] * scale : -INFINITY;
-    }
-    softmax_step<NDT>(s[0], s[1], st.m, st.l, st.o, P, g, r16);
-    wave_lds_sync();
-    const u32x4 pa = *reinterpret_cast<const u32x4 *>(&P[r16 * 32 + 8 * g]);
-    const int vk = key0 + 8 * g;                  // this lane's 8 keys
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-        u32x4 vb = f.v[dt];
-        if (vk + 8 > vlive_to) {                  // keys at or past vlive_to: zero operand
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint32_t w = vb[j];
-                if (vk + 2 * j >= vlive_to) w &= 0xffff0000u;
-                if (vk + 2 * j + 1 >= vlive_to) w &= 0x0000ffffu;
-                vb[j] = w;
-            }
-        }
-        st.o[dt] = mfma_f16_k32(pa, vb, st.o[dt]);
-    }
-    wave_lds_sync();
-}
-
-// ---------------------------------------------------------------------------
-// Self-attention over the paged KV cache, causal inside the block (or over
-// the whole block, causal = 0). grid = (n * H, ceil(T / 16)), 256 threads.
-template <int HD>
-__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
-    constexpr int NDT = HD / 16;
-    constexpr int PW = HD + 2;
-    __shared__ __attribute__((aligned(16))) uint16_t Pt[4][16 * 32];
-    __shared__ float mbuf[2][16 * PW];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int r16 = lane & 15, g = lane >> 4;
-    const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
-    const int row0 = blockIdx.y * 16;
-    const int ntok = a.req_ntok[b];
-
-    if (ntok == 0 || row0 >= ntok) {
-        // skipped request or a tile of padding rows: zeros
-        for (int idx = tid; idx < 16 * HD; idx += 256) {
-            const int rr = idx / HD, c = idx - rr * HD;
-            const int row = row0 + rr;
-            if (row < a.T) store_act(a.out, b * a.T + row, h * HD + c, a.d, 0.f);
-        }
-        return;
-    }
-    const int L = a.req_L[b];
-    // last key any row of this tile may see (the whole block when not causal)
-    const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
-    int lim[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) lim[r] = a.causal ? L + min(row0 + 4 * g + r, ntok - 1) : kmax;
-    const int last_page = kmax >> 4;   // pages past this one were never validated
-    // the request's page ids, one per lane (at most 64 pages)
-    const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
-    const int ptl = lane <= last_page ? pt[lane] : 0;
-    const int qrow = row0 + r16;
-    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
-
-    const uint16_t *kvl = a.kv_layer;
-    const size_t vt_off = (size_t)a.H * 16 * HD;
-    auto load = [&](int j, KVStep<HD> &f) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const int page = __shfl(ptl, min(2 * j + t, last_page));
-            const uint16_t *krow = kvl + (size_t)page * a.page_elems + ((size_t)h * 16 + r16) * HD;
-            if constexpr (HD == 64) {
-                f.k[t][0] = ld16(krow + 8 * g);
-                f.k[t][1] = ld16(krow + 32 + 8 * g);
-            } else {
-                f.k16[t] = ld8(krow + 4 * g);
-            }
-        }
-        const int vkey = 32 * j + 8 * g;
-        const int vpage = __shfl(ptl, min(vkey >> 4, last_page));
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-            f.v[dt] = ld16(kvl + (size_t)vpage * a.page_elems + vt_off +
-                           ((size_t)h * HD + dt * 16 + r16) * 16 + (vkey & 15));
-    };
-    auto live = [&](int r, int key) { return key <= lim[r]; };
-
-    SmState<NDT> st;
-    st.init();
-    const int nsteps = (kmax >> 5) + 1;             // absolute 32-key steps
-    KVStep<HD> cur, nxt;
-    if (wave < nsteps) load(wave, cur);
-    for (int j = wave; j < nsteps; j += 4) {
-        load(min(j + 4, nsteps - 1), nxt);        // unconditional: exact wait counts
-        attend_step<HD>(q, cur, 32 * j, kmax + 1, a.scale, st, Pt[wave], g, r16, live);
-        cur = nxt;
-    }
-    merge_waves<HD>(st, mbuf, wave, g, r16);
-    if (wave == 0) {
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 4 * g + r;
-                if (row < a.T)
-                    store_act(a.out, b * a.T + row, h * HD + dt * 16 + r16, a.d,
-                                st.o[dt][r] / st.l[r]);
-            }
-    }
-}
 
 // ---------------------------------------------------------------------------
 // Transposed online softmax (cross-attention): the running state of query row
@@ -324,15 +87,16 @@ struct SmRow {
     }
 };
 
-// One 32-frame step (frames key0 .. key0 + 31). Scores stay unscaled: the
+// One 32-key step (keys key0 .. key0 + 31). Scores stay unscaled: the
 // running max m is in raw score units and every weight is
-// 2^((s - m) * sl2e), sl2e = scale * log2(e). MASK (the chunk's tail step):
-// frames >= live_to get weight 0 and a zero V operand; other steps skip the
-// masking and the -inf guards (their scores are finite).
+// 2^((s - m) * sl2e), sl2e = scale * log2(e). MASK (a step some row cannot
+// see whole): keys >= live_to (this lane's row) get weight 0 and keys >=
+// vlive_to (past the data) a zero V operand; other steps skip the masking
+// and the -inf guards (their scores are finite).
 template <int HD, bool MASK>
 __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
-                                              int live_to, float sl2e, SmRow<HD / 16> &st,
-                                              int g) {
+                                              int live_to, int vlive_to, float sl2e,
+                                              SmRow<HD / 16> &st, int g) {
     constexpr int NDT = HD / 16;
     f32x4 s[2];
 #pragma unroll
@@ -380,7 +144,7 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
             const int fr = key0 + (w < 2 ? 4 * g + 2 * w : 16 + 4 * g + 2 * (w - 2));
-            vm[w] = (fr < live_to ? 0x0000ffffu : 0u) | (fr + 1 < live_to ? 0xffff0000u : 0u);
+            vm[w] = (fr < vlive_to ? 0x0000ffffu : 0u) | (fr + 1 < vlive_to ? 0xffff0000u : 0u);
         }
     }
 #pragma unroll
@@ -428,6 +192,92 @@ __device__ __forceinline__ void merge_waves_t(SmRow<NDT> &s, float (*mbuf)[16 * 
     if (wave == 2) put_row<HD>(mbuf[0], s, g, r16);
     __syncthreads();
     if (wave == 0) merge_row<HD>(s, mbuf[0], sl2e, g, r16);
+}
+
+// ---------------------------------------------------------------------------
+// Self-attention over the paged KV cache, causal inside the block (or over
+// the whole block, causal = 0). grid = (n * H, ceil(T / 16)), 256 threads.
+template <int HD>
+__global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
+    constexpr int NDT = HD / 16;
+    __shared__ __attribute__((aligned(16))) float mbuf[2][16 * (HD + 4)];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int b = blockIdx.x / a.H, h = blockIdx.x - (blockIdx.x / a.H) * a.H;
+    const int row0 = blockIdx.y * 16;
+    const int ntok = a.req_ntok[b];
+
+    if (ntok == 0 || row0 >= ntok) {
+        // skipped request or a tile of padding rows: zeros
+        for (int idx = tid; idx < 16 * HD; idx += 256) {
+            const int rr = idx / HD, c = idx - rr * HD;
+            const int row = row0 + rr;
+            if (row < a.T) store_act(a.out, b * a.T + row, h * HD + c, a.d, 0.f);
+        }
+        return;
+    }
+    const int L = a.req_L[b];
+    // last key any row of this tile may see (the whole block when not causal)
+    const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
+    // this lane's row r16 sees keys <= lim; keys below mask_from every row sees
+    const int lim = a.causal ? L + min(row0 + r16, ntok - 1) : kmax;
+    const int mask_from = (a.causal ? L + min(row0, ntok - 1) : kmax) + 1;
+    const int last_page = kmax >> 4;   // pages past this one were never validated
+    // the request's page ids, one per lane (at most 64 pages)
+    const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
+    const int ptl = lane <= last_page ? pt[lane] : 0;
+    const int qrow = row0 + r16;
+    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
+
+    const uint16_t *kvl = a.kv_layer;
+    const size_t vt_off = (size_t)a.H * 16 * HD;
+    // step j: keys 32j .. 32j+31 on pages 2j, 2j+1. K tile t as the A operand
+    // of S^T = K Q^T; V^T as the A operand of O^T += V^T P^T, positions
+    // 4g..4g+3 of each page (the order the score tiles leave P in)
+    auto load = [&](int j, KVStep<HD> &f) {
+        int page[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            page[t] = __shfl(ptl, min(2 * j + t, last_page));
+            const uint16_t *krow = kvl + (size_t)page[t] * a.page_elems + ((size_t)h * 16 + r16) * HD;
+            if constexpr (HD == 64) {
+                f.k[t][0] = ld16(krow + 8 * g);
+                f.k[t][1] = ld16(krow + 32 + 8 * g);
+            } else {
+                f.k16[t] = ld8(krow + 4 * g);
+            }
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const size_t dim_off = vt_off + ((size_t)h * HD + dt * 16 + r16) * 16 + 4 * g;
+            const u32x2 lo = ld8(kvl + (size_t)page[0] * a.page_elems + dim_off);
+            const u32x2 hi = ld8(kvl + (size_t)page[1] * a.page_elems + dim_off);
+            f.v[dt] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        }
+    };
+
+    SmRow<NDT> st;
+    st.init();
+    const float sl2e = a.scale * 1.4426950408889634f;
+    const int nsteps = (kmax >> 5) + 1;             // absolute 32-key steps
+    KVStep<HD> cur, nxt;
+    if (wave < nsteps) load(wave, cur);
+    for (int j = wave; j < nsteps; j += 4) {
+        load(min(j + 4, nsteps - 1), nxt);        // unconditional: exact wait counts
+        const int key0 = 32 * j;
+        if (key0 + 32 > mask_from) attend_step_t<HD, true>(q, cur, key0, lim + 1, kmax + 1, sl2e, st, g);
+        else attend_step_t<HD, false>(q, cur, key0, lim + 1, kmax + 1, sl2e, st, g);
+        cur = nxt;
+    }
+    merge_waves_t<HD>(st, mbuf, sl2e, wave, g, r16);
+    if (wave == 0 && qrow < a.T) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                store_act(a.out, b * a.T + qrow, h * HD + dt * 16 + 4 * g + r, a.d,
+                          st.o[dt][r] / st.l);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -493,8 +343,8 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
 #pragma unroll
         for (int i = 0; i < kXaRing; ++i) {
             const int key0 = c0 + 32 * (s0 + i);
-            if (key0 + 32 > c1) attend_step_t<HD, true>(q, f[i], key0, c1, sl2e, st, g);
-            else attend_step_t<HD, false>(q, f[i], key0, c1, sl2e, st, g);
+            if (key0 + 32 > c1) attend_step_t<HD, true>(q, f[i], key0, c1, c1, sl2e, st, g);
+            else attend_step_t<HD, false>(q, f[i], key0, c1, c1, sl2e, st, g);
             __builtin_amdgcn_sched_barrier(0);
             load(min(s0 + i + kXaRing, a.spw - 1), f[i]);
             __builtin_amdgcn_sched_barrier(0);
