@@ -20,6 +20,7 @@ def margins(logits: np.ndarray) -> np.ndarray:
 
 def assert_logits_close(gpu: np.ndarray, ref: np.ndarray, tol: float = LOGIT_TOL, what=""):
     err = float(np.abs(gpu.astype(np.float64) - ref).max())
+    print(f"[parity] {what}: max |logit error| {err:.3e}", flush=True)
     assert err <= tol, f"{what}: max |logit error| {err:.3e} > {tol}"
     return err
 
