@@ -274,13 +274,14 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     if (e->tall_gemm && M >= kTallMinRows && M <= kTallMaxRows && gemm_tl_built(role, S, ck) &&
         !fuse_ln) {
         // tall blocks (tens of requests), 64-column tiles (from a sweep on
-        // MI355X): the wide projections (QKV, fc1) 96 or 128 rows over the
-        // whole of K; the d-wide ones (O, O_c, cross Q) 96 rows
+        // MI355X): the wide projections (QKV, fc1, the LM head, the
+        // drafter's QKV and history K/V) 96 or 128 rows over the whole of K; the d-wide ones (O, O_c, cross Q) 96 rows
         // from 576 rows on (below, the register-tiled kernel's 64 x 32 tiles
         // win); fc2 (K = 5120) 96 rows in 4 K groups
         int mbt = 6, P = 1;
         bool take = true;
-        if (role == ROLE_QKV || role == ROLE_FC1) {
+        if (role == ROLE_QKV || role == ROLE_FC1 || role == ROLE_LM_HEAD ||
+            role == ROLE_DRAFT_QKV || role == ROLE_HIST_KV) {
             // 96 or 128 rows: the fewer rounds of 256 workgroups times the
             // rows per workgroup (measured: 864 x 3840 128 rows 31.9 vs 39.5 us,
             // 864 x 5120 96 rows 43.2 vs 45.3 us)

@@ -229,57 +229,44 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
     }
 
     if constexpr (EPI == EPI_ARGMAX) {
-        // per row and 64-column sub-tile: (max, lowest index); a sub-tile is
-        // covered by 4 / NW waves, merged in wave order
-        __shared__ float smax[4][BM];
-        __shared__ int sidx[4][BM], snan[4][BM];
+        // per row and 64-column tile: (max, lowest index), NaN flagged. The
+        // workgroup's BM x 64 scores go to LDS; two threads per row scan 32
+        // columns each in column order and merge.
+        static_assert(NW == 1, "one 64-column tile per workgroup");
+        __shared__ float sv[BM][65];
         const EpiArgs &e = a.e;
+        const int n = n_wave + r16;
 #pragma unroll
         for (int mt = 0; mt < MB; ++mt) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = mt * 16 + 4 * g + r;
-                const int m = m_base + row;
-                float bv = -INFINITY;
-                int bi = 0x7fffffff, nn = 0;
-#pragma unroll
-                for (int nt = 0; nt < NW; ++nt) {
-                    const int n = n_wave + nt * 16 + r16;
-                    if (n >= a.N) continue;
-                    const float x = total[mt * NW + nt][r];
-                    if (e.logits && m < a.M) e.logits[(size_t)m * a.N + n] = x;
-                    if (x != x) nn = 1;
-                    else argmax_merge(bv, bi, x, n);
-                }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    const float v2 = __shfl_xor(bv, o);
-                    const int i2 = __shfl_xor(bi, o);
-                    argmax_merge(bv, bi, v2, i2);
-                    nn |= __shfl_xor(nn, o);
-                }
-                if (r16 == 0) {
-                    smax[wave][row] = bv;
-                    sidx[wave][row] = bi;
-                    snan[wave][row] = nn;
-                }
+                const float x = total[mt][r];
+                sv[row][wave * 16 + r16] = x;
+                if (e.logits && m_base + row < a.M && n < a.N) e.logits[(size_t)(m_base + row) * a.N + n] = x;
             }
         }
         __syncthreads();
-        constexpr int WPS = 4 / NW;                    // waves per 64-column sub-tile
-        for (int idx = tid; idx < NW * BM; idx += 256) {
-            const int sub = idx / BM, row = idx - sub * BM;
-            const int m = m_base + row;
-            const int t64 = ntile * NW + sub;
-            if (m >= a.M || t64 * 64 >= a.N) continue;
-            float bv = smax[sub * WPS][row];
-            int bi = sidx[sub * WPS][row], nn = snan[sub * WPS][row];
-            for (int w = 1; w < WPS; ++w) {
-                argmax_merge(bv, bi, smax[sub * WPS + w][row], sidx[sub * WPS + w][row]);
-                nn |= snan[sub * WPS + w][row];
+        if (tid < 2 * BM) {                       // whole waves: BM is a multiple of 32
+            const int row = tid >> 1, half = tid & 1;
+            float bv = -INFINITY;
+            int bi = 0x7fffffff, nn = 0;
+            for (int c = 0; c < 32; ++c) {
+                const int col = ntile * 64 + half * 32 + c;
+                if (col >= a.N) break;
+                const float x = sv[row][half * 32 + c];
+                if (x != x) nn = 1;
+                else argmax_merge(bv, bi, x, col);
             }
-            e.tile_max[(size_t)m * e.ld + t64] = bv;
-            e.tile_idx[(size_t)m * e.ld + t64] = nn ? -1 : bi;
+            const float v2 = __shfl_xor(bv, 1);
+            const int i2 = __shfl_xor(bi, 1);
+            nn |= __shfl_xor(nn, 1);
+            argmax_merge(bv, bi, v2, i2);
+            const int m = m_base + row;
+            if (half == 0 && m < a.M) {
+                e.tile_max[(size_t)m * e.ld + ntile] = bv;
+                e.tile_idx[(size_t)m * e.ld + ntile] = nn ? -1 : bi;
+            }
         }
     } else {
         int m0[MB];

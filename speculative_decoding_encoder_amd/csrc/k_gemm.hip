@@ -307,18 +307,22 @@ hipError_t launch_gemm_rk_c(int role, const GemmArgs &a, int mb, int nb, hipStre
 
 hipError_t launch_gemm_tl_a(int role, const GemmArgs &a, int mb, hipStream_t st);
 hipError_t launch_gemm_tl_b(int role, const GemmArgs &a, int mb, hipStream_t st);
+hipError_t launch_gemm_tl_c(int role, const GemmArgs &a, int mb, hipStream_t st);
 
 hipError_t launch_gemm_tl(int role, const GemmArgs &a, int mb, hipStream_t st) {
     switch (role) {
         case ROLE_QKV: case ROLE_OPROJ: case ROLE_CROSS_Q: return launch_gemm_tl_a(role, a, mb, st);
         case ROLE_FC1: case ROLE_FC2: return launch_gemm_tl_b(role, a, mb, st);
+        case ROLE_LM_HEAD: case ROLE_DRAFT_QKV: case ROLE_HIST_KV:
+            return launch_gemm_tl_c(role, a, mb, st);
     }
     return hipErrorInvalidValue;
 }
 
 bool gemm_tl_built(int role, int S, int ck) {
     if (S != 8) return false;
-    if (role == ROLE_QKV || role == ROLE_FC1 || role == ROLE_OPROJ || role == ROLE_CROSS_Q)
+    if (role == ROLE_QKV || role == ROLE_FC1 || role == ROLE_OPROJ || role == ROLE_CROSS_Q ||
+        role == ROLE_LM_HEAD || role == ROLE_DRAFT_QKV || role == ROLE_HIST_KV)
         return ck == 5;
     return role == ROLE_FC2 && ck == 20;
 }
