@@ -217,13 +217,7 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
                     if (x != x) nn = 1;
                     else argmax_merge(bv, bi, x, n);
                 }
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    const float v2 = __shfl_xor(bv, o);
-                    const int i2 = __shfl_xor(bi, o);
-                    argmax_merge(bv, bi, v2, i2);
-                    nn |= __shfl_xor(nn, o);
-                }
+                argmax16(bv, bi, nn);
                 if (r16 == 0 && m < a.M) {
                     e.tile_max[(size_t)m * e.ld + ntile] = bv;
                     e.tile_idx[(size_t)m * e.ld + ntile] = nn ? -1 : bi;

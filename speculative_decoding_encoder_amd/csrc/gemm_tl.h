@@ -258,10 +258,8 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
                 if (x != x) nn = 1;
                 else argmax_merge(bv, bi, x, col);
             }
-            const float v2 = __shfl_xor(bv, 1);
-            const int i2 = __shfl_xor(bi, 1);
-            nn |= __shfl_xor(nn, 1);
-            argmax_merge(bv, bi, v2, i2);
+            argmax_bfly16<0>(bv, bi);                 // the lane pair (xor 1)
+            nn |= bfly16<0>(nn);
             const int m = m_base + row;
             if (half == 0 && m < a.M) {
                 e.tile_max[(size_t)m * e.ld + ntile] = bv;

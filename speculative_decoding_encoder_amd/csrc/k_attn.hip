@@ -116,8 +116,12 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
     }
     float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                      fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-    tm = fmaxf(tm, __shfl_xor(tm, 16));
-    tm = fmaxf(tm, __shfl_xor(tm, 32));
+    {
+        float a, b;
+        rows16_pair(tm, a, b);
+        halves32_pair(fmaxf(a, b), a, b);
+        tm = fmaxf(a, b);
+    }
     const float mnew = fmaxf(st.m, tm);
     const float ms = mnew * sl2e;
     // unmasked steps: mnew is finite, and st.m = -inf (first step) gives 0
@@ -132,8 +136,12 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
                                                       : __builtin_amdgcn_exp2f(__fmaf_rn(s[t][r], sl2e, -ms));
     float ls = ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
                ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-    ls += __shfl_xor(ls, 16);                 // a + b = b + a: the four lanes agree
-    ls += __shfl_xor(ls, 32);
+    {
+        float a, b;                           // the four lanes of a row agree
+        rows16_pair(ls, a, b);
+        halves32_pair(a + b, a, b);
+        ls = a + b;
+    }
     st.l = alpha * st.l + ls;
     st.m = mnew;
     const u32x4 pb = {pack_h2(p[0][0], p[0][1]), pack_h2(p[0][2], p[0][3]),

@@ -215,13 +215,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
                 float bv = (ok && !isn) ? v : -INFINITY;
                 int bi = ok ? n_out : 0x7fffffff;
                 int nn = isn ? 1 : 0;
-#pragma unroll
-                for (int o = 1; o < 16; o <<= 1) {
-                    float v2 = __shfl_xor(bv, o);
-                    int i2 = __shfl_xor(bi, o);
-                    argmax_merge(bv, bi, v2, i2);
-                    nn |= __shfl_xor(nn, o);
-                }
+                argmax16(bv, bi, nn);
                 if (r16 == 0) {
                     smax[wave][row] = bv;
                     sidx[wave][row] = bi;

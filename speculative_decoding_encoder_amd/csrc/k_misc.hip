@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void lm_reduce_kernel(LmReduceArgs a) {
         else argmax_merge(v, idx, tv, ti);
     }
     wave_argmax(v, idx);
-    for (int o = 1; o < 64; o <<= 1) nan |= __shfl_xor(nan, o);
+    nan = wave_or(nan);
     if (lane == 0) {
         sv[wave] = v;
         si[wave] = idx;

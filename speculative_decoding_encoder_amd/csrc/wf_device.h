@@ -108,40 +108,130 @@ __device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 w) {
     return r;
 }
 
-// Reductions within groups of 16 lanes (lanes 16g .. 16g+15), fixed tree.
+// Cross-lane exchange without LDS. Within a row of 16 lanes, DPP: level 0
+// and 1 of a butterfly read the xor-1 / xor-2 partner (quad_perm); levels 2
+// and 3 read the mirrored lane within 8 / 16 lanes (row_half_mirror /
+// row_mirror), which holds the xor-4 / xor-8 partner's value because a
+// butterfly has made every quad / every 8 lanes agree by then. Across rows
+// (gfx950 permlane swaps of a register with itself): the two halves of the
+// result hold the values of the xor-16 (xor-32) partners in the same order in
+// every lane, so a symmetric operation on them gives one result for both.
+template <int S>
+__device__ __forceinline__ uint32_t bfly16_u(uint32_t v) {
+    constexpr int C = S == 0 ? 0xB1 : (S == 1 ? 0x4E : (S == 2 ? 0x141 : 0x140));
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, C, 0xf, 0xf, false);
+}
+template <int S>
+__device__ __forceinline__ float bfly16(float v) { return __uint_as_float(bfly16_u<S>(__float_as_uint(v))); }
+template <int S>
+__device__ __forceinline__ int bfly16(int v) { return (int)bfly16_u<S>((uint32_t)v); }
+__device__ __forceinline__ void rows16_pair(float v, float &a, float &b) {
+    const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void halves32_pair(float v, float &a, float &b) {
+    const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    a = __uint_as_float(p[0]);
+    b = __uint_as_float(p[1]);
+}
+__device__ __forceinline__ void rows16_pair(int v, int &a, int &b) {
+    const auto p = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+    a = (int)p[0];
+    b = (int)p[1];
+}
+__device__ __forceinline__ void halves32_pair(int v, int &a, int &b) {
+    const auto p = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+    a = (int)p[0];
+    b = (int)p[1];
+}
+
+// Reductions within groups of 16 lanes (lanes 16g .. 16g+15), fixed
+// butterfly; every lane of the group gets the same bits.
 __device__ __forceinline__ float max16(float v) {
-    v = fmaxf(v, __shfl_xor(v, 1));
-    v = fmaxf(v, __shfl_xor(v, 2));
-    v = fmaxf(v, __shfl_xor(v, 4));
-    v = fmaxf(v, __shfl_xor(v, 8));
+    v = fmaxf(v, bfly16<0>(v));
+    v = fmaxf(v, bfly16<1>(v));
+    v = fmaxf(v, bfly16<2>(v));
+    v = fmaxf(v, bfly16<3>(v));
     return v;
 }
 __device__ __forceinline__ float sum16(float v) {
-    v += __shfl_xor(v, 1);
-    v += __shfl_xor(v, 2);
-    v += __shfl_xor(v, 4);
-    v += __shfl_xor(v, 8);
+    v += bfly16<0>(v);
+    v += bfly16<1>(v);
+    v += bfly16<2>(v);
+    v += bfly16<3>(v);
     return v;
 }
-// Whole-wave reductions, fixed tree.
+// Whole-wave reductions, fixed tree (the 16-lane butterfly, then the row
+// pairs, then the halves).
 __device__ __forceinline__ float wave_sum(float v) {
-    for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o);
-    return v;
+    v = sum16(v);
+    float a, b;
+    rows16_pair(v, a, b);
+    v = a + b;
+    halves32_pair(v, a, b);
+    return a + b;
 }
 __device__ __forceinline__ float wave_max(float v) {
-    for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    v = max16(v);
+    float a, b;
+    rows16_pair(v, a, b);
+    v = fmaxf(a, b);
+    halves32_pair(v, a, b);
+    return fmaxf(a, b);
 }
-// (value, index) argmax: larger value wins, equal values go to the lower index.
+__device__ __forceinline__ int wave_or(int v) {
+    v |= bfly16<0>(v);
+    v |= bfly16<1>(v);
+    v |= bfly16<2>(v);
+    v |= bfly16<3>(v);
+    int a, b;
+    rows16_pair(v, a, b);
+    v = a | b;
+    halves32_pair(v, a, b);
+    return a | b;
+}
+// (value, index) argmax: larger value wins, equal values go to the lower
+// index (symmetric: the merge of two candidates does not depend on order).
 __device__ __forceinline__ void argmax_merge(float &v, int &i, float v2, int i2) {
     if (v2 > v || (v2 == v && i2 < i)) { v = v2; i = i2; }
 }
+template <int S>
+__device__ __forceinline__ void argmax_bfly16(float &v, int &i) {
+    const float v2 = bfly16<S>(v);
+    const int i2 = bfly16<S>(i);
+    argmax_merge(v, i, v2, i2);
+}
+// argmax over the 16 lanes of each group; nan: OR over the group
+__device__ __forceinline__ void argmax16(float &v, int &i, int &nan) {
+    argmax_bfly16<0>(v, i);
+    argmax_bfly16<1>(v, i);
+    argmax_bfly16<2>(v, i);
+    argmax_bfly16<3>(v, i);
+    nan |= bfly16<0>(nan);
+    nan |= bfly16<1>(nan);
+    nan |= bfly16<2>(nan);
+    nan |= bfly16<3>(nan);
+}
 __device__ __forceinline__ void wave_argmax(float &v, int &i) {
-    for (int o = 1; o < 64; o <<= 1) {
-        float v2 = __shfl_xor(v, o);
-        int i2 = __shfl_xor(i, o);
-        argmax_merge(v, i, v2, i2);
-    }
+    argmax_bfly16<0>(v, i);
+    argmax_bfly16<1>(v, i);
+    argmax_bfly16<2>(v, i);
+    argmax_bfly16<3>(v, i);
+    float va, vb;
+    int ia, ib;
+    rows16_pair(v, va, vb);
+    rows16_pair(i, ia, ib);
+    v = va;
+    i = ia;
+    argmax_merge(v, i, vb, ib);
+    halves32_pair(v, va, vb);
+    halves32_pair(i, ia, ib);
+    v = va;
+    i = ia;
+    argmax_merge(v, i, vb, ib);
 }
 
 // Handoff of partial results between workgroups (possibly on different
