@@ -3,7 +3,8 @@
 Covers: the tiny 2-layer model (several tiles, ragged tails, head_dim 16),
 the full 32-layer large-v3 shape at batch 1 with a 64-token prefix and a
 block of K+1 = 9, the 4-layer turbo shape at batch 32 with ragged prefixes
-and a shuffled page table, row invariance (a row gives the same bits alone
+and a shuffled page table, a block that ends at the last context position
+beside an inactive and a ragged request, row invariance (a row gives the same bits alone
 or inside a block; speculative = greedy on the GPU), and the device error
 words.
 """
@@ -349,6 +350,60 @@ def test_turbo_b32_ragged_shuffled_pages(torch_cuda):
     err, ln = eng.wf_device_state()
     assert (err == 0).all()
     log("turbo b32: parity on sampled requests ok")
+    eng.close()
+
+
+def test_turbo_full_context_inactive_and_ragged(torch_cuda):
+    """Edge cases at full width (4-layer turbo shape, 3 requests): request 0
+    fills the context (a prefill of n_ctx - 9 = 439 rows in one call, then a
+    block of 9 at positions 439..447 = n_ctx - 1); request 1 is inactive in
+    the block call (n_tok = 0: its rows give -1 and its cache keeps its
+    length); request 2 has a ragged block (n_tok = 6 of T = 9: rows 6..8
+    give -1). The 3 x 439-row prefill also takes the LDS-staged GEMM (more
+    than 1024 rows)."""
+    wl = WORKLOADS[2]
+    shape = TURBO
+    B = 3
+    wbits = make_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, 40 + r) for r in range(B)])
+    rng = np.random.default_rng(11)
+    lens = np.array([shape.n_ctx - 9, 5, 100], np.int32)
+    T = int(lens.max())
+    toks = rng.integers(0, shape.vocab - 1, (B, T)).astype(np.int32)
+    eng = _engine(shape, wbits, max_batch=B, max_rows=B * T)
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    log("turbo full context: GPU prefill of 3 x 439 rows")
+    am, lg = _verify(eng, slots, toks, lens)
+    eng.wf_rollback(eng.i32(slots), eng.i32(lens - 1))
+    m = om.Model(shape, wbits)
+    reqs = []
+    for b in range(B):
+        req = m.new_request(encs[b])
+        ref = m.rows(req, toks[b, :lens[b]], 0)
+        assert_logits_close(lg[b, :lens[b]], ref, what=f"full-context prefill req {b}")
+        assert_argmax_where_clear(am[b, :lens[b]], ref, what=f"full-context prefill req {b}")
+        assert (am[b, lens[b]:] == -1).all()
+        reqs.append(req)
+    del lg
+    blocks = rng.integers(0, shape.vocab - 1, (B, 9)).astype(np.int32)
+    blocks[:, 0] = [am[b, lens[b] - 1] for b in range(B)]
+    n_tok = np.array([9, 0, 6], np.int32)
+    am2, lg2 = _verify(eng, slots, blocks, n_tok)
+    ref0 = m.rows(reqs[0], blocks[0], int(lens[0]))
+    assert_logits_close(lg2[0], ref0, what="block at positions 439..447")
+    assert_argmax_where_clear(am2[0], ref0, what="block at positions 439..447")
+    ref2 = m.rows(reqs[2], blocks[2, :6], int(lens[2]))
+    assert_logits_close(lg2[2, :6], ref2, what="ragged block (6 of 9)")
+    assert_argmax_where_clear(am2[2, :6], ref2, what="ragged block (6 of 9)")
+    assert (am2[1] == -1).all() and (am2[2, 6:] == -1).all()
+    err, ln = eng.wf_device_state()
+    assert (err == 0).all() and ln[1] == lens[1]
+    eng.wf_rollback(eng.i32(slots), eng.i32(n_tok.clip(min=1) - 1))
+    err, ln = eng.wf_device_state()
+    assert (err == 0).all()
+    assert list(ln[:B]) == [shape.n_ctx, lens[1], lens[2] + 6]
+    log("turbo full context: ok")
     eng.close()
 
 
