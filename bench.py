@@ -65,7 +65,7 @@ def log(*a):
 
 
 class Workload:
-    def __init__(self, cfg_id: int, greedy: bool = False):
+    def __init__(self, cfg_id: int, greedy: bool = False, k: int = 0, batch: int = 0):
         from synthetic import (DRAFTER_TAPS, WORKLOADS, make_draft_table, make_drafter_weights,
                                make_encoder_out, make_prefixes, make_weights, rng)
         from speculative_decoding_encoder_amd.binding import Engine
@@ -74,8 +74,8 @@ class Workload:
         self.torch = torch
         self.wl = wl = WORKLOADS[cfg_id]
         self.shape = s = wl.shape
-        self.B = B = wl.batch
-        self.K = wl.k_draft
+        self.B = B = batch or wl.batch
+        self.K = k or wl.k_draft
         self.sampling = cfg_id == 4 and not greedy
         self.temperature = wl.temperature if self.sampling else 0.0
         self.name = wl.name if (cfg_id != 4 or self.sampling) else "large-v3-verify-b32-greedy"
@@ -84,7 +84,7 @@ class Workload:
         self.drafter = wl.drafter_layers > 0
         self.dbits = make_drafter_weights(s, wl.cfg_id, wl.drafter_layers) if self.drafter else None
         self.encs = np.stack([make_encoder_out(s, wl.cfg_id, r) for r in range(B)])
-        self.prefixes = make_prefixes(wl)
+        self.prefixes = make_prefixes(wl, B)
         self.P = np.array([len(p) for p in self.prefixes], np.int32)
         log(f"[bench] inputs generated in {time.time() - t0:.1f}s")
         max_rows = max(B * (self.K + 1), B * int(self.P.max()))
@@ -439,6 +439,30 @@ def summary(w: "Workload", r: dict) -> dict:
 EXTRA = {"32": (4, True), "96": (3, False)}   # batch -> (config, greedy)
 
 
+def k_sweep(args):
+    """Step time at each K of --k-sweep on one workload (same prompts, weights and
+    draft tables; a fresh engine per K). The pages find the verify pass nearly flat
+    in K (a few candidates cost little more than one); this measures that here."""
+    import torch
+    rows = {}
+    name = None
+    for k in [int(v) for v in args.k_sweep.split(",") if v]:
+        w = Workload(args.config, greedy=args.greedy, k=k, batch=args.batch)
+        r = measure(w, args.steps, args.warmup, use_graph=not args.no_graph)
+        name = w.name
+        rows[str(k)] = {"ms_per_step": round(r["ms_step"], 4),
+                        "tokens_per_step": r["tokens_per_step"],
+                        "tokens_per_s": round(r["value"], 2),
+                        "verify_rows": w.B * (k + 1)}
+        log(f"[bench] K = {k}: {r['ms_step']:.3f} ms/step")
+        w.eng.close()
+        del w, r
+        torch.cuda.empty_cache()
+    print(json.dumps({"k_sweep": rows, "workload": name, "batch": args.batch or None,
+                      "steps": args.steps,
+                      "warmup": args.warmup, "graph": not args.no_graph}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -452,6 +476,12 @@ def main():
     ap.add_argument("--batches", default="32,96",
                     help="also measure these batch sizes (32: large-v3 greedy verify, 96: "
                          "large-v3 with the parallel drafter); empty for none")
+    ap.add_argument("--k-sweep", default="",
+                    help="comma-separated K values: time the step of --config at each K "
+                         "(the pass cost against the number of candidates) and print that "
+                         "as the one JSON line instead")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="with --k-sweep: this many requests instead of the workload's")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run device-to-device copies of this size (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
@@ -464,6 +494,9 @@ def main():
     import torch
     torch.cuda.set_device(0)
     K, W = args.steps, args.warmup
+    if args.k_sweep:
+        k_sweep(args)
+        return
     w = Workload(args.config, greedy=args.greedy)
     r = measure(w, K, W, use_graph=not args.no_graph)
     kinds, dom = r["kinds"], r["dom"]

@@ -318,6 +318,15 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
             mb = 1;
             nb = (role == ROLE_LM_HEAD || (fuse_ln && N >= 4096)) ? 4 : 1;
             if (split_k_ok && S >= 2 && cdiv(N, 16 * nb) < 128 && fits(2)) P = 2;
+        } else if (mt_need <= 8) {
+            // a few requests (2 to 8 row tiles): one-row-tile blocks of 16
+            // columns up to 3 row tiles, then 32 x 32 tiles in 2 K groups
+            // (from a sweep of verify steps at 18 / 36 / 72 rows on MI355X:
+            // 2.42 / 2.60 / 3.17 ms against 3.47 / 3.26 / 3.61 with the taller
+            // tiles below)
+            mb = mt_need <= 3 ? 1 : 2;
+            nb = role == ROLE_LM_HEAD ? 4 : (mt_need <= 3 ? 1 : 2);
+            if (split_k_ok && mt_need > 3 && fits(2)) P = 2;
         } else {
             // the LM head reads the activations once per 64-column tile:
             // 96-row blocks from 6 row tiles on (1.2x faster at 288 rows);
