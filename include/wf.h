@@ -251,6 +251,48 @@ wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
 wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots,
                       const int32_t *d_n_acc, void *stream);
 
+/* Tree verification ("Alignment Drift in Single-Model Speculative Decoding for
+ * ASR", appendix E.3: the target verifies every node of a draft tree in one
+ * pass under a tree attention mask; a one-branch tree reproduces the linear
+ * decoder). As wf_verify_block, with
+ * d_parents int32 [n][T]: parents[b][0] = -1 (node 0 is the anchor, the
+ *   root) and 0 <= parents[b][i] < i for the other nodes i < n_tok[b]
+ *   (entries at or beyond n_tok are ignored).
+ * Node i sits at position L + depth(i), attends to cache positions 0..L-1
+ * and to its ancestors and itself among the nodes, and its K/V are written
+ * at cache slot L + i until wf_rollback_tree. Its argmax row is the target's
+ * choice after the node's root-to-node path. A bad parent array sets
+ * WF_DERR_TOKEN. Requires 1 <= T <= 64 and an engine without a drafter
+ * (WF_ESTATE: the tree does not feed the drafter's history). */
+wf_status wf_verify_tree(wf_engine *e, int32_t n, const int32_t *d_slots,
+                         const int32_t *d_tokens, int32_t T, const int32_t *d_parents,
+                         const int32_t *d_n_tok, int32_t *d_argmax, float *d_logits,
+                         void *stream);
+
+/* Greedy acceptance on a tree after wf_verify_tree. A node is accepted when
+ * its parent is (the root always is), the parent is not an accepted EOS, and
+ * its token equals the target's argmax at the parent. The kept path ends at
+ * the deepest accepted node no deeper than R - 1 (R = d_budget[b] output
+ * tokens left; the lowest node index among equally deep ones), and a is its
+ * depth. Then, as in wf_accept: an accepted EOS ends the request with no
+ * bonus; otherwise the argmax at that node is emitted and is the next anchor.
+ * Outputs: d_path int32 [n][T], the kept nodes root first (entries past a
+ * are -1), and d_n_acc, d_next_token, d_n_emit, d_done as in wf_accept.
+ * Requires 1 <= T <= 64. */
+wf_status wf_accept_tree(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
+                         const int32_t *d_parents, const int32_t *d_n_tok,
+                         const int32_t *d_budget, const int32_t *d_argmax, int32_t *d_path,
+                         int32_t *d_n_acc, int32_t *d_next_token, int32_t *d_n_emit,
+                         int32_t *d_done, void *stream);
+
+/* Rollback of a tree verify: in every layer the K/V of path node k (slot
+ * L + path[k]) move to position L + k for k = 1..a, then the slot keeps
+ * L + 1 + a positions as after wf_rollback. d_path int32 [n][T] as written by
+ * wf_accept_tree. A path that is not one of this verify's nodes (path[k]
+ * outside [k, n_tok)) sets WF_DERR_ACCEPT. Requires 1 <= T <= 64. */
+wf_status wf_rollback_tree(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_path,
+                           int32_t T, const int32_t *d_n_acc, void *stream);
+
 /* Shorten the cache of n slots to d_len[b] positions (0 <= d_len[b] <= the
  * current length; the slot must not be pending), e.g. to verify the same
  * block again from the same state. A bad length sets WF_DERR_STATE. */

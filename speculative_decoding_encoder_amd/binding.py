@@ -88,6 +88,9 @@ def load():
         "wf_accept": (I32, [P, I32, P, I32, P, P, P, P, P, P, ctypes.c_float, ctypes.c_uint64,
                             P, P, P, P, P, P, P]),
         "wf_rollback": (I32, [P, I32, P, P, P]),
+        "wf_verify_tree": (I32, [P, I32, P, P, I32, P, P, P, P, P]),
+        "wf_accept_tree": (I32, [P, I32, P, I32, P, P, P, P, P, P, P, P, P, P]),
+        "wf_rollback_tree": (I32, [P, I32, P, P, I32, P, P]),
         "wf_draft": (I32, [P, I32, P, P, I32, P, P, P]),
         "wf_truncate": (I32, [P, I32, P, P, P]),
         "wf_device_state": (I32, [P, P, P, P]),
@@ -238,6 +241,25 @@ class Engine:
     def wf_rollback(self, slots, n_acc, stream=None):
         _check(self.lib.wf_rollback(self.h, slots.numel(), _p(slots), _p(n_acc),
                                     _stream(stream)), "wf_rollback")
+
+    def wf_verify_tree(self, slots, tokens, parents, n_tok, argmax, logits=None, stream=None):
+        n, T = tokens.shape
+        _check(self.lib.wf_verify_tree(self.h, n, _p(slots), _p(tokens), T, _p(parents),
+                                       _p(n_tok), _p(argmax), _p(logits), _stream(stream)),
+               "wf_verify_tree")
+
+    def wf_accept_tree(self, tokens, parents, n_tok, budget, argmax, path, n_acc, next_token,
+                       n_emit, done, stream=None):
+        n, T = tokens.shape
+        _check(self.lib.wf_accept_tree(self.h, n, _p(tokens), T, _p(parents), _p(n_tok),
+                                       _p(budget), _p(argmax), _p(path), _p(n_acc),
+                                       _p(next_token), _p(n_emit), _p(done), _stream(stream)),
+               "wf_accept_tree")
+
+    def wf_rollback_tree(self, slots, path, n_acc, stream=None):
+        n, T = path.shape
+        _check(self.lib.wf_rollback_tree(self.h, n, _p(slots), _p(path), T, _p(n_acc),
+                                         _stream(stream)), "wf_rollback_tree")
 
     def wf_draft(self, slots, anchor, K, block, logits=None, stream=None):
         _check(self.lib.wf_draft(self.h, slots.numel(), _p(slots), _p(anchor), int(K), _p(block),

@@ -69,7 +69,7 @@ void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
 int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
 
 struct Layout {
-    size_t x, xs, hs, q, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
+    size_t x, xs, hs, q, tdepth, tanc, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
     size_t taps, dam, rowkv;
     size_t total;
     size_t part_bytes, xapart_bytes;
@@ -125,6 +125,8 @@ Layout layout_of(const wf_config *c) {
     // the MLP hidden layer (fp16), or the drafter's fp32 projections [M][3d]
     L.hs = take(Mp * std::max(f * 2, 3 * d * 4));
     L.q = take(M * d * 2);
+    L.tdepth = take(M * 4);   // tree verification: node depths
+    L.tanc = take(M * 8);     // and ancestor masks
     L.part = take(part);
     L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 16) * (cdiv((int)M, 16) + 1) * 4);
     L.xapart = take(xap);
@@ -168,6 +170,8 @@ struct wf_engine {
     char *ws;
     float *x;
     uint16_t *xs, *hs, *q;
+    int32_t *tdepth;                         // tree verification: per row, its node's depth
+    uint64_t *tanc;                          // and ancestor-or-self mask
     float *part;
     int32_t *gcnt;
     float *xapart;
@@ -515,6 +519,8 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->xs = (uint16_t *)(ws + L.xs);
     e->hs = (uint16_t *)(ws + L.hs);
     e->q = (uint16_t *)(ws + L.q);
+    e->tdepth = (int32_t *)(ws + L.tdepth);
+    e->tanc = (uint64_t *)(ws + L.tanc);
     e->part = (float *)(ws + L.part);
     e->gcnt = (int32_t *)(ws + L.gcnt);
     e->xapart = (float *)(ws + L.xapart);
@@ -708,9 +714,11 @@ wf_status run_rope_append(wf_engine *e, int dl, const Pass &p, int ncols, int q_
 
 }  // namespace
 
-wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
-                          const int32_t *d_tokens, int32_t T, const int32_t *d_n_tok,
-                          int32_t *d_argmax, float *d_logits, void *stream) {
+// One verify pass; d_parents (nullable) makes the block a token tree.
+static wf_status verify_pass(wf_engine *e, int32_t n, const int32_t *d_slots,
+                             const int32_t *d_tokens, int32_t T, const int32_t *d_parents,
+                             const int32_t *d_n_tok, int32_t *d_argmax, float *d_logits,
+                             void *stream) {
     if (!e || !d_slots || !d_tokens || !d_n_tok || !d_argmax)
         return fail(WF_EINVAL, "null argument");
     const wf_config &c = e->c;
@@ -723,10 +731,12 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
     cross_plan(e, n, p.mt, p.cf, p.G, p.spw);
 
     PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
-                   d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN};
+                   d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN,
+                   d_parents, e->tdepth, e->tanc};
     WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_prepare(pa, st); }));
     EmbedArgs ema{M,      T,      d,        c.vocab,         c.n_ctx, d_tokens, e->reqL,
-                  e->tok_emb, e->pos_emb, e->x, e->reqN, d_slots, e->pt, e->pt_stride, e->rowkv};
+                  e->tok_emb, e->pos_emb, e->x, e->reqN, d_slots, e->pt, e->pt_stride, e->rowkv,
+                  d_parents ? e->tdepth : nullptr};
     WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_embed(ema, st); }));
 
     for (int l = 0; l < c.n_layers; ++l) {
@@ -751,7 +761,8 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         WF_TRY(run_gemm(e, TK_QKV, ROLE_QKV, e->xs, M, d, w.wq, w.wk, w.wv, d, 3 * d, qa, st,
                         w.ln1_g, w.ln1_b));
         SelfAttnArgs sa{e->q, kvl, e->pt, d_slots, e->reqL, e->reqN, e->pt_stride,
-                        e->page_elems, n, T, H, d, 1, 1.0f / std::sqrt((float)hd), e->xs};
+                        e->page_elems, n, T, H, d, 1, 1.0f / std::sqrt((float)hd), e->xs,
+                        d_parents ? e->tanc : nullptr};
         WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, p.mt, st); }));
         WF_TRY(run_out_cross_mlp(e, w, l, p, st));
         // history taps for the drafter (residual stream after this block)
@@ -782,6 +793,55 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
         }
     }
     return WF_OK;
+}
+
+wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
+                          const int32_t *d_tokens, int32_t T, const int32_t *d_n_tok,
+                          int32_t *d_argmax, float *d_logits, void *stream) {
+    return verify_pass(e, n, d_slots, d_tokens, T, nullptr, d_n_tok, d_argmax, d_logits, stream);
+}
+
+wf_status wf_verify_tree(wf_engine *e, int32_t n, const int32_t *d_slots,
+                         const int32_t *d_tokens, int32_t T, const int32_t *d_parents,
+                         const int32_t *d_n_tok, int32_t *d_argmax, float *d_logits,
+                         void *stream) {
+    if (!e || !d_parents) return fail(WF_EINVAL, "null argument");
+    if (T < 1 || T > 64) return fail(WF_EINVAL, "a tree has 1 to 64 nodes");
+    if (e->c.drafter_layers > 0)
+        return fail(WF_ESTATE, "tree verification does not feed the drafter's history");
+    return verify_pass(e, n, d_slots, d_tokens, T, d_parents, d_n_tok, d_argmax, d_logits,
+                       stream);
+}
+
+wf_status wf_accept_tree(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
+                         const int32_t *d_parents, const int32_t *d_n_tok,
+                         const int32_t *d_budget, const int32_t *d_argmax, int32_t *d_path,
+                         int32_t *d_n_acc, int32_t *d_next_token, int32_t *d_n_emit,
+                         int32_t *d_done, void *stream) {
+    if (!e || !d_tokens || !d_parents || !d_n_tok || !d_budget || !d_argmax || !d_path ||
+        !d_n_acc || !d_next_token || !d_n_emit || !d_done)
+        return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    if (T < 1 || T > 64) return fail(WF_EINVAL, "a tree has 1 to 64 nodes");
+    TreeAcceptArgs a{n, T, e->c.eos_id, d_tokens, d_parents, d_n_tok, d_budget, d_argmax,
+                     d_path, d_n_acc, d_next_token, d_n_emit, d_done};
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_accept_tree(a, st); });
+}
+
+wf_status wf_rollback_tree(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_path,
+                           int32_t T, const int32_t *d_n_acc, void *stream) {
+    if (!e || !d_slots || !d_path || !d_n_acc) return fail(WF_EINVAL, "null argument");
+    if (n < 1 || n > e->c.max_batch) return fail(WF_ECAPACITY, "n outside [1, max_batch]");
+    if (T < 1 || T > 64) return fail(WF_EINVAL, "a tree has 1 to 64 nodes");
+    const wf_config &c = e->c;
+    CompactArgs ca{n, T, c.n_layers, c.n_heads, c.head_dim, c.max_batch, e->pt_stride,
+                   e->page_elems, e->kv_layer_elems, d_slots, d_path, d_n_acc, e->len, e->pend,
+                   e->pt, e->err, e->kv};
+    hipStream_t st = (hipStream_t)stream;
+    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_compact(ca, st); }));
+    RollbackArgs ra{n, c.max_batch, d_slots, d_n_acc, e->len, e->pend, e->err};
+    return timed(e, TK_OTHER, st, [&] { return launch_rollback(ra, st); });
 }
 
 wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_anchor,

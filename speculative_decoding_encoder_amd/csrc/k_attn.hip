@@ -19,6 +19,10 @@
 // Self-attention reads the paged cache: a page holds 16 positions; K is
 // [head][16][hd] and V is stored transposed, [head][hd][16], so that a V^T
 // operand is two 8-byte loads (positions 4g..4g+3 of the step's two pages).
+// Tree verification ("Alignment Drift ...", App. E.3) replaces the in-block
+// causal mask with each node's ancestors (and itself): node i's K/V sit at
+// cache slot L+i, and row i sees block key L+j only where bit j of its
+// ancestor mask is set (node 0, the root, at L is everyone's ancestor).
 // Row i of the block (position L+i) sees keys 0..L+i ("one causal target pass
 // over the anchor and the candidates", Whisper-Flash section 3.1).
 //
@@ -92,11 +96,13 @@ struct SmRow {
 // 2^((s - m) * sl2e), sl2e = scale * log2(e). MASK (a step some row cannot
 // see whole): keys >= live_to (this lane's row) get weight 0 and keys >=
 // vlive_to (past the data) a zero V operand; other steps skip the masking
-// and the -inf guards (their scores are finite).
-template <int HD, bool MASK>
+// and the -inf guards (their scores are finite). TREE (tree verification):
+// block keys tree_L + j also need bit j of the row's ancestor mask anc.
+template <int HD, bool MASK, bool TREE = false>
 __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<HD> &f, int key0,
                                               int live_to, int vlive_to, float sl2e,
-                                              SmRow<HD / 16> &st, int g) {
+                                              SmRow<HD / 16> &st, int g, uint64_t anc = ~0ull,
+                                              int tree_L = 0) {
     constexpr int NDT = HD / 16;
     f32x4 s[2];
 #pragma unroll
@@ -110,8 +116,15 @@ __device__ __forceinline__ void attend_step_t(const QFrag<HD> &q, const KVStep<H
         }
         if constexpr (MASK) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                if (key0 + 16 * t + 4 * g + r >= live_to) s[t][r] = -INFINITY;
+            for (int r = 0; r < 4; ++r) {
+                const int key = key0 + 16 * t + 4 * g + r;
+                bool dead = key >= live_to;
+                if constexpr (TREE) {
+                    const int j = key - tree_L;
+                    dead = dead || (j >= 0 && j < 64 && !((anc >> j) & 1ull));
+                }
+                if (dead) s[t][r] = -INFINITY;
+            }
         }
     }
     float tm = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -205,7 +218,7 @@ __device__ __forceinline__ void merge_waves_t(SmRow<NDT> &s, float (*mbuf)[16 * 
 // ---------------------------------------------------------------------------
 // Self-attention over the paged KV cache, causal inside the block (or over
 // the whole block, causal = 0). grid = (n * H, ceil(T / 16)), 256 threads.
-template <int HD>
+template <int HD, bool TREE>
 __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     constexpr int NDT = HD / 16;
     __shared__ __attribute__((aligned(16))) float mbuf[2][16 * (HD + 4)];
@@ -229,13 +242,16 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
     // this lane's row r16 sees keys <= lim; keys below mask_from every row sees
     const int lim = a.causal ? L + min(row0 + r16, ntok - 1) : kmax;
-    const int mask_from = (a.causal ? L + min(row0, ntok - 1) : kmax) + 1;
+    // tree verification: a row sees its ancestors among block keys L + 1 ..
+    // (key L, the root, is every row's ancestor)
+    const int mask_from = TREE ? L + 1 : (a.causal ? L + min(row0, ntok - 1) : kmax) + 1;
     const int last_page = kmax >> 4;   // pages past this one were never validated
     // the request's page ids, one per lane (at most 64 pages)
     const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
     const int ptl = lane <= last_page ? pt[lane] : 0;
     const int qrow = row0 + r16;
     const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
+    const uint64_t anc = TREE ? a.anc[(size_t)b * a.T + min(qrow, a.T - 1)] : ~0ull;
 
     const uint16_t *kvl = a.kv_layer;
     const size_t vt_off = (size_t)a.H * 16 * HD;
@@ -273,7 +289,8 @@ __global__ __launch_bounds__(256) void self_attn_kernel(SelfAttnArgs a) {
     for (int j = wave; j < nsteps; j += 4) {
         load(min(j + 4, nsteps - 1), nxt);        // unconditional: exact wait counts
         const int key0 = 32 * j;
-        if (key0 + 32 > mask_from) attend_step_t<HD, true>(q, cur, key0, lim + 1, kmax + 1, sl2e, st, g);
+        if (key0 + 32 > mask_from)
+            attend_step_t<HD, true, TREE>(q, cur, key0, lim + 1, kmax + 1, sl2e, st, g, anc, L);
         else attend_step_t<HD, false>(q, cur, key0, lim + 1, kmax + 1, sl2e, st, g);
         cur = nxt;
     }
@@ -458,9 +475,15 @@ __global__ __launch_bounds__(256, 3) void cross_attn_kernel(CrossAttnArgs a) {
 
 hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t st) {
     dim3 grid(a.n * a.H, mt);
-    if (hd == 64) hipLaunchKernelGGL(self_attn_kernel<64>, grid, dim3(256), 0, st, a);
-    else if (hd == 16) hipLaunchKernelGGL(self_attn_kernel<16>, grid, dim3(256), 0, st, a);
-    else return hipErrorInvalidValue;
+    if (a.anc) {
+        if (hd == 64) hipLaunchKernelGGL((self_attn_kernel<64, true>), grid, dim3(256), 0, st, a);
+        else if (hd == 16) hipLaunchKernelGGL((self_attn_kernel<16, true>), grid, dim3(256), 0, st, a);
+        else return hipErrorInvalidValue;
+    } else {
+        if (hd == 64) hipLaunchKernelGGL((self_attn_kernel<64, false>), grid, dim3(256), 0, st, a);
+        else if (hd == 16) hipLaunchKernelGGL((self_attn_kernel<16, false>), grid, dim3(256), 0, st, a);
+        else return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

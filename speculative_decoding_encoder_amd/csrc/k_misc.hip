@@ -24,6 +24,25 @@ __global__ void prepare_kernel(PrepareArgs a) {
     int code = 0;
     if (a.slot_err[slot] != 0) code = -1;   // already failed: skip quietly
     if (nt < 0 || nt > a.T) code |= WF_DERR_TOKEN;
+    if (a.parents) {
+        // tree: node 0 is the root, parents[i] < i; depth and the
+        // ancestor-or-self mask of every node (padding rows and skipped
+        // requests: the root's)
+        const int32_t *par = a.parents + (size_t)b * a.T;
+        int32_t *dep = a.depth + (size_t)b * a.T;
+        uint64_t *anc = a.anc + (size_t)b * a.T;
+        const bool live = code == 0 && nt > 0;
+        if (live && par[0] != -1) code |= WF_DERR_TOKEN;
+        dep[0] = 0;
+        anc[0] = 1ull;
+        for (int i = 1; i < a.T; ++i) {
+            const int p = (live && i < nt) ? par[i] : 0;
+            if (p < 0 || p >= i) code |= WF_DERR_TOKEN;
+            const bool ok = live && i < nt && p >= 0 && p < i;
+            dep[i] = ok ? dep[p] + 1 : 0;
+            anc[i] = ok ? (anc[p] | (1ull << i)) : 1ull;
+        }
+    }
     if (code == 0 && nt > 0) {
         if (L + nt > a.n_ctx) code |= WF_DERR_CONTEXT;
         for (int i = 0; i < nt; ++i) {
@@ -55,8 +74,8 @@ __global__ __launch_bounds__(256) void embed_kernel(EmbedArgs a) {
     const int b = m / a.T, i = m - (m / a.T) * a.T;
     int tok = a.tokens[m];
     tok = tok < 0 ? 0 : (tok >= a.V ? a.V - 1 : tok);
-    int pos = a.req_L[b] + i;
-    pos = pos >= a.n_ctx ? a.n_ctx - 1 : pos;
+    int pos = a.req_L[b] + (a.depth ? a.depth[m] : i);
+    pos = pos >= a.n_ctx ? a.n_ctx - 1 : (pos < 0 ? 0 : pos);
     const u32x4 e = ld16(a.tok_emb + (size_t)tok * a.d + kg * 8);
     const u32x4 p = ld16(a.pos_emb + (size_t)pos * a.d + kg * 8);
     float v[8];
@@ -238,6 +257,114 @@ __global__ void reset_kernel(int32_t n, int32_t max_batch, const int32_t *slots,
     len[s] = 0;
     pending[s] = 0;
     err[s] = 0;
+}
+
+// Greedy acceptance on a token tree ("Alignment Drift ...", App. E.3), one
+// thread per request: a node is accepted when its parent is (the root
+// always is), the parent is not an accepted EOS and its token is the
+// target's choice at the parent; the kept path ends at the deepest accepted
+// node no deeper than R - 1 (the lowest index among equally deep ones).
+// Then as in the linear round: an accepted EOS ends the transcript with no
+// bonus, else the target's choice there is emitted and is the next anchor.
+// The parents were validated by the verify pass; a request whose rows
+// failed (argmax -1 on the path) is rejected (n_acc = -1).
+__global__ void accept_tree_kernel(TreeAcceptArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.n) return;
+    const int nt = a.n_tok[b];
+    int32_t *path = a.path + (size_t)b * a.T;
+    for (int i = 0; i < a.T; ++i) path[i] = -1;
+    int n_acc = 0, next = -1, n_emit = 0, done = 0;
+    const int R = a.budget[b];
+    if (nt > 0 && nt <= a.T && nt <= 64 && R >= 1) {
+        const int32_t *tok = a.tokens + (size_t)b * a.T;
+        const int32_t *par = a.parents + (size_t)b * a.T;
+        const int32_t *am = a.argmax + (size_t)b * a.T;
+        uint64_t acc = 1ull;                      // bit i: node i accepted
+        int depth[64];
+        depth[0] = 0;
+        int best = 0;
+        for (int i = 1; i < nt; ++i) {
+            const int p = par[i];
+            depth[i] = 0;
+            if (p < 0 || p >= i) continue;        // invalid: never accepted
+            depth[i] = depth[p] + 1;
+            const bool ok = ((acc >> p) & 1ull) && !(p > 0 && tok[p] == a.eos) &&
+                            am[p] >= 0 && tok[i] == am[p];
+            if (ok) {
+                acc |= 1ull << i;
+                if (depth[i] <= R - 1 && depth[i] > depth[best]) best = i;
+            }
+        }
+        n_acc = depth[best];
+        for (int i = best, k = n_acc; k >= 0; i = par[i], --k) path[k] = i;
+        if (n_acc > 0 && tok[best] == a.eos) {
+            n_emit = n_acc;
+            done = 1;
+        } else if (am[best] < 0) {
+            n_acc = -1;                           // the target row failed
+            done = 1;
+        } else {
+            next = am[best];
+            n_emit = n_acc + 1;
+            done = (next == a.eos) || (n_acc + 1 >= R);
+        }
+    } else if (nt > 0) {
+        n_acc = -1;
+        done = 1;
+    }
+    a.n_acc[b] = n_acc;
+    a.next_token[b] = next;
+    a.n_emit[b] = n_emit;
+    a.done[b] = done;
+}
+
+// Rollback of a tree verify, first half: in every layer, the K and V of the
+// accepted path's node at depth k (cache slot L + path[k], k = 1..a) move to
+// position L + k. One workgroup per (request, layer); each thread owns some
+// (head, dimension) elements and copies them in depth order. A source slot
+// L + path[k] (path[k] >= k) is only ever a destination L + k' for k' >
+// path[k] >= k, which the same thread writes later, so no copy reads a
+// moved value. The slot's length is then updated by the linear rollback.
+__global__ __launch_bounds__(256) void compact_kernel(CompactArgs a) {
+    const int b = blockIdx.x / a.n_layers, l = blockIdx.x - b * a.n_layers;
+    const int slot = a.slots[b];
+    if (slot < 0 || slot >= a.max_batch) return;
+    const int p = a.slot_pending[slot];
+    const int acc = a.n_acc[b];
+    if (p == 0 || acc < 1 || acc > p - 1 || acc > 63) return;   // rollback checks the rest
+    const int32_t *path = a.path + (size_t)b * a.T;
+    for (int k = 1; k <= acc; ++k) {
+        const int s = path[k];
+        if (s < k || s >= p) {                    // not a path of this verify
+            if (threadIdx.x == 0 && l == 0) atomicOr(&a.slot_err[slot], WF_DERR_ACCEPT);
+            return;
+        }
+    }
+    const int L = a.slot_len[slot];
+    const int32_t *pt = a.page_table + (size_t)slot * a.pt_stride;
+    uint16_t *kvl = a.kv + (size_t)l * a.layer_elems;
+    const size_t v_off = (size_t)a.H * 16 * a.hd;
+    for (int e = threadIdx.x; e < a.H * a.hd; e += blockDim.x) {
+        const int h = e / a.hd, dim = e - h * a.hd;
+        for (int k = 1; k <= acc; ++k) {
+            const int src = L + path[k], dst = L + k;
+            uint16_t *ps = kvl + (size_t)pt[src >> 4] * a.page_elems;
+            uint16_t *pd = kvl + (size_t)pt[dst >> 4] * a.page_elems;
+            pd[((size_t)h * 16 + (dst & 15)) * a.hd + dim] = ps[((size_t)h * 16 + (src & 15)) * a.hd + dim];
+            pd[v_off + ((size_t)h * a.hd + dim) * 16 + (dst & 15)] =
+                ps[v_off + ((size_t)h * a.hd + dim) * 16 + (src & 15)];
+        }
+    }
+}
+
+hipError_t launch_accept_tree(const TreeAcceptArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(accept_tree_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_compact(const CompactArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(compact_kernel, dim3(a.n * a.n_layers), dim3(256), 0, st, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_prepare(const PrepareArgs &a, hipStream_t st) {

@@ -64,6 +64,11 @@ struct PrepareArgs {
     const int32_t *slots, *tokens, *n_tok, *page_table;
     int32_t *slot_len, *slot_pending, *slot_err;
     int32_t *req_L, *req_ntok;
+    // tree verification (null for a linear block): parent of every node in,
+    // its depth and ancestor-or-self bit mask out ([n][T], T <= 64)
+    const int32_t *parents;
+    int32_t *depth;
+    uint64_t *anc;
 };
 
 struct EmbedArgs {
@@ -75,6 +80,7 @@ struct EmbedArgs {
     const int32_t *req_ntok, *slots, *page_table;
     int32_t pt_stride;
     int32_t *row_kv;               // [M]: page * 16 + offset, or -1 (padding / skipped)
+    const int32_t *depth;          // tree verification: row m at position L + depth[m]
 };
 
 struct LnArgs {
@@ -94,6 +100,7 @@ struct SelfAttnArgs {
     int32_t causal;                // 1: row i sees keys <= L+i; 0: the whole block
     float scale;
     uint16_t *out;                 // fp16 [M][d], fragment-tiled
+    const uint64_t *anc;           // tree verification: per row, the block keys it sees
 };
 
 // Cross-attention load ring depth (32-frame steps in flight per wave); a
@@ -182,6 +189,25 @@ struct EmbedDraftArgs {
     float *x;
 };
 
+// Greedy acceptance on a token tree, one thread per request.
+struct TreeAcceptArgs {
+    int32_t n, T, eos;
+    const int32_t *tokens, *parents, *n_tok, *budget, *argmax;
+    int32_t *path, *n_acc, *next_token, *n_emit, *done;
+};
+
+// Move the K/V of each pending slot's accepted tree path (cache slot
+// L + path[k]) to position L + k, every layer.
+struct CompactArgs {
+    int32_t n, T, n_layers, H, hd, max_batch, pt_stride, page_elems;
+    size_t layer_elems;
+    const int32_t *slots, *path, *n_acc, *slot_len, *slot_pending, *page_table;
+    int32_t *slot_err;
+    uint16_t *kv;
+};
+
+hipError_t launch_accept_tree(const TreeAcceptArgs &a, hipStream_t st);
+hipError_t launch_compact(const CompactArgs &a, hipStream_t st);
 hipError_t launch_tap(const TapArgs &a, hipStream_t st);
 hipError_t launch_rope_append(const RopeArgs &a, hipStream_t st);
 hipError_t launch_prepare_draft(const PrepareDraftArgs &a, hipStream_t st);
