@@ -109,11 +109,13 @@ class Model:
 
     # -- one causal pass over a block of rows ------------------------------
     def rows(self, req: Request, tokens, L: int, taps: Optional[list] = None,
-             return_hidden: bool = False) -> np.ndarray:
+             return_hidden: bool = False, probe=None) -> np.ndarray:
         """Run ``tokens`` at positions L..L+n-1 through every layer, writing
         their self-attention K/V into the cache at those positions. Returns
         logits [n, V]. ``taps``: list of layer indices whose post-block
-        residual stream is returned too (as ``(logits, {layer: x})``)."""
+        residual stream is returned too (as ``(logits, {layer: x})``).
+        ``probe(l, qc, kc, vc)``, if given, sees every layer's cross-attention
+        queries and the request's cross K/V."""
         s = self.s
         tokens = np.asarray(tokens, dtype=np.int64)
         n = len(tokens)
@@ -136,6 +138,8 @@ class Model:
             h = layer_norm(x, self.w(l, "ln2_g"), self.w(l, "ln2_b"), s.ln_eps)
             qc = h @ self.w(l, "wqc").T + self.w(l, "bqc")
             kc, vc = req.xkv[l]
+            if probe is not None:
+                probe(l, qc, kc, vc)
             o = multi_head_attention(qc, kc, vc, s.n_heads, None)
             x = x + (o @ self.w(l, "woc").T + self.w(l, "boc"))
 
