@@ -65,7 +65,8 @@ def log(*a):
 
 
 class Workload:
-    def __init__(self, cfg_id: int, greedy: bool = False, k: int = 0, batch: int = 0):
+    def __init__(self, cfg_id: int, greedy: bool = False, k: int = 0, batch: int = 0,
+                 readout: int = -1):
         from synthetic import (DRAFTER_TAPS, WORKLOADS, make_draft_table, make_drafter_weights,
                                make_encoder_out, make_prefixes, make_weights, rng)
         from speculative_decoding_encoder_amd.binding import Engine
@@ -97,6 +98,11 @@ class Workload:
                                 taps=DRAFTER_TAPS if self.drafter else ())
         self.slots = list(range(B))
         self.d_slots = eng.i32(self.slots)
+        self.readout = readout
+        if readout >= 0:
+            # anchor readout at that layer in every verify pass
+            self.d_frame = torch.full((max_rows,), -1, dtype=torch.int32, device=eng.dev)
+            eng.wf_set_readout(readout, self.d_frame)
         d_enc = eng.bf16(self.encs)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -447,7 +453,8 @@ def k_sweep(args):
     rows = {}
     name = None
     for k in [int(v) for v in args.k_sweep.split(",") if v]:
-        w = Workload(args.config, greedy=args.greedy, k=k, batch=args.batch)
+        w = Workload(args.config, greedy=args.greedy, k=k, batch=args.batch,
+                     readout=args.readout)
         r = measure(w, args.steps, args.warmup, use_graph=not args.no_graph)
         name = w.name
         rows[str(k)] = {"ms_per_step": round(r["ms_step"], 4),
@@ -459,6 +466,7 @@ def k_sweep(args):
         del w, r
         torch.cuda.empty_cache()
     print(json.dumps({"k_sweep": rows, "workload": name, "batch": args.batch or None,
+                      "readout_layer": args.readout if args.readout >= 0 else None,
                       "steps": args.steps,
                       "warmup": args.warmup, "graph": not args.no_graph}), flush=True)
 
@@ -480,6 +488,9 @@ def main():
                     help="comma-separated K values: time the step of --config at each K "
                          "(the pass cost against the number of candidates) and print that "
                          "as the one JSON line instead")
+    ap.add_argument("--readout", type=int, default=-1,
+                    help="with --k-sweep: also run the verification-attention anchor "
+                         "readout at this decoder layer in every verify pass")
     ap.add_argument("--batch", type=int, default=0,
                     help="with --k-sweep: this many requests instead of the workload's")
     ap.add_argument("--calib-copy-mib", type=int, default=0,

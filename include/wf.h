@@ -251,6 +251,19 @@ wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
 wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots,
                       const int32_t *d_n_acc, void *stream);
 
+/* Verification-attention anchor readout ("Alignment Drift in Single-Model
+ * Speculative Decoding for ASR", Verification-Attention Correction and
+ * appendix D.2: the target's audio attention at one decoder layer, averaged
+ * over heads, peaks at the current audio position; the scores are recomputed
+ * from the key cache). With 0 <= layer < n_layers, every later verify pass
+ * (wf_verify_block, wf_verify_tree) also writes into d_frame (int32, the
+ * pass's [n][T] rows, at least max_rows entries; device memory the caller
+ * keeps alive) the audio frame where that layer's per-head softmax over the
+ * frames, averaged over heads, is largest for each row (the lowest frame
+ * among equal values; -1 for rows at or beyond n_tok and skipped requests).
+ * layer < 0 turns it off. */
+wf_status wf_set_readout(wf_engine *e, int32_t layer, int32_t *d_frame);
+
 /* Tree verification ("Alignment Drift in Single-Model Speculative Decoding for
  * ASR", appendix E.3: the target verifies every node of a draft tree in one
  * pass under a tree attention mask; a one-branch tree reproduces the linear

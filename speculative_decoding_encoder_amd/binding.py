@@ -89,6 +89,7 @@ def load():
                             P, P, P, P, P, P, P]),
         "wf_rollback": (I32, [P, I32, P, P, P]),
         "wf_verify_tree": (I32, [P, I32, P, P, I32, P, P, P, P, P]),
+        "wf_set_readout": (I32, [P, I32, P]),
         "wf_accept_tree": (I32, [P, I32, P, I32, P, P, P, P, P, P, P, P, P, P]),
         "wf_rollback_tree": (I32, [P, I32, P, P, I32, P, P]),
         "wf_draft": (I32, [P, I32, P, P, I32, P, P, P]),
@@ -241,6 +242,9 @@ class Engine:
     def wf_rollback(self, slots, n_acc, stream=None):
         _check(self.lib.wf_rollback(self.h, slots.numel(), _p(slots), _p(n_acc),
                                     _stream(stream)), "wf_rollback")
+
+    def wf_set_readout(self, layer, frame=None):
+        _check(self.lib.wf_set_readout(self.h, int(layer), _p(frame)), "wf_set_readout")
 
     def wf_verify_tree(self, slots, tokens, parents, n_tok, argmax, logits=None, stream=None):
         n, T = tokens.shape

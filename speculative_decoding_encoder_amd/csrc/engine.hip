@@ -69,7 +69,7 @@ void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
 int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
 
 struct Layout {
-    size_t x, xs, hs, q, tdepth, tanc, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
+    size_t x, xs, hs, q, tdepth, tanc, rdml, rdpart, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
     size_t taps, dam, rowkv;
     size_t total;
     size_t part_bytes, xapart_bytes;
@@ -127,6 +127,9 @@ Layout layout_of(const wf_config *c) {
     L.q = take(M * d * 2);
     L.tdepth = take(M * 4);   // tree verification: node depths
     L.tanc = take(M * 8);     // and ancestor masks
+    // anchor readout: per row and head (max, sum), per row and 128-frame chunk a peak
+    L.rdml = take(M * H * 8);
+    L.rdpart = take(M * (size_t)cdiv(c->n_frames, 128) * 8);
     L.part = take(part);
     L.gcnt = take((size_t)cdiv(std::max(3 * (int)d, (int)f), 16) * (cdiv((int)M, 16) + 1) * 4);
     L.xapart = take(xap);
@@ -172,6 +175,9 @@ struct wf_engine {
     uint16_t *xs, *hs, *q;
     int32_t *tdepth;                         // tree verification: per row, its node's depth
     uint64_t *tanc;                          // and ancestor-or-self mask
+    float2 *rdml, *rdpart;                   // anchor readout scratch
+    int readout_layer = -1;                  // wf_set_readout: layer, or -1
+    int32_t *readout_frame = nullptr;        // and its output [rows]
     float *part;
     int32_t *gcnt;
     float *xapart;
@@ -521,6 +527,8 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->q = (uint16_t *)(ws + L.q);
     e->tdepth = (int32_t *)(ws + L.tdepth);
     e->tanc = (uint64_t *)(ws + L.tanc);
+    e->rdml = (float2 *)(ws + L.rdml);
+    e->rdpart = (float2 *)(ws + L.rdpart);
     e->part = (float *)(ws + L.part);
     e->gcnt = (int32_t *)(ws + L.gcnt);
     e->xapart = (float *)(ws + L.xapart);
@@ -765,6 +773,15 @@ static wf_status verify_pass(wf_engine *e, int32_t n, const int32_t *d_slots,
                         d_parents ? e->tanc : nullptr};
         WF_TRY(timed(e, TK_SELF, st, [&] { return launch_self_attn(sa, hd, p.mt, st); }));
         WF_TRY(run_out_cross_mlp(e, w, l, p, st));
+        if (l == e->readout_layer) {
+            // the layer's cross queries are still in q
+            ReadoutArgs ra{e->q, e->xkv, (int64_t)e->xkv_slot_elems,
+                           (int64_t)(l * e->xkv_layer_elems), d_slots, e->reqN, n, T, H, hd, d,
+                           c.n_frames, e->F_pad, c.max_batch, cdiv(c.n_frames, 128),
+                           1.4426950408889634f / std::sqrt((float)hd), e->rdml, e->rdpart,
+                           e->readout_frame};
+            WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_readout(ra, p.mt, st); }));
+        }
         // history taps for the drafter (residual stream after this block)
         for (int j = 0; j < (c.drafter_layers > 0 ? c.n_taps : 0); ++j) {
             if (c.tap_layers[j] != l) continue;
@@ -799,6 +816,15 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
                           const int32_t *d_tokens, int32_t T, const int32_t *d_n_tok,
                           int32_t *d_argmax, float *d_logits, void *stream) {
     return verify_pass(e, n, d_slots, d_tokens, T, nullptr, d_n_tok, d_argmax, d_logits, stream);
+}
+
+wf_status wf_set_readout(wf_engine *e, int32_t layer, int32_t *d_frame) {
+    if (!e) return fail(WF_EINVAL, "null engine");
+    if (layer >= e->c.n_layers) return fail(WF_EINVAL, "layer outside the decoder");
+    if (layer >= 0 && !d_frame) return fail(WF_EINVAL, "null output");
+    e->readout_layer = layer < 0 ? -1 : layer;
+    e->readout_frame = layer < 0 ? nullptr : d_frame;
+    return WF_OK;
 }
 
 wf_status wf_verify_tree(wf_engine *e, int32_t n, const int32_t *d_slots,

@@ -189,6 +189,22 @@ struct EmbedDraftArgs {
     float *x;
 };
 
+// Verification-attention anchor readout at one decoder layer: the layer's
+// cross-attention scores recomputed from the cross K cache, per head the
+// softmax over frames, summed over heads, and the peak frame per row.
+struct ReadoutArgs {
+    const uint16_t *q;             // the layer's cross queries, fp16 [M][d]
+    const uint16_t *xkv;           // write-once pool
+    int64_t slot_stride, layer_off;
+    const int32_t *slots, *req_ntok;
+    int32_t n, T, H, hd, d, F, F_pad, max_batch, nc;   // nc: 128-frame chunks
+    float sl2e;                    // scale * log2(e)
+    float2 *ml;                    // [M][H]: row max and sum of 2^((s - max) sl2e)
+    float2 *part;                  // [M][nc]: (peak value, frame) per chunk
+    int32_t *frame;                // [M] out: peak frame, -1 for skipped rows
+};
+hipError_t launch_readout(const ReadoutArgs &a, int mt, hipStream_t st);
+
 // Greedy acceptance on a token tree, one thread per request.
 struct TreeAcceptArgs {
     int32_t n, T, eos;
