@@ -499,8 +499,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
-              "single MI355X (requests shard by data parallelism with no exchange; see "
-              "DESIGN.md). --gpus N > 1 is not supported.", file=sys.stderr)
+              "single MI355X (requests would shard by data parallelism, with no exchange "
+              "between GPUs). --gpus N > 1 is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch
     torch.cuda.set_device(0)

@@ -12,7 +12,7 @@ Whisper-Flash §3.1 and App. A.1 define one round:
 * rollback keeps L+1+a cache positions (old anchor plus accepted candidates);
 * with R output tokens left at most R-1 candidates are proposed.
 
-Readings (the design doc lists them): argmax ties go to the lowest token id; the
+Readings where the pages leave a step open: argmax ties go to the lowest token id; the
 first anchor, emitted by prefill, counts toward the output budget; a request
 is done when it has emitted ``n_max`` tokens or emitted EOS.
 """

@@ -17,7 +17,7 @@ Whisper-Flash §3.2 (eq. 2) and App. A.2:
 * the token embedding and the output head are shared with the target; mask
   position i predicts the token at position t + i.
 
-Readings (listed in the design doc): a drafter layer has the target block's
+Readings where the pages leave a step open: a drafter layer has the target block's
 pre-LN structure (self-attention, cross-attention, GELU MLP, same biases);
 history rows enter a layer's attention like block rows — k = RoPE(W_k
 LN1(h), pos), v = W_v LN1(h) + b_v — and are not updated across layers;

@@ -16,7 +16,7 @@ at position L+i and predicts position L+i+1 (App. A.1). Cross-attention K/V
 are a per-request constant written once (SGLang-Omni cookbook, "Breakable
 Prefill CUDA Graph"); ``encode_kv`` computes them.
 
-Readings where the pages are silent (each listed in the design doc): learned
+Readings where the pages are silent: learned
 absolute positions of length 448; LN eps 1e-5 with gain/bias; biases on
 q, v, o, cross q/v/o, fc1, fc2 but none on k (a key bias shifts all scores
 of a row equally, so it cannot change the output); scores scaled by

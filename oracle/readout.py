@@ -7,7 +7,7 @@ Verification-Attention Correction and App. D.2: the target's audio
 layer, peaks at the current audio position; inference recomputes that
 layer's attention scores from the existing key cache and takes the peak.
 
-Readings (the design doc lists them): the readout is given for every verify row
+Readings where the pages leave a step open: the readout is given for every verify row
 (the caller takes the row it needs, e.g. the last kept one); probabilities
 are the layer's softmax over the audio frames with the 1/sqrt(head_dim)
 scale, averaged over heads with equal weight; the peak is the lowest frame

@@ -8,7 +8,7 @@ accepted it samples a bonus from the next row's p. App. A.4: softmax and the
 acceptance probabilities are computed in FP32; EOS and the output budget
 work as in greedy decoding.
 
-Readings (listed in the design doc): the acceptance test is u*q(y) < p(y) with
+Readings where the pages leave a step open: the acceptance test is u*q(y) < p(y) with
 u uniform on [0, 1), equivalent to u < p/q for q(y) > 0 (which holds since
 y ~ q); a draw from weights w uses the inverse CDF in ascending token order,
 c = min{v : sum_{w<=v} w > u * sum(w)}; if the residual sums to zero, which

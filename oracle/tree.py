@@ -7,7 +7,7 @@ candidate tokens, the target verifies every node in one pass under a tree
 attention mask, and a tree with a single branch reproduces the linear
 decoder token for token.
 
-Readings (the design doc lists them):
+Readings where the pages leave a step open:
 
 * node 0 is the anchor (the root) and ``parents[i] < i`` for every other
   node, so a node's ancestors come before it;

@@ -1,7 +1,7 @@
 """Pins of the oracle's parallel drafter (Whisper-Flash §3.2, App. A.2).
 
 The pages print no drafter values, so beyond these checks the drafter's
-parity is unpinned:
+parity is unpinned beyond them:
 * RoPE equals multiplying each (i, i + hd/2) pair, read as a complex
   number, by exp(i * pos * 10000^(-2i/hd));
 * after RoPE a query-key product depends only on the position difference
