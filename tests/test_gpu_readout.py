@@ -47,8 +47,8 @@ def _scale_bf16(bits: np.ndarray, k: int) -> np.ndarray:
     return np.where(nz, b + (k << 7), b).astype(bits.dtype)
 
 
-@pytest.mark.parametrize("shape_name,layer", [("tiny", 1), ("turbo", 2)])
-def test_readout_against_the_oracle(torch_cuda, shape_name, layer):
+@pytest.mark.parametrize("shape_name,layer,T", [("tiny", 1, 9), ("tiny", 0, 20), ("turbo", 2, 9)])
+def test_readout_against_the_oracle(torch_cuda, shape_name, layer, T):
     from speculative_decoding_encoder_amd.binding import Engine
     torch = torch_cuda
     shape = TINY if shape_name == "tiny" else TURBO
@@ -61,7 +61,7 @@ def test_readout_against_the_oracle(torch_cuda, shape_name, layer):
             # several near-equal ones: give every head head 0's projections
             w = _same_heads(w, shape.d_model // shape.n_heads)
         wbits[f"L{layer}.{name}"] = w
-    B, T = 3, 9
+    B = 3
     prefixes = [p[:40] for p in make_prefixes(wl, B)]
     encs = np.stack([make_encoder_out(shape, wl.cfg_id, 20 + r) for r in range(B)])
     eng = Engine(shape, wbits, max_batch=B, max_rows=B * 64)
@@ -77,7 +77,7 @@ def test_readout_against_the_oracle(torch_cuda, shape_name, layer):
     eng.wf_rollback(eng.i32(slots), eng.i32(lens - 1))
     blocks = np.random.default_rng(5).integers(0, shape.vocab - 1, (B, T)).astype(np.int32)
     blocks[:, 0] = am.cpu().numpy()[np.arange(B), lens - 1]
-    n_tok = [9, 5, 9]
+    n_tok = [T, 5, T]
     frame = torch.full((B * 64,), -7, dtype=torch.int32, device=eng.dev)
     outs = []
     for on in (True, False):
