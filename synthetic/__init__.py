@@ -246,3 +246,90 @@ def make_drafter_weights(shape: ModelShape, cfg_id: int, n_layers: int = 2, n_ta
         else _draw(cfg_id, 30003, (d,), 0.1, 1.0)
     out["lnd_b"] = np.zeros((d,), np.uint16) if not ln_random else _draw(cfg_id, 30004, (d,), 0.1)
     return out
+
+
+# -- encoder (audio features -> audio memory) ---------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class EncoderShape:
+    """Audio encoder shape: ``n_mels`` log-mel channels over ``2 * n_frames``
+    feature frames (10 ms hop) in, ``n_frames`` frames of width ``d_model``
+    out (the stride-2 stem halves the frame rate)."""
+    n_layers: int
+    d_model: int
+    n_heads: int
+    head_dim: int
+    d_ffn: int
+    n_mels: int
+    n_frames: int
+    ln_eps: float = 1e-5
+
+
+# Whisper large-v3 encoder (the turbo variant shares it): 32 blocks, width
+# 1280, 20 heads of 64, MLP 5120, 128 mel channels, 3000 feature frames ->
+# 1500 frames for a 30 s window. The small shape keeps head_dim 64.
+ENC_LARGE_V3 = EncoderShape(n_layers=32, d_model=1280, n_heads=20, head_dim=64,
+                            d_ffn=5120, n_mels=128, n_frames=1500)
+ENC_SMALL = EncoderShape(n_layers=2, d_model=128, n_heads=2, head_dim=64,
+                         d_ffn=512, n_mels=64, n_frames=100)
+
+ENC_LAYER_TENSORS: List[str] = [
+    "ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
+    "ln2_g", "ln2_b", "w1", "b1", "w2", "b2",
+]
+ENC_GLOBAL_TENSORS: List[str] = ["conv1_w", "conv1_b", "conv2_w", "conv2_b", "lnp_g", "lnp_b"]
+__all__ += ["EncoderShape", "ENC_LARGE_V3", "ENC_SMALL", "ENC_LAYER_TENSORS",
+            "ENC_GLOBAL_TENSORS", "make_encoder_weights", "make_mel"]
+
+
+def _enc_shapes(s: EncoderShape):
+    d, f = s.d_model, s.d_ffn
+    g = {"conv1_w": (d, s.n_mels, 3), "conv1_b": (d,), "conv2_w": (d, d, 3), "conv2_b": (d,),
+         "lnp_g": (d,), "lnp_b": (d,)}
+    lay = {}
+    for n in ENC_LAYER_TENSORS:
+        if n in ("w1",):
+            lay[n] = (f, d)
+        elif n == "w2":
+            lay[n] = (d, f)
+        elif n == "b1":
+            lay[n] = (f,)
+        elif n.startswith("w"):
+            lay[n] = (d, d)
+        else:
+            lay[n] = (d,)
+    return g, lay
+
+
+def make_encoder_weights(shape: EncoderShape, cfg_id: int, ln_random: bool = False,
+                         n_layers: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Random-init encoder (bf16 bits): globals ``conv1_w`` [d, n_mels, 3],
+    ``conv1_b``, ``conv2_w`` [d, d, 3], ``conv2_b`` (PyTorch Conv1d layout),
+    the final norm ``lnp_g`` / ``lnp_b``, and ``"E<l>.<name>"`` per block.
+    Same recipe as the decoder: 0.02 N(0, 1), gains 1, norm biases 0. Tensor
+    ids 40000 + i (globals) and 41000 + 64 l + i (blocks)."""
+    nl = shape.n_layers if n_layers is None else n_layers
+    gs, ls = _enc_shapes(shape)
+    out: Dict[str, np.ndarray] = {}
+
+    def one(tid, name, shp):
+        if name.startswith("ln") and name.endswith("_g"):
+            return _draw(cfg_id, tid, shp, 0.1, 1.0) if ln_random \
+                else f32_to_bf16_bits(np.ones(shp, np.float32))
+        if name.startswith("ln") and name.endswith("_b"):
+            return _draw(cfg_id, tid, shp, 0.1) if ln_random else np.zeros(shp, np.uint16)
+        return _draw(cfg_id, tid, shp, 0.02)
+
+    for i, name in enumerate(ENC_GLOBAL_TENSORS):
+        out[name] = one(40000 + i, name, gs[name])
+    for l in range(nl):
+        for i, name in enumerate(ENC_LAYER_TENSORS):
+            out[f"E{l}.{name}"] = one(41000 + 64 * l + i, name, ls[name])
+    return out
+
+
+def make_mel(shape: EncoderShape, cfg_id: int, request: int) -> np.ndarray:
+    """Log-mel features of one request: bf16 bits [n_mels, 2 * n_frames],
+    N(0, 1) (tensor id 4000 + request). They stand in for normalised
+    log-mel features of a 30 s window."""
+    return _draw(cfg_id, 4000 + request, (shape.n_mels, 2 * shape.n_frames), 1.0)
