@@ -329,6 +329,82 @@ wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *st
 wf_status wf_set_timing(wf_engine *e, int32_t enable);
 wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count);
 
+
+/* ------------------------------------------------------------------------
+ * Audio encoder: log-mel features of a fixed window to the audio memory
+ * (the encoder stage before wf_encode_kv; "Whisper-Flash ...", sections 1-2
+ * and appendix A.3, Table A2, where it is a fixed cost per request; the
+ * 30 s mel window of the SGLang-Omni "Whisper ASR" cookbook, "Long Audio
+ * Chunking"). The pages give no layer detail; the encoder follows the
+ * Whisper architecture they cite: two width-3 convolutions over time (zero
+ * padding 1, the second with stride 2, each followed by exact GELU), a fixed
+ * sinusoidal position table (channel j < d/2: sin(t w_j), d/2 + j:
+ * cos(t w_j), w_j = 10000^(-j/(d/2-1))), n_layers pre-LN blocks of
+ * bidirectional self-attention (scores / sqrt(64), biases on q, v and the
+ * output projection, none on k) and a GELU MLP, then a final layer norm.
+ *
+ * Numerics: bf16 MFMA with fp32 accumulation; the residual stream, layer
+ * norms, softmax and GELU are fp32; activations between kernels (layer-norm
+ * outputs, q, k, v, attention output, MLP hidden, convolution outputs) and
+ * the attention probabilities entering the PV product are bf16.
+ * ------------------------------------------------------------------------ */
+typedef struct wf_encoder wf_encoder;
+
+typedef struct {
+    int32_t n_layers;   /* encoder blocks (32 for large-v3 and turbo) */
+    int32_t d_model;    /* width: n_heads * 64, at most 1280 */
+    int32_t n_heads;    /* attention heads (head_dim must be 64) */
+    int32_t head_dim;   /* 64 */
+    int32_t d_ffn;      /* MLP width, a multiple of 64 (5120) */
+    int32_t n_mels;     /* mel channels (128), at most 256, 3 n_mels % 32 == 0 */
+    int32_t n_frames;   /* output frames F (1500); the input has 2F frames */
+    int32_t max_batch;  /* largest n of one wf_encode call */
+    float ln_eps;       /* 1e-5 */
+} wf_enc_config;
+
+/* One block (bf16, PyTorch Linear convention: weight [out, in]). */
+typedef struct {
+    const void *ln1_g, *ln1_b;                    /* [d] */
+    const void *wq, *bq, *wk, *wv, *bv, *wo, *bo; /* [d, d] / [d]; no key bias */
+    const void *ln2_g, *ln2_b;
+    const void *w1, *b1;                          /* [d_ffn, d], [d_ffn] */
+    const void *w2, *b2;                          /* [d, d_ffn], [d] */
+} wf_enc_layer_weights;
+
+typedef struct {
+    const void *conv1_w, *conv1_b;  /* [d, n_mels, 3] (PyTorch Conv1d), [d] */
+    const void *conv2_w, *conv2_b;  /* [d, d, 3], [d] */
+    const void *lnp_g, *lnp_b;      /* final layer norm [d] */
+    const wf_enc_layer_weights *layers; /* host array of n_layers entries (copied) */
+} wf_enc_weights;
+
+/* Workspace of an encoder (activations for max_batch requests, the position
+ * table and the convolution weights re-laid in window order); 0 for an
+ * invalid configuration. */
+size_t wf_enc_workspace_bytes(const wf_enc_config *cfg);
+
+/* Create an encoder on the current HIP device (gfx950). The weights stay
+ * the caller's and must outlive the encoder; the workspace is zeroed and
+ * prepared here (synchronously). */
+wf_status wf_enc_create(const wf_enc_config *cfg, const wf_enc_weights *w, void *workspace,
+                        size_t ws_bytes, wf_encoder **out);
+void wf_enc_destroy(wf_encoder *e);
+
+/* d_mel: bf16 [n][n_mels][2 n_frames] (channel-major, as a feature
+ * extractor produces it); d_out: bf16 [n][n_frames][d_model], the audio
+ * memory that wf_encode_kv takes. 1 <= n <= max_batch. Asynchronous on the
+ * stream; calls on one encoder must not overlap (they share the workspace). */
+wf_status wf_encode(wf_encoder *e, int32_t n, const void *d_mel, void *d_out, void *stream);
+
+/* Per-kind launch timing as for the engine. Kinds: 0 stem convolutions,
+ * 1 QKV projection, 2 attention, 3 output projection + residual,
+ * 4 fc1 + GELU, 5 fc2 + residual, 6 layer norms, 7 feature transpose. */
+enum { WF_ENC_TK_STEM = 0, WF_ENC_TK_QKV = 1, WF_ENC_TK_ATTN = 2, WF_ENC_TK_OPROJ = 3,
+       WF_ENC_TK_FC1 = 4, WF_ENC_TK_FC2 = 5, WF_ENC_TK_LN = 6, WF_ENC_TK_OTHER = 7,
+       WF_ENC_TK_N = 8 };
+wf_status wf_enc_set_timing(wf_encoder *e, int32_t enable);
+wf_status wf_enc_get_timing(wf_encoder *e, int32_t kind, double *total_ms, int32_t *count);
+
 #ifdef __cplusplus
 }
 #endif

@@ -51,10 +51,11 @@ def conv3(x: np.ndarray, w: np.ndarray, b: np.ndarray, stride: int) -> np.ndarra
     xp = np.zeros((c_in, T + 2), dtype=x.dtype)
     xp[:, 1:T + 1] = x
     t_out = (T - 1) // stride + 1
-    out = np.empty((w.shape[0], t_out), dtype=x.dtype)
-    for t in range(t_out):
-        win = xp[:, stride * t: stride * t + 3]            # input frames s t - 1 .. s t + 1
-        out[:, t] = b + np.einsum("oik,ik->o", w, win)
+    out = np.repeat(b[:, None], t_out, axis=1).astype(x.dtype)
+    for k in range(3):
+        # tap k reads input frame s t + k - 1, padded index s t + k
+        out += (np.ascontiguousarray(w[:, :, k])
+                @ np.ascontiguousarray(xp[:, k: k + stride * (t_out - 1) + 1: stride]))
     return out
 
 

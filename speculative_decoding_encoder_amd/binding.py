@@ -56,6 +56,26 @@ class Weights(ctypes.Structure):
                 ("drafter", ctypes.POINTER(DrafterWeights))]
 
 
+class EncConfig(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "n_layers", "d_model", "n_heads", "head_dim", "d_ffn", "n_mels", "n_frames",
+        "max_batch")] + [("ln_eps", ctypes.c_float)]
+
+
+ENC_LAYER_FIELDS = ["ln1_g", "ln1_b", "wq", "bq", "wk", "wv", "bv", "wo", "bo",
+                    "ln2_g", "ln2_b", "w1", "b1", "w2", "b2"]
+
+
+class EncLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ENC_LAYER_FIELDS]
+
+
+class EncWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("conv1_w", "conv1_b", "conv2_w", "conv2_b", "lnp_g", "lnp_b")] + [
+        ("layers", ctypes.POINTER(EncLayerWeights))]
+
+
 def header_functions() -> list:
     """Names of the functions include/wf.h declares."""
     txt = open(HEADER).read()
@@ -98,6 +118,14 @@ def load():
         "wf_set_timing": (I32, [P, I32]),
         "wf_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
                                 ctypes.POINTER(ctypes.c_int32)]),
+        "wf_enc_workspace_bytes": (SZ, [ctypes.POINTER(EncConfig)]),
+        "wf_enc_create": (I32, [ctypes.POINTER(EncConfig), ctypes.POINTER(EncWeights), P, SZ,
+                                ctypes.POINTER(VP)]),
+        "wf_enc_destroy": (None, [P]),
+        "wf_encode": (I32, [P, I32, P, P, P]),
+        "wf_enc_set_timing": (I32, [P, I32]),
+        "wf_enc_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
+                                    ctypes.POINTER(ctypes.c_int32)]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -301,3 +329,68 @@ class Engine:
 
 TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn", "cross_attn",
                 "other", "encode_kv", "draft", "history"]
+
+
+ENC_TIMING_KINDS = ["stem", "qkv", "attn", "oproj", "fc1", "fc2", "ln", "other"]
+
+
+class Encoder:
+    """Audio encoder through the C ABI. Owns the device copies of the
+    weights (bf16 bits from ``synthetic.make_encoder_weights``) and the
+    workspace, allocated with torch."""
+
+    def __init__(self, shape, wbits: Dict[str, np.ndarray], max_batch: int, device: int = 0):
+        import torch
+        self.torch = torch
+        self.shape = shape
+        self.dev = torch.device("cuda", device)
+        lib = load()
+        self.cfg = EncConfig(n_layers=shape.n_layers, d_model=shape.d_model,
+                             n_heads=shape.n_heads, head_dim=shape.head_dim, d_ffn=shape.d_ffn,
+                             n_mels=shape.n_mels, n_frames=shape.n_frames, max_batch=max_batch,
+                             ln_eps=shape.ln_eps)
+        self.max_batch = max_batch
+        self._bufs = {k: torch.from_numpy(v.view(np.int16).copy()).to(self.dev)
+                      for k, v in wbits.items()}
+        lay = (EncLayerWeights * shape.n_layers)()
+        for l in range(shape.n_layers):
+            for f in ENC_LAYER_FIELDS:
+                setattr(lay[l], f, self._bufs[f"E{l}.{f}"].data_ptr())
+        self._lay = lay
+        w = EncWeights(layers=lay)
+        for f in ("conv1_w", "conv1_b", "conv2_w", "conv2_b", "lnp_g", "lnp_b"):
+            setattr(w, f, self._bufs[f].data_ptr())
+        nb = int(lib.wf_enc_workspace_bytes(ctypes.byref(self.cfg)))
+        if nb == 0:
+            raise WFError("invalid encoder configuration")
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=self.dev)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.dev):
+            _check(lib.wf_enc_create(ctypes.byref(self.cfg), ctypes.byref(w), self.ws.data_ptr(),
+                                     nb, ctypes.byref(h)), "wf_enc_create")
+        self.h = h
+
+    def bf16(self, bits: np.ndarray):
+        return self.torch.from_numpy(np.ascontiguousarray(bits).view(np.int16).copy()).to(self.dev)
+
+    def wf_encode(self, d_mel, d_out, stream=None):
+        n = d_mel.shape[0]
+        _check(load().wf_encode(self.h, n, d_mel.data_ptr(), d_out.data_ptr(), _stream(stream)),
+               "wf_encode")
+
+    def set_timing(self, on: bool):
+        _check(load().wf_enc_set_timing(self.h, 1 if on else 0), "wf_enc_set_timing")
+
+    def timing(self) -> Dict[str, tuple]:
+        out = {}
+        for i, name in enumerate(ENC_TIMING_KINDS):
+            ms, cnt = ctypes.c_double(), ctypes.c_int32()
+            _check(load().wf_enc_get_timing(self.h, i, ctypes.byref(ms), ctypes.byref(cnt)),
+                   "wf_enc_get_timing")
+            out[name] = (ms.value, cnt.value)
+        return out
+
+    def close(self):
+        if self.h:
+            load().wf_enc_destroy(self.h)
+            self.h = None

@@ -1,0 +1,829 @@
+// Audio encoder forward on gfx950: a fixed window of log-mel features to the
+// audio memory that wf_encode_kv projects (the encoder stage of
+// "Whisper-Flash ...", §1-2 and App. A.3 Table A2; the 30 s mel window of the
+// SGLang-Omni "Whisper ASR" cookbook, "Long Audio Chunking").
+//
+//   melT    = features transposed to time-major rows, one zero row each side
+//   g1      = GELU(conv3(melT) + b1)            GEMM, K = 3 n_mels (3 taps)
+//   x       = GELU(conv3_s2(g1) + b2) + pos     GEMM, K = 3 d, A rows 2 apart
+//   per block: LN1 -> QKV GEMM (q, k, v^T per head) -> attention (all frames)
+//              -> O GEMM + residual -> LN2 -> fc1 GEMM + GELU -> fc2 + residual
+//   out     = LN_post(x)                        bf16 [n][F][d]
+//
+// Unlike the decoder pass this work is MFMA-bound (a 30 s window is about
+// 2.3 TFLOP through 32 blocks), so the kernels are dense-contraction designs:
+//
+//  * GEMM: C = A W^T, bf16 x bf16 -> fp32 (16x16x32 MFMA). A workgroup of 4
+//    waves owns a 128 x 256 tile (each wave 64 x 128: 4 x 8 accumulator
+//    tiles); both operands go through double-buffered LDS in 32-deep k-steps
+//    (rows padded to 80 B: conflict-free 16-byte fragment reads). The MFMA
+//    computes C^T so a lane holds one output row and four consecutive
+//    columns (8- or 16-byte epilogue stores). Row tiles are grouped by 8 per
+//    column walk and workgroups are dealt to the 8 XCDs in consecutive
+//    runs, so the tiles that share operands meet in one L2.
+//    A row m of the A operand is A + (m / rpr) * sreq + (m % rpr) * srow: a
+//    plain matrix (rpr = M), or a width-3 convolution read in place from
+//    time-major rows with zero borders (K = 3 C_in consecutive elements,
+//    srow = C_in for stride 1, 2 C_in for stride 2).
+//  * Attention: one workgroup per (request, head, 256 queries), each wave 64
+//    queries; 64-key steps of K ([key][dim]) and V^T ([dim][key]) through
+//    double-buffered LDS. S^T = K Q^T and O^T += V^T P^T keep a query per
+//    lane, so P stays in registers as the B operand (bf16) and only the
+//    running max crosses lanes (two exchanges) per step; the row sums are
+//    per-lane partials combined once at the end.
+#include "../../include/wf.h"
+#include "wf_device.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+namespace wf {
+wf_status set_error(wf_status s, const char *msg);   // engine.hip (wf_last_error)
+}
+
+namespace wf {
+namespace enc {
+
+enum { EE_CONV1 = 0, EE_CONV2 = 1, EE_QKV = 2, EE_RESID = 3, EE_GELU = 4 };
+
+struct GemmArgs {
+    const uint16_t *A;                 // bf16; row m at A + (m / rpr) * sreq + (m % rpr) * srow
+    int rpr;
+    long long sreq;
+    int srow;
+    const uint16_t *W0, *W1, *W2;      // bf16 [N][K], in segments of seg_n rows
+    const uint16_t *b0, *b1, *b2;      // per-segment biases (nullable)
+    int M, N, K, seg_n;
+    int n_m, n_n, n_wg;                // row tiles, column tiles, workgroups
+    float *x;                          // EE_RESID, EE_CONV2: fp32 [M][N]
+    const float *pos;                  // EE_CONV2: fp32 [F][N]
+    uint16_t *out;                     // EE_GELU: bf16 [M][N]; EE_CONV1: padded rows
+    int F, Tm;                         // frames and feature frames per request
+    uint16_t *q, *k, *vt;              // EE_QKV
+    int H, Fq;                         // heads; frames padded to the query tile
+};
+
+constexpr int GBM = 128, GBN = 256, GBK = 32, GROW = 40;
+
+__device__ __forceinline__ float gelu(float t) {
+    return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+__device__ __forceinline__ float bias4(const uint16_t *b, int c, int r) {
+    return b ? bf2f(b[c + r]) : 0.0f;
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][GBM * GROW];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][GBN * GROW];
+    const int per = gridDim.x >> 3;
+    const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (lid >= a.n_wg) return;
+    constexpr int GM = 8;                           // row tiles per column walk
+    const int grp = lid / (GM * a.n_n);
+    const int first_m = grp * GM;
+    const int gsz = min(a.n_m - first_m, GM);
+    const int in_grp = lid - grp * GM * a.n_n;
+    const int mt = first_m + in_grp % gsz;
+    const int nt = in_grp / gsz;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = mt * GBM, n0 = nt * GBN;
+
+    // 16-byte pieces of a k-step: A 128 rows x 4 (2 per thread), W 256 rows
+    // x 4 (4 per thread). Rows past M / N repeat the last (never stored).
+    const uint16_t *xsrc[2];
+    const uint16_t *wsrc[4];
+    int xoff[2], woff[4];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int p = tid + 256 * v, row = p >> 2, pc = p & 3;
+        const int m = min(m0 + row, a.M - 1);
+        const int rq = m / a.rpr;
+        xsrc[v] = a.A + (size_t)rq * a.sreq + (size_t)(m - rq * a.rpr) * a.srow + pc * 8;
+        xoff[v] = row * GROW + pc * 8;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int p = tid + 256 * v, row = p >> 2, pc = p & 3;
+        const int n = min(n0 + row, a.N - 1);
+        const int seg = n / a.seg_n;
+        const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
+        wsrc[v] = wb + (size_t)(n - seg * a.seg_n) * a.K + pc * 8;
+        woff[v] = row * GROW + pc * 8;
+    }
+    u32x4 rx[2], rw[4];
+    auto gload = [&](int kt) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) rx[v] = ld16(xsrc[v] + kt * GBK);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) rw[v] = ld16(wsrc[v] + kt * GBK);
+    };
+    auto sstore = [&](int b) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) *reinterpret_cast<u32x4 *>(&xs[b][xoff[v]]) = rx[v];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4 *>(&ws[b][woff[v]]) = rw[v];
+    };
+
+    f32x4 acc[4][8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int KT = a.K / GBK;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const int b = kt & 1;
+        if (kt + 1 < KT) gload(kt + 1);
+        u32x4 xf[4], wf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 64 + i * 16 + r16) * GROW + g * 8]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            wf[j] = *reinterpret_cast<const u32x4 *>(&ws[b][(wn * 128 + j * 16 + r16) * GROW + g * 8]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16_k32(wf[j], xf[i], acc[i][j]);
+        if (kt + 1 < KT) sstore(b ^ 1);
+        __syncthreads();
+    }
+
+    // epilogue: tile (i, j) gives this lane row m and columns n .. n + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 64 + i * 16 + r16;
+        if (m >= a.M) continue;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = n0 + wn * 128 + j * 16 + 4 * g;
+            if (n >= a.N) continue;
+            const f32x4 c = acc[i][j];
+            if constexpr (EPI == EE_RESID) {
+                float4 *px = reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n);
+                float4 xv = *px;
+                xv.x += c[0] + bias4(a.b0, n, 0);
+                xv.y += c[1] + bias4(a.b0, n, 1);
+                xv.z += c[2] + bias4(a.b0, n, 2);
+                xv.w += c[3] + bias4(a.b0, n, 3);
+                *px = xv;
+            } else if constexpr (EPI == EE_GELU || EPI == EE_CONV1) {
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] = gelu(c[r] + bias4(a.b0, n, r));
+                size_t row = m;
+                if constexpr (EPI == EE_CONV1) {
+                    const int rq = m / a.Tm;
+                    row = (size_t)rq * (a.Tm + 2) + 1 + (m - rq * a.Tm);
+                }
+                *reinterpret_cast<u32x2 *>(a.out + row * a.N + n) =
+                    u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+            } else if constexpr (EPI == EE_CONV2) {
+                const int t = m % a.F;
+                const float4 pv = *reinterpret_cast<const float4 *>(a.pos + (size_t)t * a.N + n);
+                float4 xv;
+                xv.x = gelu(c[0] + bias4(a.b0, n, 0)) + pv.x;
+                xv.y = gelu(c[1] + bias4(a.b0, n, 1)) + pv.y;
+                xv.z = gelu(c[2] + bias4(a.b0, n, 2)) + pv.z;
+                xv.w = gelu(c[3] + bias4(a.b0, n, 3)) + pv.w;
+                *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = xv;
+            } else {   // EE_QKV
+                const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
+                const int h = cc >> 6, dim = cc & 63;
+                const int rq = m / a.F, t = m - rq * a.F;
+                const uint16_t *bb = seg == 0 ? a.b0 : (seg == 2 ? a.b2 : nullptr);
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] = c[r] + bias4(bb, cc, r);
+                const size_t bh = (size_t)rq * a.H + h;
+                if (seg < 2) {
+                    uint16_t *dst = (seg == 0 ? a.q : a.k) + (bh * a.Fq + t) * 64 + dim;
+                    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+                } else {
+                    uint16_t *dst = a.vt + (bh * 64 + dim) * a.Fq + t;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[(size_t)r * a.Fq] = f2bf(y[r]);
+                }
+            }
+        }
+    }
+}
+
+struct AttnArgs {
+    const uint16_t *q, *k, *vt;        // [n][H][Fq][64], [n][H][Fq][64], [n][H][64][Fq]
+    uint16_t *o;                       // bf16 [n][F][d]
+    int H, F, Fq, d, n_qt, n_wg;
+    float sl2e;                        // log2(e) / sqrt(64)
+};
+
+constexpr int AROW = 72;               // LDS row: 64 elements + 16 B pad
+
+__global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t ks[2][64 * AROW];   // [key][dim]
+    __shared__ __attribute__((aligned(16))) uint16_t vs[2][64 * AROW];   // [dim][key]
+    const int per = gridDim.x >> 3;
+    const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (lid >= a.n_wg) return;
+    const int qt = lid % a.n_qt;
+    const int bh = lid / a.n_qt;                  // request * H + head
+    const int rq = bh / a.H, h = bh - rq * a.H;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const uint16_t *qb = a.q + (size_t)bh * a.Fq * 64;
+    const uint16_t *kb = a.k + (size_t)bh * a.Fq * 64;
+    const uint16_t *vb = a.vt + (size_t)bh * 64 * a.Fq;
+    const int q0 = qt * 256 + wave * 64;
+
+    u32x4 qf[4][2];
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+            qf[s][kk] = ld16(qb + (size_t)(q0 + 16 * s + r16) * 64 + kk * 32 + g * 8);
+
+    // staging: pieces tid, tid + 256 of K (key = p / 8), of V^T (dim = p / 8)
+    u32x4 rk[2], rv[2];
+    int soff[2];
+    const uint16_t *ksrc[2], *vsrc[2];
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+        const int p = tid + 256 * v, row = p >> 3, pc = p & 7;
+        soff[v] = row * AROW + pc * 8;
+        ksrc[v] = kb + (size_t)row * 64 + pc * 8;
+        vsrc[v] = vb + (size_t)row * a.Fq + pc * 8;
+    }
+    auto gload = [&](int key0) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            rk[v] = ld16(ksrc[v] + (size_t)key0 * 64);
+            rv[v] = ld16(vsrc[v] + key0);
+        }
+    };
+    auto sstore = [&](int b) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            *reinterpret_cast<u32x4 *>(&ks[b][soff[v]]) = rk[v];
+            *reinterpret_cast<u32x4 *>(&vs[b][soff[v]]) = rv[v];
+        }
+    };
+
+    float mrow[4], lsum[4];
+    f32x4 o[4][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        mrow[s] = -INFINITY;
+        lsum[s] = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) o[dt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    const int steps = (a.F + 63) >> 6;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    for (int st = 0; st < steps; ++st) {
+        const int b = st & 1, key0 = st * 64;
+        if (st + 1 < steps) gload(key0 + 64);
+        f32x4 sc[4][4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+            const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&ks[b][(kt * 16 + r16) * AROW + g * 8]);
+            const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&ks[b][(kt * 16 + r16) * AROW + 32 + g * 8]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                sc[kt][s] = mfma_bf16_k32(k0, qf[s][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                sc[kt][s] = mfma_bf16_k32(k1, qf[s][1], sc[kt][s]);
+            }
+        }
+        if (key0 + 64 > a.F) {                       // the tail step: keys past F
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (key0 + kt * 16 + 4 * g + r >= a.F)
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) sc[kt][s][r] = -INFINITY;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float ml = sc[0][s][0];
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ml = fmaxf(ml, sc[kt][s][r]);
+            float x0, x1;
+            rows16_pair(ml, x0, x1);
+            ml = fmaxf(x0, x1);
+            halves32_pair(ml, x0, x1);
+            ml = fmaxf(x0, x1);
+            // every step holds a live key, so mnew is finite; the first step's
+            // mrow = -inf gives alpha = 0
+            const float mnew = fmaxf(mrow[s], ml);
+            const float ms = mnew * a.sl2e;
+            const float alpha = __builtin_amdgcn_exp2f(__fmaf_rn(mrow[s], a.sl2e, -ms));
+            mrow[s] = mnew;
+            float ps = 0.f;
+#pragma unroll
+            for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float sv = sc[kt][s][r];
+                    const float p = sv == -INFINITY ? 0.f
+                                                    : __builtin_amdgcn_exp2f(__fmaf_rn(sv, a.sl2e, -ms));
+                    sc[kt][s][r] = p;
+                    ps += p;
+                }
+            lsum[s] = __fmaf_rn(lsum[s], alpha, ps);
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) o[dt][s] = o[dt][s] * alpha;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            u32x4 pf[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                pf[s] = u32x4{pack_bf2(sc[2 * kk][s][0], sc[2 * kk][s][1]),
+                              pack_bf2(sc[2 * kk][s][2], sc[2 * kk][s][3]),
+                              pack_bf2(sc[2 * kk + 1][s][0], sc[2 * kk + 1][s][1]),
+                              pack_bf2(sc[2 * kk + 1][s][2], sc[2 * kk + 1][s][3])};
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) {
+                const uint16_t *vrow = &vs[b][(dt * 16 + r16) * AROW + kk * 32 + 4 * g];
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
+                const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) o[dt][s] = mfma_bf16_k32(vf, pf[s], o[dt][s]);
+            }
+        }
+        if (st + 1 < steps) sstore(b ^ 1);
+        __syncthreads();
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float l = lsum[s], x0, x1;
+        rows16_pair(l, x0, x1);
+        l = x0 + x1;
+        halves32_pair(l, x0, x1);
+        l = x0 + x1;
+        const float inv = 1.0f / l;
+        const int qi = q0 + 16 * s + r16;
+        if (qi >= a.F) continue;
+        uint16_t *dst = a.o + ((size_t)rq * a.F + qi) * a.d + h * 64 + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+            const f32x4 v = o[dt][s];
+            *reinterpret_cast<u32x2 *>(dst + dt * 16) =
+                u32x2{pack_bf2(v[0] * inv, v[1] * inv), pack_bf2(v[2] * inv, v[3] * inv)};
+        }
+    }
+}
+
+// Layer norm of fp32 rows (one wave per row, d <= 1280, d % 4 == 0) to bf16
+// rows at out + row * d.
+__global__ __launch_bounds__(256) void ln_kernel(const float *x, int M, int d, const uint16_t *gam,
+                                                 const uint16_t *bet, float eps, uint16_t *out) {
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= M) return;
+    const float *xr = x + (size_t)row * d;
+    float4 v[5];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int c = 4 * lane + 256 * i;
+        v[i] = c < d ? *reinterpret_cast<const float4 *>(xr + c) : float4{0.f, 0.f, 0.f, 0.f};
+        s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+    }
+    const float mean = wave_sum(s) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int c = 4 * lane + 256 * i;
+        if (c < d) {
+            const float t0 = v[i].x - mean, t1 = v[i].y - mean, t2 = v[i].z - mean, t3 = v[i].w - mean;
+            q = __fmaf_rn(t0, t0, q);
+            q = __fmaf_rn(t1, t1, q);
+            q = __fmaf_rn(t2, t2, q);
+            q = __fmaf_rn(t3, t3, q);
+        }
+    }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)d + eps);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        const int c = 4 * lane + 256 * i;
+        if (c < d) {
+            const float y0 = __fmaf_rn((v[i].x - mean) * rstd, bf2f(gam[c]), bf2f(bet[c]));
+            const float y1 = __fmaf_rn((v[i].y - mean) * rstd, bf2f(gam[c + 1]), bf2f(bet[c + 1]));
+            const float y2 = __fmaf_rn((v[i].z - mean) * rstd, bf2f(gam[c + 2]), bf2f(bet[c + 2]));
+            const float y3 = __fmaf_rn((v[i].w - mean) * rstd, bf2f(gam[c + 3]), bf2f(bet[c + 3]));
+            *reinterpret_cast<u32x2 *>(out + (size_t)row * d + c) = u32x2{pack_bf2(y0, y1), pack_bf2(y2, y3)};
+        }
+    }
+}
+
+// Features [n][C][T] (channel-major) to time-major rows melT[n][1 + t][C];
+// rows 0 and T + 1 of each request stay zero. One workgroup per (request,
+// 64 frames), staged through LDS (C <= 256).
+__global__ __launch_bounds__(256) void mel_kernel(const uint16_t *mel, int C, int T, uint16_t *melT) {
+    __shared__ uint16_t tile[64][257];
+    const int nb = (T + 63) >> 6;
+    const int rq = blockIdx.x / nb, t0 = (blockIdx.x - rq * nb) * 64;
+    const uint16_t *src = mel + (size_t)rq * C * T;
+    for (int e = threadIdx.x; e < C * 64; e += 256) {
+        const int c = e >> 6, t = e & 63;
+        if (t0 + t < T) tile[t][c] = src[(size_t)c * T + t0 + t];
+    }
+    __syncthreads();
+    uint16_t *dst = melT + ((size_t)rq * (T + 2) + 1 + t0) * C;
+    for (int e = threadIdx.x; e < C * 64; e += 256) {
+        const int t = e / C, c = e - t * C;
+        if (t0 + t < T) dst[(size_t)t * C + c] = tile[t][c];
+    }
+}
+
+// Convolution weight [out][in][3] (PyTorch Conv1d) to [out][tap][in], the
+// order of a time-major 3-row window.
+__global__ void conv_relayout_kernel(const uint16_t *w, int O, int I, uint16_t *wr) {
+    const size_t e = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (e >= (size_t)O * I * 3) return;
+    const int o = (int)(e / ((size_t)I * 3));
+    const int rem = (int)(e - (size_t)o * I * 3);
+    const int i = rem / 3, k = rem - i * 3;
+    wr[((size_t)o * 3 + k) * I + i] = w[e];
+}
+
+// Sinusoidal positions [F][d] in fp32: channel j < d/2 holds sin(t w_j),
+// channel d/2 + j holds cos(t w_j), w_j = 10000^(-j / (d/2 - 1)); the angle
+// is formed in fp64.
+__global__ void pos_kernel(int F, int d, float *pos) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= F * d) return;
+    const int t = e / d, c = e - t * d, hh = d / 2;
+    const int j = c < hh ? c : c - hh;
+    const double ang = (double)t * exp(-log(10000.0) * (double)j / (double)(hh - 1));
+    pos[e] = (float)(c < hh ? sin(ang) : cos(ang));
+}
+
+inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
+    a.n_m = cdiv(a.M, GBM);
+    a.n_n = cdiv(a.N, GBN);
+    a.n_wg = a.n_m * a.n_n;
+    const dim3 grid(cdiv(a.n_wg, 8) * 8), blk(256);
+    switch (epi) {
+    case EE_CONV1: hipLaunchKernelGGL(gemm_kernel<EE_CONV1>, grid, blk, 0, st, a); break;
+    case EE_CONV2: hipLaunchKernelGGL(gemm_kernel<EE_CONV2>, grid, blk, 0, st, a); break;
+    case EE_QKV: hipLaunchKernelGGL(gemm_kernel<EE_QKV>, grid, blk, 0, st, a); break;
+    case EE_RESID: hipLaunchKernelGGL(gemm_kernel<EE_RESID>, grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL(gemm_kernel<EE_GELU>, grid, blk, 0, st, a); break;
+    }
+    return hipGetLastError();
+}
+
+struct LayerW {
+    const uint16_t *ln1_g, *ln1_b, *wq, *bq, *wk, *wv, *bv, *wo, *bo;
+    const uint16_t *ln2_g, *ln2_b, *w1, *b1, *w2, *b2;
+};
+
+struct Layout {
+    size_t melT, g1, x, h, q, k, vt, o, hid, pos, w1r, w2r, total;
+};
+
+int f_q(const wf_enc_config *c) { return cdiv(c->n_frames, 256) * 256; }
+
+Layout layout_of(const wf_enc_config *c) {
+    Layout L{};
+    const size_t B = c->max_batch, F = c->n_frames, Tm = 2 * (size_t)c->n_frames, d = c->d_model;
+    const size_t Fq = f_q(c), H = c->n_heads;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+    };
+    L.melT = take(B * (Tm + 2) * c->n_mels * 2);
+    L.g1 = take(B * (Tm + 2) * d * 2);
+    L.x = take(B * F * d * 4);
+    L.h = take(B * F * d * 2);
+    L.q = take(B * H * Fq * 64 * 2);
+    L.k = take(B * H * Fq * 64 * 2);
+    L.vt = take(B * H * 64 * Fq * 2);
+    L.o = take(B * F * d * 2);
+    L.hid = take(B * F * c->d_ffn * 2);
+    L.pos = take(F * d * 4);
+    L.w1r = take(d * 3 * c->n_mels * 2);
+    L.w2r = take(d * 3 * d * 2);
+    L.total = off;
+    return L;
+}
+
+bool config_ok(const wf_enc_config *c, const char **why) {
+    const char *w = nullptr;
+    if (!c) w = "null config";
+    else if (c->n_layers < 1) w = "n_layers < 1";
+    else if (c->head_dim != 64) w = "head_dim must be 64";
+    else if (c->n_heads < 1 || c->n_heads * 64 != c->d_model) w = "d_model must be n_heads * 64";
+    else if (c->d_model > 1280) w = "d_model above 1280";
+    else if (c->d_ffn < 64 || c->d_ffn % 64) w = "d_ffn must be a positive multiple of 64";
+    else if (c->n_mels < 1 || c->n_mels > 256 || (3 * c->n_mels) % 32) w = "n_mels must be in [1, 256] with 3 n_mels a multiple of 32";
+    else if (c->n_frames < 1 || c->n_frames > 4096) w = "n_frames outside [1, 4096]";
+    else if (c->max_batch < 1 || (long long)c->max_batch * 2 * (c->n_frames + 1) > 0x3fffffff) w = "max_batch out of range";
+    else if (!(c->ln_eps > 0.f)) w = "ln_eps must be positive";
+    if (why) *why = w;
+    return w == nullptr;
+}
+
+}  // namespace enc
+}  // namespace wf
+
+using namespace wf::enc;
+
+struct wf_encoder {
+    wf_enc_config c;
+    Layout lay;
+    std::vector<LayerW> layers;
+    const uint16_t *c1b, *c2b, *lnp_g, *lnp_b;
+    uint16_t *melT, *g1, *h, *q, *k, *vt, *o, *hid, *w1r, *w2r;
+    float *x, *pos;
+    bool timing = false;
+    std::vector<hipEvent_t> ev_pool;
+    size_t ev_used = 0;
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> spans[WF_ENC_TK_N];
+};
+
+namespace {
+
+wf_status efail(wf_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    return wf::set_error(s, buf);
+}
+
+hipEvent_t next_event(wf_encoder *e) {
+    if (e->ev_used == e->ev_pool.size()) {
+        hipEvent_t ev;
+        if (hipEventCreateWithFlags(&ev, hipEventDisableSystemFence) != hipSuccess) return nullptr;
+        e->ev_pool.push_back(ev);
+    }
+    return e->ev_pool[e->ev_used++];
+}
+
+template <typename Fn>
+wf_status timed(wf_encoder *e, int kind, hipStream_t st, Fn &&launch) {
+    hipEvent_t a = nullptr, b = nullptr;
+    if (e->timing) {
+        a = next_event(e);
+        b = next_event(e);
+        if (a) (void)hipEventRecord(a, st);
+    }
+    const hipError_t err = launch();
+    if (err != hipSuccess) return efail(WF_EHIP, "kernel launch failed: %s", hipGetErrorString(err));
+    if (e->timing && a && b) {
+        (void)hipEventRecord(b, st);
+        e->spans[kind].push_back({a, b});
+    }
+    return WF_OK;
+}
+
+#define WFE_TRY(expr)                     \
+    do {                                  \
+        const wf_status _s = (expr);      \
+        if (_s != WF_OK) return _s;       \
+    } while (0)
+
+wf_status run_ln(wf_encoder *e, int M, const uint16_t *g, const uint16_t *b, uint16_t *out,
+                 hipStream_t st) {
+    const wf_enc_config &c = e->c;
+    return timed(e, WF_ENC_TK_LN, st, [&] {
+        hipLaunchKernelGGL(ln_kernel, dim3(cdiv(M, 4)), dim3(256), 0, st, e->x, M, c.d_model, g, b,
+                           c.ln_eps, out);
+        return hipGetLastError();
+    });
+}
+
+GemmArgs plain(const uint16_t *A, int M, int K, const uint16_t *W, const uint16_t *b, int N) {
+    GemmArgs a{};
+    a.A = A;
+    a.rpr = M;
+    a.sreq = 0;
+    a.srow = K;
+    a.W0 = a.W1 = a.W2 = W;
+    a.b0 = b;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.seg_n = N;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t wf_enc_workspace_bytes(const wf_enc_config *c) {
+    if (!config_ok(c, nullptr)) return 0;
+    return layout_of(c).total;
+}
+
+wf_status wf_enc_create(const wf_enc_config *cfg, const wf_enc_weights *w, void *workspace,
+                        size_t ws_bytes, wf_encoder **out) {
+    if (!out) return efail(WF_EINVAL, "out is null");
+    *out = nullptr;
+    const char *why = nullptr;
+    if (!config_ok(cfg, &why)) return efail(WF_ESHAPE, "bad encoder config: %s", why);
+    if (!w || !w->conv1_w || !w->conv1_b || !w->conv2_w || !w->conv2_b || !w->lnp_g || !w->lnp_b ||
+        !w->layers)
+        return efail(WF_EINVAL, "null encoder weight pointer");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const wf_enc_layer_weights &L = w->layers[l];
+        const void *ps[] = {L.ln1_g, L.ln1_b, L.wq, L.bq, L.wk, L.wv, L.bv, L.wo,
+                            L.bo,    L.ln2_g, L.ln2_b, L.w1, L.b1, L.w2, L.b2};
+        for (const void *p : ps)
+            if (!p) return efail(WF_EINVAL, "null weight pointer in encoder block %d", l);
+    }
+    if (!workspace) return efail(WF_EINVAL, "null workspace");
+    if (ws_bytes < wf_enc_workspace_bytes(cfg)) return efail(WF_ECAPACITY, "workspace too small");
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return efail(WF_EDEVICE, "no HIP device");
+    if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+        return efail(WF_EDEVICE, "device is %s, not gfx950", prop.gcnArchName);
+
+    wf_encoder *e = new wf_encoder();
+    e->c = *cfg;
+    e->lay = layout_of(cfg);
+    const Layout &L = e->lay;
+    char *ws = (char *)workspace;
+    e->melT = (uint16_t *)(ws + L.melT);
+    e->g1 = (uint16_t *)(ws + L.g1);
+    e->x = (float *)(ws + L.x);
+    e->h = (uint16_t *)(ws + L.h);
+    e->q = (uint16_t *)(ws + L.q);
+    e->k = (uint16_t *)(ws + L.k);
+    e->vt = (uint16_t *)(ws + L.vt);
+    e->o = (uint16_t *)(ws + L.o);
+    e->hid = (uint16_t *)(ws + L.hid);
+    e->pos = (float *)(ws + L.pos);
+    e->w1r = (uint16_t *)(ws + L.w1r);
+    e->w2r = (uint16_t *)(ws + L.w2r);
+    e->c1b = (const uint16_t *)w->conv1_b;
+    e->c2b = (const uint16_t *)w->conv2_b;
+    e->lnp_g = (const uint16_t *)w->lnp_g;
+    e->lnp_b = (const uint16_t *)w->lnp_b;
+    e->layers.resize(cfg->n_layers);
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const wf_enc_layer_weights &s = w->layers[l];
+        e->layers[l] = LayerW{(const uint16_t *)s.ln1_g, (const uint16_t *)s.ln1_b,
+                              (const uint16_t *)s.wq,    (const uint16_t *)s.bq,
+                              (const uint16_t *)s.wk,    (const uint16_t *)s.wv,
+                              (const uint16_t *)s.bv,    (const uint16_t *)s.wo,
+                              (const uint16_t *)s.bo,    (const uint16_t *)s.ln2_g,
+                              (const uint16_t *)s.ln2_b, (const uint16_t *)s.w1,
+                              (const uint16_t *)s.b1,    (const uint16_t *)s.w2,
+                              (const uint16_t *)s.b2};
+    }
+    // zero padding everywhere (the convolution borders and the padded frames
+    // of q / k / v^T are never written), then the position table and the
+    // convolution weights in window order
+    const int d = cfg->d_model, F = cfg->n_frames;
+    bool ok = hipMemset(workspace, 0, L.total) == hipSuccess;
+    if (ok) {
+        hipLaunchKernelGGL(pos_kernel, dim3(cdiv(F * d, 256)), dim3(256), 0, 0, F, d, e->pos);
+        hipLaunchKernelGGL(conv_relayout_kernel, dim3(cdiv(d * cfg->n_mels * 3, 256)), dim3(256), 0, 0,
+                           (const uint16_t *)w->conv1_w, d, cfg->n_mels, e->w1r);
+        hipLaunchKernelGGL(conv_relayout_kernel, dim3(cdiv(d * d * 3, 256)), dim3(256), 0, 0,
+                           (const uint16_t *)w->conv2_w, d, d, e->w2r);
+        ok = hipGetLastError() == hipSuccess && hipDeviceSynchronize() == hipSuccess;
+    }
+    if (!ok) {
+        delete e;
+        return efail(WF_EHIP, "preparing the encoder workspace failed");
+    }
+    *out = e;
+    return WF_OK;
+}
+
+void wf_enc_destroy(wf_encoder *e) {
+    if (!e) return;
+    for (hipEvent_t ev : e->ev_pool) (void)hipEventDestroy(ev);
+    delete e;
+}
+
+wf_status wf_encode(wf_encoder *e, int32_t n, const void *d_mel, void *d_out, void *stream) {
+    if (!e || !d_mel || !d_out) return efail(WF_EINVAL, "null argument");
+    const wf_enc_config &c = e->c;
+    if (n < 1 || n > c.max_batch) return efail(WF_ECAPACITY, "n outside [1, max_batch]");
+    hipStream_t st = (hipStream_t)stream;
+    const int d = c.d_model, F = c.n_frames, Tm = 2 * F, H = c.n_heads, Fq = f_q(&c);
+    const int M = n * F;
+    WFE_TRY(timed(e, WF_ENC_TK_OTHER, st, [&] {
+        hipLaunchKernelGGL(mel_kernel, dim3(n * cdiv(Tm, 64)), dim3(256), 0, st,
+                           (const uint16_t *)d_mel, c.n_mels, Tm, e->melT);
+        return hipGetLastError();
+    }));
+    {   // stem: conv1 (stride 1) into padded rows, conv2 (stride 2) + positions
+        GemmArgs a = plain(e->melT, n * Tm, 3 * c.n_mels, e->w1r, e->c1b, d);
+        a.rpr = Tm;
+        a.sreq = (long long)(Tm + 2) * c.n_mels;
+        a.srow = c.n_mels;
+        a.out = e->g1;
+        a.Tm = Tm;
+        WFE_TRY(timed(e, WF_ENC_TK_STEM, st, [&] { return launch_gemm(EE_CONV1, a, st); }));
+        GemmArgs b = plain(e->g1, M, 3 * d, e->w2r, e->c2b, d);
+        b.rpr = F;
+        b.sreq = (long long)(Tm + 2) * d;
+        b.srow = 2 * d;
+        b.x = e->x;
+        b.pos = e->pos;
+        b.F = F;
+        WFE_TRY(timed(e, WF_ENC_TK_STEM, st, [&] { return launch_gemm(EE_CONV2, b, st); }));
+    }
+    for (int l = 0; l < c.n_layers; ++l) {
+        const LayerW &w = e->layers[l];
+        WFE_TRY(run_ln(e, M, w.ln1_g, w.ln1_b, e->h, st));
+        GemmArgs a = plain(e->h, M, d, w.wq, w.bq, 3 * d);
+        a.W1 = w.wk;
+        a.W2 = w.wv;
+        a.b1 = nullptr;
+        a.b2 = w.bv;
+        a.seg_n = d;
+        a.q = e->q;
+        a.k = e->k;
+        a.vt = e->vt;
+        a.H = H;
+        a.Fq = Fq;
+        a.F = F;
+        WFE_TRY(timed(e, WF_ENC_TK_QKV, st, [&] { return launch_gemm(EE_QKV, a, st); }));
+        AttnArgs t{};
+        t.q = e->q;
+        t.k = e->k;
+        t.vt = e->vt;
+        t.o = e->o;
+        t.H = H;
+        t.F = F;
+        t.Fq = Fq;
+        t.d = d;
+        t.n_qt = Fq / 256;
+        t.n_wg = n * H * t.n_qt;
+        t.sl2e = 1.4426950408889634f / 8.0f;
+        WFE_TRY(timed(e, WF_ENC_TK_ATTN, st, [&] {
+            hipLaunchKernelGGL(attn_kernel, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
+            return hipGetLastError();
+        }));
+        GemmArgs ob = plain(e->o, M, d, w.wo, w.bo, d);
+        ob.x = e->x;
+        WFE_TRY(timed(e, WF_ENC_TK_OPROJ, st, [&] { return launch_gemm(EE_RESID, ob, st); }));
+        WFE_TRY(run_ln(e, M, w.ln2_g, w.ln2_b, e->h, st));
+        GemmArgs f1 = plain(e->h, M, d, w.w1, w.b1, c.d_ffn);
+        f1.out = e->hid;
+        WFE_TRY(timed(e, WF_ENC_TK_FC1, st, [&] { return launch_gemm(EE_GELU, f1, st); }));
+        GemmArgs f2 = plain(e->hid, M, c.d_ffn, w.w2, w.b2, d);
+        f2.x = e->x;
+        WFE_TRY(timed(e, WF_ENC_TK_FC2, st, [&] { return launch_gemm(EE_RESID, f2, st); }));
+    }
+    return run_ln(e, M, e->lnp_g, e->lnp_b, (uint16_t *)d_out, st);
+}
+
+wf_status wf_enc_set_timing(wf_encoder *e, int32_t enable) {
+    if (!e) return efail(WF_EINVAL, "null encoder");
+    e->timing = enable != 0;
+    for (auto &v : e->spans) v.clear();
+    e->ev_used = 0;
+    return WF_OK;
+}
+
+wf_status wf_enc_get_timing(wf_encoder *e, int32_t kind, double *total_ms, int32_t *count) {
+    if (!e || !total_ms || !count) return efail(WF_EINVAL, "null argument");
+    if (kind < 0 || kind >= WF_ENC_TK_N) return efail(WF_EINVAL, "unknown timing kind");
+    double tot = 0;
+    for (auto &p : e->spans[kind]) {
+        if (hipEventSynchronize(p.second) != hipSuccess) return efail(WF_EHIP, "event synchronize failed");
+        float ms = 0;
+        if (hipEventElapsedTime(&ms, p.first, p.second) != hipSuccess)
+            return efail(WF_EHIP, "elapsed time failed");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *count = (int32_t)e->spans[kind].size();
+    return WF_OK;
+}
+
+}  // extern "C"

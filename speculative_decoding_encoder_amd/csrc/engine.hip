@@ -415,6 +415,11 @@ void read_tile_override(wf_engine *e) {
 
 }  // namespace
 
+// Error message setter shared with the encoder's host code.
+namespace wf {
+wf_status set_error(wf_status s, const char *msg) { return fail(s, "%s", msg); }
+}  // namespace wf
+
 extern "C" {
 
 size_t wf_kv_pool_bytes(const wf_config *c) {

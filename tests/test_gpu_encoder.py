@@ -1,0 +1,126 @@
+"""GPU audio encoder (wf_encode) through the C ABI against the CPU oracle
+(oracle/encoder.py).
+
+* Small shape (2 blocks, width 128, 2 heads of 64, 100 frames from 200
+  feature frames, perturbed norm gains): three requests, every output
+  against the oracle's fp64 forward.
+* Full large-v3 width (1280, 20 heads, MLP 5120, 128 mel channels, 1500
+  frames) with 2 blocks: one request against the oracle, and batch
+  invariance (a request encoded inside a batch of two equals the same
+  request alone, bit for bit: no kernel mixes requests or depends on the
+  batch size).
+* The full 32-block encoder: finite outputs whose rows have mean 0 and
+  variance 1 (the final norm with unit gain), and the audio memory it
+  produces drives wf_encode_kv and a verify pass.
+
+Tolerance. The GPU keeps the residual stream, norms, softmax and GELU in
+fp32 but hands bf16 activations between kernels (norm outputs, q, k, v,
+attention output and probabilities, MLP hidden, convolution outputs):
+about a dozen roundings of relative size <= 2^-9 on every path through a
+block. On unit-variance outputs whose largest values are about 5 that
+bounds the error near 5 * 2^-9 * sqrt(12) ~ 3.4e-2; the test allows 5e-2
+max and 5e-3 root-mean-square per request.
+"""
+import numpy as np
+import pytest
+
+from gpu_common import log
+from oracle import encoder as oe
+from synthetic import (ENC_LARGE_V3, ENC_SMALL, bf16_bits_to_f32, make_encoder_weights,
+                       make_mel)
+
+pytestmark = pytest.mark.gpu
+
+ENC_MAX_TOL = 5e-2
+ENC_RMS_TOL = 5e-3
+
+
+@pytest.fixture(scope="module")
+def torch_cuda():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _encode(torch, enc, mels):
+    d_mel = enc.bf16(np.stack(mels))
+    out = torch.empty((len(mels), enc.shape.n_frames, enc.shape.d_model), dtype=torch.int16,
+                      device=enc.dev)
+    enc.wf_encode(d_mel, out)
+    torch.cuda.synchronize()
+    return bf16_bits_to_f32(out.cpu().numpy().view(np.uint16))
+
+
+def _close(got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    mx, rms = float(err.max()), float(np.sqrt((err ** 2).mean()))
+    log(f"[parity] {what}: max {mx:.3e} rms {rms:.3e}")
+    assert mx <= ENC_MAX_TOL and rms <= ENC_RMS_TOL, (what, mx, rms)
+
+
+def test_small_encoder_against_the_oracle(torch_cuda):
+    from speculative_decoding_encoder_amd.binding import Encoder
+    s = ENC_SMALL
+    wb = make_encoder_weights(s, 0, ln_random=True)
+    enc = Encoder(s, wb, max_batch=3)
+    mels = [make_mel(s, 0, r) for r in range(3)]
+    got = _encode(torch_cuda, enc, mels)
+    ref = oe.Encoder(s, wb)
+    for r in range(3):
+        _close(got[r], ref.forward(mels[r]), f"small encoder req {r}")
+    enc.close()
+
+
+def test_large_width_two_blocks_and_batch_invariance(torch_cuda):
+    import dataclasses
+    from speculative_decoding_encoder_amd.binding import Encoder
+    s = dataclasses.replace(ENC_LARGE_V3, n_layers=2)
+    wb = make_encoder_weights(s, 1)
+    enc = Encoder(s, wb, max_batch=2)
+    mels = [make_mel(s, 1, r) for r in range(2)]
+    both = _encode(torch_cuda, enc, mels)
+    alone = _encode(torch_cuda, enc, mels[1:])
+    assert np.array_equal(both[1].view(np.uint32), alone[0].view(np.uint32))
+    log("large-width encoder: request 1 in a batch of 2 equals request 1 alone")
+    _close(both[0], oe.Encoder(s, wb).forward(mels[0]), "large-width 2-block encoder req 0")
+    enc.close()
+
+
+def test_full_encoder_feeds_the_decoder(torch_cuda):
+    import dataclasses
+    from speculative_decoding_encoder_amd.binding import Encoder, Engine
+    from synthetic import TURBO, WORKLOADS, make_prefixes, make_weights
+    torch = torch_cuda
+    s = ENC_LARGE_V3
+    wb = make_encoder_weights(s, 2)
+    enc = Encoder(s, wb, max_batch=2)
+    mels = [make_mel(s, 2, r) for r in range(2)]
+    d_mel = enc.bf16(np.stack(mels))
+    out = torch.empty((2, s.n_frames, s.d_model), dtype=torch.int16, device=enc.dev)
+    enc.wf_encode(d_mel, out)
+    torch.cuda.synchronize()
+    y = bf16_bits_to_f32(out.cpu().numpy().view(np.uint16)).astype(np.float64)
+    assert np.isfinite(y).all()
+    np.testing.assert_allclose(y.mean(axis=-1), 0.0, atol=2e-2)
+    np.testing.assert_allclose(y.var(axis=-1), 1.0, atol=3e-2)
+    log(f"full encoder: |row mean| <= {np.abs(y.mean(-1)).max():.2e}, "
+        f"row var in [{y.var(-1).min():.4f}, {y.var(-1).max():.4f}]")
+    # the audio memory goes straight into the decoder's write-once cross K/V
+    wl = WORKLOADS[2]
+    shape = dataclasses.replace(TURBO, n_layers=2)
+    eng = Engine(shape, make_weights(shape, wl.cfg_id), max_batch=2, max_rows=2 * 64)
+    slots = eng.i32([0, 1])
+    eng.wf_encode_kv(slots, out)
+    prefixes = [p[:20] for p in make_prefixes(wl, 2)]
+    T = max(len(p) for p in prefixes)
+    toks = np.zeros((2, T), np.int32)
+    for b, p in enumerate(prefixes):
+        toks[b, :len(p)] = p
+    am = torch.empty((2, T), dtype=torch.int32, device=eng.dev)
+    eng.wf_verify_block(slots, eng.i32(toks), eng.i32([len(p) for p in prefixes]), am)
+    torch.cuda.synchronize()
+    err, _ = eng.wf_device_state()
+    assert (err == 0).all() and (am.cpu().numpy()[0, :len(prefixes[0])] >= 0).all()
+    eng.close()
+    enc.close()
