@@ -26,6 +26,10 @@ timing. Tokens per second count the tokens a round emits, sum over requests
 of (accepted + 1); audio seconds per second divide that by 3.5 tokens per
 audio second (the tokens-to-audio ratio of Whisper-Flash Table 1).
 
+``--encoder N`` instead times the audio encoder (wf_encode: N log-mel windows
+of 30 s through the 32-block large-v3 encoder) and prints its own line in
+audio seconds per second, with the bf16 MFMA roofline of its dominant kernel.
+
 The timed loop replays one HIP graph per step. Kernel durations for the
 roofline come from HIP events around every launch over a second pass of the
 same steps; the dominant kernel is the one with the largest total time.
@@ -471,6 +475,127 @@ def k_sweep(args):
                       "warmup": args.warmup, "graph": not args.no_graph}), flush=True)
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+ENC_AUDIO_S = 30.0              # one encoder window is 30 s of audio
+ENC_SYMBOL = {"stem": "wf::enc::gemm_kernel<0|1>", "qkv": "wf::enc::gemm_kernel<2>",
+              "attn": "wf::enc::attn_kernel", "oproj": "wf::enc::gemm_kernel<3>",
+              "fc1": "wf::enc::gemm_kernel<4>", "fc2": "wf::enc::gemm_kernel<3>",
+              "ln": "wf::enc::ln_kernel", "other": "wf::enc::mel_kernel"}
+
+
+def encoder_flops(s, n: int) -> dict:
+    """Algorithmic flops per kind for n windows (2 per multiply-add): the two
+    stem convolutions, and per block the QKV, attention (QK^T and PV), output
+    and MLP products."""
+    F, d, f, L, Tm = s.n_frames, s.d_model, s.d_ffn, s.n_layers, 2 * s.n_frames
+    return {"stem": 2 * n * (Tm * 3 * s.n_mels * d + F * 3 * d * d),
+            "qkv": 2 * n * L * F * d * 3 * d, "attn": 4 * n * L * F * F * d,
+            "oproj": 2 * n * L * F * d * d, "fc1": 2 * n * L * F * d * f,
+            "fc2": 2 * n * L * F * f * d}
+
+
+def encoder_cpu_baseline(s, wb, timed_s: float = 12.0) -> dict:
+    """The oracle encoder (fp64 numpy) on a bounded sample: the stem and as
+    many blocks of one window as fit in about ``timed_s`` seconds; the
+    window's time is the stem plus n_layers times the mean block time."""
+    from oracle import encoder as oe
+    from synthetic import bf16_bits_to_f32, make_mel
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    e = oe.Encoder(s, wb)
+    mel = make_mel(s, 0, 0)
+    t0 = time.perf_counter()
+    x = e.stem(bf16_bits_to_f32(mel).astype(np.float64))
+    t_stem = time.perf_counter() - t0
+    t_blocks, nb = 0.0, 0
+    while nb < s.n_layers and (nb == 0 or t_stem + t_blocks < timed_s):
+        t0 = time.perf_counter()
+        x = e.block(nb, x)
+        t_blocks += time.perf_counter() - t0
+        nb += 1
+    t_window = t_stem + s.n_layers * t_blocks / nb
+    return {"value": round(ENC_AUDIO_S / t_window, 4), "unit": "audio-s/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one 30 s window: the stem and {nb} of {s.n_layers} blocks timed "
+                      f"({t_stem + t_blocks:.2f} s, fp64 numpy), the window's time taken as the "
+                      f"stem plus {s.n_layers} x the mean block time ({t_window:.1f} s)"}
+
+
+def encoder_bench(args):
+    """The audio encoder (30 s log-mel windows through the 32-block large-v3
+    encoder) on --encoder windows: its own JSON line."""
+    import torch
+    from synthetic import ENC_LARGE_V3, make_encoder_weights, make_mel
+    from speculative_decoding_encoder_amd.binding import ENC_TIMING_KINDS, Encoder
+    s = ENC_LARGE_V3
+    n = args.encoder
+    wb = make_encoder_weights(s, 0)
+    enc = Encoder(s, wb, max_batch=n)
+    mel = enc.bf16(np.stack([make_mel(s, 0, r) for r in range(n)]))
+    out_t = torch.empty((n, s.n_frames, s.d_model), dtype=torch.int16, device=enc.dev)
+    st = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        enc.wf_encode(mel, out_t, st)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        enc.wf_encode(mel, out_t, st)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] encoder n = {n}: {ms:.3f} ms per call")
+    # per-kind launch durations (HIP events on the launch stream), one call
+    enc.set_timing(True)
+    enc.wf_encode(mel, out_t, st)
+    torch.cuda.synchronize()
+    tk = enc.timing()
+    enc.set_timing(False)
+    fl = encoder_flops(s, n)
+    kinds = {}
+    for k in ENC_TIMING_KINDS:
+        tot, cnt = tk[k]
+        if cnt == 0:
+            continue
+        row = {"ms": round(tot, 4), "launches": cnt, "avg_us": round(tot * 1e3 / cnt, 2)}
+        if k in fl and tot > 0:
+            row["tflops"] = round(fl[k] / (tot * 1e-3) / 1e12, 1)
+        kinds[k] = row
+    dom = max((k for k in kinds if k in fl), key=lambda k: kinds[k]["ms"])
+    per_launch = fl[dom] / kinds[dom]["launches"]
+    achieved = per_launch / (kinds[dom]["avg_us"] * 1e-6) / 1e12
+    total_flop = sum(fl.values())
+    res = {
+        "metric": "encoder audio-s/sec (30 s log-mel windows, 32-block large-v3 encoder); "
+                  "% bf16 MFMA roofline",
+        "value": round(n * ENC_AUDIO_S / (ms * 1e-3), 2), "unit": "audio-s/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "precision": "bf16 MFMA operands and activations between kernels, fp32 accumulate, "
+                     "fp32 residual stream, layer norms, softmax and GELU",
+        "data": "synthetic (seeded weights N(0,0.02) in bf16, log-mel features N(0,1))",
+        "config": {"workload": f"large-v3 encoder, {n} x 30 s windows", "layers": s.n_layers,
+                   "d_model": s.d_model, "n_mels": s.n_mels, "frames": s.n_frames, "batch": n},
+        "tflops": round(total_flop / (ms * 1e-3) / 1e12, 1),
+        "mfma_frac": round(total_flop / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {"bound": "mfma", "kernel": dom, "symbol": ENC_SYMBOL[dom],
+                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "flop_per_launch": per_launch,
+                     "avg_us": kinds[dom]["avg_us"]},
+        "kernels": kinds,
+    }
+    if not args.no_cpu:
+        t0 = time.time()
+        res["cpu_baseline"] = encoder_cpu_baseline(s, wb)
+        log(f"[bench] encoder cpu baseline took {time.time() - t0:.1f}s")
+    enc.close()
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -493,6 +618,8 @@ def main():
                          "readout at this decoder layer in every verify pass")
     ap.add_argument("--batch", type=int, default=0,
                     help="with --k-sweep: this many requests instead of the workload's")
+    ap.add_argument("--encoder", type=int, default=0,
+                    help="time the audio encoder on this many 30 s windows instead (own JSON line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run device-to-device copies of this size (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
@@ -507,6 +634,9 @@ def main():
     K, W = args.steps, args.warmup
     if args.k_sweep:
         k_sweep(args)
+        return
+    if args.encoder:
+        encoder_bench(args)
         return
     w = Workload(args.config, greedy=args.greedy)
     r = measure(w, K, W, use_graph=not args.no_graph)

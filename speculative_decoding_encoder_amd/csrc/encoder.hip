@@ -71,8 +71,11 @@ constexpr int GBM = 128, GBN = 256, GBK = 32, GROW = 40;
 __device__ __forceinline__ float gelu(float t) {
     return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
 }
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// Two floats to packed bf16, round to nearest even (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bias4(const uint16_t *b, int c, int r) {
     return b ? bf2f(b[c + r]) : 0.0f;
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
                 } else {
                     uint16_t *dst = a.vt + (bh * 64 + dim) * a.Fq + t;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(size_t)r * a.Fq] = f2bf(y[r]);
+                    for (int r = 0; r < 4; ++r) dst[(size_t)r * a.Fq] = (uint16_t)(pack_bf2(y[r], 0.f) & 0xffffu);
                 }
             }
         }
@@ -296,40 +299,51 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
     for (int st = 0; st < steps; ++st) {
         const int b = st & 1, key0 = st * 64;
         if (st + 1 < steps) gload(key0 + 64);
-        f32x4 sc[4][4];
+        // fragments of this step, shared by the four query subtiles
+        u32x4 kf[4][2], vf[4][2];
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-            const u32x4 k0 = *reinterpret_cast<const u32x4 *>(&ks[b][(kt * 16 + r16) * AROW + g * 8]);
-            const u32x4 k1 = *reinterpret_cast<const u32x4 *>(&ks[b][(kt * 16 + r16) * AROW + 32 + g * 8]);
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                sc[kt][s] = mfma_bf16_k32(k0, qf[s][0], f32x4{0.f, 0.f, 0.f, 0.f});
-                sc[kt][s] = mfma_bf16_k32(k1, qf[s][1], sc[kt][s]);
+            for (int kk = 0; kk < 2; ++kk)
+                kf[kt][kk] = *reinterpret_cast<const u32x4 *>(&ks[b][(kt * 16 + r16) * AROW + kk * 32 + g * 8]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const uint16_t *vrow = &vs[b][(dt * 16 + r16) * AROW + kk * 32 + 4 * g];
+                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
+                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
+                vf[dt][kk] = u32x4{lo[0], lo[1], hi[0], hi[1]};
             }
-        }
-        if (key0 + 64 > a.F) {                       // the tail step: keys past F
-#pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (key0 + kt * 16 + 4 * g + r >= a.F)
-#pragma unroll
-                        for (int s = 0; s < 4; ++s) sc[kt][s][r] = -INFINITY;
-        }
+        const bool tail = key0 + 64 > a.F;
+        // one subtile at a time (scores, softmax, PV), so one subtile's VALU
+        // work can overlap the next one's MFMAs
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            float ml = sc[0][s][0];
+            f32x4 sc[4];
 #pragma unroll
-            for (int kt = 0; kt < 4; ++kt)
+            for (int kt = 0; kt < 4; ++kt) {
+                sc[kt] = mfma_bf16_k32(kf[kt][0], qf[s][0], f32x4{0.f, 0.f, 0.f, 0.f});
+                sc[kt] = mfma_bf16_k32(kf[kt][1], qf[s][1], sc[kt]);
+            }
+            if (tail) {                                  // keys past F
 #pragma unroll
-                for (int r = 0; r < 4; ++r) ml = fmaxf(ml, sc[kt][s][r]);
+                for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (key0 + kt * 16 + 4 * g + r >= a.F) sc[kt][r] = -INFINITY;
+            }
+            float ml = fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3]));
+#pragma unroll
+            for (int kt = 1; kt < 4; ++kt)
+                ml = fmaxf(ml, fmaxf(fmaxf(sc[kt][0], sc[kt][1]), fmaxf(sc[kt][2], sc[kt][3])));
             float x0, x1;
             rows16_pair(ml, x0, x1);
             ml = fmaxf(x0, x1);
             halves32_pair(ml, x0, x1);
             ml = fmaxf(x0, x1);
             // every step holds a live key, so mnew is finite; the first step's
-            // mrow = -inf gives alpha = 0
+            // mrow = -inf gives alpha = 0, a masked score exp2(-inf) = 0
             const float mnew = fmaxf(mrow[s], ml);
             const float ms = mnew * a.sl2e;
             const float alpha = __builtin_amdgcn_exp2f(__fmaf_rn(mrow[s], a.sl2e, -ms));
@@ -339,33 +353,22 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float sv = sc[kt][s][r];
-                    const float p = sv == -INFINITY ? 0.f
-                                                    : __builtin_amdgcn_exp2f(__fmaf_rn(sv, a.sl2e, -ms));
-                    sc[kt][s][r] = p;
+                    const float p = __builtin_amdgcn_exp2f(__fmaf_rn(sc[kt][r], a.sl2e, -ms));
+                    sc[kt][r] = p;
                     ps += p;
                 }
             lsum[s] = __fmaf_rn(lsum[s], alpha, ps);
 #pragma unroll
-            for (int dt = 0; dt < 4; ++dt) o[dt][s] = o[dt][s] * alpha;
-        }
+            for (int kk = 0; kk < 2; ++kk) {
+                const u32x4 pf = u32x4{pack_bf2(sc[2 * kk][0], sc[2 * kk][1]),
+                                       pack_bf2(sc[2 * kk][2], sc[2 * kk][3]),
+                                       pack_bf2(sc[2 * kk + 1][0], sc[2 * kk + 1][1]),
+                                       pack_bf2(sc[2 * kk + 1][2], sc[2 * kk + 1][3])};
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            u32x4 pf[4];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                pf[s] = u32x4{pack_bf2(sc[2 * kk][s][0], sc[2 * kk][s][1]),
-                              pack_bf2(sc[2 * kk][s][2], sc[2 * kk][s][3]),
-                              pack_bf2(sc[2 * kk + 1][s][0], sc[2 * kk + 1][s][1]),
-                              pack_bf2(sc[2 * kk + 1][s][2], sc[2 * kk + 1][s][3])};
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-                const uint16_t *vrow = &vs[b][(dt * 16 + r16) * AROW + kk * 32 + 4 * g];
-                const u32x2 lo = *reinterpret_cast<const u32x2 *>(vrow);
-                const u32x2 hi = *reinterpret_cast<const u32x2 *>(vrow + 16);
-                const u32x4 vf = u32x4{lo[0], lo[1], hi[0], hi[1]};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) o[dt][s] = mfma_bf16_k32(vf, pf[s], o[dt][s]);
+                for (int dt = 0; dt < 4; ++dt) {
+                    if (kk == 0) o[dt][s] = o[dt][s] * alpha;
+                    o[dt][s] = mfma_bf16_k32(vf[dt][kk], pf, o[dt][s]);
+                }
             }
         }
         if (st + 1 < steps) sstore(b ^ 1);
