@@ -588,6 +588,16 @@ def encoder_bench(args):
                      "avg_us": kinds[dom]["avg_us"]},
         "kernels": kinds,
     }
+    res["roofline"]["traffic"] = traffic_of(res["config"]["workload"], dom)
+    if args.calib_copy_mib:
+        nb = args.calib_copy_mib << 20
+        src = torch.ones(nb, dtype=torch.uint8, device=enc.dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["calib_copy_bytes"] = nb
+        del src, dst
     if not args.no_cpu:
         t0 = time.time()
         res["cpu_baseline"] = encoder_cpu_baseline(s, wb)
