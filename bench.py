@@ -414,7 +414,7 @@ def traffic_of(workload: str, symbol_kind: str):
             entries = json.load(f)
     except (OSError, ValueError):
         return None
-    h = kernel_source_hash()
+    h = kernel_source_hash(workload)
     for ent in entries:
         if ent.get("workload") == workload and ent.get("kind") == symbol_kind \
                 and ent.get("source_hash") == h:
@@ -422,16 +422,31 @@ def traffic_of(workload: str, symbol_kind: str):
     return None
 
 
-def kernel_source_hash() -> str:
-    """sha256 over the kernel sources (csrc/*.hip, csrc/*.h), in name order."""
+ENCODER_SOURCES = ("encoder.hip", "wf_device.h")
+
+
+def kernel_source_hash(workload: str = "") -> str:
+    """sha256 over the kernel sources of a workload, in name order: the
+    encoder's (encoder.hip and the device helpers) for an encoder workload,
+    every other csrc/*.hip and csrc/*.h for the verify path."""
     import hashlib
     csrc = os.path.join(ROOT, "speculative_decoding_encoder_amd", "csrc")
+    enc = is_encoder_workload(workload)
     hsh = hashlib.sha256()
     for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                hsh.update(name.encode() + b"\0" + f.read())
+        if not name.endswith((".hip", ".h")):
+            continue
+        if enc and name not in ENCODER_SOURCES:
+            continue
+        if not enc and name == "encoder.hip":
+            continue
+        with open(os.path.join(csrc, name), "rb") as f:
+            hsh.update(name.encode() + b"\0" + f.read())
     return hsh.hexdigest()[:16]
+
+
+def is_encoder_workload(workload: str) -> bool:
+    return "encoder" in workload
 
 
 def summary(w: "Workload", r: dict) -> dict:

@@ -9,7 +9,7 @@
       dispatch), each scaled by what the counter reads for the largest buffer
       copy in the run (COPY_BYTES read and written); appends the figure to
       profiles/hbm_traffic.json, keyed by workload, kernel kind and a hash of
-      the kernel sources, and writes a text summary to OUT_TXT.
+      the workload's kernel sources, and writes a text summary to OUT_TXT.
 """
 from __future__ import annotations
 
@@ -82,7 +82,7 @@ def traffic(fdir, wdir, workload, kind, symbol, copy_bytes, out_txt, cmd):
     w_b = sum(kw) / len(kw) * 1024.0 * sw
     sys.path.insert(0, ROOT)
     from bench import kernel_source_hash
-    h = kernel_source_hash()
+    h = kernel_source_hash(workload)
     ent = {"workload": workload, "kind": kind, "symbol": symbol, "dispatches": len(kf),
            "fetch_kib_avg": sum(kf) / len(kf), "write_kib_avg": sum(kw) / len(kw),
            "fetch_scale": sf, "write_scale": sw, "hbm_bytes_per_launch": f_b + w_b,
