@@ -47,7 +47,7 @@ wf_status set_error(wf_status s, const char *msg);   // engine.hip (wf_last_erro
 namespace wf {
 namespace enc {
 
-enum { EE_CONV1 = 0, EE_CONV2 = 1, EE_QKV = 2, EE_RESID = 3, EE_GELU = 4 };
+enum { EE_CONV1 = 0, EE_CONV2 = 1, EE_QKV = 2, EE_RESID = 3, EE_GELU = 4, EE_XKV = 5 };
 
 struct GemmArgs {
     const uint16_t *A;                 // bf16; row m at A + (m / rpr) * sreq + (m % rpr) * srow
@@ -64,6 +64,12 @@ struct GemmArgs {
     int F, Tm;                         // frames and feature frames per request
     uint16_t *q, *k, *vt;              // EE_QKV
     int H, Fq;                         // heads; frames padded to the query tile
+    // EE_XKV: a decoder layer's cross K (segment 0) and V (segment 1, bias b1)
+    // into the write-once pool, fp16, in its per-head layouts
+    uint16_t *xkv;
+    long long slot_stride, layer_off;
+    const int32_t *slots;
+    int F_pad, hd, max_batch;
 };
 
 constexpr int GBM = 128, GBN = 256, GBK = 32, GROW = 40;
@@ -203,6 +209,23 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
                 xv.z = gelu(c[2] + bias4(a.b0, n, 2)) + pv.z;
                 xv.w = gelu(c[3] + bias4(a.b0, n, 3)) + pv.w;
                 *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = xv;
+            } else if constexpr (EPI == EE_XKV) {
+                const int rq = m / a.F, f = m - rq * a.F;
+                const int slot = a.slots[rq];
+                if (slot < 0 || slot >= a.max_batch) continue;   // skipped request
+                const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
+                const int h = cc / a.hd, dim = cc - h * a.hd;
+                uint16_t *base = a.xkv + (size_t)slot * a.slot_stride + a.layer_off +
+                                 (size_t)(seg * a.H + h) * a.F_pad * a.hd;
+                if (seg == 0) {   // K: the four dims are adjacent in the fragment order
+                    *reinterpret_cast<u32x2 *>(base + xk_index(f, dim, a.hd)) =
+                        u32x2{pack_h2(c[0], c[1]), pack_h2(c[2], c[3])};
+                } else {          // V: [hd][32] per 32-frame step, frame at xv_pos
+                    uint16_t *vb = base + (size_t)(f >> 5) * a.hd * 32 + xv_pos(f & 31);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        vb[(size_t)(dim + r) * 32] = f2h_bits(c[r] + bias4(a.b1, cc, r));
+                }
             } else {   // EE_QKV
                 const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
                 const int h = cc >> 6, dim = cc & 63;
@@ -492,10 +515,45 @@ hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
     case EE_CONV2: hipLaunchKernelGGL(gemm_kernel<EE_CONV2>, grid, blk, 0, st, a); break;
     case EE_QKV: hipLaunchKernelGGL(gemm_kernel<EE_QKV>, grid, blk, 0, st, a); break;
     case EE_RESID: hipLaunchKernelGGL(gemm_kernel<EE_RESID>, grid, blk, 0, st, a); break;
+    case EE_XKV: hipLaunchKernelGGL(gemm_kernel<EE_XKV>, grid, blk, 0, st, a); break;
     default: hipLaunchKernelGGL(gemm_kernel<EE_GELU>, grid, blk, 0, st, a); break;
     }
     return hipGetLastError();
 }
+
+}  // namespace enc
+
+// A decoder layer's cross K = enc W_k^T and V = enc W_v^T + b_v for n
+// requests (enc bf16 [n][F][K] rows), written in fp16 into each request's
+// slot of the write-once pool: the dense GEMM above with the pool epilogue.
+hipError_t launch_xkv_dense(const uint16_t *enc, int M, int K, const uint16_t *wk,
+                            const uint16_t *wv, const uint16_t *bv, uint16_t *xkv,
+                            long long slot_stride, long long layer_off, const int32_t *slots,
+                            int F, int F_pad, int H, int hd, int max_batch, hipStream_t st) {
+    enc::GemmArgs a{};
+    a.A = enc;
+    a.rpr = M;
+    a.srow = K;
+    a.W0 = wk;
+    a.W1 = a.W2 = wv;
+    a.b1 = bv;
+    a.M = M;
+    a.N = 2 * H * hd;
+    a.K = K;
+    a.seg_n = H * hd;
+    a.F = F;
+    a.H = H;
+    a.xkv = xkv;
+    a.slot_stride = slot_stride;
+    a.layer_off = layer_off;
+    a.slots = slots;
+    a.F_pad = F_pad;
+    a.hd = hd;
+    a.max_batch = max_batch;
+    return enc::launch_gemm(enc::EE_XKV, a, st);
+}
+
+namespace enc {
 
 struct LayerW {
     const uint16_t *ln1_g, *ln1_b, *wq, *bq, *wk, *wv, *bv, *wo, *bo;

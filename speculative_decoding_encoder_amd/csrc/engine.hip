@@ -582,20 +582,12 @@ wf_status wf_encode_kv(wf_engine *e, int32_t n, const int32_t *d_slots, const vo
     hipStream_t st = (hipStream_t)stream;
     for (int l = 0; l < all_layers(&c); ++l) {
         const LayerW &w = l < c.n_layers ? e->layers[l] : e->dlayers[l - c.n_layers];
-        EpiArgs ea{};
-        ea.b0 = nullptr;
-        ea.b1 = w.bvc;
-        ea.xkv = e->xkv;
-        ea.xkv_slot_stride = (int64_t)e->xkv_slot_elems;
-        ea.xkv_layer_off = (int64_t)l * e->xkv_layer_elems;
-        ea.F = c.n_frames;
-        ea.F_pad = e->F_pad;
-        ea.slots = d_slots;
-        ea.H = c.n_heads;
-        ea.hd = c.head_dim;
-        ea.max_batch = c.max_batch;
-        WF_TRY(run_gemm(e, TK_XKV, ROLE_XKV, (const uint16_t *)d_enc, (int)M, c.d_model, w.wkc,
-                        w.wvc, nullptr, c.d_model, 2 * c.d_model, ea, st));
+        WF_TRY(timed(e, TK_XKV, st, [&] {
+            return launch_xkv_dense((const uint16_t *)d_enc, (int)M, c.d_model, w.wkc, w.wvc, w.bvc,
+                                    e->xkv, (long long)e->xkv_slot_elems,
+                                    (long long)l * (long long)e->xkv_layer_elems, d_slots,
+                                    c.n_frames, e->F_pad, c.n_heads, c.head_dim, c.max_batch, st);
+        }));
     }
     return WF_OK;
 }

@@ -24,7 +24,6 @@ struct EpiCol {
     float bias;                    // the column's bias (0 without one)
     int seg, c;                    // weight segment and column within it
     int kcol, vcol;                // EPI_QKV: the column's place in a K / V page
-    int h, dim;                    // EPI_XKV: head and dimension
 };
 
 template <int EPI>
@@ -32,7 +31,7 @@ __device__ __forceinline__ EpiCol epi_col(const GemmArgs &a, int n) {
     const EpiArgs &e = a.e;
     EpiCol k{};
     n = min(n, a.N - 1);                        // columns past N are never stored
-    if constexpr (EPI == EPI_QKV || EPI == EPI_XKV || EPI == EPI_STORE32) {
+    if constexpr (EPI == EPI_QKV || EPI == EPI_STORE32) {
         k.seg = n / a.seg_n;
         k.c = n - k.seg * a.seg_n;
     } else {
@@ -43,10 +42,6 @@ __device__ __forceinline__ EpiCol epi_col(const GemmArgs &a, int n) {
         k.kcol = h * 16 * e.hd + dim;                       // K page: [H][16][hd]
         k.vcol = e.H * 16 * e.hd + (h * e.hd + dim) * 16;   // V page: [H][hd][16]
         k.bias = k.seg == 0 ? bias_at(e.b0, k.c) : (k.seg == 2 ? bias_at(e.b2, k.c) : 0.0f);
-    } else if constexpr (EPI == EPI_XKV) {
-        k.h = k.c / e.hd;
-        k.dim = k.c - k.h * e.hd;
-        k.bias = k.seg == 1 ? bias_at(e.b1, k.c) : 0.0f;
     } else if constexpr (EPI == EPI_STORE32) {
         const uint16_t *bb = k.seg == 0 ? e.b0 : (k.seg == 1 ? e.b1 : e.b2);
         k.bias = bias_at(bb, k.c);
@@ -93,20 +88,6 @@ __device__ __forceinline__ void epi_store(const GemmArgs &a, const EpiCol &k, in
         else pg[k.vcol + (rk & 15)] = f2h_bits(v + k.bias);
     } else if constexpr (EPI == EPI_STORE32) {
         e.out32[(size_t)m * a.N + n] = v + k.bias;
-    } else if constexpr (EPI == EPI_XKV) {
-        const int b = m / e.F;
-        const int f = m - b * e.F;
-        const int slot = e.slots[b];
-        if (slot < 0 || slot >= e.max_batch) return;
-        uint16_t *base = e.xkv + (size_t)slot * e.xkv_slot_stride + e.xkv_layer_off;
-        if (k.seg == 0) {
-            base[(size_t)k.h * e.F_pad * e.hd + xk_index(f, k.dim, e.hd)] = f2h_bits(v);
-        } else {
-            // V: per head, 32-frame steps of [hd][32 positions] (one
-            // contiguous block per step, frame j of a step at xv_pos(j))
-            base[(size_t)e.H * e.F_pad * e.hd + (size_t)k.h * e.F_pad * e.hd +
-                 ((size_t)(f >> 5) * e.hd + k.dim) * 32 + xv_pos(f & 31)] = f2h_bits(v + k.bias);
-        }
     }
 }
 
@@ -150,7 +131,6 @@ __host__ __device__ constexpr int epi_of(int role) {
          : role == ROLE_CROSS_Q ? EPI_F16
          : role == ROLE_FC1 ? EPI_GELU
          : role == ROLE_LM_HEAD ? EPI_ARGMAX
-         : role == ROLE_XKV ? EPI_XKV
          : (role == ROLE_DRAFT_QKV || role == ROLE_HIST || role == ROLE_HIST_KV) ? EPI_STORE32
          : EPI_RESID;
 }

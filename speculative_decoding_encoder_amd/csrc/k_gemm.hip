@@ -348,7 +348,6 @@ hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st) {
         case ROLE_FC1: return launch_mb<ROLE_FC1>(a, mb, st);
         case ROLE_FC2: return launch_mb<ROLE_FC2>(a, mb, st);
         case ROLE_LM_HEAD: return launch_mb<ROLE_LM_HEAD>(a, mb, st);
-        case ROLE_XKV: return launch_mb<ROLE_XKV>(a, mb, st);
         case ROLE_DRAFT_QKV: return launch_mb<ROLE_DRAFT_QKV>(a, mb, st);
         case ROLE_HIST: return launch_mb<ROLE_HIST>(a, mb, st);
         case ROLE_HIST_KV: return launch_mb<ROLE_HIST_KV>(a, mb, st);

@@ -14,7 +14,7 @@ enum Epi : int {
     EPI_F16 = 2,    // out[m][n] = fp16(C + b[n])      (cross-attention query)
     EPI_GELU = 3,   // out = fp16(GELU(C + b)), fragment-tiled (MLP hidden)
     EPI_ARGMAX = 4, // tied LM head: per 64-column tile (max, lowest argmax), logits
-    EPI_XKV = 5,    // cross K/V of one layer into the write-once pool
+    EPI_XKV = 5,    // (unused: the cross K/V come from the encoder's dense GEMM)
     EPI_STORE32 = 6,// out32[m][n] = C + b_seg[n]      (drafter temporaries, history)
 };
 
@@ -30,11 +30,6 @@ struct EpiArgs {
     const int32_t *slots, *req_L, *req_ntok;
     int32_t T, H, hd, page_elems;
     const int32_t *row_kv;         // per row: page * 16 + offset of its position, -1: no append
-    // EPI_XKV
-    uint16_t *xkv;
-    int64_t xkv_slot_stride, xkv_layer_off;
-    int32_t F, F_pad;
-    int32_t max_batch;             // slot ids outside [0, max_batch) are skipped
     // EPI_ARGMAX
     float *logits;                 // null or [M][V]
     float *tile_max;               // [M][ld]: per row, its 64-column tiles
@@ -153,7 +148,7 @@ struct RollbackArgs {
 // GEMM roles: each is its own kernel instantiation (and profiler symbol).
 enum Role : int {
     ROLE_QKV = 0, ROLE_OPROJ = 1, ROLE_CROSS_Q = 2, ROLE_FC1 = 3, ROLE_FC2 = 4,
-    ROLE_LM_HEAD = 5, ROLE_XKV = 6,
+    ROLE_LM_HEAD = 5, ROLE_XKV = 6,   // ROLE_XKV: retired (wf_encode_kv uses launch_xkv_dense)
     ROLE_DRAFT_QKV = 7,   // drafter q, k, v (fp32 temporaries before RoPE)
     ROLE_HIST = 8,        // history projection of the tapped streams
     ROLE_HIST_KV = 9,     // drafter k, v of history rows
@@ -231,6 +226,12 @@ hipError_t launch_embed_draft(const EmbedDraftArgs &a, hipStream_t st);
 hipError_t launch_draft_out(const int32_t *anchor, const int32_t *argmax, const int32_t *req_ntok,
                             int n, int K, int32_t *block, hipStream_t st);
 hipError_t launch_gemm(int role, const GemmArgs &a, int mb, hipStream_t st);
+// dense bf16 MFMA GEMM of the audio encoder with the cross K/V pool epilogue
+// (encoder.hip); K a multiple of 32, H * hd the model width
+hipError_t launch_xkv_dense(const uint16_t *enc, int M, int K, const uint16_t *wk,
+                            const uint16_t *wv, const uint16_t *bv, uint16_t *xkv,
+                            long long slot_stride, long long layer_off, const int32_t *slots,
+                            int F, int F_pad, int H, int hd, int max_batch, hipStream_t st);
 // register-tiled variant for short blocks: (mb, nb) in {1x1, 1x2, 1x4, 2x2,
 // 2x4, 4x2, 4x4} (the LM head: nb = 4, mb up to 6); built for the chunk lengths
 // gemm_rk_built accepts, one wave per chunk of the workgroup's K group
