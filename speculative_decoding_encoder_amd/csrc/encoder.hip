@@ -37,6 +37,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <vector>
 
@@ -85,6 +86,75 @@ __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
 }
 __device__ __forceinline__ float bias4(const uint16_t *b, int c, int r) {
     return b ? bf2f(b[c + r]) : 0.0f;
+}
+
+// Epilogue of one 16x16 output tile: this lane's row m and columns n .. n + 3
+// (c[r] is column n + r); m < M and n < N.
+template <int EPI>
+__device__ __forceinline__ void epi_tile(const GemmArgs &a, int m, int n, const f32x4 c) {
+    if constexpr (EPI == EE_RESID) {
+        float4 *px = reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n);
+        float4 xv = *px;
+        xv.x += c[0] + bias4(a.b0, n, 0);
+        xv.y += c[1] + bias4(a.b0, n, 1);
+        xv.z += c[2] + bias4(a.b0, n, 2);
+        xv.w += c[3] + bias4(a.b0, n, 3);
+        *px = xv;
+    } else if constexpr (EPI == EE_GELU || EPI == EE_CONV1) {
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = gelu(c[r] + bias4(a.b0, n, r));
+        size_t row = m;
+        if constexpr (EPI == EE_CONV1) {
+            const int rq = m / a.Tm;
+            row = (size_t)rq * (a.Tm + 2) + 1 + (m - rq * a.Tm);
+        }
+        *reinterpret_cast<u32x2 *>(a.out + row * a.N + n) =
+            u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+    } else if constexpr (EPI == EE_CONV2) {
+        const int t = m % a.F;
+        const float4 pv = *reinterpret_cast<const float4 *>(a.pos + (size_t)t * a.N + n);
+        float4 xv;
+        xv.x = gelu(c[0] + bias4(a.b0, n, 0)) + pv.x;
+        xv.y = gelu(c[1] + bias4(a.b0, n, 1)) + pv.y;
+        xv.z = gelu(c[2] + bias4(a.b0, n, 2)) + pv.z;
+        xv.w = gelu(c[3] + bias4(a.b0, n, 3)) + pv.w;
+        *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = xv;
+    } else if constexpr (EPI == EE_XKV) {
+        const int rq = m / a.F, f = m - rq * a.F;
+        const int slot = a.slots[rq];
+        if (slot < 0 || slot >= a.max_batch) return;   // skipped request
+        const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
+        const int h = cc / a.hd, dim = cc - h * a.hd;
+        uint16_t *base = a.xkv + (size_t)slot * a.slot_stride + a.layer_off +
+                         (size_t)(seg * a.H + h) * a.F_pad * a.hd;
+        if (seg == 0) {   // K: the four dims are adjacent in the fragment order
+            *reinterpret_cast<u32x2 *>(base + xk_index(f, dim, a.hd)) =
+                u32x2{pack_h2(c[0], c[1]), pack_h2(c[2], c[3])};
+        } else {          // V: [hd][32] per 32-frame step, frame at xv_pos
+            uint16_t *vb = base + (size_t)(f >> 5) * a.hd * 32 + xv_pos(f & 31);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vb[(size_t)(dim + r) * 32] = f2h_bits(c[r] + bias4(a.b1, cc, r));
+        }
+    } else {   // EE_QKV
+        const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
+        const int h = cc >> 6, dim = cc & 63;
+        const int rq = m / a.F, t = m - rq * a.F;
+        const uint16_t *bb = seg == 0 ? a.b0 : (seg == 2 ? a.b2 : nullptr);
+        float y[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] = c[r] + bias4(bb, cc, r);
+        const size_t bh = (size_t)rq * a.H + h;
+        if (seg < 2) {
+            uint16_t *dst = (seg == 0 ? a.q : a.k) + (bh * a.Fq + t) * 64 + dim;
+            *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
+        } else {
+            uint16_t *dst = a.vt + (bh * 64 + dim) * a.Fq + t;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)r * a.Fq] = (uint16_t)(pack_bf2(y[r], 0.f) & 0xffffu);
+        }
+    }
 }
 
 template <int EPI>
@@ -179,71 +249,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int n = n0 + wn * 128 + j * 16 + 4 * g;
-            if (n >= a.N) continue;
-            const f32x4 c = acc[i][j];
-            if constexpr (EPI == EE_RESID) {
-                float4 *px = reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n);
-                float4 xv = *px;
-                xv.x += c[0] + bias4(a.b0, n, 0);
-                xv.y += c[1] + bias4(a.b0, n, 1);
-                xv.z += c[2] + bias4(a.b0, n, 2);
-                xv.w += c[3] + bias4(a.b0, n, 3);
-                *px = xv;
-            } else if constexpr (EPI == EE_GELU || EPI == EE_CONV1) {
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = gelu(c[r] + bias4(a.b0, n, r));
-                size_t row = m;
-                if constexpr (EPI == EE_CONV1) {
-                    const int rq = m / a.Tm;
-                    row = (size_t)rq * (a.Tm + 2) + 1 + (m - rq * a.Tm);
-                }
-                *reinterpret_cast<u32x2 *>(a.out + row * a.N + n) =
-                    u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
-            } else if constexpr (EPI == EE_CONV2) {
-                const int t = m % a.F;
-                const float4 pv = *reinterpret_cast<const float4 *>(a.pos + (size_t)t * a.N + n);
-                float4 xv;
-                xv.x = gelu(c[0] + bias4(a.b0, n, 0)) + pv.x;
-                xv.y = gelu(c[1] + bias4(a.b0, n, 1)) + pv.y;
-                xv.z = gelu(c[2] + bias4(a.b0, n, 2)) + pv.z;
-                xv.w = gelu(c[3] + bias4(a.b0, n, 3)) + pv.w;
-                *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = xv;
-            } else if constexpr (EPI == EE_XKV) {
-                const int rq = m / a.F, f = m - rq * a.F;
-                const int slot = a.slots[rq];
-                if (slot < 0 || slot >= a.max_batch) continue;   // skipped request
-                const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
-                const int h = cc / a.hd, dim = cc - h * a.hd;
-                uint16_t *base = a.xkv + (size_t)slot * a.slot_stride + a.layer_off +
-                                 (size_t)(seg * a.H + h) * a.F_pad * a.hd;
-                if (seg == 0) {   // K: the four dims are adjacent in the fragment order
-                    *reinterpret_cast<u32x2 *>(base + xk_index(f, dim, a.hd)) =
-                        u32x2{pack_h2(c[0], c[1]), pack_h2(c[2], c[3])};
-                } else {          // V: [hd][32] per 32-frame step, frame at xv_pos
-                    uint16_t *vb = base + (size_t)(f >> 5) * a.hd * 32 + xv_pos(f & 31);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        vb[(size_t)(dim + r) * 32] = f2h_bits(c[r] + bias4(a.b1, cc, r));
-                }
-            } else {   // EE_QKV
-                const int seg = n / a.seg_n, cc = n - seg * a.seg_n;
-                const int h = cc >> 6, dim = cc & 63;
-                const int rq = m / a.F, t = m - rq * a.F;
-                const uint16_t *bb = seg == 0 ? a.b0 : (seg == 2 ? a.b2 : nullptr);
-                float y[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] = c[r] + bias4(bb, cc, r);
-                const size_t bh = (size_t)rq * a.H + h;
-                if (seg < 2) {
-                    uint16_t *dst = (seg == 0 ? a.q : a.k) + (bh * a.Fq + t) * 64 + dim;
-                    *reinterpret_cast<u32x2 *>(dst) = u32x2{pack_bf2(y[0], y[1]), pack_bf2(y[2], y[3])};
-                } else {
-                    uint16_t *dst = a.vt + (bh * 64 + dim) * a.Fq + t;
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[(size_t)r * a.Fq] = (uint16_t)(pack_bf2(y[r], 0.f) & 0xffffu);
-                }
-            }
+            if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
         }
     }
 }
@@ -257,7 +263,8 @@ struct AttnArgs {
 
 constexpr int AROW = 72;               // LDS row: 64 elements + 16 B pad
 
-__global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
+template <int QT>   // 16-query subtiles per wave (the workgroup takes 64 QT queries)
+__global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][64 * AROW];   // [key][dim]
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][64 * AROW];   // [dim][key]
     const int per = gridDim.x >> 3;
@@ -271,11 +278,11 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
     const uint16_t *qb = a.q + (size_t)bh * a.Fq * 64;
     const uint16_t *kb = a.k + (size_t)bh * a.Fq * 64;
     const uint16_t *vb = a.vt + (size_t)bh * 64 * a.Fq;
-    const int q0 = qt * 256 + wave * 64;
+    const int q0 = qt * 64 * QT + wave * 16 * QT;
 
-    u32x4 qf[4][2];
+    u32x4 qf[QT][2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int s = 0; s < QT; ++s)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
             qf[s][kk] = ld16(qb + (size_t)(q0 + 16 * s + r16) * 64 + kk * 32 + g * 8);
@@ -306,10 +313,10 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
         }
     };
 
-    float mrow[4], lsum[4];
-    f32x4 o[4][4];
+    float mrow[QT], lsum[QT];
+    f32x4 o[4][QT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < QT; ++s) {
         mrow[s] = -INFINITY;
         lsum[s] = 0.f;
 #pragma unroll
@@ -342,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
         // one subtile at a time (scores, softmax, PV), so one subtile's VALU
         // work can overlap the next one's MFMAs
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < QT; ++s) {
             f32x4 sc[4];
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt) {
@@ -398,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void attn_kernel(AttnArgs a) {
         __syncthreads();
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < QT; ++s) {
         float l = lsum[s], x0, x1;
         rows16_pair(l, x0, x1);
         l = x0 + x1;
@@ -620,6 +627,7 @@ struct wf_encoder {
     const uint16_t *c1b, *c2b, *lnp_g, *lnp_b;
     uint16_t *melT, *g1, *h, *q, *k, *vt, *o, *hid, *w1r, *w2r;
     float *x, *pos;
+    int attn_qt = 2;   // 16-query subtiles per attention wave (WF_ENC_ATTN_QT=4: four)
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -730,6 +738,7 @@ wf_status wf_enc_create(const wf_enc_config *cfg, const wf_enc_weights *w, void 
 
     wf_encoder *e = new wf_encoder();
     e->c = *cfg;
+    if (const char *v = std::getenv("WF_ENC_ATTN_QT")) e->attn_qt = std::atoi(v) == 4 ? 4 : 2;
     e->lay = layout_of(cfg);
     const Layout &L = e->lay;
     char *ws = (char *)workspace;
@@ -842,11 +851,14 @@ wf_status wf_encode(wf_encoder *e, int32_t n, const void *d_mel, void *d_out, vo
         t.F = F;
         t.Fq = Fq;
         t.d = d;
-        t.n_qt = Fq / 256;
+        t.n_qt = Fq / (64 * e->attn_qt);
         t.n_wg = n * H * t.n_qt;
         t.sl2e = 1.4426950408889634f / 8.0f;
         WFE_TRY(timed(e, WF_ENC_TK_ATTN, st, [&] {
-            hipLaunchKernelGGL(attn_kernel, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
+            if (e->attn_qt == 4)
+                hipLaunchKernelGGL(attn_kernel<4>, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
+            else
+                hipLaunchKernelGGL(attn_kernel<2>, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
             return hipGetLastError();
         }));
         GemmArgs ob = plain(e->o, M, d, w.wo, w.bo, d);
