@@ -264,7 +264,7 @@ struct AttnArgs {
 constexpr int AROW = 72;               // LDS row: 64 elements + 16 B pad
 
 template <int QT>   // 16-query subtiles per wave (the workgroup takes 64 QT queries)
-__global__ __launch_bounds__(256, QT == 2 ? 2 : 1) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, QT == 1 ? 3 : (QT == 2 ? 2 : 1)) void attn_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t ks[2][64 * AROW];   // [key][dim]
     __shared__ __attribute__((aligned(16))) uint16_t vs[2][64 * AROW];   // [dim][key]
     const int per = gridDim.x >> 3;
@@ -627,7 +627,7 @@ struct wf_encoder {
     const uint16_t *c1b, *c2b, *lnp_g, *lnp_b;
     uint16_t *melT, *g1, *h, *q, *k, *vt, *o, *hid, *w1r, *w2r;
     float *x, *pos;
-    int attn_qt = 2;   // 16-query subtiles per attention wave (WF_ENC_ATTN_QT=4: four)
+    int attn_qt = 2;   // 16-query subtiles per attention wave (WF_ENC_ATTN_QT=1 / 4: a tuning aid)
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -738,7 +738,10 @@ wf_status wf_enc_create(const wf_enc_config *cfg, const wf_enc_weights *w, void 
 
     wf_encoder *e = new wf_encoder();
     e->c = *cfg;
-    if (const char *v = std::getenv("WF_ENC_ATTN_QT")) e->attn_qt = std::atoi(v) == 4 ? 4 : 2;
+    if (const char *v = std::getenv("WF_ENC_ATTN_QT")) {
+        const int q = std::atoi(v);
+        e->attn_qt = q == 4 ? 4 : (q == 1 ? 1 : 2);
+    }
     e->lay = layout_of(cfg);
     const Layout &L = e->lay;
     char *ws = (char *)workspace;
@@ -857,6 +860,8 @@ wf_status wf_encode(wf_encoder *e, int32_t n, const void *d_mel, void *d_out, vo
         WFE_TRY(timed(e, WF_ENC_TK_ATTN, st, [&] {
             if (e->attn_qt == 4)
                 hipLaunchKernelGGL(attn_kernel<4>, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
+            else if (e->attn_qt == 1)
+                hipLaunchKernelGGL(attn_kernel<1>, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
             else
                 hipLaunchKernelGGL(attn_kernel<2>, dim3(cdiv(t.n_wg, 8) * 8), dim3(256), 0, st, t);
             return hipGetLastError();
