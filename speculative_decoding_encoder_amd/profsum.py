@@ -10,6 +10,10 @@
       copy in the run (COPY_BYTES read and written); appends the figure to
       profiles/hbm_traffic.json, keyed by workload, kernel kind and a hash of
       the workload's kernel sources, and writes a text summary to OUT_TXT.
+  python -m speculative_decoding_encoder_amd.profsum mfma DIR TITLE CMD
+      per-kernel MFMA utilisation (MfmaUtil: MFMA-busy cycles over active
+      cycles times SIMDs) and MFMA flops per dispatch (MfmaFlopsBF16 +
+      MfmaFlopsF16) of a --pmc MfmaUtil MfmaFlopsBF16 MfmaFlopsF16 run.
 """
 from __future__ import annotations
 
@@ -110,9 +114,35 @@ def traffic(fdir, wdir, workload, kind, symbol, copy_bytes, out_txt, cmd):
     return ent
 
 
+def mfma(d: str, title: str, cmd: str) -> str:
+    per = {}
+    for r in csv.DictReader(open(os.path.join(d, "run_counter_collection.csv"))):
+        key = (r["Kernel_Name"], r["Dispatch_Id"])
+        per.setdefault(key, {})[r["Counter_Name"]] = \
+            per.get(key, {}).get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg = {}
+    for (name, _), c in per.items():
+        a = agg.setdefault(name, [0, 0.0, 0.0])
+        a[0] += 1
+        a[1] += c.get("MfmaUtil", 0.0)
+        a[2] += c.get("MfmaFlopsBF16", 0.0) + c.get("MfmaFlopsF16", 0.0)
+    rows = sorted(agg.items(), key=lambda kv: -kv[1][2])
+    out = [f"# rocprofv3 MFMA counters -- {title}", "# command (repo root on the MI355X box):",
+           f"#   {cmd}", "# MfmaUtil: MFMA-busy cycles / (active cycles x SIMDs), per dispatch;",
+           "# GFLOP: MFMA flops per dispatch (bf16 + fp16 MOPS x 512)", "",
+           f"{'kernel':66s} {'calls':>7s} {'mfma_util_%':>11s} {'gflop':>10s}"]
+    for name, (n, u, f) in rows:
+        if f <= 0:
+            continue
+        out.append(f"{_short(name, 66):66s} {n:7d} {u / n:11.2f} {f / n / 1e9:10.3f}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if argv and argv[0] == "stats":
         sys.stdout.write(stats(argv[1], argv[2], " ".join(argv[3:])))
+    elif argv and argv[0] == "mfma":
+        sys.stdout.write(mfma(argv[1], argv[2], " ".join(argv[3:])))
     elif argv and argv[0] == "traffic":
         ent = traffic(argv[1], argv[2], argv[3], argv[4], argv[5], float(argv[6]), argv[7],
                       " ".join(argv[8:]))
