@@ -356,7 +356,7 @@ typedef struct {
     int32_t n_heads;    /* attention heads (head_dim must be 64) */
     int32_t head_dim;   /* 64 */
     int32_t d_ffn;      /* MLP width, a multiple of 64 (5120) */
-    int32_t n_mels;     /* mel channels (128), at most 256, 3 n_mels % 32 == 0 */
+    int32_t n_mels;     /* mel channels (128): 64, 128, 192 or 256 */
     int32_t n_frames;   /* output frames F (1500); the input has 2F frames */
     int32_t max_batch;  /* largest n of one wf_encode call */
     float ln_eps;       /* 1e-5 */

@@ -16,7 +16,8 @@
 //  * GEMM: C = A W^T, bf16 x bf16 -> fp32 (16x16x32 MFMA). A workgroup of 4
 //    waves owns a 128 x 256 tile (each wave 64 x 128: 4 x 8 accumulator
 //    tiles); both operands go through double-buffered LDS in 32-deep k-steps
-//    (rows padded to 80 B: conflict-free 16-byte fragment reads). The MFMA
+//    (rows padded to 80 B: conflict-free 16-byte fragment reads), the global
+//    loads of a k-step issued two k-steps ahead (K % 64 == 0). The MFMA
 //    computes C^T so a lane holds one output row and four consecutive
 //    columns (8- or 16-byte epilogue stores). Row tiles are grouped by 8 per
 //    column walk and workgroups are dealt to the 8 XCDs in consecutive
@@ -199,18 +200,20 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         wsrc[v] = wb + (size_t)(n - seg * a.seg_n) * a.K + pc * 8;
         woff[v] = row * GROW + pc * 8;
     }
-    u32x4 rx[2], rw[4];
-    auto gload = [&](int kt) {
+    const int KT = a.K / GBK;
+    struct Stage { u32x4 x[2], w[4]; };
+    auto gload = [&](Stage &r, int kt) {
+        kt = min(kt, KT - 1);                       // past the end: a valid repeat, never stored
 #pragma unroll
-        for (int v = 0; v < 2; ++v) rx[v] = ld16(xsrc[v] + kt * GBK);
+        for (int v = 0; v < 2; ++v) r.x[v] = ld16(xsrc[v] + kt * GBK);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) rw[v] = ld16(wsrc[v] + kt * GBK);
+        for (int v = 0; v < 4; ++v) r.w[v] = ld16(wsrc[v] + kt * GBK);
     };
-    auto sstore = [&](int b) {
+    auto sstore = [&](const Stage &r, int b) {
 #pragma unroll
-        for (int v = 0; v < 2; ++v) *reinterpret_cast<u32x4 *>(&xs[b][xoff[v]]) = rx[v];
+        for (int v = 0; v < 2; ++v) *reinterpret_cast<u32x4 *>(&xs[b][xoff[v]]) = r.x[v];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4 *>(&ws[b][woff[v]]) = rw[v];
+        for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4 *>(&ws[b][woff[v]]) = r.w[v];
     };
 
     f32x4 acc[4][8];
@@ -218,26 +221,45 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    const int KT = a.K / GBK;
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-        const int b = kt & 1;
-        if (kt + 1 < KT) gload(kt + 1);
-        u32x4 xf[4], wf[8];
+    // one k-step from LDS buffer b: the W fragments in two halves of four,
+    // so only 8 fragments are live at a time
+    auto step = [&](int b) {
+        u32x4 xf[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 64 + i * 16 + r16) * GROW + g * 8]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            wf[j] = *reinterpret_cast<const u32x4 *>(&ws[b][(wn * 128 + j * 16 + r16) * GROW + g * 8]);
+        for (int h = 0; h < 2; ++h) {
+            u32x4 wf[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int j = 0; j < 4; ++j)
+                wf[j] = *reinterpret_cast<const u32x4 *>(
+                    &ws[b][(wn * 128 + (4 * h + j) * 16 + r16) * GROW + g * 8]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) acc[i][j] = mfma_bf16_k32(wf[j], xf[i], acc[i][j]);
-        if (kt + 1 < KT) sstore(b ^ 1);
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][4 * h + j] = mfma_bf16_k32(wf[j], xf[i], acc[i][4 * h + j]);
+        }
+    };
+    // k-step kt is read from LDS buffer kt & 1; its global loads were issued
+    // two k-steps earlier (register sets r0 / r1 alternate), so a load has
+    // two k-steps of MFMA work to arrive
+    Stage r0, r1;
+    gload(r0, 0);
+    gload(r1, 1);
+    sstore(r0, 0);
+    __syncthreads();
+    // KT is even (K % 64 == 0); past the end the copies land in a buffer
+    // nothing reads again
+    for (int kt = 0; kt < KT; kt += 2) {
+        gload(r0, kt + 2);
+        step(0);
+        sstore(r1, 1);
+        __syncthreads();
+        gload(r1, kt + 3);
+        step(1);
+        sstore(r0, 0);
         __syncthreads();
     }
 
@@ -513,6 +535,7 @@ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
+    if (a.K % (2 * GBK) || a.M < 1 || a.N % 4) return hipErrorInvalidValue;   // loop unrolled by 2
     a.n_m = cdiv(a.M, GBM);
     a.n_n = cdiv(a.N, GBN);
     a.n_wg = a.n_m * a.n_n;
@@ -607,7 +630,7 @@ bool config_ok(const wf_enc_config *c, const char **why) {
     else if (c->n_heads < 1 || c->n_heads * 64 != c->d_model) w = "d_model must be n_heads * 64";
     else if (c->d_model > 1280) w = "d_model above 1280";
     else if (c->d_ffn < 64 || c->d_ffn % 64) w = "d_ffn must be a positive multiple of 64";
-    else if (c->n_mels < 1 || c->n_mels > 256 || (3 * c->n_mels) % 32) w = "n_mels must be in [1, 256] with 3 n_mels a multiple of 32";
+    else if (c->n_mels < 64 || c->n_mels > 256 || c->n_mels % 64) w = "n_mels must be 64, 128, 192 or 256";
     else if (c->n_frames < 1 || c->n_frames > 4096) w = "n_frames outside [1, 4096]";
     else if (c->max_batch < 1 || (long long)c->max_batch * 2 * (c->n_frames + 1) > 0x3fffffff) w = "max_batch out of range";
     else if (!(c->ln_eps > 0.f)) w = "ln_eps must be positive";
