@@ -355,15 +355,19 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
         for _ in range(W):
             graph.replay()
     torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
     t0 = time.perf_counter()
-    for _ in range(K):
+    evs[0].record()
+    for i in range(K):
         if graph is not None:
             graph.replay()
         else:
             w.step()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / K
+    per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
     n_acc2 = w.outs[0].cpu().numpy()
     assert np.array_equal(n_acc, n_acc2), "graph replay changed the round's outcome"
     used_graph = graph is not None
@@ -391,8 +395,19 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
             kinds[k]["gbs"] = kb[k] / (kinds[k]["avg_us"] * 1e-6) / 1e9
     bytes_pass = w.pass_bytes()
     value = tokens_per_step / (ms_step * 1e-3)
+    # acceptance of the round every step repeats: alpha = accepted / proposed
+    # candidates, tau = tokens per target call, s_k = P(a >= k),
+    # a_k^c = s_k / s_(k-1) (acceptance of candidate k given k - 1 accepted)
+    live = n_acc[:w.B]
+    s_k = [float(np.mean(live >= k)) for k in range(1, w.K + 1)]
+    acc = {"alpha": round(float(live.sum()) / (w.B * w.K), 4) if w.K else None,
+           "tau": round(float(np.mean(live + 1)), 4), "s_k": [round(v, 4) for v in s_k],
+           "a_k_c": [round(s_k[0], 4)] + [round(s_k[k] / s_k[k - 1], 4) if s_k[k - 1] else None
+                                           for k in range(1, w.K)]}
     return {
         "value": value, "ms_step": ms_step, "tokens_per_step": tokens_per_step,
+        "step_ms_p10_p50_p90": [round(float(np.percentile(per_step, q)), 4) for q in (10, 50, 90)],
+        "acceptance": acc,
         "accepted": [int(a) for a in n_acc[:8]], "bytes_pass": bytes_pass,
         "pass_frac": bytes_pass / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
         "dom": dom, "achieved": achieved, "dom_bytes": kb[dom],
@@ -488,6 +503,27 @@ def k_sweep(args):
                       "readout_layer": args.readout if args.readout >= 0 else None,
                       "steps": args.steps,
                       "warmup": args.warmup, "graph": not args.no_graph}), flush=True)
+
+
+def stream_bandwidth(torch, dev, gib: int = 4) -> float:
+    """Device copy of a 4 GiB buffer (past the 256 MB last-level cache):
+    bytes read plus written per second, best of 5, in GB/s."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    best = None
+    for _ in range(5):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) * 1e-3
+        best = t if best is None else min(best, t)
+    del src, dst
+    torch.cuda.empty_cache()
+    return 2 * n / best / 1e9
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
@@ -643,6 +679,8 @@ def main():
                          "readout at this decoder layer in every verify pass")
     ap.add_argument("--batch", type=int, default=0,
                     help="with --k-sweep: this many requests instead of the workload's")
+    ap.add_argument("--no-stream-bw", action="store_true",
+                    help="skip the 4 GiB streaming-copy bandwidth measurement")
     ap.add_argument("--encoder", type=int, default=0,
                     help="time the audio encoder on this many 30 s windows instead (own JSON line)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -692,7 +730,9 @@ def main():
                    "temperature": w.temperature, "graph": r["graph"]},
         "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
         "tokens_per_step": r["tokens_per_step"],
+        "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
         "accepted": r["accepted"],
+        "acceptance": r["acceptance"],
         "pass": {"bytes": r["bytes_pass"], "roofline_frac_of_step": round(r["pass_frac"], 4)},
         "roofline": {"bound": "hbm", "kernel": dom, "symbol": KIND_SYMBOL.get(dom, dom),
                      "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -703,6 +743,10 @@ def main():
         "encode_kv_s": round(w.encode_kv_s, 4),
         "batches": {str(w.B): summary(w, r)},
     }
+    if not args.no_stream_bw:
+        out["stream_gbs"] = round(stream_bandwidth(torch, w.eng.dev), 1)
+        out["pass"]["stream_frac"] = round(r["bytes_pass"] / (r["ms_step"] * 1e-3)
+                                           / (out["stream_gbs"] * 1e9), 4)
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         src = torch.ones(n, dtype=torch.uint8, device=w.eng.dev)
