@@ -74,7 +74,7 @@ struct GemmArgs {
     int F_pad, hd, max_batch;
 };
 
-constexpr int GBM = 128, GBN = 256, GBK = 32, GROW = 40;
+constexpr int GBK = 32, GROW = 40;   // k-step depth; LDS row (32 k + 8 pad)
 
 __device__ __forceinline__ float gelu(float t) {
     return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
@@ -158,10 +158,16 @@ __device__ __forceinline__ void epi_tile(const GemmArgs &a, int m, int n, const 
     }
 }
 
-template <int EPI>
+// MT x NT accumulator tiles per wave, 2 x 2 waves: a (32 MT) x (32 NT) tile per
+// workgroup (4 x 8: 128 x 256, the default; 2 x 4: 64 x 128 for grids that
+// would not fill the chip). A tile's shape does not change any element's
+// arithmetic: every output sums its k-steps in order in one lane.
+template <int EPI, int MT, int NT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][GBM * GROW];
-    __shared__ __attribute__((aligned(16))) uint16_t ws[2][GBN * GROW];
+    constexpr int BM = 32 * MT, BN = 32 * NT;
+    constexpr int XL = BM / 64, WL = BN / 64;       // 16-byte pieces per thread per k-step
+    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * GROW];
+    __shared__ __attribute__((aligned(16))) uint16_t ws[2][BN * GROW];
     const int per = gridDim.x >> 3;
     const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (lid >= a.n_wg) return;
@@ -176,15 +182,15 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int m0 = mt * GBM, n0 = nt * GBN;
+    const int m0 = mt * BM, n0 = nt * BN;
 
-    // 16-byte pieces of a k-step: A 128 rows x 4 (2 per thread), W 256 rows
-    // x 4 (4 per thread). Rows past M / N repeat the last (never stored).
-    const uint16_t *xsrc[2];
-    const uint16_t *wsrc[4];
-    int xoff[2], woff[4];
+    // 16-byte pieces of a k-step: A BM rows x 4, W BN rows x 4. Rows past
+    // M / N repeat the last (never stored).
+    const uint16_t *xsrc[XL];
+    const uint16_t *wsrc[WL];
+    int xoff[XL], woff[WL];
 #pragma unroll
-    for (int v = 0; v < 2; ++v) {
+    for (int v = 0; v < XL; ++v) {
         const int p = tid + 256 * v, row = p >> 2, pc = p & 3;
         const int m = min(m0 + row, a.M - 1);
         const int rq = m / a.rpr;
@@ -192,7 +198,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         xoff[v] = row * GROW + pc * 8;
     }
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
+    for (int v = 0; v < WL; ++v) {
         const int p = tid + 256 * v, row = p >> 2, pc = p & 3;
         const int n = min(n0 + row, a.N - 1);
         const int seg = n / a.seg_n;
@@ -201,45 +207,45 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         woff[v] = row * GROW + pc * 8;
     }
     const int KT = a.K / GBK;
-    struct Stage { u32x4 x[2], w[4]; };
+    struct Stage { u32x4 x[XL], w[WL]; };
     auto gload = [&](Stage &r, int kt) {
         kt = min(kt, KT - 1);                       // past the end: a valid repeat, never stored
 #pragma unroll
-        for (int v = 0; v < 2; ++v) r.x[v] = ld16(xsrc[v] + kt * GBK);
+        for (int v = 0; v < XL; ++v) r.x[v] = ld16(xsrc[v] + kt * GBK);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) r.w[v] = ld16(wsrc[v] + kt * GBK);
+        for (int v = 0; v < WL; ++v) r.w[v] = ld16(wsrc[v] + kt * GBK);
     };
     auto sstore = [&](const Stage &r, int b) {
 #pragma unroll
-        for (int v = 0; v < 2; ++v) *reinterpret_cast<u32x4 *>(&xs[b][xoff[v]]) = r.x[v];
+        for (int v = 0; v < XL; ++v) *reinterpret_cast<u32x4 *>(&xs[b][xoff[v]]) = r.x[v];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) *reinterpret_cast<u32x4 *>(&ws[b][woff[v]]) = r.w[v];
+        for (int v = 0; v < WL; ++v) *reinterpret_cast<u32x4 *>(&ws[b][woff[v]]) = r.w[v];
     };
 
-    f32x4 acc[4][8];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MT; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // one k-step from LDS buffer b: the W fragments in two halves of four,
-    // so only 8 fragments are live at a time
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // one k-step from LDS buffer b: the W fragments in halves, so fewer
+    // fragments are live at a time
     auto step = [&](int b) {
-        u32x4 xf[4];
+        u32x4 xf[MT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 64 + i * 16 + r16) * GROW + g * 8]);
+        for (int i = 0; i < MT; ++i)
+            xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 16 * MT + i * 16 + r16) * GROW + g * 8]);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            u32x4 wf[4];
+            u32x4 wf[NT / 2];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NT / 2; ++j)
                 wf[j] = *reinterpret_cast<const u32x4 *>(
-                    &ws[b][(wn * 128 + (4 * h + j) * 16 + r16) * GROW + g * 8]);
+                    &ws[b][(wn * 16 * NT + (NT / 2 * h + j) * 16 + r16) * GROW + g * 8]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < MT; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][4 * h + j] = mfma_bf16_k32(wf[j], xf[i], acc[i][4 * h + j]);
+                for (int j = 0; j < NT / 2; ++j)
+                    acc[i][NT / 2 * h + j] = mfma_bf16_k32(wf[j], xf[i], acc[i][NT / 2 * h + j]);
         }
     };
     // k-step kt is read from LDS buffer kt & 1; its global loads were issued
@@ -265,12 +271,12 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 
     // epilogue: tile (i, j) gives this lane row m and columns n .. n + 3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = m0 + wm * 64 + i * 16 + r16;
+    for (int i = 0; i < MT; ++i) {
+        const int m = m0 + wm * 16 * MT + i * 16 + r16;
         if (m >= a.M) continue;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = n0 + wn * 128 + j * 16 + 4 * g;
+        for (int j = 0; j < NT; ++j) {
+            const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
             if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
         }
     }
@@ -534,21 +540,29 @@ __global__ void pos_kernel(int F, int d, float *pos) {
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
-    if (a.K % (2 * GBK) || a.M < 1 || a.N % 4) return hipErrorInvalidValue;   // loop unrolled by 2
-    a.n_m = cdiv(a.M, GBM);
-    a.n_n = cdiv(a.N, GBN);
-    a.n_wg = a.n_m * a.n_n;
+template <int MT, int NT>
+hipError_t launch_tiles(int epi, const GemmArgs &a, hipStream_t st) {
     const dim3 grid(cdiv(a.n_wg, 8) * 8), blk(256);
     switch (epi) {
-    case EE_CONV1: hipLaunchKernelGGL(gemm_kernel<EE_CONV1>, grid, blk, 0, st, a); break;
-    case EE_CONV2: hipLaunchKernelGGL(gemm_kernel<EE_CONV2>, grid, blk, 0, st, a); break;
-    case EE_QKV: hipLaunchKernelGGL(gemm_kernel<EE_QKV>, grid, blk, 0, st, a); break;
-    case EE_RESID: hipLaunchKernelGGL(gemm_kernel<EE_RESID>, grid, blk, 0, st, a); break;
-    case EE_XKV: hipLaunchKernelGGL(gemm_kernel<EE_XKV>, grid, blk, 0, st, a); break;
-    default: hipLaunchKernelGGL(gemm_kernel<EE_GELU>, grid, blk, 0, st, a); break;
+    case EE_CONV1: hipLaunchKernelGGL((gemm_kernel<EE_CONV1, MT, NT>), grid, blk, 0, st, a); break;
+    case EE_CONV2: hipLaunchKernelGGL((gemm_kernel<EE_CONV2, MT, NT>), grid, blk, 0, st, a); break;
+    case EE_QKV: hipLaunchKernelGGL((gemm_kernel<EE_QKV, MT, NT>), grid, blk, 0, st, a); break;
+    case EE_RESID: hipLaunchKernelGGL((gemm_kernel<EE_RESID, MT, NT>), grid, blk, 0, st, a); break;
+    case EE_XKV: hipLaunchKernelGGL((gemm_kernel<EE_XKV, MT, NT>), grid, blk, 0, st, a); break;
+    default: hipLaunchKernelGGL((gemm_kernel<EE_GELU, MT, NT>), grid, blk, 0, st, a); break;
     }
     return hipGetLastError();
+}
+
+// 128 x 256 tiles, or 64 x 128 when those would leave most of the 256 CUs
+// idle (a window or two through the d-wide projections)
+hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
+    if (a.K % (2 * GBK) || a.M < 1 || a.N % 4) return hipErrorInvalidValue;   // loop unrolled by 2
+    const bool small = cdiv(a.M, 128) * cdiv(a.N, 256) < 128;
+    a.n_m = cdiv(a.M, small ? 64 : 128);
+    a.n_n = cdiv(a.N, small ? 128 : 256);
+    a.n_wg = a.n_m * a.n_n;
+    return small ? launch_tiles<2, 4>(epi, a, st) : launch_tiles<4, 8>(epi, a, st);
 }
 
 }  // namespace enc

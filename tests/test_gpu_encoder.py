@@ -6,9 +6,10 @@
   against the oracle's fp64 forward.
 * Full large-v3 width (1280, 20 heads, MLP 5120, 128 mel channels, 1500
   frames) with 2 blocks: one request against the oracle, and batch
-  invariance (a request encoded inside a batch of two equals the same
-  request alone, bit for bit: no kernel mixes requests or depends on the
-  batch size).
+  invariance (a request encoded inside a batch of four equals the same
+  request alone, bit for bit: no kernel mixes requests, and the smaller
+  GEMM tiles a lone window's d-wide projections take do not change any
+  element's arithmetic).
 * The full 32-block encoder: finite outputs whose rows have mean 0 and
   variance 1 (the final norm with unit gain), and the audio memory it
   produces drives wf_encode_kv and a verify pass.
@@ -77,13 +78,13 @@ def test_large_width_two_blocks_and_batch_invariance(torch_cuda):
     from speculative_decoding_encoder_amd.binding import Encoder
     s = dataclasses.replace(ENC_LARGE_V3, n_layers=2)
     wb = make_encoder_weights(s, 1)
-    enc = Encoder(s, wb, max_batch=2)
-    mels = [make_mel(s, 1, r) for r in range(2)]
-    both = _encode(torch_cuda, enc, mels)
-    alone = _encode(torch_cuda, enc, mels[1:])
-    assert np.array_equal(both[1].view(np.uint32), alone[0].view(np.uint32))
-    log("large-width encoder: request 1 in a batch of 2 equals request 1 alone")
-    _close(both[0], oe.Encoder(s, wb).forward(mels[0]), "large-width 2-block encoder req 0")
+    enc = Encoder(s, wb, max_batch=4)
+    mels = [make_mel(s, 1, r) for r in range(4)]
+    four = _encode(torch_cuda, enc, mels)
+    alone = _encode(torch_cuda, enc, mels[1:2])
+    assert np.array_equal(four[1].view(np.uint32), alone[0].view(np.uint32))
+    log("large-width encoder: request 1 in a batch of 4 equals request 1 alone")
+    _close(four[0], oe.Encoder(s, wb).forward(mels[0]), "large-width 2-block encoder req 0")
     enc.close()
 
 
