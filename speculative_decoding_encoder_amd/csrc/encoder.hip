@@ -274,10 +274,33 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     for (int i = 0; i < MT; ++i) {
         const int m = m0 + wm * 16 * MT + i * 16 + r16;
         if (m >= a.M) continue;
+        if constexpr (EPI == EE_RESID) {
+            // the residual read-modify-write: all of the row's loads first, so
+            // their latencies overlap (columns past N load a valid address)
+            float4 xv[NT];
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-            const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
-            if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
+            for (int j = 0; j < NT; ++j) {
+                const int n = min(n0 + wn * 16 * NT + j * 16 + 4 * g, a.N - 4);
+                xv[j] = *reinterpret_cast<const float4 *>(a.x + (size_t)m * a.N + n);
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
+                if (n >= a.N) continue;
+                const f32x4 c = acc[i][j];
+                float4 v = xv[j];
+                v.x += c[0] + bias4(a.b0, n, 0);
+                v.y += c[1] + bias4(a.b0, n, 1);
+                v.z += c[2] + bias4(a.b0, n, 2);
+                v.w += c[3] + bias4(a.b0, n, 3);
+                *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
+                if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
+            }
         }
     }
 }
