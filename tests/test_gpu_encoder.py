@@ -125,3 +125,36 @@ def test_full_encoder_feeds_the_decoder(torch_cuda):
     assert (err == 0).all() and (am.cpu().numpy()[0, :len(prefixes[0])] >= 0).all()
     eng.close()
     enc.close()
+
+
+def test_graph_replays_equal_the_eager_encode(torch_cuda):
+    """wf_encode allocates and clears nothing per call (its padding was
+    zeroed at create), so it can be captured in a HIP graph: every replay,
+    with eager calls and synchronisations between, gives the eager bits."""
+    from speculative_decoding_encoder_amd.binding import Encoder
+    torch = torch_cuda
+    s = ENC_SMALL
+    wb = make_encoder_weights(s, 3, ln_random=True)
+    enc = Encoder(s, wb, max_batch=2)
+    d_mel = enc.bf16(np.stack([make_mel(s, 3, r) for r in range(2)]))
+    out = torch.empty((2, s.n_frames, s.d_model), dtype=torch.int16, device=enc.dev)
+    enc.wf_encode(d_mel, out)
+    torch.cuda.synchronize()
+    ref = out.cpu().numpy().copy()
+    stream = torch.cuda.Stream()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        enc.wf_encode(d_mel, out, stream)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        out.fill_(0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), ref), rep
+        enc.wf_encode(d_mel[:1], out[:1])          # eager work between the replays
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy()[0], ref[0]), rep
+    log("encoder graph: 3 replays equal the eager call")
+    del graph
+    enc.close()
