@@ -30,8 +30,8 @@
 //    queries; 64-key steps of K ([key][dim]) and V^T ([dim][key]) through
 //    double-buffered LDS. S^T = K Q^T and O^T += V^T P^T keep a query per
 //    lane, so P stays in registers as the B operand (bf16) and only the
-//    running max crosses lanes (two exchanges) per step; the row sums are
-//    per-lane partials combined once at the end.
+//    running max crosses lanes (two exchanges) per step; the row sums come
+//    from the MFMA too (a tile of ones times P^T).
 #include "../../include/wf.h"
 #include "wf_device.h"
 
@@ -364,12 +364,16 @@ __global__ __launch_bounds__(256, QT == 1 ? 3 : (QT == 2 ? 2 : 1)) void attn_ker
         }
     };
 
-    float mrow[QT], lsum[QT];
+    // row sums ride on the MFMA: a tile of ones times P^T adds, in every
+    // row of lsum[s], the bf16 probabilities the PV product uses
+    const u32x4 ones = u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+    float mrow[QT];
+    f32x4 lsum[QT];
     f32x4 o[4][QT];
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
         mrow[s] = -INFINITY;
-        lsum[s] = 0.f;
+        lsum[s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) o[dt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -429,16 +433,12 @@ __global__ __launch_bounds__(256, QT == 1 ? 3 : (QT == 2 ? 2 : 1)) void attn_ker
             const float ms = mnew * a.sl2e;
             const float alpha = __builtin_amdgcn_exp2f(__fmaf_rn(mrow[s], a.sl2e, -ms));
             mrow[s] = mnew;
-            float ps = 0.f;
 #pragma unroll
             for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = __builtin_amdgcn_exp2f(__fmaf_rn(sc[kt][r], a.sl2e, -ms));
-                    sc[kt][r] = p;
-                    ps += p;
-                }
-            lsum[s] = __fmaf_rn(lsum[s], alpha, ps);
+                for (int r = 0; r < 4; ++r)
+                    sc[kt][r] = __builtin_amdgcn_exp2f(__fmaf_rn(sc[kt][r], a.sl2e, -ms));
+            lsum[s] = lsum[s] * alpha;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const u32x4 pf = u32x4{pack_bf2(sc[2 * kk][0], sc[2 * kk][1]),
@@ -450,6 +450,7 @@ __global__ __launch_bounds__(256, QT == 1 ? 3 : (QT == 2 ? 2 : 1)) void attn_ker
                     if (kk == 0) o[dt][s] = o[dt][s] * alpha;
                     o[dt][s] = mfma_bf16_k32(vf[dt][kk], pf, o[dt][s]);
                 }
+                lsum[s] = mfma_bf16_k32(ones, pf, lsum[s]);
             }
         }
         if (st + 1 < steps) sstore(b ^ 1);
@@ -457,12 +458,7 @@ __global__ __launch_bounds__(256, QT == 1 ? 3 : (QT == 2 ? 2 : 1)) void attn_ker
     }
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
-        float l = lsum[s], x0, x1;
-        rows16_pair(l, x0, x1);
-        l = x0 + x1;
-        halves32_pair(l, x0, x1);
-        l = x0 + x1;
-        const float inv = 1.0f / l;
+        const float inv = 1.0f / lsum[s][0];      // every row of the tile holds the sum
         const int qi = q0 + 16 * s + r16;
         if (qi >= a.F) continue;
         uint16_t *dst = a.o + ((size_t)rq * a.F + qi) * a.d + h * 64 + 4 * g;
