@@ -158,3 +158,20 @@ def test_graph_replays_equal_the_eager_encode(torch_cuda):
     log("encoder graph: 3 replays equal the eager call")
     del graph
     enc.close()
+
+
+def test_encode_rejects_more_windows_than_max_batch(torch_cuda):
+    from speculative_decoding_encoder_amd.binding import Encoder, WFError
+    torch = torch_cuda
+    s = ENC_SMALL
+    enc = Encoder(s, make_encoder_weights(s, 0), max_batch=1)
+    d_mel = enc.bf16(np.stack([make_mel(s, 0, r) for r in range(2)]))
+    out = torch.zeros((2, s.n_frames, s.d_model), dtype=torch.int16, device=enc.dev)
+    with pytest.raises(WFError):
+        enc.wf_encode(d_mel, out)
+    torch.cuda.synchronize()
+    assert not out.any()                       # nothing was launched
+    enc.wf_encode(d_mel[:1], out[:1])          # the encoder is still usable
+    torch.cuda.synchronize()
+    assert out[0].any()
+    enc.close()
