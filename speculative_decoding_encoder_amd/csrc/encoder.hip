@@ -234,6 +234,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
         for (int i = 0; i < MT; ++i)
             xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 16 * MT + i * 16 + r16) * GROW + g * 8]);
+        __builtin_amdgcn_s_setprio(1);              // the MFMA block issues first on its SIMD
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             u32x4 wf[NT / 2];
@@ -247,6 +248,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
                 for (int j = 0; j < NT / 2; ++j)
                     acc[i][NT / 2 * h + j] = mfma_bf16_k32(wf[j], xf[i], acc[i][NT / 2 * h + j]);
         }
+        __builtin_amdgcn_s_setprio(0);
     };
     // k-step kt is read from LDS buffer kt & 1; its global loads were issued
     // two k-steps earlier (register sets r0 / r1 alternate), so a load has
