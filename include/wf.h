@@ -39,9 +39,11 @@
  *    across the ABI.
  *
  * Numerics
- *  - Weights are bf16. GEMMs run on bf16 MFMA with fp32 accumulation; the
- *    activation operand is carried as an unevaluated pair of bf16 values
- *    (hi + lo), so its rounding error is about 2^-16 relative.
+ *  - Weights are bf16. The decoder GEMMs take fp16 activations (layer-norm,
+ *    attention and GELU outputs rounded to fp16, about 2^-11 relative)
+ *    against the bf16 weights converted to fp16 in registers, on fp16 MFMA
+ *    with fp32 accumulation; wf_encode_kv multiplies the bf16 audio memory
+ *    on bf16 MFMA.
  *  - The residual stream, layer-norm statistics, softmax and GELU are fp32.
  *  - Self-attention K/V pages and cross-attention K/V are stored in fp16;
  *    attention products run on fp16 MFMA with fp32 accumulation.
@@ -81,6 +83,9 @@ typedef enum {
 #define WF_DERR_NAN     16  /* a NaN logit */
 #define WF_DERR_PAGE    32  /* page-table entry outside [0, n_pages) */
 #define WF_DERR_SAMPLE  64  /* sampling inputs missing or q(y) = 0 for a draft */
+#define WF_DERR_TIMEOUT 128 /* the persistent pass hit its internal wait limit
+                               (WF_OPT_PASS_TIMEOUT_US); that pass's outputs are
+                               not valid */
 
 /* Model and capacity description. The supported shapes have head_dim 16 or
  * 64, d_model = n_heads * head_dim with d_model a multiple of 64, d_ffn a
@@ -328,6 +333,48 @@ wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *st
  * history append inside the verify pass. */
 wf_status wf_set_timing(wf_engine *e, int32_t enable);
 wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *count);
+/* Kind 12: the persistent pass kernel (below), one launch per verify pass. */
+
+/* Execution-path options of an engine (host state, read at each call; the
+ * defaults are the fastest paths). None changes a result beyond the
+ * summation order named here:
+ *  WF_OPT_PERSISTENT (default 1): run a linear verify pass whose model has
+ *    d_model 1280, d_ffn 5120 and head_dim 64, with n * T <= 1024 and
+ *    T <= 64 and no anchor readout, as one persistent kernel: one workgroup
+ *    per CU walks every layer's tasks and waits for the rows it reads on
+ *    arrival counters. Bit-identical to the multi-kernel path. 0 runs the
+ *    multi-kernel path. A pass that exceeds the kernel's internal wait limit
+ *    sets WF_DERR_TIMEOUT in its requests' error words.
+ *  WF_OPT_TALL_GEMM, WF_OPT_LN_FUSION (default 1): the tall-block GEMM for
+ *    blocks of 97..1024 rows, the layer norm in the GEMM prologue for one
+ *    row tile; 0 takes the other GEMM kernels (bit-identical).
+ *  WF_OPT_XA_CHUNKS (default 0 = chosen by batch size; 4, 8, 16 or 32):
+ *    frame chunks per (request, head) of cross-attention; this changes the
+ *    cross-attention summation order (every choice is still independent of
+ *    the block length).
+ *  WF_OPT_PASS_TIMEOUT_US (default 500000): the persistent pass's wait limit
+ *    in microseconds, measured per wait. Past it the pass aborts (every
+ *    wait ends at once, every workgroup drains) and sets WF_DERR_TIMEOUT;
+ *    a small value forces that path, for tests of the error handling.
+ * Unknown options or values return WF_EINVAL. */
+#define WF_OPT_PERSISTENT 1
+#define WF_OPT_TALL_GEMM  2
+#define WF_OPT_LN_FUSION  3
+#define WF_OPT_XA_CHUNKS  4
+#define WF_OPT_PASS_TIMEOUT_US 5
+wf_status wf_set_option(wf_engine *e, int32_t option, int32_t value);
+
+/* Task trace of the persistent pass: with d_trace non-NULL (device memory,
+ * bytes / 16 tasks; the caller keeps it alive), every later persistent pass
+ * whose task list fits writes for task t the 100 MHz device clock at its
+ * start and end (uint64 [t][2]). NULL turns it off. wf_pass_schedule copies
+ * the last pass's task list layout to h_info (int32 [20]): total tasks,
+ * tasks per layer, layers, the 12 phase offsets within a layer (LN1, QKV,
+ * self-attention, O, LN2, cross Q, cross-attention, O_c, LN3, fc1, fc2, end),
+ * the 3 head offsets after the layers (final LN, LM head, end) and the
+ * grid. */
+wf_status wf_set_trace(wf_engine *e, void *d_trace, size_t bytes);
+wf_status wf_pass_schedule(wf_engine *e, int32_t *h_info);
 
 
 /* ------------------------------------------------------------------------

@@ -118,6 +118,9 @@ def load():
         "wf_set_timing": (I32, [P, I32]),
         "wf_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
                                 ctypes.POINTER(ctypes.c_int32)]),
+        "wf_set_option": (I32, [P, I32, I32]),
+        "wf_set_trace": (I32, [P, P, SZ]),
+        "wf_pass_schedule": (I32, [P, ctypes.POINTER(ctypes.c_int32)]),
         "wf_enc_workspace_bytes": (SZ, [ctypes.POINTER(EncConfig)]),
         "wf_enc_create": (I32, [ctypes.POINTER(EncConfig), ctypes.POINTER(EncWeights), P, SZ,
                                 ctypes.POINTER(VP)]),
@@ -318,6 +321,23 @@ class Engine:
                "wf_get_timing")
         return ms.value, cnt.value
 
+    def wf_set_option(self, option: int, value: int):
+        _check(self.lib.wf_set_option(self.h, int(option), int(value)), "wf_set_option")
+
+    def wf_set_trace(self, buf=None):
+        """buf: a device tensor (uint64 [tasks][2]) or None to stop tracing."""
+        nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+        _check(self.lib.wf_set_trace(self.h, _p(buf), nbytes), "wf_set_trace")
+
+    def wf_pass_schedule(self):
+        """Task-list layout of the last persistent pass: dict of total,
+        per_layer, layers, phase offsets (12), head offsets (3), grid."""
+        info = (ctypes.c_int32 * 20)()
+        _check(self.lib.wf_pass_schedule(self.h, info), "wf_pass_schedule")
+        v = list(info)
+        return {"total": v[0], "per_layer": v[1], "layers": v[2], "ph_off": v[3:15],
+                "head_off": v[15:18], "grid": v[18]}
+
     # -- helpers ---------------------------------------------------------
     def i32(self, a: Sequence[int]):
         return self.torch.as_tensor(np.asarray(a, dtype=np.int32), device=self.dev)
@@ -328,7 +348,14 @@ class Engine:
 
 
 TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn", "cross_attn",
-                "other", "encode_kv", "draft", "history"]
+                "other", "encode_kv", "draft", "history", "pass"]
+
+# wf_set_option options (include/wf.h)
+WF_OPT_PERSISTENT, WF_OPT_TALL_GEMM, WF_OPT_LN_FUSION, WF_OPT_XA_CHUNKS = 1, 2, 3, 4
+WF_OPT_PASS_TIMEOUT_US = 5
+WF_DERR_TIMEOUT = 128
+PASS_PHASES = ["ln1", "qkv", "self_attn", "oproj", "ln2", "cross_q", "cross_attn", "oproj_c",
+               "ln3", "fc1", "fc2"]
 
 
 ENC_TIMING_KINDS = ["stem", "qkv", "attn", "oproj", "fc1", "fc2", "ln", "other"]

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libwf.so")
 SOURCES = ["engine.hip", "k_gemm.hip", "k_gemm_rk_attn.hip", "k_gemm_rk_mlp.hip",
-           "k_gemm_rk_head.hip", "k_attn.hip", "k_misc.hip", "k_sample.hip", "k_draft.hip", "encoder.hip"]
+           "k_gemm_rk_head.hip", "k_attn.hip", "k_misc.hip", "k_sample.hip", "k_draft.hip", "k_pass.hip", "encoder.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

@@ -685,7 +685,7 @@ struct wf_encoder {
     const uint16_t *c1b, *c2b, *lnp_g, *lnp_b;
     uint16_t *melT, *g1, *h, *q, *k, *vt, *o, *hid, *w1r, *w2r;
     float *x, *pos;
-    int attn_qt = 2;   // 16-query subtiles per attention wave (WF_ENC_ATTN_QT=1 / 4: a tuning aid)
+    int attn_qt = 2;   // 16-query subtiles per attention wave (measured best of 1, 2, 4)
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
     size_t ev_used = 0;
@@ -796,10 +796,6 @@ wf_status wf_enc_create(const wf_enc_config *cfg, const wf_enc_weights *w, void 
 
     wf_encoder *e = new wf_encoder();
     e->c = *cfg;
-    if (const char *v = std::getenv("WF_ENC_ATTN_QT")) {
-        const int q = std::atoi(v);
-        e->attn_qt = q == 4 ? 4 : (q == 1 ? 1 : 2);
-    }
     e->lay = layout_of(cfg);
     const Layout &L = e->lay;
     char *ws = (char *)workspace;

@@ -28,12 +28,6 @@ wf_status fail(wf_status s, const char *fmt, ...) {
     return s;
 }
 
-struct LayerW {
-    const uint16_t *ln1_g, *ln1_b, *wq, *bq, *wk, *wv, *bv, *wo, *bo;
-    const uint16_t *ln2_g, *ln2_b, *wqc, *bqc, *wkc, *wvc, *bvc, *woc, *boc;
-    const uint16_t *ln3_g, *ln3_b, *w1, *b1, *w2, *b2;
-};
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
@@ -50,16 +44,14 @@ constexpr int kSplitRowsCap = 128;   // GEMM K-split scratch sized for this many
 // each (a multiple of the load ring depth), then the fewest chunks (a
 // multiple of 4, one per wave of a group) that still cover the frames at that
 // length. Depends on the number of requests only, never on the block length,
-// so a row's bits do not depend on its block. WF_XA_CHUNKS (4, 8, 16 or 32)
-// fixes the first choice: a tuning aid.
-void cross_chunks(int n, int H, int F, int &cf, int &G, int &spw) {
+// so a row's bits do not depend on its block. want_chunks (4, 8, 16 or 32;
+// wf_set_option WF_OPT_XA_CHUNKS) fixes the first choice instead.
+void cross_chunks(int n, int H, int F, int want_chunks, int &cf, int &G, int &spw) {
     const int steps = cdiv(F, 32);
     const int want = cdiv(2048, n * H);
     int C = want >= 32 ? 32 : (want >= 16 ? 16 : (want >= 8 ? 8 : 4));
-    if (const char *ov = std::getenv("WF_XA_CHUNKS")) {
-        const int o = std::atoi(ov);
-        if (o == 4 || o == 8 || o == 16 || o == 32) C = o;
-    }
+    if (want_chunks == 4 || want_chunks == 8 || want_chunks == 16 || want_chunks == 32)
+        C = want_chunks;
     spw = cdiv(cdiv(steps, C), kXaRing) * kXaRing;
     C = cdiv(cdiv(steps, spw), 4) * 4;
     cf = spw * 32;
@@ -71,10 +63,25 @@ int all_layers(const wf_config *c) { return c->n_layers + c->drafter_layers; }
 struct Layout {
     size_t x, xs, hs, q, tdepth, tanc, rdml, rdpart, part, gcnt, xapart, xacnt, lmmax, lmidx, reqL, reqN, len, pend, err;
     size_t taps, dam, rowkv;
+    // persistent pass (absent when pass_rows == 0): per-layer activations,
+    // written once per launch, the arrival counters and the weight table
+    size_t pxv, plnv, pqv, pcqv, psav, pxav, phsv, pcnt, plw;
+    int pass_rows;                 // rows (multiple of 16) the pass buffers hold
     size_t total;
     size_t part_bytes, xapart_bytes;
     int n_vtiles;
 };
+
+// The persistent pass covers the Whisper large-v3 / turbo decoder width
+// (its GEMM chunking and layer-norm registers are built for d = 1280, MLP
+// 5120, head_dim 64) and blocks of up to 1024 rows.
+bool pass_shape_ok(const wf_config *c) {
+    return c->d_model == 1280 && c->d_ffn == 5120 && c->head_dim == 64;
+}
+int pass_rows_of(const wf_config *c) {
+    if (!pass_shape_ok(c)) return 0;
+    return std::min((c->max_rows + 15) / 16 * 16, kPassMaxRows);
+}
 
 bool config_ok(const wf_config *c, std::string *why) {
     auto bad = [&](const char *m) { if (why) *why = m; return false; };
@@ -144,6 +151,20 @@ Layout layout_of(const wf_config *c) {
     L.taps = take(c->drafter_layers > 0 ? Mp * (size_t)c->n_taps * d * 2 : 0);
     L.dam = take(M * 4);
     L.rowkv = take(M * 4);
+    L.pass_rows = pass_rows_of(c);
+    if (L.pass_rows > 0) {
+        const size_t Pm = (size_t)L.pass_rows, NL = (size_t)c->n_layers;
+        L.pxv = take((3 * NL + 1) * Pm * d * 4);
+        L.plnv = take((3 * NL + 1) * Pm * d * 2);
+        L.pqv = take(NL * Pm * d * 2);
+        L.pcqv = take(NL * Pm * d * 2);
+        L.psav = take(NL * Pm * d * 2);
+        L.pxav = take(NL * Pm * d * 2);
+        L.phsv = take(NL * Pm * f * 2);
+        // counters [(NL * phases + 2) * 64 tiles], then the abort flag
+        L.pcnt = take(((NL * PH_PER_LAYER + 2) * 64 + 64) * 4);
+        L.plw = take(NL * sizeof(LayerW));
+    }
     L.total = o;
     return L;
 }
@@ -152,7 +173,8 @@ int f_pad_of(const wf_config *c) { return cdiv(c->n_frames, 32) * 32; }
 
 enum TimingKind {
     TK_QKV = 0, TK_OPROJ = 1, TK_QC = 2, TK_FC1 = 3, TK_FC2 = 4, TK_LMHEAD = 5,
-    TK_SELF = 6, TK_CROSS = 7, TK_OTHER = 8, TK_XKV = 9, TK_DRAFT = 10, TK_HIST = 11, TK_N = 12
+    TK_SELF = 6, TK_CROSS = 7, TK_OTHER = 8, TK_XKV = 9, TK_DRAFT = 10, TK_HIST = 11,
+    TK_PASS = 12, TK_N = 13
 };
 
 }  // namespace
@@ -186,9 +208,22 @@ struct wf_engine {
     int32_t *lmidx;
     int32_t *reqL, *reqN, *len, *pend, *err;
     int32_t *rowkv;                          // per verify row: KV page * 16 + offset, or -1
-    int tiles_ovr[16][3] = {};               // WF_GEMM_TILES: per role (mb, nb, P)
-    bool ln_fusion = true;                   // WF_LN_FUSION=0 turns the LN prologue off
-    bool tall_gemm = true;                   // WF_TALL_GEMM=0 turns the tall-block kernel off
+    bool ln_fusion = true;                   // wf_set_option(WF_OPT_LN_FUSION)
+    bool tall_gemm = true;                   // wf_set_option(WF_OPT_TALL_GEMM)
+    bool persistent = true;                  // wf_set_option(WF_OPT_PERSISTENT)
+    int n_cu = 0;                            // compute units: the pass kernel's grid
+    int xa_chunks = 0;                       // wf_set_option(WF_OPT_XA_CHUNKS); 0: by batch
+    int64_t pass_timeout_ticks = 50000000;   // wf_set_option(WF_OPT_PASS_TIMEOUT_US): 0.5 s
+    // persistent pass buffers (see Layout)
+    float *pxv = nullptr;
+    uint16_t *plnv = nullptr, *pqv = nullptr, *pcqv = nullptr, *psav = nullptr, *pxav = nullptr,
+             *phsv = nullptr;
+    int32_t *pcnt = nullptr;
+    LayerW *plw = nullptr;
+    uint64_t *trace = nullptr;               // wf_set_trace: per task (start, end)
+    size_t trace_tasks = 0;
+    int last_pass_tasks = 0;
+    int32_t last_sched[20] = {};             // total, per_layer, n_layers, ph_off[12], head_off[3]
     // optional per-kernel timing with HIP events
     bool timing = false;
     std::vector<hipEvent_t> ev_pool;
@@ -353,14 +388,6 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
                     P *= 2;
             }
         }
-        const int *o = e->tiles_ovr[role];
-        if (o[0] > 0 && (!fuse_ln || (o[0] == 1 && (o[1] == 1 || o[1] == 4)))) {
-            mb = o[0];
-            nb = o[1];
-            if (role == ROLE_LM_HEAD) nb = 4;
-            P = split_k_ok ? o[2] : 1;
-            if ((P != 1 && P != 2 && P != 4 && P != 8) || P > S || S % P || !fits(P)) P = 1;
-        }
         a.n_tiles = cdiv(N, 16 * nb);
         a.m_blocks = cdiv(M, 16 * mb);
         a.n_groups = P;
@@ -378,33 +405,6 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
     a.n_groups = 1;
     a.n_wg = a.n_tiles * a.m_blocks;
     return timed(e, kind, st, [&] { return launch_gemm(role, a, mb, st); });
-}
-
-// WF_GEMM_TILES="role:mb:nb:P;..." (role an integer or '*') fixes the tiles
-// of the register-tiled GEMM per role; a tuning aid, read at wf_create.
-void read_tile_override(wf_engine *e) {
-    const char *env = std::getenv("WF_GEMM_TILES");
-    if (!env) return;
-    std::string s(env);
-    size_t pos = 0;
-    while (pos < s.size()) {
-        size_t end = s.find(';', pos);
-        if (end == std::string::npos) end = s.size();
-        const std::string item = s.substr(pos, end - pos);
-        pos = end + 1;
-        char r[8] = {0};
-        int mb = 0, nb = 0, P = 0;
-        if (std::sscanf(item.c_str(), "%7[^:]:%d:%d:%d", r, &mb, &nb, &P) != 4) continue;
-        const bool ok_t = (mb == 1 || mb == 2 || mb == 4) && (nb == 1 || nb == 2 || nb == 4) &&
-                          !(mb > 1 && nb == 1) && (P == 1 || P == 2 || P == 4 || P == 8);
-        if (!ok_t) continue;
-        for (int role = 0; role < 16; ++role) {
-            if (r[0] != '*' && std::atoi(r) != role) continue;
-            e->tiles_ovr[role][0] = mb;
-            e->tiles_ovr[role][1] = nb;
-            e->tiles_ovr[role][2] = P;
-        }
-    }
 }
 
 #define WF_TRY(expr)                      \
@@ -485,9 +485,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     wf_engine *e = new wf_engine();
     e->c = *cfg;
     e->lay = layout_of(cfg);
-    read_tile_override(e);
-    if (const char *f = std::getenv("WF_LN_FUSION")) e->ln_fusion = std::strcmp(f, "0") != 0;
-    if (const char *f = std::getenv("WF_TALL_GEMM")) e->tall_gemm = std::strcmp(f, "0") != 0;
+    e->n_cu = prop.multiProcessorCount;
     e->F_pad = f_pad_of(cfg);
     e->pt_stride = cfg->n_ctx / cfg->page_size;
     e->page_elems = 2 * cfg->n_heads * cfg->page_size * cfg->head_dim;
@@ -548,9 +546,27 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
     e->rowkv = (int32_t *)(ws + L.rowkv);
     e->taps = (uint16_t *)(ws + L.taps);
     e->dam = (int32_t *)(ws + L.dam);
+    if (L.pass_rows > 0) {
+        e->pxv = (float *)(ws + L.pxv);
+        e->plnv = (uint16_t *)(ws + L.plnv);
+        e->pqv = (uint16_t *)(ws + L.pqv);
+        e->pcqv = (uint16_t *)(ws + L.pcqv);
+        e->psav = (uint16_t *)(ws + L.psav);
+        e->pxav = (uint16_t *)(ws + L.pxav);
+        e->phsv = (uint16_t *)(ws + L.phsv);
+        e->pcnt = (int32_t *)(ws + L.pcnt);
+        e->plw = (LayerW *)(ws + L.plw);
+    }
     if (hipMemset(workspace, 0, L.total) != hipSuccess || hipDeviceSynchronize() != hipSuccess) {
         delete e;
         return fail(WF_EHIP, "clearing the workspace failed");
+    }
+    if (L.pass_rows > 0 &&
+        (hipMemcpy(e->plw, e->layers.data(), e->layers.size() * sizeof(LayerW),
+                   hipMemcpyHostToDevice) != hipSuccess ||
+         hipDeviceSynchronize() != hipSuccess)) {
+        delete e;
+        return fail(WF_EHIP, "copying the layer weight table failed");
     }
     *out = e;
     return WF_OK;
@@ -598,7 +614,7 @@ namespace {
 void cross_plan(const wf_engine *e, int n, int mt, int &cf, int &G, int &spw) {
     const wf_config &c = e->c;
     const int H = c.n_heads, hd = c.head_dim;
-    cross_chunks(n, H, c.n_frames, cf, G, spw);
+    cross_chunks(n, H, c.n_frames, e->xa_chunks, cf, G, spw);
     const size_t rowbytes = (size_t)16 * (hd + 4) * 4;
     while (G > 1 && (size_t)n * H * mt * G * rowbytes > e->lay.xapart_bytes) {
         // long prefill blocks: fewer, longer chunks so the group partials fit
@@ -626,6 +642,7 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     EpiArgs ra{};
     ra.b0 = w.bo;
     ra.x = e->x;
+    ra.x_in = e->x;
     WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.wo, nullptr, nullptr, d, d, ra,
                     st));
     EpiArgs fa{};
@@ -659,6 +676,7 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     EpiArgs oa{};
     oa.b0 = w.boc;
     oa.x = e->x;
+    oa.x_in = e->x;
     WF_TRY(run_gemm(e, K_(p, TK_OPROJ), ROLE_OPROJ, e->xs, M, d, w.woc, nullptr, nullptr, d, d, oa,
                     st));
     EpiArgs ga{};
@@ -669,6 +687,7 @@ wf_status run_out_cross_mlp(wf_engine *e, const LayerW &w, int xkv_layer, const 
     EpiArgs f2{};
     f2.b0 = w.b2;
     f2.x = e->x;
+    f2.x_in = e->x;
     WF_TRY(run_gemm(e, K_(p, TK_FC2), ROLE_FC2, e->hs, M, c.d_ffn, w.w2, nullptr, nullptr, d, d, f2,
                     st));
     return WF_OK;
@@ -717,6 +736,175 @@ wf_status run_rope_append(wf_engine *e, int dl, const Pass &p, int ncols, int q_
     return timed(e, kind, st, [&] { return launch_rope_append(ra, st); });
 }
 
+int grid_of(const wf_engine *e) { return e->n_cu > 0 ? e->n_cu : 256; }
+
+// Drafter history of the rows just written to the cache: h = W_h taps (into
+// the residual buffer, free after the head), then per drafter layer
+// k = RoPE(W_k LN1(h)), v = W_v LN1(h) + b_v into its pages.
+wf_status run_history(wf_engine *e, const Pass &p, hipStream_t st) {
+    const wf_config &c = e->c;
+    if (c.drafter_layers <= 0) return WF_OK;
+    const int M = p.M, d = c.d_model;
+    EpiArgs ha{};
+    ha.out32 = e->x;
+    WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST, e->taps, M, c.n_taps * d, e->w_hist, nullptr,
+                    nullptr, d, d, ha, st));
+    for (int dl = 0; dl < c.drafter_layers; ++dl) {
+        const LayerW &w = e->dlayers[dl];
+        EpiArgs ka{};
+        ka.b1 = w.bv;
+        ka.out32 = reinterpret_cast<float *>(e->hs);
+        WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST_KV, e->xs, M, d, w.wk, w.wv, nullptr, d, 2 * d, ka,
+                        st, w.ln1_g, w.ln1_b));
+        WF_TRY(run_rope_append(e, dl, p, 2 * d, -1, 0, d, TK_HIST, st));
+    }
+    return WF_OK;
+}
+
+// The persistent pass (k_pass.hip): every layer, the final layer norm and the
+// LM head with its argmax in one launch after prepare and embed. Returns
+// WF_ESTATE when this pass cannot take it (the caller then runs the
+// multi-kernel path).
+wf_status run_pass(wf_engine *e, const Pass &p, const int32_t *d_tokens, const int32_t *d_n_tok,
+                   int32_t *d_argmax, float *d_logits, hipStream_t st) {
+    const wf_config &c = e->c;
+    const int n = p.n, T = p.T, M = p.M, d = c.d_model, H = c.n_heads, NL = c.n_layers;
+    const int cl = pass_class_of_rows(M);
+    PassArgs a{};
+    a.n = n;
+    a.T = T;
+    a.M = M;
+    a.RT = cdiv(M, 16);
+    a.mt = p.mt;
+    a.max_batch = c.max_batch;
+    a.n_layers = NL;
+    a.d = d;
+    a.H = H;
+    a.hd = c.head_dim;
+    a.F = c.d_ffn;
+    a.V = c.vocab;
+    a.ln_eps = c.ln_eps;
+    a.scale = 1.0f / std::sqrt((float)c.head_dim);
+    // tilings: column tiles, row blocks and K groups of every projection
+    const int Ns[PG_N] = {3 * d, d, d, d, c.d_ffn, d, c.vocab};
+    for (int g = 0; g < PG_N; ++g) {
+        int bm = 0, bn = 0, P = 0;
+        pass_tiling(cl, g, bm, bn, P);
+        if (bm == 0) return WF_ESTATE;
+        PassGemmCfg &t = a.g[g];
+        t.n_tiles = cdiv(Ns[g], bn);
+        t.m_blocks = cdiv(M, bm);
+        t.n_groups = P;
+        t.n_tasks = cdiv(t.n_tiles, 8) * 8 * t.m_blocks * P;
+        if (g == PG_LMH && bn != 64) return WF_ESTATE;
+        if (P > 1) {
+            // K-group sums: per (tile, row block) P groups of whole MFMA tiles
+            const size_t bytes = (size_t)t.n_tiles * t.m_blocks * P * bm * bn * 4;
+            if (bytes > e->lay.part_bytes) return WF_ESTATE;
+        }
+    }
+    WF_TRY(timed(e, TK_OTHER, st, [&] {
+        PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
+                       p.slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL,
+                       e->reqN, nullptr, e->tdepth, e->tanc};
+        return launch_prepare(pa, st);
+    }));
+    const int n_cnt = (NL * PH_PER_LAYER + 2) * 64 + 64;
+    WF_TRY(timed(e, TK_OTHER, st, [&] { return launch_fill_i32(e->pcnt, n_cnt, 0, st); }));
+    const size_t Pm = (size_t)e->lay.pass_rows;
+    WF_TRY(timed(e, TK_OTHER, st, [&] {
+        EmbedArgs ema{M,        T,      d,       c.vocab, c.n_ctx, d_tokens, e->reqL,
+                      e->tok_emb, e->pos_emb, e->pxv, e->reqN, p.slots, e->pt, e->pt_stride,
+                      e->rowkv, nullptr};
+        return launch_embed(ema, st);
+    }));
+    a.lw = e->plw;
+    a.tok_emb = e->tok_emb;
+    a.lnf_g = e->lnf_g;
+    a.lnf_b = e->lnf_b;
+    a.slots = p.slots;
+    a.req_L = e->reqL;
+    a.req_ntok = e->reqN;
+    a.row_kv = e->rowkv;
+    a.page_table = e->pt;
+    a.slot_err = e->err;
+    a.pt_stride = e->pt_stride;
+    a.page_elems = e->page_elems;
+    a.kv = e->kv;
+    a.kv_layer_elems = (int64_t)e->kv_layer_elems;
+    a.xkv = e->xkv;
+    a.xkv_slot_elems = (int64_t)e->xkv_slot_elems;
+    a.xkv_layer_elems = (int64_t)e->xkv_layer_elems;
+    a.n_frames = c.n_frames;
+    a.F_pad = e->F_pad;
+    a.xa_G = p.G;
+    a.xa_cf = p.cf;
+    a.xa_spw = p.spw;
+    a.xv = e->pxv;
+    a.lnv = e->plnv;
+    a.qv = e->pqv;
+    a.cqv = e->pcqv;
+    a.sav = e->psav;
+    a.xav = e->pxav;
+    a.hsv = e->phsv;
+    a.x_stride = (int64_t)(Pm * d);
+    a.act_stride = (int64_t)(Pm * d);
+    a.q_stride = (int64_t)(Pm * d);
+    a.hs_stride = (int64_t)(Pm * c.d_ffn);
+    a.part = e->part;
+    a.gcnt = e->gcnt;
+    a.xapart = e->xapart;
+    a.xacnt = e->xacnt;
+    a.logits = d_logits;
+    a.tile_max = e->lmmax;
+    a.tile_idx = e->lmidx;
+    a.ld = e->lay.n_vtiles;
+    a.n_vtiles = e->lay.n_vtiles;
+    a.argmax = d_argmax;
+    a.taps = e->taps;
+    a.n_taps = c.drafter_layers > 0 ? c.n_taps : 0;
+    for (int j = 0; j < 8; ++j) a.tap_layers[j] = c.tap_layers[j];
+    a.cnt = e->pcnt;
+    a.abort_flag = e->pcnt + (NL * PH_PER_LAYER + 2) * 64;
+    const int n_ln = cdiv(a.RT, 2);
+    a.sa_items = n * H * p.mt;
+    a.xa_items = n * H * p.mt * p.G;
+    const int per[PH_PER_LAYER] = {n_ln,
+                                   a.g[PG_QKV].n_tasks,
+                                   cdiv(a.sa_items, 2),
+                                   a.g[PG_O].n_tasks,
+                                   n_ln,
+                                   a.g[PG_CQ].n_tasks,
+                                   cdiv(a.xa_items, 2),
+                                   a.g[PG_OC].n_tasks,
+                                   n_ln,
+                                   a.g[PG_FC1].n_tasks,
+                                   a.g[PG_FC2].n_tasks};
+    int off = 0;
+    for (int k = 0; k < PH_PER_LAYER; ++k) {
+        a.ph_off[k] = off;
+        off += per[k];
+    }
+    a.ph_off[PH_PER_LAYER] = off;
+    a.per_layer = off;
+    a.head_off[0] = 0;
+    a.head_off[1] = n_ln;
+    a.head_off[2] = n_ln + a.g[PG_LMH].n_tasks;
+    a.total = NL * a.per_layer + a.head_off[2];
+    a.timeout_ticks = e->pass_timeout_ticks;   // 100 MHz clock; a pass takes milliseconds
+    a.trace = (e->trace && (size_t)a.total <= e->trace_tasks) ? e->trace : nullptr;
+    e->last_pass_tasks = a.total;
+    e->last_sched[0] = a.total;
+    e->last_sched[1] = a.per_layer;
+    e->last_sched[2] = NL;
+    for (int k = 0; k <= PH_PER_LAYER; ++k) e->last_sched[3 + k] = a.ph_off[k];
+    for (int k = 0; k < 3; ++k) e->last_sched[15 + k] = a.head_off[k];
+    e->last_sched[18] = grid_of(e);
+    const int grid = grid_of(e);
+    WF_TRY(timed(e, TK_PASS, st, [&] { return launch_pass(a, cl, grid, st); }));
+    return run_history(e, p, st);
+}
+
 }  // namespace
 
 // One verify pass; d_parents (nullable) makes the block a token tree.
@@ -734,6 +922,12 @@ static wf_status verify_pass(wf_engine *e, int32_t n, const int32_t *d_slots,
     const int M = n * T, d = c.d_model, H = c.n_heads, hd = c.head_dim;
     Pass p{n, T, M, cdiv(T, 16), 0, 0, 0, d_slots, -1};
     cross_plan(e, n, p.mt, p.cf, p.G, p.spw);
+
+    if (e->persistent && e->lay.pass_rows > 0 && !d_parents && e->readout_layer < 0 && T <= 64 &&
+        M <= e->lay.pass_rows) {
+        const wf_status s = run_pass(e, p, d_tokens, d_n_tok, d_argmax, d_logits, st);
+        if (s != WF_ESTATE) return s;   // WF_ESTATE: this shape takes the multi-kernel path
+    }
 
     PrepareArgs pa{n, T, c.vocab, c.n_ctx, c.n_pages, e->pt_stride, c.page_size, c.max_batch,
                    d_slots, d_tokens, d_n_tok, e->pt, e->len, e->pend, e->err, e->reqL, e->reqN,
@@ -787,26 +981,7 @@ static wf_status verify_pass(wf_engine *e, int32_t n, const int32_t *d_slots,
         }
     }
     WF_TRY(run_head(e, e->lnf_g, e->lnf_b, p, d_logits, d_argmax, st));
-
-    if (c.drafter_layers > 0) {
-        // drafter history of the rows just written to the cache: h = W_h taps
-        // (into the residual buffer, free after the head), then per drafter
-        // layer k = RoPE(W_k LN1(h)), v = W_v LN1(h) + b_v into its pages
-        EpiArgs ha{};
-        ha.out32 = e->x;
-        WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST, e->taps, M, c.n_taps * d, e->w_hist, nullptr,
-                        nullptr, d, d, ha, st));
-        for (int dl = 0; dl < c.drafter_layers; ++dl) {
-            const LayerW &w = e->dlayers[dl];
-            EpiArgs ka{};
-            ka.b1 = w.bv;
-            ka.out32 = reinterpret_cast<float *>(e->hs);
-            WF_TRY(run_gemm(e, TK_HIST, ROLE_HIST_KV, e->xs, M, d, w.wk, w.wv, nullptr, d, 2 * d, ka,
-                            st, w.ln1_g, w.ln1_b));
-            WF_TRY(run_rope_append(e, dl, p, 2 * d, -1, 0, d, TK_HIST, st));
-        }
-    }
-    return WF_OK;
+    return run_history(e, p, st);
 }
 
 wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
@@ -974,6 +1149,38 @@ wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *st
         return fail(WF_EHIP, "copy of error words failed");
     if (h_len && hipMemcpy(h_len, e->len, bytes, hipMemcpyDeviceToHost) != hipSuccess)
         return fail(WF_EHIP, "copy of lengths failed");
+    return WF_OK;
+}
+
+wf_status wf_set_option(wf_engine *e, int32_t option, int32_t value) {
+    if (!e) return fail(WF_EINVAL, "null engine");
+    switch (option) {
+        case WF_OPT_PERSISTENT: e->persistent = value != 0; return WF_OK;
+        case WF_OPT_TALL_GEMM: e->tall_gemm = value != 0; return WF_OK;
+        case WF_OPT_LN_FUSION: e->ln_fusion = value != 0; return WF_OK;
+        case WF_OPT_XA_CHUNKS:
+            if (value != 0 && value != 4 && value != 8 && value != 16 && value != 32)
+                return fail(WF_EINVAL, "WF_OPT_XA_CHUNKS takes 0, 4, 8, 16 or 32");
+            e->xa_chunks = value;
+            return WF_OK;
+        case WF_OPT_PASS_TIMEOUT_US:
+            if (value < 0) return fail(WF_EINVAL, "WF_OPT_PASS_TIMEOUT_US must be >= 0");
+            e->pass_timeout_ticks = (int64_t)value * 100;
+            return WF_OK;
+    }
+    return fail(WF_EINVAL, "unknown option %d", option);
+}
+
+wf_status wf_set_trace(wf_engine *e, void *d_trace, size_t bytes) {
+    if (!e) return fail(WF_EINVAL, "null engine");
+    e->trace = d_trace ? (uint64_t *)d_trace : nullptr;
+    e->trace_tasks = d_trace ? bytes / 16 : 0;
+    return WF_OK;
+}
+
+wf_status wf_pass_schedule(wf_engine *e, int32_t *h_info) {
+    if (!e || !h_info) return fail(WF_EINVAL, "null argument");
+    for (int k = 0; k < 20; ++k) h_info[k] = e->last_sched[k];
     return WF_OK;
 }
 

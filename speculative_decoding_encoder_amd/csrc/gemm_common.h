@@ -58,7 +58,7 @@ template <int EPI>
 __device__ __forceinline__ uint32_t epi_load(const GemmArgs &a, int m, int n) {
     m = min(m, a.M - 1);
     if constexpr (EPI == EPI_RESID)
-        return __float_as_uint(a.e.x[(size_t)m * a.N + min(n, a.N - 1)]);
+        return __float_as_uint(a.e.x_in[(size_t)m * a.N + min(n, a.N - 1)]);
     else if constexpr (EPI == EPI_QKV)
         return (uint32_t)a.e.row_kv[m];
     else

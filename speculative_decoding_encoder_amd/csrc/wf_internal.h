@@ -20,7 +20,8 @@ enum Epi : int {
 
 struct EpiArgs {
     const uint16_t *b0, *b1, *b2;  // bias per weight segment (bf16), may be null
-    float *x;                      // EPI_RESID
+    float *x;                      // EPI_RESID: x = x_in + C + b (x_in may be x)
+    const float *x_in;
     float *out32;                  // EPI_STORE32 [M][N]
     uint16_t *out;                 // EPI_F16 / EPI_QKV (q) fp16 [M][N or d]; EPI_GELU fp16 tiled
     // EPI_QKV: KV append
@@ -216,6 +217,91 @@ struct CompactArgs {
     int32_t *slot_err;
     uint16_t *kv;
 };
+
+// ---------------------------------------------------------------------------
+// Persistent pass kernel (k_pass.hip): one launch runs every decoder layer of
+// a linear verify pass, the final layer norm, the tied LM head and the per-row
+// argmax. Its workgroups (one per CU) walk a fixed task list; a task waits
+// for the 16-row tiles it reads through per-(layer, phase, tile) arrival
+// counters, so phases overlap wherever their rows allow.
+
+// Decoder weights of one layer (bf16, the layout of wf_layer_weights).
+struct LayerW {
+    const uint16_t *ln1_g, *ln1_b, *wq, *bq, *wk, *wv, *bv, *wo, *bo;
+    const uint16_t *ln2_g, *ln2_b, *wqc, *bqc, *wkc, *wvc, *bvc, *woc, *boc;
+    const uint16_t *ln3_g, *ln3_b, *w1, *b1, *w2, *b2;
+};
+
+// Phases of one layer, in task-list order, then the head's two phases.
+enum PassPhase : int {
+    PH_LN1 = 0, PH_QKV, PH_SA, PH_O, PH_LN2, PH_CQ, PH_XA, PH_OC, PH_LN3, PH_FC1, PH_FC2,
+    PH_PER_LAYER,                  // 11
+    PH_LNF = PH_PER_LAYER, PH_LMH, // head phases (after the last layer)
+};
+// GEMM phases' tilings, in this order in PassArgs::g
+enum PassGemm : int { PG_QKV = 0, PG_O, PG_CQ, PG_OC, PG_FC1, PG_FC2, PG_LMH, PG_N };
+
+struct PassGemmCfg {
+    int32_t n_tiles, m_blocks, n_groups;   // column tiles, row blocks, K groups
+    int32_t n_tasks;                       // ceil8(n_tiles) * m_blocks * n_groups
+};
+
+constexpr int kPassMaxRows = 1024;         // M <= 1024: at most 64 row tiles
+
+struct PassArgs {
+    int32_t n, T, M, RT, mt;               // requests, block, rows, row tiles, tiles per request
+    int32_t max_batch;                     // slot ids are [0, max_batch)
+    int32_t n_layers, d, H, hd, F, V;      // F: MLP width
+    float ln_eps, scale;
+    const LayerW *lw;                      // [n_layers], device
+    const uint16_t *tok_emb, *lnf_g, *lnf_b;
+    // per-request state of the pass
+    const int32_t *slots, *req_L, *req_ntok, *row_kv, *page_table;
+    int32_t *slot_err;
+    int32_t pt_stride, page_elems;
+    uint16_t *kv;                          // KV pool; layer l at kv + l * kv_layer_elems
+    int64_t kv_layer_elems;
+    const uint16_t *xkv;
+    int64_t xkv_slot_elems, xkv_layer_elems;
+    int32_t n_frames, F_pad, xa_G, xa_cf, xa_spw;
+    // activations, each written once per launch (see k_pass.hip)
+    float *xv;                             // residual versions [3 n_layers + 1][M][d]
+    uint16_t *lnv;                         // layer-norm outputs [3 n_layers + 1][Mp][d] (tiled)
+    uint16_t *qv, *cqv;                    // self / cross queries [n_layers][M][d]
+    uint16_t *sav, *xav;                   // attention outputs [n_layers][Mp][d] (tiled)
+    uint16_t *hsv;                         // MLP hidden [n_layers][Mp][F] (tiled)
+    int64_t x_stride, act_stride, q_stride, hs_stride;
+    float *part;                           // GEMM K-group sums
+    int32_t *gcnt;                         // and their arrival counters
+    float *xapart;                         // cross-attention chunk-group partials
+    int32_t *xacnt;
+    // head
+    float *logits;                         // nullable [M][V]
+    float *tile_max;
+    int32_t *tile_idx;
+    int32_t ld, n_vtiles;
+    int32_t *argmax;                       // [M]
+    // drafter history taps (n_taps = 0: none)
+    uint16_t *taps;
+    int32_t n_taps, tap_layers[8];
+    // schedule
+    int32_t *cnt;                          // [(n_layers * PH_PER_LAYER + 2) * RT] arrival counters
+    int32_t *abort_flag;
+    int32_t ph_off[PH_PER_LAYER + 1];      // task offsets of the phases within a layer
+    int32_t per_layer, head_off[3], total;
+    PassGemmCfg g[PG_N];
+    int32_t sa_items, xa_items;            // per layer
+    int64_t timeout_ticks;                 // wait limit, 100 MHz clock
+    uint64_t *trace;                       // nullable: per task (start, end) clock
+};
+
+hipError_t launch_pass(const PassArgs &a, int mb_class, int grid, hipStream_t st);
+hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t st);
+// Size class of the pass kernel's GEMM tiles for a block of M rows, and
+// per class and projection (PassGemm) the rows and columns of a task and
+// the number of K groups.
+int pass_class_of_rows(int M);
+void pass_tiling(int cl, int pg, int &bm, int &bn, int &groups);
 
 hipError_t launch_accept_tree(const TreeAcceptArgs &a, hipStream_t st);
 hipError_t launch_compact(const CompactArgs &a, hipStream_t st);

@@ -136,11 +136,9 @@ def test_tiny_fused_layer_norm_bitwise(tiny):
         return _verify(e, slots, np.stack([block] * n), [5] * n)[1]
 
     fused = run(eng, 1)[0]
-    os.environ["WF_LN_FUSION"] = "0"
-    try:
-        plain_eng = _engine(TINY, wbits, max_batch=4, max_rows=512)
-    finally:
-        del os.environ["WF_LN_FUSION"]
+    from speculative_decoding_encoder_amd.binding import WF_OPT_LN_FUSION
+    plain_eng = _engine(TINY, wbits, max_batch=4, max_rows=512)
+    plain_eng.wf_set_option(WF_OPT_LN_FUSION, 0)
     plain = run(plain_eng, 1)[0]
     assert np.array_equal(fused.view(np.uint32), plain.view(np.uint32))
     four = run(eng, 4)
@@ -465,12 +463,12 @@ def test_tall_gemm_matches_register_tiled_bitwise(torch_cuda, B):
         prefixes = [p[:8] for p in prefixes]
     blocks = np.random.default_rng(11).integers(0, shape.vocab, (B, 9)).astype(np.int32)
     out = []
-    for tall in ("1", "0"):
-        os.environ["WF_TALL_GEMM"] = tall
-        try:
-            eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224)
-        finally:
-            del os.environ["WF_TALL_GEMM"]
+    from speculative_decoding_encoder_amd.binding import WF_OPT_PERSISTENT, WF_OPT_TALL_GEMM
+    for tall in (1, 0):
+        eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224)
+        # the multi-kernel path (the persistent pass would take the blocks)
+        eng.wf_set_option(WF_OPT_PERSISTENT, 0)
+        eng.wf_set_option(WF_OPT_TALL_GEMM, tall)
         slots = list(range(B))
         eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
         T = max(len(p) for p in prefixes)
