@@ -52,7 +52,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TOKENS_PER_AUDIO_S = 3.5
 METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
 KIND_NAMES = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
-              "cross_attn", "other", "encode_kv", "draft", "history"]
+              "cross_attn", "other", "encode_kv", "draft", "history", "pass"]
 # kernel symbols (rocprofv3 name prefixes) of each timing kind: a GEMM role
 # runs the register-tiled, the tall-block or the LDS-staged kernel by block
 # height; the first template argument is the role
@@ -61,6 +61,7 @@ KIND_SYMBOL = {
                                                     "gemm_kernel"))
        for r, k in enumerate(["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head"])},
     "self_attn": "wf::self_attn_kernel<64>", "cross_attn": "wf::cross_attn_kernel<64>",
+    "pass": "wf::(anonymous namespace)::pass_kernel<",
 }
 
 
@@ -210,12 +211,17 @@ class Workload:
         kv_pos = 4 * d                              # fp16 K and V of one position, one layer
         self_bytes = kv_pos * float(np.sum(self.P + T))
         cross_bytes = self.B * s.n_frames * 4.0 * d
-        return {
+        kb = {
             "qkv": 3.0 * d * d * 2 + kv_pos * self.B * T,   # weights + K/V appended
             "oproj": d * d * 2.0, "cross_q": d * d * 2.0, "fc1": d * F * 2.0,
             "fc2": F * d * 2.0, "lm_head": V * d * 2.0, "self_attn": self_bytes,
             "cross_attn": cross_bytes,
         }
+        # the persistent pass kernel: every layer and the LM head per launch
+        nl = s.n_layers
+        kb["pass"] = nl * (kb["qkv"] + 2 * kb["oproj"] + kb["cross_q"] + kb["fc1"] + kb["fc2"]
+                           + self_bytes + cross_bytes) + kb["lm_head"]
+        return kb
 
     def pass_bytes(self):
         """bytes_pass = N_L (45.875 MB + sum_b [7.68 MB + 5120 (L_b + n_tok_b)])
@@ -413,6 +419,56 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
         "dom": dom, "achieved": achieved, "dom_bytes": kb[dom],
         "dom_avg_us": kinds[dom]["avg_us"], "kinds": kinds, "graph": used_graph,
     }
+
+
+def pass_trace(w: "Workload") -> dict:
+    """Per-phase picture of one persistent verify pass from its task trace
+    (wf_set_trace: the 100 MHz device clock at each task's start, when its
+    inputs were ready, and at its end): per phase, the tasks' summed wait
+    and work time over all layers, and the mean per-layer span from the
+    first task's start to the last one's end; the kernel's span."""
+    from speculative_decoding_encoder_amd.binding import PASS_PHASES
+    torch, eng = w.torch, w.eng
+    buf = torch.zeros((1 << 17, 4), dtype=torch.int64, device=eng.dev)
+    eng.wf_set_trace(buf)
+    w.step()
+    torch.cuda.synchronize()
+    eng.wf_set_trace(None)
+    sc = eng.wf_pass_schedule()
+    total, per, nl = sc["total"], sc["per_layer"], sc["layers"]
+    if total == 0 or total > buf.shape[0]:
+        return {}
+    tr = buf[:total].cpu().numpy().astype(np.int64)
+    t0 = int(tr[:, 0].min())
+    out = {"kernel_us": round((int(tr[:, 2].max()) - t0) / 100.0, 2), "tasks": total,
+           "grid": sc["grid"], "phases": {}}
+
+    def stats(seg):
+        return {"wait_us": round(int((seg[:, 1] - seg[:, 0]).sum()) / 100.0, 1),
+                "work_us": round(int((seg[:, 2] - seg[:, 1]).sum()) / 100.0, 1),
+                "work_us_per_task": round(float((seg[:, 2] - seg[:, 1]).mean()) / 100.0, 2)}
+    offs = sc["ph_off"]
+    for k, name in enumerate(PASS_PHASES):
+        segs, spans = [], []
+        for l in range(nl):
+            a, b = l * per + offs[k], l * per + offs[k + 1]
+            if b <= a:
+                continue
+            segs.append(tr[a:b])
+            spans.append(int(tr[a:b, 2].max() - tr[a:b, 0].min()))
+        if not segs:
+            continue
+        st = stats(np.concatenate(segs))
+        st.update({"tasks_per_layer": offs[k + 1] - offs[k],
+                   "span_us_per_layer": round(float(np.mean(spans)) / 100.0, 2)})
+        out["phases"][name] = st
+    ho = sc["head_off"]
+    for k, name in enumerate(["ln_final", "lm_head"]):
+        a, b = nl * per + ho[k], nl * per + ho[k + 1]
+        st = stats(tr[a:b])
+        st.update({"tasks": b - a, "span_us": round(int(tr[a:b, 2].max() - tr[a:b, 0].min()) / 100.0, 2)})
+        out["phases"][name] = st
+    return out
 
 
 def traffic_of(workload: str, symbol_kind: str):
@@ -688,6 +744,9 @@ def main():
                     help="skip the 4 GiB streaming-copy bandwidth measurement")
     ap.add_argument("--encoder", type=int, default=0,
                     help="time the audio encoder on this many 30 s windows instead (own JSON line)")
+    ap.add_argument("--trace", action="store_true",
+                    help="also record one persistent pass's task trace per batch and report "
+                         "the per-phase busy time and spans under pass_trace")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run device-to-device copies of this size (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
@@ -748,6 +807,8 @@ def main():
         "encode_kv_s": round(w.encode_kv_s, 4),
         "batches": {str(w.B): summary(w, r)},
     }
+    if args.trace:
+        out["batches"][str(w.B)]["pass_trace"] = pass_trace(w)
     if not args.no_stream_bw:
         out["stream_gbs"] = round(stream_bandwidth(torch, w.eng.dev), 1)
         out["pass"]["stream_frac"] = round(r["bytes_pass"] / (r["ms_step"] * 1e-3)
@@ -778,6 +839,8 @@ def main():
         out["batches"][bkey] = summary(w, r2)
         out["batches"][bkey]["kernels_avg_us"] = {k: round(v["avg_us"], 2)
                                                   for k, v in r2["kinds"].items()}
+        if args.trace:
+            out["batches"][bkey]["pass_trace"] = pass_trace(w)
         log(f"[bench] batch {bkey}: {r2['ms_step']:.3f} ms/step")
     print(json.dumps(out), flush=True)
 

@@ -336,9 +336,9 @@ wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *c
 /* Kind 12: the persistent pass kernel (below), one launch per verify pass. */
 
 /* Execution-path options of an engine (host state, read at each call; the
- * defaults are the fastest paths). None changes a result beyond the
- * summation order named here:
- *  WF_OPT_PERSISTENT (default 1): run a linear verify pass whose model has
+ * defaults are the fastest paths measured on MI355X). None changes a result
+ * beyond the summation order named here:
+ *  WF_OPT_PERSISTENT (default 0): run a linear verify pass whose model has
  *    d_model 1280, d_ffn 5120 and head_dim 64, with n * T <= 1024 and
  *    T <= 64 and no anchor readout, as one persistent kernel: one workgroup
  *    per CU walks every layer's tasks and waits for the rows it reads on
@@ -365,9 +365,10 @@ wf_status wf_get_timing(wf_engine *e, int32_t kind, double *total_ms, int32_t *c
 wf_status wf_set_option(wf_engine *e, int32_t option, int32_t value);
 
 /* Task trace of the persistent pass: with d_trace non-NULL (device memory,
- * bytes / 16 tasks; the caller keeps it alive), every later persistent pass
+ * bytes / 32 tasks; the caller keeps it alive), every later persistent pass
  * whose task list fits writes for task t the 100 MHz device clock at its
- * start and end (uint64 [t][2]). NULL turns it off. wf_pass_schedule copies
+ * start, when its inputs were ready, and at its end, and the workgroup that
+ * ran it (uint64 [t][4]). NULL turns it off. wf_pass_schedule copies
  * the last pass's task list layout to h_info (int32 [20]): total tasks,
  * tasks per layer, layers, the 12 phase offsets within a layer (LN1, QKV,
  * self-attention, O, LN2, cross Q, cross-attention, O_c, LN3, fc1, fc2, end),

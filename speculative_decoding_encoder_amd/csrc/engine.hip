@@ -210,7 +210,7 @@ struct wf_engine {
     int32_t *rowkv;                          // per verify row: KV page * 16 + offset, or -1
     bool ln_fusion = true;                   // wf_set_option(WF_OPT_LN_FUSION)
     bool tall_gemm = true;                   // wf_set_option(WF_OPT_TALL_GEMM)
-    bool persistent = true;                  // wf_set_option(WF_OPT_PERSISTENT)
+    bool persistent = false;                 // wf_set_option(WF_OPT_PERSISTENT)
     int n_cu = 0;                            // compute units: the pass kernel's grid
     int xa_chunks = 0;                       // wf_set_option(WF_OPT_XA_CHUNKS); 0: by batch
     int64_t pass_timeout_ticks = 50000000;   // wf_set_option(WF_OPT_PASS_TIMEOUT_US): 0.5 s
@@ -1174,7 +1174,7 @@ wf_status wf_set_option(wf_engine *e, int32_t option, int32_t value) {
 wf_status wf_set_trace(wf_engine *e, void *d_trace, size_t bytes) {
     if (!e) return fail(WF_EINVAL, "null engine");
     e->trace = d_trace ? (uint64_t *)d_trace : nullptr;
-    e->trace_tasks = d_trace ? bytes / 16 : 0;
+    e->trace_tasks = d_trace ? bytes / 32 : 0;
     return WF_OK;
 }
 

@@ -61,7 +61,8 @@ __device__ __forceinline__ bool gemm_task(const GemmArgs &a, int ntile, int mblo
     using S = GemmTaskShape<MB, NB, WN>;
     constexpr int WC = S::WC, NT = S::NT, BM = S::BM, BN = S::BN;
     constexpr int DD = D > CK ? CK : D;
-    const int P = a.n_groups;
+    // K groups: S / WC with S = 8 chunks (the caller's n_groups agrees)
+    constexpr int P = WN;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r16 = lane & 15, g = lane >> 4;
     const int cw = wave / WN, sl = wave - (wave / WN) * WN;
@@ -145,7 +146,7 @@ __device__ __forceinline__ bool gemm_task(const GemmArgs &a, int ntile, int mblo
     }
 
     int *flag = reinterpret_cast<int *>(smem + S::LDS_BYTES - 16);
-    if (P > 1) {
+    if constexpr (P > 1) {
         // K groups: the cw = 0 waves publish their slice's sum in the MFMA
         // lane layout (16 bytes per lane and tile, device-coherent); the
         // last group to arrive combines every group's tiles in the tree
@@ -176,8 +177,8 @@ __device__ __forceinline__ bool gemm_task(const GemmArgs &a, int ntile, int mblo
                                         : __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                               rs, ((q * WN + sl) * NT + j) * 1024 + lane * 16, 0,
                                               CPOL_SC1));
-                if (P == 2) c[j] = v[0] + v[1];
-                else if (P == 4) c[j] = (v[0] + v[1]) + (v[2] + v[3]);
+                if constexpr (P == 2) c[j] = v[0] + v[1];
+                else if constexpr (P == 4) c[j] = (v[0] + v[1]) + (v[2] + v[3]);
                 else c[j] = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
             }
         }

@@ -92,26 +92,41 @@ __device__ __forceinline__ void pass_abort(PA a) {
     }
 }
 
+// Time the current task's inputs became ready (trace only).
+__shared__ long long g_t_ready;
+
 // The calling wave polls the counters of row tiles [r0, r1) (at most 64)
 // until each reaches c (per_item: c times the attention items over the
-// tile). No workgroup barrier: every wave that reads the inputs waits itself.
-__device__ __forceinline__ void wait_tiles(PA a, const int *cnt, int r0, int r1, int c,
-                           bool per_item) {
+// tile). One wave per item polls and the workgroup then meets at a barrier:
+// hundreds of waves spinning on the same counter lines would hold up the
+// producers' own increments to them. The poll interval grows from ~50 ns
+// to ~0.5 us while the inputs are far from ready.
+__device__ __forceinline__ void poll_tiles(PA a, const int *cnt, int r0, int r1, int c,
+                                           bool per_item) {
     const int lane = threadIdx.x & 63;
     const int r = r0 + lane;
     const bool mine = r < r1;
     const int want = mine ? (per_item ? c * items_over_tile(a, r) : c) : 0;
     const long long t0 = clock100();
-    for (;;) {
+    for (int it = 0;; ++it) {
         const int v = mine ? ld_acq(cnt + r) : 0;
-        if (__all(v >= want)) return;
-        if (ld_acq(a.abort_flag)) return;
+        if (__all(v >= want)) break;
+        if (ld_acq(a.abort_flag)) break;
         if (clock100() - t0 > a.timeout_ticks) {
             pass_abort(a);
-            return;
+            break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        if (it < 16) __builtin_amdgcn_s_sleep(2);
+        else if (it < 64) __builtin_amdgcn_s_sleep(8);
+        else __builtin_amdgcn_s_sleep(20);
     }
+    if (a.trace && lane == 0) g_t_ready = clock100();
+}
+// The whole workgroup waits: wave 0 polls, then the barrier.
+__device__ __forceinline__ void wait_tiles(PA a, const int *cnt, int r0, int r1, int c,
+                                           bool per_item) {
+    if ((threadIdx.x >> 6) == 0) poll_tiles(a, cnt, r0, r1, c, per_item);
+    __syncthreads();
 }
 
 // Every wave: its stores are complete; then the workgroup meets.
@@ -139,11 +154,15 @@ __device__ __forceinline__ int publish_tiles(int *cnt, int r0, int r1) {
 template <int CL, int PG>
 struct Tile {
     static constexpr bool DW = PG == PG_O || PG == PG_CQ || PG == PG_OC;   // d-wide output
-    static constexpr int MB = CL == 0 ? 1 : CL == 1 ? 2 : (DW || PG == PG_LMH) ? 3 : 6;
-    static constexpr int NB = PG == PG_LMH ? 4 : PG == PG_FC2 ? 1 : CL == 0 ? 1 : (DW && CL == 1) ? 1 : 2;
+    static constexpr int MB = CL == 0 ? 1 : CL == 1 ? 2 : PG == PG_FC2 ? 6 : 3;
+    static constexpr int NB = PG == PG_LMH ? 4 : PG == PG_FC2 ? 1 : CL == 0 ? 1
+                            : DW ? (CL == 1 ? 1 : 2) : (CL == 1 ? 2 : 4);
     static constexpr int WN = PG == PG_FC2 ? 4 : 1;
     static constexpr int NT = MB * NB;
-    static constexpr int D = NT >= 8 ? 2 : (NT >= 4 ? 3 : 4);
+    // loads in flight per wave: the whole 5-k-step chunk of the d-deep
+    // projections (issued at once, the weights before the input wait), a
+    // 5-deep ring over fc2's 20-k-step chunks
+    static constexpr int D = PG == PG_FC2 ? 3 : PG == PG_LMH ? 3 : (CL == 2 && !DW) ? 4 : 5;
 };
 
 template <int CL, int PG>
@@ -231,15 +250,32 @@ __device__ __forceinline__ void ln_task(PA a, int l, int which, int j) {
         LnRow row;
         ln_load16(x + (size_t)m * d, d, r16, row);
         const int last = (d >> 3) - 1;
+        // gains and biases in two halves: the first with the row, the second
+        // once the first half's outputs are out (register budget)
+        constexpr int H1 = LN_GPL / 2;
+        u32x4 gg[H1], bb[H1];
+#pragma unroll
+        for (int i = 0; i < H1; ++i) {
+            const int kg = min(r16 + 16 * i, last);
+            gg[i] = ld16(gg_p + kg * 8);
+            bb[i] = ld16(bb_p + kg * 8);
+        }
         float mean, rstd;
         ln_reduce16(row, d, r16, a.ln_eps, mean, rstd);
 #pragma unroll
         for (int i = 0; i < LN_GPL; ++i) {
             const int kg = r16 + 16 * i;
+            if (i == H1) {
+#pragma unroll
+                for (int q = 0; q < H1; ++q) {
+                    const int kq = min(r16 + 16 * (H1 + q), last);
+                    gg[q] = ld16(gg_p + kq * 8);
+                    bb[q] = ld16(bb_p + kq * 8);
+                }
+            }
             if (kg > last) break;
-            const u32x4 gg = ld16(gg_p + kg * 8), bb = ld16(bb_p + kg * 8);
             *reinterpret_cast<u32x4 *>(out + xh_index(m, kg * 8, d)) =
-                ln_h8(row.v[2 * i], row.v[2 * i + 1], gg, bb, mean, rstd);
+                ln_h8(row.v[2 * i], row.v[2 * i + 1], gg[i % H1], bb[i % H1], mean, rstd);
             if (tap >= 0) {
                 const float4 x0 = row.v[2 * i], x1 = row.v[2 * i + 1];
                 const u32x4 v = {pack_h2(x0.x, x0.y), pack_h2(x0.z, x0.w), pack_h2(x1.x, x1.y),
@@ -268,11 +304,12 @@ __device__ __forceinline__ void sa_task(PA a, int l, int j, char *smem) {
     const bool valid = item < a.sa_items;
     const int bh = valid ? item / a.mt : 0, mtile = valid ? item - bh * a.mt : 0;
     const int b = bh / a.H;
-    if (valid) {
+    if (valid && w4 == 0) {
         // the request's K/V rows and its queries
         const int r0 = (b * a.T) >> 4, r1 = ((b * a.T + a.T - 1) >> 4) + 1;
-        wait_tiles(a, slot_cnt(a, l, PH_QKV), r0, r1, a.g[PG_QKV].n_tiles, false);
+        poll_tiles(a, slot_cnt(a, l, PH_QKV), r0, r1, a.g[PG_QKV].n_tiles, false);
     }
+    __syncthreads();
     SelfAttnArgs s{};
     s.q = a.qv + (size_t)l * a.q_stride;
     s.kv_layer = a.kv + (size_t)l * a.kv_layer_elems;
@@ -317,10 +354,9 @@ __device__ __forceinline__ void xa_task(PA a, int l, int j, char *smem) {
     const int bhm = valid ? item / a.xa_G : 0;
     const int mtile = bhm % a.mt, b = (bhm / a.mt) / a.H;
     int p0 = 0, p1 = 0;
-    if (valid) {
-        item_tiles(a, b, mtile, p0, p1);
-        wait_tiles(a, slot_cnt(a, l, PH_CQ), p0, p1, a.g[PG_CQ].n_tiles, false);
-    }
+    if (valid) item_tiles(a, b, mtile, p0, p1);
+    if (valid && w4 == 0) poll_tiles(a, slot_cnt(a, l, PH_CQ), p0, p1, a.g[PG_CQ].n_tiles, false);
+    __syncthreads();
     CrossAttnArgs c{};
     c.q = a.cqv + (size_t)l * a.q_stride;
     c.xkv = a.xkv;
@@ -588,12 +624,15 @@ __global__ __launch_bounds__(kThreads) void pass_kernel(PassArgs args) {
     for (int t = blockIdx.x; t < total; t += gridDim.x) {
         PA a = pass_args(kp);
         const long long t0 = a.trace ? clock100() : 0;
+        if (a.trace && threadIdx.x == 0) g_t_ready = t0;
         run_task<CL>(a, kp, t, smem);
-        if (a.trace && threadIdx.x == 0) {
-            a.trace[2 * (size_t)t] = (uint64_t)t0;
-            a.trace[2 * (size_t)t + 1] = (uint64_t)clock100();
-        }
         __syncthreads();   // the task's LDS is free for the next one
+        if (a.trace && threadIdx.x == 0) {
+            a.trace[4 * (size_t)t] = (uint64_t)t0;
+            a.trace[4 * (size_t)t + 1] = (uint64_t)g_t_ready;
+            a.trace[4 * (size_t)t + 2] = (uint64_t)clock100();
+            a.trace[4 * (size_t)t + 3] = (uint64_t)blockIdx.x;
+        }
     }
 }
 

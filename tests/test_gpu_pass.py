@@ -169,14 +169,14 @@ def test_pass_trace_covers_the_schedule(torch_cuda):
     wl, shape, wbits, encs, prefixes, eng, slots = _setup(B, seed=6)
     _prefill(eng, slots, prefixes)
     blocks = np.random.default_rng(3).integers(0, shape.vocab - 1, (B, 9)).astype(np.int32)
-    buf = torch.zeros((20000, 2), dtype=torch.int64, device=eng.dev)
+    buf = torch.zeros((20000, 4), dtype=torch.int64, device=eng.dev)
     eng.wf_set_trace(buf)
     _verify(eng, slots, blocks, [9] * B, logits=False)
     eng.wf_set_trace(None)
     sched = eng.wf_pass_schedule()
     tr = buf.cpu().numpy()[:sched["total"]]
-    assert (tr[:, 0] > 0).all() and (tr[:, 1] >= tr[:, 0]).all()
-    span = (tr[:, 1].max() - tr[:, 0].min()) / 100.0
+    assert (tr[:, 0] > 0).all() and (tr[:, 1] >= tr[:, 0]).all() and (tr[:, 2] >= tr[:, 1]).all()
+    span = (tr[:, 2].max() - tr[:, 0].min()) / 100.0
     log(f"pass trace: {sched['total']} tasks, {span:.1f} us from first start to last end")
     eng.close()
 
