@@ -1,38 +1,46 @@
 """Benchmark of the block-verification hot path on one MI355X.
 
-A step is one full round of the path over one batch: wf_verify_block on the
-anchor plus K = 8 candidates per request (every decoder layer, the tied LM
-head and the per-row argmax), wf_accept and wf_rollback, followed by
-wf_truncate back to the prefix length so that every step verifies the same
-block from the same state. Inputs are seeded and synthetic (no datasets, no
-trained weights); weights, audio memory, prompts and KV caches are resident
-in HBM before the timed region starts.
+A step is one round of the running speculative loop over one batch: the
+round's block (the anchor plus K = 8 candidates per request, from the
+workload's drafter), wf_verify_block (every decoder layer, the tied LM head
+and the per-row argmax), wf_accept, wf_rollback and the loop's state update,
+all on the device and replayed from one captured HIP graph. Each timed round
+verifies a new block at the positions the loop has reached, so tokens per
+second come from the realized acceptance: the tokens the timed rounds emit,
+sum over requests of (accepted + 1), over their time. Inputs are seeded and
+synthetic (no datasets, no trained weights); weights, audio memory, prompts
+and KV caches are resident in HBM before the timed region starts, and the
+prompts are prefilled before it.
 
-Workloads (``--config``):
-  1  32-layer large-v3 shape, batch 1, 64-token prefix, one block of 9,
-     drafts = the greedy token with probability 0.7, else a uniform id (default)
-  2  4-layer turbo shape, batch 32, prefixes uniform in [4, 200], p = 0.75
+Workloads (``--config`` for the headline, ``--batches`` and ``--configs`` for
+the rest of the line):
+  1  32-layer large-v3 shape, batch 1, 64-token prefix, drafts = the greedy
+     token with probability 0.7, else a uniform id (default headline)
+  2  4-layer turbo shape, batch 32, prefixes uniform in [4, 200], p = 0.75,
+     rounds until 200 tokens per request
   3  32-layer large-v3 shape, batch 96, prefixes Poisson(80) clipped to
      [4, 224], shuffled 16-token pages; K = 8 drafts come from the 2-layer
      random-init parallel drafter (wf_draft), timed together with the verify
   4  32-layer large-v3 shape, batch 32, prefixes uniform in [4, 200], temperature
      0.7 rejection sampling; draft distributions q_i = 0.7 p~_i + 0.3 softmax(z_i),
-     z_i ~ N(0, 1) seeded, where p~_i is the target's T = 0.7 distribution along
-     its own greedy continuation; candidates are drawn from q_i. With --greedy:
-     the same batch-32 pass with Bernoulli-copy drafts (p = 0.7) and greedy
-     acceptance.
-The greedy continuation that drafts copy is the engine's own, computed before
-timing. Tokens per second count the tokens a round emits, sum over requests
-of (accepted + 1); audio seconds per second divide that by 3.5 tokens per
-audio second (the tokens-to-audio ratio of Whisper-Flash Table 1).
+     z_i ~ N(0, 1), where p~_i is the target's T = 0.7 distribution at the
+     drafted prefix (single-row passes, untimed, then truncated back);
+     candidates are drawn from q_i. Its greedy variant (batch 32 of the
+     metric) takes Bernoulli-copy drafts (p = 0.7) and greedy acceptance.
+The greedy continuation that Bernoulli-copy drafts copy is the engine's own,
+computed before timing. Audio seconds per second divide tokens per second by
+3.5 tokens per audio second (the tokens-to-audio ratio of Whisper-Flash
+Table 1).
+
+Per workload the line also gives the fixed-block pass: one block verified
+again and again from the same state (wf_truncate back after each round),
+timed per step and, in a second pass, per kernel launch with HIP events.
+That is the pass whose whole HBM bytes give pass_roofline_frac, and whose
+dominant kernel (the largest total time) gives the roofline object.
 
 ``--encoder N`` instead times the audio encoder (wf_encode: N log-mel windows
 of 30 s through the 32-block large-v3 encoder) and prints its own line in
 audio seconds per second, with the bf16 MFMA roofline of its dominant kernel.
-
-The timed loop replays one HIP graph per step. Kernel durations for the
-roofline come from HIP events around every launch over a second pass of the
-same steps; the dominant kernel is the one with the largest total time.
 """
 from __future__ import annotations
 
@@ -115,12 +123,16 @@ class Workload:
         torch.cuda.synchronize()
         self.encode_kv_s = time.perf_counter() - t0
         del d_enc
-        # the engine's own greedy continuation (untimed) for the drafts
+        # the engine's own greedy continuation (untimed) for the drafts: the
+        # whole budget, so that the running loop's table drafter can copy it
         eng.wf_reset(self.d_slots)
         if not self.drafter:
-            g = run_loop(eng, self.slots, self.prefixes, self.K + 1, 0, None, s.eos_id)
+            t0 = time.time()
+            g = run_loop(eng, self.slots, self.prefixes, wl.n_max, 0, None, s.eos_id)
             self.greedy = g.tokens
             eng.wf_reset(self.d_slots)
+            log(f"[bench] {self.name}: greedy continuation ({wl.n_max} tokens) in "
+                f"{time.time() - t0:.1f}s")
         anchors = prefill(eng, self.slots, self.prefixes)
         self.anchors = anchors
         blocks = np.zeros((B, self.K + 1), np.int32)
@@ -250,91 +262,325 @@ class Workload:
         return nl * per_layer + kb["lm_head"] + extra
 
 
-def cpu_baseline(w: Workload, timed_s: float = 10.0, wall_s: float = 90.0):
-    """The oracle, as it stands (fp64 numpy), on a bounded sample of the same
-    workload. For each of the first requests it builds, untimed, the request's
-    cross K/V and prefix cache and its own block by the workload's recipe (its
-    own greedy continuation for Bernoulli-copy drafts, its own probe logits
-    for the sampling q, its own drafter history); it then times the round's
-    work — the drafter pass (config 3), the verify pass (K+1 rows through
-    every layer and the LM head) and the acceptance — up to 3 times per
-    request (as often as needed with one request), until about ``timed_s``
-    seconds of timed CPU work."""
+def cpu_info() -> dict:
+    """The host CPU model (/proc/cpuinfo) and the threads this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "threads_available": len(os.sched_getaffinity(0))}
+
+
+def cpu_baseline(w: Workload, timed_s: float = 6.0, wall_s: float = 90.0, threads: int = 0,
+                 dtype=np.float32):
+    """The oracle, as it stands (numpy; fp32 for timing), running the same
+    loop as the device on a bounded sample of the workload: request after
+    request (starting over when all have been run), the prompt prefilled
+    untimed, then rounds until the request is done or about ``timed_s``
+    seconds of timed CPU work. Timed per round: the drafter pass (with the
+    engine's drafter), the verify pass of the anchor plus k candidates
+    through every layer and the LM head, the acceptance (greedy, or
+    rejection sampling at the workload's temperature) and the drafter's
+    history append. Built untimed per round: Bernoulli-copy candidates (the
+    oracle's own greedy tokens, from single-row passes, up to the first
+    replaced position; replacement ids after it, where acceptance has stopped
+    either way) or, for sampling, the K single-row probe passes that give
+    q_i = 0.7 p~_i + 0.3 softmax(z_i) and the candidates drawn from it.
+    ``threads`` > 0 caps the BLAS threads (0: all the process may use)."""
     from oracle import decode as od
     from oracle import drafter as odr
     from oracle import model as om
     from oracle import sampling as osmp
     from synthetic import DRAFTER_TAPS, make_draft_table, rng
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
-    s = w.shape
-    K = w.K
-    m = om.Model(s, w.wbits)
-    dr = odr.Drafter(s, w.wbits, w.dbits, taps=DRAFTER_TAPS) if w.drafter else None
-    toks = 0
-    t_total = 0.0
-    passes = 0
-    reqs = 0
-    t_start = time.time()
-    for b in range(w.B):
-        P = int(w.P[b])
-        req = m.new_request(w.encs[b])
-        if dr is not None:
-            dreq = dr.new_request(w.encs[b])
-            lg, taps = m.rows(req, w.prefixes[b], 0, taps=set(DRAFTER_TAPS))
-            dr.append_history(dreq, taps, 0)
-        else:
-            lg = m.rows(req, w.prefixes[b], 0)
-        anchor = od.argmax_lowest(lg[-1])
-        q = None
-        if dr is None:
-            greedy = [anchor]
-            for i in range(K):
-                greedy.append(od.argmax_lowest(m.rows(req, [greedy[-1]], P + i)[0]))
-            if w.sampling:
-                plg = m.rows(req, greedy, P)
-                g = rng(w.wl.cfg_id, 4000 + b)
-                q = np.empty((K, s.vocab), np.float32)
-                drafts = []
-                for i in range(K):
-                    pt = osmp.probs(plg[i], w.temperature).astype(np.float64)
-                    zz = g.standard_normal(s.vocab)
-                    sm = np.exp(zz - zz.max())
-                    qi = 0.7 * pt + 0.3 * sm / sm.sum()
-                    q[i] = qi.astype(np.float32)
-                    drafts.append(int(g.choice(s.vocab, p=qi / qi.sum())))
-            else:
-                keep, repl = make_draft_table(w.wl, b)
-                drafts = [greedy[i] if keep[P + i] else int(repl[P + i]) for i in range(1, K + 1)]
-        reqs += 1
-        for _ in range(3 if w.B > 1 else 200):
-            t0 = time.perf_counter()
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:   # pragma: no cover - threadpoolctl is installed here
+        threadpool_info = threadpool_limits = None
+    ctx = threadpool_limits(limits=threads) if (threads and threadpool_limits) else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        try:
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            used = threads or len(os.sched_getaffinity(0))
+        s = w.shape
+        K, V, eos, n_max = w.K, s.vocab, s.eos_id, w.wl.n_max
+        taps = set(DRAFTER_TAPS) if w.drafter else None
+        m = om.Model(s, w.wbits, dtype=dtype)
+        dr = odr.Drafter(s, w.wbits, w.dbits, taps=DRAFTER_TAPS, dtype=dtype) if w.drafter else None
+        toks = rounds = reqs = 0
+        t_total = 0.0
+        t_start = time.time()
+
+        def budget_left():
+            return t_total < timed_s and time.time() - t_start < wall_s
+
+        n = 0
+        while budget_left():
+            b = n % w.B
+            n += 1
+            P = int(w.P[b])
+            req = m.new_request(w.encs[b])
             if dr is not None:
-                drafts = odr.draft_tokens(dr.block(dreq, anchor, P, K), K)
-            lg = m.rows(req, [anchor] + drafts, P)
-            if w.sampling:
-                a, *_ = osmp.sample_round(lg.astype(np.float32), q, drafts, w.temperature, 0, b,
-                                          0, s.eos_id, w.wl.n_max - 1)
+                dreq = dr.new_request(w.encs[b])
+                lg, tp = m.rows(req, w.prefixes[b], 0, taps=taps)
+                dr.append_history(dreq, tp, 0)
             else:
-                a, *_ = od.greedy_accept(drafts, [od.argmax_lowest(r) for r in lg], s.eos_id,
-                                         w.wl.n_max - 1)
-            t_total += time.perf_counter() - t0
-            toks += a + 1
-            passes += 1
-            if t_total >= timed_s:
-                break
-        if t_total >= timed_s or time.time() - t_start > wall_s:
-            break
+                lg = m.rows(req, w.prefixes[b], 0)
+            anchor = od.argmax_lowest(lg[-1])
+            keep, repl = make_draft_table(w.wl, b)
+            L, emitted, done, step = P, 1, anchor == eos or n_max <= 1, 0
+            reqs += 1
+            while not done and budget_left():
+                R = n_max - emitted
+                k = min(K, R - 1, s.n_ctx - L - 1)
+                q = None
+                drafts = []
+                if w.sampling:
+                    g = rng(w.wl.cfg_id, 4000 + 1000 * b + step)
+                    q = np.empty((k, V), np.float32)
+                    tok = anchor
+                    for i in range(k):
+                        pt = osmp.probs(m.rows(req, [tok], L + i)[0], w.temperature)
+                        zz = g.standard_normal(V)
+                        sm = np.exp(zz - zz.max())
+                        qi = 0.7 * pt.astype(np.float64) + 0.3 * sm / sm.sum()
+                        q[i] = qi.astype(np.float32)
+                        tok = int(g.choice(V, p=qi / qi.sum()))
+                        drafts.append(tok)
+                elif dr is None:
+                    tok, live = anchor, True
+                    for i in range(1, k + 1):
+                        live = live and bool(keep[L + i])
+                        if live:
+                            tok = od.argmax_lowest(m.rows(req, [tok], L + i - 1)[0])
+                            drafts.append(tok)
+                        else:
+                            drafts.append(int(repl[L + i]))
+                t0 = time.perf_counter()
+                if dr is not None:
+                    drafts = odr.draft_tokens(dr.block(dreq, anchor, L, K), K)[:k]
+                    lg, tp = m.rows(req, [anchor] + drafts, L, taps=taps)
+                else:
+                    lg = m.rows(req, [anchor] + drafts, L)
+                if w.sampling:
+                    a, out, nxt, done = osmp.sample_round(lg.astype(np.float32), q, drafts,
+                                                          w.temperature, 0, b, step, eos, R)
+                else:
+                    a, out, nxt, done = od.greedy_accept(
+                        drafts, [od.argmax_lowest(r) for r in lg], eos, R)
+                if dr is not None:
+                    dr.append_history(dreq, {t: x[:a + 1] for t, x in tp.items()}, L)
+                t_total += time.perf_counter() - t0
+                toks += len(out)
+                rounds += 1
+                L += a + 1
+                emitted += len(out)
+                step += 1
+                if nxt is not None:
+                    anchor = nxt
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
     what = "drafter pass + verify pass" if dr is not None else "verify pass"
-    return {"value": round(toks / t_total, 3), "unit": "tokens/s", "cores": int(threads),
+    acc = "rejection sampling" if w.sampling else "greedy acceptance"
+    return {"value": round(toks / t_total, 3), "unit": "tokens/s", "cores": int(used),
             "kind": "oracle",
-            "sample": f"{passes} rounds ({what}, K+1 = {K + 1} rows, all layers, LM head, "
-                      f"{'rejection sampling' if w.sampling else 'greedy acceptance'}) over "
-                      f"{reqs} of {w.B} requests, fp64 numpy, {t_total:.2f} s timed; cross K/V, "
-                      f"prefix caches and blocks built untimed by the oracle itself"}
+            "sample": f"{w.name}: {rounds} rounds of the running loop ({what} of up to "
+                      f"K+1 = {K + 1} rows, all {s.n_layers} layers, LM head, {acc}) over "
+                      f"{reqs} request(s), {toks} tokens, tau {toks / max(rounds, 1):.2f}, "
+                      f"{np.dtype(dtype).name} numpy, {t_total:.2f} s timed; cross K/V, "
+                      f"prompts and candidates built untimed by the oracle itself",
+            "dtype": np.dtype(dtype).name, "timed_s": round(t_total, 2)}
+
+
+def _prefill(w: "Workload"):
+    from speculative_decoding_encoder_amd.harness import prefill
+    w.eng.wf_reset(w.d_slots)
+    return prefill(w.eng, w.slots, w.prefixes)
+
+
+def _fresh_loop(w: "Workload", logits: bool = False):
+    """Reset the slots, prefill the prompts (untimed) and set up a device
+    round loop from there: the table drafter's candidates per absolute
+    position (Bernoulli-copy drafts of the greedy continuation) or the
+    engine's drafter."""
+    from speculative_decoding_encoder_amd.harness import DeviceLoop, draft_table
+    from synthetic import make_draft_table
+    s = w.shape
+    anchors = _prefill(w)
+    table = None
+    if not w.drafter and not w.sampling:
+        size = s.n_ctx + w.K + 2
+        table = np.stack([draft_table(w.greedy[b], int(w.P[b]), *make_draft_table(w.wl, b),
+                                      size) for b in range(w.B)])
+    return DeviceLoop(w.eng, w.slots, anchors, w.P, w.wl.n_max, w.K, s.eos_id, draft_table=table,
+                      drafter=w.drafter, logits=logits)
+
+
+def _loop_stats(w: "Workload", c0: dict, c1: dict, rounds: int, ms: float, restarts: int) -> dict:
+    toks = c1["tokens"] - c0["tokens"]
+    rr = c1["request_rounds"] - c0["request_rounds"]
+    acc = c1["accepted"] - c0["accepted"]
+    prop = c1["proposed"] - c0["proposed"]
+    hist = (c1["hist"] - c0["hist"]).astype(np.float64)
+    s_k = [float(hist[k:].sum() / max(hist.sum(), 1)) for k in range(1, w.K + 1)]
+    return {"rounds_timed": rounds, "ms_per_round": round(ms / rounds, 4),
+            "tokens": int(toks), "tokens_per_s": round(toks / (ms * 1e-3), 2),
+            "audio_s_per_s": round(toks / (ms * 1e-3) / TOKENS_PER_AUDIO_S, 2),
+            "request_rounds": int(rr), "mean_active_batch": round(rr / rounds, 2),
+            "tau": round(toks / max(rr, 1), 4), "alpha": round(acc / max(prop, 1), 4),
+            "s_k": [round(v, 4) for v in s_k], "restarts": restarts}
+
+
+def measure_loop(w: "Workload", K: int, W: int, chunk: int = 8) -> dict:
+    """The real cached loop over distinct blocks: from the prompts, rounds
+    of (the block from the drafter, wf_verify_block, wf_accept, wf_rollback,
+    the loop's state update) captured once as a HIP graph; W untimed rounds,
+    then K timed rounds, replayed back to back in chunks between HIP events.
+    tokens/s counts the tokens the timed rounds emit (realized acceptance),
+    tau the tokens per active request-round. When every request has
+    finished, the prompts are prefilled again between chunks (untimed) and
+    the loop starts over. The table drafter's gather and the state update (a
+    few small kernels) are inside the timed region."""
+    torch = w.torch
+    loop = _fresh_loop(w)
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        loop.round()            # the first round eagerly, then capture the next
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=stream):
+            loop.round()
+    torch.cuda.synchronize()
+    restarts = 0
+
+    def run(n: int) -> float:
+        nonlocal restarts
+        ms, left = 0.0, n
+        while left > 0:
+            if loop.counters()["all_done"]:
+                loop.restart(_prefill(w), w.P)
+                restarts += 1
+            c = min(chunk, left)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(c):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms += e0.elapsed_time(e1)
+            left -= c
+        return ms
+
+    run(max(W - 2, 1))
+    c0 = loop.counters()
+    restarts = 0
+    ms = run(K)
+    c1 = loop.counters()
+    err, _ = w.eng.wf_device_state()
+    assert (err == 0).all(), f"engine error words {err}"
+    del graph
+    out = _loop_stats(w, c0, c1, K, ms, restarts)
+    log(f"[bench] {w.name}: loop {K} rounds {ms / K:.3f} ms/round, {out['tokens']} tokens, "
+        f"tau {out['tau']}")
+    return out
+
+
+def measure_sampling_loop(w: "Workload", K: int, W: int) -> dict:
+    """The temperature-sampling loop. Each round the untimed harness builds
+    the candidates: for i = 1..K the target's T-tempered
+    distribution p~_i at the drafted prefix (single-row GPU passes, kept, then
+    truncated back), q_i = 0.7 p~_i + 0.3 softmax(z_i) with z_i ~ N(0, 1), and
+    y_i ~ q_i (torch generators seeded by the round). The timed part is the
+    round itself (wf_verify_block with the logits, wf_accept with rejection
+    sampling, wf_rollback, the counters), replayed from a HIP graph between
+    HIP events; the timed rounds are summed."""
+    torch, eng, s = w.torch, w.eng, w.shape
+    B, Kd, V, T = w.B, w.K, s.vocab, w.temperature
+    loop = _fresh_loop(w, logits=True)
+    q = torch.empty((B, Kd, V), dtype=torch.float32, device=eng.dev)
+    req = eng.i32(np.arange(B, dtype=np.int32))
+    probe_am = torch.empty((B, 1), dtype=torch.int32, device=eng.dev)
+    probe_lg = torch.empty((B, 1, V), dtype=torch.float32, device=eng.dev)
+    zeros = torch.zeros(B, dtype=torch.int32, device=eng.dev)
+    gen = torch.Generator(device=eng.dev)
+    kw = dict(logits=loop.logits, q=q, temperature=T, seed=0, request_id=req, step=loop.step)
+
+    def harness(rnd):
+        gen.manual_seed(1000 + rnd)
+        R = loop.n_max - loop.emitted
+        room = s.n_ctx - loop.L - 1
+        k = torch.clamp(torch.minimum(torch.minimum(torch.full_like(R, Kd), R - 1), room), min=0)
+        active = loop.done == 0
+        loop.ntok.copy_(torch.where(active, k + 1, torch.zeros_like(k)))
+        loop.budget.copy_(torch.clamp(R, min=1))
+        L0 = loop.L.clone()
+        tok = loop.anchor.clone()
+        loop.block[:, 0].copy_(loop.anchor)
+        for i in range(Kd):
+            live = (active & (k > i)).to(torch.int32)
+            eng.wf_verify_block(loop.d_slots, tok[:, None], live, probe_am, probe_lg)
+            p = torch.softmax(probe_lg[:, 0, :] / T, dim=-1)
+            z = torch.randn((B, V), generator=gen, device=eng.dev)
+            qi = 0.7 * p + 0.3 * torch.softmax(z, dim=-1)
+            y = torch.multinomial(qi, 1, generator=gen)[:, 0].to(torch.int32)
+            q[:, i, :].copy_(qi)
+            loop.block[:, i + 1].copy_(torch.where(live > 0, y, torch.zeros_like(y)))
+            eng.wf_rollback(loop.d_slots, zeros)
+            tok = y
+        eng.wf_truncate(loop.d_slots, L0)
+
+    def timed_round():
+        loop.verify()
+        loop.accept(**kw)
+        loop.finish()
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    rnd = 0
+    with torch.cuda.stream(stream):
+        harness(rnd)
+        timed_round()
+        rnd += 1
+        torch.cuda.synchronize()
+        harness(rnd)
+        with torch.cuda.graph(graph, stream=stream):
+            timed_round()
+        rnd += 1
+    torch.cuda.synchronize()
+    for _ in range(max(W - 2, 0)):
+        harness(rnd)
+        graph.replay()
+        rnd += 1
+    torch.cuda.synchronize()
+    c0 = loop.counters()
+    ms = 0.0
+    for _ in range(K):
+        harness(rnd)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms += e0.elapsed_time(e1)
+        rnd += 1
+    c1 = loop.counters()
+    err, _ = eng.wf_device_state()
+    assert (err == 0).all(), f"engine error words {err}"
+    del graph
+    out = _loop_stats(w, c0, c1, K, ms, 0)
+    log(f"[bench] {w.name}: sampling loop {K} rounds {ms / K:.3f} ms/round, "
+        f"{out['tokens']} tokens, tau {out['tau']}")
+    return out
 
 
 def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
@@ -520,19 +766,48 @@ def is_encoder_workload(workload: str) -> bool:
     return "encoder" in workload
 
 
-def summary(w: "Workload", r: dict) -> dict:
-    return {
+def expected_tau(p: float, K: int) -> float:
+    """E[tokens per round] when each candidate independently equals the
+    target's token with probability p and acceptance stops at the first
+    miss (plus the target's own token): sum_{j=0..K} p^j."""
+    return float(sum(p ** j for j in range(K + 1)))
+
+
+def entry(w: "Workload", r: dict, lp: dict) -> dict:
+    """One workload's figures: the running loop (tokens/s at realized
+    acceptance), the fixed-block pass (its time against the whole-pass HBM
+    bytes) and the dominant kernel's roofline."""
+    dom = r["dom"]
+    et = None
+    if not (w.sampling or w.drafter):
+        et = expected_tau(w.wl.p_keep, w.K)
+    out = {
         "workload": w.name, "batch": w.B, "layers": w.shape.n_layers,
-        "tokens_per_s": round(r["value"], 2),
-        "audio_s_per_s": round(r["value"] / TOKENS_PER_AUDIO_S, 2),
-        "ms_per_step": round(r["ms_step"], 4), "tokens_per_step": r["tokens_per_step"],
+        "d_model": w.shape.d_model, "K": w.K, "tokens_per_s": lp["tokens_per_s"], "audio_s_per_s": lp["audio_s_per_s"],
+        "ms_per_round": lp["ms_per_round"], "tau": lp["tau"], "alpha": lp["alpha"],
+        "loop": lp,
+        "expected_tau": round(et, 4) if et else None,
+        "tokens_per_s_at_expected_tau": round(w.B * et / (r["ms_step"] * 1e-3), 2) if et else None,
+        "pass_ms": round(r["ms_step"], 4), "pass_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
         "pass_bytes": r["bytes_pass"], "pass_roofline_frac": round(r["pass_frac"], 4),
-        "dominant_kernel": r["dom"], "dominant_gbs": round(r["achieved"], 1),
-        "dominant_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+        "dominant_kernel": dom, "dominant_frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "kernel": dom, "symbol": KIND_SYMBOL.get(dom, dom),
+                     "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic_of(w.name, dom),
+                     "bytes_per_launch": r["dom_bytes"], "avg_us": round(r["dom_avg_us"], 3)},
+        "kernels_avg_us": {k: round(v["avg_us"], 2) for k, v in r["kinds"].items()},
+        "kernels_ms_per_pass": {k: round(v["total_ms_per_step"], 4) for k, v in r["kinds"].items()},
+        "encode_kv_s": round(w.encode_kv_s, 4),
     }
+    if w.sampling:
+        out["temperature"] = w.temperature
+    return out
 
 
-EXTRA = {"32": (4, True), "96": (3, False)}   # batch -> (config, greedy)
+# the metric's batch sizes and the other workloads: key -> (workload id, greedy acceptance)
+BATCHES = {"1": (1, False), "32": (4, True), "96": (3, False)}
+CONFIGS = {"2": (2, False), "4": (4, False)}
 
 
 def k_sweep(args):
@@ -731,6 +1006,9 @@ def main():
     ap.add_argument("--batches", default="32,96",
                     help="also measure these batch sizes (32: large-v3 greedy verify, 96: "
                          "large-v3 with the parallel drafter); empty for none")
+    ap.add_argument("--configs", default="2,4",
+                    help="also measure these workloads (2: turbo batch 32, 4: large-v3 batch 32 "
+                         "at T = 0.7); empty for none")
     ap.add_argument("--k-sweep", default="",
                     help="comma-separated K values: time the step of --config at each K "
                          "(the pass cost against the number of candidates) and print that "
@@ -765,18 +1043,64 @@ def main():
     if args.encoder:
         encoder_bench(args)
         return
-    w = Workload(args.config, greedy=args.greedy)
-    r = measure(w, K, W, use_graph=not args.no_graph)
-    kinds, dom = r["kinds"], r["dom"]
-    value = r["value"]
+    cpu = {}
+    stream_gbs = None
+    results = {}
+    head_key = None
+    # the headline workload first, then the metric's other batch sizes and
+    # the other workloads, each on its own engine
+    plan = [("config", args.config, args.greedy)]
+    for bkey in [b.strip() for b in args.batches.split(",") if b.strip()]:
+        if bkey in BATCHES and BATCHES[bkey] != (args.config, args.greedy):
+            plan.append(("batch", *BATCHES[bkey]))
+    for ckey in [c.strip() for c in args.configs.split(",") if c.strip()]:
+        if ckey in CONFIGS and CONFIGS[ckey] != (args.config, args.greedy):
+            plan.append(("config", *CONFIGS[ckey]))
+    for n, (what, cfg, greedy) in enumerate(plan):
+        w = Workload(cfg, greedy=greedy)
+        r = measure(w, K, W, use_graph=not args.no_graph)
+        lp = measure_sampling_loop(w, K, W) if w.sampling else measure_loop(w, K, W)
+        ent = entry(w, r, lp)
+        ent["config_id"] = cfg
+        if args.trace:
+            ent["pass_trace"] = pass_trace(w)
+        if n == 0:
+            head_key = w.name
+            if not args.no_stream_bw:
+                stream_gbs = round(stream_bandwidth(torch, w.eng.dev), 1)
+            if args.calib_copy_mib:
+                nb = args.calib_copy_mib << 20
+                src = torch.ones(nb, dtype=torch.uint8, device=w.eng.dev)
+                dst = torch.empty_like(src)
+                for _ in range(3):
+                    dst.copy_(src)
+                torch.cuda.synchronize()
+                ent["calib_copy_bytes"] = nb
+                del src, dst
+        if not args.no_cpu and (n == 0 or cfg in (2, 3) or w.sampling):
+            t0 = time.time()
+            if n == 0:
+                cpu[cfg] = cpu_baseline(w, timed_s=8.0)
+                cpu["threads_1"] = cpu_baseline(w, timed_s=5.0, threads=1)
+            else:
+                cpu[cfg] = cpu_baseline(w, timed_s=4.0)
+            log(f"[bench] {w.name}: cpu baseline took {time.time() - t0:.1f}s")
+        results[w.name] = (w.B, cfg, ent)
+        log(f"[bench] {w.name}: pass {r['ms_step']:.3f} ms, loop {lp['ms_per_round']:.3f} "
+            f"ms/round, {lp['tokens_per_s']:.1f} tokens/s")
+        w.eng.close()
+        del w, r
+        torch.cuda.empty_cache()
+
+    B0, cfg0, head = results[head_key]
     out = {
         "metric": METRIC,
-        "value": round(value, 2),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": W,
-        "ms_per_step": round(r["ms_step"], 4),
+        "ms_per_step": head["ms_per_round"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -785,63 +1109,37 @@ def main():
                      "fp16 in registers), fp32 accumulate, fp32 residual stream, softmax and "
                      "layer-norm statistics",
         "data": "synthetic (seeded weights N(0,0.02) in bf16, audio memory N(0,1), "
-                "Bernoulli-copy drafts)",
-        "config": {"workload": w.name, "layers": w.shape.n_layers,
-                   "d_model": w.shape.d_model, "batch": w.B, "K": w.K,
-                   "prefix": w.wl.prefix,
-                   "p_keep": w.wl.p_keep if not (w.sampling or w.drafter) else None,
-                   "drafter_layers": w.wl.drafter_layers,
-                   "temperature": w.temperature, "graph": r["graph"]},
-        "audio_s_per_s": round(value / TOKENS_PER_AUDIO_S, 2),
-        "tokens_per_step": r["tokens_per_step"],
-        "step_ms_p10_p50_p90": r["step_ms_p10_p50_p90"],
-        "accepted": r["accepted"],
-        "acceptance": r["acceptance"],
-        "pass": {"bytes": r["bytes_pass"], "roofline_frac_of_step": round(r["pass_frac"], 4)},
-        "roofline": {"bound": "hbm", "kernel": dom, "symbol": KIND_SYMBOL.get(dom, dom),
-                     "achieved": round(r["achieved"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(r["achieved"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic_of(w.name, dom),
-                     "bytes_per_launch": r["dom_bytes"], "avg_us": round(r["dom_avg_us"], 3)},
-        "kernels": {k: {kk: round(vv, 3) for kk, vv in v.items()} for k, v in kinds.items()},
-        "encode_kv_s": round(w.encode_kv_s, 4),
-        "batches": {str(w.B): summary(w, r)},
+                "Bernoulli-copy drafts of the engine's own greedy continuation)",
+        "config": {"workload": head_key, "layers": head["layers"], "d_model": head["d_model"],
+                   "batch": B0, "K": head["K"], "graph": not args.no_graph,
+                   "step": "one round of the running loop: drafts, wf_verify_block, wf_accept, "
+                           "wf_rollback, loop state"},
+        "audio_s_per_s": head["audio_s_per_s"],
+        "tau": head["tau"],
+        "expected_tau": head["expected_tau"],
+        "tokens_per_s_at_expected_tau": head["tokens_per_s_at_expected_tau"],
+        "pass": {"ms": head["pass_ms"], "bytes": head["pass_bytes"],
+                 "roofline_frac_of_step": head["pass_roofline_frac"]},
+        "roofline": head["roofline"],
+        "batches": {}, "configs": {},
     }
-    if args.trace:
-        out["batches"][str(w.B)]["pass_trace"] = pass_trace(w)
-    if not args.no_stream_bw:
-        out["stream_gbs"] = round(stream_bandwidth(torch, w.eng.dev), 1)
-        out["pass"]["stream_frac"] = round(r["bytes_pass"] / (r["ms_step"] * 1e-3)
-                                           / (out["stream_gbs"] * 1e9), 4)
-    if args.calib_copy_mib:
-        n = args.calib_copy_mib << 20
-        src = torch.ones(n, dtype=torch.uint8, device=w.eng.dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        out["calib_copy_bytes"] = n
-        del src, dst
-    if not args.no_cpu:
-        t0 = time.time()
-        out["cpu_baseline"] = cpu_baseline(w)
-        log(f"[bench] cpu baseline took {time.time() - t0:.1f}s")
-    # the other batch sizes of the metric, each its own engine
-    for bkey in [b for b in args.batches.split(",") if b.strip()]:
-        if bkey not in EXTRA or bkey == str(w.B):
-            continue
-        w.eng.close()
-        del w
-        torch.cuda.empty_cache()
-        cfg, greedy = EXTRA[bkey]
-        w = Workload(cfg, greedy=greedy)
-        r2 = measure(w, max(5, K // 2), max(2, W // 2), use_graph=not args.no_graph)
-        out["batches"][bkey] = summary(w, r2)
-        out["batches"][bkey]["kernels_avg_us"] = {k: round(v["avg_us"], 2)
-                                                  for k, v in r2["kinds"].items()}
-        if args.trace:
-            out["batches"][bkey]["pass_trace"] = pass_trace(w)
-        log(f"[bench] batch {bkey}: {r2['ms_step']:.3f} ms/step")
+    if stream_gbs:
+        out["stream_gbs"] = stream_gbs
+        out["pass"]["stream_frac"] = round(head["pass_bytes"] / (head["pass_ms"] * 1e-3)
+                                           / (stream_gbs * 1e9), 4)
+    for name, (B, cfg, ent) in results.items():
+        if ent is head or cfg in (1, 3) or (cfg == 4 and "greedy" in name):
+            out["batches"][str(B)] = ent
+        if cfg in (2, 4) and "greedy" not in name:
+            out["configs"][str(cfg)] = ent
+    if cpu:
+        base = dict(cpu[cfg0])
+        base.update(cpu_info())
+        if "threads_1" in cpu:
+            base["threads_1"] = {k: cpu["threads_1"][k] for k in ("value", "cores", "timed_s")}
+        base["configs"] = {str(c): {k: v[k] for k in ("value", "unit", "cores", "sample")}
+                           for c, v in cpu.items() if c not in (cfg0, "threads_1")}
+        out["cpu_baseline"] = base
     print(json.dumps(out), flush=True)
 
 

@@ -221,8 +221,10 @@ wf_status wf_verify_block(wf_engine *e, int32_t n, const int32_t *d_slots,
  * d_anchor int32 [n]; d_block int32 [n][K+1] receives the anchor followed
  * by the K drafts, ready for wf_verify_block; d_logits: NULL or fp32
  * [n][K+1][vocab] drafter logits (row 0 is the anchor row). The slot must not be pending;
- * its length is unchanged. Requires drafter_layers > 0, 1 <= K,
- * n*(K+1) <= max_rows. */
+ * its length is unchanged. Within K tokens of the context end the block is
+ * cut to the n_ctx - L rows that fit: drafts past them are -1 (a verify
+ * must then propose at most n_ctx - L - 1 candidates). Requires
+ * drafter_layers > 0, 1 <= K, n*(K+1) <= max_rows. */
 wf_status wf_draft(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_anchor,
                    int32_t K, int32_t *d_block, float *d_logits, void *stream);
 

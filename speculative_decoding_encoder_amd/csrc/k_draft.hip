@@ -75,9 +75,12 @@ __global__ void prepare_draft_kernel(PrepareDraftArgs a) {
     const int anc = a.anchor[b];
     if (anc < 0 || anc >= a.V) code |= WF_DERR_TOKEN;
     if (a.slot_pending[slot] != 0) code |= WF_DERR_STATE;
-    if (L + a.K + 1 > a.n_ctx) code |= WF_DERR_CONTEXT;
+    // near the end of the context the block keeps the rows that fit (the
+    // drafts past them come out as -1); a full cache drafts nothing
+    const int nt = min(a.K + 1, a.n_ctx - L);
+    if (nt <= 0) return;
     if (code == 0) {
-        for (int j = 0; j <= (L + a.K) / 16; ++j) {
+        for (int j = 0; j <= (L + nt - 1) / 16; ++j) {
             const int p = a.page_table[(size_t)slot * a.pt_stride + j];
             if (p < 0 || p >= a.n_pages) code |= WF_DERR_PAGE;
         }
@@ -87,7 +90,7 @@ __global__ void prepare_draft_kernel(PrepareDraftArgs a) {
         return;
     }
     a.req_L[b] = L;
-    a.req_ntok[b] = a.K + 1;
+    a.req_ntok[b] = nt;
 }
 
 __global__ __launch_bounds__(256) void embed_draft_kernel(EmbedDraftArgs a) {
@@ -107,8 +110,8 @@ __global__ void draft_out_kernel(const int32_t *anchor, const int32_t *argmax,
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= n * (K + 1)) return;
     const int b = idx / (K + 1), i = idx - (idx / (K + 1)) * (K + 1);
-    if (req_ntok[b] == 0) block[idx] = -1;
-    else block[idx] = i == 0 ? anchor[b] : argmax[idx];
+    if (req_ntok[b] == 0) block[idx] = i == 0 ? anchor[b] : -1;
+    else block[idx] = i == 0 ? anchor[b] : (i < req_ntok[b] ? argmax[idx] : -1);
 }
 
 hipError_t launch_tap(const TapArgs &a, hipStream_t st) {

@@ -94,7 +94,7 @@ def run_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], n_max: i
             if done[b]:
                 continue
             R = n_max - len(res.tokens[b])
-            k = min(K, R - 1)
+            k = min(K, R - 1, eng.shape.n_ctx - L[b] - 1)
             drafts = draft_fn(b, L[b], y[b], k) if k > 0 else []
             toks[b, 0] = y[b]
             toks[b, 1:1 + k] = drafts
@@ -155,6 +155,7 @@ def run_drafter_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], 
         res.tokens[b].append(y[b])
     done = [y[b] == eos or n_max <= 1 for b in range(n)]
     T = K + 1
+    L = [len(p) for p in prefixes]
     d_slots = eng.i32(slots)
     d_block = torch.empty((n, T), dtype=torch.int32, device=eng.dev)
     d_am = torch.empty((n, T), dtype=torch.int32, device=eng.dev)
@@ -166,7 +167,7 @@ def run_drafter_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], 
             if done[b]:
                 continue
             R = n_max - len(res.tokens[b])
-            ntok[b] = 1 + min(K, R - 1)
+            ntok[b] = 1 + min(K, R - 1, eng.shape.n_ctx - L[b] - 1)
             budget[b] = R
         anchor = np.array([max(v, 0) for v in y], np.int32)
         eng.wf_draft(d_slots, eng.i32(anchor), K, d_block)
@@ -189,6 +190,138 @@ def run_drafter_loop(eng, slots: Sequence[int], prefixes: Sequence[np.ndarray], 
             res.tokens[b].extend(emitted)
             res.accepted[b].append(a)
             res.proposed[b].append(int(ntok[b] - 1))
+            L[b] += 1 + a
             y[b] = int(nxt[b])
             done[b] = bool(dn[b])
     return res
+
+
+class DeviceLoop:
+    """A speculative round loop whose state lives on the device, so that a
+    round (build the block, wf_verify_block, wf_accept, wf_rollback, update
+    the state) needs no host synchronisation and can be captured once and
+    replayed as a HIP graph.
+
+    Drafts: ``draft_table`` int32 [n][n_ctx + K + 2] gives the candidate at
+    each absolute position (the synthetic table drafter: the greedy token
+    there with probability p, else a replacement id), or ``drafter=True``
+    takes the engine's own parallel drafter (wf_draft). Requests that are
+    done get n_tok = 0 and are skipped by the engine. The torch operations
+    here are the harness (indexing and counters), not method arithmetic."""
+
+    def __init__(self, eng, slots: Sequence[int], anchors: np.ndarray, lens: np.ndarray,
+                 n_max: int, K: int, eos: int, draft_table: Optional[np.ndarray] = None,
+                 drafter: bool = False, logits: bool = False):
+        torch = eng.torch
+        self.eng, self.torch, self.K, self.n_max, self.eos = eng, torch, K, n_max, eos
+        n = len(slots)
+        self.n = n
+        dev = eng.dev
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.d_slots = eng.i32(slots)
+        self.anchor = torch.as_tensor(np.asarray(anchors, np.int32), device=dev)
+        self.L = torch.as_tensor(np.asarray(lens, np.int32), device=dev)
+        anchors = np.asarray(anchors)
+        self.emitted = torch.ones(n, **i32)
+        self.done = torch.as_tensor(((anchors == eos) | (n_max <= 1)).astype(np.int32), device=dev)
+        self.acc_sum = torch.zeros(n, **i32)
+        self.prop_sum = torch.zeros(n, **i32)
+        self.rounds_active = torch.zeros(n, **i32)
+        self.step = torch.zeros(n, **i32)
+        self.tok_sum = torch.zeros(n, **i32)       # tokens emitted by the rounds
+        self.hist = torch.zeros(K + 1, dtype=torch.int64, device=dev)   # accepted-length counts
+        T = K + 1
+        self.block = torch.zeros((n, T), **i32)
+        self.ntok = torch.zeros(n, **i32)
+        self.budget = torch.ones(n, **i32)
+        self.am = torch.empty((n, T), **i32)
+        self.outs = [torch.empty(n, **i32) for _ in range(4)]
+        self.logits = (torch.empty((n, T, eng.shape.vocab), dtype=torch.float32, device=dev)
+                       if logits else None)
+        self.drafter = drafter
+        self.table = None
+        if draft_table is not None:
+            self.table = torch.as_tensor(np.ascontiguousarray(draft_table, np.int32), device=dev)
+        self.ar = torch.arange(1, T, device=dev, dtype=torch.int32)
+
+    def prepare(self):
+        """This round's block, n_tok and budgets from the state."""
+        torch = self.torch
+        R = self.n_max - self.emitted
+        room = self.eng.shape.n_ctx - self.L - 1     # candidates that still fit the context
+        k = torch.clamp(torch.minimum(torch.minimum(torch.full_like(R, self.K), R - 1), room), min=0)
+        self.ntok.copy_(torch.where(self.done > 0, torch.zeros_like(k), k + 1))
+        self.budget.copy_(torch.clamp(R, min=1))
+        if self.drafter:
+            self.eng.wf_draft(self.d_slots, self.anchor, self.K, self.block)
+        else:
+            pos = (self.L[:, None] + self.ar[None, :]).clamp(max=self.table.shape[1] - 1)
+            self.block[:, 1:].copy_(torch.gather(self.table, 1, pos.long()))
+            self.block[:, 0].copy_(self.anchor)
+
+    def verify(self):
+        self.eng.wf_verify_block(self.d_slots, self.block, self.ntok, self.am, self.logits)
+
+    def accept(self, **kw):
+        self.eng.wf_accept(self.block, self.ntok, self.budget, self.am, *self.outs, **kw)
+
+    def finish(self):
+        """Rollback and the state update of the round."""
+        torch = self.torch
+        n_acc, nxt, n_emit, dn = self.outs
+        self.eng.wf_rollback(self.d_slots, n_acc)
+        active = self.ntok > 0
+        zero = torch.zeros_like(n_acc)
+        acc = torch.where(active, n_acc, zero)
+        self.L.add_(torch.where(active, acc + 1, zero))
+        self.anchor.copy_(torch.where(active & (nxt >= 0), nxt, self.anchor))
+        self.emitted.add_(torch.where(active, n_emit, zero))
+        self.tok_sum.add_(torch.where(active, n_emit, zero))
+        self.done.copy_(torch.where(active & (dn > 0), torch.ones_like(dn), self.done))
+        self.acc_sum.add_(acc)
+        self.prop_sum.add_(torch.where(active, self.ntok - 1, zero))
+        self.rounds_active.add_(active.to(torch.int32))
+        self.step.add_(active.to(torch.int32))
+        self.hist.index_add_(0, acc.clamp(0, self.K).long(), active.long())
+
+    def restart(self, anchors: np.ndarray, lens: np.ndarray):
+        """Start every request again from a fresh prefill (anchors, lengths),
+        in place, so that a captured round stays valid; the totals carry on."""
+        torch = self.torch
+        anchors = np.asarray(anchors, np.int32)
+        self.anchor.copy_(torch.as_tensor(anchors, device=self.eng.dev))
+        self.L.copy_(torch.as_tensor(np.asarray(lens, np.int32), device=self.eng.dev))
+        self.emitted.fill_(1)
+        self.done.copy_(torch.as_tensor(((anchors == self.eos) | (self.n_max <= 1)).astype(np.int32),
+                                        device=self.eng.dev))
+
+    def round(self, **accept_kw):
+        self.prepare()
+        self.verify()
+        self.accept(**accept_kw)
+        self.finish()
+
+    def counters(self) -> dict:
+        """Host copy of the totals: tokens emitted so far per request
+        (including its first anchor), tokens the rounds emitted, accepted and proposed candidates, active request-rounds,
+        the accepted-length histogram, and whether every request is done."""
+        return {"emitted": self.emitted.cpu().numpy().copy(),
+                "tokens": int(self.tok_sum.sum().item()),
+                "accepted": int(self.acc_sum.sum().item()),
+                "proposed": int(self.prop_sum.sum().item()),
+                "request_rounds": int(self.rounds_active.sum().item()),
+                "hist": self.hist.cpu().numpy().copy(),
+                "all_done": bool((self.done > 0).all().item())}
+
+
+def draft_table(greedy: Sequence[int], prefix_len: int, keep: np.ndarray, repl: np.ndarray,
+                size: int) -> np.ndarray:
+    """Per absolute position t < size: the table drafter's candidate there
+    (greedy[t - prefix_len] when keep[t], else repl[t]; past the known greedy
+    continuation, repl[t])."""
+    out = np.zeros(size, np.int32)
+    for t in range(size):
+        j = t - prefix_len
+        g = greedy[j] if 0 <= j < len(greedy) else int(repl[min(t, len(repl) - 1)])
+        out[t] = int(g) if keep[min(t, len(keep) - 1)] else int(repl[min(t, len(repl) - 1)])
+    return out

@@ -112,6 +112,34 @@ def test_tiny_drafter_loop_equals_greedy(torch_cuda):
     eng.close()
 
 
+def test_tiny_drafter_loop_at_the_context_end_equals_greedy(torch_cuda):
+    """Requests whose decoding runs into the last K positions of the context
+    (prompts of 430 and 441 tokens, n_ctx 448, K 8): the drafter proposes
+    only the rows that fit (no error word) and the loop still equals plain
+    greedy decoding token for token."""
+    from speculative_decoding_encoder_amd.harness import run_drafter_loop, run_loop
+    wl = WORKLOADS[0]
+    tw = make_weights(TINY, wl.cfg_id)
+    dw = make_drafter_weights(TINY, wl.cfg_id)
+    rng = np.random.default_rng(31)
+    encs = np.stack([make_encoder_out(TINY, wl.cfg_id, r) for r in range(2)])
+    prefixes = [rng.integers(0, TINY.eos_id, 430).astype(np.int32),
+                rng.integers(0, TINY.eos_id, 441).astype(np.int32)]
+    # budgets that end exactly at the context end: P + n_max - 1 <= n_ctx
+    n_max = TINY.n_ctx - 441 + 1
+    eng = _engine(TINY, tw, dw, TINY_TAPS, 2, 2 * 448)
+    eng.wf_encode_kv(eng.i32([0, 1]), eng.bf16(encs))
+    g = run_loop(eng, [0, 1], prefixes, n_max, 0, None, TINY.eos_id)
+    eng.wf_reset(eng.i32([0, 1]))
+    s = run_drafter_loop(eng, [0, 1], prefixes, n_max, 8, TINY.eos_id)
+    err, ln = eng.wf_device_state()
+    assert (err == 0).all(), err
+    for b in range(2):
+        assert s.tokens[b] == g.tokens[b], b
+    log(f"tiny drafter loop at the context end == greedy ({n_max} tokens, lengths {ln[:2]})")
+    eng.close()
+
+
 def test_large_v3_drafter_logits(torch_cuda):
     torch = torch_cuda
     wl = WORKLOADS[3]
