@@ -668,18 +668,21 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
 
 
 def pass_trace(w: "Workload") -> dict:
-    """Per-phase picture of one persistent verify pass from its task trace
+    """Per-phase picture of one persistent verify pass (switched on for this
+    one step; the library's default is the multi-kernel path) from its task trace
     (wf_set_trace: the 100 MHz device clock at each task's start, when its
     inputs were ready, and at its end): per phase, the tasks' summed wait
     and work time over all layers, and the mean per-layer span from the
     first task's start to the last one's end; the kernel's span."""
-    from speculative_decoding_encoder_amd.binding import PASS_PHASES
+    from speculative_decoding_encoder_amd.binding import PASS_PHASES, WF_OPT_PERSISTENT
     torch, eng = w.torch, w.eng
     buf = torch.zeros((1 << 17, 4), dtype=torch.int64, device=eng.dev)
+    eng.wf_set_option(WF_OPT_PERSISTENT, 1)
     eng.wf_set_trace(buf)
     w.step()
     torch.cuda.synchronize()
     eng.wf_set_trace(None)
+    eng.wf_set_option(WF_OPT_PERSISTENT, 0)
     sc = eng.wf_pass_schedule()
     total, per, nl = sc["total"], sc["per_layer"], sc["layers"]
     if total == 0 or total > buf.shape[0]:

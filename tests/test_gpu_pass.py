@@ -45,7 +45,8 @@ def _verify(eng, slots, tokens, n_tok, logits=True):
 
 
 def _setup(B, seed=0, drafter=False):
-    from speculative_decoding_encoder_amd.binding import Engine
+    """Turbo engine on the persistent pass (not the library's default)."""
+    from speculative_decoding_encoder_amd.binding import Engine, WF_OPT_PERSISTENT
     wl = WORKLOADS[2]
     shape = TURBO
     wbits = make_weights(shape, wl.cfg_id)
@@ -54,6 +55,7 @@ def _setup(B, seed=0, drafter=False):
     pps = shape.n_ctx // 16
     perm = np.random.default_rng(7 + seed).permutation(B * pps).astype(np.int32)
     eng = Engine(shape, wbits, max_batch=B, max_rows=max(B * 9, 64), page_table=perm.reshape(B, pps))
+    eng.wf_set_option(WF_OPT_PERSISTENT, 1)
     slots = list(range(B))
     eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
     return wl, shape, wbits, encs, prefixes, eng, slots
@@ -143,8 +145,7 @@ def test_pass_timeout_aborts_and_flags(torch_cuda):
     wait ends on the abort flag and the kernel drains. The requests' error
     words carry WF_DERR_TIMEOUT; after wf_reset and a normal limit the
     pass is exact again."""
-    from speculative_decoding_encoder_amd.binding import (WF_DERR_TIMEOUT, WF_OPT_PASS_TIMEOUT_US,
-                                                          WF_OPT_PERSISTENT)
+    from speculative_decoding_encoder_amd.binding import WF_DERR_TIMEOUT, WF_OPT_PASS_TIMEOUT_US
     B = 8
     wl, shape, wbits, encs, prefixes, eng, slots = _setup(B, seed=5)
     _prefill(eng, slots, prefixes)
@@ -174,6 +175,7 @@ def test_pass_trace_covers_the_schedule(torch_cuda):
     _verify(eng, slots, blocks, [9] * B, logits=False)
     eng.wf_set_trace(None)
     sched = eng.wf_pass_schedule()
+    assert 0 < sched["total"] <= buf.shape[0]
     tr = buf.cpu().numpy()[:sched["total"]]
     assert (tr[:, 0] > 0).all() and (tr[:, 1] >= tr[:, 0]).all() and (tr[:, 2] >= tr[:, 1]).all()
     span = (tr[:, 2].max() - tr[:, 0].min()) / 100.0
