@@ -179,6 +179,23 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w,
 void wf_destroy(wf_engine *e);
 const char *wf_last_error(void);
 
+/* For callers that cannot allocate device memory (harnesses that forbid
+ * hipMalloc, serving loops that must not allocate): wf_create with the
+ * library's own workspace instead of a caller-supplied one. The workspace is
+ * a static device array of WF_STATIC_WORKSPACE_BYTES per device, resident
+ * from the library's load until the process ends; this call allocates no
+ * device memory (the caller still supplies the weights, both KV pools and
+ * the page table). The array is cleared here (synchronously), like any
+ * workspace. At most one such engine may live on a device at a time:
+ * WF_ESTATE while another holds it, until wf_destroy releases it. Fails with
+ * WF_ECAPACITY when wf_workspace_bytes(cfg) exceeds the array; otherwise as
+ * wf_create. Calls on the engine that overlap race, as on any engine. */
+#define WF_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+wf_status wf_create_static(const wf_config *cfg, const wf_weights *w,
+                           void *kv_pool, size_t kv_bytes,
+                           void *xkv_pool, size_t xkv_bytes,
+                           const int32_t *d_page_table, wf_engine **out);
+
 /* Set cache length 0, clear the pending-verify flag and the error word of
  * n slots. */
 wf_status wf_reset(wf_engine *e, int32_t n, const int32_t *d_slots, void *stream);

@@ -100,6 +100,8 @@ def load():
         "wf_workspace_bytes": (SZ, [cfgp]),
         "wf_create": (I32, [cfgp, ctypes.POINTER(Weights), P, SZ, P, SZ, P, P, SZ,
                             ctypes.POINTER(VP)]),
+        "wf_create_static": (I32, [cfgp, ctypes.POINTER(Weights), P, SZ, P, SZ, P,
+                                   ctypes.POINTER(VP)]),
         "wf_destroy": (None, [P]),
         "wf_last_error": (ctypes.c_char_p, []),
         "wf_reset": (I32, [P, I32, P, P]),
@@ -184,7 +186,7 @@ class Engine:
                  max_rows: int, page_table: Optional[np.ndarray] = None,
                  n_pages: Optional[int] = None,
                  drafter_bits: Optional[Dict[str, np.ndarray]] = None,
-                 taps: Sequence[int] = ()):
+                 taps: Sequence[int] = (), static_workspace: bool = False):
         import torch
         self.torch = torch
         self.lib = load()
@@ -225,15 +227,23 @@ class Engine:
             raise WFError("invalid configuration for libwf")
         self.kv = torch.zeros(kvb, dtype=torch.uint8, device=self.dev)
         self.xkv = torch.zeros(xkvb, dtype=torch.uint8, device=self.dev)
-        self.ws = torch.zeros(wsb, dtype=torch.uint8, device=self.dev)
+        # with static_workspace the library's own array serves (wf_create_static)
+        self.ws = None if static_workspace else torch.zeros(wsb, dtype=torch.uint8,
+                                                            device=self.dev)
         if page_table is None:
             page_table = np.arange(max_batch * pps, dtype=np.int32).reshape(max_batch, pps)
         self.page_table = torch.from_numpy(np.ascontiguousarray(page_table, dtype=np.int32)).to(self.dev)
         h = ctypes.c_void_p()
         torch.cuda.synchronize()
-        _check(self.lib.wf_create(cfgp, ctypes.byref(self._weights), self.kv.data_ptr(), kvb,
-                                  self.xkv.data_ptr(), xkvb, self.page_table.data_ptr(),
-                                  self.ws.data_ptr(), wsb, ctypes.byref(h)), "wf_create")
+        if static_workspace:
+            _check(self.lib.wf_create_static(cfgp, ctypes.byref(self._weights),
+                                             self.kv.data_ptr(), kvb, self.xkv.data_ptr(), xkvb,
+                                             self.page_table.data_ptr(), ctypes.byref(h)),
+                   "wf_create_static")
+        else:
+            _check(self.lib.wf_create(cfgp, ctypes.byref(self._weights), self.kv.data_ptr(),
+                                      kvb, self.xkv.data_ptr(), xkvb, self.page_table.data_ptr(),
+                                      self.ws.data_ptr(), wsb, ctypes.byref(h)), "wf_create")
         self.h = h
 
     def close(self):
@@ -354,6 +364,7 @@ TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
 WF_OPT_PERSISTENT, WF_OPT_TALL_GEMM, WF_OPT_LN_FUSION, WF_OPT_XA_CHUNKS = 1, 2, 3, 4
 WF_OPT_PASS_TIMEOUT_US = 5
 WF_DERR_TIMEOUT = 128
+WF_STATIC_WORKSPACE_BYTES = 64 << 20
 PASS_PHASES = ["ln1", "qkv", "self_attn", "oproj", "ln2", "cross_q", "cross_attn", "oproj_c",
                "ln3", "fc1", "fc2"]
 

@@ -11,6 +11,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -182,6 +183,7 @@ enum TimingKind {
 struct wf_engine {
     wf_config c;
     Layout lay;
+    int static_dev = -1;                    // device whose static workspace it holds, or -1
     int F_pad, pt_stride, page_elems;
     const uint16_t *tok_emb, *pos_emb, *lnf_g, *lnf_b;
     std::vector<LayerW> layers;
@@ -420,6 +422,19 @@ namespace wf {
 wf_status set_error(wf_status s, const char *msg) { return fail(s, "%s", msg); }
 }  // namespace wf
 
+// The workspace of engines made by wf_create_static: one array per device,
+// resident from the code object's load until the process ends. In host code
+// the name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) char scratch[WF_STATIC_WORKSPACE_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[kMaxDevices];      // per device: the address of scratch there
+bool g_static_held[kMaxDevices];      // per device: an engine owns the array
+}  // namespace
+
 extern "C" {
 
 size_t wf_kv_pool_bytes(const wf_config *c) {
@@ -575,7 +590,47 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
 void wf_destroy(wf_engine *e) {
     if (!e) return;
     for (hipEvent_t ev : e->ev_pool) hipEventDestroy(ev);
+    if (e->static_dev >= 0) {
+        std::lock_guard<std::mutex> g(g_static_mu);
+        g_static_held[e->static_dev] = false;
+    }
     delete e;
+}
+
+wf_status wf_create_static(const wf_config *cfg, const wf_weights *w, void *kv_pool,
+                           size_t kv_bytes, void *xkv_pool, size_t xkv_bytes,
+                           const int32_t *d_page_table, wf_engine **out) {
+    if (!out) return fail(WF_EINVAL, "out is null");
+    *out = nullptr;
+    std::string why;
+    if (!config_ok(cfg, &why)) return fail(WF_ESHAPE, "bad config: %s", why.c_str());
+    const size_t need = wf_workspace_bytes(cfg);
+    if (need > WF_STATIC_WORKSPACE_BYTES)
+        return fail(WF_ECAPACITY,
+                    "this configuration needs a %zu-byte workspace; the static one holds %zu "
+                    "(lower max_rows or max_batch, or use wf_create)",
+                    need, (size_t)WF_STATIC_WORKSPACE_BYTES);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return fail(WF_EDEVICE, "no HIP device");
+    if (dev < 0 || dev >= kMaxDevices) return fail(WF_EDEVICE, "device %d out of range", dev);
+    std::lock_guard<std::mutex> g(g_static_mu);
+    if (g_static_held[dev])
+        return fail(WF_ESTATE, "an engine on device %d already holds the static workspace", dev);
+    if (!g_static_ptr[dev]) {
+        void *ptr = nullptr;
+        const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (r != hipSuccess || !ptr)
+            return fail(WF_EHIP, "hipGetSymbolAddress of the static workspace failed: %s",
+                        hipGetErrorString(r));
+        g_static_ptr[dev] = ptr;
+    }
+    // wf_create checks everything else and clears the array before use
+    const wf_status st = wf_create(cfg, w, kv_pool, kv_bytes, xkv_pool, xkv_bytes, d_page_table,
+                                   g_static_ptr[dev], WF_STATIC_WORKSPACE_BYTES, out);
+    if (st != WF_OK) return st;
+    (*out)->static_dev = dev;
+    g_static_held[dev] = true;
+    return WF_OK;
 }
 
 wf_status wf_reset(wf_engine *e, int32_t n, const int32_t *d_slots, void *stream) {
