@@ -363,6 +363,9 @@ TIMING_KINDS = ["qkv", "oproj", "cross_q", "fc1", "fc2", "lm_head", "self_attn",
 # wf_set_option options (include/wf.h)
 WF_OPT_PERSISTENT, WF_OPT_TALL_GEMM, WF_OPT_LN_FUSION, WF_OPT_XA_CHUNKS = 1, 2, 3, 4
 WF_OPT_PASS_TIMEOUT_US = 5
+# device error word bits (include/wf.h)
+WF_DERR_CONTEXT, WF_DERR_TOKEN, WF_DERR_STATE, WF_DERR_ACCEPT = 1, 2, 4, 8
+WF_DERR_NAN, WF_DERR_PAGE, WF_DERR_SAMPLE = 16, 32, 64
 WF_DERR_TIMEOUT = 128
 WF_STATIC_WORKSPACE_BYTES = 64 << 20
 PASS_PHASES = ["ln1", "qkv", "self_attn", "oproj", "ln2", "cross_q", "cross_attn", "oproj_c",

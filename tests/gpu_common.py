@@ -35,14 +35,15 @@ def assert_argmax_where_clear(gpu_am: np.ndarray, ref_logits: np.ndarray, what="
 
 
 def oracle_accept_pinned(drafts, ref_logits, k):
-    """The oracle's accepted length, and whether the GPU must match it:
-    every row the decision reads (0..min(a, k)) has a clear margin."""
+    """The oracle's accepted length and next token, and whether the GPU
+    must match them: every row they read (0..a) has a clear margin."""
     g = ref_logits.argmax(-1)
     a = 0
     while a < k and drafts[a] == g[a]:
         a += 1
     m = margins(ref_logits)
-    pinned = bool((m[:min(a, k - 1) + 1 if k > 0 else 1] > MARGIN).all())
+    # rows 0..a-1 decide the acceptance, row a gives the next token
+    pinned = bool((m[:a + 1] > MARGIN).all())
     return a, int(g[a]), pinned
 
 

@@ -7,7 +7,10 @@ against the oracle drafter.
   pages print no drafter values);
 * speculative decoding with the engine's own drafter equals GPU greedy
   decoding (the lossless property holds for any drafts);
-* the full large-v3 shape with taps after blocks 1, 8, 15, 22 and 29.
+* the full large-v3 shape with taps after blocks 1, 8, 15, 22 and 29;
+* a round at 96 requests (turbo shape, Poisson prefixes, shuffled pages):
+  drafter, 864-row verify and the next drafter pass of three sampled
+  requests against the oracle.
 """
 import numpy as np
 import pytest
@@ -16,7 +19,7 @@ from gpu_common import assert_argmax_where_clear, assert_logits_close, log
 from oracle import decode as od
 from oracle import drafter as odr
 from oracle import model as om
-from synthetic import (DRAFTER_TAPS, LARGE_V3, TINY, WORKLOADS, make_drafter_weights,
+from synthetic import (DRAFTER_TAPS, LARGE_V3, TINY, TURBO, WORKLOADS, make_drafter_weights,
                        make_encoder_out, make_prefixes, make_weights)
 
 pytestmark = pytest.mark.gpu
@@ -167,4 +170,90 @@ def test_large_v3_drafter_logits(torch_cuda):
     err = assert_logits_close(glg[0], ref, what="large-v3 drafter")
     assert_argmax_where_clear(blk[0, 1:], ref[1:], what="large-v3 drafts")
     log(f"large-v3 drafter: max err {err:.2e}")
+    eng.close()
+
+
+def test_turbo_b96_drafter_round_against_oracle(torch_cuda):
+    """Config 3's batch on the turbo shape: 96 requests with Poisson(80)
+    prefixes clipped to [4, 224] and shuffled pages. Three sampled requests
+    (the first, the longest and the shortest prompt) against the oracle:
+    their drafter logits after the prefill, the target's logits of the
+    864-row verify pass, and the drafter logits of the next round after a
+    rollback that kept 3, 0 and 8 candidates (the history appended from the
+    taps of the kept rows). The sampled requests' anchors and blocks are the
+    oracle's own; the other 93 run on the GPU's drafts."""
+    wl = WORKLOADS[3]
+    shape = TURBO
+    B, K = wl.batch, wl.k_draft
+    taps = (0, 1, 2, 3, 3)
+    tw = make_weights(shape, wl.cfg_id)
+    dw = make_drafter_weights(shape, wl.cfg_id)
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    prefixes = make_prefixes(wl, B)
+    lens = np.array([len(p) for p in prefixes], np.int32)
+    pps = shape.n_ctx // 16
+    perm = np.random.default_rng(11).permutation(B * pps).astype(np.int32).reshape(B, pps)
+    from speculative_decoding_encoder_amd.binding import Engine
+    eng = Engine(shape, tw, max_batch=B, max_rows=B * (K + 1), page_table=perm,
+                 drafter_bits=dw, taps=taps)
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    torch = eng.torch
+    anchors = np.zeros(B, np.int32)
+    for b in range(B):
+        P = int(lens[b])
+        am = torch.empty((1, P), dtype=torch.int32, device=eng.dev)
+        eng.wf_verify_block(eng.i32([b]), eng.i32(prefixes[b][None]), eng.i32([P]), am)
+        eng.wf_rollback(eng.i32([b]), eng.i32([P - 1]))
+        anchors[b] = int(am[0, P - 1].item())
+    sample = sorted({0, int(np.argmax(lens)), int(np.argmin(lens))})
+    log(f"b96 drafter: prompts {lens.min()}..{lens.max()}, sampled requests {sample}")
+    m = om.Model(shape, tw)
+    dr = odr.Drafter(shape, tw, dw, taps=taps)
+    ora = {}
+    for b in sample:
+        req, dreq = m.new_request(encs[b]), dr.new_request(encs[b])
+        lg, tp = m.rows(req, prefixes[b], 0, taps=set(taps))
+        dr.append_history(dreq, tp, 0)
+        assert_argmax_where_clear(anchors[b:b + 1], lg[-1:], what=f"b96 anchor {b}")
+        anchors[b] = od.argmax_lowest(lg[-1])
+        ora[b] = [req, dreq, int(lens[b])]
+    blk, dlg = _draft(eng, slots, anchors, K)
+    block = blk.copy()
+    for b in sample:
+        req, dreq, L = ora[b]
+        ref = dr.block(dreq, int(anchors[b]), L, K)
+        assert_logits_close(dlg[b], ref, what=f"b96 drafter req {b}")
+        assert_argmax_where_clear(blk[b, 1:], ref[1:], what=f"b96 drafts req {b}")
+        block[b] = [anchors[b]] + odr.draft_tokens(ref, K)
+    am = torch.empty((B, K + 1), dtype=torch.int32, device=eng.dev)
+    lg = torch.empty((B, K + 1, shape.vocab), dtype=torch.float32, device=eng.dev)
+    eng.wf_verify_block(eng.i32(slots), eng.i32(block), eng.i32(np.full(B, K + 1, np.int32)),
+                        am, lg)
+    am, lg = am.cpu().numpy(), lg.cpu().numpy()
+    keep = np.random.default_rng(12).integers(0, K + 1, B).astype(np.int32)
+    for b, a in zip(sample, [3, 0, 8]):
+        keep[b] = a
+    for b in sample:
+        req, dreq, L = ora[b]
+        ref, tp = m.rows(req, block[b], L, taps=set(taps))
+        assert_logits_close(lg[b], ref, what=f"b96 verify req {b}")
+        assert_argmax_where_clear(am[b], ref, what=f"b96 verify req {b}")
+        a = int(keep[b])
+        dr.append_history(dreq, {t: x[:a + 1] for t, x in tp.items()}, L)
+        ora[b] = [req, dreq, L + a + 1]
+        anchors[b] = od.argmax_lowest(ref[a])
+    for b in range(B):
+        if b not in ora:
+            anchors[b] = am[b, keep[b]]
+    eng.wf_rollback(eng.i32(slots), eng.i32(keep))
+    blk2, dlg2 = _draft(eng, slots, anchors, K)
+    for b in sample:
+        req, dreq, L = ora[b]
+        ref = dr.block(dreq, int(anchors[b]), L, K)
+        assert_logits_close(dlg2[b], ref, what=f"b96 drafter after the round, req {b}")
+        assert_argmax_where_clear(blk2[b, 1:], ref[1:], what=f"b96 drafts after the round {b}")
+    err, ln = eng.wf_device_state()
+    assert (err == 0).all()
+    assert (ln[:B] == lens + keep + 1).all()
     eng.close()

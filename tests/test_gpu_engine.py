@@ -235,6 +235,37 @@ def test_device_error_words(tiny):
     assert err[0] == 0 and err[1] == 0 and ln[0] == 0
 
 
+@pytest.mark.parametrize("persistent", [0, 1])
+def test_nan_logit_flags_the_slot(torch_cuda, persistent):
+    """A NaN in one row of the tied embedding (an id no input uses) makes
+    that logit NaN in every row: every active row's argmax is -1 and the
+    active requests' error words carry WF_DERR_NAN; the inactive request
+    keeps a clean word. On the multi-kernel path and on the persistent
+    pass (turbo width)."""
+    from speculative_decoding_encoder_amd.binding import WF_DERR_NAN, WF_OPT_PERSISTENT
+    wl = WORKLOADS[2]
+    shape = TURBO
+    wbits = dict(make_weights(shape, wl.cfg_id))
+    v_nan = 777
+    emb = wbits["tok_emb"].copy()
+    emb[v_nan, 5] = 0x7FC0                              # bf16 quiet NaN
+    wbits["tok_emb"] = emb
+    B = 3
+    encs = np.stack([make_encoder_out(shape, wl.cfg_id, r) for r in range(B)])
+    eng = _engine(shape, wbits, max_batch=B, max_rows=64)
+    eng.wf_set_option(WF_OPT_PERSISTENT, persistent)
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    toks = np.random.default_rng(4).integers(0, 700, (B, 9)).astype(np.int32)
+    n_tok = np.array([9, 0, 4], np.int32)
+    am, lg = _verify(eng, slots, toks, n_tok)
+    assert np.isnan(lg[0, :, v_nan]).all() and np.isnan(lg[2, :4, v_nan]).all()
+    assert (am == -1).all()
+    err, _ = eng.wf_device_state()
+    assert err[0] & WF_DERR_NAN and err[2] & WF_DERR_NAN and err[1] == 0, err[:B]
+    eng.close()
+
+
 # --------------------------------------------------------------------------
 # full 32-layer shape, batch 1, prefix 64, one block of 9
 def test_large_v3_b1_prefix64_block9(torch_cuda):
@@ -502,7 +533,7 @@ def test_turbo_b32_speculative_equals_greedy_on_gpu(torch_cuda):
     eng = _engine(shape, wbits, max_batch=B, max_rows=B * 224, page_table=perm.reshape(B, pps))
     slots = list(range(B))
     eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
-    n_max = 40
+    n_max = wl.n_max                                  # 200 tokens per request
     eng.wf_reset(eng.i32(slots))
     g = run_loop(eng, slots, prefixes, n_max, 0, None, shape.eos_id)
     fn = table_drafter(g.tokens, [len(p) for p in prefixes],

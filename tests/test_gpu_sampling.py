@@ -8,9 +8,10 @@
 * distribution preservation on the GPU itself (Whisper-Flash §3.1): over many
   Philox-keyed trials the first emitted token follows p (chi-square) and the
   first candidate is accepted with probability sum_v min(p_v, q_v);
-* one end-to-end round on the tiny model: GPU verify + sampling against the
-  oracle's own fp64 logits, compared where |log(u q / p)| exceeds the logit
-  error bound.
+* end-to-end rounds on the tiny model: GPU verify + sampling against the
+  oracle's own fp64 logits, compared where every decision holds for any
+  logits within the measured error (accept tests by |log(u q / p)|, the
+  final draw by bounds on the CDF); at least a third of the rounds count.
 """
 import dataclasses
 
@@ -154,7 +155,39 @@ def test_sampling_preserves_target_distribution_on_gpu(torch_cuda):
     eng.close()
 
 
+def _draw_pinned(z, qrow, u, c, delta):
+    """Whether a draw with uniform u lands on id c for every logit vector
+    within delta of z entry by entry: bounds on the (residual) CDF at c - 1
+    and at c. With logits within delta, each probability lies within a
+    factor exp(2 delta / T) of p; the CDF through id j, A / (A + B) with A
+    the mass up to j and B the rest, is smallest with A low and B high."""
+    z = np.asarray(z, np.float64) / TEMP
+    e = np.exp(z - z.max())
+    p = e / e.sum()
+    f = np.exp(2 * delta / TEMP)
+    if qrow is None:
+        wlo, whi = p / f, p * f
+    else:
+        wlo, whi = np.maximum(p / f - qrow, 0), np.maximum(p * f - qrow, 0)
+        if wlo.sum() <= 0:
+            return False           # the residual may vanish: no bound
+    def bounds(j):
+        le_lo, le_hi = wlo[:j + 1].sum(), whi[:j + 1].sum()
+        gt_lo, gt_hi = wlo[j + 1:].sum(), whi[j + 1:].sum()
+        return le_lo / (le_lo + gt_hi), le_hi / (le_hi + gt_lo)
+    ok = u < bounds(c)[0]
+    if c > 0:
+        ok = ok and u > bounds(c - 1)[1]
+    return bool(ok)
+
+
 def test_sampling_round_tiny_model_against_oracle(torch_cuda):
+    """Rounds of GPU verify + GPU rejection sampling against the oracle's
+    fp64 logits and rule. A round is compared when every decision the
+    oracle took holds for any logits within the measured GPU error delta:
+    the accept tests by |log(u q / p)| > 2 delta / T, the final draw by the
+    CDF bounds of _draw_pinned. At least a third of the rounds must be
+    compared."""
     from oracle import model as om
     from speculative_decoding_encoder_amd.binding import Engine
     wl = WORKLOADS[0]
@@ -168,9 +201,11 @@ def test_sampling_round_tiny_model_against_oracle(torch_cuda):
     eng.wf_encode_kv(eng.i32([0]), eng.bf16(enc[None]))
     K = 4
     T = K + 1
+    rounds = 24
     g = np.random.default_rng(43)
     checked = 0
-    for rnd in range(12):
+    deltas = []
+    for rnd in range(rounds):
         eng.wf_reset(eng.i32([0]))
         req = m.new_request(enc)
         m.rows(req, prefix, 0)
@@ -190,28 +225,29 @@ def test_sampling_round_tiny_model_against_oracle(torch_cuda):
                       q=d_q, temperature=TEMP, seed=7, request_id=eng.i32([0]),
                       step=eng.i32([rnd]))
         a_gpu, c_gpu = int(outs[0].item()), int(outs[1].item())
-        ref = m.rows(req, block, P).astype(np.float32)
-        delta = float(np.abs(lg.cpu().numpy()[0] - ref).max())
+        ref64 = m.rows(req, block, P)
+        ref = ref64.astype(np.float32)
+        # the GPU's logit error, plus slack for its own fp32 softmax rounding
+        delta = float(np.abs(lg.cpu().numpy()[0] - ref64).max()) + 1e-6
+        deltas.append(delta)
         u_acc = [ph.uniform(7, 0, rnd, i, ph.STREAM_ACCEPT) for i in range(K)]
         u_res = [ph.uniform(7, 0, rnd, i, ph.STREAM_RESAMPLE) for i in range(K + 1)]
         pk = np.stack([osmp.probs(ref[i], TEMP) for i in range(T)])
         a, em, c, dn = osmp.rejection_round(pk, qz.astype(np.float32), drafts, u_acc, u_res,
                                             eos=TINY.eos_id, budget=50)
-        # every accept decision up to a must clear 2*delta/T in log space, and
-        # the final draw must sit away from a CDF boundary by the induced error
         pinned = True
         for i in range(min(a + 1, K)):
             y = drafts[i]
             r = np.log(max(u_acc[i] * qz[i][y], 1e-30) / max(pk[i][y], 1e-30))
             if abs(r) <= 2 * delta / TEMP:
                 pinned = False
-        w = np.maximum(pk[a] - qz[a], 0) if a < K else pk[a]
-        cum = np.cumsum(w.astype(np.float64)) / max(w.sum(), 1e-30)
-        eps = np.exp(2 * delta / TEMP) - 1
-        if np.min(np.abs(cum - u_res[a])) <= eps:
+        if c is not None and not _draw_pinned(ref64[a], qz[a] if a < K else None, u_res[a], c,
+                                              delta):
             pinned = False
         if pinned:
             checked += 1
             assert (a_gpu, c_gpu) == (a, c), (rnd, a_gpu, c_gpu, a, c, delta)
-    log(f"tiny sampling rounds: {checked}/12 pinned and identical")
+    log(f"tiny sampling rounds: {checked}/{rounds} pinned and identical, max logit error "
+        f"{max(deltas):.2e}")
+    assert checked >= rounds // 3, (checked, max(deltas))
     eng.close()
