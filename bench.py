@@ -56,6 +56,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
+from speculative_decoding_encoder_amd.prof_summary import (  # noqa: E402
+    is_encoder_workload, kernel_source_hash)
+
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 TOKENS_PER_AUDIO_S = 3.5
 METRIC = "verified tokens/sec & audio-s/sec at batch 1/32/96, K=8; % HBM roofline"
@@ -75,6 +78,29 @@ KIND_SYMBOL = {
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+class Window:
+    """With --mark-timed, the host clock (CLOCK_MONOTONIC, ns; the clock of
+    rocprofv3's kernel timestamps) at the start and the end of the timed
+    replays of each workload's fixed-block pass (and of the calibration
+    copies), printed to stderr, so that a kernel trace or a counter run can
+    be cut to the steady-state dispatches (prof_summary --window)."""
+
+    def __init__(self, on: bool = False):
+        self.on = on
+        self.t0 = 0
+
+    def start(self):
+        if self.on:
+            self.t0 = time.monotonic_ns()
+
+    def end(self, what: str):
+        if self.on:
+            log(f"[bench] timed-window {what} {self.t0} {time.monotonic_ns()}")
+
+
+WINDOW = Window(False)
 
 
 class Workload:
@@ -608,6 +634,7 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
             graph.replay()
     torch.cuda.synchronize()
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    WINDOW.start()
     t0 = time.perf_counter()
     evs[0].record()
     for i in range(K):
@@ -618,6 +645,7 @@ def measure(w: "Workload", K: int, W: int, use_graph: bool = True) -> dict:
         evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    WINDOW.end(w.name)
     ms_step = (t1 - t0) * 1e3 / K
     per_step = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(K)])
     n_acc2 = w.outs[0].cpu().numpy()
@@ -740,33 +768,6 @@ def traffic_of(workload: str, symbol_kind: str):
                 and ent.get("source_hash") == h:
             return float(ent["hbm_bytes_per_launch"])
     return None
-
-
-ENCODER_SOURCES = ("encoder.hip", "wf_device.h")
-
-
-def kernel_source_hash(workload: str = "") -> str:
-    """sha256 over the kernel sources of a workload, in name order: the
-    encoder's (encoder.hip and the device helpers) for an encoder workload,
-    every other csrc/*.hip and csrc/*.h for the verify path."""
-    import hashlib
-    csrc = os.path.join(ROOT, "speculative_decoding_encoder_amd", "csrc")
-    enc = is_encoder_workload(workload)
-    hsh = hashlib.sha256()
-    for name in sorted(os.listdir(csrc)):
-        if not name.endswith((".hip", ".h")):
-            continue
-        if enc and name not in ENCODER_SOURCES:
-            continue
-        if not enc and name == "encoder.hip":
-            continue
-        with open(os.path.join(csrc, name), "rb") as f:
-            hsh.update(name.encode() + b"\0" + f.read())
-    return hsh.hexdigest()[:16]
-
-
-def is_encoder_workload(workload: str) -> bool:
-    return "encoder" in workload
 
 
 def expected_tau(p: float, K: int) -> float:
@@ -1031,7 +1032,12 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run device-to-device copies of this size (calibrates "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE against known bytes)")
+    ap.add_argument("--mark-timed", action="store_true",
+                    help="print the host-clock window of each workload's timed fixed-block "
+                         "replays (and of the calibration copies) for cutting a rocprofv3 trace")
     args = ap.parse_args()
+    global WINDOW
+    WINDOW = Window(args.mark_timed)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the verify path is built and measured on a "
               "single MI355X (requests would shard by data parallelism, with no exchange "
@@ -1075,9 +1081,12 @@ def main():
                 nb = args.calib_copy_mib << 20
                 src = torch.ones(nb, dtype=torch.uint8, device=w.eng.dev)
                 dst = torch.empty_like(src)
+                torch.cuda.synchronize()
+                WINDOW.start()
                 for _ in range(3):
                     dst.copy_(src)
                 torch.cuda.synchronize()
+                WINDOW.end("calibration-copy")
                 ent["calib_copy_bytes"] = nb
                 del src, dst
         if not args.no_cpu and (n == 0 or cfg in (2, 3) or w.sampling):

@@ -186,7 +186,8 @@ class Engine:
                  max_rows: int, page_table: Optional[np.ndarray] = None,
                  n_pages: Optional[int] = None,
                  drafter_bits: Optional[Dict[str, np.ndarray]] = None,
-                 taps: Sequence[int] = (), static_workspace: bool = False):
+                 taps: Sequence[int] = (), static_workspace: bool = False,
+                 share_weights: Optional["Engine"] = None):
         import torch
         self.torch = torch
         self.lib = load()
@@ -198,9 +199,13 @@ class Engine:
         self.cfg = make_config(shape, max_batch, max_rows, n_pages, n_dl, taps)
         pps = shape.n_ctx // 16
         self.w = {}
-        for k, v in list(weights_bits.items()) + list((drafter_bits or {}).items()):
-            t = torch.from_numpy(np.ascontiguousarray(v).view(np.int16))
-            self.w[k] = t.to(self.dev).view(torch.bfloat16)
+        if share_weights is not None:
+            # the same device weights as another engine (one copy in HBM)
+            self.w = share_weights.w
+        else:
+            for k, v in list(weights_bits.items()) + list((drafter_bits or {}).items()):
+                t = torch.from_numpy(np.ascontiguousarray(v).view(np.int16))
+                self.w[k] = t.to(self.dev).view(torch.bfloat16)
         lw = (LayerWeights * shape.n_layers)()
         for l in range(shape.n_layers):
             for f in LAYER_FIELDS:
