@@ -114,9 +114,10 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     LnRow lrow;
     const int ln_rows = min(16, a.M - m_base);
     if constexpr (LNX) {
-        if (4 * wave < ln_rows)
-            ln_load16(a.lnx + (size_t)(m_base + min(4 * wave + g, ln_rows - 1)) * a.K, a.K, r16,
-                      lrow);
+        // unconditional (rows past the block repeat its last row), so that
+        // the statistics wait for these loads only
+        ln_load16(a.lnx + (size_t)(m_base + min(4 * wave + g, ln_rows - 1)) * a.K, a.K, r16,
+                  lrow);
     }
     // sched_barrier(0) pins the issue order (the scheduler would otherwise
     // sink the ring's loads next to their MFMAs to save registers)
@@ -127,8 +128,17 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
     float ln_mean = 0.f, ln_rstd = 0.f;
     if constexpr (LNX) {
         __shared__ float lnst[16][2];
-        for (int r = 4 * wave + g; r < ln_rows; r += 4 * W) {
-            if (r >= 4 * W) ln_load16(a.lnx + (size_t)(m_base + r) * a.K, a.K, r16, lrow);
+        {
+            const int r = 4 * wave + g;
+            float mean, rstd;
+            ln_reduce16(lrow, a.K, r16, a.ln_eps, mean, rstd);
+            if (r16 == 0 && r < ln_rows) {
+                lnst[r][0] = mean;
+                lnst[r][1] = rstd;
+            }
+        }
+        for (int r = 4 * wave + g + 4 * W; r < ln_rows; r += 4 * W) {   // fewer than 4 waves
+            ln_load16(a.lnx + (size_t)(m_base + r) * a.K, a.K, r16, lrow);
             float mean, rstd;
             ln_reduce16(lrow, a.K, r16, a.ln_eps, mean, rstd);
             if (r16 == 0) {
@@ -136,7 +146,10 @@ __global__ __launch_bounds__(512) void gemm_rk_kernel(GemmArgs a) {
                 lnst[r][1] = rstd;
             }
         }
-        __syncthreads();
+        // LDS-only barrier: the ring's loads stay in flight
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
         const int rr = min(r16, ln_rows - 1);
         ln_mean = lnst[rr][0];
         ln_rstd = lnst[rr][1];

@@ -284,26 +284,27 @@ __device__ __forceinline__ void ln_load16(const float *xrow, int d, int r16, LnR
 }
 __device__ __forceinline__ void ln_reduce16(const LnRow &row, int d, int r16, float eps,
                                             float &mean, float &rstd) {
+    // groups past the row add nothing (selects, not branches: the compiler
+    // then waits only for this row's loads, not for every load in flight)
     const int ng = d >> 3;
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_GPL; ++i) {
-        if (r16 + 16 * i < ng) {
-            const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
-            s += ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
-        }
+        const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
+        const float t = ((v0.x + v0.y) + (v0.z + v0.w)) + ((v1.x + v1.y) + (v1.z + v1.w));
+        s = r16 + 16 * i < ng ? s + t : s;
     }
     mean = sum16(s) / (float)d;
     float q = 0.f;
 #pragma unroll
     for (int i = 0; i < LN_GPL; ++i) {
-        if (r16 + 16 * i < ng) {
-            const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
-            const float t[8] = {v0.x - mean, v0.y - mean, v0.z - mean, v0.w - mean,
-                                v1.x - mean, v1.y - mean, v1.z - mean, v1.w - mean};
+        const float4 v0 = row.v[2 * i], v1 = row.v[2 * i + 1];
+        const float t[8] = {v0.x - mean, v0.y - mean, v0.z - mean, v0.w - mean,
+                            v1.x - mean, v1.y - mean, v1.z - mean, v1.w - mean};
+        float qi = q;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) q = __fmaf_rn(t[j], t[j], q);
-        }
+        for (int j = 0; j < 8; ++j) qi = __fmaf_rn(t[j], t[j], qi);
+        q = r16 + 16 * i < ng ? qi : q;
     }
     const float var = sum16(q) / (float)d;
     rstd = 1.0f / sqrtf(var + eps);
