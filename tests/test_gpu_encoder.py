@@ -10,9 +10,10 @@
   request alone, bit for bit: no kernel mixes requests, and the smaller
   GEMM tiles a lone window's d-wide projections take do not change any
   element's arithmetic).
-* The full 32-block encoder: finite outputs whose rows have mean 0 and
-  variance 1 (the final norm with unit gain), and the audio memory it
-  produces drives wf_encode_kv and a verify pass.
+* The full 32-block encoder: one window against the oracle's 32-block
+  forward (fp32), finite outputs whose rows have mean 0 and variance 1 (the
+  final norm with unit gain), and the audio memory it produces drives
+  wf_encode_kv and a verify pass.
 
 Tolerance. The GPU keeps the residual stream, norms, softmax and GELU in
 fp32 but hands bf16 activations between kernels (norm outputs, q, k, v,
@@ -125,6 +126,31 @@ def test_full_encoder_feeds_the_decoder(torch_cuda):
     assert (err == 0).all() and (am.cpu().numpy()[0, :len(prefixes[0])] >= 0).all()
     eng.close()
     enc.close()
+
+
+def test_full_32_block_encoder_against_the_oracle(torch_cuda):
+    """One 30 s window through the whole 32-block large-v3 encoder, against
+    the oracle's forward of every block. The oracle runs in fp32 here (its
+    fp32 and fp64 forwards differ by about 3e-6 over two blocks, far below
+    the GPU's bf16 hand-offs), so that 32 blocks take seconds on the host.
+    Tolerance: the roundings of every block add up in the fp32 residual
+    stream, which the final norm rescales; as independent errors they would
+    grow the two-block bound of the module docstring (5e-2 max, 5e-3 rms)
+    by at most the square root of 32 / 2 = 4. The test allows twice the
+    two-block bound: 0.1 max and 1e-2 rms."""
+    from speculative_decoding_encoder_amd.binding import Encoder
+    s = ENC_LARGE_V3
+    wb = make_encoder_weights(s, 2)
+    enc = Encoder(s, wb, max_batch=1)
+    mel = make_mel(s, 2, 0)
+    got = _encode(torch_cuda, enc, [mel])[0]
+    enc.close()
+    log("full encoder: oracle forward (32 blocks, fp32)")
+    ref = oe.Encoder(s, wb, dtype=np.float32).forward(mel).astype(np.float64)
+    err = np.abs(got.astype(np.float64) - ref)
+    mx, rms = float(err.max()), float(np.sqrt((err ** 2).mean()))
+    log(f"[parity] 32-block encoder: max {mx:.3e} rms {rms:.3e}")
+    assert mx <= 2 * ENC_MAX_TOL and rms <= 2 * ENC_RMS_TOL, (mx, rms)
 
 
 def test_graph_replays_equal_the_eager_encode(torch_cuda):
