@@ -10,7 +10,12 @@ parity is unpinned beyond them:
 * the history built round by round from the accepted rows' taps equals the
   history built from one full recompute of the target;
 * the drafter's one-softmax attention over [history; block] equals torch's
-  scaled_dot_product_attention with no mask.
+  scaled_dot_product_attention with no mask;
+* structure: attention inside the block is bidirectional (a mask row
+  changes when a later row is added), the block reads the audio memory
+  (another request's audio changes every row, the same audio gives the same
+  bits) and the history below the anchor (a perturbed accepted row changes
+  every block row; rows at or past the anchor are never read).
 """
 import numpy as np
 import pytest
@@ -122,3 +127,57 @@ def test_draft_rows_predict_their_own_positions(tiny_pair):
     assert np.abs(out[1] - out[2]).max() > 1e-6       # positions differ
     d = odr.draft_tokens(out, 8)
     assert len(d) == 8 and all(0 <= x < TINY.vocab for x in d)
+
+
+def _primed(m, dr, enc, prefix):
+    req, dreq = m.new_request(enc), dr.new_request(enc)
+    lg, taps = m.rows(req, prefix, 0, taps=set(TINY_TAPS))
+    dr.append_history(dreq, taps, 0)
+    return dreq
+
+
+def test_block_attention_is_bidirectional(tiny_pair):
+    """Mask rows see the rows after them (WF eq. 2: one softmax over the
+    history and the whole block): row 1 changes when a third row is added
+    to the block. Under a causal mask inside the block it could not."""
+    m, dr, enc, prefix = tiny_pair
+    dreq = _primed(m, dr, enc, prefix)
+    L = len(prefix)
+    k1 = dr.block(dreq, 7, L, 1)
+    k2 = dr.block(dreq, 7, L, 2)
+    assert np.abs(k1[1] - k2[1]).max() > 1e-6
+    assert np.abs(k1[0] - k2[0]).max() > 1e-6          # the anchor row sees the mask rows too
+
+
+def test_block_reads_the_audio_through_cross_attention(tiny_pair):
+    """Same history, same block, another request's audio memory: every row
+    changes (the drafter cross-attends with its own acoustic K/V); the same
+    audio gives the same rows exactly."""
+    m, dr, enc, prefix = tiny_pair
+    dreq = _primed(m, dr, enc, prefix)
+    L = len(prefix)
+    other = dr.new_request(make_encoder_out(TINY, WORKLOADS[0].cfg_id, 1))
+    other.h[:L] = dreq.h[:L]
+    a = dr.block(dreq, 7, L, 4)
+    b = dr.block(other, 7, L, 4)
+    same = dr.new_request(enc)
+    same.h[:L] = dreq.h[:L]
+    c = dr.block(same, 7, L, 4)
+    assert (np.abs(a - b).max(axis=1) > 1e-6).all()
+    np.testing.assert_array_equal(a, c)
+
+
+def test_block_reads_the_history(tiny_pair):
+    """Changing one accepted position's history row changes every block row
+    (history keys and values enter each layer's softmax); history rows at
+    or beyond L are never read."""
+    m, dr, enc, prefix = tiny_pair
+    dreq = _primed(m, dr, enc, prefix)
+    L = len(prefix)
+    a = dr.block(dreq, 7, L, 4)
+    dreq.h[L:L + 8] = 123.0                             # past the history: ignored
+    np.testing.assert_array_equal(a, dr.block(dreq, 7, L, 4))
+    # (not a constant shift: the history goes through a layer norm)
+    dreq.h[1] += 0.5 * np.random.default_rng(9).standard_normal(dreq.h.shape[1])
+    b = dr.block(dreq, 7, L, 4)
+    assert (np.abs(a - b).max(axis=1) > 1e-6).all()
