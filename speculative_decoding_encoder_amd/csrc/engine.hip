@@ -322,19 +322,25 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
         !fuse_ln) {
         // tall blocks (tens of requests), 64-column tiles (from a sweep on
         // MI355X): the wide projections (QKV, fc1, the LM head, the
-        // drafter's QKV and history K/V) 96 or 128 rows over the whole of K; the d-wide ones (O, O_c, cross Q) 96 rows
-        // from 576 rows on (below, the register-tiled kernel's 64 x 32 tiles
-        // win); fc2 (K = 5120) 96 rows in 4 K groups
+        // drafter's QKV and history K/V) 96 or 128 rows over the whole of K,
+        // or 64 rows at two workgroups per CU when that gives more than 512
+        // tiles; the d-wide ones (O, O_c, cross Q) 96 rows from 576 rows on
+        // (below, the register-tiled kernel's 64 x 32 tiles win); fc2 (K =
+        // 5120) 96 rows in 4 K groups
         int mbt = 6, P = 1;
         bool take = true;
         if (role == ROLE_QKV || role == ROLE_FC1 || role == ROLE_LM_HEAD ||
             role == ROLE_DRAFT_QKV || role == ROLE_HIST_KV) {
             // 96 or 128 rows: the fewer rounds of 256 workgroups times the
             // rows per workgroup (measured: 864 x 3840 128 rows 31.9 vs 39.5 us,
-            // 864 x 5120 96 rows 43.2 vs 45.3 us)
+            // 864 x 5120 96 rows 43.2 vs 45.3 us); 64 rows two per CU
+            // (measured: the LM head 288 x 51866 122 vs 155 us, 864 x 51866
+            // 312 vs 417 us, 864 x 3840 30.7 us, 864 x 5120 38.4 vs 42.6 us;
+            // at 288 x 3840 17.9 against 15.7 us with 96 rows)
             const int c6 = cdiv(cdiv(N, 64) * cdiv(M, 96), 256) * 6;
             const int c8 = cdiv(cdiv(N, 64) * cdiv(M, 128), 256) * 8;
             mbt = c8 < c6 ? 8 : 6;
+            if (cdiv(N, 64) * cdiv(M, 64) > 512) mbt = 4;
         }
         else if (role == ROLE_OPROJ || role == ROLE_CROSS_Q) take = M >= 576;
         else P = 4;

@@ -63,8 +63,11 @@ struct ChunkStack {
     }
 };
 
-template <int ROLE, int MB, int NW, int CPG, int CK, int D = 5>
-__global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
+// OCC: workgroups per CU the registers are budgeted for. Two co-resident
+// workgroups hide each other's barrier and load waits; it pays once a launch
+// has more than a CU's worth of tiles per CU.
+template <int ROLE, int MB, int NW, int CPG, int CK, int D = 5, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void gemm_tl_kernel(GemmArgs a) {
     constexpr int EPI = epi_of(ROLE);
     constexpr int NT = MB * NW;                    // accumulator tiles per wave
     // D: ring depth (k-steps ahead); the k-step loop is unrolled by L, a
@@ -281,8 +284,16 @@ __global__ __launch_bounds__(256, 1) void gemm_tl_kernel(GemmArgs a) {
 }
 
 // The verify-pass instances. K = 1280 (5 k-steps per chunk): 96 x 64 tiles
-// (mb 6) or 128 x 64 (mb 8) over the whole of K. K = 5120 (fc2, 20 k-steps
-// per chunk): 96 x 64 tiles in 4 K groups of 2 chunks.
+// (mb 6) or 128 x 64 (mb 8) over the whole of K, and for the wide
+// projections with many tiles 64 x 64 (mb 4) at two workgroups per CU. K =
+// 5120 (fc2, 20 k-steps per chunk): 96 x 64 tiles in 4 K groups of 2
+// chunks, two workgroups per CU.
+template <int ROLE>
+constexpr bool tl_has_mb4() {
+    return ROLE == ROLE_QKV || ROLE == ROLE_FC1 || ROLE == ROLE_LM_HEAD || ROLE == ROLE_DRAFT_QKV ||
+           ROLE == ROLE_HIST_KV;
+}
+
 template <int ROLE>
 hipError_t launch_tl(const GemmArgs &a, int mb, hipStream_t st) {
     if (a.S != 8) return hipErrorInvalidValue;
@@ -292,8 +303,14 @@ hipError_t launch_tl(const GemmArgs &a, int mb, hipStream_t st) {
     else if (a.ck == 5 && a.n_groups == 1 && mb == 8)
         hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 8, 1, 8, 5>), dim3(grid), dim3(256), 0, st, a);
     else if (a.ck == 20 && a.n_groups == 4 && mb == 6)
-        hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 2, 20, 4>), dim3(grid), dim3(256), 0, st, a);
-    else
+        hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 6, 1, 2, 20, 4, 2>), dim3(grid), dim3(256), 0, st, a);
+    else if constexpr (tl_has_mb4<ROLE>()) {
+        if (a.ck == 5 && a.n_groups == 1 && mb == 4)
+            hipLaunchKernelGGL((gemm_tl_kernel<ROLE, 4, 1, 8, 5, 5, 2>), dim3(grid), dim3(256), 0, st,
+                               a);
+        else
+            return hipErrorInvalidValue;
+    } else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
