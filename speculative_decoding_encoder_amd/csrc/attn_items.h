@@ -246,8 +246,13 @@ __device__ __forceinline__ void self_attn_item(const SelfAttnArgs &a, int bh, in
     st.init();
     const float sl2e = a.scale * 1.4426950408889634f;
     const int qrow = row0 + r16;
+    // the request's length and slot and this tile's queries go out together
+    // with n_tok (in bounds for any request of the batch), so the chain to
+    // the first K/V load is the page table only
+    const int L = a.req_L[b];
+    const int slot = a.slots[b];
+    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
     if (live) {
-        const int L = a.req_L[b];
         // last key any row of this tile may see (the whole block when not causal)
         const int kmax = a.causal ? L + min(row0 + 15, ntok - 1) : L + ntok - 1;
         // this lane's row r16 sees keys <= lim; keys below mask_from every row sees
@@ -257,10 +262,8 @@ __device__ __forceinline__ void self_attn_item(const SelfAttnArgs &a, int bh, in
         const int mask_from = TREE ? L + 1 : (a.causal ? L + min(row0, ntok - 1) : kmax) + 1;
         const int last_page = kmax >> 4;   // pages past this one were never validated
         // the request's page ids, one per lane (at most 64 pages)
-        const int32_t *pt = a.page_table + (size_t)a.slots[b] * a.pt_stride;
+        const int32_t *pt = a.page_table + (size_t)slot * a.pt_stride;
         const int ptl = lane <= last_page ? pt[lane] : 0;
-        const QFrag<HD> q =
-            load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
         const uint64_t anc = TREE ? a.anc[(size_t)b * a.T + min(qrow, a.T - 1)] : ~0ull;
 
         const uint16_t *kvl = a.kv_layer;
@@ -347,12 +350,14 @@ __device__ __forceinline__ bool cross_attn_item(const CrossAttnArgs &a, int item
 
     SmRow<NDT> st;
     st.init();
+    // the slot and this tile's queries go out together with n_tok (in bounds
+    // for any request of the batch)
+    const int slot = a.slots[b];
+    const QFrag<HD> q = load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
     if (live) {
-        const uint16_t *base = a.xkv + (size_t)a.slots[b] * a.slot_stride + a.layer_off;
+        const uint16_t *base = a.xkv + (size_t)slot * a.slot_stride + a.layer_off;
         const uint16_t *kh = base + (size_t)h * a.F_pad * HD;
         const uint16_t *vh = base + (size_t)a.H * a.F_pad * HD + (size_t)h * a.F_pad * HD;
-        const QFrag<HD> q =
-            load_q<HD>(a.q + (size_t)(b * a.T + qrow) * a.d + h * HD, qrow < a.T, g);
 
         const int c0 = (grp * 4 + w4) * a.cf;          // first frame of this wave's chunk
         const int c1 = min(c0 + a.cf, a.F);            // end of its live frames

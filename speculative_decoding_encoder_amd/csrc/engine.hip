@@ -367,10 +367,18 @@ wf_status run_gemm(wf_engine *e, int kind, int role, const uint16_t *X, int M,
         };
         if (mt_need <= 1) {
             // with the layer-norm prologue every workgroup recomputes the row
-            // statistics: wide projections take 64-column tiles
+            // statistics: wide projections take 64-column tiles. K groups
+            // (from sweeps at 9 rows on MI355X, weights from HBM): O and O_c
+            // run unsplit (4.9 against 5.4 us in 2 groups), fc2 (K = 5120) in
+            // 4 (7.9 against 8.2 in 2 and 10.7 unsplit), the layer-norm
+            // consumers below 128 tiles in 2 (cross-Q unsplit: 9.1 against
+            // 8.1 us in the pass)
             mb = 1;
             nb = (role == ROLE_LM_HEAD || (fuse_ln && N >= 4096)) ? 4 : 1;
-            if (split_k_ok && S >= 2 && cdiv(N, 16 * nb) < 128 && fits(2)) P = 2;
+            if (split_k_ok && S >= 2) {
+                if (K >= 4096 && S >= 4 && fits(4)) P = 4;
+                else if (fuse_ln && cdiv(N, 16 * nb) < 128 && fits(2)) P = 2;
+            }
         } else if (mt_need <= 8) {
             // a few requests (2 to 8 row tiles): one-row-tile blocks of 16
             // columns up to 3 row tiles, then 32 x 32 tiles in 2 K groups
