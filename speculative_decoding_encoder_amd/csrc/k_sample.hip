@@ -14,9 +14,10 @@
 // (seed, 0) and counter (request, step, position, stream): the top 24 bits
 // of the first output word times 2^-24, exact in fp32.
 //
-// One 1024-thread workgroup per request walks the candidate rows in order;
-// row statistics (max, sum of exp) and the residual's segment sums are block
-// reductions in a fixed order.
+// The row statistics (max, sum of exp) of every row come first, one
+// 1024-thread workgroup per row; then one 1024-thread workgroup per request
+// walks the candidate rows in order. Row statistics and the residual's
+// segment sums are block reductions in a fixed order.
 #include "wf_device.h"
 #include "wf_internal.h"
 #include "../../include/wf.h"
@@ -99,24 +100,71 @@ __device__ __forceinline__ float zval(const float *row, int v, float T, const ui
     if (sup && sup[v]) return -INFINITY;
     return row[v] / T;
 }
+__device__ __forceinline__ float zof(float x, bool suppressed, float T) {
+    return suppressed ? -INFINITY : x / T;
+}
+
+// Walk thread t's elements v = t, t + NT, t + 2 NT, ... of a row in
+// ascending order, calling f(v, z) with z = zval of element v (and qv, the
+// draft probability, when qrow is given). The loads of a run of U elements
+// go out together before any is used, so the walk waits for memory once per
+// run instead of once per element; the arithmetic order is unchanged.
+constexpr int kRun = 16;
+template <typename F>
+__device__ __forceinline__ void walk_strided(const float *row, const float *qrow, int V, float T,
+                                             const uint8_t *sup, F f) {
+    for (int v0 = threadIdx.x; v0 < V; v0 += NT * kRun) {
+        float x[kRun], q[kRun];
+        bool sp[kRun];
+#pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            const int v = min(v0 + NT * u, V - 1);
+            x[u] = row[v];
+            q[u] = qrow ? qrow[v] : 0.f;
+            sp[u] = sup ? sup[v] != 0 : false;
+        }
+#pragma unroll
+        for (int u = 0; u < kRun; ++u)
+            if (v0 + NT * u < V) f(v0 + NT * u, zof(x[u], sp[u], T), q[u]);
+    }
+}
+// The same over a contiguous range [v0, v1), ascending.
+template <typename F>
+__device__ __forceinline__ void walk_range(const float *row, const float *qrow, int v0, int v1,
+                                           float T, const uint8_t *sup, F f) {
+    for (int b = v0; b < v1; b += kRun) {
+        float x[kRun], q[kRun];
+        bool sp[kRun];
+#pragma unroll
+        for (int u = 0; u < kRun; ++u) {
+            const int v = min(b + u, v1 - 1);
+            x[u] = row[v];
+            q[u] = qrow ? qrow[v] : 0.f;
+            sp[u] = sup ? sup[v] != 0 : false;
+        }
+#pragma unroll
+        for (int u = 0; u < kRun; ++u)
+            if (b + u < v1) f(b + u, zof(x[u], sp[u], T), q[u]);
+    }
+}
 
 __device__ RowStats row_stats(const float *row, int V, float T, const uint8_t *sup, float *sh) {
     float m = -INFINITY;
-    for (int v = threadIdx.x; v < V; v += NT) m = fmaxf(m, zval(row, v, T, sup));
+    walk_strided(row, nullptr, V, T, sup, [&](int, float z, float) { m = fmaxf(m, z); });
     m = block_max(m, sh);
     float s = 0.f;
-    for (int v = threadIdx.x; v < V; v += NT) {
-        const float z = zval(row, v, T, sup);
-        s += (z == -INFINITY) ? 0.f : expf(z - m);
-    }
+    walk_strided(row, nullptr, V, T, sup,
+                 [&](int, float z, float) { s += (z == -INFINITY) ? 0.f : expf(z - m); });
     s = block_sum(s, sh);
     return RowStats{m, s};
 }
 
+__device__ __forceinline__ float prob_z(float z, const RowStats &st) {
+    return (z == -INFINITY) ? 0.f : expf(z - st.m) / st.s;
+}
 __device__ __forceinline__ float prob(const float *row, int v, float T, const uint8_t *sup,
                                       const RowStats &st) {
-    const float z = zval(row, v, T, sup);
-    return (z == -INFINITY) ? 0.f : expf(z - st.m) / st.s;
+    return prob_z(zval(row, v, T, sup), st);
 }
 
 // Inverse CDF in ascending id order over weights w_v (p_v, or (p_v - q_v)+):
@@ -128,13 +176,17 @@ __device__ int icdf(const float *row, const float *qrow, int V, float T, const u
     const int seglen = (V + NT - 1) / NT;
     const int v0 = threadIdx.x * seglen;
     const int v1 = min(v0 + seglen, V);
-    auto weight = [&](int v) -> float {
-        const float p = prob(row, v, T, sup, st);
-        if constexpr (RESID) return fmaxf(p - qrow[v], 0.f);
+    auto weight_z = [&](float z, float qv) -> float {
+        const float p = prob_z(z, st);
+        if constexpr (RESID) return fmaxf(p - qv, 0.f);
         return p;
     };
+    auto weight = [&](int v) -> float {
+        return weight_z(zval(row, v, T, sup), RESID ? qrow[v] : 0.f);
+    };
+    const float *qr = RESID ? qrow : nullptr;
     float local = 0.f;
-    for (int v = v0; v < v1; ++v) local += weight(v);
+    walk_range(row, qr, v0, v1, T, sup, [&](int, float z, float qv) { local += weight_z(z, qv); });
     seg[threadIdx.x] = local;
     if (threadIdx.x == 0) *found = 0x7fffffff;
     __syncthreads();
@@ -152,13 +204,15 @@ __device__ int icdf(const float *row, const float *qrow, int V, float T, const u
     const float thr = u * total;
     float c = seg[threadIdx.x];
     if (c <= thr && v0 < v1) {
-        for (int v = v0; v < v1; ++v) {
-            c += weight(v);
+        bool hit = false;
+        walk_range(row, qr, v0, v1, T, sup, [&](int v, float z, float qv) {
+            if (hit) return;
+            c += weight_z(z, qv);
             if (c > thr) {
                 atomicMin(found, v);
-                break;
+                hit = true;
             }
-        }
+        });
     }
     __syncthreads();
     int r = *found;
@@ -178,6 +232,22 @@ __device__ int icdf(const float *row, const float *qrow, int V, float T, const u
 }
 
 }  // namespace
+
+// The softmax statistics (max, sum of exp) of every row a round may read
+// (rows 0 .. n_tok - 1 of each request), one workgroup per row, all rows at
+// once: the acceptance kernel then walks its candidates without reducing a
+// row. Same reduction code, so the same bits.
+__global__ __launch_bounds__(1024) void sample_row_stats_kernel(AcceptArgs a) {
+    __shared__ float sh[NT / 64 + 2];
+    const int b = blockIdx.x / a.T, i = blockIdx.x - b * a.T;
+    if (i >= a.n_tok[b]) return;
+    const float *row = a.logits + ((size_t)b * a.T + i) * a.V;
+    const RowStats st = row_stats(row, a.V, a.temperature, a.suppress, sh);
+    if (threadIdx.x == 0) {
+        a.stats[2 * ((size_t)b * a.T + i)] = st.m;
+        a.stats[2 * ((size_t)b * a.T + i) + 1] = st.s;
+    }
+}
 
 __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
     __shared__ float sh[NT / 64 + 2];
@@ -204,7 +274,9 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
             for (int i = 0; i < k && !stopped; ++i) {
                 const float *row = a.logits + ((size_t)b * a.T + i) * a.V;
                 const float *qrow = a.q + ((size_t)b * (a.T - 1) + i) * a.V;
-                const RowStats st = row_stats(row, a.V, T, a.suppress, sh);
+                const RowStats st = a.stats ? RowStats{a.stats[2 * ((size_t)b * a.T + i)],
+                                                       a.stats[2 * ((size_t)b * a.T + i) + 1]}
+                                            : row_stats(row, a.V, T, a.suppress, sh);
                 const int y = tok[i + 1];
                 const float py = prob(row, y, T, a.suppress, st);
                 const float qy = qrow[y];
@@ -221,8 +293,8 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
                 // first rejection: draw from (p - q)+, or p when that is all zero
                 const float ur = uniform24(a.seed, req, step, i, STREAM_RESAMPLE);
                 float rs = 0.f;
-                for (int v = threadIdx.x; v < a.V; v += NT)
-                    rs += fmaxf(prob(row, v, T, a.suppress, st) - qrow[v], 0.f);
+                walk_strided(row, qrow, a.V, T, a.suppress,
+                             [&](int, float z, float qv) { rs += fmaxf(prob_z(z, st) - qv, 0.f); });
                 rs = block_sum(rs, sh);
                 const int c = rs > 0.f
                     ? icdf<true>(row, qrow, a.V, T, a.suppress, st, ur, sh, seg, &found)
@@ -234,7 +306,9 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
             }
             if (!stopped) {                    // every candidate accepted: bonus from row k
                 const float *row = a.logits + ((size_t)b * a.T + k) * a.V;
-                const RowStats st = row_stats(row, a.V, T, a.suppress, sh);
+                const RowStats st = a.stats ? RowStats{a.stats[2 * ((size_t)b * a.T + k)],
+                                                       a.stats[2 * ((size_t)b * a.T + k) + 1]}
+                                            : row_stats(row, a.V, T, a.suppress, sh);
                 const float ub = uniform24(a.seed, req, step, k, STREAM_RESAMPLE);
                 const int c = icdf<false>(row, nullptr, a.V, T, a.suppress, st, ub, sh, seg, &found);
                 next = c;
@@ -253,6 +327,7 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
 }
 
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
+    if (a.stats) hipLaunchKernelGGL(sample_row_stats_kernel, dim3(a.n * a.T), dim3(NT), 0, st, a);
     hipLaunchKernelGGL(accept_sample_kernel, dim3(a.n), dim3(NT), 0, st, a);
     return hipGetLastError();
 }

@@ -138,6 +138,9 @@ struct AcceptArgs {
     float temperature;
     uint64_t seed;
     const int32_t *request_id, *step;
+    // scratch for the rows' softmax statistics, 2 floats per row [n][T]
+    // (nullable: then the acceptance kernel reduces each row itself)
+    float *stats;
 };
 
 struct RollbackArgs {
