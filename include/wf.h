@@ -330,6 +330,52 @@ wf_status wf_accept_tree(wf_engine *e, int32_t n, const int32_t *d_tokens, int32
 wf_status wf_rollback_tree(wf_engine *e, int32_t n, const int32_t *d_slots, const int32_t *d_path,
                            int32_t T, const int32_t *d_n_acc, void *stream);
 
+/* Device-resident bookkeeping of a running speculative loop (the loop of
+ * Whisper-Flash section 3.1: each round verifies the anchor and its
+ * candidates, emits the a accepted candidates and the next token, and the
+ * next token is the next round's anchor; appendix A.1 for the output budget
+ * and EOS). Keeping it on the device lets a caller capture a whole round
+ * (prepare, wf_draft or a table, wf_verify_block, wf_accept, wf_rollback,
+ * finish) once as a graph. Per request b (int32 [n] unless noted; the
+ * caller owns the buffers):
+ *   anchor   the next round's anchor token;
+ *   len      the slot's cache length (as wf_rollback leaves it);
+ *   emitted  tokens emitted so far, the first anchor included;
+ *   done     1 once the request has ended (EOS emitted or budget used up);
+ *   acc_sum, prop_sum  accepted and proposed candidates over the rounds;
+ *   rounds, step       rounds the request took part in (step also keys the
+ *                      sampling uniforms of wf_accept);
+ *   tok_sum  tokens the rounds emitted;
+ *   hist     int64 [K + 1], rounds per accepted length. */
+typedef struct wf_loop_state {
+    int32_t *anchor, *len, *emitted, *done;
+    int32_t *acc_sum, *prop_sum, *rounds, *step, *tok_sum;
+    int64_t *hist;
+} wf_loop_state;
+
+/* A round's inputs from the loop state, per request: R = n_max - emitted
+ * outputs left, k = max(0, min(K, R - 1, n_ctx - len - 1)) candidates (so
+ * that k <= R - 1 and the block fits the context), d_n_tok = k + 1, or 0
+ * once done; d_budget = max(R, 1). With d_table (int32 [n][table_cols], the
+ * candidate for each absolute position) the block d_block int32 [n][K + 1]
+ * is the anchor followed by table[b][min(len + i, table_cols - 1)] for
+ * i = 1..K; with d_table NULL only n_tok and the budget are written (the
+ * caller fills the block, e.g. with wf_draft). Requires 0 <= K, K + 1 <=
+ * n_ctx, n_max >= 1, table_cols >= 1 with a table; no state pointer NULL. */
+wf_status wf_loop_prepare(wf_engine *e, int32_t n, const wf_loop_state *s, int32_t K,
+                          int32_t n_max, const int32_t *d_table, int32_t table_cols,
+                          int32_t *d_block, int32_t *d_n_tok, int32_t *d_budget, void *stream);
+
+/* The state update after wf_accept and wf_rollback, per request active this
+ * round (d_n_tok > 0): len += a + 1; anchor = next_token when >= 0; emitted
+ * and tok_sum += n_emit; done = 1 when d_done; acc_sum += a; prop_sum +=
+ * n_tok - 1; rounds and step += 1; hist[min(max(a, 0), K)] += 1 (a =
+ * d_n_acc). Inactive requests are left unchanged. */
+wf_status wf_loop_finish(wf_engine *e, int32_t n, const wf_loop_state *s, int32_t K,
+                         const int32_t *d_n_tok, const int32_t *d_n_acc,
+                         const int32_t *d_next_token, const int32_t *d_n_emit,
+                         const int32_t *d_done, void *stream);
+
 /* Shorten the cache of n slots to d_len[b] positions (0 <= d_len[b] <= the
  * current length; the slot must not be pending), e.g. to verify the same
  * block again from the same state. A bad length sets WF_DERR_STATE. */

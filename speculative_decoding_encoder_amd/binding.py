@@ -56,6 +56,12 @@ class Weights(ctypes.Structure):
                 ("drafter", ctypes.POINTER(DrafterWeights))]
 
 
+class LoopState(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "anchor", "len", "emitted", "done", "acc_sum", "prop_sum", "rounds", "step", "tok_sum",
+        "hist")]
+
+
 class EncConfig(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "d_model", "n_heads", "head_dim", "d_ffn", "n_mels", "n_frames",
@@ -116,6 +122,9 @@ def load():
         "wf_rollback_tree": (I32, [P, I32, P, P, I32, P, P]),
         "wf_draft": (I32, [P, I32, P, P, I32, P, P, P]),
         "wf_truncate": (I32, [P, I32, P, P, P]),
+        "wf_loop_prepare": (I32, [P, I32, ctypes.POINTER(LoopState), I32, I32, P, I32, P, P, P,
+                                  P]),
+        "wf_loop_finish": (I32, [P, I32, ctypes.POINTER(LoopState), I32, P, P, P, P, P, P]),
         "wf_device_state": (I32, [P, P, P, P]),
         "wf_set_timing": (I32, [P, I32]),
         "wf_get_timing": (I32, [P, I32, ctypes.POINTER(ctypes.c_double),
@@ -314,6 +323,27 @@ class Engine:
     def wf_draft(self, slots, anchor, K, block, logits=None, stream=None):
         _check(self.lib.wf_draft(self.h, slots.numel(), _p(slots), _p(anchor), int(K), _p(block),
                                  _p(logits), _stream(stream)), "wf_draft")
+
+    @staticmethod
+    def loop_state(anchor, len, emitted, done, acc_sum, prop_sum, rounds, step, tok_sum,
+                   hist) -> LoopState:
+        """The device pointers of a running loop's state (torch tensors:
+        int32 [n] each, hist int64 [K + 1])."""
+        return LoopState(*[_p(t) for t in (anchor, len, emitted, done, acc_sum, prop_sum,
+                                             rounds, step, tok_sum, hist)])
+
+    def wf_loop_prepare(self, state: LoopState, n, K, n_max, table, block, n_tok, budget,
+                        stream=None):
+        cols = int(table.shape[1]) if table is not None else 0
+        _check(self.lib.wf_loop_prepare(self.h, int(n), ctypes.byref(state), int(K), int(n_max),
+                                        _p(table), cols, _p(block), _p(n_tok), _p(budget),
+                                        _stream(stream)), "wf_loop_prepare")
+
+    def wf_loop_finish(self, state: LoopState, n, K, n_tok, n_acc, next_token, n_emit, done,
+                       stream=None):
+        _check(self.lib.wf_loop_finish(self.h, int(n), ctypes.byref(state), int(K), _p(n_tok),
+                                       _p(n_acc), _p(next_token), _p(n_emit), _p(done),
+                                       _stream(stream)), "wf_loop_finish")
 
     def wf_truncate(self, slots, lens, stream=None):
         _check(self.lib.wf_truncate(self.h, slots.numel(), _p(slots), _p(lens),

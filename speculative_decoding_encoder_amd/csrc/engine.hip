@@ -1213,6 +1213,56 @@ wf_status wf_truncate(wf_engine *e, int32_t n, const int32_t *d_slots, const int
     return timed(e, TK_OTHER, st, [&] { return launch_truncate(a, st); });
 }
 
+static bool loop_state_ok(const wf_loop_state *s) {
+    return s && s->anchor && s->len && s->emitted && s->done && s->acc_sum && s->prop_sum &&
+           s->rounds && s->step && s->tok_sum && s->hist;
+}
+
+wf_status wf_loop_prepare(wf_engine *e, int32_t n, const wf_loop_state *s, int32_t K,
+                          int32_t n_max, const int32_t *d_table, int32_t table_cols,
+                          int32_t *d_block, int32_t *d_n_tok, int32_t *d_budget, void *stream) {
+    if (!e || !loop_state_ok(s) || !d_n_tok || !d_budget || (d_table && !d_block))
+        return fail(WF_EINVAL, "null argument");
+    if (n < 1) return fail(WF_EINVAL, "n < 1");
+    if (K < 0 || K + 1 > e->c.n_ctx) return fail(WF_EINVAL, "K outside [0, n_ctx - 1]");
+    if (n_max < 1) return fail(WF_EINVAL, "n_max < 1");
+    if (d_table && table_cols < 1) return fail(WF_EINVAL, "table_cols < 1");
+    LoopArgs a{};
+    a.n = n;
+    a.K = K;
+    a.n_max = n_max;
+    a.n_ctx = e->c.n_ctx;
+    a.table_cols = table_cols;
+    a.s = *s;
+    a.table = d_table;
+    a.block = d_block;
+    a.n_tok_out = d_n_tok;
+    a.budget = d_budget;
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_loop_prepare(a, st); });
+}
+
+wf_status wf_loop_finish(wf_engine *e, int32_t n, const wf_loop_state *s, int32_t K,
+                         const int32_t *d_n_tok, const int32_t *d_n_acc,
+                         const int32_t *d_next_token, const int32_t *d_n_emit,
+                         const int32_t *d_done, void *stream) {
+    if (!e || !loop_state_ok(s) || !d_n_tok || !d_n_acc || !d_next_token || !d_n_emit || !d_done)
+        return fail(WF_EINVAL, "null argument");
+    if (n < 1) return fail(WF_EINVAL, "n < 1");
+    if (K < 0) return fail(WF_EINVAL, "K < 0");
+    LoopArgs a{};
+    a.n = n;
+    a.K = K;
+    a.s = *s;
+    a.n_tok = d_n_tok;
+    a.n_acc = d_n_acc;
+    a.next_token = d_next_token;
+    a.n_emit = d_n_emit;
+    a.done = d_done;
+    hipStream_t st = (hipStream_t)stream;
+    return timed(e, TK_OTHER, st, [&] { return launch_loop_finish(a, st); });
+}
+
 wf_status wf_device_state(wf_engine *e, int32_t *h_err, int32_t *h_len, void *stream) {
     if (!e) return fail(WF_EINVAL, "null engine");
     hipStream_t st = (hipStream_t)stream;

@@ -235,6 +235,43 @@ __global__ void rollback_kernel(RollbackArgs a) {
 }
 
 // Shorten a slot's cache to a given length (never lengthen it).
+// Running-loop bookkeeping, one thread per request (the arithmetic is
+// integer: the same results in any order).
+__global__ void loop_prepare_kernel(LoopArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.n) return;
+    const int R = a.n_max - a.s.emitted[b];
+    const int L = a.s.len[b];
+    const int k = max(0, min(min(a.K, R - 1), a.n_ctx - L - 1));
+    a.n_tok_out[b] = a.s.done[b] > 0 ? 0 : k + 1;
+    a.budget[b] = max(R, 1);
+    if (a.table) {
+        const int T = a.K + 1;
+        int32_t *blk = a.block + (size_t)b * T;
+        const int32_t *tab = a.table + (size_t)b * a.table_cols;
+        blk[0] = a.s.anchor[b];
+        for (int i = 1; i < T; ++i) blk[i] = tab[min(max(L + i, 0), a.table_cols - 1)];
+    }
+}
+
+__global__ void loop_finish_kernel(LoopArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.n) return;
+    const int nt = a.n_tok[b];
+    if (nt <= 0) return;
+    const int acc = a.n_acc[b], nxt = a.next_token[b], ne = a.n_emit[b];
+    a.s.len[b] += acc + 1;
+    if (nxt >= 0) a.s.anchor[b] = nxt;
+    a.s.emitted[b] += ne;
+    a.s.tok_sum[b] += ne;
+    if (a.done[b] > 0) a.s.done[b] = 1;
+    a.s.acc_sum[b] += acc;
+    a.s.prop_sum[b] += nt - 1;
+    a.s.rounds[b] += 1;
+    a.s.step[b] += 1;
+    atomicAdd(reinterpret_cast<unsigned long long *>(a.s.hist) + min(max(acc, 0), a.K), 1ull);
+}
+
 __global__ void truncate_kernel(RollbackArgs a) {
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= a.n) return;
@@ -391,6 +428,14 @@ hipError_t launch_accept(const AcceptArgs &a, hipStream_t st) {
 }
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st) {
     hipLaunchKernelGGL(rollback_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_loop_prepare(const LoopArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(loop_prepare_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_loop_finish(const LoopArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL(loop_finish_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st) {

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include "../../include/wf.h"
 
 namespace wf {
 
@@ -141,6 +142,14 @@ struct AcceptArgs {
     // scratch for the rows' softmax statistics, 2 floats per row [n][T]
     // (nullable: then the acceptance kernel reduces each row itself)
     float *stats;
+};
+
+struct LoopArgs {
+    int32_t n, K, n_max, n_ctx, table_cols;
+    wf_loop_state s;
+    const int32_t *table;
+    int32_t *block, *n_tok_out, *budget;
+    const int32_t *n_tok, *n_acc, *next_token, *n_emit, *done;
 };
 
 struct RollbackArgs {
@@ -338,6 +347,8 @@ hipError_t launch_self_attn(const SelfAttnArgs &a, int hd, int mt, hipStream_t s
 hipError_t launch_cross_attn(const CrossAttnArgs &a, int hd, hipStream_t st);
 hipError_t launch_lm_reduce(const LmReduceArgs &a, hipStream_t st);
 hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
+hipError_t launch_loop_prepare(const LoopArgs &a, hipStream_t st);
+hipError_t launch_loop_finish(const LoopArgs &a, hipStream_t st);
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st);
 hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st);  // n_acc = new lengths

@@ -206,8 +206,9 @@ class DeviceLoop:
     each absolute position (the synthetic table drafter: the greedy token
     there with probability p, else a replacement id), or ``drafter=True``
     takes the engine's own parallel drafter (wf_draft). Requests that are
-    done get n_tok = 0 and are skipped by the engine. The torch operations
-    here are the harness (indexing and counters), not method arithmetic."""
+    done get n_tok = 0 and are skipped by the engine. The round's bookkeeping
+    (n_tok, budgets, the table block, the state update) runs in the
+    library's wf_loop_prepare / wf_loop_finish kernels."""
 
     def __init__(self, eng, slots: Sequence[int], anchors: np.ndarray, lens: np.ndarray,
                  n_max: int, K: int, eos: int, draft_table: Optional[np.ndarray] = None,
@@ -242,22 +243,17 @@ class DeviceLoop:
         self.table = None
         if draft_table is not None:
             self.table = torch.as_tensor(np.ascontiguousarray(draft_table, np.int32), device=dev)
-        self.ar = torch.arange(1, T, device=dev, dtype=torch.int32)
+        self.state = eng.loop_state(self.anchor, self.L, self.emitted, self.done, self.acc_sum,
+                                    self.prop_sum, self.rounds_active, self.step, self.tok_sum,
+                                    self.hist)
 
     def prepare(self):
         """This round's block, n_tok and budgets from the state."""
-        torch = self.torch
-        R = self.n_max - self.emitted
-        room = self.eng.shape.n_ctx - self.L - 1     # candidates that still fit the context
-        k = torch.clamp(torch.minimum(torch.minimum(torch.full_like(R, self.K), R - 1), room), min=0)
-        self.ntok.copy_(torch.where(self.done > 0, torch.zeros_like(k), k + 1))
-        self.budget.copy_(torch.clamp(R, min=1))
+        self.eng.wf_loop_prepare(self.state, self.n, self.K, self.n_max,
+                                 None if self.drafter else self.table, self.block, self.ntok,
+                                 self.budget)
         if self.drafter:
             self.eng.wf_draft(self.d_slots, self.anchor, self.K, self.block)
-        else:
-            pos = (self.L[:, None] + self.ar[None, :]).clamp(max=self.table.shape[1] - 1)
-            self.block[:, 1:].copy_(torch.gather(self.table, 1, pos.long()))
-            self.block[:, 0].copy_(self.anchor)
 
     def verify(self):
         self.eng.wf_verify_block(self.d_slots, self.block, self.ntok, self.am, self.logits)
@@ -267,22 +263,9 @@ class DeviceLoop:
 
     def finish(self):
         """Rollback and the state update of the round."""
-        torch = self.torch
         n_acc, nxt, n_emit, dn = self.outs
         self.eng.wf_rollback(self.d_slots, n_acc)
-        active = self.ntok > 0
-        zero = torch.zeros_like(n_acc)
-        acc = torch.where(active, n_acc, zero)
-        self.L.add_(torch.where(active, acc + 1, zero))
-        self.anchor.copy_(torch.where(active & (nxt >= 0), nxt, self.anchor))
-        self.emitted.add_(torch.where(active, n_emit, zero))
-        self.tok_sum.add_(torch.where(active, n_emit, zero))
-        self.done.copy_(torch.where(active & (dn > 0), torch.ones_like(dn), self.done))
-        self.acc_sum.add_(acc)
-        self.prop_sum.add_(torch.where(active, self.ntok - 1, zero))
-        self.rounds_active.add_(active.to(torch.int32))
-        self.step.add_(active.to(torch.int32))
-        self.hist.index_add_(0, acc.clamp(0, self.K).long(), active.long())
+        self.eng.wf_loop_finish(self.state, self.n, self.K, self.ntok, n_acc, nxt, n_emit, dn)
 
     def restart(self, anchors: np.ndarray, lens: np.ndarray):
         """Start every request again from a fresh prefill (anchors, lengths),
