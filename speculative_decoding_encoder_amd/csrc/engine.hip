@@ -1189,7 +1189,8 @@ wf_status wf_accept(wf_engine *e, int32_t n, const int32_t *d_tokens, int32_t T,
     a.step = d_step;
     // the LM head's per-tile maxima are consumed by then: their buffer holds
     // the rows' softmax statistics when it is large enough
-    if (temperature > 0.f && (size_t)n * T * 2 <= (size_t)e->lay.n_vtiles * e->c.max_rows)
+    if (temperature > 0.f &&
+        sample_scratch_floats(n, T) <= (size_t)e->lay.n_vtiles * e->c.max_rows)
         a.stats = e->lmmax;
     hipStream_t st = (hipStream_t)stream;
     return timed(e, TK_OTHER, st, [&] { return launch_accept(a, st); });

@@ -326,9 +326,284 @@ __global__ __launch_bounds__(1024) void accept_sample_kernel(AcceptArgs a) {
     }
 }
 
+// With the row statistics in scratch the round is split so that the row a
+// request draws from is spread over many workgroups:
+//  1. decide (one thread per request): the candidate walk with the
+//     statistics; writes the outputs of requests that end without a draw
+//     (refused, accepted EOS) and, for the others, the accepted count, the
+//     row to draw from (the first rejected candidate's, or row k for the
+//     bonus) and the uniform;
+//  2. segment sums (one workgroup per request and segment of the row): the
+//     residual's and p's mass of each of kSeg segments, each thread summing
+//     a contiguous run in id order, then a block reduction;
+//  3. draw (one workgroup per drawing request): the residual when its total
+//     mass is positive (a rejection), else p; the crossing segment by a
+//     sequential prefix over the segment sums, then the crossing id inside
+//     it by a sequential prefix over the threads' runs and the run's walk.
+//     If rounding leaves the threshold past the mass: the last id with
+//     positive weight.
+// Scratch after the statistics: per request (acc, row, kind, uniform), then
+// per request and segment (residual sum, p sum).
+constexpr int kSeg = 64;
+constexpr int kSegThreads = 256;
+
+struct DrawScratch {
+    int32_t *acc, *row;
+    float *u;
+    float *seg;                 // [n][kSeg][2]
+};
+__device__ __forceinline__ DrawScratch draw_scratch(const AcceptArgs &a) {
+    float *base = a.stats + 2 * (size_t)a.n * a.T;
+    DrawScratch d;
+    d.acc = reinterpret_cast<int32_t *>(base);
+    d.row = d.acc + a.n;
+    d.u = reinterpret_cast<float *>(d.row + a.n);
+    d.seg = d.u + a.n;
+    return d;
+}
+
+__global__ void sample_decide_kernel(AcceptArgs a) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= a.n) return;
+    const DrawScratch d = draw_scratch(a);
+    d.row[b] = -1;
+    const int nt = a.n_tok[b];
+    int n_acc = 0, n_emit = 0, done = 0;
+    if (nt > 0) {
+        const int k = nt - 1;
+        const int R = a.budget[b];
+        const int32_t *tok = a.tokens + (size_t)b * a.T;
+        bool ok = !(R < 1 || k > R - 1 || nt > a.T);
+        for (int i = 1; ok && i <= k; ++i)
+            if (tok[i] < 0 || tok[i] >= a.V) ok = false;
+        if (!ok) {
+            n_acc = -1;
+            done = 1;
+        } else {
+            const int req = a.request_id[b], step = a.step[b];
+            const float T = a.temperature;
+            int acc = 0;
+            bool stopped = false;
+            for (int i = 0; i < k && !stopped; ++i) {
+                const float *row = a.logits + ((size_t)b * a.T + i) * a.V;
+                const float *qrow = a.q + ((size_t)b * (a.T - 1) + i) * a.V;
+                const RowStats st{a.stats[2 * ((size_t)b * a.T + i)],
+                                  a.stats[2 * ((size_t)b * a.T + i) + 1]};
+                const int y = tok[i + 1];
+                const float py = prob(row, y, T, a.suppress, st);
+                const float qy = qrow[y];
+                const float u = uniform24(a.seed, req, step, i, STREAM_ACCEPT);
+                if (u * qy < py) {
+                    acc = i + 1;
+                    if (y == a.eos) {          // accepted EOS: finished, no bonus
+                        n_emit = acc;
+                        done = 1;
+                        stopped = true;
+                    }
+                    continue;
+                }
+                d.row[b] = i;                  // first rejection: draw from row i
+                d.u[b] = uniform24(a.seed, req, step, i, STREAM_RESAMPLE);
+                stopped = true;
+            }
+            if (!stopped) {                    // every candidate accepted: bonus from row k
+                d.row[b] = k;
+                d.u[b] = uniform24(a.seed, req, step, k, STREAM_RESAMPLE);
+            }
+            d.acc[b] = acc;
+            n_acc = acc;
+        }
+    }
+    if (d.row[b] < 0) {
+        a.n_acc[b] = n_acc;
+        a.next_token[b] = -1;
+        a.n_emit[b] = n_emit;
+        a.done[b] = done;
+    }
+}
+
+__device__ __forceinline__ float block_sum_t(float v, float *sh) {   // kSegThreads threads
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) sh[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSegThreads / 64; ++i) t += sh[i];
+    __syncthreads();
+    return t;
+}
+
+// The ids of thread t of segment g: [v0, v1).
+__device__ __forceinline__ void seg_run(int V, int g, int t, int &v0, int &v1) {
+    const int sl = (V + kSeg - 1) / kSeg;
+    const int lo = g * sl, hi = min(lo + sl, V);
+    const int rl = (sl + kSegThreads - 1) / kSegThreads;
+    v0 = min(lo + t * rl, hi);
+    v1 = min(v0 + rl, hi);
+}
+
+__global__ __launch_bounds__(kSegThreads) void sample_segsum_kernel(AcceptArgs a) {
+    __shared__ float sh[kSegThreads / 64];
+    const int b = blockIdx.x / kSeg, g = blockIdx.x - b * kSeg;
+    const DrawScratch d = draw_scratch(a);
+    const int r = d.row[b];
+    if (r < 0) return;
+    const int k = a.n_tok[b] - 1;
+    const bool resid = r < k;                  // a rejection: the residual; the bonus: p
+    const float *row = a.logits + ((size_t)b * a.T + r) * a.V;
+    const float *qrow = resid ? a.q + ((size_t)b * (a.T - 1) + r) * a.V : nullptr;
+    const RowStats st{a.stats[2 * ((size_t)b * a.T + r)], a.stats[2 * ((size_t)b * a.T + r) + 1]};
+    int v0, v1;
+    seg_run(a.V, g, threadIdx.x, v0, v1);
+    float sr = 0.f, sp = 0.f;
+    walk_range(row, qrow, v0, v1, a.temperature, a.suppress, [&](int, float z, float qv) {
+        const float p = prob_z(z, st);
+        sp += p;
+        sr += fmaxf(p - qv, 0.f);
+    });
+    sr = block_sum_t(sr, sh);
+    sp = block_sum_t(sp, sh);
+    if (threadIdx.x == 0) {
+        d.seg[((size_t)b * kSeg + g) * 2] = resid ? sr : 0.f;
+        d.seg[((size_t)b * kSeg + g) * 2 + 1] = sp;
+    }
+}
+
+__global__ __launch_bounds__(kSegThreads) void sample_draw_kernel(AcceptArgs a) {
+    __shared__ float run[kSegThreads];
+    __shared__ int sel_g, sel_t, found;
+    __shared__ float sel_base, sel_thr;
+    __shared__ int use_resid;
+    const int b = blockIdx.x;
+    const DrawScratch d = draw_scratch(a);
+    const int r = d.row[b];
+    if (r < 0) return;
+    const int k = a.n_tok[b] - 1;
+    const float *row = a.logits + ((size_t)b * a.T + r) * a.V;
+    const float *qrow = r < k ? a.q + ((size_t)b * (a.T - 1) + r) * a.V : nullptr;
+    const RowStats st{a.stats[2 * ((size_t)b * a.T + r)], a.stats[2 * ((size_t)b * a.T + r) + 1]};
+    const float *sg = d.seg + (size_t)b * kSeg * 2;
+    if (threadIdx.x == 0) {
+        float rs = 0.f, ps = 0.f;
+        for (int g = 0; g < kSeg; ++g) {
+            rs += sg[2 * g];
+            ps += sg[2 * g + 1];
+        }
+        const int ur = r < k && rs > 0.f;
+        const float total = ur ? rs : ps;
+        const float thr = d.u[b] * total;
+        float acc = 0.f;
+        int gsel = -1;
+        for (int g = 0; g < kSeg; ++g) {
+            const float x = sg[2 * g + (ur ? 0 : 1)];
+            if (acc + x > thr && x > 0.f) {
+                gsel = g;
+                break;
+            }
+            acc += x;
+        }
+        use_resid = ur;
+        sel_g = gsel;
+        sel_base = acc;
+        sel_thr = thr;
+        found = 0x7fffffff;
+    }
+    __syncthreads();
+    const bool ur = use_resid != 0;
+    auto weight = [&](float z, float qv) {
+        const float p = prob_z(z, st);
+        return ur ? fmaxf(p - qv, 0.f) : p;
+    };
+    const int g = sel_g;
+    if (g >= 0) {
+        int v0, v1;
+        seg_run(a.V, g, threadIdx.x, v0, v1);
+        float s = 0.f;
+        walk_range(row, ur ? qrow : nullptr, v0, v1, a.temperature, a.suppress,
+                   [&](int, float z, float qv) { s += weight(z, qv); });
+        run[threadIdx.x] = s;
+        __syncthreads();
+        if (threadIdx.x == 0) {                 // the crossing run, in id order
+            float acc = sel_base;
+            int t = 0;
+            for (; t < kSegThreads; ++t) {
+                if (acc + run[t] > sel_thr && run[t] > 0.f) break;
+                acc += run[t];
+            }
+            sel_t = t;
+            sel_base = acc;
+        }
+        __syncthreads();
+        if (threadIdx.x == sel_t) {
+            // the crossing id; if rounding keeps the walk under the threshold,
+            // the run's last id with positive weight
+            float c = sel_base;
+            int hit = -1, last = -1;
+            walk_range(row, ur ? qrow : nullptr, v0, v1, a.temperature, a.suppress,
+                       [&](int v, float z, float qv) {
+                           if (hit >= 0) return;
+                           const float w = weight(z, qv);
+                           c += w;
+                           if (w > 0.f) last = v;
+                           if (c > sel_thr) hit = v;
+                       });
+            found = hit >= 0 ? hit : last;
+        }
+        __syncthreads();
+        if (sel_t == kSegThreads) {
+            // no run crossed (rounding): the segment's last id with positive weight
+            int last = -1;
+            walk_range(row, ur ? qrow : nullptr, v0, v1, a.temperature, a.suppress,
+                       [&](int v, float z, float qv) {
+                           if (weight(z, qv) > 0.f) last = v;
+                       });
+            if (threadIdx.x == 0) found = -1;
+            __syncthreads();
+            atomicMax(&found, last);
+            __syncthreads();
+            if (found < 0 && threadIdx.x == 0) found = 0x7fffffff;
+            __syncthreads();
+        }
+    }
+    if (found == 0x7fffffff) {
+        // rounding put the threshold at or past the mass: the last id with
+        // positive weight (-1 when there is none)
+        int last = -1;
+        for (int v = threadIdx.x; v < a.V; v += kSegThreads) {
+            const float w = weight(zval(row, v, a.temperature, a.suppress), ur ? qrow[v] : 0.f);
+            if (w > 0.f) last = max(last, v);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) found = -1;
+        __syncthreads();
+        atomicMax(&found, last);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const int c = found;
+        const int acc = d.acc[b];
+        const int R = a.budget[b];
+        a.n_acc[b] = acc;
+        a.next_token[b] = c;
+        a.n_emit[b] = acc + 1;
+        a.done[b] = (c == a.eos) || (acc + 1 >= R) || c < 0;
+    }
+}
+
+size_t sample_scratch_floats(int n, int T) {
+    return 2 * (size_t)n * T + 3 * (size_t)n + (size_t)n * kSeg * 2;
+}
+
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st) {
-    if (a.stats) hipLaunchKernelGGL(sample_row_stats_kernel, dim3(a.n * a.T), dim3(NT), 0, st, a);
-    hipLaunchKernelGGL(accept_sample_kernel, dim3(a.n), dim3(NT), 0, st, a);
+    if (!a.stats) {
+        hipLaunchKernelGGL(accept_sample_kernel, dim3(a.n), dim3(NT), 0, st, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(sample_row_stats_kernel, dim3(a.n * a.T), dim3(NT), 0, st, a);
+    hipLaunchKernelGGL(sample_decide_kernel, dim3((a.n + 63) / 64), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(sample_segsum_kernel, dim3(a.n * kSeg), dim3(kSegThreads), 0, st, a);
+    hipLaunchKernelGGL(sample_draw_kernel, dim3(a.n), dim3(kSegThreads), 0, st, a);
     return hipGetLastError();
 }
 

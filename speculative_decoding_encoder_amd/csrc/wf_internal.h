@@ -350,6 +350,7 @@ hipError_t launch_accept(const AcceptArgs &a, hipStream_t st);
 hipError_t launch_loop_prepare(const LoopArgs &a, hipStream_t st);
 hipError_t launch_loop_finish(const LoopArgs &a, hipStream_t st);
 hipError_t launch_accept_sample(const AcceptArgs &a, hipStream_t st);
+size_t sample_scratch_floats(int n, int T);   // floats of AcceptArgs::stats the split draw uses
 hipError_t launch_rollback(const RollbackArgs &a, hipStream_t st);
 hipError_t launch_truncate(const RollbackArgs &a, hipStream_t st);  // n_acc = new lengths
 hipError_t launch_reset(int32_t n, int32_t max_batch, const int32_t *slots, int32_t *len,
