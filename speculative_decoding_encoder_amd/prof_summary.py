@@ -10,6 +10,9 @@ dispatches that start inside such a window.
       --dir gpurun_out/prof_b32_tr --log gpurun_out/prof_b32_tr.log \\
       --window large-v3-verify-b32-greedy --title "..." --command "..." --out FILE
 
+  python -m speculative_decoding_encoder_amd.prof_summary mfma --dir D --log L \\
+      --window WORKLOAD --title "..." --command "..." --out FILE
+
   python -m speculative_decoding_encoder_amd.prof_summary traffic \\
       --fetch-dir D1 --fetch-log L1 --write-dir D2 --write-log L2 \\
       --window WORKLOAD --kind oproj --symbol 'wf::gemm_rk_kernel<1,' \\
@@ -185,6 +188,39 @@ def cmd_traffic(a) -> str:
     return text
 
 
+def cmd_mfma(a) -> str:
+    """MfmaUtil (MFMA-busy cycles over active cycles times SIMDs) and MFMA
+    flops (MfmaFlopsBF16 + MfmaFlopsF16) per dispatch, for the dispatches that
+    start inside the timed window, averaged per kernel."""
+    wins = windows(a.log).get(a.window, [])
+    if not wins:
+        raise SystemExit(f"no timed window for {a.window} in {a.log}")
+    per: Dict[Tuple[str, str], Dict[str, float]] = {}
+    for r in read_rows(a.dir, "*counter_collection.csv"):
+        if not in_window(r, wins):
+            continue
+        c = per.setdefault((short_name(r["Kernel_Name"]), r["Dispatch_Id"]), {})
+        c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    agg: Dict[str, List[float]] = {}
+    for (name, _), c in per.items():
+        x = agg.setdefault(name, [0, 0.0, 0.0])
+        x[0] += 1
+        x[1] += c.get("MfmaUtil", 0.0)
+        x[2] += c.get("MfmaFlopsBF16", 0.0) + c.get("MfmaFlopsF16", 0.0)
+    lines = [f"# rocprofv3 MFMA counters -- {a.title}",
+             "# command (repo root on the MI355X box):",
+             f"#   {a.command}",
+             f"# dispatches that start inside the timed window of {a.window} (bench.py",
+             "# --mark-timed); MfmaUtil: MFMA-busy cycles / (active cycles x SIMDs), per",
+             "# dispatch; GFLOP: MFMA flops per dispatch (bf16 + fp16)", "",
+             f"{'kernel':<66}{'calls':>7}{'mfma_util_%':>13}{'gflop':>11}"]
+    for name, (n, u, f) in sorted(agg.items(), key=lambda kv: -kv[1][2]):
+        if f <= 0:
+            continue
+        lines.append(f"{name[:65]:<66}{int(n):>7}{u / n:>13.2f}{f / n / 1e9:>11.3f}")
+    return "\n".join(lines) + "\n"
+
+
 def main(argv: Optional[List[str]] = None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -195,6 +231,10 @@ def main(argv: Optional[List[str]] = None):
     s.add_argument("--title", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--out")
+    mf = sub.add_parser("mfma")
+    for k in ("dir", "log", "window", "title", "command"):
+        mf.add_argument("--" + k, required=True)
+    mf.add_argument("--out")
     t = sub.add_parser("traffic")
     for k in ("fetch-dir", "fetch-log", "write-dir", "write-log", "window", "kind", "symbol",
               "command"):
@@ -204,7 +244,7 @@ def main(argv: Optional[List[str]] = None):
     t.add_argument("--out")
     t.add_argument("--json")
     a = ap.parse_args(argv)
-    text = cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    text = {"stats": cmd_stats, "mfma": cmd_mfma, "traffic": cmd_traffic}[a.cmd](a)
     if a.out:
         with open(a.out, "w") as f:
             f.write(text)
