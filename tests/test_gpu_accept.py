@@ -14,7 +14,10 @@ Integer logic on random arrays, so every outcome is exact:
   and ending the request, an EOS bonus, the budget ending it) and disjoint
   supports (the suppression mask zeroes p where q lives: the first candidate
   is always rejected and the correction comes from p, EOS included).
-  Decisions within fp32 rounding of their boundary are not compared.
+  Decisions within fp32 rounding of their boundary are not compared. Both
+  on a 64-id vocabulary (the one-kernel draw) and on a 1000-id one, ragged
+  against the 64-id tiles, whose engine holds the split draw's scratch (row
+  statistics, segment sums, then the draw).
 * trees: random parent arrays with accepted chains, an accepted EOS node,
   EOS as the next token, budgets 1..depth+1. Against ``oracle.tree.tree_accept``.
 """
@@ -44,6 +47,28 @@ def eng(request):
     from speculative_decoding_encoder_amd.binding import Engine
     shape = dataclasses.replace(TINY, n_layers=1, d_ffn=64, vocab=V, n_frames=32, eos_id=EOS)
     e = Engine(shape, make_weights(shape, 91), max_batch=1024, max_rows=64)
+    yield e
+    e.close()
+
+
+# A vocabulary that is no multiple of the LM head's 64-id tiles, on an engine
+# whose per-tile maxima buffer (ceil(V / 64) x max_rows floats) can hold the
+# split draw's scratch for 512 requests of K + 1 = 9 rows (2nT + 3n + 128n
+# floats): sampling then takes the row-statistics / segment-sum / draw
+# kernels, where the narrow engine above takes the one-kernel fallback.
+V_WIDE = 1000
+WIDE_ROWS = -(-(2 * 512 * 9 + 3 * 512 + 128 * 512) // -(-V_WIDE // 64))
+
+
+@pytest.fixture(scope="module")
+def eng_wide(request):
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from speculative_decoding_encoder_amd.binding import Engine
+    shape = dataclasses.replace(TINY, n_layers=1, d_ffn=64, vocab=V_WIDE, n_frames=32,
+                                eos_id=V_WIDE - 1)
+    e = Engine(shape, make_weights(shape, 92), max_batch=1024, max_rows=WIDE_ROWS)
     yield e
     e.close()
 
@@ -154,14 +179,14 @@ def _sampling_case(eng, logits, q, tok, n_tok, budget, suppress, seed, step):
     return _host(outs)
 
 
-def _oracle_round(logits, q, drafts, suppress, seed, req, step, R):
+def _oracle_round(logits, q, drafts, suppress, seed, req, step, R, eos=EOS):
     """The oracle's outcome and the smallest relative distance of any
     decision it took from its fp32 boundary."""
     k = len(drafts)
     p = np.stack([osmp.probs(logits[i], TEMP, suppress) for i in range(k + 1)])
     u_acc = [ph.uniform(seed, req, step, i, ph.STREAM_ACCEPT) for i in range(k)]
     u_res = [ph.uniform(seed, req, step, i, ph.STREAM_RESAMPLE) for i in range(k + 1)]
-    a, em, c, dn = osmp.rejection_round(p, q[:k], drafts, u_acc, u_res, EOS, R)
+    a, em, c, dn = osmp.rejection_round(p, q[:k], drafts, u_acc, u_res, eos, R)
     worst = np.inf
     for i in range(min(a + 1, k)):
         y = drafts[i]
@@ -176,10 +201,12 @@ def _oracle_round(logits, q, drafts, suppress, seed, req, step, R):
     return (a, -1 if c is None else c, len(em), int(dn)), worst
 
 
-def sampling_case(case, n=512, K=8):
+def sampling_case(case, n=512, K=8, V=V):
     """Logits, draft distributions, blocks, n_tok, budgets and the
-    suppression mask of one edge case of rejection sampling."""
+    suppression mask of one edge case of rejection sampling over a
+    vocabulary of V ids, EOS the last."""
     T = K + 1
+    EOS = V - 1
     g = np.random.default_rng(77 if case == "q_equals_p" else 78)
     logits = (g.standard_normal((n, T, V)) * 2.0).astype(np.float32)
     suppress = None
@@ -221,6 +248,7 @@ SEED, STEP = 31337, 5
 def sampling_expected(logits, q, tok, n_tok, budget, suppress):
     """Per request: None when the kernel must refuse the block, else the
     oracle's (n_acc, next, n_emit, done) and its smallest decision margin."""
+    eos = logits.shape[-1] - 1
     out = []
     for b in range(tok.shape[0]):
         nt, R = int(n_tok[b]), int(budget[b])
@@ -228,11 +256,11 @@ def sampling_expected(logits, q, tok, n_tok, budget, suppress):
             out.append(None)
         else:
             out.append(_oracle_round(logits[b], q[b], [int(t) for t in tok[b, 1:nt]], suppress,
-                                     SEED, b, STEP, R))
+                                     SEED, b, STEP, R, eos))
     return out
 
 
-def sampling_edges_met(expected):
+def sampling_edges_met(expected, EOS=EOS):
     seen = {"eos_accepted": 0, "eos_next": 0, "refused": 0, "budget_end": 0}
     for e in expected:
         if e is None:
@@ -246,9 +274,12 @@ def sampling_edges_met(expected):
     return seen
 
 
+@pytest.mark.parametrize("vocab", [V, V_WIDE])
 @pytest.mark.parametrize("case", ["q_equals_p", "disjoint_supports"])
-def test_sampling_accept_edges_against_oracle(eng, case):
-    logits, q, tok, n_tok, budget, suppress = sampling_case(case)
+def test_sampling_accept_edges_against_oracle(request, case, vocab):
+    eng = request.getfixturevalue("eng" if vocab == V else "eng_wide")
+    EOS = vocab - 1
+    logits, q, tok, n_tok, budget, suppress = sampling_case(case, V=vocab)
     n = tok.shape[0]
     n_acc, nxt, n_emit, done = _sampling_case(eng, logits, q, tok, n_tok, budget, suppress,
                                               SEED, STEP)
@@ -266,8 +297,8 @@ def test_sampling_accept_edges_against_oracle(eng, case):
             assert got == exp, (b, got, exp, worst)
         if case == "disjoint_supports":
             assert got[0] == 0 and (got[1] < 24 or got[1] == EOS), (b, got)
-    seen = sampling_edges_met(expected)
-    log(f"sampling edges {case}: {agree} identical, {pinned} pinned, {seen}")
+    seen = sampling_edges_met(expected, EOS)
+    log(f"sampling edges {case} V={vocab}: {agree} identical, {pinned} pinned, {seen}")
     checked = n - seen["refused"]
     assert pinned >= 0.9 * checked and agree >= checked - 3
     assert seen["eos_next"] >= 10 and seen["budget_end"] >= 10 and seen["refused"] >= 10
