@@ -16,8 +16,10 @@
 //  * GEMM: C = A W^T, bf16 x bf16 -> fp32 (16x16x32 MFMA). A workgroup of 4
 //    waves owns a 128 x 256 tile (each wave 64 x 128: 4 x 8 accumulator
 //    tiles); both operands go through double-buffered LDS in 32-deep k-steps
-//    (rows padded to 80 B: conflict-free 16-byte fragment reads), the global
-//    loads of a k-step issued two k-steps ahead (K % 64 == 0). The MFMA
+//    (the 16-byte chunks of a row XOR-swizzled: conflict-free fragment
+//    reads), the global loads of a k-step issued two k-steps ahead (K % 64
+//    == 0). Grids of two or more rounds take 256 x 256 tiles on eight waves
+//    whose operands are copied straight into a four-stage LDS ring. The MFMA
 //    computes C^T so a lane holds one output row and four consecutive
 //    columns (8- or 16-byte epilogue stores). Row tiles are grouped by 8 per
 //    column walk and workgroups are dealt to the 8 XCDs in consecutive
@@ -74,7 +76,12 @@ struct GemmArgs {
     int F_pad, hd, max_batch;
 };
 
-constexpr int GBK = 32, GROW = 40;   // k-step depth; LDS row (32 k + 8 pad)
+constexpr int GBK = 32, GROW = 32;   // k-step depth; LDS row: the k-step's 32 elements
+// The four 16-byte chunks of LDS row r are stored XOR-swizzled: chunk c at
+// c ^ ((r >> 1) & 3). Eight lanes reading one chunk of eight consecutive
+// rows (a fragment read) then hit eight different 16-byte bank groups, and
+// so do eight lanes writing two whole rows.
+__host__ __device__ constexpr int swz(int r, int c) { return r * GROW + ((c ^ ((r >> 1) & 3)) << 3); }
 
 __device__ __forceinline__ float gelu(float t) {
     return 0.5f * t * (1.0f + erff(t * 0.70710678118654752f));
@@ -162,6 +169,47 @@ __device__ __forceinline__ void epi_tile(const GemmArgs &a, int m, int n, const 
 // workgroup (4 x 8: 128 x 256, the default; 2 x 4: 64 x 128 for grids that
 // would not fill the chip). A tile's shape does not change any element's
 // arithmetic: every output sums its k-steps in order in one lane.
+// The epilogue of a wave's MT x NT accumulator tiles: tile (i, j) gives this
+// lane row mw + 16 i + r16 and columns nw + 16 j + 4 g .. + 3.
+template <int EPI, int MT, int NT>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const f32x4 (&acc)[MT][NT], int mw,
+                                         int nw) {
+    const int lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int i = 0; i < MT; ++i) {
+        const int m = mw + i * 16 + r16;
+        if (m >= a.M) continue;
+        if constexpr (EPI == EE_RESID) {
+            // the residual read-modify-write: all of the row's loads first, so
+            // their latencies overlap (columns past N load a valid address)
+            float4 xv[NT];
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = min(nw + j * 16 + 4 * g, a.N - 4);
+                xv[j] = *reinterpret_cast<const float4 *>(a.x + (size_t)m * a.N + n);
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = nw + j * 16 + 4 * g;
+                if (n >= a.N) continue;
+                const f32x4 c = acc[i][j];
+                float4 v = xv[j];
+                v.x += c[0] + bias4(a.b0, n, 0);
+                v.y += c[1] + bias4(a.b0, n, 1);
+                v.z += c[2] + bias4(a.b0, n, 2);
+                v.w += c[3] + bias4(a.b0, n, 3);
+                *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = v;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int n = nw + j * 16 + 4 * g;
+                if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
+            }
+        }
+    }
+}
+
 template <int EPI, int MT, int NT>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
     constexpr int BM = 32 * MT, BN = 32 * NT;
@@ -195,7 +243,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         const int m = min(m0 + row, a.M - 1);
         const int rq = m / a.rpr;
         xsrc[v] = a.A + (size_t)rq * a.sreq + (size_t)(m - rq * a.rpr) * a.srow + pc * 8;
-        xoff[v] = row * GROW + pc * 8;
+        xoff[v] = swz(row, pc);
     }
 #pragma unroll
     for (int v = 0; v < WL; ++v) {
@@ -204,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         const int seg = n / a.seg_n;
         const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
         wsrc[v] = wb + (size_t)(n - seg * a.seg_n) * a.K + pc * 8;
-        woff[v] = row * GROW + pc * 8;
+        woff[v] = swz(row, pc);
     }
     const int KT = a.K / GBK;
     struct Stage { u32x4 x[XL], w[WL]; };
@@ -233,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         u32x4 xf[MT];
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-            xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][(wm * 16 * MT + i * 16 + r16) * GROW + g * 8]);
+            xf[i] = *reinterpret_cast<const u32x4 *>(&xs[b][swz(wm * 16 * MT + i * 16 + r16, g)]);
         __builtin_amdgcn_s_setprio(1);              // the MFMA block issues first on its SIMD
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -241,7 +289,7 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 #pragma unroll
             for (int j = 0; j < NT / 2; ++j)
                 wf[j] = *reinterpret_cast<const u32x4 *>(
-                    &ws[b][(wn * 16 * NT + (NT / 2 * h + j) * 16 + r16) * GROW + g * 8]);
+                    &ws[b][swz(wn * 16 * NT + (NT / 2 * h + j) * 16 + r16, g)]);
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -271,40 +319,138 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
         __syncthreads();
     }
 
-    // epilogue: tile (i, j) gives this lane row m and columns n .. n + 3
+    epilogue<EPI, MT, NT>(a, acc, m0 + wm * 16 * MT, n0 + wn * 16 * NT);
+}
+
+// Large grids: 256 x 256 tiles on eight waves, a 2 x 4 grid of 128 x 64 wave
+// tiles (8 x 4 accumulator tiles), one workgroup and so two waves per SIMD
+// per CU (one wave per SIMD leaves a third of the MFMA issue rate unused:
+// 1.3-1.9 against 2.45 PFLOP/s in a register-only loop on MI355X). Operands
+// go from global memory straight into LDS (global_load_lds, 16 bytes per
+// lane) through a ring of DST k-step stages. A stage holds 256 A rows and 256 W rows of 64 bytes whose four
+// 16-byte chunks are XOR-swizzled by row (chunk c of row r sits at
+// c ^ ((r >> 1) & 3)), so the fragment reads are free of bank conflicts
+// without padding. Per k-step: wait for the next stage's copies, one
+// barrier, the copies of the stage DST k-steps ahead into the buffer just
+// consumed, the next stage's fragments into registers while this stage's 32
+// MFMAs run. Every output still sums its k-steps in order in one lane with
+// the same MFMA as gemm_kernel, so the two give the same bits.
+constexpr int DBT = 256, DST = 4;          // tile rows / columns, ring stages
+
+// gfx9 s_waitcnt immediates: vmcnt bits [3:0] and [15:14], expcnt [6:4],
+// lgkmcnt [11:8]; the counters not waited for stay at their maxima
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
+    constexpr int MT = 8, NT = 4;
+    constexpr int RPW = DBT / 8;                    // rows of each operand a wave copies
+    constexpr int CPO = RPW / 16;                   // its 16-row copies per operand
+    constexpr int DCOPY = 2 * CPO;                  // copies per wave per stage
+    // [stage][A rows 0..255 | W rows 0..255][32 elements]: 128 KB
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[DST][2 * DBT * 32];
+    const int per = gridDim.x >> 3;
+    const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+    if (lid >= a.n_wg) return;
+    constexpr int GM = 8;                           // row tiles per column walk
+    const int grp = lid / (GM * a.n_n);
+    const int first_m = grp * GM;
+    const int gsz = min(a.n_m - first_m, GM);
+    const int in_grp = lid - grp * GM * a.n_n;
+    const int mt = first_m + in_grp % gsz;
+    const int nt = in_grp / gsz;
+
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int wm = wave >> 2, wn = wave & 3;
+    const int m0 = mt * DBT, n0 = nt * DBT;
+
+    // copies: wave w brings rows RPW w .. RPW w + RPW - 1 of the A and W
+    // tiles in 16-row copies; lane L fills row L / 4 of a copy, LDS chunk
+    // L % 4, with k-chunk (L % 4) ^ ((L >> 3) & 3). Rows past M / N repeat
+    // the last (never stored).
+    const int crow = lane >> 2, cchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const uint16_t *asrc[CPO], *wsrc[CPO];
 #pragma unroll
-    for (int i = 0; i < MT; ++i) {
-        const int m = m0 + wm * 16 * MT + i * 16 + r16;
-        if (m >= a.M) continue;
-        if constexpr (EPI == EE_RESID) {
-            // the residual read-modify-write: all of the row's loads first, so
-            // their latencies overlap (columns past N load a valid address)
-            float4 xv[NT];
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int n = min(n0 + wn * 16 * NT + j * 16 + 4 * g, a.N - 4);
-                xv[j] = *reinterpret_cast<const float4 *>(a.x + (size_t)m * a.N + n);
-            }
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
-                if (n >= a.N) continue;
-                const f32x4 c = acc[i][j];
-                float4 v = xv[j];
-                v.x += c[0] + bias4(a.b0, n, 0);
-                v.y += c[1] + bias4(a.b0, n, 1);
-                v.z += c[2] + bias4(a.b0, n, 2);
-                v.w += c[3] + bias4(a.b0, n, 3);
-                *reinterpret_cast<float4 *>(a.x + (size_t)m * a.N + n) = v;
-            }
-        } else {
-#pragma unroll
-            for (int j = 0; j < NT; ++j) {
-                const int n = n0 + wn * 16 * NT + j * 16 + 4 * g;
-                if (n < a.N) epi_tile<EPI>(a, m, n, acc[i][j]);
-            }
-        }
+    for (int i = 0; i < CPO; ++i) {
+        const int r = RPW * wave + 16 * i + crow;
+        const int m = min(m0 + r, a.M - 1);
+        const int rq = m / a.rpr;
+        asrc[i] = a.A + (size_t)rq * a.sreq + (size_t)(m - rq * a.rpr) * a.srow + cchunk * 8;
+        const int n = min(n0 + r, a.N - 1);
+        const int seg = n / a.seg_n;
+        const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
+        wsrc[i] = wb + (size_t)(n - seg * a.seg_n) * a.K + cchunk * 8;
     }
+    const int KT = a.K / GBK;
+    // stage kt into buffer kt % DST; past the end a valid repeat of the last
+    // k-step into a buffer nothing reads again, so every k-step issues the
+    // same number of copies and the wait counts stay exact
+    auto copy = [&](int kt) {
+        const int kk = min(kt, KT - 1) * GBK;
+        uint16_t *buf = lds[kt % DST];
+#pragma unroll
+        for (int i = 0; i < CPO; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(asrc[i] + kk),
+                (__attribute__((address_space(3))) void *)&buf[(RPW * wave + 16 * i) * 32], 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < CPO; ++i)
+            __builtin_amdgcn_global_load_lds(
+                (const void *)(wsrc[i] + kk),
+                (__attribute__((address_space(3))) void *)&buf[(DBT + RPW * wave + 16 * i) * 32], 16,
+                0, 0);
+    };
+    const int sw = (g ^ ((r16 >> 1) & 3)) * 8;     // where this lane's k-chunk g sits
+    auto frags = [&](u32x4 (&xf)[MT], u32x4 (&wf)[NT], int kt) {
+        const uint16_t *buf = lds[kt % DST];
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+            xf[i] = *reinterpret_cast<const u32x4 *>(&buf[(wm * 128 + 16 * i + r16) * 32 + sw]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+            wf[j] = *reinterpret_cast<const u32x4 *>(&buf[(DBT + wn * 16 * NT + 16 * j + r16) * 32 + sw]);
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // k-step kt: its fragments are in registers (read during k-step kt - 1);
+    // stages kt + 1 .. kt + DST - 1 are in flight or landed
+    auto step = [&](int kt, const u32x4 (&xc)[MT], const u32x4 (&wc)[NT], u32x4 (&xn)[MT],
+                    u32x4 (&wn_)[NT]) {
+        wait_vmcnt<(DST - 2) * DCOPY>();            // this wave's copies of stage kt + 1
+        wait_lgkmcnt0();                            // its reads of stage kt (refilled below)
+        __builtin_amdgcn_s_barrier();               // every wave's, likewise
+        copy(kt + DST);
+        frags(xn, wn_, kt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int i = 0; i < MT; ++i)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) acc[i][j] = mfma_bf16_k32(wc[j], xc[i], acc[i][j]);
+        __builtin_amdgcn_s_setprio(0);
+    };
+#pragma unroll
+    for (int s = 0; s < DST; ++s) copy(s);
+    wait_vmcnt<(DST - 1) * DCOPY>();                // stage 0
+    __builtin_amdgcn_s_barrier();
+    u32x4 xa[MT], wa[NT], xb[MT], wb[NT];
+    frags(xa, wa, 0);
+    for (int kt = 0; kt < KT; kt += 2) {            // KT is even (K % 64 == 0)
+        step(kt, xa, wa, xb, wb);
+        step(kt + 1, xb, wb, xa, wa);
+    }
+    wait_vmcnt<0>();                                // no copy outlives the workgroup's LDS
+    epilogue<EPI, MT, NT>(a, acc, m0 + wm * 128, n0 + wn * 16 * NT);
 }
 
 struct AttnArgs {
@@ -575,10 +721,33 @@ hipError_t launch_tiles(int epi, const GemmArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// 128 x 256 tiles, or 64 x 128 when those would leave most of the 256 CUs
-// idle (a window or two through the d-wide projections)
+template <int EPI>
+hipError_t launch_dma_epi(const GemmArgs &a, hipStream_t st) {
+    hipLaunchKernelGGL((gemm_dma_kernel<EPI>), dim3(cdiv(a.n_wg, 8) * 8), dim3(512), 0, st, a);
+    return hipGetLastError();
+}
+hipError_t launch_dma(int epi, const GemmArgs &a, hipStream_t st) {
+    switch (epi) {
+    case EE_CONV1: return launch_dma_epi<EE_CONV1>(a, st);
+    case EE_CONV2: return launch_dma_epi<EE_CONV2>(a, st);
+    case EE_QKV: return launch_dma_epi<EE_QKV>(a, st);
+    case EE_RESID: return launch_dma_epi<EE_RESID>(a, st);
+    case EE_XKV: return launch_dma_epi<EE_XKV>(a, st);
+    default: return launch_dma_epi<EE_GELU>(a, st);
+    }
+}
+
+// 256 x 256 tiles (the LDS-copy kernel) from two rounds of workgroups on;
+// else 128 x 256 tiles, or 64 x 128 when those would leave most of the 256
+// CUs idle (a window or two through the d-wide projections)
 hipError_t launch_gemm(int epi, GemmArgs &a, hipStream_t st) {
     if (a.K % (2 * GBK) || a.M < 1 || a.N % 4) return hipErrorInvalidValue;   // loop unrolled by 2
+    if (cdiv(a.M, DBT) * cdiv(a.N, DBT) >= 512) {
+        a.n_m = cdiv(a.M, DBT);
+        a.n_n = cdiv(a.N, DBT);
+        a.n_wg = a.n_m * a.n_n;
+        return launch_dma(epi, a, st);
+    }
     const bool small = cdiv(a.M, 128) * cdiv(a.N, 256) < 128;
     a.n_m = cdiv(a.M, small ? 64 : 128);
     a.n_n = cdiv(a.N, small ? 128 : 256);

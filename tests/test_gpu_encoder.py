@@ -9,7 +9,8 @@
   invariance (a request encoded inside a batch of four equals the same
   request alone, bit for bit: no kernel mixes requests, and the smaller
   GEMM tiles a lone window's d-wide projections take do not change any
-  element's arithmetic).
+  element's arithmetic). Twenty windows, whose grids take the 256 x 256
+  LDS-copy tiles, give the bits of the same windows alone.
 * The full 32-block encoder: one window against the oracle's 32-block
   forward (fp32), finite outputs whose rows have mean 0 and variance 1 (the
   final norm with unit gain), and the audio memory it produces drives
@@ -86,6 +87,29 @@ def test_large_width_two_blocks_and_batch_invariance(torch_cuda):
     assert np.array_equal(four[1].view(np.uint32), alone[0].view(np.uint32))
     log("large-width encoder: request 1 in a batch of 4 equals request 1 alone")
     _close(four[0], oe.Encoder(s, wb).forward(mels[0]), "large-width 2-block encoder req 0")
+    enc.close()
+
+
+def test_large_grids_give_the_bits_of_small_ones(torch_cuda):
+    """Twenty windows make every GEMM grid of the encoder two or more rounds
+    of workgroups, so they take the 256 x 256 tiles whose operands are copied
+    straight into LDS (the last row tile ragged: 30000 rows); a window alone
+    takes the 128 x 256 and 64 x 128 tiles. Both sum every output's k-steps
+    in order with the same MFMA, so a window gives the same bits either way;
+    window 0 of the batch also matches the oracle."""
+    import dataclasses
+    from speculative_decoding_encoder_amd.binding import Encoder
+    s = dataclasses.replace(ENC_LARGE_V3, n_layers=2)
+    wb = make_encoder_weights(s, 3)
+    n = 20
+    enc = Encoder(s, wb, max_batch=n)
+    mels = [make_mel(s, 3, r) for r in range(n)]
+    many = _encode(torch_cuda, enc, mels)
+    for r in (0, 13, n - 1):
+        alone = _encode(torch_cuda, enc, mels[r:r + 1])
+        assert np.array_equal(many[r].view(np.uint32), alone[0].view(np.uint32)), r
+    log(f"large-width encoder: windows 0, 13, {n - 1} of {n} equal the windows alone")
+    _close(many[0], oe.Encoder(s, wb).forward(mels[0]), f"large-width 2-block encoder, {n} windows")
     enc.close()
 
 
