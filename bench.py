@@ -863,14 +863,16 @@ def stream_bandwidth(torch, dev, gib: int = 4) -> float:
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 ENC_AUDIO_S = 30.0              # one encoder window is 30 s of audio
-# kernel symbols per kind (epilogue, then the per-wave tile counts: 4, 8 for
-# 128 x 256 tiles, 2, 4 for 64 x 128)
-ENC_SYMBOL = {"stem": "wf::enc::gemm_kernel<0|1, 4, 8>|<0|1, 2, 4>",
-              "qkv": "wf::enc::gemm_kernel<2, 4, 8>|<2, 2, 4>",
+# kernel symbols per kind: the 256 x 256 LDS-copy kernel (template argument:
+# the epilogue) on grids of two or more rounds, else the register-staged one
+# (epilogue, then the per-wave tile counts: 4, 8 for 128 x 256 tiles, 2, 4
+# for 64 x 128)
+ENC_SYMBOL = {"stem": "wf::enc::gemm_dma_kernel<0|1>|wf::enc::gemm_kernel<0|1, 4, 8>|<0|1, 2, 4>",
+              "qkv": "wf::enc::gemm_dma_kernel<2>|wf::enc::gemm_kernel<2, 4, 8>|<2, 2, 4>",
               "attn": "wf::enc::attn_kernel<2>",
-              "oproj": "wf::enc::gemm_kernel<3, 4, 8>|<3, 2, 4>",
-              "fc1": "wf::enc::gemm_kernel<4, 4, 8>|<4, 2, 4>",
-              "fc2": "wf::enc::gemm_kernel<3, 4, 8>|<3, 2, 4>",
+              "oproj": "wf::enc::gemm_dma_kernel<3>|wf::enc::gemm_kernel<3, 4, 8>|<3, 2, 4>",
+              "fc1": "wf::enc::gemm_dma_kernel<4>|wf::enc::gemm_kernel<4, 4, 8>|<4, 2, 4>",
+              "fc2": "wf::enc::gemm_dma_kernel<3>|wf::enc::gemm_kernel<3, 4, 8>|<3, 2, 4>",
               "ln": "wf::enc::ln_kernel", "other": "wf::enc::mel_kernel"}
 
 

@@ -603,7 +603,7 @@ wf_status wf_create(const wf_config *cfg, const wf_weights *w, void *kv_pool, si
 
 void wf_destroy(wf_engine *e) {
     if (!e) return;
-    for (hipEvent_t ev : e->ev_pool) (void)hipEventDestroy(ev);
+    for (hipEvent_t ev : e->ev_pool) hipEventDestroy(ev);
     if (e->static_dev >= 0) {
         std::lock_guard<std::mutex> g(g_static_mu);
         g_static_held[e->static_dev] = false;
