@@ -8,17 +8,21 @@
  *    layer are computed from the audio memory once per request and are only
  *    read afterwards (SGLang-Omni "Whisper ASR" cookbook, section "Breakable
  *    Prefill CUDA Graph").
- *  - wf_verify_block: one causal target pass over the anchor plus K
- *    candidates yields the target's prediction at every position
- *    ("Whisper-Flash: Acoustically Conditioned Parallel Drafting for Faster
- *    Whisper Decoding", section 3.1, eq. 1). A prefill is the same call with
- *    the prompt as the block.
- *  - wf_accept: keep candidates while they agree and emit the target's own
- *    token at the first disagreement, or a bonus after a full block (section
- *    3.1); at temperature T > 0 accept with probability min(1, p/q) and
- *    resample from (p - q)+ (section 3.1, appendix A.4).
- *  - wf_rollback: keep L + 1 + a cache positions, the old anchor plus the
- *    accepted candidates (appendix A.1).
+ *  - wf_verify_block: the anchor and its K candidates go through the target
+ *    decoder in a single causally masked forward, which gives the target's
+ *    next-token choice for every row of the block ("Whisper-Flash:
+ *    Acoustically Conditioned Parallel Drafting for Faster Whisper
+ *    Decoding", section 3.1, eq. 1). A prefill is the same call with the
+ *    prompt as the block.
+ *  - wf_accept: the longest prefix of candidates that matches the target's
+ *    choices is accepted; the target's choice at the row after that prefix
+ *    (a correction, or a bonus when every candidate matched) is emitted too
+ *    (section 3.1); at temperature T > 0 candidate i is accepted with
+ *    probability min(1, p/q) and a rejection draws from (p - q)+ (section
+ *    3.1, appendix A.4).
+ *  - wf_rollback: of the block's rows written to the cache, those of the
+ *    anchor and of the a accepted candidates stay (L + 1 + a positions in
+ *    all); the rest are dropped (appendix A.1).
  *
  * Conventions
  *  - Every pointer named d_* is device memory (HIP); h_* is host memory.
@@ -106,8 +110,9 @@ typedef struct {
     int32_t eos_id;       /* end-of-transcript token id */
     float ln_eps;         /* layer-norm epsilon (1e-5) */
     /* Parallel drafter (Whisper-Flash section 3.2, appendix A.2); 0 layers
-     * disables it. History features are the residual streams after target
-     * blocks tap_layers[0..n_taps) (zero-based, before the final LN). */
+     * disables it. Its history rows take the target's fp32 residual stream
+     * as it leaves each block listed in tap_layers[0..n_taps) (zero-based,
+     * before the final LN). */
     int32_t drafter_layers;   /* 0 or the number of drafter blocks (2) */
     int32_t n_taps;           /* 5 */
     int32_t tap_layers[8];    /* 1, 8, 15, 22, 29 for large-v3 */
@@ -289,9 +294,9 @@ wf_status wf_rollback(wf_engine *e, int32_t n, const int32_t *d_slots,
 wf_status wf_set_readout(wf_engine *e, int32_t layer, int32_t *d_frame);
 
 /* Tree verification ("Alignment Drift in Single-Model Speculative Decoding for
- * ASR", appendix E.3: the target verifies every node of a draft tree in one
- * pass under a tree attention mask; a one-branch tree reproduces the linear
- * decoder). As wf_verify_block, with
+ * ASR", appendix E.3: all nodes of a draft tree are checked by one target
+ * forward in which each node sees only its ancestors; a tree that is a single
+ * chain gives the same result as the linear block). As wf_verify_block, with
  * d_parents int32 [n][T]: parents[b][0] = -1 (node 0 is the anchor, the
  *   root) and 0 <= parents[b][i] < i for the other nodes i < n_tok[b]
  *   (entries at or beyond n_tok are ignored).

@@ -2,15 +2,17 @@
 
 Whisper-Flash §3.1 and App. A.1 define one round:
 
-* the anchor y (emitted, not yet in the target cache, which holds the L
-  positions before it) and k candidates d_1..d_k go through one causal pass;
-  row i yields the target's choice g_i for position L+i+1 (eq. 1: argmax);
-* candidates are kept while they agree, d_i = g_{i-1}; a is the number kept;
-* the target's own token c = g_a is emitted next (the correction at the first
-  disagreement, or the bonus when all k agree) and becomes the next anchor;
-* an accepted EOS ends the transcript and no bonus follows;
+* the anchor y (already emitted; the target cache holds the L positions
+  before it, not y itself) and k candidates d_1..d_k form one block of rows
+  run through the decoder with a causal mask; row i gives the target's
+  choice g_i for position L+i+1 (eq. 1: argmax);
+* a is the length of the longest prefix with d_i = g_{i-1} for every i in it;
+* c = g_a, the target's choice after that prefix, is emitted as well (a
+  correction when a < k, a bonus when a = k) and anchors the next round;
+* once an accepted candidate is EOS the request is finished, with no bonus;
 * rollback keeps L+1+a cache positions (old anchor plus accepted candidates);
-* with R output tokens left at most R-1 candidates are proposed.
+* a request with R tokens of output budget left gets no more than R-1
+  candidates.
 
 Readings where the pages leave a step open: argmax ties go to the lowest token id; the
 first anchor, emitted by prefill, counts toward the output budget; a request

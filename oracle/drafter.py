@@ -3,19 +3,20 @@ beyond self-consistency: the pages print no drafter values).
 
 Whisper-Flash §3.2 (eq. 2) and App. A.2:
 
-* the block is X_t = [Emb(y_t), m, ..., m]: the anchor's token embedding and
-  K copies of a learned mask vector m, at text positions t .. t+K;
+* the block is X_t = [Emb(y_t), m, ..., m]: the anchor's token embedding
+  followed by the same trained vector m repeated K times, at text positions
+  t .. t+K;
 * the history memory holds, for every accepted position before the anchor,
-  the target's residual streams after decoder blocks 1, 8, 15, 22 and 29
-  (zero-based, before the final layer norm), concatenated (5 d) and
+  the target's residual streams leaving blocks 1, 8, 15, 22, 29 (counting
+  from 0; before the final layer norm), concatenated (5 d) and
   projected to the drafter width d;
-* in each drafter layer the block's queries attend to the projected history
-  and to the block itself in one softmax, bidirectionally inside the block,
-  with rotary embeddings (base 10,000, fp32 phases, explicit text
-  positions); cross-attention with the drafter's own acoustic key/value
-  projections and a feed-forward update follow;
-* the token embedding and the output head are shared with the target; mask
-  position i predicts the token at position t + i.
+* in each drafter layer a block row's query scores the projected history
+  rows and every row of the block (no causal mask within it) under a single
+  softmax, with rotary embeddings (base 10,000, fp32 phases, explicit text
+  positions); then cross-attention over the audio with the drafter's own
+  key/value projections, then a feed-forward update;
+* the drafter reuses the target's token embedding and output head; the
+  i-th mask row gives the guess for position t + i.
 
 Readings where the pages leave a step open: a drafter layer has the target block's
 pre-LN structure (self-attention, cross-attention, GELU MLP, same biases);

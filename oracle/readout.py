@@ -2,10 +2,11 @@
 only tests, smoke() and bench.py's CPU baseline may use it).
 
 "Alignment Drift in Single-Model Speculative Decoding for ASR",
-Verification-Attention Correction and App. D.2: the target's audio
-(cross-)attention during verification, averaged over heads at one decoder
-layer, peaks at the current audio position; inference recomputes that
-layer's attention scores from the existing key cache and takes the peak.
+Verification-Attention Correction and App. D.2: at one decoder layer the
+target's cross-attention over the audio frames, averaged over the heads,
+has its maximum near the frame being transcribed; at inference that layer's
+scores are computed again from the keys already cached, and the frame of
+the maximum is the readout.
 
 Readings where the pages leave a step open: the readout is given for every verify row
 (the caller takes the row it needs, e.g. the last kept one); probabilities

@@ -4,9 +4,9 @@ Whisper-Flash §3.1: with target distribution p_i and draft distribution q_i
 (same temperature and token suppression), candidate i is accepted with
 probability min(1, p_i(y_i)/q_i(y_i)); at the first rejection the verifier
 samples from the normalised residual (p_i - q_i)_+; when every candidate is
-accepted it samples a bonus from the next row's p. App. A.4: softmax and the
-acceptance probabilities are computed in FP32; EOS and the output budget
-work as in greedy decoding.
+accepted it samples a bonus from the next row's p. App. A.4: the softmax and
+the acceptance test run in single precision; the end-of-transcript token and
+the budget work the same way as in greedy acceptance.
 
 Readings where the pages leave a step open: the acceptance test is u*q(y) < p(y) with
 u uniform on [0, 1), equivalent to u < p/q for q(y) > 0 (which holds since

@@ -3,9 +3,9 @@ and bench.py's CPU baseline may use it).
 
 "Alignment Drift in Single-Model Speculative Decoding for ASR", App. E.3
 (the tree-decoder implementation check): the draft is a fixed tree of
-candidate tokens, the target verifies every node in one pass under a tree
-attention mask, and a tree with a single branch reproduces the linear
-decoder token for token.
+candidate tokens, one target forward scores all its nodes with each node
+attending only to its ancestors, and a tree that is a single chain must give
+exactly the tokens of the linear block.
 
 Readings where the pages leave a step open:
 
@@ -19,8 +19,8 @@ Readings where the pages leave a step open:
   is), the parent is not an accepted EOS, and its token equals the target's
   choice at the parent. The kept path ends at the deepest accepted node no
   deeper than R - 1 (R output tokens left), the lowest node index among
-  equally deep ones. Then, as in the linear round, an accepted EOS ends the
-  transcript with no bonus, otherwise the target's choice there is emitted
+  equally deep ones. Then, as in the linear round, accepting EOS finishes
+  the request with no bonus; otherwise the target's choice there is emitted
   and becomes the next anchor;
 * rollback keeps the anchor and the path at positions L .. L + a.
 """

@@ -301,7 +301,7 @@ __global__ void reset_kernel(int32_t n, int32_t max_batch, const int32_t *slots,
 // always is), the parent is not an accepted EOS and its token is the
 // target's choice at the parent; the kept path ends at the deepest accepted
 // node no deeper than R - 1 (the lowest index among equally deep ones).
-// Then as in the linear round: an accepted EOS ends the transcript with no
+// Then as in the linear round: accepting EOS finishes the request with no
 // bonus, else the target's choice there is emitted and is the next anchor.
 // The parents were validated by the verify pass; a request whose rows
 // failed (argmax -1 on the path) is rejected (n_acc = -1).

@@ -4,9 +4,9 @@
 // Candidate i (drawn by the drafter from q_i) is accepted when
 // u * q_i(y) < p_i(y), u uniform on [0, 1) — the same as accepting with
 // probability min(1, p_i(y) / q_i(y)). p_i = softmax(z_i / T) in fp32 with
-// suppressed ids at probability 0. At the first rejection the next token is
-// drawn from the normalised residual (p_i - q_i)+, and after a fully accepted
-// block a bonus token is drawn from the next row's p. Draws use the inverse
+// suppressed ids at probability 0. A rejection at candidate i draws the next
+// token from (p_i - q_i)+ renormalised; when no candidate is rejected the
+// extra token comes from p of the row after the last candidate. Draws use the inverse
 // CDF in ascending id order. An accepted EOS ends the request with no bonus;
 // the output budget works as in greedy decoding.
 //

@@ -1,8 +1,9 @@
 """Pins of the oracle's acceptance, rollback and decode loops.
 
 * the worked example of Whisper-Flash Figure 1 (golden fixture);
-* App. A.1 arithmetic: rollback keeps L+1+a; an accepted EOS ends the
-  transcript with no bonus; at most R-1 candidates with R tokens left;
+* App. A.1 arithmetic: the cache keeps L+1+a positions after a round;
+  accepting EOS finishes the request with no bonus; a budget of R tokens
+  allows at most R-1 candidates;
 * the lossless property of greedy verification (Whisper-Flash §3.1; the
   "Speculative Loop" paragraph of "Alignment Drift ..."): the speculative
   output equals plain greedy decoding for ANY drafts, checked against a

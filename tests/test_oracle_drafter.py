@@ -1,11 +1,11 @@
 """Pins of the oracle's parallel drafter (Whisper-Flash §3.2, App. A.2).
 
-The pages print no drafter values, so beyond these checks the drafter's
-parity is unpinned beyond them:
+The pages print no drafter values, so the drafter's parity is unpinned
+beyond these checks:
 * RoPE equals multiplying each (i, i + hd/2) pair, read as a complex
   number, by exp(i * pos * 10000^(-2i/hd));
-* after RoPE a query-key product depends only on the position difference
-  ("explicit text positions, so cached history keys keep their indices");
+* after RoPE a query-key product depends only on the position difference,
+  so a history key cached in an earlier round stays valid in later ones;
 * the architecture reading reproduces the page's 60.7M trainable parameters;
 * the history built round by round from the accepted rows' taps equals the
   history built from one full recompute of the target;

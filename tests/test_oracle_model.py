@@ -155,7 +155,8 @@ def test_block_incremental_and_full_recompute_agree(tiny):
 
 def test_rejected_rows_are_dead_after_rollback(tiny):
     """Rows written past the kept length must not influence later rounds
-    (Whisper-Flash App. A.5: rejected positions stay allocated but masked)."""
+    (Whisper-Flash App. A.5: the rows of rejected candidates keep their
+    memory but are hidden from every later query)."""
     shape, wbits, enc = tiny
     m = om.Model(shape, wbits)
     g = np.random.default_rng(6)
