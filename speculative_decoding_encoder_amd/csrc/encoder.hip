@@ -19,7 +19,7 @@
 //    (the 16-byte chunks of a row XOR-swizzled: conflict-free fragment
 //    reads), the global loads of a k-step issued two k-steps ahead (K % 64
 //    == 0). Grids of two or more rounds take 256 x 256 tiles on eight waves
-//    whose operands are copied straight into a four-stage LDS ring. The MFMA
+//    whose operands are copied straight into LDS, two 64-deep stages. The MFMA
 //    computes C^T so a lane holds one output row and four consecutive
 //    columns (8- or 16-byte epilogue stores). Row tiles are grouped by 8 per
 //    column walk and workgroups are dealt to the 8 XCDs in consecutive
@@ -327,37 +327,34 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs a) {
 // per CU (one wave per SIMD leaves a third of the MFMA issue rate unused:
 // 1.3-1.9 against 2.45 PFLOP/s in a register-only loop on MI355X). Operands
 // go from global memory straight into LDS (global_load_lds, 16 bytes per
-// lane) through a ring of DST k-step stages. A stage holds 256 A rows and 256 W rows of 64 bytes whose four
-// 16-byte chunks are XOR-swizzled by row (chunk c of row r sits at
-// c ^ ((r >> 1) & 3)), so the fragment reads are free of bank conflicts
-// without padding. Per k-step: wait for the next stage's copies, one
-// barrier, the copies of the stage DST k-steps ahead into the buffer just
-// consumed, the next stage's fragments into registers while this stage's 32
-// MFMAs run. Every output still sums its k-steps in order in one lane with
-// the same MFMA as gemm_kernel, so the two give the same bits.
-constexpr int DBT = 256, DST = 4;          // tile rows / columns, ring stages
+// lane) in stages of two k-steps (64 elements of K), two stage buffers of
+// 64 KB. A copy instruction fills eight whole 128-byte rows, so every global
+// access reads full cache lines; the eight 16-byte chunks of a row are
+// XOR-swizzled (chunk c of row r sits at c ^ (r & 7)), so the copies and
+// the fragment reads are free of bank conflicts without padding. Per stage:
+// wait for this wave's copies of the stage, one barrier (every wave's copies
+// landed, every wave done with the other buffer), the copies of the next
+// stage into the other buffer, then both k-steps' fragments and their 2 x 32
+// MFMAs. Every output still sums its k-steps in order in one lane with the
+// same MFMA as gemm_kernel, so the two give the same bits.
+constexpr int DBT = 256;                   // tile rows / columns
 
 // gfx9 s_waitcnt immediates: vmcnt bits [3:0] and [15:14], expcnt [6:4],
 // lgkmcnt [11:8]; the counters not waited for stay at their maxima
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0070 | (0xF << 8)); }
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
     constexpr int MT = 8, NT = 4;
     constexpr int RPW = DBT / 8;                    // rows of each operand a wave copies
-    constexpr int CPO = RPW / 16;                   // its 16-row copies per operand
-    constexpr int DCOPY = 2 * CPO;                  // copies per wave per stage
-    // [stage][A rows 0..255 | W rows 0..255][32 elements]: 128 KB
-    __shared__ __attribute__((aligned(1024))) uint16_t lds[DST][2 * DBT * 32];
+    constexpr int CPO = RPW / 8;                    // its eight-row copies per operand
+    // [buffer][A rows 0..255 | W rows 0..255][64 elements]: 128 KB
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[2][2 * DBT * 64];
     const int per = gridDim.x >> 3;
     const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
     if (lid >= a.n_wg) return;
-    constexpr int GM = 8;                           // row tiles per column walk
+    constexpr int GM = 4;                           // row tiles per column walk
     const int grp = lid / (GM * a.n_n);
     const int first_m = grp * GM;
     const int gsz = min(a.n_m - first_m, GM);
@@ -371,14 +368,14 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
     const int m0 = mt * DBT, n0 = nt * DBT;
 
     // copies: wave w brings rows RPW w .. RPW w + RPW - 1 of the A and W
-    // tiles in 16-row copies; lane L fills row L / 4 of a copy, LDS chunk
-    // L % 4, with k-chunk (L % 4) ^ ((L >> 3) & 3). Rows past M / N repeat
-    // the last (never stored).
-    const int crow = lane >> 2, cchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    // tiles in eight-row copies; lane L fills row L / 8 of a copy, LDS chunk
+    // L % 8, with k-chunk (L % 8) ^ (L / 8). Rows past M / N repeat the last
+    // (never stored).
+    const int crow = lane >> 3, cchunk = (lane & 7) ^ ((lane >> 3) & 7);
     const uint16_t *asrc[CPO], *wsrc[CPO];
 #pragma unroll
     for (int i = 0; i < CPO; ++i) {
-        const int r = RPW * wave + 16 * i + crow;
+        const int r = RPW * wave + 8 * i + crow;
         const int m = min(m0 + r, a.M - 1);
         const int rq = m / a.rpr;
         asrc[i] = a.A + (size_t)rq * a.sreq + (size_t)(m - rq * a.rpr) * a.srow + cchunk * 8;
@@ -387,34 +384,35 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
         const uint16_t *wb = seg == 0 ? a.W0 : (seg == 1 ? a.W1 : a.W2);
         wsrc[i] = wb + (size_t)(n - seg * a.seg_n) * a.K + cchunk * 8;
     }
-    const int KT = a.K / GBK;
-    // stage kt into buffer kt % DST; past the end a valid repeat of the last
-    // k-step into a buffer nothing reads again, so every k-step issues the
-    // same number of copies and the wait counts stay exact
-    auto copy = [&](int kt) {
-        const int kk = min(kt, KT - 1) * GBK;
-        uint16_t *buf = lds[kt % DST];
+    const int KP = a.K / (2 * GBK);                 // stages (K % 64 == 0)
+    // stage p into buffer p & 1; past the end a valid repeat of the last stage
+    // into a buffer nothing reads again
+    auto copy = [&](int p) {
+        const int kk = min(p, KP - 1) * 2 * GBK;
+        uint16_t *buf = lds[p & 1];
 #pragma unroll
         for (int i = 0; i < CPO; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const void *)(asrc[i] + kk),
-                (__attribute__((address_space(3))) void *)&buf[(RPW * wave + 16 * i) * 32], 16, 0, 0);
+                (__attribute__((address_space(3))) void *)&buf[(RPW * wave + 8 * i) * 64], 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < CPO; ++i)
             __builtin_amdgcn_global_load_lds(
                 (const void *)(wsrc[i] + kk),
-                (__attribute__((address_space(3))) void *)&buf[(DBT + RPW * wave + 16 * i) * 32], 16,
+                (__attribute__((address_space(3))) void *)&buf[(DBT + RPW * wave + 8 * i) * 64], 16,
                 0, 0);
     };
-    const int sw = (g ^ ((r16 >> 1) & 3)) * 8;     // where this lane's k-chunk g sits
-    auto frags = [&](u32x4 (&xf)[MT], u32x4 (&wf)[NT], int kt) {
-        const uint16_t *buf = lds[kt % DST];
+    // k-step h of stage p: this lane's k-chunk 4 h + g of its rows
+    auto frags = [&](u32x4 (&xf)[MT], u32x4 (&wf)[NT], int p, int h) {
+        const uint16_t *buf = lds[p & 1];
+        const int sw = ((4 * h + g) ^ (r16 & 7)) * 8;
 #pragma unroll
         for (int i = 0; i < MT; ++i)
-            xf[i] = *reinterpret_cast<const u32x4 *>(&buf[(wm * 128 + 16 * i + r16) * 32 + sw]);
+            xf[i] = *reinterpret_cast<const u32x4 *>(&buf[(wm * 128 + 16 * i + r16) * 64 + sw]);
 #pragma unroll
         for (int j = 0; j < NT; ++j)
-            wf[j] = *reinterpret_cast<const u32x4 *>(&buf[(DBT + wn * 16 * NT + 16 * j + r16) * 32 + sw]);
+            wf[j] = *reinterpret_cast<const u32x4 *>(
+                &buf[(DBT + wn * 16 * NT + 16 * j + r16) * 64 + sw]);
     };
 
     f32x4 acc[MT][NT];
@@ -422,16 +420,7 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
     for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // k-step kt: its fragments are in registers (read during k-step kt - 1);
-    // stages kt + 1 .. kt + DST - 1 are in flight or landed
-    auto step = [&](int kt, const u32x4 (&xc)[MT], const u32x4 (&wc)[NT], u32x4 (&xn)[MT],
-                    u32x4 (&wn_)[NT]) {
-        wait_vmcnt<(DST - 2) * DCOPY>();            // this wave's copies of stage kt + 1
-        wait_lgkmcnt0();                            // its reads of stage kt (refilled below)
-        __builtin_amdgcn_s_barrier();               // every wave's, likewise
-        copy(kt + DST);
-        frags(xn, wn_, kt + 1);
-        __builtin_amdgcn_sched_barrier(0);
+    auto mfmas = [&](const u32x4 (&xc)[MT], const u32x4 (&wc)[NT]) {
         __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int i = 0; i < MT; ++i)
@@ -439,17 +428,20 @@ __global__ __launch_bounds__(512, 1) void gemm_dma_kernel(GemmArgs a) {
             for (int j = 0; j < NT; ++j) acc[i][j] = mfma_bf16_k32(wc[j], xc[i], acc[i][j]);
         __builtin_amdgcn_s_setprio(0);
     };
-#pragma unroll
-    for (int s = 0; s < DST; ++s) copy(s);
-    wait_vmcnt<(DST - 1) * DCOPY>();                // stage 0
-    __builtin_amdgcn_s_barrier();
+    copy(0);
     u32x4 xa[MT], wa[NT], xb[MT], wb[NT];
-    frags(xa, wa, 0);
-    for (int kt = 0; kt < KT; kt += 2) {            // KT is even (K % 64 == 0)
-        step(kt, xa, wa, xb, wb);
-        step(kt + 1, xb, wb, xa, wa);
+    for (int p = 0; p < KP; ++p) {
+        wait_vmcnt0();                              // this wave's copies of stage p
+        wait_lgkmcnt0();                            // its reads of stage p - 1
+        __builtin_amdgcn_s_barrier();               // every wave's, likewise
+        copy(p + 1);                                // into stage p - 1's buffer
+        frags(xa, wa, p, 0);
+        frags(xb, wb, p, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(xa, wa);
+        mfmas(xb, wb);
     }
-    wait_vmcnt<0>();                                // no copy outlives the workgroup's LDS
+    wait_vmcnt0();                                  // no copy outlives the workgroup's LDS
     epilogue<EPI, MT, NT>(a, acc, m0 + wm * 128, n0 + wn * 16 * NT);
 }
 
