@@ -8,9 +8,10 @@
 //    one weight fragment feeds MB MFMAs, one activation fragment NW.
 //  * The activations of a k-step (MB fragments of 1 KB, already in MFMA
 //    lane order) are fetched once per workgroup into a register ring D
-//    k-steps ahead and copied to a triple-buffered LDS stage two k-steps
+//    k-steps ahead and copied into a ring of five LDS buffers three k-steps
 //    ahead; all four waves read them from there, the next k-step's
-//    fragments while the current k-step's MFMAs run. Weight fragments go
+//    fragments while the current k-step's MFMAs run, and meet at a barrier
+//    after every second k-step. Weight fragments go
 //    from global memory straight into each wave's registers through the
 //    same ring; each weight element is loaded by exactly one wave per row
 //    block.
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_tl_kernel(GemmArgs a) {
     constexpr int XL = (XF * 64 + 255) / 256;      // 16-byte activation loads per thread
     constexpr int BM = 16 * MB, BN = 64 * NW;
     constexpr int P = 8 / CPG;                     // K groups (the K chunks are 8)
-    __shared__ __attribute__((aligned(16))) uint16_t xs[3][XF * 512];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[5][XF * 512];
 
     const int per = gridDim.x >> 3;
     const int lid = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
@@ -140,21 +141,28 @@ __global__ __launch_bounds__(256, OCC) void gemm_tl_kernel(GemmArgs a) {
     };
 
     // Entering k-step s: ring slot t % D holds the weights of k-step t for
-    // t in [s, s + D) and the activations of k-step t for t in [s + 2,
-    // s + 2 + D); LDS buffer (s + 1) % 3 holds the activations of k-step
-    // s + 1 and xc those of k-step s. Each k-step stages k-step s + 2, reads
-    // the fragments of k-step s + 1 while its MFMAs run, and ends with a
-    // barrier.
+    // t in [s, s + D) and the activations of k-step t for t in [s + 3,
+    // s + 3 + D) (D >= 4); LDS buffer t % 5 holds the activations of k-step
+    // t for t in [s + 1, s + 3) and xc those of k-step s. Each k-step stages
+    // k-step s + 3 and reads the fragments of k-step s + 1 while its MFMAs
+    // run; odd k-steps end with a barrier. That is enough: the fragments of
+    // k-step t are read at k-step t - 1, two or more k-steps after they were
+    // staged (at t - 3), with a barrier after t - 3 or t - 2; and buffer
+    // t % 5 is staged again at k-step t + 2, after the barrier that follows
+    // t - 1 or t.
     Slot ring[D];
 #pragma unroll
     for (int i = 0; i < D; ++i) {
         load_x(ring[i], i);
         load_w(ring[i], i);
     }
+    static_assert(D >= 4, "the ring holds the activations three k-steps ahead");
     stage(ring[0], 0);
     stage(ring[1], 1);
+    stage(ring[2], 2);
     load_x(ring[0], D);
     load_x(ring[1], D + 1);
+    load_x(ring[2], D + 2);
     __syncthreads();
     u32x4 xa[XF], xb[XF];
     read_frags(xa, 0);
@@ -168,10 +176,10 @@ __global__ __launch_bounds__(256, OCC) void gemm_tl_kernel(GemmArgs a) {
         }
         // sched_barrier(0) pins the phase order (the scheduler would
         // otherwise sink the fragment reads next to their MFMAs a step later)
-        stage(two, (s + 2) % 3);
-        load_x(two, s + 2 + D);
+        stage(two, (s + 3) % 5);
+        load_x(two, s + 3 + D);
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(xn, (s + 1) % 3);
+        read_frags(xn, (s + 1) % 5);
         __builtin_amdgcn_sched_barrier(0);
         u32x4 wh[NW];
 #pragma unroll
@@ -184,14 +192,14 @@ __global__ __launch_bounds__(256, OCC) void gemm_tl_kernel(GemmArgs a) {
         __builtin_amdgcn_sched_barrier(0);
         load_w(cur, s + D);
         if ((s + 1) % CK == 0) tree.push(s / CK, c);
-        __syncthreads();
+        if (s & 1) __syncthreads();
     };
     for (int ss = 0; ss < NSTEPS / L; ++ss) {
 #pragma unroll
         for (int i = 0; i < L; ++i) {
             const int s = ss * L + i;
-            if (i % 2 == 0) step(s, ring[i % D], ring[(i + 2) % D], xa, xb);
-            else step(s, ring[i % D], ring[(i + 2) % D], xb, xa);
+            if (i % 2 == 0) step(s, ring[i % D], ring[(i + 3) % D], xa, xb);
+            else step(s, ring[i % D], ring[(i + 3) % D], xb, xa);
         }
     }
     f32x4 (&total)[NT] = tree.l0;
