@@ -235,6 +235,70 @@ def test_device_error_words(tiny):
     assert err[0] == 0 and err[1] == 0 and ln[0] == 0
 
 
+def test_host_checks_reject_bad_calls_and_leave_state(tiny):
+    """The four calls through the C-ABI with an empty batch, more requests
+    than max_batch, a block past max_rows, a zero-row block, a null pointer
+    and non-finite or negative temperatures: each returns its status code
+    (WF_ECAPACITY -3, WF_EINVAL -1) with a message, launches nothing, and a
+    block verified afterwards gives the bits it gave before them."""
+    from speculative_decoding_encoder_amd.binding import _stream
+    eng = tiny["eng"]
+    torch, lib, h = eng.torch, eng.lib, eng.h
+    st = _stream(None)
+    EINVAL, ECAP = -1, -3
+    prefix = tiny["prefix"]
+    P = len(prefix)
+    eng.wf_reset(eng.i32([0]))
+    am0, lg0 = _verify(eng, [0], np.array([prefix], np.int32), [P])
+
+    slots, ntok = eng.i32([0, 1, 2, 3, 0]), eng.i32([1] * 5)
+    toks = eng.i32(np.ones((5, 300), np.int32))
+    am = torch.empty((5, 300), dtype=torch.int32, device=eng.dev)
+    enc = torch.zeros(5 * TINY.n_frames * TINY.d_model, dtype=torch.int16, device=eng.dev)
+    p = lambda t: t.data_ptr()
+    cases = [
+        ("verify n=0", lib.wf_verify_block(h, 0, p(slots), p(toks), 1, p(ntok), p(am), None, st), ECAP),
+        ("verify n>max_batch", lib.wf_verify_block(h, 5, p(slots), p(toks), 1, p(ntok), p(am), None, st), ECAP),
+        ("verify n*T>max_rows", lib.wf_verify_block(h, 2, p(slots), p(toks), 300, p(ntok), p(am), None, st), ECAP),
+        ("verify T=0", lib.wf_verify_block(h, 1, p(slots), p(toks), 0, p(ntok), p(am), None, st), EINVAL),
+        ("verify null slots", lib.wf_verify_block(h, 1, None, p(toks), 1, p(ntok), p(am), None, st), EINVAL),
+        ("rollback n=0", lib.wf_rollback(h, 0, p(slots), p(ntok), st), ECAP),
+        ("rollback n>max_batch", lib.wf_rollback(h, 5, p(slots), p(ntok), st), ECAP),
+        ("encode n=0", lib.wf_encode_kv(h, 0, p(slots), p(enc), st), ECAP),
+        ("encode n>max_batch", lib.wf_encode_kv(h, 5, p(slots), p(enc), st), ECAP),
+    ]
+    outs = [torch.zeros(5, dtype=torch.int32, device=eng.dev) for _ in range(4)]
+    acc = lambda n, temp, am_=am: lib.wf_accept(h, n, p(toks), 2, p(ntok), p(ntok), p(am_), None,
+                                             None, None, temp, 0, None, None,
+                                             *[p(o) for o in outs], st)
+    cases += [
+        ("accept n=0", acc(0, 0.0), ECAP),
+        ("accept n>max_batch", acc(5, 0.0), ECAP),
+        ("accept T<0", acc(1, -1.0), EINVAL),
+        ("accept T=nan", acc(1, float("nan")), EINVAL),
+        ("accept T=inf", acc(1, float("inf")), EINVAL),
+        ("accept sampling without logits", acc(1, 0.7), EINVAL),
+        ("accept greedy without argmax", lib.wf_accept(h, 1, p(toks), 2, p(ntok), p(ntok), None,
+                                                       None, None, None, 0.0, 0, None, None,
+                                                       *[p(o) for o in outs], st), EINVAL),
+    ]
+    for what, got, want in cases:
+        assert got == want, f"{what}: status {got}, expected {want}"
+        assert lib.wf_last_error().decode(), what
+    torch.cuda.synchronize()
+    assert not any(o.any().item() for o in outs)      # no accept kernel ran
+    err, ln = eng.wf_device_state()
+    assert err[0] == 0 and ln[0] == 0                 # the block is still pending
+    eng.wf_rollback(eng.i32([0]), eng.i32([P - 1]))
+    err, ln = eng.wf_device_state()
+    assert err[0] == 0 and ln[0] == P
+    eng.wf_reset(eng.i32([0]))
+    am1, lg1 = _verify(eng, [0], np.array([prefix], np.int32), [P])
+    assert np.array_equal(am0, am1)
+    assert np.array_equal(lg0.view(np.uint32), lg1.view(np.uint32))
+    eng.wf_reset(eng.i32([0]))
+
+
 @pytest.mark.parametrize("persistent", [0, 1])
 def test_nan_logit_flags_the_slot(torch_cuda, persistent):
     """A NaN in one row of the tied embedding (an id no input uses) makes
