@@ -388,6 +388,71 @@ def test_large_v3_b1_prefix64_block9(torch_cuda):
 
 
 # --------------------------------------------------------------------------
+# full 32-layer shape, batch 32, prefixes U[4, 200], one block of 9 each
+def test_large_v3_b32_block_on_sampled_requests(torch_cuda):
+    """The batch-32 verify of the 32-layer large-v3 shape in the launch
+    configuration the benchmark times (288 rows: tall-block QKV / fc1 / fc2
+    and LM head, register-tiled O / O_c / cross Q, cross-attention in
+    chunk groups): the requests with the shortest and the longest prompt
+    against the oracle (logits within 2e-2, argmax and acceptance where the
+    margins are clear); their blocks are the oracle's greedy continuation
+    with Bernoulli-copy drafts, the other requests' blocks random ids."""
+    from speculative_decoding_encoder_amd.harness import prefill
+    wl = WORKLOADS[4]
+    B, K = wl.batch, wl.k_draft
+    log("large-v3 b32: generating weights and inputs")
+    wbits = make_weights(LARGE_V3, wl.cfg_id)
+    encs = np.stack([make_encoder_out(LARGE_V3, wl.cfg_id, r) for r in range(B)])
+    prefixes = make_prefixes(wl, B)
+    lens = np.array([len(p) for p in prefixes], np.int32)
+    picks = sorted({int(lens.argmin()), int(lens.argmax())})
+    rng = np.random.default_rng(432)
+    blocks = rng.integers(0, LARGE_V3.vocab, (B, K + 1)).astype(np.int32)
+    m = om.Model(LARGE_V3, wbits)
+    refs = {}
+    for b in picks:
+        log(f"large-v3 b32: oracle request {b} (prompt {lens[b]})")
+        req = m.new_request(encs[b])
+        ref_pre = m.rows(req, prefixes[b], 0)
+        greedy = [od.argmax_lowest(ref_pre[-1])]
+        L = int(lens[b])
+        for _ in range(K):
+            greedy.append(od.argmax_lowest(m.rows(req, [greedy[-1]], L)[0]))
+            L += 1
+        keep, repl = make_draft_table(wl, b)
+        drafts = od.table_drafts(greedy, int(lens[b]), keep, repl)(int(lens[b]), greedy[0], K)
+        blocks[b] = [greedy[0]] + drafts
+        # rows() writes the block's K/V over the continuation's at the same
+        # positions, so the request state serves again
+        refs[b] = (ref_pre[-1], m.rows(req, blocks[b], int(lens[b])), drafts)
+    del m
+    log("large-v3 b32: GPU")
+    eng = _engine(LARGE_V3, wbits, max_batch=B, max_rows=B * int(lens.max()))
+    torch = eng.torch
+    slots = list(range(B))
+    eng.wf_encode_kv(eng.i32(slots), eng.bf16(encs))
+    anchors = prefill(eng, slots, prefixes)
+    am, lg = _verify(eng, slots, blocks, [K + 1] * B)
+    outs = [torch.empty(B, dtype=torch.int32, device=eng.dev) for _ in range(4)]
+    eng.wf_accept(eng.i32(blocks), eng.i32([K + 1] * B), eng.i32([wl.n_max] * B), eng.i32(am),
+                  *outs)
+    a_gpu, c_gpu = outs[0].cpu().numpy(), outs[1].cpu().numpy()
+    err, _ = eng.wf_device_state()
+    assert (err[:B] == 0).all()
+    for b in picks:
+        last_pre, ref_blk, drafts = refs[b]
+        assert_argmax_where_clear(anchors[b:b + 1], last_pre[None], what=f"b32 anchor {b}")
+        e = assert_logits_close(lg[b], ref_blk, what=f"b32 block {b}")
+        assert_argmax_where_clear(am[b], ref_blk, what=f"b32 block {b}")
+        a_ref, c_ref, pinned = oracle_accept_pinned(drafts, ref_blk, K)
+        if pinned:
+            assert (a_gpu[b], c_gpu[b]) == (a_ref, c_ref), b
+        log(f"large-v3 b32 request {b}: prompt {lens[b]}, max err {e:.2e}, a={a_gpu[b]} "
+            f"(oracle {a_ref}, pinned={pinned})")
+    eng.close()
+
+
+# --------------------------------------------------------------------------
 # turbo shape, batch 32, ragged prefixes, shuffled pages
 def test_turbo_b32_ragged_shuffled_pages(torch_cuda):
     wl = WORKLOADS[2]
