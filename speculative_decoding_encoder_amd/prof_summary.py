@@ -7,7 +7,7 @@ rocprofv3 CSV output of a kernel-trace run or of a counter run and keeps the
 dispatches that start inside such a window.
 
   python -m speculative_decoding_encoder_amd.prof_summary stats \\
-      --dir gpurun_out/prof_b32_tr --log gpurun_out/prof_b32_tr.log \\
+      --dir RUN_DIR --log BENCH_LOG \\
       --window large-v3-verify-b32-greedy --title "..." --command "..." --out FILE
 
   python -m speculative_decoding_encoder_amd.prof_summary mfma --dir D --log L \\
